@@ -1,0 +1,162 @@
+"""mla8 oracle -- TEST INFRASTRUCTURE ONLY.
+
+Thin numpy/ctypes wrapper over ``mla8_oracle.c``, the plain double-precision CPU
+implementation of the fp8 latent-KV MLA decode path.  Only the tests, the smoke
+check and the CPU-baseline leg of the benchmark may import this package; the
+product library never does.  Nothing here shares code with the HIP library.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "mla8_oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+
+# -ffp-contract=off: every f32 product and quotient in the quantizer is rounded
+# on its own, as the definition states; -fno-fast-math keeps IEEE semantics.
+CFLAGS = ["-O2", "-std=c11", "-fPIC", "-shared", "-fopenmp", "-ffp-contract=off",
+          "-fno-fast-math", "-Wall", "-Wextra"]
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle with gcc into ``oracle/liboracle.so``."""
+    if force or not os.path.exists(_LIB):
+        tmp = _LIB + ".tmp"
+        subprocess.check_call(["gcc", *CFLAGS, "-o", tmp, _SRC, "-lm"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB):
+            build()
+        L = ctypes.CDLL(_LIB)
+        P = ctypes.c_void_p
+        i64, i32, f32 = ctypes.c_int64, ctypes.c_int32, ctypes.c_float
+        L.mla8o_dec.restype = ctypes.c_double
+        L.mla8o_dec.argtypes = [ctypes.c_uint8]
+        L.mla8o_enc.restype = ctypes.c_uint8
+        L.mla8o_enc.argtypes = [f32]
+        L.mla8o_encode_array.argtypes = [P, i64, P]
+        L.mla8o_decode_array.argtypes = [P, i64, P]
+        L.mla8o_quantize_row.argtypes = [P, i32, P, P]
+        L.mla8o_quantize_rows.argtypes = [P, i64, i32, P, P]
+        L.mla8o_decode.argtypes = [P, P, i64, i32, i32, P, P, i32, f32, P, P]
+        L.mla8o_decode_sel.argtypes = [P, P, i64, i32, i32, P, i64, P, P, i32, f32, P, P]
+        L.mla8o_batch.argtypes = [P, P, i64, i32, i32, P, P, i32, i64, i32, f32, P, P]
+        L.mla8o_decode_chunked.argtypes = [P, P, i64, i32, i32, P, P, i32, f32, i64, P, P]
+        L.mla8o_threads.restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def _ptr(a: np.ndarray) -> int:
+    assert a.flags["C_CONTIGUOUS"]
+    return a.ctypes.data
+
+
+def _c(a, dtype) -> np.ndarray:
+    return np.ascontiguousarray(a, dtype=dtype)
+
+
+def dec(codes) -> np.ndarray:
+    """e4m3 bytes -> float64 values (NaN for 0x7F / 0xFF)."""
+    c = _c(codes, np.uint8)
+    out = np.empty(c.shape, np.float64)
+    lib().mla8o_decode_array(_ptr(c), c.size, _ptr(out))
+    return out
+
+
+def enc(x) -> np.ndarray:
+    """float32 values -> e4m3 bytes (RNE, saturating, NaN -> 0x00)."""
+    v = _c(x, np.float32)
+    out = np.empty(v.shape, np.uint8)
+    lib().mla8o_encode_array(_ptr(v), v.size, _ptr(out))
+    return out
+
+
+def quantize_rows(x) -> tuple[np.ndarray, np.ndarray]:
+    """f32 rows [n, D] -> (e4m3 codes [n, D] uint8, f32 scales [n])."""
+    v = _c(x, np.float32)
+    n, d = v.shape
+    codes = np.empty((n, d), np.uint8)
+    scales = np.empty((n,), np.float32)
+    lib().mla8o_quantize_rows(_ptr(v), n, d, _ptr(codes), _ptr(scales))
+    return codes, scales
+
+
+def dequant(codes, scales) -> np.ndarray:
+    """Exact float64 values of a quantized shadow: dec(code) * scale."""
+    return dec(codes) * np.asarray(scales, np.float64)[..., None]
+
+
+def decode(codes, scales, t_rows, lc, rc, q_lat, q_rope, sm_scale):
+    """Dense decode of H heads over rows [0, t_rows): (out [H, lc] f64, lse [H] f64)."""
+    codes = _c(codes, np.uint8)
+    scales = _c(scales, np.float32)
+    ql = _c(q_lat, np.float32)
+    qr = _c(q_rope, np.float32)
+    h = ql.shape[0]
+    out = np.empty((h, lc), np.float64)
+    lse = np.empty((h,), np.float64)
+    lib().mla8o_decode(_ptr(codes), _ptr(scales), t_rows, lc, rc, _ptr(ql), _ptr(qr), h,
+                       float(np.float32(sm_scale)), _ptr(out), _ptr(lse))
+    return out, lse
+
+
+def decode_sel(codes, scales, t_rows, lc, rc, sel, q_lat, q_rope, sm_scale):
+    """Decode over the selected absolute rows ``sel`` (a multiset; out-of-range skipped)."""
+    codes = _c(codes, np.uint8)
+    scales = _c(scales, np.float32)
+    s = _c(sel, np.int32)
+    ql = _c(q_lat, np.float32)
+    qr = _c(q_rope, np.float32)
+    h = ql.shape[0]
+    out = np.empty((h, lc), np.float64)
+    lse = np.empty((h,), np.float64)
+    lib().mla8o_decode_sel(_ptr(codes), _ptr(scales), t_rows, lc, rc, _ptr(s), s.size,
+                           _ptr(ql), _ptr(qr), h, float(np.float32(sm_scale)), _ptr(out),
+                           _ptr(lse))
+    return out, lse
+
+
+def batch(codes, scales, t_rows, lc, rc, q_lat, q_rope, pos0, sm_scale):
+    """Causal batch: query s (position pos0+s) attends rows [0, pos0+s]."""
+    codes = _c(codes, np.uint8)
+    scales = _c(scales, np.float32)
+    ql = _c(q_lat, np.float32)
+    qr = _c(q_rope, np.float32)
+    n_q, h = ql.shape[0], ql.shape[1]
+    out = np.empty((n_q, h, lc), np.float64)
+    lse = np.empty((n_q, h), np.float64)
+    lib().mla8o_batch(_ptr(codes), _ptr(scales), t_rows, lc, rc, _ptr(ql), _ptr(qr), n_q,
+                      pos0, h, float(np.float32(sm_scale)), _ptr(out), _ptr(lse))
+    return out, lse
+
+
+def decode_chunked(codes, scales, t_rows, lc, rc, q_lat, q_rope, sm_scale, n_chunks):
+    """Split-T decode: per-chunk streaming partials + log-sum-exp merge."""
+    codes = _c(codes, np.uint8)
+    scales = _c(scales, np.float32)
+    ql = _c(q_lat, np.float32)
+    qr = _c(q_rope, np.float32)
+    h = ql.shape[0]
+    out = np.empty((h, lc), np.float64)
+    lse = np.empty((h,), np.float64)
+    lib().mla8o_decode_chunked(_ptr(codes), _ptr(scales), t_rows, lc, rc, _ptr(ql), _ptr(qr),
+                               h, float(np.float32(sm_scale)), n_chunks, _ptr(out), _ptr(lse))
+    return out, lse
+
+
+def threads() -> int:
+    return int(lib().mla8o_threads())
