@@ -1,0 +1,227 @@
+#!/usr/bin/env python3
+"""Long-context fp8 latent-KV MLA decode benchmark on one MI355X.
+
+Workload (the long-context split-T decode of colibri PR #300, "KV8
+long-context CUDA", second commit): H=64 heads, kv_lora Lc=512, rope Rc=64,
+T=262144 e4m3 rows + f32 scales resident in HBM, batch 1.  One layer-token =
+quantize and append one fresh row at row T-1 (the shadow holds T-1 rows before
+it), then attend all T rows (split-T partial kernel + log-sum-exp merge).
+
+A step is one decode token through `--layers` independent layers (default 8,
+1.22 GB of shadows, so the 256 MB Infinity Cache cannot hold the stream).  The
+step is captured once as a HIP graph and replayed; W untimed warm-up steps,
+then K timed steps between synchronisations.  Inputs are seeded synthetic
+N(0,1) rows and queries.
+
+Prints one JSON line: value = ms per layer-token (lower is better), plus the
+effective HBM rate of the fp8 KV stream, the roofline of the split-T partial
+kernel (its own duration from HIP events recorded on its launch stream around
+every launch in a separate eager pass), and the CPU oracle timed on a bounded
+sample on this host.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "ms/layer-token + achieved HBM GB/s (fp8 KV stream), MLA decode at T=262144"
+HBM_PEAK_GBS = 8000.0
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--layers", type=int, default=8)
+    ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of a graph")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-heads", type=int, default=16,
+                    help="heads of the CPU-oracle sample (full T, scaled to 64 heads)")
+    ap.add_argument("--traffic", type=str, default=None,
+                    help="JSON file with rocprofv3 FETCH/WRITE bytes per partial launch")
+    return ap.parse_args()
+
+
+def cpu_baseline(w, heads):
+    """The oracle (as it stands) on a bounded sample of the same step: quantize
+    one fresh row, then dense fp64 attention of `heads` heads over all T rows.
+    Scaled to the full 64-head layer-token."""
+    import numpy as np
+
+    import oracle
+    from fp8_mla_latent_amd import workloads as W
+
+    x = W.rows(w, w.t_rows, seed_offset=0)
+    codes, scales = oracle.quantize_rows(x[:-1])
+    codes = np.concatenate([codes, np.zeros((1, w.d), np.uint8)])
+    scales = np.concatenate([scales, np.zeros(1, np.float32)])
+    ql, qr = W.queries(w, seed_offset=0)
+    t0 = time.perf_counter()
+    c1, s1 = oracle.quantize_rows(x[-1:])
+    codes[-1], scales[-1] = c1[0], s1[0]
+    oracle.decode(codes, scales, w.t_rows, w.lc, w.rc, ql[:heads], qr[:heads], w.sm_scale)
+    dt = time.perf_counter() - t0
+    ms = dt * 1e3 * (w.n_heads / heads)
+    return {"value": round(ms, 3), "unit": "ms/layer-token", "cores": oracle.threads(),
+            "kind": "oracle",
+            "sample": f"append 1 row + fp64 attention of {heads} of {w.n_heads} heads over "
+                      f"T={w.t_rows} rows ({dt:.2f} s), scaled x{w.n_heads / heads:g} to all heads"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build measures one GPU; --gpus {args.gpus} is not supported "
+              "(the split-T path would shard rows across GPUs with one all-gather of partials; "
+              "that exchange is not built)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from fp8_mla_latent_amd import mla8 as m
+    from fp8_mla_latent_amd import workloads as W
+
+    w = W.LONG
+    L, K, WU = args.layers, args.steps, args.warmup
+    T, D = w.t_rows, w.d
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    # ---- setup (untimed): L layer shadows of T-1 rows, quantized on the GPU
+    layers = []
+    for l in range(L):
+        x = torch.from_numpy(W.rows(w, T, seed_offset=l)).to(dev)
+        codes = torch.empty((T, D), dtype=torch.uint8, device=dev)
+        scales = torch.empty((T,), dtype=torch.float32, device=dev)
+        t = m.mla8_append(codes, scales, 0, x[:T - 1], w.lc, w.rc)
+        assert t == T - 1
+        fresh = x[T - 1:].clone()
+        del x
+        ql, qr = W.queries(w, seed_offset=l)
+        layers.append(dict(codes=codes, scales=scales, fresh=fresh,
+                           ql=torch.from_numpy(ql).to(dev), qr=torch.from_numpy(qr).to(dev),
+                           out=torch.empty((w.n_heads, w.lc), dtype=torch.float32, device=dev),
+                           lse=torch.empty((w.n_heads,), dtype=torch.float32, device=dev)))
+        log(f"layer {l}: {T - 1} rows quantized")
+    ws_bytes = m.mla8_workspace_bytes(m.MLA8_OP_DECODE, T, w.n_heads, 1, w.lc)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+
+    def step():
+        for ly in layers:
+            t = m.mla8_append(ly["codes"], ly["scales"], T - 1, ly["fresh"], w.lc, w.rc)
+            m.mla8_decode(ly["codes"], ly["scales"], t, w.lc, w.rc, ly["ql"], ly["qr"],
+                          w.sm_scale, out=ly["out"], lse=ly["lse"], workspace=ws)
+
+    # ---- main measurement: K steps (graph replay unless --no-graph)
+    for _ in range(max(WU, 1)):
+        step()
+    torch.cuda.synchronize()
+    graph = None
+    if not args.no_graph:
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step()
+        torch.cuda.synchronize()
+        run = graph.replay
+    else:
+        run = step
+    for _ in range(WU):
+        run()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    t_wall = time.perf_counter()
+    e0.record()
+    for _ in range(K):
+        run()
+    e1.record()
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall
+    ms_step = e0.elapsed_time(e1) / K
+    ms_lt = ms_step / L
+    kv_bytes = T * (D + 4)
+    log(f"step {ms_step:.4f} ms ({L} layers), {ms_lt * 1e3:.2f} us/layer-token, "
+        f"wall {t_wall:.3f} s")
+
+    # ---- partial-kernel duration: HIP events recorded by the library around
+    # every split-T partial launch, on the launch stream, eager pass of K steps
+    n_ev = K * L
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(n_ev)]
+    i = 0
+    try:
+        for _ in range(K):
+            for ly in layers:
+                t = m.mla8_append(ly["codes"], ly["scales"], T - 1, ly["fresh"], w.lc, w.rc)
+                m.mla8_profile_events(*evs[i])
+                m.mla8_decode(ly["codes"], ly["scales"], t, w.lc, w.rc, ly["ql"], ly["qr"],
+                              w.sm_scale, out=ly["out"], lse=ly["lse"], workspace=ws)
+                i += 1
+    finally:
+        m.mla8_profile_events(None, None)
+    torch.cuda.synchronize()
+    durs = np.array([a.elapsed_time(b) for a, b in evs]) * 1e3  # us
+    part_us = float(np.mean(durs))
+    alg_bytes = kv_bytes + w.n_heads * D * 4  # fp8 rows + scales, f32 query
+    achieved = alg_bytes / (part_us * 1e-6) / 1e9
+    traffic = None
+    if args.traffic and os.path.exists(args.traffic):
+        traffic = json.load(open(args.traffic)).get("bytes_per_launch")
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                "kernel": "k_split_partial<9>", "kernel_us": round(part_us, 3),
+                "kernel_us_p10_p90": [round(float(np.percentile(durs, 10)), 3),
+                                      round(float(np.percentile(durs, 90)), 3)],
+                "algorithmic_bytes": alg_bytes}
+    log(f"partial kernel {part_us:.2f} us mean -> {achieved:.0f} GB/s "
+        f"({100 * achieved / HBM_PEAK_GBS:.1f}% of {HBM_PEAK_GBS:.0f})")
+
+    # sanity: outputs finite
+    for ly in layers:
+        assert torch.isfinite(ly["out"]).all() and torch.isfinite(ly["lse"]).all()
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(w, args.cpu_heads)
+        log(f"cpu oracle: {cpu}")
+
+    rec = {
+        "metric": METRIC,
+        "value": round(ms_lt, 6),
+        "unit": "ms/layer-token",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": WU,
+        "ms_per_step": round(ms_step, 6),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "e4m3 kv, f16+e4m3 mfma, f32 accumulate",
+        "data": "synthetic: seeded N(0,1) rows and queries",
+        "config": {"workload": w.name, "heads": w.n_heads, "kv_lora": w.lc, "rope": w.rc,
+                   "t_rows": T, "batch": 1, "layers_per_step": L,
+                   "launch": "hip graph" if graph is not None else "eager",
+                   "splits": m.mla8_plan_splits(m.MLA8_OP_DECODE, T, w.n_heads)},
+        "kv_stream_gb_per_s": round(kv_bytes / (ms_lt * 1e-3) / 1e9, 1),
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,313 @@
+// C-ABI entry points of libmla8 (declared in include/mla8.h): argument checks,
+// split planning, workspace carving and kernel launches.  Every check runs on
+// the host before any HIP call, so the error paths work without a GPU.
+#include "mla8.h"
+#include "mla8_internal.h"
+
+#include <math.h>
+#include <stdint.h>
+
+namespace {
+
+using namespace mla8;
+
+int32_t g_forced_splits = 0;
+hipEvent_t g_ev_before = nullptr;
+hipEvent_t g_ev_after = nullptr;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int check_shape(int32_t lc, int32_t rc)
+{
+    if (lc < 16 || lc > 512 || (lc % 16) != 0)
+        return MLA8_E_UNSUPPORTED;
+    if (rc < 0 || rc > 128 || (rc % 16) != 0)
+        return MLA8_E_UNSUPPORTED;
+    if (lc + rc > 640)
+        return MLA8_E_UNSUPPORTED;
+    return MLA8_OK;
+}
+
+struct Plan {
+    int32_t n_chunks;
+    int32_t chunk_rows;
+    int32_t n_groups;
+};
+
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Row chunks for a call that attends `rows` rows with `n_qh` query-heads.
+// Aim for one workgroup per CU; prefer a multiple of 8 chunks (one per XCD
+// round); keep chunks at least 256 rows (64 for a gather), so that the partial
+// (m, z, cl) traffic stays small next to the rows it summarises.
+Plan make_plan(int32_t op, int64_t rows, int32_t n_qh)
+{
+    Plan p;
+    p.n_groups = (int32_t)cdiv(n_qh, kHeadsPerGroup);
+    int64_t P;
+    if (g_forced_splits > 0) {
+        P = g_forced_splits;
+    } else {
+        P = kTargetGroups / p.n_groups;
+        if (P < 1)
+            P = 1;
+        if (P >= 8)
+            P &= ~int64_t(7);
+        const int64_t min_rows = (op == MLA8_OP_DECODE_SEL) ? kTileRows : 4 * kTileRows;
+        const int64_t cap = cdiv(rows, min_rows);
+        if (P > cap)
+            P = cap;
+    }
+    const int64_t max_p = cdiv(rows, kTileRows);
+    if (P > max_p)
+        P = max_p;
+    if (P < 1)
+        P = 1;
+    int64_t chunk = cdiv(cdiv(rows, P), kTileRows) * kTileRows;
+    p.chunk_rows = (int32_t)chunk;
+    p.n_chunks = (int32_t)cdiv(rows, chunk);
+    return p;
+}
+
+size_t ws_bytes_for(const Plan& p, int32_t n_qh, int32_t lc)
+{
+    // m, z and cl, each section rounded up to 256 bytes
+    auto r256 = [](size_t b) { return (b + 255) & ~size_t(255); };
+    const size_t mz = (size_t)p.n_chunks * (size_t)n_qh * sizeof(float);
+    const size_t cl = mz * (size_t)lc;
+    return 2 * r256(mz) + r256(cl);
+}
+
+int run_attention(int32_t op, const uint8_t* codes, const float* scales, int64_t t_rows,
+                  int32_t lc, int32_t rc, const int32_t* sel, int64_t n_list, const float* q_lat,
+                  const float* q_rope, int32_t n_qh, int32_t n_heads, int64_t pos0,
+                  float sm_scale, float* out, float* lse, void* workspace, size_t ws_bytes,
+                  void* stream)
+{
+    const Plan p = make_plan(op, n_list, n_qh);
+    const size_t need = ws_bytes_for(p, n_qh, lc);
+    if (workspace == nullptr || ws_bytes < need)
+        return MLA8_E_WORKSPACE;
+    if (!aligned16(workspace))
+        return MLA8_E_INVAL;
+    auto r256 = [](size_t b) { return (b + 255) & ~size_t(255); };
+    const size_t mz = (size_t)p.n_chunks * (size_t)n_qh * sizeof(float);
+    char* ws = static_cast<char*>(workspace);
+
+    AttnArgs a;
+    a.codes = codes;
+    a.scales = scales;
+    a.t_rows = (int32_t)t_rows;
+    a.sel = sel;
+    a.n_list = (int32_t)n_list;
+    a.q_lat = q_lat;
+    a.q_rope = q_rope;
+    a.lc = lc;
+    a.rc = rc;
+    a.d = lc + rc;
+    a.n_qh = n_qh;
+    a.n_heads = n_heads;
+    a.pos0 = (int32_t)pos0;
+    a.mode = op == MLA8_OP_DECODE_SEL ? kSelect : (op == MLA8_OP_BATCH ? kCausal : kDense);
+    a.sm_log2 = sm_scale * 1.4426950408889634f;
+    a.n_chunks = p.n_chunks;
+    a.chunk_rows = p.chunk_rows;
+    a.n_groups = p.n_groups;
+    a.ws_m = reinterpret_cast<float*>(ws);
+    a.ws_z = reinterpret_cast<float*>(ws + r256(mz));
+    a.ws_cl = reinterpret_cast<float*>(ws + 2 * r256(mz));
+    a.out = out;
+    a.lse = lse;
+    return launch_attention(a, static_cast<hipStream_t>(stream), g_ev_before, g_ev_after) ==
+                   hipSuccess
+               ? MLA8_OK
+               : MLA8_E_HIP;
+}
+
+constexpr int64_t kMaxRows = 0x7FFFFFFF;
+
+}  // namespace
+
+extern "C" {
+
+int mla8_quantize_rows(const float* x, int64_t n_rows, int32_t lc, int32_t rc, uint8_t* codes,
+                       float* scales, void* stream)
+{
+    int st = check_shape(lc, rc);
+    if (st != MLA8_OK)
+        return st;
+    if (n_rows < 0 || n_rows > kMaxRows)
+        return MLA8_E_INVAL;
+    if (n_rows == 0)
+        return MLA8_OK;
+    if (!x || !codes || !scales || !aligned16(x) || !aligned16(codes) ||
+        (reinterpret_cast<uintptr_t>(scales) & 3u))
+        return MLA8_E_INVAL;
+    return launch_quantize(x, n_rows, lc + rc, codes, scales, static_cast<hipStream_t>(stream)) ==
+                   hipSuccess
+               ? MLA8_OK
+               : MLA8_E_HIP;
+}
+
+int mla8_append(uint8_t* kv_codes, float* kv_scales, int64_t cap_rows, int64_t* t_rows,
+                const float* x, int64_t n_rows, int32_t lc, int32_t rc, void* stream)
+{
+    int st = check_shape(lc, rc);
+    if (st != MLA8_OK)
+        return st;
+    if (!kv_codes || !kv_scales || !t_rows || !x)
+        return MLA8_E_INVAL;
+    if (cap_rows <= 0 || cap_rows > kMaxRows || n_rows < 0 || *t_rows < 0 || *t_rows > cap_rows)
+        return MLA8_E_INVAL;
+    if (!aligned16(kv_codes) || !aligned16(x) || (reinterpret_cast<uintptr_t>(kv_scales) & 3u))
+        return MLA8_E_INVAL;
+    if (n_rows > cap_rows - *t_rows)
+        return MLA8_E_CAPACITY;
+    if (n_rows == 0)
+        return MLA8_OK;
+    const int64_t d = lc + rc;
+    const hipError_t e = launch_quantize(x, n_rows, (int32_t)d, kv_codes + *t_rows * d,
+                                         kv_scales + *t_rows, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess)
+        return MLA8_E_HIP;
+    *t_rows += n_rows;
+    return MLA8_OK;
+}
+
+static int check_decode_common(const uint8_t* codes, const float* scales, int64_t t_rows,
+                               int32_t lc, int32_t rc, const float* q_lat, const float* q_rope,
+                               int32_t n_heads, float sm_scale, const float* out)
+{
+    int st = check_shape(lc, rc);
+    if (st != MLA8_OK)
+        return st;
+    if (!codes || !scales || !q_lat || !out || (rc > 0 && !q_rope))
+        return MLA8_E_INVAL;
+    if (t_rows <= 0 || t_rows > kMaxRows || n_heads <= 0 || !isfinite(sm_scale))
+        return MLA8_E_INVAL;
+    if (!aligned16(codes) || !aligned16(q_lat) || (rc > 0 && !aligned16(q_rope)) ||
+        !aligned16(out) || (reinterpret_cast<uintptr_t>(scales) & 3u))
+        return MLA8_E_INVAL;
+    return MLA8_OK;
+}
+
+int mla8_decode(const uint8_t* kv_codes, const float* kv_scales, int64_t t_rows, int32_t lc,
+                int32_t rc, const float* q_lat, const float* q_rope, int32_t n_heads,
+                float sm_scale, float* out, float* lse, void* workspace, size_t ws_bytes,
+                void* stream)
+{
+    int st = check_decode_common(kv_codes, kv_scales, t_rows, lc, rc, q_lat, q_rope, n_heads,
+                                 sm_scale, out);
+    if (st != MLA8_OK)
+        return st;
+    return run_attention(MLA8_OP_DECODE, kv_codes, kv_scales, t_rows, lc, rc, nullptr, t_rows,
+                         q_lat, q_rope, n_heads, n_heads, 0, sm_scale, out, lse, workspace,
+                         ws_bytes, stream);
+}
+
+int mla8_decode_sel(const uint8_t* kv_codes, const float* kv_scales, int64_t t_rows, int32_t lc,
+                    int32_t rc, const int32_t* sel, int64_t ns, const float* q_lat,
+                    const float* q_rope, int32_t n_heads, float sm_scale, float* out, float* lse,
+                    void* workspace, size_t ws_bytes, void* stream)
+{
+    int st = check_decode_common(kv_codes, kv_scales, t_rows, lc, rc, q_lat, q_rope, n_heads,
+                                 sm_scale, out);
+    if (st != MLA8_OK)
+        return st;
+    if (!sel || ns <= 0 || ns > kMaxRows || (reinterpret_cast<uintptr_t>(sel) & 3u))
+        return MLA8_E_INVAL;
+    return run_attention(MLA8_OP_DECODE_SEL, kv_codes, kv_scales, t_rows, lc, rc, sel, ns, q_lat,
+                         q_rope, n_heads, n_heads, 0, sm_scale, out, lse, workspace, ws_bytes,
+                         stream);
+}
+
+int mla8_batch(const uint8_t* kv_codes, const float* kv_scales, int64_t t_rows, int32_t lc,
+               int32_t rc, const float* q_lat, const float* q_rope, int32_t n_q, int64_t pos0,
+               int32_t n_heads, float sm_scale, float* out, float* lse, void* workspace,
+               size_t ws_bytes, void* stream)
+{
+    int st = check_decode_common(kv_codes, kv_scales, t_rows, lc, rc, q_lat, q_rope, n_heads,
+                                 sm_scale, out);
+    if (st != MLA8_OK)
+        return st;
+    if (n_q <= 0 || pos0 < 0)
+        return MLA8_E_INVAL;
+    if ((int64_t)n_q * (int64_t)n_heads > kMaxRows / 1024)
+        return MLA8_E_UNSUPPORTED;
+    if (pos0 + n_q > t_rows)
+        return MLA8_E_RANGE;
+    return run_attention(MLA8_OP_BATCH, kv_codes, kv_scales, t_rows, lc, rc, nullptr, pos0 + n_q,
+                         q_lat, q_rope, n_q * n_heads, n_heads, pos0, sm_scale, out, lse,
+                         workspace, ws_bytes, stream);
+}
+
+size_t mla8_workspace_bytes(int32_t op, int64_t rows, int32_t n_heads, int32_t n_q, int32_t lc)
+{
+    if (op < MLA8_OP_DECODE || op > MLA8_OP_BATCH || rows <= 0 || rows > kMaxRows ||
+        n_heads <= 0 || lc <= 0)
+        return 0;
+    int64_t n_qh = n_heads;
+    if (op == MLA8_OP_BATCH) {
+        if (n_q <= 0)
+            return 0;
+        n_qh = (int64_t)n_q * n_heads;
+        if (n_qh > kMaxRows / 1024)
+            return 0;
+    }
+    return ws_bytes_for(make_plan(op, rows, (int32_t)n_qh), (int32_t)n_qh, lc);
+}
+
+int32_t mla8_force_splits(int32_t n_splits)
+{
+    const int32_t prev = g_forced_splits;
+    g_forced_splits = n_splits > 0 ? n_splits : 0;
+    return prev;
+}
+
+int32_t mla8_plan_splits(int32_t op, int64_t rows, int32_t n_heads, int32_t n_q)
+{
+    if (rows <= 0 || n_heads <= 0)
+        return 0;
+    const int64_t n_qh = op == MLA8_OP_BATCH ? (int64_t)n_q * n_heads : n_heads;
+    if (n_qh <= 0 || n_qh > kMaxRows / 1024)
+        return 0;
+    return make_plan(op, rows, (int32_t)n_qh).n_chunks;
+}
+
+const char* mla8_status_string(int status)
+{
+    switch (status) {
+    case MLA8_OK: return "ok";
+    case MLA8_E_INVAL: return "invalid argument (NULL pointer, bad size or misaligned buffer)";
+    case MLA8_E_RANGE: return "row range outside the shadow (pos0 + n_q > t_rows)";
+    case MLA8_E_CAPACITY: return "append would exceed cap_rows";
+    case MLA8_E_WORKSPACE: return "workspace smaller than mla8_workspace_bytes()";
+    case MLA8_E_UNSUPPORTED:
+        return "unsupported shape: need 16<=lc<=512, 0<=rc<=128, both multiples of 16, "
+               "lc+rc<=640";
+    case MLA8_E_HIP: return "HIP launch failed";
+    default: return "unknown status";
+    }
+}
+
+int mla8_profile_events(void* before, void* after)
+{
+    g_ev_before = static_cast<hipEvent_t>(before);
+    g_ev_after = static_cast<hipEvent_t>(after);
+    return MLA8_OK;
+}
+
+const char* mla8_version(void) { return "mla8 0.1.0 gfx950"; }
+
+int mla8_test_encode(const float* x, int64_t n, uint8_t* codes, void* stream)
+{
+    if (!x || !codes || n < 0)
+        return MLA8_E_INVAL;
+    if (n == 0)
+        return MLA8_OK;
+    return launch_test_encode(x, n, codes, static_cast<hipStream_t>(stream)) == hipSuccess
+               ? MLA8_OK
+               : MLA8_E_HIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,53 @@
+// Internal interface between the C-ABI layer (mla8_api.hip) and the kernels
+// (mla8_kernels.hip).  Not installed; the public interface is include/mla8.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mla8 {
+
+// Rows per tile streamed through LDS, query-heads per workgroup, threads per
+// workgroup of the split-T partial kernel.
+constexpr int kTileRows = 64;
+constexpr int kHeadsPerGroup = 32;
+constexpr int kThreads = 256;
+// Workgroups the automatic split plan aims for: one per compute unit of an
+// MI355X (256 CUs in 8 XCDs).
+constexpr int kTargetGroups = 256;
+
+enum RowMode : int32_t { kDense = 0, kSelect = 1, kCausal = 2 };
+
+// One launch of the split-T attention (partial kernel + merge kernel).
+struct AttnArgs {
+    const uint8_t* codes;   // shadow codes [t_rows][d]
+    const float* scales;    // shadow scales [t_rows]
+    int32_t t_rows;         // rows present in the shadow
+    const int32_t* sel;     // kSelect: absolute row indices [n_list]
+    int32_t n_list;         // length of the attended row list
+    const float* q_lat;     // [n_qh][lc]
+    const float* q_rope;    // [n_qh][rc]
+    int32_t lc, rc, d;
+    int32_t n_qh;           // query-heads: n_heads, or n_q * n_heads for kCausal
+    int32_t n_heads;        // heads per query position (kCausal)
+    int32_t pos0;           // kCausal: position of query 0
+    int32_t mode;           // RowMode
+    float sm_log2;          // sm_scale * log2(e)
+    int32_t n_chunks;       // row chunks (split-T partials)
+    int32_t chunk_rows;     // rows per chunk, a multiple of kTileRows
+    int32_t n_groups;       // head groups of kHeadsPerGroup
+    float* ws_m;            // [n_chunks][n_qh]  running max, log2 units
+    float* ws_z;            // [n_chunks][n_qh]  softmax normaliser
+    float* ws_cl;           // [n_chunks][n_qh][lc] unnormalised context
+    float* out;             // [n_qh][lc]
+    float* lse;             // [n_qh] or nullptr
+};
+
+hipError_t launch_quantize(const float* x, int64_t n_rows, int32_t d, uint8_t* codes,
+                           float* scales, hipStream_t stream);
+hipError_t launch_test_encode(const float* x, int64_t n, uint8_t* codes, hipStream_t stream);
+// ev_before / ev_after (may be null) are recorded around the partial kernel.
+hipError_t launch_attention(const AttnArgs& a, hipStream_t stream, hipEvent_t ev_before,
+                            hipEvent_t ev_after);
+
+}  // namespace mla8

@@ -1,0 +1,203 @@
+"""Thin Python binding over libmla8.so (include/mla8.h), same names as the C ABI.
+
+Argument marshalling only: torch tensors supply device memory and the current
+HIP stream; every step of the computation runs in the library's kernels.  The
+library must be built (``python -m fp8_mla_latent_amd.build``); importing this
+module without it raises, there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmla8.so")
+
+MLA8_OK = 0
+MLA8_E_INVAL = -1
+MLA8_E_RANGE = -2
+MLA8_E_CAPACITY = -3
+MLA8_E_WORKSPACE = -4
+MLA8_E_UNSUPPORTED = -5
+MLA8_E_HIP = -6
+MLA8_OP_DECODE = 0
+MLA8_OP_DECODE_SEL = 1
+MLA8_OP_BATCH = 2
+
+EXPORTED = ("mla8_quantize_rows", "mla8_append", "mla8_decode", "mla8_decode_sel", "mla8_batch",
+            "mla8_workspace_bytes", "mla8_force_splits", "mla8_plan_splits",
+            "mla8_status_string", "mla8_version", "mla8_test_encode", "mla8_profile_events")
+
+
+class Mla8Error(RuntimeError):
+    def __init__(self, status: int, call: str):
+        self.status = status
+        super().__init__(f"{call}: status {status}: {mla8_status_string(status)}")
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(_LIB_PATH):
+        raise ImportError(f"libmla8.so not built at {_LIB_PATH}; run "
+                          "`python -m fp8_mla_latent_amd.build` (no fallback path exists)")
+    L = ctypes.CDLL(_LIB_PATH)
+    P, i64, i32, f32, sz = (ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_float,
+                            ctypes.c_size_t)
+    sig = {
+        "mla8_quantize_rows": (ctypes.c_int, [P, i64, i32, i32, P, P, P]),
+        "mla8_append": (ctypes.c_int, [P, P, i64, ctypes.POINTER(i64), P, i64, i32, i32, P]),
+        "mla8_decode": (ctypes.c_int, [P, P, i64, i32, i32, P, P, i32, f32, P, P, P, sz, P]),
+        "mla8_decode_sel": (ctypes.c_int,
+                            [P, P, i64, i32, i32, P, i64, P, P, i32, f32, P, P, P, sz, P]),
+        "mla8_batch": (ctypes.c_int,
+                       [P, P, i64, i32, i32, P, P, i32, i64, i32, f32, P, P, P, sz, P]),
+        "mla8_workspace_bytes": (sz, [i32, i64, i32, i32, i32]),
+        "mla8_force_splits": (i32, [i32]),
+        "mla8_plan_splits": (i32, [i32, i64, i32, i32]),
+        "mla8_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+        "mla8_version": (ctypes.c_char_p, []),
+        "mla8_test_encode": (ctypes.c_int, [P, i64, P, P]),
+        "mla8_profile_events": (ctypes.c_int, [P, P]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(L, name)
+        fn.restype = res
+        fn.argtypes = args
+    return L
+
+
+lib = _load()
+
+
+def _ptr(t: torch.Tensor | None) -> int | None:
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("mla8: tensors must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(t: torch.Tensor) -> int | None:
+    if t.is_cuda:
+        return torch.cuda.current_stream(t.device).cuda_stream
+    return None
+
+
+def _check(status: int, call: str) -> None:
+    if status != MLA8_OK:
+        raise Mla8Error(status, call)
+
+
+def mla8_status_string(status: int) -> str:
+    return lib.mla8_status_string(status).decode()
+
+
+def mla8_version() -> str:
+    return lib.mla8_version().decode()
+
+
+def mla8_workspace_bytes(op: int, rows: int, n_heads: int, n_q: int, lc: int) -> int:
+    return int(lib.mla8_workspace_bytes(op, rows, n_heads, n_q, lc))
+
+
+def mla8_force_splits(n_splits: int) -> int:
+    return int(lib.mla8_force_splits(n_splits))
+
+
+def mla8_plan_splits(op: int, rows: int, n_heads: int, n_q: int = 1) -> int:
+    return int(lib.mla8_plan_splits(op, rows, n_heads, n_q))
+
+
+def _workspace(op, rows, n_heads, n_q, lc, device, workspace):
+    need = mla8_workspace_bytes(op, rows, n_heads, n_q, lc)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=device)
+    return workspace
+
+
+def mla8_quantize_rows(x: torch.Tensor, lc: int, rc: int, codes: torch.Tensor | None = None,
+                       scales: torch.Tensor | None = None):
+    """f32 rows [n, lc+rc] -> (uint8 codes [n, lc+rc], f32 scales [n])."""
+    n = x.shape[0]
+    if codes is None:
+        codes = torch.empty((n, lc + rc), dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty((n,), dtype=torch.float32, device=x.device)
+    _check(lib.mla8_quantize_rows(_ptr(x), n, lc, rc, _ptr(codes), _ptr(scales), _stream(x)),
+           "mla8_quantize_rows")
+    return codes, scales
+
+
+def mla8_append(kv_codes: torch.Tensor, kv_scales: torch.Tensor, t_rows: int, x: torch.Tensor,
+                lc: int, rc: int) -> int:
+    """Quantize rows x into the shadow at [t_rows, t_rows + n); returns the new t_rows."""
+    t = ctypes.c_int64(t_rows)
+    _check(lib.mla8_append(_ptr(kv_codes), _ptr(kv_scales), kv_codes.shape[0], ctypes.byref(t),
+                           _ptr(x), x.shape[0], lc, rc, _stream(x)), "mla8_append")
+    return int(t.value)
+
+
+def mla8_decode(kv_codes, kv_scales, t_rows: int, lc: int, rc: int, q_lat, q_rope,
+                sm_scale: float, out=None, lse=None, workspace=None, want_lse: bool = True):
+    """Dense decode over shadow rows [0, t_rows): returns (out [H, lc], lse [H] or None)."""
+    h = q_lat.shape[0]
+    dev = q_lat.device
+    if out is None:
+        out = torch.empty((h, lc), dtype=torch.float32, device=dev)
+    if lse is None and want_lse:
+        lse = torch.empty((h,), dtype=torch.float32, device=dev)
+    ws = _workspace(MLA8_OP_DECODE, t_rows, h, 1, lc, dev, workspace)
+    _check(lib.mla8_decode(_ptr(kv_codes), _ptr(kv_scales), t_rows, lc, rc, _ptr(q_lat),
+                           _ptr(q_rope), h, float(sm_scale), _ptr(out), _ptr(lse), _ptr(ws),
+                           ws.numel(), _stream(q_lat)), "mla8_decode")
+    return out, lse
+
+
+def mla8_decode_sel(kv_codes, kv_scales, t_rows: int, lc: int, rc: int, sel, q_lat, q_rope,
+                    sm_scale: float, out=None, lse=None, workspace=None, want_lse: bool = True):
+    """Decode over the selected absolute rows sel [ns] (int32)."""
+    h = q_lat.shape[0]
+    dev = q_lat.device
+    ns = sel.numel()
+    if out is None:
+        out = torch.empty((h, lc), dtype=torch.float32, device=dev)
+    if lse is None and want_lse:
+        lse = torch.empty((h,), dtype=torch.float32, device=dev)
+    ws = _workspace(MLA8_OP_DECODE_SEL, ns, h, 1, lc, dev, workspace)
+    _check(lib.mla8_decode_sel(_ptr(kv_codes), _ptr(kv_scales), t_rows, lc, rc, _ptr(sel), ns,
+                               _ptr(q_lat), _ptr(q_rope), h, float(sm_scale), _ptr(out),
+                               _ptr(lse), _ptr(ws), ws.numel(), _stream(q_lat)),
+           "mla8_decode_sel")
+    return out, lse
+
+
+def mla8_batch(kv_codes, kv_scales, t_rows: int, lc: int, rc: int, q_lat, q_rope, pos0: int,
+               sm_scale: float, out=None, lse=None, workspace=None, want_lse: bool = True):
+    """Causal batch: q [S, H, *]; query s attends rows [0, pos0 + s]."""
+    n_q, h = q_lat.shape[0], q_lat.shape[1]
+    dev = q_lat.device
+    if out is None:
+        out = torch.empty((n_q, h, lc), dtype=torch.float32, device=dev)
+    if lse is None and want_lse:
+        lse = torch.empty((n_q, h), dtype=torch.float32, device=dev)
+    ws = _workspace(MLA8_OP_BATCH, pos0 + n_q, h, n_q, lc, dev, workspace)
+    _check(lib.mla8_batch(_ptr(kv_codes), _ptr(kv_scales), t_rows, lc, rc, _ptr(q_lat),
+                          _ptr(q_rope), n_q, pos0, h, float(sm_scale), _ptr(out), _ptr(lse),
+                          _ptr(ws), ws.numel(), _stream(q_lat)), "mla8_batch")
+    return out, lse
+
+
+def mla8_profile_events(before: "torch.cuda.Event | None", after: "torch.cuda.Event | None"):
+    """Record `before`/`after` around the split-T partial kernel of the next
+    attention calls (None, None clears).  The events must already exist."""
+    def raw(ev):
+        return None if ev is None else ev.cuda_event
+    _check(lib.mla8_profile_events(raw(before), raw(after)), "mla8_profile_events")
+
+
+def mla8_test_encode(x: torch.Tensor, codes: torch.Tensor | None = None) -> torch.Tensor:
+    """Device e4m3 encoder applied elementwise (test hook, not product API)."""
+    if codes is None:
+        codes = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
+    _check(lib.mla8_test_encode(_ptr(x), x.numel(), _ptr(codes), _stream(x)), "mla8_test_encode")
+    return codes

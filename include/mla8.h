@@ -1,0 +1,193 @@
+/*
+ * mla8 -- absorbed MLA decode attention over an fp8-e4m3 latent KV cache, for
+ * AMD Instinct MI355X (gfx950).  C ABI.
+ *
+ * Sources, cited by page and passage:
+ *   [KV8-base]  colibri PR #300 "KV8 long-context CUDA: fp8 device shadow,
+ *               split-T kernels, DSA-aware gather", first commit message
+ *               ("KV8 base"): the c/kv_fp8.h bullet (RNE encoder saturating at
+ *               +/-448, signed zero kept, NaN stored as 0; per-row quantizer
+ *               with a subnormal-amax guard) and the attention_rows bullet
+ *               (the producer quantizes the fresh row; the latent row is both
+ *               key and value; the row scale is hoisted out of the dot).
+ *   [KV8-long]  same page, second commit message ("KV8 long-context CUDA") and
+ *               the PR description: the kv_dev_sync8 device shadow that only
+ *               receives new rows, split-T partial blocks (cl[K], m, z) with a
+ *               log-sum-exp merge kernel, the batch path, and the DSA gather
+ *               kernel over absolute row indices.
+ *   [B1-FMHA]   "B1 Mixed FP8/BF16 FMHA first pass" (nvfp4-megamoe-kernel
+ *               docs): a C-ABI launcher under a thin Python bridge that refuses
+ *               unsupported shapes loudly instead of falling back.
+ *
+ * Conventions for every call:
+ *   - Pointers are DEVICE pointers unless marked [host].  `stream` is a
+ *     hipStream_t passed as void* (NULL = the default stream).
+ *   - Calls only enqueue work on `stream` and return; nothing synchronizes.
+ *     Buffers must stay alive until the stream work has finished.
+ *   - The caller owns every buffer.  The library never allocates device memory:
+ *     scratch space comes in through `workspace` (size from
+ *     mla8_workspace_bytes).
+ *   - All scalar arguments are checked on the host before any HIP call; a
+ *     failed check returns a negative status and enqueues nothing.  Device
+ *     contents are not inspected.
+ *   - Shadow layout ("latent row"): codes[row][Lc + Rc] uint8 e4m3 bytes, the
+ *     Lc kv_lora part first, then the Rc rope part; scales[row] float32, one per
+ *     row, equal to amax/448 of the f32 row it came from.
+ *   - Supported shapes: 16 <= Lc <= 512, 0 <= Rc <= 128, both multiples of 16,
+ *     Lc + Rc <= 640.  Other shapes return MLA8_E_UNSUPPORTED.
+ *   - Row counts and indices are below 2^31.
+ *   - Pointers must be 16-byte aligned (torch allocations are).
+ */
+#ifndef MLA8_H
+#define MLA8_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+/* Exported symbols are marked explicitly; the library is built with
+ * -fvisibility=hidden. */
+#define MLA8_API __attribute__((visibility("default")))
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+    MLA8_OK = 0,
+    MLA8_E_INVAL = -1,       /* NULL pointer, non-positive size, misalignment */
+    MLA8_E_RANGE = -2,       /* a row range outside the shadow (batch, decode) */
+    MLA8_E_CAPACITY = -3,    /* append beyond cap_rows; *t_rows left unchanged */
+    MLA8_E_WORKSPACE = -4,   /* workspace smaller than mla8_workspace_bytes() */
+    MLA8_E_UNSUPPORTED = -5, /* shape outside the supported set (see above) */
+    MLA8_E_HIP = -6          /* a HIP launch or device query failed */
+};
+
+/* Operation codes for mla8_workspace_bytes. */
+enum { MLA8_OP_DECODE = 0, MLA8_OP_DECODE_SEL = 1, MLA8_OP_BATCH = 2 };
+
+/*
+ * Quantize n_rows f32 rows x[n_rows][lc + rc] into e4m3 codes[n_rows][lc + rc]
+ * and f32 scales[n_rows]  [KV8-base, c/kv_fp8.h bullet]:
+ *   amax  = max |x_i| over the row's finite entries (NaN and +/-inf excluded);
+ *   scale = f32(amax / 448)            -- stored;
+ *   inv   = f32(448 / amax), or 0 when that is not finite (the guard: amax = 0
+ *           or so small that 448/amax overflows);
+ *   code_i = enc(f32(x_i * inv)), enc = round-to-nearest-even onto OCP e4m3
+ *           (E4M3FN), saturating to +/-448 (0x7E/0xFE), sign of zero kept,
+ *           NaN -> 0x00.
+ * Bytes and scales are bit-exact with that definition.  n_rows == 0 is a no-op.
+ * Errors: E_INVAL (NULL pointer, n_rows < 0), E_UNSUPPORTED (shape), E_HIP.
+ */
+MLA8_API int mla8_quantize_rows(const float* x, int64_t n_rows, int32_t lc, int32_t rc, uint8_t* codes,
+                       float* scales, void* stream);
+
+/*
+ * Quantize n_rows fresh f32 rows into the device-resident shadow at rows
+ * [*t_rows, *t_rows + n_rows), then advance *t_rows by n_rows
+ * [KV8-base, attention_rows bullet: the producer quantizes the fresh row;
+ *  KV8-long, kv_dev_sync8 bullet: the shadow only receives the new rows].
+ * kv_codes[cap_rows][lc + rc] and kv_scales[cap_rows] are caller-owned.
+ * t_rows is a [host] pointer.  Same arithmetic as mla8_quantize_rows.
+ * Errors: E_INVAL, E_UNSUPPORTED, E_CAPACITY (*t_rows + n_rows > cap_rows;
+ * nothing enqueued, *t_rows unchanged), E_HIP (*t_rows unchanged).
+ */
+MLA8_API int mla8_append(uint8_t* kv_codes, float* kv_scales, int64_t cap_rows, int64_t* t_rows,
+                const float* x, int64_t n_rows, int32_t lc, int32_t rc, void* stream);
+
+/*
+ * Dense absorbed decode of n_heads query heads over shadow rows [0, t_rows)
+ * [KV8-long, split-T bullet; KV8-base, attention_rows bullet].  Per head h with
+ * q = q_lat[h] || q_rope[h] and k_t = dec(codes[t]) * scales[t]:
+ *   s_t = sm_scale * (q . k_t);  p = softmax_t(s)  (natural exponential);
+ *   out[h][k] = sum_t p_t k_t[k]  for k < lc;  lse[h] = ln sum_t e^{s_t}.
+ * Computed split-T: row chunks yield (m, z, cl[lc]) partials in `workspace`,
+ * then a log-sum-exp merge writes out.
+ *   q_lat[n_heads][lc], q_rope[n_heads][rc]: f32.  out[n_heads][lc]: f32.
+ *   lse[n_heads]: f32, or NULL to skip.
+ * Errors: E_INVAL (NULL, t_rows <= 0, n_heads <= 0, non-finite sm_scale),
+ * E_UNSUPPORTED, E_WORKSPACE (ws_bytes < mla8_workspace_bytes(MLA8_OP_DECODE,
+ * t_rows, n_heads, 1, lc)), E_HIP.
+ */
+MLA8_API int mla8_decode(const uint8_t* kv_codes, const float* kv_scales, int64_t t_rows, int32_t lc,
+                int32_t rc, const float* q_lat, const float* q_rope, int32_t n_heads,
+                float sm_scale, float* out, float* lse, void* workspace, size_t ws_bytes,
+                void* stream);
+
+/*
+ * Selected-row (DSA gather) decode [KV8-long, DSA bullet]: as mla8_decode, but
+ * each head attends only the rows listed in sel[0..ns), absolute indices into
+ * the shadow read straight from it.  sel is a multiset (repeats count as often
+ * as they appear); entries outside [0, t_rows) are skipped.  If no entry is in
+ * range, out is all zeros and lse is -inf.  No cap on ns beyond 2^31.
+ * Errors: as mla8_decode, plus E_INVAL for ns <= 0; workspace from
+ * mla8_workspace_bytes(MLA8_OP_DECODE_SEL, ns, n_heads, 1, lc).
+ */
+MLA8_API int mla8_decode_sel(const uint8_t* kv_codes, const float* kv_scales, int64_t t_rows, int32_t lc,
+                    int32_t rc, const int32_t* sel, int64_t ns, const float* q_lat,
+                    const float* q_rope, int32_t n_heads, float sm_scale, float* out, float* lse,
+                    void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * Batched causal attention [KV8-long: the batch/prefill path over the cached
+ * rows, one (query, head) pair per work unit]: query s in [0, n_q) sits at
+ * absolute position pos0 + s and attends rows [0, pos0 + s] (its own row
+ * included), with the same per-head arithmetic as mla8_decode.
+ *   q_lat[n_q][n_heads][lc], q_rope[n_q][n_heads][rc]: f32.
+ *   out[n_q][n_heads][lc]: f32.  lse[n_q][n_heads] or NULL.
+ * Errors: E_INVAL (NULL, n_q <= 0, pos0 < 0, ...), E_RANGE (pos0 + n_q >
+ * t_rows), E_UNSUPPORTED, E_WORKSPACE (see mla8_workspace_bytes(MLA8_OP_BATCH,
+ * pos0 + n_q, n_heads, n_q, lc)), E_HIP.
+ */
+MLA8_API int mla8_batch(const uint8_t* kv_codes, const float* kv_scales, int64_t t_rows, int32_t lc,
+               int32_t rc, const float* q_lat, const float* q_rope, int32_t n_q, int64_t pos0,
+               int32_t n_heads, float sm_scale, float* out, float* lse, void* workspace,
+               size_t ws_bytes, void* stream);
+
+/*
+ * Workspace bytes the given call needs on the current device.  `rows` is the
+ * number of rows the call attends: t_rows for MLA8_OP_DECODE, ns for
+ * MLA8_OP_DECODE_SEL, pos0 + n_q for MLA8_OP_BATCH.  n_q is ignored except for
+ * MLA8_OP_BATCH.  Returns 0 for invalid arguments.
+ */
+MLA8_API size_t mla8_workspace_bytes(int32_t op, int64_t rows, int32_t n_heads, int32_t n_q, int32_t lc);
+
+/*
+ * Tuning / testing control: force the number of row chunks (split-T
+ * partials) that subsequent decode calls in this process use; 0 restores the
+ * automatic choice.  The value is clamped to what the row count allows.  Not
+ * thread-safe with concurrent decode calls.  Returns the previous value.
+ */
+MLA8_API int32_t mla8_force_splits(int32_t n_splits);
+
+/* Number of row chunks the automatic (or forced) plan uses for a call. */
+MLA8_API int32_t mla8_plan_splits(int32_t op, int64_t rows, int32_t n_heads, int32_t n_q);
+
+/*
+ * Measurement hook: while set, every attention call (mla8_decode,
+ * mla8_decode_sel, mla8_batch) records the hipEvent_t `before` on its stream
+ * just before launching the split-T partial kernel and `after` just after it,
+ * so hipEventElapsedTime(before, after) is that kernel's duration.  Pass NULL,
+ * NULL to clear.  Events are caller-owned.  Not thread-safe.  Returns MLA8_OK.
+ */
+MLA8_API int mla8_profile_events(void* before, void* after);
+
+/* Human-readable text for a status code (static storage). */
+MLA8_API const char* mla8_status_string(int status);
+
+/* Library version string (static storage). */
+MLA8_API const char* mla8_version(void);
+
+/*
+ * Not part of the product API: apply the device e4m3 encoder elementwise,
+ * codes[i] = enc(x[i]) for i < n, with no scaling.  Exported so that tests can
+ * compare the device encoder with the reference on every f32 bit pattern,
+ * including finite |x| > 448 which the quantizer never produces.
+ * Errors: E_INVAL, E_HIP.
+ */
+MLA8_API int mla8_test_encode(const float* x, int64_t n, uint8_t* codes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MLA8_H */

@@ -1,0 +1,333 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 CPU oracle.
+
+Quantization is compared bit for bit; attention within the per-vector
+tolerance in tests/tolerance.py.  Inputs come from the seeded synthetic
+workloads (fp8_mla_latent_amd.workloads) and from edge-case constructions.
+"""
+from __future__ import annotations
+
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from fp8_mla_latent_amd import workloads as W
+from tests.encoder_set import encoder_values
+from tests.tolerance import check_attention
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+@pytest.fixture(scope="module")
+def m():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from fp8_mla_latent_amd import mla8
+    return mla8
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+
+
+def host(t):
+    torch.cuda.synchronize()
+    return t.cpu().numpy()
+
+
+# ------------------------------------------------------------ quantization
+def _edge_rows(d):
+    g = np.random.Generator(np.random.PCG64(21))
+    rows = [g.standard_normal(d).astype(np.float32) for _ in range(16)]
+    rows += [(g.standard_normal(d) * 1e-30).astype(np.float32),
+             (g.standard_normal(d) * 1e30).astype(np.float32)]
+    r = g.standard_normal(d).astype(np.float32)
+    r[[3, 9]] = np.inf
+    r[7] = -np.inf
+    r[[11, 2]] = np.nan
+    r[13] = -np.nan
+    rows.append(r)
+    rows.append(np.zeros(d, np.float32))
+    z = np.zeros(d, np.float32)
+    z[::3] = -0.0
+    rows.append(z)
+    f32max = np.finfo(np.float32).max
+    b = np.float32(448) / f32max
+    for amax in (1e-40, 1e-37, np.finfo(np.float32).tiny, np.nextafter(b, np.float32(0)), b,
+                 np.nextafter(b, np.float32(1)), 1.4e-36, 3e38):
+        t = (g.uniform(-1, 1, d) * amax).astype(np.float32)
+        t[5] = np.float32(amax)
+        rows.append(t)
+    enc = encoder_values()
+    # one row per 448-multiple: inv = 1 exactly, so codes = enc(x) for |x| <= 448
+    for i in range(0, enc.size, d - 1):
+        chunk = enc[i:i + d - 1]
+        row = np.zeros(d, np.float32)
+        row[:chunk.size] = np.where(np.isfinite(chunk) & (np.abs(chunk) > 448), 0, chunk)
+        row[-1] = 448.0
+        rows.append(row)
+    return np.stack(rows)
+
+
+@pytest.mark.parametrize("lc,rc", [(64, 16), (512, 64), (128, 0), (256, 32)])
+def test_quantize_edge_rows_bitexact(m, lc, rc):
+    x = _edge_rows(lc + rc)
+    say(f"quantize edge rows lc={lc} rc={rc} n={x.shape[0]}")
+    codes, scales = m.mla8_quantize_rows(dev(x), lc, rc)
+    oc, os_ = oracle.quantize_rows(x)
+    assert np.array_equal(host(codes), oc)
+    assert np.array_equal(host(scales).view(np.uint32), os_.view(np.uint32))
+
+
+@pytest.mark.parametrize("w", [W.TINY, W.DSV3], ids=lambda w: w.name)
+def test_quantize_workload_rows_bitexact(m, w):
+    x = W.rows(w, w.t_rows)
+    say(f"quantize {w.name} rows n={x.shape[0]}")
+    codes, scales = m.mla8_quantize_rows(dev(x), w.lc, w.rc)
+    oc, os_ = oracle.quantize_rows(x)
+    assert np.array_equal(host(codes), oc)
+    assert np.array_equal(host(scales).view(np.uint32), os_.view(np.uint32))
+
+
+def test_device_encoder_encoder_set(m):
+    v = encoder_values()
+    say("device encoder on the 4096-value encoder set")
+    got = host(m.mla8_test_encode(dev(v)))
+    assert np.array_equal(got, oracle.enc(v))
+
+
+@pytest.mark.slow
+def test_device_encoder_every_f32(m):
+    """All 2^32 f32 bit patterns, 2^28 at a time, device encoder vs oracle."""
+    chunk = 1 << 28
+    base = torch.arange(chunk, dtype=torch.int64, device=DEV)
+    out = torch.empty(chunk, dtype=torch.uint8, device=DEV)
+    for k in range(16):
+        say(f"device encoder sweep chunk {k}/16")
+        bits = (base + k * chunk).to(torch.int32)  # wraps into the upper half
+        x = bits.view(torch.float32)
+        m.mla8_test_encode(x, out)
+        got = host(out)
+        ref = oracle.enc(np.arange(k * chunk, (k + 1) * chunk, dtype=np.uint64)
+                         .astype(np.uint32).view(np.float32))
+        bad = np.flatnonzero(got != ref)
+        assert bad.size == 0, (k, hex(k * chunk + int(bad[0])), got[bad[0]], ref[bad[0]])
+
+
+def test_append_writes_rows_and_checks_capacity(m):
+    w = W.TINY
+    x = W.rows(w, 40)
+    cap = 32
+    codes = torch.zeros((cap, w.d), dtype=torch.uint8, device=DEV)
+    scales = torch.zeros((cap,), dtype=torch.float32, device=DEV)
+    say("append 5 + 20 rows, then overflow")
+    t = m.mla8_append(codes, scales, 0, dev(x[:5]), w.lc, w.rc)
+    assert t == 5
+    t = m.mla8_append(codes, scales, t, dev(x[5:25]), w.lc, w.rc)
+    assert t == 25
+    with pytest.raises(m.Mla8Error) as e:
+        m.mla8_append(codes, scales, t, dev(x[25:40]), w.lc, w.rc)
+    assert e.value.status == m.MLA8_E_CAPACITY
+    oc, os_ = oracle.quantize_rows(x[:25])
+    assert np.array_equal(host(codes)[:25], oc)
+    assert np.array_equal(host(scales)[:25].view(np.uint32), os_.view(np.uint32))
+    assert np.all(host(codes)[25:] == 0)
+
+
+# ------------------------------------------------------------ attention
+def _make_shadow(m, w, n, seed_offset=0):
+    x = W.rows(w, n, seed_offset=seed_offset)
+    oc, os_ = oracle.quantize_rows(x)
+    codes, scales = m.mla8_quantize_rows(dev(x), w.lc, w.rc)
+    assert np.array_equal(host(codes), oc) and np.array_equal(host(scales), os_)
+    return codes, scales, oc, os_
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+@pytest.mark.parametrize("w", [W.TINY, W.DSV3], ids=lambda w: w.name)
+def test_decode_workloads(m, w, seed):
+    say(f"decode {w.name} seed {seed}")
+    codes, scales, oc, os_ = _make_shadow(m, w, w.t_rows, seed)
+    ql, qr = W.queries(w, seed_offset=seed)
+    out, lse = m.mla8_decode(codes, scales, w.t_rows, w.lc, w.rc, dev(ql), dev(qr), w.sm_scale)
+    ro, rl = oracle.decode(oc, os_, w.t_rows, w.lc, w.rc, ql, qr, w.sm_scale)
+    check_attention(host(out), ro, host(lse), rl, f"{w.name} seed {seed}")
+
+
+SHAPES = [
+    # (H, lc, rc, T)
+    (1, 64, 16, 1), (4, 64, 16, 63), (4, 64, 16, 65), (5, 64, 16, 1000),
+    (17, 128, 0, 777), (33, 256, 32, 3001), (64, 512, 64, 2049), (128, 512, 64, 1),
+    (48, 512, 128, 4500), (3, 16, 16, 130), (64, 448, 64, 515),
+]
+
+
+@pytest.mark.parametrize("h,lc,rc,t", SHAPES, ids=lambda v: str(v))
+def test_decode_shapes(m, h, lc, rc, t):
+    say(f"decode shape H={h} lc={lc} rc={rc} T={t}")
+    g = np.random.Generator(np.random.PCG64(1000 + h + t))
+    x = (g.standard_normal((t, lc + rc)) * g.uniform(0.1, 10, (t, 1))).astype(np.float32)
+    ql = g.standard_normal((h, lc)).astype(np.float32)
+    qr = g.standard_normal((h, rc)).astype(np.float32)
+    sm = 1 / math.sqrt(lc / 4 + rc)
+    oc, os_ = oracle.quantize_rows(x)
+    out, lse = m.mla8_decode(dev(oc), dev(os_), t, lc, rc, dev(ql), dev(qr), sm)
+    ro, rl = oracle.decode(oc, os_, t, lc, rc, ql, qr, sm)
+    check_attention(host(out), ro, host(lse), rl, f"H={h} lc={lc} rc={rc} T={t}")
+
+
+@pytest.mark.parametrize("splits", [1, 3, 8, 16, 64])
+def test_decode_split_count_invariance(m, splits):
+    w = W.DSV3
+    say(f"decode split invariance P={splits}")
+    codes, scales, oc, os_ = _make_shadow(m, w, w.t_rows)
+    ql, qr = W.queries(w)
+    prev = m.mla8_force_splits(splits)
+    try:
+        out, lse = m.mla8_decode(codes, scales, w.t_rows, w.lc, w.rc, dev(ql), dev(qr),
+                                 w.sm_scale)
+        o = host(out)
+    finally:
+        m.mla8_force_splits(prev)
+    ro, rl = oracle.decode(oc, os_, w.t_rows, w.lc, w.rc, ql, qr, w.sm_scale)
+    check_attention(o, ro, host(lse), rl, f"P={splits}")
+
+
+def test_decode_degenerate_rows(m):
+    """Zero rows, guarded rows, huge and tiny scales mixed in one cache."""
+    lc, rc, t, h = 64, 16, 300, 6
+    g = np.random.Generator(np.random.PCG64(77))
+    x = g.standard_normal((t, lc + rc)).astype(np.float32)
+    x[10:20] = 0
+    x[30:35] *= 1e-37
+    x[40:45] *= 1e12
+    x[50:55] *= 1e-12
+    ql = g.standard_normal((h, lc)).astype(np.float32) * 1e-6
+    qr = g.standard_normal((h, rc)).astype(np.float32) * 1e-6
+    say("decode degenerate rows")
+    oc, os_ = oracle.quantize_rows(x)
+    out, lse = m.mla8_decode(dev(oc), dev(os_), t, lc, rc, dev(ql), dev(qr), 0.1)
+    ro, rl = oracle.decode(oc, os_, t, lc, rc, ql, qr, 0.1)
+    check_attention(host(out), ro, host(lse), rl, "degenerate rows")
+    # all-zero cache: uniform softmax over zero rows
+    z = np.zeros((70, lc + rc), np.float32)
+    oc, os_ = oracle.quantize_rows(z)
+    out, lse = m.mla8_decode(dev(oc), dev(os_), 70, lc, rc, dev(ql), dev(qr), 0.1)
+    assert np.all(host(out) == 0) and np.allclose(host(lse), math.log(70), atol=1e-5)
+
+
+def test_decode_sel_workload(m):
+    w = W.DSA
+    say(f"decode_sel {w.name}")
+    codes, scales, oc, os_ = _make_shadow(m, w, w.t_rows)
+    sel = W.selection(w)
+    ql, qr = W.queries(w)
+    out, lse = m.mla8_decode_sel(codes, scales, w.t_rows, w.lc, w.rc, dev(sel), dev(ql),
+                                 dev(qr), w.sm_scale)
+    ro, rl = oracle.decode_sel(oc, os_, w.t_rows, w.lc, w.rc, sel, ql, qr, w.sm_scale)
+    check_attention(host(out), ro, host(lse), rl, w.name)
+
+
+@pytest.mark.parametrize("case", ["dups", "out_of_range", "single", "all_rows", "none_valid",
+                                  "ragged"])
+def test_decode_sel_edges(m, case):
+    lc, rc, t, h = 512, 64, 1500, 20
+    g = np.random.Generator(np.random.PCG64(5))
+    x = g.standard_normal((t, lc + rc)).astype(np.float32)
+    ql = g.standard_normal((h, lc)).astype(np.float32)
+    qr = g.standard_normal((h, rc)).astype(np.float32)
+    sel = {
+        "dups": np.array([5, 5, 5, 900, 17, 900, 1499, 0] * 9, np.int32),
+        "out_of_range": np.array([-1, 3, 1500, 77, 1 << 30, -5, 1200, 2 ** 31 - 1], np.int32),
+        "single": np.array([1234], np.int32),
+        "all_rows": np.arange(t, dtype=np.int32),
+        "none_valid": np.array([-3, 1500, 99999], np.int32),
+        "ragged": np.sort(g.choice(t, 131, replace=False)).astype(np.int32),
+    }[case]
+    say(f"decode_sel edge {case} ns={sel.size}")
+    oc, os_ = oracle.quantize_rows(x)
+    sm = 1 / math.sqrt(192)
+    out, lse = m.mla8_decode_sel(dev(oc), dev(os_), t, lc, rc, dev(sel), dev(ql), dev(qr), sm)
+    ro, rl = oracle.decode_sel(oc, os_, t, lc, rc, sel, ql, qr, sm)
+    if case == "none_valid":
+        assert np.all(host(out) == 0) and np.all(np.isneginf(host(lse)))
+    else:
+        check_attention(host(out), ro, host(lse), rl, case)
+
+
+@pytest.mark.parametrize("h,n_q,t,lc,rc", [(3, 7, 300, 64, 16), (64, 5, 200, 512, 64),
+                                           (2, 40, 2000, 128, 64), (33, 2, 70, 64, 16)],
+                         ids=lambda v: str(v))
+def test_batch_small(m, h, n_q, t, lc, rc):
+    say(f"batch H={h} S={n_q} T={t}")
+    g = np.random.Generator(np.random.PCG64(h * 100 + n_q))
+    x = g.standard_normal((t, lc + rc)).astype(np.float32)
+    ql = g.standard_normal((n_q, h, lc)).astype(np.float32)
+    qr = g.standard_normal((n_q, h, rc)).astype(np.float32)
+    sm = 1 / math.sqrt(192)
+    pos0 = t - n_q
+    oc, os_ = oracle.quantize_rows(x)
+    out, lse = m.mla8_batch(dev(oc), dev(os_), t, lc, rc, dev(ql), dev(qr), pos0, sm)
+    ro, rl = oracle.batch(oc, os_, t, lc, rc, ql, qr, pos0, sm)
+    check_attention(host(out), ro, host(lse), rl, f"batch H={h} S={n_q}")
+
+
+def test_batch_workload_sampled(m):
+    """Full-size causal batch (S=64, H=64, T=32768, 64 fresh rows appended
+    through the quantizer first), checked on sampled (query, head) pairs."""
+    w = W.BATCH
+    base = w.t_rows - w.n_append
+    say(f"batch {w.name}: build shadow")
+    x = W.rows(w, w.t_rows)
+    codes = torch.zeros((w.t_rows, w.d), dtype=torch.uint8, device=DEV)
+    scales = torch.zeros((w.t_rows,), dtype=torch.float32, device=DEV)
+    t = m.mla8_append(codes, scales, 0, dev(x[:base]), w.lc, w.rc)
+    t = m.mla8_append(codes, scales, t, dev(x[base:]), w.lc, w.rc)
+    assert t == w.t_rows
+    oc, os_ = oracle.quantize_rows(x)
+    assert np.array_equal(host(codes), oc)
+    ql, qr = W.queries(w)
+    say(f"batch {w.name}: attend")
+    out, lse = m.mla8_batch(codes, scales, t, w.lc, w.rc, dev(ql), dev(qr), base, w.sm_scale)
+    o, l = host(out), host(lse)
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(l))
+    for s in (0, 1, 31, 63):
+        heads = np.array([0, 17, 42, 63])
+        ro, rl = oracle.decode(oc, os_, base + s + 1, w.lc, w.rc, ql[s, heads], qr[s, heads],
+                               w.sm_scale)
+        check_attention(o[s, heads], ro, l[s, heads], rl, f"batch s={s}")
+
+
+def test_long_context_sampled(m):
+    """The long-context decode step at full size: 262143 quantized rows, one
+    fresh row appended through the quantizer, then all 262144 rows attended by
+    64 heads; sampled heads against the oracle, every head for sanity."""
+    w = W.LONG
+    say(f"{w.name}: build shadow")
+    x = W.rows(w, w.t_rows)
+    codes = torch.zeros((w.t_rows, w.d), dtype=torch.uint8, device=DEV)
+    scales = torch.zeros((w.t_rows,), dtype=torch.float32, device=DEV)
+    t = m.mla8_append(codes, scales, 0, dev(x[:-1]), w.lc, w.rc)
+    t = m.mla8_append(codes, scales, t, dev(x[-1:]), w.lc, w.rc)
+    assert t == w.t_rows
+    oc, os_ = oracle.quantize_rows(x)
+    assert np.array_equal(host(codes), oc)
+    assert np.array_equal(host(scales).view(np.uint32), os_.view(np.uint32))
+    ql, qr = W.queries(w)
+    say(f"{w.name}: decode")
+    out, lse = m.mla8_decode(codes, scales, t, w.lc, w.rc, dev(ql), dev(qr), w.sm_scale)
+    o, l = host(out), host(lse)
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(l))
+    heads = np.array([0, 21, 63])
+    ro, rl = oracle.decode(oc, os_, t, w.lc, w.rc, ql[heads], qr[heads], w.sm_scale)
+    check_attention(o[heads], ro, l[heads], rl, w.name)
