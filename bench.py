@@ -51,6 +51,8 @@ def parse():
                     help="heads of the CPU-oracle sample (full T, scaled to 64 heads)")
     ap.add_argument("--traffic", type=str, default=None,
                     help="JSON file with rocprofv3 FETCH/WRITE bytes per partial launch")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain 1 GiB device copy (counter calibration) and exit")
     return ap.parse_args()
 
 
@@ -90,6 +92,19 @@ def main():
 
     import numpy as np
     import torch
+
+    if args.calibrate_copy:
+        # A plain copy of known size: 1 GiB read + 1 GiB written per launch.
+        # rocprofv3 FETCH_SIZE / WRITE_SIZE of this kernel calibrate the same
+        # counters taken on the attention kernels.
+        n = 1 << 30
+        src = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(max(args.steps, 1)):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes": n, "launches": max(args.steps, 1)}))
+        return
 
     from fp8_mla_latent_amd import mla8 as m
     from fp8_mla_latent_amd import workloads as W
@@ -162,6 +177,10 @@ def main():
     n_ev = K * L
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(n_ev)]
+    for a_, b_ in evs:  # torch creates the hipEvent on first record
+        a_.record()
+        b_.record()
+    torch.cuda.synchronize()
     i = 0
     try:
         for _ in range(K):

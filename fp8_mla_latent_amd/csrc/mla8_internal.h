@@ -11,7 +11,7 @@ namespace mla8 {
 // workgroup of the split-T partial kernel.
 constexpr int kTileRows = 64;
 constexpr int kHeadsPerGroup = 32;
-constexpr int kThreads = 256;
+constexpr int kThreads = 512;
 // Workgroups the automatic split plan aims for: one per compute unit of an
 // MI355X (256 CUs in 8 XCDs).
 constexpr int kTargetGroups = 256;

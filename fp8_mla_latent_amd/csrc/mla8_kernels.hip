@@ -18,15 +18,17 @@
 //   * Rows are staged through LDS in 64-row tiles.  e4m3 bytes are widened to
 //     fp16 in registers with v_cvt_scalef32_pk_f16_fp8 (exact: every e4m3 value
 //     is an fp16 normal), then fed to v_mfma_f32_16x16x32_f16.
-//   * Scores S^T[row][head] = X . Q^T: each wave takes 16 rows x 32 heads; q is
-//     resident in registers as an fp16 hi/lo pair (two MFMA passes), scaled by
-//     a power of two per head so it sits in fp16's range.
-//   * Context O[head][col] += W . X: each wave owns a 128-column slice, reading
-//     an 8x8 byte block per lane and transposing it with v_perm_b32 so the row
-//     (contraction) index becomes the per-lane MFMA K index.
+//   * 8 waves per workgroup (two per SIMD).  Scores S^T[row][head] = X . Q^T:
+//     each wave takes 16 rows x 16 heads; q is resident in registers as an fp16
+//     high part (fp16 MFMA) plus an e4m3 low part (scaled fp8 MFMA on the raw
+//     row bytes), with a power of two per head so it sits in fp16's range.
+//   * Context O[head][col] += W . X: each wave owns a 64-column slice for all
+//     32 heads, reading a 4x8 byte block per lane and transposing it with
+//     v_perm_b32 so the row (contraction) index becomes the MFMA K index.
 //   * The row scale is hoisted: scores are (q . code) * scale_t, and the PV
-//     weight of row t is exp2(u_t + log2 scale_t - mo) with its own running max
-//     mo, so fp16 weights never overflow or lose significant rows.
+//     weight of row t is exp2((u_t - m) + log2 scale_t - d) with d a running
+//     max kept relative to the score max m, so fp16 weights never overflow or
+//     lose significant rows, and large scores never swallow log2 scale_t.
 //   * Online softmax with a lazy running max: the max is only moved when a
 //     tile beats it by more than 2^8, which keeps rescaling of the register
 //     accumulators off the common path.
@@ -147,20 +149,112 @@ __device__ __forceinline__ f32x4 mfma_fp8_scaled(v8i a, v8i b, f32x4 c, int32_t 
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Source of the 16 query elements d = 64j + 16g .. +16 of query-head qh (or
+// nullptr past the row width / past the last head).
+__device__ __forceinline__ const float* q_src(const AttnArgs& a, int qh, bool hv, int j, int g)
+{
+    const int d0 = 64 * j + 16 * g;
+    if (hv && d0 < a.lc)
+        return a.q_lat + (size_t)qh * a.lc + d0;
+    if (hv && d0 < a.d)
+        return a.q_rope + (size_t)qh * a.rc + (d0 - a.lc);
+    return nullptr;
+}
+
+__device__ __forceinline__ float4 ld4(const float* p, int k)
+{
+    return p ? reinterpret_cast<const float4*>(p)[k] : make_float4(0.f, 0.f, 0.f, 0.f);
+}
+
+// Query registers for 16 heads.  Lane (n, g) holds, for head qh_base + n, the
+// elements d = 64j + 16g + e (e < 16).  The same assignment of the contraction
+// index to (lane group, operand slot) is used for the row operand, so the MFMA
+// sums the right products whatever its K labels are.
+//   qhi: fp16(q * 2^k)                 two f16x8 per j      -> fp16 MFMA
+//   qlo: e4m3((q*2^k - qhi) * 2^6)     32 bytes per j pair  -> fp8 MFMA, whose
+//        E8M0 operand scale 2^-6 undoes the 2^6 inside the instruction.
+// k puts the head's largest |q| in [2^13, 2^14), where the fp16 spacing is 8,
+// so every residual is at most 4 and 2^6 * 4 = 256 sits inside e4m3's range.
+// Every index is a compile-time constant so the arrays stay in registers.
+constexpr int kQloShift = 6;
+
+template <int NKB>
+__device__ __forceinline__ void load_query(const AttnArgs& a, int qh_base, int n, int g,
+                                           f16x8 (&qhi)[NKB][2], v8i (&qlo)[(NKB + 1) / 2],
+                                           float& hfac, int32_t& tlim)
+{
+    const int qh = qh_base + n;
+    const bool hv = qh < a.n_qh;
+    float amax = 0.0f;
+#pragma unroll
+    for (int j = 0; j < NKB; ++j) {
+        const float* src = q_src(a, qh, hv, j, g);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const float4 v = ld4(src, k);
+            amax = fmaxf(amax, fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
+        }
+    }
+    amax = fmaxf(amax, __shfl_xor(amax, 16));
+    amax = fmaxf(amax, __shfl_xor(amax, 32));
+    int ex = 0;
+    if (amax > 0.0f)
+        (void)frexpf(amax, &ex);
+    // amax * 2^k2 in [2^13, 2^14); clamped so 2^k2 and 2^-k2 stay normal
+    const int k2 = min(max(14 - ex, -126), 126);
+    const float mult = ldexpf(1.0f, k2);
+    const float lmult = (float)(1 << kQloShift);
+    hfac = a.sm_log2 * ldexpf(1.0f, -k2);
+    tlim = (a.mode == kCausal) ? a.pos0 + (hv ? qh / a.n_heads : 0) + 1 : 0x7FFFFFFF;
+#pragma unroll
+    for (int j = 0; j < NKB; ++j) {
+        const float* src = q_src(a, qh, hv, j, g);
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+            const float4 v0 = ld4(src, 2 * hh), v1 = ld4(src, 2 * hh + 1);
+            const float e[8] = {v0.x * mult, v0.y * mult, v0.z * mult, v0.w * mult,
+                                v1.x * mult, v1.y * mult, v1.z * mult, v1.w * mult};
+            f16x8 hi;
+            float r[8];
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+                hi[q] = (_Float16)e[q];
+                r[q] = (e[q] - (float)hi[q]) * lmult;  // exact: |r| <= 256
+            }
+            qhi[j][hh] = hi;
+            // v_cvt_pk_fp8_f32 rounds to nearest even onto OCP e4m3
+            int w0 = __builtin_amdgcn_cvt_pk_fp8_f32(r[0], r[1], 0, false);
+            w0 = __builtin_amdgcn_cvt_pk_fp8_f32(r[2], r[3], w0, true);
+            int w1 = __builtin_amdgcn_cvt_pk_fp8_f32(r[4], r[5], 0, false);
+            w1 = __builtin_amdgcn_cvt_pk_fp8_f32(r[6], r[7], w1, true);
+            qlo[j >> 1][4 * (j & 1) + 2 * hh] = w0;
+            qlo[j >> 1][4 * (j & 1) + 2 * hh + 1] = w1;
+        }
+    }
+    if (NKB & 1)
+#pragma unroll
+        for (int k = 4; k < 8; ++k)
+            qlo[NKB >> 1][k] = 0;
+}
+
 constexpr float kTau = 8.0f;  // lazy-max slack, log2 units: weights stay <= 2^8
 
 // ---------------------------------------------------------------------------
-// Split-T partial.  Grid: n_chunks * n_groups workgroups of 256 threads.
-// NKB = number of 64-wide blocks of the padded row width (d <= 64 * NKB).
+// Split-T partial.  Grid: n_chunks * n_groups workgroups of 512 threads (8
+// waves, two per SIMD).  NKB = number of 64-wide blocks of the padded row.
+//   scores : wave w takes rows 16*(w>>1) .. +16 of the tile and heads
+//            16*(w&1) .. +16 of the group (q for 16 heads in registers);
+//   context: wave w owns context columns 64*w .. +64 for all 32 heads.
 template <int NKB>
 __global__ __launch_bounds__(kThreads, 1) void k_split_partial(AttnArgs a)
 {
     constexpr int TR = kTileRows;
     constexpr int HG = kHeadsPerGroup;
-    constexpr int DP = 64 * NKB;      // padded row width in LDS (>= d, >= roundup(lc, 128))
-    constexpr int XS = DP + 16;       // LDS row stride (bytes)
-    constexpr int WSS = TR + 8;       // LDS stride of the weight tile (halves)
+    constexpr int DP = 64 * NKB;         // padded row width in LDS (>= d, >= roundup(lc, 128))
+    constexpr int XS = DP + 16;          // LDS row stride (bytes)
+    constexpr int WSS = TR + 8;          // LDS stride of the weight tile (halves)
     constexpr int NKB2 = (NKB + 1) / 2;  // 128-wide blocks for the fp8 pass
+    constexpr int NPRE = (TR * DP / 16 + kThreads - 1) / kThreads;  // 16-B loads per thread
 
     __shared__ __attribute__((aligned(16))) uint8_t xs[2][TR * XS];
     __shared__ float s_scale[2][TR];
@@ -172,6 +266,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_split_partial(AttnArgs a)
 
     const int tid = threadIdx.x;
     const int w = tid >> 6, lane = tid & 63, n = lane & 15, g = lane >> 4;
+    const int hh = w & 1;   // head half of the group this wave scores
+    const int rq = w >> 1;  // row quarter of the tile this wave scores
 
     // Workgroup -> (chunk, head group).  Dispatch is round-robin over the 8
     // XCDs; keep the head groups of one chunk on one XCD, launched back to back.
@@ -192,125 +288,35 @@ __global__ __launch_bounds__(kThreads, 1) void k_split_partial(AttnArgs a)
     const int c1 = min(a.n_list, c0 + a.chunk_rows);
     const int ntiles = c1 > c0 ? (c1 - c0 + TR - 1) / TR : 0;
 
-    // ---- query registers.  Lane (n, g) holds, for heads qh0 + n + 16*ht, the
-    // elements d = 64j + 16g + e (e < 16).  The same assignment of the
-    // contraction index to (lane group, operand slot) is used for the row
-    // operand, so the MFMA sums the right products whatever its K labels are.
-    //   qhi: fp16(q * 2^k)             two f16x8 per (j, ht)   -> fp16 MFMA
-    //   qlo: e4m3((q*2^k - qhi) * 2^k') 32 bytes per (j pair, ht) -> fp8 MFMA
-    //        with the E8M0 operand scale 2^-k' undoing k' inside the MFMA.
-    f16x8 qhi[NKB][2][2];
-    v8i qlo[NKB2][2];
-    int32_t qlo_scale[2];
-    float hfac[2];
-    int32_t tlim[2];
-#pragma unroll
-    for (int ht = 0; ht < 2; ++ht) {
-        const int qh = qh0 + 16 * ht + n;
-        const bool hv = qh < a.n_qh;
-        auto qsrc = [&](int j) -> const float* {
-            const int d0 = 64 * j + 16 * g;
-            if (hv && d0 < a.lc)
-                return a.q_lat + (size_t)qh * a.lc + d0;
-            if (hv && d0 < a.d)
-                return a.q_rope + (size_t)qh * a.rc + (d0 - a.lc);
-            return nullptr;
-        };
-        float amax = 0.0f;
-#pragma unroll
-        for (int j = 0; j < NKB; ++j) {
-            const float* src = qsrc(j);
-            if (src) {
-#pragma unroll
-                for (int k = 0; k < 4; ++k) {
-                    const float4 v = reinterpret_cast<const float4*>(src)[k];
-                    amax = fmaxf(amax, fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)),
-                                             fmaxf(fabsf(v.z), fabsf(v.w))));
-                }
-            }
-        }
-        amax = fmaxf(amax, __shfl_xor(amax, 16));
-        amax = fmaxf(amax, __shfl_xor(amax, 32));
-        int ex = 0;
-        if (amax > 0.0f)
-            (void)frexpf(amax, &ex);
-        // amax * 2^k2 in [2^13, 2^14); clamped so 2^k2 and 2^-k2 stay normal
-        const int k2 = min(max(14 - ex, -126), 126);
-        const float mult = ldexpf(1.0f, k2);
-        hfac[ht] = a.sm_log2 * ldexpf(1.0f, -k2);
-        tlim[ht] = (a.mode == kCausal) ? a.pos0 + (hv ? qh / a.n_heads : 0) + 1 : 0x7FFFFFFF;
-        // pass 1: fp16 high part; remember the largest residual
-        float lmax = 0.0f;
-#pragma unroll
-        for (int j = 0; j < NKB; ++j) {
-            const float* src = qsrc(j);
-#pragma unroll
-            for (int hh = 0; hh < 2; ++hh) {
-                f16x8 hi;
-#pragma unroll
-                for (int k = 0; k < 2; ++k) {
-                    const float4 v = src ? reinterpret_cast<const float4*>(src)[2 * hh + k]
-                                         : make_float4(0.f, 0.f, 0.f, 0.f);
-                    const float e4[4] = {v.x * mult, v.y * mult, v.z * mult, v.w * mult};
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        const _Float16 h = (_Float16)e4[q];
-                        hi[4 * k + q] = h;
-                        lmax = fmaxf(lmax, fabsf(e4[q] - (float)h));
-                    }
-                }
-                qhi[j][ht][hh] = hi;
-            }
-        }
-        lmax = fmaxf(lmax, __shfl_xor(lmax, 16));
-        lmax = fmaxf(lmax, __shfl_xor(lmax, 32));
-        int exl = 0;
-        if (lmax > 0.0f)
-            (void)frexpf(lmax, &exl);
-        // lmax * 2^kl in [128, 256), inside e4m3's range; E8M0 needs |kl| <= 126
-        const int kl = min(max(8 - exl, -126), 126);
-        const float lmult = ldexpf(1.0f, kl);
-        qlo_scale[ht] = 127 - kl;  // E8M0 exponent of 2^-kl
-        // pass 2: e4m3 low part, packed four codes per dword
-#pragma unroll
-        for (int i = 0; i < NKB2; ++i) {
-            v8i pk;
-#pragma unroll
-            for (int half = 0; half < 2; ++half) {
-                const int j = 2 * i + half;
-#pragma unroll
-                for (int k = 0; k < 4; ++k) {
-                    uint32_t word = 0u;
-                    if (j < NKB) {
-                        const float* src = qsrc(j);
-                        const float4 v = src ? reinterpret_cast<const float4*>(src)[k]
-                                             : make_float4(0.f, 0.f, 0.f, 0.f);
-                        const float e4[4] = {v.x * mult, v.y * mult, v.z * mult, v.w * mult};
-#pragma unroll
-                        for (int q = 0; q < 4; ++q) {
-                            const float r = e4[q] - (float)(_Float16)e4[q];
-                            word |= enc_e4m3(r * lmult) << (8 * q);
-                        }
-                    }
-                    pk[4 * half + k] = (int)word;
-                }
-            }
-            qlo[i][ht] = pk;
-        }
-    }
+    // ---- query registers for heads qh0 + 16*hh + n
+    f16x8 qhi[NKB][2];
+    v8i qlo[NKB2];
+    float hfac;
+    int32_t tlim;
+    load_query<NKB>(a, qh0 + 16 * hh, n, g, qhi, qlo, hfac, tlim);
 
     // ---- LDS init: zero both row buffers (pads stay zero for the whole run).
     for (int i = tid; i < 2 * TR * XS / 16; i += kThreads)
         reinterpret_cast<uint4*>(&xs[0][0])[i] = make_uint4(0u, 0u, 0u, 0u);
 
-    // ---- tile loader: global -> registers, registers -> LDS.
+    // ---- tile loader: global -> registers (one tile ahead), registers -> LDS.
+    // Thread chunk i covers 16 bytes: row r_i of the tile, bytes 16*c_i of the
+    // row; the (r, c) split is computed once.
     const int cpr = a.d >> 4;  // 16-byte chunks per row
     const int tot = TR * cpr;
-    uint4 pre[NKB];
+    // packed as r * 1024 + byte offset (rows < 64, offsets < 640); -1 = idle
+    int ld_rc[NPRE];
+#pragma unroll
+    for (int i = 0; i < NPRE; ++i) {
+        const int id = tid + kThreads * i;
+        const int r = id / cpr;
+        ld_rc[i] = id < tot ? r * 1024 + 16 * (id - r * cpr) : -1;
+    }
+    uint4 pre[NPRE];
     float pre_scale = 0.0f;
     int32_t pre_row = -1;
 
-    auto row_of = [&](int pos) -> int32_t {
+    auto row_of = [&](int pos) __attribute__((always_inline)) -> int32_t {
         if (pos >= c1)
             return -1;
         if (a.mode == kSelect) {
@@ -319,16 +325,15 @@ __global__ __launch_bounds__(kThreads, 1) void k_split_partial(AttnArgs a)
         }
         return pos;
     };
-    auto load_tile = [&](int p0) {
+    auto load_tile = [&](int p0) __attribute__((always_inline)) {
 #pragma unroll
-        for (int i = 0; i < NKB; ++i) {
-            const int id = tid + kThreads * i;
+        for (int i = 0; i < NPRE; ++i) {
             pre[i] = make_uint4(0u, 0u, 0u, 0u);
-            if (id < tot) {
-                const int r = id / cpr, c = id - r * cpr;
-                const int32_t row = row_of(p0 + r);
+            if (ld_rc[i] >= 0) {
+                const int32_t row = row_of(p0 + (ld_rc[i] >> 10));
                 if (row >= 0)
-                    pre[i] = *reinterpret_cast<const uint4*>(a.codes + (size_t)row * a.d + c * 16);
+                    pre[i] = *reinterpret_cast<const uint4*>(a.codes + (size_t)row * a.d +
+                                                             (ld_rc[i] & 1023));
             }
         }
         if (tid < TR) {
@@ -336,15 +341,12 @@ __global__ __launch_bounds__(kThreads, 1) void k_split_partial(AttnArgs a)
             pre_scale = pre_row >= 0 ? a.scales[pre_row] : 0.0f;
         }
     };
-    auto store_tile = [&](int buf) {
+    auto store_tile = [&](int buf) __attribute__((always_inline)) {
 #pragma unroll
-        for (int i = 0; i < NKB; ++i) {
-            const int id = tid + kThreads * i;
-            if (id < tot) {
-                const int r = id / cpr, c = id - r * cpr;
-                *reinterpret_cast<uint4*>(&xs[buf][r * XS + c * 16]) = pre[i];
-            }
-        }
+        for (int i = 0; i < NPRE; ++i)
+            if (ld_rc[i] >= 0)
+                *reinterpret_cast<uint4*>(&xs[buf][(ld_rc[i] >> 10) * XS + (ld_rc[i] & 1023)]) =
+                    pre[i];
         if (tid < TR) {
             s_scale[buf][tid] = pre_scale;
             s_lscale[buf][tid] = log2f(pre_scale);  // -inf for a zero scale
@@ -352,16 +354,19 @@ __global__ __launch_bounds__(kThreads, 1) void k_split_partial(AttnArgs a)
         }
     };
 
-    float mrun[2] = {-INFINITY, -INFINITY};   // running max of u (z side)
-    float morun[2] = {-INFINITY, -INFINITY};  // running max of u + log2 scale (O side)
-    float zacc[2] = {0.0f, 0.0f};
-    f32x4 O[2][8];
+    // Running softmax state, replicated in every wave for heads n and 16 + n
+    // of the group: m = lazy max of u (z side), d = lazy max of
+    // (u - m) + log2 scale (context side, relative to m).
+    float mrun[2] = {-INFINITY, -INFINITY};
+    float drun[2] = {-INFINITY, -INFINITY};
+    float zacc = 0.0f;  // z partial over this lane's rows, head 16*hh + n
+    f32x4 O[2][4];
 #pragma unroll
     for (int ht = 0; ht < 2; ++ht)
 #pragma unroll
-        for (int jm = 0; jm < 8; ++jm)
+        for (int jm = 0; jm < 4; ++jm)
             O[ht][jm] = f32x4{0.f, 0.f, 0.f, 0.f};
-    const int cb = 128 * w;  // this wave's context column block
+    const int cb = 64 * w;  // this wave's context columns
     const bool pv_active = cb < a.lc;
 
     __syncthreads();  // zero fill done before the first tile lands
@@ -376,102 +381,103 @@ __global__ __launch_bounds__(kThreads, 1) void k_split_partial(AttnArgs a)
         if (it + 1 < ntiles)
             load_tile(c0 + (it + 1) * TR);
 
-        // ---- scores: S^T[16 rows of this wave][32 heads]
-        f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
-        const uint8_t* xrow = &xs[buf][(16 * w + n) * XS + 16 * g];
+        // ---- scores: S^T[16 rows][16 heads]
+        f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+        const uint8_t* xrow = &xs[buf][(16 * rq + n) * XS + 16 * g];
 #pragma unroll
         for (int i = 0; i < NKB2; ++i) {
             const uint4 x0 = *reinterpret_cast<const uint4*>(xrow + 128 * i);
             const uint4 x1 = (2 * i + 1 < NKB)
                                  ? *reinterpret_cast<const uint4*>(xrow + 128 * i + 64)
                                  : make_uint4(0u, 0u, 0u, 0u);
-            {
-                const f16x8 a0 = cvt8(x0.x, x0.y), a1 = cvt8(x0.z, x0.w);
-#pragma unroll
-                for (int ht = 0; ht < 2; ++ht) {
-                    acc[ht] = mfma16(a0, qhi[2 * i][ht][0], acc[ht]);
-                    acc[ht] = mfma16(a1, qhi[2 * i][ht][1], acc[ht]);
-                }
-            }
+            acc = mfma16(cvt8(x0.x, x0.y), qhi[2 * i][0], acc);
+            acc = mfma16(cvt8(x0.z, x0.w), qhi[2 * i][1], acc);
             if (2 * i + 1 < NKB) {
-                const f16x8 a0 = cvt8(x1.x, x1.y), a1 = cvt8(x1.z, x1.w);
-#pragma unroll
-                for (int ht = 0; ht < 2; ++ht) {
-                    acc[ht] = mfma16(a0, qhi[2 * i + 1][ht][0], acc[ht]);
-                    acc[ht] = mfma16(a1, qhi[2 * i + 1][ht][1], acc[ht]);
-                }
+                acc = mfma16(cvt8(x1.x, x1.y), qhi[2 * i + 1][0], acc);
+                acc = mfma16(cvt8(x1.z, x1.w), qhi[2 * i + 1][1], acc);
             }
             const v8i x8 = v8i{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w,
                                (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
-#pragma unroll
-            for (int ht = 0; ht < 2; ++ht)
-                acc[ht] = mfma_fp8_scaled(x8, qlo[i][ht], acc[ht], qlo_scale[ht]);
+            acc = mfma_fp8_scaled(x8, qlo[i], acc, 127 - kQloShift);
         }
 
-        // ---- log2-domain scores u and O-side logits uo; per-wave maxima
-        float u[2][4], uo[2][4], tm[2], tmo[2];
-#pragma unroll
-        for (int ht = 0; ht < 2; ++ht) {
-            tm[ht] = -INFINITY;
-            tmo[ht] = -INFINITY;
-        }
+        // ---- log2-domain scores u (rows 16rq + 4g + v, head 16hh + n); per wave:
+        // the tile max Tw of u and Cw = max_t (u_t - Tw) + log2 scale_t.
+        // Everything after this stays relative to a running max, so a large
+        // |u| never swallows log2 scale.
+        float u[4], lsv[4];
+        float tw = -INFINITY;
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
-            const int r = 16 * w + 4 * g + v;
-            const float sc = s_scale[buf][r], ls = s_lscale[buf][r];
+            const int r = 16 * rq + 4 * g + v;
+            const float sc = s_scale[buf][r];
+            lsv[v] = s_lscale[buf][r];
             const int32_t row = s_row[buf][r];
-#pragma unroll
-            for (int ht = 0; ht < 2; ++ht) {
-                const bool valid = row >= 0 && row < tlim[ht];
-                const float uu = valid ? (acc[ht][v] * hfac[ht]) * sc : -INFINITY;
-                u[ht][v] = uu;
-                uo[ht][v] = valid ? uu + ls : -INFINITY;
-                tm[ht] = fmaxf(tm[ht], u[ht][v]);
-                tmo[ht] = fmaxf(tmo[ht], uo[ht][v]);
-            }
+            const bool valid = row >= 0 && row < tlim;
+            u[v] = valid ? (acc[v] * hfac) * sc : -INFINITY;
+            tw = fmaxf(tw, u[v]);
         }
+        tw = fmaxf(tw, __shfl_xor(tw, 16));
+        tw = fmaxf(tw, __shfl_xor(tw, 32));
+        float cw = -INFINITY;
+        if (tw != -INFINITY) {
 #pragma unroll
-        for (int ht = 0; ht < 2; ++ht) {
-            tm[ht] = fmaxf(tm[ht], __shfl_xor(tm[ht], 16));
-            tm[ht] = fmaxf(tm[ht], __shfl_xor(tm[ht], 32));
-            tmo[ht] = fmaxf(tmo[ht], __shfl_xor(tmo[ht], 16));
-            tmo[ht] = fmaxf(tmo[ht], __shfl_xor(tmo[ht], 32));
-            if (g == 0) {
-                s_red[w][0][16 * ht + n] = tm[ht];
-                s_red[w][1][16 * ht + n] = tmo[ht];
-            }
+            for (int v = 0; v < 4; ++v)
+                cw = fmaxf(cw, (u[v] - tw) + lsv[v]);
+        }
+        cw = fmaxf(cw, __shfl_xor(cw, 16));
+        cw = fmaxf(cw, __shfl_xor(cw, 32));
+        if (g == 0) {
+            s_red[rq][0][16 * hh + n] = tw;
+            s_red[rq][1][16 * hh + n] = cw;
         }
         __syncthreads();
 
-        // ---- running maxima (identical in every wave), weights, z
-        float alo[2];
+        // ---- running state for heads n, 16 + n (every wave computes both)
+        float alz[2], alo[2];
 #pragma unroll
         for (int ht = 0; ht < 2; ++ht) {
             const int h = 16 * ht + n;
-            const float T = fmaxf(fmaxf(s_red[0][0][h], s_red[1][0][h]),
-                                  fmaxf(s_red[2][0][h], s_red[3][0][h]));
-            const float TO = fmaxf(fmaxf(s_red[0][1][h], s_red[1][1][h]),
-                                   fmaxf(s_red[2][1][h], s_red[3][1][h]));
-            const float mnew = (T > mrun[ht] + kTau) ? T : mrun[ht];
-            const float alz = (mnew == mrun[ht]) ? 1.0f : fast_exp2(mrun[ht] - mnew);
+            float T = -INFINITY;
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+                T = fmaxf(T, s_red[k][0][h]);
+            const float mold = mrun[ht];
+            const float mnew = (T > mold + kTau) ? T : mold;
+            alz[ht] = (mnew == mold) ? 1.0f : fast_exp2(mold - mnew);
+            const float mu = (mnew == -INFINITY) ? 0.0f : mnew;
+            float tb = -INFINITY;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const float Tk = s_red[k][0][h];
+                if (Tk != -INFINITY)
+                    tb = fmaxf(tb, s_red[k][1][h] + (Tk - mu));
+            }
+            const float dshift = (mnew == mold) ? drun[ht] : drun[ht] + (mold - mnew);
+            const float dnew = (tb > dshift + kTau) ? tb : dshift;
+            alo[ht] = (dnew == dshift) ? 1.0f : fast_exp2(dshift - dnew);
             mrun[ht] = mnew;
-            const float monew = (TO > morun[ht] + kTau) ? TO : morun[ht];
-            alo[ht] = (monew == morun[ht]) ? 1.0f : fast_exp2(morun[ht] - monew);
-            morun[ht] = monew;
-            const float mu = (mrun[ht] == -INFINITY) ? 0.0f : mrun[ht];
-            const float muo = (morun[ht] == -INFINITY) ? 0.0f : morun[ht];
+            drun[ht] = dnew;
+        }
+        // ---- this wave's rows: p = 2^(u - m) into z, w = 2^((u - m) + ls - d)
+        {
+            const float mu = hh ? mrun[1] : mrun[0];
+            const float dd = hh ? drun[1] : drun[0];
+            const float mz = (mu == -INFINITY) ? 0.0f : mu;
+            const float dn = (dd == -INFINITY) ? 0.0f : dd;
             float ps = 0.0f;
             f16x4 wv;
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
-                ps += fast_exp2(u[ht][v] - mu);
-                wv[v] = (_Float16)fast_exp2(uo[ht][v] - muo);
+                const float av = u[v] - mz;
+                ps += fast_exp2(av);
+                wv[v] = (_Float16)fast_exp2((av + lsv[v]) - dn);
             }
-            zacc[ht] = zacc[ht] * alz + ps;
-            *reinterpret_cast<f16x4*>(&s_w[h * WSS + 16 * w + 4 * g]) = wv;
+            zacc = zacc * (hh ? alz[1] : alz[0]) + ps;
+            *reinterpret_cast<f16x4*>(&s_w[(16 * hh + n) * WSS + 16 * rq + 4 * g]) = wv;
         }
-        // Rescale the context accumulators when a running max moved.  O holds
-        // heads 16*ht + 4*g + v; their factors live in lanes 4*g + v.
+        // Rescale the context accumulators when a context offset moved.  O
+        // holds heads 16*ht + 4*g + v; their factors live in lanes 4*g + v.
         if (__any((alo[0] != 1.0f) || (alo[1] != 1.0f))) {
 #pragma unroll
             for (int ht = 0; ht < 2; ++ht)
@@ -479,13 +485,16 @@ __global__ __launch_bounds__(kThreads, 1) void k_split_partial(AttnArgs a)
                 for (int v = 0; v < 4; ++v) {
                     const float f = __shfl(alo[ht], 4 * g + v);
 #pragma unroll
-                    for (int jm = 0; jm < 8; ++jm)
+                    for (int jm = 0; jm < 4; ++jm)
                         O[ht][jm][v] *= f;
                 }
         }
         __syncthreads();  // weight tile complete
 
-        // ---- context: O[32 heads][128 cols of this wave] += W . X
+        // ---- context: O[32 heads][64 cols of this wave] += W . X.  Lane (n, g)
+        // reads rows 32ks + 8g + 0..7, columns cb + 4n .. +4, and byte-transposes
+        // them so the row index becomes the MFMA K index; MFMA jm covers the
+        // columns cb + 4n' + jm over the 16 lanes n'.
         if (pv_active) {
 #pragma unroll
             for (int ks = 0; ks < TR / 32; ++ks) {
@@ -494,25 +503,20 @@ __global__ __launch_bounds__(kThreads, 1) void k_split_partial(AttnArgs a)
                 for (int ht = 0; ht < 2; ++ht)
                     wa[ht] = *reinterpret_cast<const f16x8*>(
                         &s_w[(16 * ht + n) * WSS + 32 * ks + 8 * g]);
-                uint2 xr[8];
+                uint32_t xr[8];
 #pragma unroll
                 for (int v = 0; v < 8; ++v)
-                    xr[v] = *reinterpret_cast<const uint2*>(
-                        &xs[buf][(32 * ks + 8 * g + v) * XS + cb + 8 * n]);
+                    xr[v] = *reinterpret_cast<const uint32_t*>(
+                        &xs[buf][(32 * ks + 8 * g + v) * XS + cb + 4 * n]);
 #pragma unroll
-                for (int jp = 0; jp < 4; ++jp) {
-                    // columns 2jp and 2jp+1 of this lane's 8-byte block
-                    const int jj = (2 * jp) & 3;
-                    const uint32_t selb = (uint32_t)jj | ((uint32_t)(jj + 4) << 8) |
-                                          ((uint32_t)(jj + 1) << 16) |
-                                          ((uint32_t)(jj + 5) << 24);
+                for (int jp = 0; jp < 2; ++jp) {
+                    // columns 2jp and 2jp+1: bytes [r0.c, r1.c, r0.c+1, r1.c+1]
+                    const uint32_t jj = 2 * jp;
+                    const uint32_t selb = jj | ((jj + 4) << 8) | ((jj + 1) << 16) | ((jj + 5) << 24);
                     f16x8 bA, bB;
 #pragma unroll
                     for (int uu = 0; uu < 4; ++uu) {
-                        const uint32_t r0 = jp < 2 ? xr[2 * uu].x : xr[2 * uu].y;
-                        const uint32_t r1 = jp < 2 ? xr[2 * uu + 1].x : xr[2 * uu + 1].y;
-                        // bytes: [r0.jj, r1.jj, r0.jj+1, r1.jj+1]
-                        const uint32_t pk = __builtin_amdgcn_perm(r1, r0, selb);
+                        const uint32_t pk = __builtin_amdgcn_perm(xr[2 * uu + 1], xr[2 * uu], selb);
                         const f16x2 lo = cvt2<false>(pk), hi = cvt2<true>(pk);
                         bA[2 * uu] = lo[0];
                         bA[2 * uu + 1] = lo[1];
@@ -533,45 +537,38 @@ __global__ __launch_bounds__(kThreads, 1) void k_split_partial(AttnArgs a)
         __syncthreads();
     }
 
-    // ---- epilogue: z over lane groups and waves; partial (m, z, cl)
-#pragma unroll
-    for (int ht = 0; ht < 2; ++ht) {
-        float zz = zacc[ht];
+    // ---- epilogue: z over lane groups and row quarters; partial (m, z, cl)
+    {
+        float zz = zacc;
         zz += __shfl_xor(zz, 16);
         zz += __shfl_xor(zz, 32);
         if (g == 0)
-            s_z[w][16 * ht + n] = zz;
+            s_z[rq][16 * hh + n] = zz;
     }
     __syncthreads();
     const size_t pbase = (size_t)chunk * a.n_qh;
-    if (w == 0 && g == 0) {
-#pragma unroll
-        for (int ht = 0; ht < 2; ++ht) {
-            const int h = 16 * ht + n, qh = qh0 + h;
-            if (qh < a.n_qh) {
-                a.ws_m[pbase + qh] = mrun[ht];
-                a.ws_z[pbase + qh] = (s_z[0][h] + s_z[1][h]) + (s_z[2][h] + s_z[3][h]);
-            }
+    if (rq == 0 && g == 0) {
+        const int h = 16 * hh + n, qh = qh0 + h;
+        if (qh < a.n_qh) {
+            a.ws_m[pbase + qh] = hh ? mrun[1] : mrun[0];
+            a.ws_z[pbase + qh] = (s_z[0][h] + s_z[1][h]) + (s_z[2][h] + s_z[3][h]);
         }
     }
     if (pv_active) {
 #pragma unroll
         for (int ht = 0; ht < 2; ++ht) {
-            const float fown = (mrun[ht] == -INFINITY || morun[ht] == -INFINITY)
-                                   ? 0.0f
-                                   : fast_exp2(morun[ht] - mrun[ht]);
+            // cl = sum_t p_t scale_t x_t = 2^d * O
+            const float fown =
+                (mrun[ht] == -INFINITY || drun[ht] == -INFINITY) ? 0.0f : fast_exp2(drun[ht]);
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
                 const float f = __shfl(fown, 4 * g + v);
                 const int qh = qh0 + 16 * ht + 4 * g + v;
-                const int col = cb + 8 * n;
-                if (qh < a.n_qh && col < a.lc) {
-                    float4* dst = reinterpret_cast<float4*>(a.ws_cl + (pbase + qh) * a.lc + col);
-                    dst[0] = make_float4(O[ht][0][v] * f, O[ht][1][v] * f, O[ht][2][v] * f,
-                                         O[ht][3][v] * f);
-                    dst[1] = make_float4(O[ht][4][v] * f, O[ht][5][v] * f, O[ht][6][v] * f,
-                                         O[ht][7][v] * f);
-                }
+                const int col = cb + 4 * n;
+                if (qh < a.n_qh && col < a.lc)
+                    *reinterpret_cast<float4*>(a.ws_cl + (pbase + qh) * a.lc + col) =
+                        make_float4(O[ht][0][v] * f, O[ht][1][v] * f, O[ht][2][v] * f,
+                                    O[ht][3][v] * f);
             }
         }
     }

@@ -189,9 +189,14 @@ def mla8_batch(kv_codes, kv_scales, t_rows: int, lc: int, rc: int, q_lat, q_rope
 
 def mla8_profile_events(before: "torch.cuda.Event | None", after: "torch.cuda.Event | None"):
     """Record `before`/`after` around the split-T partial kernel of the next
-    attention calls (None, None clears).  The events must already exist."""
+    attention calls (None, None clears).  torch creates an event's hipEvent on
+    its first record(), so record both once before passing them."""
     def raw(ev):
-        return None if ev is None else ev.cuda_event
+        if ev is None:
+            return None
+        if not ev.cuda_event:
+            raise ValueError("mla8_profile_events: record the event once first")
+        return ev.cuda_event
     _check(lib.mla8_profile_events(raw(before), raw(after)), "mla8_profile_events")
 
 
