@@ -15,13 +15,16 @@
 //   * One workgroup owns a chunk of rows and 32 query-heads, so every row is
 //     read from HBM once for all its heads; workgroups sharing a chunk are
 //     placed on the same XCD so the second head group hits that XCD's L2.
-//   * Rows are staged through LDS in 64-row tiles.  e4m3 bytes are widened to
-//     fp16 in registers with v_cvt_scalef32_pk_f16_fp8 (exact: every e4m3 value
-//     is an fp16 normal), then fed to v_mfma_f32_16x16x32_f16.
+//   * Rows stream HBM -> LDS in 64-row tiles through a 3-stage ring of direct
+//     global_load_lds_dwordx4 loads (two tiles in flight, no register
+//     staging).  e4m3 bytes are widened to fp16 in registers with
+//     v_cvt_scalef32_pk_f16_fp8 (exact: every e4m3 value is an fp16 normal),
+//     then fed to v_mfma_f32_16x16x32_f16.
 //   * 8 waves per workgroup (two per SIMD).  Scores S^T[row][head] = X . Q^T:
-//     each wave takes 16 rows x 16 heads; q is resident in registers as an fp16
-//     high part (fp16 MFMA) plus an e4m3 low part (scaled fp8 MFMA on the raw
-//     row bytes), with a power of two per head so it sits in fp16's range.
+//     each wave takes 16 rows x 16 heads; q is split into an fp16 high part
+//     held in registers (fp16 MFMA) and an e4m3 low part held in LDS (scaled
+//     fp8 MFMA straight on the row bytes), with a power of two per head so it
+//     sits in fp16's range.
 //   * Context O[head][col] += W . X: each wave owns a 64-column slice for all
 //     32 heads, reading a 4x8 byte block per lane and transposing it with
 //     v_perm_b32 so the row (contraction) index becomes the MFMA K index.
@@ -35,6 +38,8 @@
 #include "mla8_internal.h"
 
 #include <math.h>
+
+#include <type_traits>
 
 namespace mla8 {
 
@@ -149,38 +154,48 @@ __device__ __forceinline__ f32x4 mfma_fp8_scaled(v8i a, v8i b, f32x4 c, int32_t 
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// Source of the 16 query elements d = 64j + 16g .. +16 of query-head qh (or
-// nullptr past the row width / past the last head).
-__device__ __forceinline__ const float* q_src(const AttnArgs& a, int qh, bool hv, int j, int g)
+// Source of the 16 query elements d = 64j + 16g .. +16 of query-head qh, and
+// whether they exist (false past the row width or past the last head; the
+// pointer then still addresses valid memory, the first q_lat row, so that every
+// load can be issued unconditionally and many can be in flight at once).
+struct QSrc {
+    const float* p;
+    bool ok;
+};
+
+__device__ __forceinline__ QSrc q_src(const AttnArgs& a, int qh, bool hv, int j, int g)
 {
     const int d0 = 64 * j + 16 * g;
     if (hv && d0 < a.lc)
-        return a.q_lat + (size_t)qh * a.lc + d0;
+        return {a.q_lat + (size_t)qh * a.lc + d0, true};
     if (hv && d0 < a.d)
-        return a.q_rope + (size_t)qh * a.rc + (d0 - a.lc);
-    return nullptr;
+        return {a.q_rope + (size_t)qh * a.rc + (d0 - a.lc), true};
+    return {a.q_lat, false};
 }
 
-__device__ __forceinline__ float4 ld4(const float* p, int k)
+__device__ __forceinline__ float4 ld4(const QSrc& s, int k)
 {
-    return p ? reinterpret_cast<const float4*>(p)[k] : make_float4(0.f, 0.f, 0.f, 0.f);
+    const float4 v = reinterpret_cast<const float4*>(s.p)[k];
+    return s.ok ? v : make_float4(0.f, 0.f, 0.f, 0.f);
 }
 
-// Query registers for 16 heads.  Lane (n, g) holds, for head qh_base + n, the
+// Query operands for 16 heads.  Lane (n, g) holds, for head qh_base + n, the
 // elements d = 64j + 16g + e (e < 16).  The same assignment of the contraction
 // index to (lane group, operand slot) is used for the row operand, so the MFMA
 // sums the right products whatever its K labels are.
-//   qhi: fp16(q * 2^k)                 two f16x8 per j      -> fp16 MFMA
+//   qhi: fp16(q * 2^k)                 two f16x8 per j      -> fp16 MFMA,
+//        kept in registers;
 //   qlo: e4m3((q*2^k - qhi) * 2^6)     32 bytes per j pair  -> fp8 MFMA, whose
-//        E8M0 operand scale 2^-6 undoes the 2^6 inside the instruction.
+//        E8M0 operand scale 2^-6 undoes the 2^6 inside the instruction; written
+//        lane-linear to LDS (qlo_lds[i][lane], 32 bytes) when write_lo is set.
 // k puts the head's largest |q| in [2^13, 2^14), where the fp16 spacing is 8,
 // so every residual is at most 4 and 2^6 * 4 = 256 sits inside e4m3's range.
-// Every index is a compile-time constant so the arrays stay in registers.
+// Every index is a compile-time constant so qhi stays in registers.
 constexpr int kQloShift = 6;
 
 template <int NKB>
-__device__ __forceinline__ void load_query(const AttnArgs& a, int qh_base, int n, int g,
-                                           f16x8 (&qhi)[NKB][2], v8i (&qlo)[(NKB + 1) / 2],
+__device__ __forceinline__ void load_query(const AttnArgs& a, int qh_base, int n, int g, int lane,
+                                           f16x8 (&qhi)[NKB][2], v8i* qlo_lds, bool write_lo,
                                            float& hfac, int32_t& tlim)
 {
     const int qh = qh_base + n;
@@ -188,7 +203,7 @@ __device__ __forceinline__ void load_query(const AttnArgs& a, int qh_base, int n
     float amax = 0.0f;
 #pragma unroll
     for (int j = 0; j < NKB; ++j) {
-        const float* src = q_src(a, qh, hv, j, g);
+        const QSrc src = q_src(a, qh, hv, j, g);
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
             const float4 v = ld4(src, k);
@@ -206,9 +221,10 @@ __device__ __forceinline__ void load_query(const AttnArgs& a, int qh_base, int n
     const float lmult = (float)(1 << kQloShift);
     hfac = a.sm_log2 * ldexpf(1.0f, -k2);
     tlim = (a.mode == kCausal) ? a.pos0 + (hv ? qh / a.n_heads : 0) + 1 : 0x7FFFFFFF;
+    int lo[8];
 #pragma unroll
     for (int j = 0; j < NKB; ++j) {
-        const float* src = q_src(a, qh, hv, j, g);
+        const QSrc src = q_src(a, qh, hv, j, g);
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
             const float4 v0 = ld4(src, 2 * hh), v1 = ld4(src, 2 * hh + 1);
@@ -227,40 +243,135 @@ __device__ __forceinline__ void load_query(const AttnArgs& a, int qh_base, int n
             w0 = __builtin_amdgcn_cvt_pk_fp8_f32(r[2], r[3], w0, true);
             int w1 = __builtin_amdgcn_cvt_pk_fp8_f32(r[4], r[5], 0, false);
             w1 = __builtin_amdgcn_cvt_pk_fp8_f32(r[6], r[7], w1, true);
-            qlo[j >> 1][4 * (j & 1) + 2 * hh] = w0;
-            qlo[j >> 1][4 * (j & 1) + 2 * hh + 1] = w1;
+            lo[4 * (j & 1) + 2 * hh] = w0;
+            lo[4 * (j & 1) + 2 * hh + 1] = w1;
+        }
+        if ((j & 1) || j == NKB - 1) {
+            if (!(j & 1))
+#pragma unroll
+                for (int k = 4; k < 8; ++k)
+                    lo[k] = 0;
+            if (write_lo)
+                qlo_lds[(j >> 1) * 64 + lane] =
+                    v8i{lo[0], lo[1], lo[2], lo[3], lo[4], lo[5], lo[6], lo[7]};
         }
     }
-    if (NKB & 1)
-#pragma unroll
-        for (int k = 4; k < 8; ++k)
-            qlo[NKB >> 1][k] = 0;
 }
 
 constexpr float kTau = 8.0f;  // lazy-max slack, log2 units: weights stay <= 2^8
 
 // ---------------------------------------------------------------------------
+// LDS barrier without a memory fence: wait for this wave's LDS operations,
+// then s_barrier.  A fenced __syncthreads would also wait for every
+// outstanding global->LDS row load (vmcnt 0) and empty the load pipeline.
+// The empty asm statements keep the compiler from moving memory accesses
+// across the barrier.
+__device__ __forceinline__ void lds_barrier()
+{
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt and expcnt not waited
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+// Wait until at most N vector-memory operations of this wave are in flight.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | 0x70 | 0xF00);
+    asm volatile("" ::: "memory");
+}
+
+#define MLA8_LDS __attribute__((address_space(3)))
+
+// Direct global -> LDS loads, lane i writing LDS bytes [base + 16i, +16)
+// (dwordx4) or [base + 4i, +4) (dword).  Issued through asm so that the
+// compiler's wait insertion does not track them: every wait on them is the
+// explicit wait_vmcnt<> of the tile pipeline (a tracked load would be waited
+// with vmcnt(0) wherever its LDS object is read, draining the pipeline).
+// These are the kernel's only users of m0.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void dma_b128(const void* src, const void* lds_dst)
+{
+    const uint32_t off = __builtin_amdgcn_readfirstlane(
+        (uint32_t)(uintptr_t)(MLA8_LDS const void*)lds_dst);
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
+                 :
+                 : "s"(off), "v"(src)
+                 : "memory", "m0");
+}
+
+__device__ __forceinline__ void dma_b32(const void* src, const void* lds_dst)
+{
+    const uint32_t off = __builtin_amdgcn_readfirstlane(
+        (uint32_t)(uintptr_t)(MLA8_LDS const void*)lds_dst);
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off"
+                 :
+                 : "s"(off), "v"(src)
+                 : "memory", "m0");
+}
+// Same with a wave-uniform 64-bit base in SGPRs and a 32-bit per-lane offset.
+__device__ __forceinline__ void dma_b128_s(const void* base, uint32_t voff, const void* lds_dst)
+{
+    const uint32_t off = __builtin_amdgcn_readfirstlane(
+        (uint32_t)(uintptr_t)(MLA8_LDS const void*)lds_dst);
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+                 :
+                 : "s"(off), "v"(voff), "s"(base)
+                 : "memory", "m0");
+}
+
+__device__ __forceinline__ void dma_b32_s(const void* base, uint32_t voff, const void* lds_dst)
+{
+    const uint32_t off = __builtin_amdgcn_readfirstlane(
+        (uint32_t)(uintptr_t)(MLA8_LDS const void*)lds_dst);
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, %2"
+                 :
+                 : "s"(off), "v"(voff), "s"(base)
+                 : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
 // Split-T partial.  Grid: n_chunks * n_groups workgroups of 512 threads (8
 // waves, two per SIMD).  NKB = number of 64-wide blocks of the padded row.
+//   loads  : 64-row tiles stream HBM -> LDS through a 3-stage ring of direct
+//            global_load_lds_dwordx4 (no register staging), two tiles in
+//            flight while a third is consumed;
 //   scores : wave w takes rows 16*(w>>1) .. +16 of the tile and heads
-//            16*(w&1) .. +16 of the group (q for 16 heads in registers);
+//            16*(w&1) .. +16 of the group (fp16 high part of q in registers,
+//            e4m3 low part in LDS);
 //   context: wave w owns context columns 64*w .. +64 for all 32 heads.
-template <int NKB>
+template <int NKB, bool GATHER>
 __global__ __launch_bounds__(kThreads, 1) void k_split_partial(AttnArgs a)
 {
     constexpr int TR = kTileRows;
     constexpr int HG = kHeadsPerGroup;
+    constexpr int NW = kThreads / 64;    // waves
     constexpr int DP = 64 * NKB;         // padded row width in LDS (>= d, >= roundup(lc, 128))
-    constexpr int XS = DP + 16;          // LDS row stride (bytes)
+    constexpr int XS = DP + 16;          // LDS row stride: DP bytes + one 16-B pad slot
+    constexpr int SPR = XS / 16;         // 16-byte slots per LDS row
+    constexpr int NINS = SPR;            // 1-KB DMA instructions per tile (64 rows x SPR slots)
+    constexpr int KW = (NINS + NW - 1) / NW;  // row DMA instructions per wave per tile
+    constexpr int NVM = KW + 1;          // + one scale DMA: vector-memory ops per wave per tile
+    constexpr int NST = 3;               // ring stages
     constexpr int WSS = TR + 8;          // LDS stride of the weight tile (halves)
     constexpr int NKB2 = (NKB + 1) / 2;  // 128-wide blocks for the fp8 pass
-    constexpr int NPRE = (TR * DP / 16 + kThreads - 1) / kThreads;  // 16-B loads per thread
+    static_assert(TR * XS == NINS * 1024, "a stage is a whole number of 1-KB DMA blocks");
+    static_assert(NVM < 64, "vmcnt range");
 
-    __shared__ __attribute__((aligned(16))) uint8_t xs[2][TR * XS];
-    __shared__ float s_scale[2][TR];
-    __shared__ float s_lscale[2][TR];
-    __shared__ int32_t s_row[2][TR];
+    // One object per ring stage: the compiler tracks memory per object.
+    __shared__ __attribute__((aligned(1024))) uint8_t xs0[TR * XS];
+    __shared__ __attribute__((aligned(1024))) uint8_t xs1[TR * XS];
+    __shared__ __attribute__((aligned(1024))) uint8_t xs2[TR * XS];
+    __shared__ __attribute__((aligned(16))) float sc0[NW][TR];  // per-wave copies of the scales
+    __shared__ __attribute__((aligned(16))) float sc1[NW][TR];
+    __shared__ __attribute__((aligned(16))) float sc2[NW][TR];
+    __shared__ int32_t s_row[NST][TR];
     __shared__ __attribute__((aligned(16))) _Float16 s_w[HG * WSS];
+    __shared__ __attribute__((aligned(32))) v8i s_qlo[2][NKB2 * 64];  // [head half][block][lane]
     __shared__ float s_red[4][2][HG];
     __shared__ float s_z[4][HG];
 
@@ -288,69 +399,93 @@ __global__ __launch_bounds__(kThreads, 1) void k_split_partial(AttnArgs a)
     const int c1 = min(a.n_list, c0 + a.chunk_rows);
     const int ntiles = c1 > c0 ? (c1 - c0 + TR - 1) / TR : 0;
 
-    // ---- query registers for heads qh0 + 16*hh + n
+    // ---- query operands for heads qh0 + 16*hh + n (the low part is written
+    // to LDS by the row-quarter-0 wave of each head half)
     f16x8 qhi[NKB][2];
-    v8i qlo[NKB2];
     float hfac;
     int32_t tlim;
-    load_query<NKB>(a, qh0 + 16 * hh, n, g, qhi, qlo, hfac, tlim);
+    load_query<NKB>(a, qh0 + 16 * hh, n, g, lane, qhi, &s_qlo[hh][0], rq == 0, hfac, tlim);
+    const v8i* qlo = &s_qlo[hh][0];
 
-    // ---- LDS init: zero both row buffers (pads stay zero for the whole run).
-    for (int i = tid; i < 2 * TR * XS / 16; i += kThreads)
-        reinterpret_cast<uint4*>(&xs[0][0])[i] = make_uint4(0u, 0u, 0u, 0u);
-
-    // ---- tile loader: global -> registers (one tile ahead), registers -> LDS.
-    // Thread chunk i covers 16 bytes: row r_i of the tile, bytes 16*c_i of the
-    // row; the (r, c) split is computed once.
-    const int cpr = a.d >> 4;  // 16-byte chunks per row
-    const int tot = TR * cpr;
-    // packed as r * 1024 + byte offset (rows < 64, offsets < 640); -1 = idle
-    int ld_rc[NPRE];
-#pragma unroll
-    for (int i = 0; i < NPRE; ++i) {
-        const int id = tid + kThreads * i;
-        const int r = id / cpr;
-        ld_rc[i] = id < tot ? r * 1024 + 16 * (id - r * cpr) : -1;
-    }
-    uint4 pre[NPRE];
-    float pre_scale = 0.0f;
-    int32_t pre_row = -1;
-
+    // ---- tile issue: every wave issues exactly NVM vector-memory operations
+    // per tile (so a fixed vmcnt marks a tile complete).  Row DMA instruction k
+    // fills LDS bytes [1024k, 1024k + 1024) of the stage: slot 64k + lane is
+    // (row r, 16-byte chunk c) with r = slot / SPR, c = slot % SPR.  Slots past
+    // the row's data (zero-pad columns, the pad slot) and rows outside the
+    // list load chunk 0 / the tile's first row instead: finite bytes that are
+    // multiplied by a zero query element, masked out of the softmax, or never
+    // read.  Spare instruction slots (k >= NINS) repeat instruction k % NINS
+    // (the same bytes to the same place).
+    const int cpr = a.d >> 4;  // 16-byte data chunks per row
+    auto xs_of = [&](auto S_) __attribute__((always_inline)) -> uint8_t* {
+        constexpr int S = decltype(S_)::value;
+        if constexpr (S == 0)
+            return xs0;
+        else if constexpr (S == 1)
+            return xs1;
+        else
+            return xs2;
+    };
+    auto sc_of = [&](auto S_) __attribute__((always_inline)) -> float* {
+        constexpr int S = decltype(S_)::value;
+        if constexpr (S == 0)
+            return &sc0[0][0];
+        else if constexpr (S == 1)
+            return &sc1[0][0];
+        else
+            return &sc2[0][0];
+    };
     auto row_of = [&](int pos) __attribute__((always_inline)) -> int32_t {
         if (pos >= c1)
             return -1;
-        if (a.mode == kSelect) {
-            const int32_t r = a.sel[pos];
-            return (r >= 0 && r < a.t_rows) ? r : -1;
-        }
-        return pos;
+        const int32_t r = a.sel[pos];
+        return (r >= 0 && r < a.t_rows) ? r : -1;
     };
-    auto load_tile = [&](int p0) __attribute__((always_inline)) {
+    // Per row DMA i of this wave: r << 16 | (r * d + chunk offset), the same
+    // for every tile, so it is packed once.
+    int dpk[KW];
 #pragma unroll
-        for (int i = 0; i < NPRE; ++i) {
-            pre[i] = make_uint4(0u, 0u, 0u, 0u);
-            if (ld_rc[i] >= 0) {
-                const int32_t row = row_of(p0 + (ld_rc[i] >> 10));
-                if (row >= 0)
-                    pre[i] = *reinterpret_cast<const uint4*>(a.codes + (size_t)row * a.d +
-                                                             (ld_rc[i] & 1023));
+    for (int i = 0; i < KW; ++i) {
+        const int k = (w + NW * i) % NINS;
+        const int slot = 64 * k + lane;
+        const int r = slot / SPR, c = slot - (slot / SPR) * SPR;
+        dpk[i] = (r << 16) | (r * a.d + (c < cpr ? 16 * c : 0));
+    }
+    auto issue = [&](int t, auto S_) __attribute__((always_inline)) {
+        constexpr int st = decltype(S_)::value;
+        uint8_t* xst = xs_of(S_);
+        float* sct = sc_of(S_) + TR * w;
+        const int p0 = c0 + t * TR;
+        if constexpr (!GATHER) {
+            // Contiguous rows p0 .. p0 + nv - 1: SGPR base + 32-bit offsets.
+            // Rows past the list reload the tile's first row.
+            const int nv = c1 - p0;
+            const uint8_t* tb = a.codes + (size_t)p0 * a.d;
+#pragma unroll
+            for (int i = 0; i < KW; ++i) {
+                const int k = (w + NW * i) % NINS;
+                const int r = dpk[i] >> 16;
+                const uint32_t off = (uint32_t)((dpk[i] & 0xFFFF) - (r < nv ? 0 : r * a.d));
+                dma_b128_s(tb, off, xst + 1024 * k);
             }
-        }
-        if (tid < TR) {
-            pre_row = row_of(p0 + tid);
-            pre_scale = pre_row >= 0 ? a.scales[pre_row] : 0.0f;
-        }
-    };
-    auto store_tile = [&](int buf) __attribute__((always_inline)) {
+            dma_b32_s(a.scales + p0, (uint32_t)(4 * (lane < nv ? lane : 0)), sct);
+            if (w == 0)
+                s_row[st][lane] = lane < nv ? p0 + lane : -1;
+        } else {
+            // Gather: absolute row indices; entries outside [0, t_rows) and
+            // positions past the list reload row 0.
 #pragma unroll
-        for (int i = 0; i < NPRE; ++i)
-            if (ld_rc[i] >= 0)
-                *reinterpret_cast<uint4*>(&xs[buf][(ld_rc[i] >> 10) * XS + (ld_rc[i] & 1023)]) =
-                    pre[i];
-        if (tid < TR) {
-            s_scale[buf][tid] = pre_scale;
-            s_lscale[buf][tid] = log2f(pre_scale);  // -inf for a zero scale
-            s_row[buf][tid] = pre_row;
+            for (int i = 0; i < KW; ++i) {
+                const int k = (w + NW * i) % NINS;
+                const int r = dpk[i] >> 16;
+                const int cc = (dpk[i] & 0xFFFF) - r * a.d;
+                const int32_t row = row_of(p0 + r);
+                dma_b128(a.codes + (size_t)(row >= 0 ? row : 0) * a.d + cc, xst + 1024 * k);
+            }
+            const int32_t srow = row_of(p0 + lane);
+            dma_b32(a.scales + (srow >= 0 ? srow : 0), sct);
+            if (w == 0)
+                s_row[st][lane] = srow;
         }
     };
 
@@ -369,21 +504,33 @@ __global__ __launch_bounds__(kThreads, 1) void k_split_partial(AttnArgs a)
     const int cb = 64 * w;  // this wave's context columns
     const bool pv_active = cb < a.lc;
 
-    __syncthreads();  // zero fill done before the first tile lands
-    if (ntiles > 0) {
-        load_tile(c0);
-        store_tile(0);
-    }
-    __syncthreads();
+    using S0 = std::integral_constant<int, 0>;
+    using S1 = std::integral_constant<int, 1>;
+    using S2 = std::integral_constant<int, 2>;
+    if (ntiles > 0)
+        issue(0, S0{});
+    if (ntiles > 1)
+        issue(1, S1{});
 
-    for (int it = 0; it < ntiles; ++it) {
-        const int buf = it & 1;
+    // One tile: wait for its loads, refill the stage freed two tiles ago,
+    // score, update the softmax state, accumulate the context.  Barrier (A)
+    // also publishes the q low part written before the first tile.
+    auto tile = [&](int it, auto S_) __attribute__((always_inline)) {
+        constexpr int st = decltype(S_)::value;
+        const uint8_t* xst = xs_of(S_);
+        const float* scs = sc_of(S_) + TR * w;
+        // Tile it is complete once only tile it+1's operations may remain.
         if (it + 1 < ntiles)
-            load_tile(c0 + (it + 1) * TR);
+            wait_vmcnt<NVM>();
+        else
+            wait_vmcnt<0>();
+        lds_barrier();  // (A) tile it visible to all waves; stage (it+2)%3 free
+        if (it + 2 < ntiles)
+            issue(it + 2, std::integral_constant<int, (st + 2) % NST>{});
 
         // ---- scores: S^T[16 rows][16 heads]
         f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-        const uint8_t* xrow = &xs[buf][(16 * rq + n) * XS + 16 * g];
+        const uint8_t* xrow = xst + (16 * rq + n) * XS + 16 * g;
 #pragma unroll
         for (int i = 0; i < NKB2; ++i) {
             const uint4 x0 = *reinterpret_cast<const uint4*>(xrow + 128 * i);
@@ -398,11 +545,11 @@ __global__ __launch_bounds__(kThreads, 1) void k_split_partial(AttnArgs a)
             }
             const v8i x8 = v8i{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w,
                                (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
-            acc = mfma_fp8_scaled(x8, qlo[i], acc, 127 - kQloShift);
+            acc = mfma_fp8_scaled(x8, qlo[i * 64 + lane], acc, 127 - kQloShift);
         }
 
-        // ---- log2-domain scores u (rows 16rq + 4g + v, head 16hh + n); per wave:
-        // the tile max Tw of u and Cw = max_t (u_t - Tw) + log2 scale_t.
+        // ---- log2-domain scores u (rows 16rq + 4g + v, head 16hh + n); per
+        // wave: the tile max Tw of u and Cw = max_t (u_t - Tw) + log2 scale_t.
         // Everything after this stays relative to a running max, so a large
         // |u| never swallows log2 scale.
         float u[4], lsv[4];
@@ -410,9 +557,9 @@ __global__ __launch_bounds__(kThreads, 1) void k_split_partial(AttnArgs a)
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
             const int r = 16 * rq + 4 * g + v;
-            const float sc = s_scale[buf][r];
-            lsv[v] = s_lscale[buf][r];
-            const int32_t row = s_row[buf][r];
+            const float sc = scs[r];
+            lsv[v] = log2f(sc);  // -inf for a zero scale
+            const int32_t row = s_row[st][r];
             const bool valid = row >= 0 && row < tlim;
             u[v] = valid ? (acc[v] * hfac) * sc : -INFINITY;
             tw = fmaxf(tw, u[v]);
@@ -431,7 +578,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_split_partial(AttnArgs a)
             s_red[rq][0][16 * hh + n] = tw;
             s_red[rq][1][16 * hh + n] = cw;
         }
-        __syncthreads();
+        lds_barrier();  // (B) per-wave maxima exchanged
 
         // ---- running state for heads n, 16 + n (every wave computes both)
         float alz[2], alo[2];
@@ -489,7 +636,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_split_partial(AttnArgs a)
                         O[ht][jm][v] *= f;
                 }
         }
-        __syncthreads();  // weight tile complete
+        lds_barrier();  // (C) weight tile complete; s_red free
 
         // ---- context: O[32 heads][64 cols of this wave] += W . X.  Lane (n, g)
         // reads rows 32ks + 8g + 0..7, columns cb + 4n .. +4, and byte-transposes
@@ -507,7 +654,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_split_partial(AttnArgs a)
 #pragma unroll
                 for (int v = 0; v < 8; ++v)
                     xr[v] = *reinterpret_cast<const uint32_t*>(
-                        &xs[buf][(32 * ks + 8 * g + v) * XS + cb + 4 * n]);
+                        xst + (32 * ks + 8 * g + v) * XS + cb + 4 * n);
 #pragma unroll
                 for (int jp = 0; jp < 2; ++jp) {
                     // columns 2jp and 2jp+1: bytes [r0.c, r1.c, r0.c+1, r1.c+1]
@@ -531,10 +678,14 @@ __global__ __launch_bounds__(kThreads, 1) void k_split_partial(AttnArgs a)
                 }
             }
         }
+    };
 
+    for (int it = 0; it < ntiles; it += NST) {
+        tile(it, S0{});
         if (it + 1 < ntiles)
-            store_tile(buf ^ 1);
-        __syncthreads();
+            tile(it + 1, S1{});
+        if (it + 2 < ntiles)
+            tile(it + 2, S2{});
     }
 
     // ---- epilogue: z over lane groups and row quarters; partial (m, z, cl)
@@ -576,34 +727,75 @@ __global__ __launch_bounds__(kThreads, 1) void k_split_partial(AttnArgs a)
 
 // ---------------------------------------------------------------------------
 // Log-sum-exp merge of the n_chunks partials of every query-head.
-// Grid (n_qh, ceil(lc / 64)), one wave per block, one column per lane.
-__global__ __launch_bounds__(64) void k_merge(const float* __restrict__ ws_m,
-                                              const float* __restrict__ ws_z,
-                                              const float* __restrict__ ws_cl, int32_t n_chunks,
-                                              int32_t n_qh, int32_t lc, float* __restrict__ out,
-                                              float* __restrict__ lse)
+// Grid (n_qh, ceil(lc / 64)), 256 threads: lane = context column, the four
+// waves split the partials (p = wave, wave + 4, ...) with independent,
+// unrolled loads, then combine through LDS.
+//   M = max_p m_p;  w_p = 2^(m_p - M);  out = sum_p w_p cl_p / sum_p w_p z_p;
+//   lse = (M + log2 sum_p w_p z_p) * ln 2.
+__global__ __launch_bounds__(256) void k_merge(const float* __restrict__ ws_m,
+                                               const float* __restrict__ ws_z,
+                                               const float* __restrict__ ws_cl, int32_t n_chunks,
+                                               int32_t n_qh, int32_t lc, float* __restrict__ out,
+                                               float* __restrict__ lse)
 {
+    __shared__ float s_part[4][64];
+    __shared__ float s_zp[4];
+    __shared__ float s_m[4];
     const int qh = blockIdx.x;
-    const int col = blockIdx.y * 64 + threadIdx.x;
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int col = blockIdx.y * 64 + lane;
+    // M over all partials
     float M = -INFINITY;
-    for (int p = 0; p < n_chunks; ++p)
+    for (int p = threadIdx.x; p < n_chunks; p += 256)
         M = fmaxf(M, ws_m[(size_t)p * n_qh + qh]);
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1)
+        M = fmaxf(M, __shfl_xor(M, off));
+    if (lane == 0)
+        s_m[wv] = M;
+    __syncthreads();
+    M = fmaxf(fmaxf(s_m[0], s_m[1]), fmaxf(s_m[2], s_m[3]));
     float Z = 0.0f, acc = 0.0f;
     if (M != -INFINITY) {
-        for (int p = 0; p < n_chunks; ++p) {
-            const float mp = ws_m[(size_t)p * n_qh + qh];
-            if (mp == -INFINITY)
-                continue;
-            const float wgt = exp2f(mp - M);
-            Z += wgt * ws_z[(size_t)p * n_qh + qh];
-            if (col < lc)
-                acc += wgt * ws_cl[((size_t)p * n_qh + qh) * lc + col];
+        const bool cv = col < lc;
+        int p = wv;
+        for (; p + 12 < n_chunks; p += 16) {
+            float mp[4], zp[4], cp[4];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const size_t i = (size_t)(p + 4 * k) * n_qh + qh;
+                mp[k] = ws_m[i];
+                zp[k] = ws_z[i];
+                cp[k] = cv ? ws_cl[i * lc + col] : 0.0f;
+            }
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const float wgt = (mp[k] == -INFINITY) ? 0.0f : exp2f(mp[k] - M);
+                Z += wgt * zp[k];
+                acc += wgt * cp[k];
+            }
+        }
+        for (; p < n_chunks; p += 4) {
+            const size_t i = (size_t)p * n_qh + qh;
+            const float mp = ws_m[i];
+            const float wgt = (mp == -INFINITY) ? 0.0f : exp2f(mp - M);
+            Z += wgt * ws_z[i];
+            if (cv)
+                acc += wgt * ws_cl[i * lc + col];
         }
     }
-    if (col < lc)
-        out[(size_t)qh * lc + col] = (M == -INFINITY) ? 0.0f : acc / Z;
-    if (lse != nullptr && blockIdx.y == 0 && threadIdx.x == 0)
-        lse[qh] = (M == -INFINITY) ? -INFINITY : (M + log2f(Z)) * 0.69314718055994531f;
+    s_part[wv][lane] = acc;
+    if (lane == 0)
+        s_zp[wv] = Z;
+    __syncthreads();
+    if (wv == 0) {
+        const float A = (s_part[0][lane] + s_part[1][lane]) + (s_part[2][lane] + s_part[3][lane]);
+        const float ZZ = (s_zp[0] + s_zp[1]) + (s_zp[2] + s_zp[3]);
+        if (col < lc)
+            out[(size_t)qh * lc + col] = (M == -INFINITY) ? 0.0f : A / ZZ;
+        if (lse != nullptr && blockIdx.y == 0 && lane == 0)
+            lse[qh] = (M == -INFINITY) ? -INFINITY : (M + log2f(ZZ)) * 0.69314718055994531f;
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -630,8 +822,12 @@ hipError_t launch_test_encode(const float* x, int64_t n, uint8_t* codes, hipStre
 template <int NKB>
 static void launch_partial(const AttnArgs& a, hipStream_t stream)
 {
-    hipLaunchKernelGGL(k_split_partial<NKB>, dim3((unsigned)(a.n_chunks * a.n_groups)),
-                       dim3(kThreads), 0, stream, a);
+    if (a.mode == kSelect)
+        hipLaunchKernelGGL((k_split_partial<NKB, true>), dim3((unsigned)(a.n_chunks * a.n_groups)),
+                           dim3(kThreads), 0, stream, a);
+    else
+        hipLaunchKernelGGL((k_split_partial<NKB, false>),
+                           dim3((unsigned)(a.n_chunks * a.n_groups)), dim3(kThreads), 0, stream, a);
 }
 
 hipError_t launch_attention(const AttnArgs& a, hipStream_t stream, hipEvent_t ev_before,
@@ -668,7 +864,7 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t stream, hipEvent_t ev
         if (e != hipSuccess)
             return e;
     }
-    hipLaunchKernelGGL(k_merge, dim3((unsigned)a.n_qh, (unsigned)((a.lc + 63) / 64)), dim3(64), 0,
+    hipLaunchKernelGGL(k_merge, dim3((unsigned)a.n_qh, (unsigned)((a.lc + 63) / 64)), dim3(256), 0,
                        stream, a.ws_m, a.ws_z, a.ws_cl, a.n_chunks, a.n_qh, a.lc, a.out, a.lse);
     return hipGetLastError();
 }
