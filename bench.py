@@ -94,14 +94,16 @@ def main():
     import torch
 
     if args.calibrate_copy:
-        # A plain copy of known size: 1 GiB read + 1 GiB written per launch.
-        # rocprofv3 FETCH_SIZE / WRITE_SIZE of this kernel calibrate the same
-        # counters taken on the attention kernels.
+        # A plain copy kernel of known size: 1 GiB read + 1 GiB written per
+        # launch (an elementwise kernel, so the counter collection sees it; a
+        # same-dtype copy_ would go to the DMA engines).  rocprofv3
+        # FETCH_SIZE / WRITE_SIZE of this kernel calibrate the same counters
+        # taken on the attention kernels.
         n = 1 << 30
         src = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
         dst = torch.empty_like(src)
         for _ in range(max(args.steps, 1)):
-            dst.copy_(src)
+            torch.bitwise_not(src, out=dst)
         torch.cuda.synchronize()
         print(json.dumps({"calibrate_copy_bytes": n, "launches": max(args.steps, 1)}))
         return
