@@ -231,7 +231,7 @@ def main():
         "higher_is_better": False,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "e4m3 kv, f16+e4m3 mfma, f32 accumulate",
+        "dtype": "e4m3 kv; scores e4m3 x 3-term e4m3 q (fp8 mfma), context f16 weights x e4m3->f16 rows (f16 mfma); f32 accumulate",
         "data": "synthetic: seeded N(0,1) rows and queries",
         "config": {"workload": w.name, "heads": w.n_heads, "kv_lora": w.lc, "rope": w.rc,
                    "t_rows": T, "batch": 1, "layers_per_step": L,

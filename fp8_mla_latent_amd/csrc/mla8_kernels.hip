@@ -17,17 +17,17 @@
 //     placed on the same XCD so the second head group hits that XCD's L2.
 //   * Rows stream HBM -> LDS in 64-row tiles through a 3-stage ring of direct
 //     global_load_lds_dwordx4 loads (two tiles in flight, no register
-//     staging).  e4m3 bytes are widened to fp16 in registers with
-//     v_cvt_scalef32_pk_f16_fp8 (exact: every e4m3 value is an fp16 normal),
-//     then fed to v_mfma_f32_16x16x32_f16.
+//     staging).
 //   * 8 waves per workgroup (two per SIMD).  Scores S^T[row][head] = X . Q^T:
-//     each wave takes 16 rows x 16 heads; q is split into an fp16 high part
-//     held in registers (fp16 MFMA) and an e4m3 low part held in LDS (scaled
-//     fp8 MFMA straight on the row bytes), with a power of two per head so it
-//     sits in fp16's range.
+//     each wave takes 16 rows x 16 heads on the scaled fp8 MFMA, straight on
+//     the e4m3 row bytes; the query is split into three e4m3 terms (about 12
+//     significant bits) held in registers, each with a per-head E8M0 operand
+//     scale.
 //   * Context O[head][col] += W . X: each wave owns a 64-column slice for all
-//     32 heads, reading a 4x8 byte block per lane and transposing it with
-//     v_perm_b32 so the row (contraction) index becomes the MFMA K index.
+//     32 heads; ds_read_b64_tr_b8 reads the row bytes transposed so the row
+//     (contraction) index becomes the MFMA K index, and v_cvt_scalef32_pk_f16_fp8
+//     widens them to fp16 exactly (every e4m3 value is an fp16 normal) for
+//     v_mfma_f32_16x16x32_f16 with fp16 weights.
 //   * The row scale is hoisted: scores are (q . code) * scale_t, and the PV
 //     weight of row t is exp2((u_t - m) + log2 scale_t - d) with d a running
 //     max kept relative to the score max m, so fp16 weights never overflow or
@@ -154,106 +154,121 @@ __device__ __forceinline__ f32x4 mfma_fp8_scaled(v8i a, v8i b, f32x4 c, int32_t 
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// Source of the 16 query elements d = 64j + 16g .. +16 of query-head qh, and
-// whether they exist (false past the row width or past the last head; the
-// pointer then still addresses valid memory, the first q_lat row, so that every
-// load can be issued unconditionally and many can be in flight at once).
-struct QSrc {
-    const float* p;
-    bool ok;
-};
-
-__device__ __forceinline__ QSrc q_src(const AttnArgs& a, int qh, bool hv, int j, int g)
-{
-    const int d0 = 64 * j + 16 * g;
-    if (hv && d0 < a.lc)
-        return {a.q_lat + (size_t)qh * a.lc + d0, true};
-    if (hv && d0 < a.d)
-        return {a.q_rope + (size_t)qh * a.rc + (d0 - a.lc), true};
-    return {a.q_lat, false};
-}
-
-__device__ __forceinline__ float4 ld4(const QSrc& s, int k)
-{
-    const float4 v = reinterpret_cast<const float4*>(s.p)[k];
-    return s.ok ? v : make_float4(0.f, 0.f, 0.f, 0.f);
-}
-
-// Query operands for 16 heads.  Lane (n, g) holds, for head qh_base + n, the
-// elements d = 64j + 16g + e (e < 16).  The same assignment of the contraction
-// index to (lane group, operand slot) is used for the row operand, so the MFMA
-// sums the right products whatever its K labels are.
-//   qhi: fp16(q * 2^k)                 two f16x8 per j      -> fp16 MFMA,
-//        kept in registers;
-//   qlo: e4m3((q*2^k - qhi) * 2^6)     32 bytes per j pair  -> fp8 MFMA, whose
-//        E8M0 operand scale 2^-6 undoes the 2^6 inside the instruction; written
-//        lane-linear to LDS (qlo_lds[i][lane], 32 bytes) when write_lo is set.
-// k puts the head's largest |q| in [2^13, 2^14), where the fp16 spacing is 8,
-// so every residual is at most 4 and 2^6 * 4 = 256 sits inside e4m3's range.
-// Every index is a compile-time constant so qhi stays in registers.
-constexpr int kQloShift = 6;
+// ---------------------------------------------------------------------------
+// Query operands: three e4m3 terms per element.
+//
+// Each query-head's vector e = (q_lat | q_rope) * sm_scale * log2(e) is scaled
+// by a power of two 2^k that puts its largest |element| in [2^7, 2^8) and
+// split as
+//     t1 = e4m3(e 2^k),  t2 = e4m3(16 (e 2^k - t1)),  t3 = e4m3(16 (16 (e 2^k - t1) - t2)),
+// so e 2^k = t1 + t2 / 16 + t3 / 256 to about 12 significant bits (every
+// subtraction is exact in f32; v_cvt_pk_fp8_f32 rounds to nearest even).  The
+// terms run on the scaled fp8 MFMA straight against the e4m3 row bytes, each
+// with the per-lane E8M0 operand scale 2^(-k - 4 t) of its head, so the f32
+// accumulator holds the log2-domain score in code units and no row byte is
+// converted for the scores.
+//
+// Operand slots: a full 128-element block j holds slots 3j + t (term t).  When
+// the padded row ends with half a block (64 elements), that block packs two
+// slots: lanes g < 2 carry t1 and lanes g >= 2 carry t2 of the same elements
+// (the row operand repeats those bytes there), then t3 | zeros.
+//
+// The terms are built once per workgroup into an LDS staging area laid out as
+// the waves consume them: qt[head half][slot][lane][32 bytes], lane n + 16 g
+// holding head 16 hh + n, elements d = 128 j + 32 g + b (b < 32), zero past
+// the row width.  The row operand uses the same (g, b) -> d assignment, so the
+// MFMA pairs matching elements whatever order it gives its K index.
+constexpr int kTermShift = 4;
 
 template <int NKB>
-__device__ __forceinline__ void load_query(const AttnArgs& a, int qh_base, int n, int g, int lane,
-                                           f16x8 (&qhi)[NKB][2], v8i* qlo_lds, bool write_lo,
-                                           float& hfac, int32_t& tlim)
+struct QueryTerms {
+    static constexpr int NB = (NKB + 1) / 2;    // 128-wide K blocks
+    static constexpr bool HALF = (NKB & 1) != 0;  // last block half filled
+    static constexpr int NFULL = HALF ? NB - 1 : NB;
+    static constexpr int NSLOT = 3 * NFULL + (HALF ? 2 : 0);
+    static constexpr int BYTES = 2 * NSLOT * 64 * 32;
+};
+
+template <int NKB>
+__device__ __forceinline__ void build_query_terms(const AttnArgs& a, int qh0, uint8_t* qt,
+                                                  int* s_k)
 {
-    const int qh = qh_base + n;
+    using Q = QueryTerms<NKB>;
+    // Thread t handles head h = t / 16 (16 threads per head, all in one wave)
+    // and the 4-element groups gi = t % 16 + 16 s of that head.
+    constexpr int PER = 2 * Q::NB;  // groups per thread: NB blocks x 32 groups / 16 threads
+    const int h = threadIdx.x >> 4, i = threadIdx.x & 15;
+    const int qh = qh0 + h;
     const bool hv = qh < a.n_qh;
+    float4 v[PER];
     float amax = 0.0f;
 #pragma unroll
-    for (int j = 0; j < NKB; ++j) {
-        const QSrc src = q_src(a, qh, hv, j, g);
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            const float4 v = ld4(src, k);
-            amax = fmaxf(amax, fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
+    for (int s = 0; s < PER; ++s) {
+        const int d = 4 * (i + 16 * s);
+        const float* p = a.q_lat;  // always a valid address
+        bool ok = false;
+        if (hv && d < a.lc) {
+            p = a.q_lat + (size_t)qh * a.lc + d;
+            ok = true;
+        } else if (hv && d < a.d) {
+            p = a.q_rope + (size_t)qh * a.rc + (d - a.lc);
+            ok = true;
         }
+        const float4 x = *reinterpret_cast<const float4*>(p);
+        v[s] = ok ? x : make_float4(0.f, 0.f, 0.f, 0.f);
+        amax = fmaxf(amax, fmaxf(fmaxf(fabsf(v[s].x), fabsf(v[s].y)),
+                                 fmaxf(fabsf(v[s].z), fabsf(v[s].w))));
     }
-    amax = fmaxf(amax, __shfl_xor(amax, 16));
-    amax = fmaxf(amax, __shfl_xor(amax, 32));
+#pragma unroll
+    for (int off = 8; off > 0; off >>= 1)
+        amax = fmaxf(amax, __shfl_xor(amax, off));
+    // e = q * sm log2(e); k from the largest |e| (computed in f32 like e)
+    const float es = a.sm_log2;
     int ex = 0;
-    if (amax > 0.0f)
-        (void)frexpf(amax, &ex);
-    // amax * 2^k2 in [2^13, 2^14); clamped so 2^k2 and 2^-k2 stay normal
-    const int k2 = min(max(14 - ex, -126), 126);
-    const float mult = ldexpf(1.0f, k2);
-    const float lmult = (float)(1 << kQloShift);
-    hfac = a.sm_log2 * ldexpf(1.0f, -k2);
-    tlim = (a.mode == kCausal) ? a.pos0 + (hv ? qh / a.n_heads : 0) + 1 : 0x7FFFFFFF;
-    int lo[8];
+    const float emax = amax * es;
+    if (emax > 0.0f)
+        (void)frexpf(emax, &ex);
+    // |e| 2^k in [2^7, 2^8); k <= 119 keeps every term scale 2^(-k - 8) an
+    // E8M0 value (heads below 2^-112 then keep fewer bits, irrelevant next to
+    // any score they could produce); k >= -120 since |e| < 2^128.
+    const int k = (emax > 0.0f) ? min(8 - ex, 119) : 0;
+    if (i == 0)
+        s_k[h] = k;
+    const float mult = ldexpf(es, k);  // e 2^k = q * mult up to one rounding
+    const int hh = h >> 4, n = h & 15;
+    uint8_t* base = qt + (size_t)hh * Q::NSLOT * 64 * 32;
 #pragma unroll
-    for (int j = 0; j < NKB; ++j) {
-        const QSrc src = q_src(a, qh, hv, j, g);
+    for (int s = 0; s < PER; ++s) {
+        const int gi = i + 16 * s;  // elements d = 4 gi .. 4 gi + 3
+        const int j = gi >> 5, g = (gi >> 3) & 3, b = 4 * (gi & 7);
+        float r[4] = {v[s].x * mult, v[s].y * mult, v[s].z * mult, v[s].w * mult};
+        int wd[3];
 #pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-            const float4 v0 = ld4(src, 2 * hh), v1 = ld4(src, 2 * hh + 1);
-            const float e[8] = {v0.x * mult, v0.y * mult, v0.z * mult, v0.w * mult,
-                                v1.x * mult, v1.y * mult, v1.z * mult, v1.w * mult};
-            f16x8 hi;
-            float r[8];
-#pragma unroll
-            for (int q = 0; q < 8; ++q) {
-                hi[q] = (_Float16)e[q];
-                r[q] = (e[q] - (float)hi[q]) * lmult;  // exact: |r| <= 256
+        for (int t = 0; t < 3; ++t) {
+            wd[t] = __builtin_amdgcn_cvt_pk_fp8_f32(r[0], r[1], 0, false);
+            wd[t] = __builtin_amdgcn_cvt_pk_fp8_f32(r[2], r[3], wd[t], true);
+            if (t < 2) {
+                const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8(wd[t], false);
+                const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8(wd[t], true);
+                r[0] = (r[0] - lo[0]) * 16.0f;
+                r[1] = (r[1] - lo[1]) * 16.0f;
+                r[2] = (r[2] - hi[0]) * 16.0f;
+                r[3] = (r[3] - hi[1]) * 16.0f;
             }
-            qhi[j][hh] = hi;
-            // v_cvt_pk_fp8_f32 rounds to nearest even onto OCP e4m3
-            int w0 = __builtin_amdgcn_cvt_pk_fp8_f32(r[0], r[1], 0, false);
-            w0 = __builtin_amdgcn_cvt_pk_fp8_f32(r[2], r[3], w0, true);
-            int w1 = __builtin_amdgcn_cvt_pk_fp8_f32(r[4], r[5], 0, false);
-            w1 = __builtin_amdgcn_cvt_pk_fp8_f32(r[6], r[7], w1, true);
-            lo[4 * (j & 1) + 2 * hh] = w0;
-            lo[4 * (j & 1) + 2 * hh + 1] = w1;
         }
-        if ((j & 1) || j == NKB - 1) {
-            if (!(j & 1))
+        auto put = [&](int slot, int gl, int val) __attribute__((always_inline)) {
+            *reinterpret_cast<int*>(base + ((slot * 64 + n + 16 * gl) * 32 + b)) = val;
+        };
+        if (!Q::HALF || j < Q::NFULL) {
 #pragma unroll
-                for (int k = 4; k < 8; ++k)
-                    lo[k] = 0;
-            if (write_lo)
-                qlo_lds[(j >> 1) * 64 + lane] =
-                    v8i{lo[0], lo[1], lo[2], lo[3], lo[4], lo[5], lo[6], lo[7]};
+            for (int t = 0; t < 3; ++t)
+                put(3 * j + t, g, wd[t]);
+        } else if (g < 2) {
+            put(3 * Q::NFULL, g, wd[0]);
+            put(3 * Q::NFULL, g + 2, wd[1]);
+            put(3 * Q::NFULL + 1, g, wd[2]);
+        } else {
+            put(3 * Q::NFULL + 1, g, 0);  // elements past the padded row: zero
         }
     }
 }
@@ -335,45 +350,86 @@ __device__ __forceinline__ void dma_b32_s(const void* base, uint32_t voff, const
 }
 #pragma clang diagnostic pop
 
+// Byte offsets of the split-T partial kernel's LDS objects (one array, so the
+// query-term staging area can reuse ring stages 1 and 2 before they fill).
+template <int NKB>
+struct PartialLds {
+    static constexpr int TR = kTileRows;
+    static constexpr int NW = kThreads / 64;
+    static constexpr int HG = kHeadsPerGroup;
+    static constexpr int NB = (NKB + 1) / 2;  // 128-wide K blocks of the scores
+    static constexpr int XS = 64 * NKB + 16;  // row stride: padded row + one 16-B pad slot
+    static constexpr int SPR = XS / 16;       // 16-byte slots per LDS row
+    static constexpr int STAGE = TR * XS;     // one ring stage (a whole number of KB)
+    static constexpr int WSS = TR + 8;        // weight-tile stride (halves)
+    static constexpr int SC = 3 * STAGE;                   // f32 [3 stages][NW waves][TR]
+    static constexpr int ROW = SC + 3 * NW * TR * 4;       // i32 [3][TR] (gather rows)
+    static constexpr int W = ROW + 3 * TR * 4;             // f16 [HG][WSS]
+    static constexpr int RED = W + HG * WSS * 2;           // float2 [HG][4 row quarters]
+    static constexpr int Z = RED + HG * 4 * 8;             // f32 [4][HG]
+    static constexpr int HK = Z + 4 * HG * 4;              // i32 [HG] query exponent k
+    static constexpr int END = HK + HG * 4;
+    static constexpr int QT_BYTES = QueryTerms<NKB>::BYTES;  // query terms, both head halves
+    static constexpr int QT = (STAGE + QT_BYTES <= SC) ? STAGE : END;
+    static constexpr int TOTAL = (QT + QT_BYTES > END) ? QT + QT_BYTES : END;
+    static_assert(STAGE % 1024 == 0, "stages are whole DMA blocks");
+    static_assert(TOTAL <= 160 * 1024, "LDS budget");
+};
+
+// max(x, x of lane ^ 16) and max(x, x of lane ^ 32) without LDS traffic.
+__device__ __forceinline__ float max_xor16(float x)
+{
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                    false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float max_xor32(float x)
+{
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                    false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+// Value of quad lane V broadcast to the four lanes of every quad.
+template <int V>
+__device__ __forceinline__ float quad_bcast(float x)
+{
+    return __int_as_float(
+        __builtin_amdgcn_mov_dpp(__float_as_int(x), V * 0x55, 0xF, 0xF, false));
+}
+
+typedef int v2i __attribute__((ext_vector_type(2)));
+
 // Split-T partial.  Grid: n_chunks * n_groups workgroups of 512 threads (8
-// waves, two per SIMD).  NKB = number of 64-wide blocks of the padded row.
+// waves, two per SIMD).  NKB = number of 64-byte blocks of the padded row.
 //   loads  : 64-row tiles stream HBM -> LDS through a 3-stage ring of direct
 //            global_load_lds_dwordx4 (no register staging), two tiles in
 //            flight while a third is consumed;
 //   scores : wave w takes rows 16*(w>>1) .. +16 of the tile and heads
-//            16*(w&1) .. +16 of the group (fp16 high part of q in registers,
-//            e4m3 low part in LDS);
-//   context: wave w owns context columns 64*w .. +64 for all 32 heads.
+//            16*(w&1) .. +16 of the group: 3 e4m3 query terms in registers x
+//            the raw e4m3 row bytes on the scaled fp8 MFMA;
+//   context: wave w owns context columns 64*w .. +64 for all 32 heads; the
+//            row bytes are read transposed (ds_read_b64_tr_b8) so the row
+//            index lands on the MFMA K index, widened to fp16 exactly.
 template <int NKB, bool GATHER>
 __global__ __launch_bounds__(kThreads, 1) void k_split_partial(AttnArgs a)
 {
-    constexpr int TR = kTileRows;
-    constexpr int HG = kHeadsPerGroup;
-    constexpr int NW = kThreads / 64;    // waves
-    constexpr int DP = 64 * NKB;         // padded row width in LDS (>= d, >= roundup(lc, 128))
-    constexpr int XS = DP + 16;          // LDS row stride: DP bytes + one 16-B pad slot
-    constexpr int SPR = XS / 16;         // 16-byte slots per LDS row
-    constexpr int NINS = SPR;            // 1-KB DMA instructions per tile (64 rows x SPR slots)
+    using L = PartialLds<NKB>;
+    constexpr int TR = L::TR, NW = L::NW, HG = L::HG, NB = L::NB, XS = L::XS, SPR = L::SPR;
+    constexpr int WSS = L::WSS;
+    constexpr int NINS = SPR;                 // 1-KB DMA instructions per tile
     constexpr int KW = (NINS + NW - 1) / NW;  // row DMA instructions per wave per tile
-    constexpr int NVM = KW + 1;          // + one scale DMA: vector-memory ops per wave per tile
-    constexpr int NST = 3;               // ring stages
-    constexpr int WSS = TR + 8;          // LDS stride of the weight tile (halves)
-    constexpr int NKB2 = (NKB + 1) / 2;  // 128-wide blocks for the fp8 pass
+    constexpr int NVM = KW + 1;               // + one scale DMA per wave
+    constexpr int NST = 3;                    // ring stages
     static_assert(TR * XS == NINS * 1024, "a stage is a whole number of 1-KB DMA blocks");
     static_assert(NVM < 64, "vmcnt range");
 
-    // One object per ring stage: the compiler tracks memory per object.
-    __shared__ __attribute__((aligned(1024))) uint8_t xs0[TR * XS];
-    __shared__ __attribute__((aligned(1024))) uint8_t xs1[TR * XS];
-    __shared__ __attribute__((aligned(1024))) uint8_t xs2[TR * XS];
-    __shared__ __attribute__((aligned(16))) float sc0[NW][TR];  // per-wave copies of the scales
-    __shared__ __attribute__((aligned(16))) float sc1[NW][TR];
-    __shared__ __attribute__((aligned(16))) float sc2[NW][TR];
-    __shared__ int32_t s_row[NST][TR];
-    __shared__ __attribute__((aligned(16))) _Float16 s_w[HG * WSS];
-    __shared__ __attribute__((aligned(32))) v8i s_qlo[2][NKB2 * 64];  // [head half][block][lane]
-    __shared__ float s_red[4][2][HG];
-    __shared__ float s_z[4][HG];
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[L::TOTAL];
+    float* const s_sc = reinterpret_cast<float*>(lds + L::SC);
+    int32_t* const s_row = reinterpret_cast<int32_t*>(lds + L::ROW);
+    _Float16* const s_w = reinterpret_cast<_Float16*>(lds + L::W);
+    float2* const s_red = reinterpret_cast<float2*>(lds + L::RED);
+    float* const s_z = reinterpret_cast<float*>(lds + L::Z);
+    int* const s_k = reinterpret_cast<int*>(lds + L::HK);
 
     const int tid = threadIdx.x;
     const int w = tid >> 6, lane = tid & 63, n = lane & 15, g = lane >> 4;
@@ -399,14 +455,6 @@ __global__ __launch_bounds__(kThreads, 1) void k_split_partial(AttnArgs a)
     const int c1 = min(a.n_list, c0 + a.chunk_rows);
     const int ntiles = c1 > c0 ? (c1 - c0 + TR - 1) / TR : 0;
 
-    // ---- query operands for heads qh0 + 16*hh + n (the low part is written
-    // to LDS by the row-quarter-0 wave of each head half)
-    f16x8 qhi[NKB][2];
-    float hfac;
-    int32_t tlim;
-    load_query<NKB>(a, qh0 + 16 * hh, n, g, lane, qhi, &s_qlo[hh][0], rq == 0, hfac, tlim);
-    const v8i* qlo = &s_qlo[hh][0];
-
     // ---- tile issue: every wave issues exactly NVM vector-memory operations
     // per tile (so a fixed vmcnt marks a tile complete).  Row DMA instruction k
     // fills LDS bytes [1024k, 1024k + 1024) of the stage: slot 64k + lane is
@@ -417,24 +465,6 @@ __global__ __launch_bounds__(kThreads, 1) void k_split_partial(AttnArgs a)
     // read.  Spare instruction slots (k >= NINS) repeat instruction k % NINS
     // (the same bytes to the same place).
     const int cpr = a.d >> 4;  // 16-byte data chunks per row
-    auto xs_of = [&](auto S_) __attribute__((always_inline)) -> uint8_t* {
-        constexpr int S = decltype(S_)::value;
-        if constexpr (S == 0)
-            return xs0;
-        else if constexpr (S == 1)
-            return xs1;
-        else
-            return xs2;
-    };
-    auto sc_of = [&](auto S_) __attribute__((always_inline)) -> float* {
-        constexpr int S = decltype(S_)::value;
-        if constexpr (S == 0)
-            return &sc0[0][0];
-        else if constexpr (S == 1)
-            return &sc1[0][0];
-        else
-            return &sc2[0][0];
-    };
     auto row_of = [&](int pos) __attribute__((always_inline)) -> int32_t {
         if (pos >= c1)
             return -1;
@@ -451,26 +481,33 @@ __global__ __launch_bounds__(kThreads, 1) void k_split_partial(AttnArgs a)
         const int r = slot / SPR, c = slot - (slot / SPR) * SPR;
         dpk[i] = (r << 16) | (r * a.d + (c < cpr ? 16 * c : 0));
     }
-    auto issue = [&](int t, auto S_) __attribute__((always_inline)) {
-        constexpr int st = decltype(S_)::value;
-        uint8_t* xst = xs_of(S_);
-        float* sct = sc_of(S_) + TR * w;
+    auto issue = [&](int t, int st) __attribute__((always_inline)) {
+        uint8_t* xst = lds + st * L::STAGE;
+        float* sct = s_sc + (st * NW + w) * TR;
         const int p0 = c0 + t * TR;
         if constexpr (!GATHER) {
             // Contiguous rows p0 .. p0 + nv - 1: SGPR base + 32-bit offsets.
             // Rows past the list reload the tile's first row.
             const int nv = c1 - p0;
             const uint8_t* tb = a.codes + (size_t)p0 * a.d;
+            if (nv >= TR) {
 #pragma unroll
-            for (int i = 0; i < KW; ++i) {
-                const int k = (w + NW * i) % NINS;
-                const int r = dpk[i] >> 16;
-                const uint32_t off = (uint32_t)((dpk[i] & 0xFFFF) - (r < nv ? 0 : r * a.d));
-                dma_b128_s(tb, off, xst + 1024 * k);
+                for (int i = 0; i < KW; ++i) {
+                    const int k = (w + NW * i) % NINS;
+                    dma_b128_s(tb, (uint32_t)(dpk[i] & 0xFFFF), xst + 1024 * k);
+                }
+                dma_b32_s(a.scales + p0, (uint32_t)(4 * lane), sct);
+            } else {
+#pragma unroll
+                for (int i = 0; i < KW; ++i) {
+                    const int k = (w + NW * i) % NINS;
+                    const int r = dpk[i] >> 16;
+                    const uint32_t off =
+                        (uint32_t)((dpk[i] & 0xFFFF) - (r < nv ? 0 : r * a.d));
+                    dma_b128_s(tb, off, xst + 1024 * k);
+                }
+                dma_b32_s(a.scales + p0, (uint32_t)(4 * (lane < nv ? lane : 0)), sct);
             }
-            dma_b32_s(a.scales + p0, (uint32_t)(4 * (lane < nv ? lane : 0)), sct);
-            if (w == 0)
-                s_row[st][lane] = lane < nv ? p0 + lane : -1;
         } else {
             // Gather: absolute row indices; entries outside [0, t_rows) and
             // positions past the list reload row 0.
@@ -485,9 +522,39 @@ __global__ __launch_bounds__(kThreads, 1) void k_split_partial(AttnArgs a)
             const int32_t srow = row_of(p0 + lane);
             dma_b32(a.scales + (srow >= 0 ? srow : 0), sct);
             if (w == 0)
-                s_row[st][lane] = srow;
+                s_row[st * TR + lane] = srow;
         }
     };
+
+    if (ntiles > 0)
+        issue(0, 0);
+
+    // ---- query terms for the group, staged in LDS (over ring stages 1-2 when
+    // they fit there), then each wave keeps its head half's in registers
+    using Q = QueryTerms<NKB>;
+    build_query_terms<NKB>(a, qh0, lds + L::QT, s_k);
+    lds_barrier();
+    v8i qv[Q::NSLOT];
+#pragma unroll
+    for (int sl = 0; sl < Q::NSLOT; ++sl)
+        qv[sl] = *reinterpret_cast<const v8i*>(
+            lds + L::QT + ((hh * Q::NSLOT + sl) * 64 + lane) * 32);
+    // E8M0 operand scales 2^(-k - 4t) of this lane's head.  The instruction
+    // takes the scale of 32-element K block kb from lane group kb, and lane
+    // group g's bytes 0-15 / 16-31 fall in blocks g / 2 and 2 + g / 2.  The
+    // packed half block carries t1 in lane groups 0-1 (blocks 0 and 2) and t2
+    // in lane groups 2-3 (blocks 1 and 3): even lane groups give t1's scale,
+    // odd ones t2's.
+    const int kq = s_k[16 * hh + n];
+    const int sbt[3] = {127 - kq, 127 - kq - kTermShift, 127 - kq - 2 * kTermShift};
+    const int sb_pack = (g & 1) ? sbt[1] : sbt[0];
+    const int qh_own = qh0 + 16 * hh + n;
+    const int32_t tlim = (a.mode == kCausal)
+                             ? a.pos0 + (qh_own < a.n_qh ? qh_own / a.n_heads : 0) + 1
+                             : 0x7FFFFFFF;
+    lds_barrier();  // staging area free for the ring
+    if (ntiles > 1)
+        issue(1, 1);
 
     // Running softmax state, replicated in every wave for heads n and 16 + n
     // of the group: m = lazy max of u (z side), d = lazy max of
@@ -503,22 +570,22 @@ __global__ __launch_bounds__(kThreads, 1) void k_split_partial(AttnArgs a)
             O[ht][jm] = f32x4{0.f, 0.f, 0.f, 0.f};
     const int cb = 64 * w;  // this wave's context columns
     const bool pv_active = cb < a.lc;
-
-    using S0 = std::integral_constant<int, 0>;
-    using S1 = std::integral_constant<int, 1>;
-    using S2 = std::integral_constant<int, 2>;
-    if (ntiles > 0)
-        issue(0, S0{});
-    if (ntiles > 1)
-        issue(1, S1{});
+    // Score operand rows: lane (n, g) reads row 16 rq + n, bytes 128 j + 32 g
+    // .. +32.  When the padded row holds an odd number of 64-byte blocks, the
+    // upper half of the last 128-byte block lies past it: lanes g >= 2 then
+    // re-read bytes of the same row, whose query elements are zero.
+    const int arow = (16 * rq + n) * XS + 32 * g;
+    const int arow_last = arow + (((NKB & 1) && g >= 2) ? -64 : 0) + 128 * (NB - 1);
+    // Context operand: source lane 2k + h of each 16-lane group addresses row
+    // 8 g + k, columns cb + 8 h .. +8; the transposed read hands lane (n, g)
+    // column n of rows 8 g .. 8 g + 7.
+    const int trb = (8 * g + ((lane & 15) >> 1)) * XS + cb + 8 * (lane & 1);
 
     // One tile: wait for its loads, refill the stage freed two tiles ago,
-    // score, update the softmax state, accumulate the context.  Barrier (A)
-    // also publishes the q low part written before the first tile.
-    auto tile = [&](int it, auto S_) __attribute__((always_inline)) {
-        constexpr int st = decltype(S_)::value;
-        const uint8_t* xst = xs_of(S_);
-        const float* scs = sc_of(S_) + TR * w;
+    // score, update the softmax state, accumulate the context.
+    auto tile = [&](int it, int st) __attribute__((always_inline)) {
+        const uint8_t* xst = lds + st * L::STAGE;
+        const float* scs = s_sc + (st * NW + w) * TR;
         // Tile it is complete once only tile it+1's operations may remain.
         if (it + 1 < ntiles)
             wait_vmcnt<NVM>();
@@ -526,58 +593,69 @@ __global__ __launch_bounds__(kThreads, 1) void k_split_partial(AttnArgs a)
             wait_vmcnt<0>();
         lds_barrier();  // (A) tile it visible to all waves; stage (it+2)%3 free
         if (it + 2 < ntiles)
-            issue(it + 2, std::integral_constant<int, (st + 2) % NST>{});
+            issue(it + 2, st == 0 ? 2 : st - 1);
+        const int p0 = c0 + it * TR;
 
-        // ---- scores: S^T[16 rows][16 heads]
-        f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-        const uint8_t* xrow = xst + (16 * rq + n) * XS + 16 * g;
+        // ---- scores: S^T[16 rows][16 heads] in log2 units of the codes, two
+        // accumulators so consecutive MFMAs do not wait on each other
+        f32x4 acc0 = f32x4{0.f, 0.f, 0.f, 0.f}, acc1 = acc0;
 #pragma unroll
-        for (int i = 0; i < NKB2; ++i) {
-            const uint4 x0 = *reinterpret_cast<const uint4*>(xrow + 128 * i);
-            const uint4 x1 = (2 * i + 1 < NKB)
-                                 ? *reinterpret_cast<const uint4*>(xrow + 128 * i + 64)
-                                 : make_uint4(0u, 0u, 0u, 0u);
-            acc = mfma16(cvt8(x0.x, x0.y), qhi[2 * i][0], acc);
-            acc = mfma16(cvt8(x0.z, x0.w), qhi[2 * i][1], acc);
-            if (2 * i + 1 < NKB) {
-                acc = mfma16(cvt8(x1.x, x1.y), qhi[2 * i + 1][0], acc);
-                acc = mfma16(cvt8(x1.z, x1.w), qhi[2 * i + 1][1], acc);
-            }
-            const v8i x8 = v8i{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w,
+        for (int j = 0; j < NB; ++j) {
+            const uint8_t* xp = xst + ((j == NB - 1) ? arow_last : arow + 128 * j);
+            const uint4 x0 = *reinterpret_cast<const uint4*>(xp);
+            const uint4 x1 = *reinterpret_cast<const uint4*>(xp + 16);
+            const v8i xv = v8i{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w,
                                (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
-            acc = mfma_fp8_scaled(x8, qlo[i * 64 + lane], acc, 127 - kQloShift);
+            if (j < Q::NFULL) {
+                acc0 = mfma_fp8_scaled(xv, qv[3 * j], acc0, sbt[0]);
+                acc1 = mfma_fp8_scaled(xv, qv[3 * j + 1], acc1, sbt[1]);
+                acc0 = mfma_fp8_scaled(xv, qv[3 * j + 2], acc0, sbt[2]);
+            } else {
+                acc1 = mfma_fp8_scaled(xv, qv[3 * j], acc1, sb_pack);
+                acc0 = mfma_fp8_scaled(xv, qv[3 * j + 1], acc0, sbt[2]);
+            }
         }
 
         // ---- log2-domain scores u (rows 16rq + 4g + v, head 16hh + n); per
         // wave: the tile max Tw of u and Cw = max_t (u_t - Tw) + log2 scale_t.
         // Everything after this stays relative to a running max, so a large
         // |u| never swallows log2 scale.
-        float u[4], lsv[4];
-        float tw = -INFINITY;
+        const float4 sc4 = *reinterpret_cast<const float4*>(scs + 16 * rq + 4 * g);
+        // log2 of the scale of row 4g + (n & 3), then broadcast within quads
+        const float myls = log2f(scs[16 * rq + 4 * g + (n & 3)]);  // -inf for a zero scale
+        const float lsv[4] = {quad_bcast<0>(myls), quad_bcast<1>(myls), quad_bcast<2>(myls),
+                              quad_bcast<3>(myls)};
+        const float scv[4] = {sc4.x, sc4.y, sc4.z, sc4.w};
+        float u[4];
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-            const int r = 16 * rq + 4 * g + v;
-            const float sc = scs[r];
-            lsv[v] = log2f(sc);  // -inf for a zero scale
-            const int32_t row = s_row[st][r];
-            const bool valid = row >= 0 && row < tlim;
-            u[v] = valid ? (acc[v] * hfac) * sc : -INFINITY;
-            tw = fmaxf(tw, u[v]);
+        for (int v = 0; v < 4; ++v)
+            u[v] = (acc0[v] + acc1[v]) * scv[v];
+        // Masking: rows past the list, invalid gathered rows, causal limit.
+        const bool full = !GATHER && a.mode != kCausal && p0 + TR <= c1;
+        if (!full) {
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int r = 16 * rq + 4 * g + v;
+                bool valid;
+                if constexpr (GATHER) {
+                    valid = s_row[st * TR + r] >= 0;
+                } else {
+                    valid = p0 + r < c1 && p0 + r < tlim;
+                }
+                u[v] = valid ? u[v] : -INFINITY;
+            }
         }
-        tw = fmaxf(tw, __shfl_xor(tw, 16));
-        tw = fmaxf(tw, __shfl_xor(tw, 32));
+        float tw = fmaxf(fmaxf(u[0], u[1]), fmaxf(u[2], u[3]));
+        tw = max_xor32(max_xor16(tw));
         float cw = -INFINITY;
         if (tw != -INFINITY) {
 #pragma unroll
             for (int v = 0; v < 4; ++v)
                 cw = fmaxf(cw, (u[v] - tw) + lsv[v]);
         }
-        cw = fmaxf(cw, __shfl_xor(cw, 16));
-        cw = fmaxf(cw, __shfl_xor(cw, 32));
-        if (g == 0) {
-            s_red[rq][0][16 * hh + n] = tw;
-            s_red[rq][1][16 * hh + n] = cw;
-        }
+        cw = max_xor32(max_xor16(cw));
+        if (g == 0)
+            s_red[(16 * hh + n) * 4 + rq] = make_float2(tw, cw);
         lds_barrier();  // (B) per-wave maxima exchanged
 
         // ---- running state for heads n, 16 + n (every wave computes both)
@@ -585,21 +663,20 @@ __global__ __launch_bounds__(kThreads, 1) void k_split_partial(AttnArgs a)
 #pragma unroll
         for (int ht = 0; ht < 2; ++ht) {
             const int h = 16 * ht + n;
-            float T = -INFINITY;
-#pragma unroll
-            for (int k = 0; k < 4; ++k)
-                T = fmaxf(T, s_red[k][0][h]);
+            const float4 r01 = *reinterpret_cast<const float4*>(&s_red[h * 4]);
+            const float4 r23 = *reinterpret_cast<const float4*>(&s_red[h * 4 + 2]);
+            const float Tk[4] = {r01.x, r01.z, r23.x, r23.z};
+            const float Ck[4] = {r01.y, r01.w, r23.y, r23.w};
+            const float T = fmaxf(fmaxf(Tk[0], Tk[1]), fmaxf(Tk[2], Tk[3]));
             const float mold = mrun[ht];
             const float mnew = (T > mold + kTau) ? T : mold;
             alz[ht] = (mnew == mold) ? 1.0f : fast_exp2(mold - mnew);
             const float mu = (mnew == -INFINITY) ? 0.0f : mnew;
             float tb = -INFINITY;
 #pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                const float Tk = s_red[k][0][h];
-                if (Tk != -INFINITY)
-                    tb = fmaxf(tb, s_red[k][1][h] + (Tk - mu));
-            }
+            for (int k = 0; k < 4; ++k)
+                if (Tk[k] != -INFINITY)
+                    tb = fmaxf(tb, Ck[k] + (Tk[k] - mu));
             const float dshift = (mnew == mold) ? drun[ht] : drun[ht] + (mold - mnew);
             const float dnew = (tb > dshift + kTau) ? tb : dshift;
             alo[ht] = (dnew == dshift) ? 1.0f : fast_exp2(dshift - dnew);
@@ -638,10 +715,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_split_partial(AttnArgs a)
         }
         lds_barrier();  // (C) weight tile complete; s_red free
 
-        // ---- context: O[32 heads][64 cols of this wave] += W . X.  Lane (n, g)
-        // reads rows 32ks + 8g + 0..7, columns cb + 4n .. +4, and byte-transposes
-        // them so the row index becomes the MFMA K index; MFMA jm covers the
-        // columns cb + 4n' + jm over the 16 lanes n'.
+        // ---- context: O[32 heads][64 cols of this wave] += W . X.  MFMA
+        // (ht, jm) covers heads 16 ht .. +16 and columns cb + 16 jm .. +16.
         if (pv_active) {
 #pragma unroll
             for (int ks = 0; ks < TR / 32; ++ks) {
@@ -650,43 +725,20 @@ __global__ __launch_bounds__(kThreads, 1) void k_split_partial(AttnArgs a)
                 for (int ht = 0; ht < 2; ++ht)
                     wa[ht] = *reinterpret_cast<const f16x8*>(
                         &s_w[(16 * ht + n) * WSS + 32 * ks + 8 * g]);
-                uint32_t xr[8];
 #pragma unroll
-                for (int v = 0; v < 8; ++v)
-                    xr[v] = *reinterpret_cast<const uint32_t*>(
-                        xst + (32 * ks + 8 * g + v) * XS + cb + 4 * n);
-#pragma unroll
-                for (int jp = 0; jp < 2; ++jp) {
-                    // columns 2jp and 2jp+1: bytes [r0.c, r1.c, r0.c+1, r1.c+1]
-                    const uint32_t jj = 2 * jp;
-                    const uint32_t selb = jj | ((jj + 4) << 8) | ((jj + 1) << 16) | ((jj + 5) << 24);
-                    f16x8 bA, bB;
-#pragma unroll
-                    for (int uu = 0; uu < 4; ++uu) {
-                        const uint32_t pk = __builtin_amdgcn_perm(xr[2 * uu + 1], xr[2 * uu], selb);
-                        const f16x2 lo = cvt2<false>(pk), hi = cvt2<true>(pk);
-                        bA[2 * uu] = lo[0];
-                        bA[2 * uu + 1] = lo[1];
-                        bB[2 * uu] = hi[0];
-                        bB[2 * uu + 1] = hi[1];
-                    }
-#pragma unroll
-                    for (int ht = 0; ht < 2; ++ht) {
-                        O[ht][2 * jp] = mfma16(wa[ht], bA, O[ht][2 * jp]);
-                        O[ht][2 * jp + 1] = mfma16(wa[ht], bB, O[ht][2 * jp + 1]);
-                    }
+                for (int jm = 0; jm < 4; ++jm) {
+                    const v2i xb = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+                        (MLA8_LDS v2i*)(MLA8_LDS uint8_t*)(xst + trb + 32 * ks * XS + 16 * jm));
+                    const f16x8 bx = cvt8((uint32_t)xb[0], (uint32_t)xb[1]);
+                    O[0][jm] = mfma16(wa[0], bx, O[0][jm]);
+                    O[1][jm] = mfma16(wa[1], bx, O[1][jm]);
                 }
             }
         }
     };
 
-    for (int it = 0; it < ntiles; it += NST) {
-        tile(it, S0{});
-        if (it + 1 < ntiles)
-            tile(it + 1, S1{});
-        if (it + 2 < ntiles)
-            tile(it + 2, S2{});
-    }
+    for (int it = 0, st = 0; it < ntiles; ++it, st = (st == NST - 1) ? 0 : st + 1)
+        tile(it, st);
 
     // ---- epilogue: z over lane groups and row quarters; partial (m, z, cl)
     {
@@ -694,7 +746,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_split_partial(AttnArgs a)
         zz += __shfl_xor(zz, 16);
         zz += __shfl_xor(zz, 32);
         if (g == 0)
-            s_z[rq][16 * hh + n] = zz;
+            s_z[rq * HG + 16 * hh + n] = zz;
     }
     __syncthreads();
     const size_t pbase = (size_t)chunk * a.n_qh;
@@ -702,7 +754,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_split_partial(AttnArgs a)
         const int h = 16 * hh + n, qh = qh0 + h;
         if (qh < a.n_qh) {
             a.ws_m[pbase + qh] = hh ? mrun[1] : mrun[0];
-            a.ws_z[pbase + qh] = (s_z[0][h] + s_z[1][h]) + (s_z[2][h] + s_z[3][h]);
+            a.ws_z[pbase + qh] = (s_z[h] + s_z[HG + h]) + (s_z[2 * HG + h] + s_z[3 * HG + h]);
         }
     }
     if (pv_active) {
@@ -715,11 +767,15 @@ __global__ __launch_bounds__(kThreads, 1) void k_split_partial(AttnArgs a)
             for (int v = 0; v < 4; ++v) {
                 const float f = __shfl(fown, 4 * g + v);
                 const int qh = qh0 + 16 * ht + 4 * g + v;
-                const int col = cb + 4 * n;
-                if (qh < a.n_qh && col < a.lc)
-                    *reinterpret_cast<float4*>(a.ws_cl + (pbase + qh) * a.lc + col) =
-                        make_float4(O[ht][0][v] * f, O[ht][1][v] * f, O[ht][2][v] * f,
-                                    O[ht][3][v] * f);
+                if (qh < a.n_qh) {
+                    float* dst = a.ws_cl + (pbase + qh) * a.lc;
+#pragma unroll
+                    for (int jm = 0; jm < 4; ++jm) {
+                        const int col = cb + 16 * jm + n;
+                        if (col < a.lc)
+                            dst[col] = O[ht][jm][v] * f;
+                    }
+                }
             }
         }
     }
@@ -833,9 +889,10 @@ static void launch_partial(const AttnArgs& a, hipStream_t stream)
 hipError_t launch_attention(const AttnArgs& a, hipStream_t stream, hipEvent_t ev_before,
                             hipEvent_t ev_after)
 {
-    // The padded LDS row must cover both the score width d and the context
-    // columns the 128-wide column blocks read (up to roundup(lc, 128)).
-    const int nkb = max((a.d + 63) / 64, 2 * ((a.lc + 127) / 128));
+    // The padded LDS row covers the row width d in 64-byte blocks (the
+    // context columns each wave reads, 64 * w .. +64 for 64 * w < lc, lie
+    // inside it since lc <= d).
+    const int nkb = (a.d + 63) / 64;
     if (nkb < 1 || nkb > 10)
         return hipErrorInvalidValue;
     if (ev_before != nullptr) {
