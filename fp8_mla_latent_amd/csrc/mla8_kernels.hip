@@ -189,19 +189,28 @@ struct QueryTerms {
     static constexpr int BYTES = 2 * NSLOT * 64 * 32;
 };
 
-template <int NKB>
-__device__ __forceinline__ void build_query_terms(const AttnArgs& a, int qh0, uint8_t* qt,
-                                                  int* s_k)
+// Maximum over the 16 lanes of each row (DPP: quad swaps, then half-row and
+// row mirrors).
+__device__ __forceinline__ float row16_max(float x)
 {
-    using Q = QueryTerms<NKB>;
-    // Thread t handles head h = t / 16 (16 threads per head, all in one wave)
-    // and the 4-element groups gi = t % 16 + 16 s of that head.
-    constexpr int PER = 2 * Q::NB;  // groups per thread: NB blocks x 32 groups / 16 threads
+    x = fmaxf(x, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xF, 0xF, false)));
+    x = fmaxf(x, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x4E, 0xF, 0xF, false)));
+    x = fmaxf(x, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x141, 0xF, 0xF, false)));
+    x = fmaxf(x, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x140, 0xF, 0xF, false)));
+    return x;
+}
+
+// Query loads of build_query_terms: thread t handles head h = t / 16 (16
+// threads per head, all in one wave) and the 4-element groups gi = t % 16 +
+// 16 s of that head.  Every load is issued before any is used.
+template <int NKB>
+__device__ __forceinline__ void load_query(const AttnArgs& a, int qh0,
+                                           float4 (&v)[2 * QueryTerms<NKB>::NB])
+{
+    constexpr int PER = 2 * QueryTerms<NKB>::NB;  // NB blocks x 32 groups / 16 threads
     const int h = threadIdx.x >> 4, i = threadIdx.x & 15;
     const int qh = qh0 + h;
     const bool hv = qh < a.n_qh;
-    float4 v[PER];
-    float amax = 0.0f;
 #pragma unroll
     for (int s = 0; s < PER; ++s) {
         const int d = 4 * (i + 16 * s);
@@ -216,12 +225,23 @@ __device__ __forceinline__ void build_query_terms(const AttnArgs& a, int qh0, ui
         }
         const float4 x = *reinterpret_cast<const float4*>(p);
         v[s] = ok ? x : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+}
+
+template <int NKB>
+__device__ __forceinline__ void build_query_terms(const AttnArgs& a,
+                                                  const float4 (&v)[2 * QueryTerms<NKB>::NB],
+                                                  uint8_t* qt, int* s_k)
+{
+    using Q = QueryTerms<NKB>;
+    constexpr int PER = 2 * Q::NB;
+    const int h = threadIdx.x >> 4, i = threadIdx.x & 15;
+    float amax = 0.0f;
+#pragma unroll
+    for (int s = 0; s < PER; ++s)
         amax = fmaxf(amax, fmaxf(fmaxf(fabsf(v[s].x), fabsf(v[s].y)),
                                  fmaxf(fabsf(v[s].z), fabsf(v[s].w))));
-    }
-#pragma unroll
-    for (int off = 8; off > 0; off >>= 1)
-        amax = fmaxf(amax, __shfl_xor(amax, off));
+    amax = row16_max(amax);
     // e = q * sm log2(e); k from the largest |e| (computed in f32 like e)
     const float es = a.sm_log2;
     int ex = 0;
@@ -301,79 +321,97 @@ __device__ __forceinline__ void wait_vmcnt()
 
 #define MLA8_LDS __attribute__((address_space(3)))
 
-// Direct global -> LDS loads, lane i writing LDS bytes [base + 16i, +16)
-// (dwordx4) or [base + 4i, +4) (dword).  Issued through asm so that the
-// compiler's wait insertion does not track them: every wait on them is the
-// explicit wait_vmcnt<> of the tile pipeline (a tracked load would be waited
-// with vmcnt(0) wherever its LDS object is read, draining the pipeline).
-// These are the kernel's only users of m0.
+// Direct global -> LDS loads, lane i writing LDS bytes [lds + 16i, +16)
+// (dwordx4) or [lds + 4i, +4) (dword); lds is a wave-uniform LDS byte
+// address.  Issued through asm so that the compiler's wait insertion does not
+// track them: every wait on them is the explicit wait_vmcnt<> of the tile
+// pipeline (a tracked load would be waited with vmcnt(0) wherever its LDS
+// object is read, draining the pipeline).  These are the kernel's only users
+// of m0.
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
-__device__ __forceinline__ void dma_b128(const void* src, const void* lds_dst)
+__device__ __forceinline__ void dma_b128(const void* src, uint32_t lds)
 {
-    const uint32_t off = __builtin_amdgcn_readfirstlane(
-        (uint32_t)(uintptr_t)(MLA8_LDS const void*)lds_dst);
+    lds = __builtin_amdgcn_readfirstlane(lds);  // wave-uniform: keep it in an SGPR
     asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
                  :
-                 : "s"(off), "v"(src)
+                 : "s"(lds), "v"(src)
                  : "memory", "m0");
 }
 
-__device__ __forceinline__ void dma_b32(const void* src, const void* lds_dst)
+__device__ __forceinline__ void dma_b32(const void* src, uint32_t lds)
 {
-    const uint32_t off = __builtin_amdgcn_readfirstlane(
-        (uint32_t)(uintptr_t)(MLA8_LDS const void*)lds_dst);
+    lds = __builtin_amdgcn_readfirstlane(lds);  // wave-uniform: keep it in an SGPR
     asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off"
                  :
-                 : "s"(off), "v"(src)
+                 : "s"(lds), "v"(src)
                  : "memory", "m0");
 }
 // Same with a wave-uniform 64-bit base in SGPRs and a 32-bit per-lane offset.
-__device__ __forceinline__ void dma_b128_s(const void* base, uint32_t voff, const void* lds_dst)
+__device__ __forceinline__ void dma_b128_s(const void* base, uint32_t voff, uint32_t lds)
 {
-    const uint32_t off = __builtin_amdgcn_readfirstlane(
-        (uint32_t)(uintptr_t)(MLA8_LDS const void*)lds_dst);
+    lds = __builtin_amdgcn_readfirstlane(lds);  // wave-uniform: keep it in an SGPR
     asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
                  :
-                 : "s"(off), "v"(voff), "s"(base)
+                 : "s"(lds), "v"(voff), "s"(base)
                  : "memory", "m0");
 }
 
-__device__ __forceinline__ void dma_b32_s(const void* base, uint32_t voff, const void* lds_dst)
+__device__ __forceinline__ void dma_b32_s(const void* base, uint32_t voff, uint32_t lds)
 {
-    const uint32_t off = __builtin_amdgcn_readfirstlane(
-        (uint32_t)(uintptr_t)(MLA8_LDS const void*)lds_dst);
+    lds = __builtin_amdgcn_readfirstlane(lds);  // wave-uniform: keep it in an SGPR
     asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, %2"
                  :
-                 : "s"(off), "v"(voff), "s"(base)
+                 : "s"(lds), "v"(voff), "s"(base)
                  : "memory", "m0");
 }
 #pragma clang diagnostic pop
 
 // Byte offsets of the split-T partial kernel's LDS objects (one array, so the
-// query-term staging area can reuse ring stages 1 and 2 before they fill).
+// query-term staging area can reuse ring stages 1-3 before they fill).
+//
+// A ring stage holds one 64-row tile, laid out for the readers rather than
+// row by row: row quarter rq (rows 16 rq .. +16) is a block of NKB KB; inside
+// it, for every 128-byte column block j and half h, the 16-byte chunks
+// (row 16 rq + n, chunk 8 j + 2 g + h) sit at slot n + 16 g of a 1-KB group
+// (a 512-byte group of slots n + 16 g, g < 2, for a trailing half block).  A
+// score read (lane n + 16 g, block j, half h) is then one linear 1-KB read and
+// a transposed context read (8 rows x 16 bytes per 16 lanes) one linear
+// 128-byte read: no LDS bank conflicts.  The direct loads choose, lane by
+// lane, which 16 bytes of HBM land in each slot.
 template <int NKB>
 struct PartialLds {
     static constexpr int TR = kTileRows;
     static constexpr int NW = kThreads / 64;
     static constexpr int HG = kHeadsPerGroup;
-    static constexpr int NB = (NKB + 1) / 2;  // 128-wide K blocks of the scores
-    static constexpr int XS = 64 * NKB + 16;  // row stride: padded row + one 16-B pad slot
-    static constexpr int SPR = XS / 16;       // 16-byte slots per LDS row
-    static constexpr int STAGE = TR * XS;     // one ring stage (a whole number of KB)
-    static constexpr int WSS = TR + 8;        // weight-tile stride (halves)
-    static constexpr int SC = 3 * STAGE;                   // f32 [3 stages][NW waves][TR]
-    static constexpr int ROW = SC + 3 * NW * TR * 4;       // i32 [3][TR] (gather rows)
-    static constexpr int W = ROW + 3 * TR * 4;             // f16 [HG][WSS]
-    static constexpr int RED = W + HG * WSS * 2;           // float2 [HG][4 row quarters]
-    static constexpr int Z = RED + HG * 4 * 8;             // f32 [4][HG]
+    static constexpr int NB = (NKB + 1) / 2;   // 128-wide K blocks of the scores
+    static constexpr int NFULL = NKB / 2;      // full 128-byte blocks
+    static constexpr int ROWB = 64 * NKB;      // padded row bytes
+    static constexpr int RQB = 16 * ROWB;      // one row quarter (NKB KB)
+    static constexpr int STAGE = TR * ROWB;    // one ring stage
+    static constexpr int WSS = TR + 8;         // weight-tile stride (halves)
+    static constexpr int FIXED = 2 * HG * WSS * 2 + 2 * HG * 4 * 4 + HG * 4 * 8 +
+                                 4 * HG * 4 + HG * 4;
+    static constexpr int LIMIT = 160 * 1024;
+    // Ring stages: 4 (loads issued two tiles ahead) when they fit, else 3
+    // (one tile ahead).  A stage is read in two phases (scores, then context).
+    static constexpr int NST = (4 * (STAGE + 2 * TR * 4) + FIXED <= LIMIT) ? 4 : 3;
+    static constexpr int DIST = NST - 2;  // tiles issued ahead
+    static constexpr int SC = NST * STAGE;                 // f32 [NST][TR] row scales
+    static constexpr int ROW = SC + NST * TR * 4;          // i32 [NST][TR] (gathered rows)
+    static constexpr int W = ROW + NST * TR * 4;           // f16 [2][HG][WSS] weights
+    static constexpr int MX = W + 2 * HG * WSS * 2;        // f32 [2][HG][4] tile check sums
+    static constexpr int CR = MX + 2 * HG * 4 * 4;         // float2 [HG][4] exact tile maxima
+    static constexpr int Z = CR + HG * 4 * 8;              // f32 [4][HG]
     static constexpr int HK = Z + 4 * HG * 4;              // i32 [HG] query exponent k
     static constexpr int END = HK + HG * 4;
     static constexpr int QT_BYTES = QueryTerms<NKB>::BYTES;  // query terms, both head halves
-    static constexpr int QT = (STAGE + QT_BYTES <= SC) ? STAGE : END;
+    // The staging area reuses the stages that are not filled before the
+    // terms are built (tiles 0 .. DIST-1 are already in flight then).
+    static constexpr int QT = (DIST * STAGE + QT_BYTES <= SC) ? DIST * STAGE : END;
     static constexpr int TOTAL = (QT + QT_BYTES > END) ? QT + QT_BYTES : END;
     static_assert(STAGE % 1024 == 0, "stages are whole DMA blocks");
-    static_assert(TOTAL <= 160 * 1024, "LDS budget");
+    static_assert(TOTAL <= LIMIT, "LDS budget");
 };
 
 // max(x, x of lane ^ 16) and max(x, x of lane ^ 32) without LDS traffic.
@@ -401,35 +439,38 @@ typedef int v2i __attribute__((ext_vector_type(2)));
 
 // Split-T partial.  Grid: n_chunks * n_groups workgroups of 512 threads (8
 // waves, two per SIMD).  NKB = number of 64-byte blocks of the padded row.
-//   loads  : 64-row tiles stream HBM -> LDS through a 3-stage ring of direct
-//            global_load_lds_dwordx4 (no register staging), two tiles in
-//            flight while a third is consumed;
+//   loads  : 64-row tiles stream HBM -> LDS through a ring of direct
+//            global_load_lds_dwordx4 (no register staging);
 //   scores : wave w takes rows 16*(w>>1) .. +16 of the tile and heads
 //            16*(w&1) .. +16 of the group: 3 e4m3 query terms in registers x
 //            the raw e4m3 row bytes on the scaled fp8 MFMA;
 //   context: wave w owns context columns 64*w .. +64 for all 32 heads; the
 //            row bytes are read transposed (ds_read_b64_tr_b8) so the row
 //            index lands on the MFMA K index, widened to fp16 exactly.
+// One barrier per tile: phase p scores tile p and writes its weights with the
+// softmax state as it stands, checks tile p-1's maxima against that state and
+// accumulates tile p-1's context.
 template <int NKB, bool GATHER>
 __global__ __launch_bounds__(kThreads, 1) void k_split_partial(AttnArgs a)
 {
     using L = PartialLds<NKB>;
-    constexpr int TR = L::TR, NW = L::NW, HG = L::HG, NB = L::NB, XS = L::XS, SPR = L::SPR;
-    constexpr int WSS = L::WSS;
-    constexpr int NINS = SPR;                 // 1-KB DMA instructions per tile
+    using Q = QueryTerms<NKB>;
+    constexpr int TR = L::TR, NW = L::NW, HG = L::HG, NB = L::NB, NFULL = L::NFULL;
+    constexpr int RQB = L::RQB, WSS = L::WSS, NST = L::NST, DIST = L::DIST;
+    constexpr int NINS = L::STAGE / 1024;     // 1-KB DMA instructions per tile
     constexpr int KW = (NINS + NW - 1) / NW;  // row DMA instructions per wave per tile
-    constexpr int NVM = KW + 1;               // + one scale DMA per wave
-    constexpr int NST = 3;                    // ring stages
-    static_assert(TR * XS == NINS * 1024, "a stage is a whole number of 1-KB DMA blocks");
-    static_assert(NVM < 64, "vmcnt range");
+    static_assert(KW + 1 < 64, "vmcnt range");
 
     __shared__ __attribute__((aligned(1024))) uint8_t lds[L::TOTAL];
     float* const s_sc = reinterpret_cast<float*>(lds + L::SC);
     int32_t* const s_row = reinterpret_cast<int32_t*>(lds + L::ROW);
     _Float16* const s_w = reinterpret_cast<_Float16*>(lds + L::W);
-    float2* const s_red = reinterpret_cast<float2*>(lds + L::RED);
+    float* const s_mx = reinterpret_cast<float*>(lds + L::MX);
+    float* const s_cr = reinterpret_cast<float*>(lds + L::CR);
     float* const s_z = reinterpret_cast<float*>(lds + L::Z);
     int* const s_k = reinterpret_cast<int*>(lds + L::HK);
+    // LDS byte address of the array (wave-uniform; the direct loads take it in m0)
+    const uint32_t lds_u32 = (uint32_t)(uintptr_t)(MLA8_LDS uint8_t*)lds;
 
     const int tid = threadIdx.x;
     const int w = tid >> 6, lane = tid & 63, n = lane & 15, g = lane >> 4;
@@ -455,15 +496,14 @@ __global__ __launch_bounds__(kThreads, 1) void k_split_partial(AttnArgs a)
     const int c1 = min(a.n_list, c0 + a.chunk_rows);
     const int ntiles = c1 > c0 ? (c1 - c0 + TR - 1) / TR : 0;
 
-    // ---- tile issue: every wave issues exactly NVM vector-memory operations
-    // per tile (so a fixed vmcnt marks a tile complete).  Row DMA instruction k
-    // fills LDS bytes [1024k, 1024k + 1024) of the stage: slot 64k + lane is
-    // (row r, 16-byte chunk c) with r = slot / SPR, c = slot % SPR.  Slots past
-    // the row's data (zero-pad columns, the pad slot) and rows outside the
-    // list load chunk 0 / the tile's first row instead: finite bytes that are
-    // multiplied by a zero query element, masked out of the softmax, or never
-    // read.  Spare instruction slots (k >= NINS) repeat instruction k % NINS
-    // (the same bytes to the same place).
+    // ---- tile issue.  Every wave issues KW row DMAs per tile and wave 0 one
+    // more for the row scales, so a fixed per-wave vmcnt marks a tile
+    // complete.  Row DMA instruction k fills stage slots [64k, 64k + 64)
+    // (16 bytes each, layout above).  Slots past the row's data (zero-pad
+    // columns) and rows outside the list load chunk 0 / the tile's first row
+    // instead: finite bytes that are multiplied by a zero query element, masked
+    // out of the softmax, or never read.  Spare instruction slots (k >= NINS)
+    // repeat instruction k % NINS (the same bytes to the same place).
     const int cpr = a.d >> 4;  // 16-byte data chunks per row
     auto row_of = [&](int pos) __attribute__((always_inline)) -> int32_t {
         if (pos >= c1)
@@ -477,13 +517,24 @@ __global__ __launch_bounds__(kThreads, 1) void k_split_partial(AttnArgs a)
 #pragma unroll
     for (int i = 0; i < KW; ++i) {
         const int k = (w + NW * i) % NINS;
-        const int slot = 64 * k + lane;
-        const int r = slot / SPR, c = slot - (slot / SPR) * SPR;
-        dpk[i] = (r << 16) | (r * a.d + (c < cpr ? 16 * c : 0));
+        const int sl = 64 * k + lane;
+        const int q4 = sl / (64 * NKB), s1 = sl - q4 * (64 * NKB);
+        int j, h, ln;
+        if (s1 < NFULL * 128) {
+            j = s1 >> 7;
+            h = (s1 >> 6) & 1;
+            ln = s1 & 63;
+        } else {
+            j = NFULL;
+            h = (s1 - NFULL * 128) >> 5;
+            ln = s1 & 31;
+        }
+        const int r = 16 * q4 + (ln & 15), c16 = 8 * j + 2 * (ln >> 4) + h;
+        dpk[i] = (r << 16) | (r * a.d + (c16 < cpr ? 16 * c16 : 0));
     }
     auto issue = [&](int t, int st) __attribute__((always_inline)) {
-        uint8_t* xst = lds + st * L::STAGE;
-        float* sct = s_sc + (st * NW + w) * TR;
+        const uint32_t xst = lds_u32 + (uint32_t)(st * L::STAGE);
+        const uint32_t sct = lds_u32 + (uint32_t)(L::SC + st * TR * 4);
         const int p0 = c0 + t * TR;
         if constexpr (!GATHER) {
             // Contiguous rows p0 .. p0 + nv - 1: SGPR base + 32-bit offsets.
@@ -496,7 +547,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_split_partial(AttnArgs a)
                     const int k = (w + NW * i) % NINS;
                     dma_b128_s(tb, (uint32_t)(dpk[i] & 0xFFFF), xst + 1024 * k);
                 }
-                dma_b32_s(a.scales + p0, (uint32_t)(4 * lane), sct);
+                if (w == 0)
+                    dma_b32_s(a.scales + p0, (uint32_t)(4 * lane), sct);
             } else {
 #pragma unroll
                 for (int i = 0; i < KW; ++i) {
@@ -506,7 +558,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_split_partial(AttnArgs a)
                         (uint32_t)((dpk[i] & 0xFFFF) - (r < nv ? 0 : r * a.d));
                     dma_b128_s(tb, off, xst + 1024 * k);
                 }
-                dma_b32_s(a.scales + p0, (uint32_t)(4 * (lane < nv ? lane : 0)), sct);
+                if (w == 0)
+                    dma_b32_s(a.scales + p0, (uint32_t)(4 * (lane < nv ? lane : 0)), sct);
             }
         } else {
             // Gather: absolute row indices; entries outside [0, t_rows) and
@@ -519,20 +572,38 @@ __global__ __launch_bounds__(kThreads, 1) void k_split_partial(AttnArgs a)
                 const int32_t row = row_of(p0 + r);
                 dma_b128(a.codes + (size_t)(row >= 0 ? row : 0) * a.d + cc, xst + 1024 * k);
             }
-            const int32_t srow = row_of(p0 + lane);
-            dma_b32(a.scales + (srow >= 0 ? srow : 0), sct);
-            if (w == 0)
+            if (w == 0) {
+                const int32_t srow = row_of(p0 + lane);
+                dma_b32(a.scales + (srow >= 0 ? srow : 0), sct);
                 s_row[st * TR + lane] = srow;
+            }
+        }
+    };
+    // Tile t is complete once at most tile t+1's operations remain in flight
+    // (two tiles ahead) or none (one tile ahead).
+    auto wait_tile = [&](bool next_in_flight) __attribute__((always_inline)) {
+        if (DIST == 2 && next_in_flight) {
+            if (w == 0)
+                wait_vmcnt<KW + 1>();
+            else
+                wait_vmcnt<KW>();
+        } else {
+            wait_vmcnt<0>();
         }
     };
 
+    // ---- query terms for the group, staged in LDS (over the ring stages not
+    // yet in flight when they fit there), then each wave keeps its head
+    // half's in registers.  The query loads go out first, then the first
+    // tiles' direct loads, so that waiting for the query does not wait for
+    // the tiles.
+    float4 qin[2 * NB];
+    load_query<NKB>(a, qh0, qin);
     if (ntiles > 0)
         issue(0, 0);
-
-    // ---- query terms for the group, staged in LDS (over ring stages 1-2 when
-    // they fit there), then each wave keeps its head half's in registers
-    using Q = QueryTerms<NKB>;
-    build_query_terms<NKB>(a, qh0, lds + L::QT, s_k);
+    if (DIST == 2 && ntiles > 1)
+        issue(1, 1);
+    build_query_terms<NKB>(a, qin, lds + L::QT, s_k);
     lds_barrier();
     v8i qv[Q::NSLOT];
 #pragma unroll
@@ -546,22 +617,36 @@ __global__ __launch_bounds__(kThreads, 1) void k_split_partial(AttnArgs a)
     // in lane groups 2-3 (blocks 1 and 3): even lane groups give t1's scale,
     // odd ones t2's.
     const int kq = s_k[16 * hh + n];
-    const int sbt[3] = {127 - kq, 127 - kq - kTermShift, 127 - kq - 2 * kTermShift};
-    const int sb_pack = (g & 1) ? sbt[1] : sbt[0];
+    const int sbt0 = 127 - kq, sbt1 = sbt0 - kTermShift, sbt2 = sbt0 - 2 * kTermShift;
+    const int sb_pack = (g & 1) ? sbt1 : sbt0;
     const int qh_own = qh0 + 16 * hh + n;
     const int32_t tlim = (a.mode == kCausal)
                              ? a.pos0 + (qh_own < a.n_qh ? qh_own / a.n_heads : 0) + 1
                              : 0x7FFFFFFF;
     lds_barrier();  // staging area free for the ring
-    if (ntiles > 1)
-        issue(1, 1);
 
-    // Running softmax state, replicated in every wave for heads n and 16 + n
-    // of the group: m = lazy max of u (z side), d = lazy max of
-    // (u - m) + log2 scale (context side, relative to m).
-    float mrun[2] = {-INFINITY, -INFINITY};
-    float drun[2] = {-INFINITY, -INFINITY};
-    float zacc = 0.0f;  // z partial over this lane's rows, head 16*hh + n
+    // Softmax state, identical in every wave, for heads n and 16 + n of the
+    // group: m = lazy max of u (z side), d = lazy max of (u - m) + log2 scale
+    // (context side, relative to m).  The weights of tile p are computed with
+    // the state as it stands, in the linear domain:
+    //     p_t = 2^(u_t - m),  w_t = p_t * (scale_t * 2^-d),
+    // and the tile's sums of p + w per wave are checked one phase later.  Only
+    // when a sum leaves [0, 2^kTau] (a new maximum by more than kTau, the first
+    // tile, or an intermediate that left f32's range) is the state recomputed
+    // exactly in the log domain, the context rescaled and the tile's weights
+    // rewritten (as 2^((u - m) + log2 scale - d)).
+    // (separate scalars, never an array: a lane-dependent pick from an array
+    // would put it in scratch memory)
+    float mrun0 = -INFINITY, mrun1 = -INFINITY, drun0 = -INFINITY, drun1 = -INFINITY;
+    float fown = 1.0f;   // 2^-d of this lane's own head (2^0 while d = -inf)
+    // A head whose m is still -inf has not met a valid row, and the linear
+    // weights of a first valid row may underflow to a zero sum: while any head
+    // of the group is in that state every check takes the exact path
+    // (uniform: every wave holds the same state).
+    bool uninit = true;
+    float zacc = 0.0f;   // z partial over this lane's rows, head 16*hh + n
+    float zsave = 0.0f;  // zacc before the last scored tile
+    float u[4], scv[4];  // this lane's scores / row scales of the last scored tile
     f32x4 O[2][4];
 #pragma unroll
     for (int ht = 0; ht < 2; ++ht)
@@ -570,63 +655,234 @@ __global__ __launch_bounds__(kThreads, 1) void k_split_partial(AttnArgs a)
             O[ht][jm] = f32x4{0.f, 0.f, 0.f, 0.f};
     const int cb = 64 * w;  // this wave's context columns
     const bool pv_active = cb < a.lc;
-    // Score operand rows: lane (n, g) reads row 16 rq + n, bytes 128 j + 32 g
-    // .. +32.  When the padded row holds an odd number of 64-byte blocks, the
-    // upper half of the last 128-byte block lies past it: lanes g >= 2 then
-    // re-read bytes of the same row, whose query elements are zero.
-    const int arow = (16 * rq + n) * XS + 32 * g;
-    const int arow_last = arow + (((NKB & 1) && g >= 2) ? -64 : 0) + 128 * (NB - 1);
-    // Context operand: source lane 2k + h of each 16-lane group addresses row
-    // 8 g + k, columns cb + 8 h .. +8; the transposed read hands lane (n, g)
-    // column n of rows 8 g .. 8 g + 7.
-    const int trb = (8 * g + ((lane & 15) >> 1)) * XS + cb + 8 * (lane & 1);
+    // Score operand: lane (n, g) of block j, half h reads slot n + 16 g of
+    // group (j, h) of its row quarter; in a trailing half block lanes g >= 2
+    // re-read the slots of g - 2, whose query elements carry the packed second
+    // term.
+    const int qa = rq * RQB + 16 * lane;
+    const int qa_half = rq * RQB + NFULL * 2048 + 16 * (lane & 31);
+    // Context operand: source lane 2k + h' of 16-lane group g' addresses row
+    // 8 g' + k (row quarter g' / 2, slot n = 8 (g' & 1) + k), bytes 8 h' .. of
+    // the column chunk; the transposed read hands lane (n, g') column n of
+    // rows 8 g' .. 8 g' + 7.  Wave w's columns 64 w .. are chunks 4 w .. 4 w
+    // + 3: block w / 2, lane groups 2 (w & 1) + jm / 2, halves jm & 1.
+    const int trl = (g >> 1) * RQB + 16 * (8 * (g & 1) + ((lane & 15) >> 1)) + 8 * (lane & 1);
+    const bool ctx_half = (w >> 1) >= NFULL;  // the wave's columns lie in a half block
+    const int trw = ctx_half ? NFULL * 2048 : (w >> 1) * 2048 + (w & 1) * 512;
+    _Float16* const s_w_own = s_w + (16 * hh + n) * WSS + 16 * rq + 4 * g;
+    constexpr float kCheck = 256.0f;  // 2^kTau
+    static_assert(kTau == 8.0f, "check threshold");
 
-    // One tile: wait for its loads, refill the stage freed two tiles ago,
-    // score, update the softmax state, accumulate the context.
-    auto tile = [&](int it, int st) __attribute__((always_inline)) {
+    // Weights of this lane's rows (linear form) into buffer buf; returns this
+    // lane's sum of p + w.
+    auto weights_linear = [&](int buf) __attribute__((always_inline)) -> float {
+        const float mu = hh ? mrun1 : mrun0;
+        const float mz = (mu == -INFINITY) ? 0.0f : mu;
+        float ps = 0.0f, chk = 0.0f;
+        f16x4 wv;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            const float pv = fast_exp2(u[v] - mz);
+            const float wt = pv * (scv[v] * fown);
+            ps += pv;
+            chk += pv + wt;
+            wv[v] = (_Float16)wt;
+        }
+        zacc = zsave + ps;
+        *reinterpret_cast<f16x4*>(s_w_own + buf * HG * WSS) = wv;
+        return chk;
+    };
+    // Same in the log domain (exact for any scale), used after a state move.
+    auto weights_log = [&](int buf) __attribute__((always_inline)) {
+        const float mu = hh ? mrun1 : mrun0;
+        const float dd = hh ? drun1 : drun0;
+        const float mz = (mu == -INFINITY) ? 0.0f : mu;
+        const float dn = (dd == -INFINITY) ? 0.0f : dd;
+        float ps = 0.0f;
+        f16x4 wv;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            const float av = u[v] - mz;
+            ps += fast_exp2(av);
+            wv[v] = (_Float16)fast_exp2((av + log2f(scv[v])) - dn);
+        }
+        zacc = zsave + ps;
+        *reinterpret_cast<f16x4*>(s_w_own + buf * HG * WSS) = wv;
+    };
+
+    // ---- context: O[32 heads][64 cols of this wave] += W . X of the tile in
+    // stage st with weight buffer buf.  MFMA (ht, jm) covers heads 16 ht ..
+    // +16 and columns cb + 16 jm .. +16.
+    auto context = [&](int st, int buf, auto HALF_) __attribute__((always_inline)) {
+        constexpr bool HALFC = decltype(HALF_)::value;
+        const uint8_t* xst = lds + st * L::STAGE + trw + trl;
+        const _Float16* sw = s_w + buf * HG * WSS;
+#pragma unroll
+        for (int ks = 0; ks < TR / 32; ++ks) {
+            f16x8 wa[2];
+#pragma unroll
+            for (int ht = 0; ht < 2; ++ht)
+                wa[ht] = *reinterpret_cast<const f16x8*>(&sw[(16 * ht + n) * WSS + 32 * ks + 8 * g]);
+#pragma unroll
+            for (int jm = 0; jm < 4; ++jm) {
+                const int off = 2 * ks * RQB + (jm & 1) * (HALFC ? 512 : 1024) + (jm >> 1) * 256;
+                const v2i xb = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+                    (MLA8_LDS v2i*)(MLA8_LDS uint8_t*)(xst + off));
+                const f16x8 bx = cvt8((uint32_t)xb[0], (uint32_t)xb[1]);
+                O[0][jm] = mfma16(wa[0], bx, O[0][jm]);
+                O[1][jm] = mfma16(wa[1], bx, O[1][jm]);
+            }
+        }
+    };
+
+    // Scores of tile p (stage st): S^T[16 rows][16 heads] in log2 units of the
+    // codes, two accumulators so consecutive MFMAs do not wait on each other.
+    f32x4 acc0, acc1;
+    auto scores = [&](int st) __attribute__((always_inline)) {
         const uint8_t* xst = lds + st * L::STAGE;
-        const float* scs = s_sc + (st * NW + w) * TR;
-        // Tile it is complete once only tile it+1's operations may remain.
-        if (it + 1 < ntiles)
-            wait_vmcnt<NVM>();
-        else
-            wait_vmcnt<0>();
-        lds_barrier();  // (A) tile it visible to all waves; stage (it+2)%3 free
-        if (it + 2 < ntiles)
-            issue(it + 2, st == 0 ? 2 : st - 1);
-        const int p0 = c0 + it * TR;
-
-        // ---- scores: S^T[16 rows][16 heads] in log2 units of the codes, two
-        // accumulators so consecutive MFMAs do not wait on each other
-        f32x4 acc0 = f32x4{0.f, 0.f, 0.f, 0.f}, acc1 = acc0;
+        acc0 = f32x4{0.f, 0.f, 0.f, 0.f};
+        acc1 = acc0;
 #pragma unroll
         for (int j = 0; j < NB; ++j) {
-            const uint8_t* xp = xst + ((j == NB - 1) ? arow_last : arow + 128 * j);
+            const uint8_t* xp = (j < NFULL) ? xst + qa + 2048 * j : xst + qa_half;
+            const int hoff = (j < NFULL) ? 1024 : 512;
             const uint4 x0 = *reinterpret_cast<const uint4*>(xp);
-            const uint4 x1 = *reinterpret_cast<const uint4*>(xp + 16);
+            const uint4 x1 = *reinterpret_cast<const uint4*>(xp + hoff);
             const v8i xv = v8i{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w,
                                (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
             if (j < Q::NFULL) {
-                acc0 = mfma_fp8_scaled(xv, qv[3 * j], acc0, sbt[0]);
-                acc1 = mfma_fp8_scaled(xv, qv[3 * j + 1], acc1, sbt[1]);
-                acc0 = mfma_fp8_scaled(xv, qv[3 * j + 2], acc0, sbt[2]);
+                acc0 = mfma_fp8_scaled(xv, qv[3 * j], acc0, sbt0);
+                acc1 = mfma_fp8_scaled(xv, qv[3 * j + 1], acc1, sbt1);
+                acc0 = mfma_fp8_scaled(xv, qv[3 * j + 2], acc0, sbt2);
             } else {
                 acc1 = mfma_fp8_scaled(xv, qv[3 * j], acc1, sb_pack);
-                acc0 = mfma_fp8_scaled(xv, qv[3 * j + 1], acc0, sbt[2]);
+                acc0 = mfma_fp8_scaled(xv, qv[3 * j + 1], acc0, sbt2);
             }
         }
+    };
 
-        // ---- log2-domain scores u (rows 16rq + 4g + v, head 16hh + n); per
-        // wave: the tile max Tw of u and Cw = max_t (u_t - Tw) + log2 scale_t.
-        // Everything after this stays relative to a running max, so a large
-        // |u| never swallows log2 scale.
+    // Check of tile p-1 (weight buffer bufp) and its context (stage stp).
+    auto check_and_context = [&](int stp, int bufp) __attribute__((always_inline)) {
+        // Sums of p + w of tile p-1 per (head, row quarter); every wave reads
+        // the same sums and holds the same state, so the vote is uniform
+        // across the workgroup and the barriers below are reached by all
+        // waves or none.
+        const float* mxp = s_mx + bufp * HG * 4;
+        bool moved = false;
+#pragma unroll
+        for (int ht = 0; ht < 2; ++ht) {
+            const float4 S4 = *reinterpret_cast<const float4*>(mxp + (16 * ht + n) * 4);
+            // false for NaN: a non-finite intermediate also recomputes
+            moved |= !(fmaxf(fmaxf(S4.x, S4.y), fmaxf(S4.z, S4.w)) <= kCheck);
+        }
+        if (uninit || __any(moved)) {
+            // exact maxima of tile p-1 per wave: Tw = max u, Cw = max (u - Tw)
+            // + log2 scale, relative so that a large |u| never swallows log2
+            // scale
+            float tw = fmaxf(fmaxf(u[0], u[1]), fmaxf(u[2], u[3]));
+            tw = max_xor32(max_xor16(tw));
+            float cw = -INFINITY;
+            if (tw != -INFINITY) {
+#pragma unroll
+                for (int v = 0; v < 4; ++v)
+                    cw = fmaxf(cw, (u[v] - tw) + log2f(scv[v]));
+            }
+            cw = max_xor32(max_xor16(cw));
+            float2* const s_cr2 = reinterpret_cast<float2*>(s_cr);
+            if (g == 0)
+                s_cr2[(16 * hh + n) * 4 + rq] = make_float2(tw, cw);
+            lds_barrier();  // (R1)
+            float alz[2], alo[2];
+#pragma unroll
+            for (int ht = 0; ht < 2; ++ht) {
+                const int h = 16 * ht + n;
+                const float4 r01 = *reinterpret_cast<const float4*>(&s_cr2[h * 4]);
+                const float4 r23 = *reinterpret_cast<const float4*>(&s_cr2[h * 4 + 2]);
+                const float Tk[4] = {r01.x, r01.z, r23.x, r23.z};
+                const float Ck[4] = {r01.y, r01.w, r23.y, r23.w};
+                const float T = fmaxf(fmaxf(Tk[0], Tk[1]), fmaxf(Tk[2], Tk[3]));
+                float& mr = ht ? mrun1 : mrun0;
+                float& dr = ht ? drun1 : drun0;
+                const float mold = mr;
+                const float mnew = (T > mold + kTau) ? T : mold;
+                alz[ht] = (mnew == mold) ? 1.0f : fast_exp2(mold - mnew);
+                const float mu = (mnew == -INFINITY) ? 0.0f : mnew;
+                float tb = -INFINITY;
+#pragma unroll
+                for (int k = 0; k < 4; ++k)
+                    if (Tk[k] != -INFINITY)
+                        tb = fmaxf(tb, Ck[k] + (Tk[k] - mu));
+                const float dshift = (mnew == mold) ? dr : dr + (mold - mnew);
+                const float dnew = (tb > dshift + kTau) ? tb : dshift;
+                alo[ht] = (dnew == dshift) ? 1.0f : fast_exp2(dshift - dnew);
+                mr = mnew;
+                dr = dnew;
+            }
+            // O holds tiles < p-1 in units of the old state; its heads
+            // 16*ht + 4*g + v take their factors from lanes 4*g + v.
+#pragma unroll
+            for (int ht = 0; ht < 2; ++ht)
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    const float f = __shfl(alo[ht], 4 * g + v);
+#pragma unroll
+                    for (int jm = 0; jm < 4; ++jm)
+                        O[ht][jm][v] *= f;
+                }
+            zsave *= hh ? alz[1] : alz[0];
+            const float dd = hh ? drun1 : drun0;
+            fown = (dd == -INFINITY) ? 1.0f : fast_exp2(-dd);
+            uninit = __any(mrun0 == -INFINITY || mrun1 == -INFINITY);
+            weights_log(bufp);  // tile p-1 under the new state
+            lds_barrier();      // (R2) rewritten weights visible; s_cr free
+        }
+        if (pv_active) {
+            if (!ctx_half)
+                context(stp, bufp, std::false_type{});
+            else
+                context(stp, bufp, std::true_type{});
+        }
+    };
+
+    // Phase p: score tile p (ring stage p % NST, buffers p & 1), check the
+    // sums of tile p - 1 and accumulate its context.  The two waves sharing a
+    // SIMD (w and w + 4) take the score MFMAs and the check/context in
+    // opposite orders, so one issues MFMAs while the other runs VALU work.
+    // One extra phase finishes the last tile.
+    for (int p = 0, st = 0, stp = NST - 1; p <= ntiles;
+         ++p, stp = st, st = (st == NST - 1) ? 0 : st + 1) {
+        // st = p % NST, stp = (p - 1) % NST
+        const int buf = p & 1, bufp = buf ^ 1;
+        if (p < ntiles)
+            wait_tile(p + 1 < ntiles);
+        lds_barrier();  // (A) tile p visible; weights and sums of tile p-1
+                        //     complete; stage (p + DIST) % NST (tile p + DIST
+                        //     - NST) and buffers p & 1 free
+        if (p + DIST < ntiles)
+            issue(p + DIST, (st + DIST) % NST);
+        if (w < NW / 2) {
+            if (p < ntiles)
+                scores(st);
+            if (p >= 1)
+                check_and_context(stp, bufp);
+        } else {
+            if (p >= 1)
+                check_and_context(stp, bufp);
+            if (p < ntiles)
+                scores(st);
+        }
+        if (p == ntiles)
+            break;
+
+        // ---- log2-domain scores u of tile p (rows 16rq + 4g + v, head
+        // 16hh + n) and this lane's weights
+        const float* scs = s_sc + st * TR;
+        const int p0 = c0 + p * TR;
         const float4 sc4 = *reinterpret_cast<const float4*>(scs + 16 * rq + 4 * g);
-        // log2 of the scale of row 4g + (n & 3), then broadcast within quads
-        const float myls = log2f(scs[16 * rq + 4 * g + (n & 3)]);  // -inf for a zero scale
-        const float lsv[4] = {quad_bcast<0>(myls), quad_bcast<1>(myls), quad_bcast<2>(myls),
-                              quad_bcast<3>(myls)};
-        const float scv[4] = {sc4.x, sc4.y, sc4.z, sc4.w};
-        float u[4];
+        scv[0] = sc4.x;
+        scv[1] = sc4.y;
+        scv[2] = sc4.z;
+        scv[3] = sc4.w;
 #pragma unroll
         for (int v = 0; v < 4; ++v)
             u[v] = (acc0[v] + acc1[v]) * scv[v];
@@ -645,100 +901,20 @@ __global__ __launch_bounds__(kThreads, 1) void k_split_partial(AttnArgs a)
                 u[v] = valid ? u[v] : -INFINITY;
             }
         }
-        float tw = fmaxf(fmaxf(u[0], u[1]), fmaxf(u[2], u[3]));
-        tw = max_xor32(max_xor16(tw));
-        float cw = -INFINITY;
-        if (tw != -INFINITY) {
-#pragma unroll
-            for (int v = 0; v < 4; ++v)
-                cw = fmaxf(cw, (u[v] - tw) + lsv[v]);
-        }
-        cw = max_xor32(max_xor16(cw));
-        if (g == 0)
-            s_red[(16 * hh + n) * 4 + rq] = make_float2(tw, cw);
-        lds_barrier();  // (B) per-wave maxima exchanged
-
-        // ---- running state for heads n, 16 + n (every wave computes both)
-        float alz[2], alo[2];
-#pragma unroll
-        for (int ht = 0; ht < 2; ++ht) {
-            const int h = 16 * ht + n;
-            const float4 r01 = *reinterpret_cast<const float4*>(&s_red[h * 4]);
-            const float4 r23 = *reinterpret_cast<const float4*>(&s_red[h * 4 + 2]);
-            const float Tk[4] = {r01.x, r01.z, r23.x, r23.z};
-            const float Ck[4] = {r01.y, r01.w, r23.y, r23.w};
-            const float T = fmaxf(fmaxf(Tk[0], Tk[1]), fmaxf(Tk[2], Tk[3]));
-            const float mold = mrun[ht];
-            const float mnew = (T > mold + kTau) ? T : mold;
-            alz[ht] = (mnew == mold) ? 1.0f : fast_exp2(mold - mnew);
-            const float mu = (mnew == -INFINITY) ? 0.0f : mnew;
-            float tb = -INFINITY;
-#pragma unroll
-            for (int k = 0; k < 4; ++k)
-                if (Tk[k] != -INFINITY)
-                    tb = fmaxf(tb, Ck[k] + (Tk[k] - mu));
-            const float dshift = (mnew == mold) ? drun[ht] : drun[ht] + (mold - mnew);
-            const float dnew = (tb > dshift + kTau) ? tb : dshift;
-            alo[ht] = (dnew == dshift) ? 1.0f : fast_exp2(dshift - dnew);
-            mrun[ht] = mnew;
-            drun[ht] = dnew;
-        }
-        // ---- this wave's rows: p = 2^(u - m) into z, w = 2^((u - m) + ls - d)
+        zsave = zacc;
+        float chk = weights_linear(buf);
+        // sum over the wave's 16 rows (lane groups g)
         {
-            const float mu = hh ? mrun[1] : mrun[0];
-            const float dd = hh ? drun[1] : drun[0];
-            const float mz = (mu == -INFINITY) ? 0.0f : mu;
-            const float dn = (dd == -INFINITY) ? 0.0f : dd;
-            float ps = 0.0f;
-            f16x4 wv;
-#pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                const float av = u[v] - mz;
-                ps += fast_exp2(av);
-                wv[v] = (_Float16)fast_exp2((av + lsv[v]) - dn);
-            }
-            zacc = zacc * (hh ? alz[1] : alz[0]) + ps;
-            *reinterpret_cast<f16x4*>(&s_w[(16 * hh + n) * WSS + 16 * rq + 4 * g]) = wv;
+            const auto r1 = __builtin_amdgcn_permlane16_swap(__float_as_uint(chk),
+                                                             __float_as_uint(chk), false, false);
+            chk = __uint_as_float(r1[0]) + __uint_as_float(r1[1]);
+            const auto r2 = __builtin_amdgcn_permlane32_swap(__float_as_uint(chk),
+                                                             __float_as_uint(chk), false, false);
+            chk = __uint_as_float(r2[0]) + __uint_as_float(r2[1]);
         }
-        // Rescale the context accumulators when a context offset moved.  O
-        // holds heads 16*ht + 4*g + v; their factors live in lanes 4*g + v.
-        if (__any((alo[0] != 1.0f) || (alo[1] != 1.0f))) {
-#pragma unroll
-            for (int ht = 0; ht < 2; ++ht)
-#pragma unroll
-                for (int v = 0; v < 4; ++v) {
-                    const float f = __shfl(alo[ht], 4 * g + v);
-#pragma unroll
-                    for (int jm = 0; jm < 4; ++jm)
-                        O[ht][jm][v] *= f;
-                }
-        }
-        lds_barrier();  // (C) weight tile complete; s_red free
-
-        // ---- context: O[32 heads][64 cols of this wave] += W . X.  MFMA
-        // (ht, jm) covers heads 16 ht .. +16 and columns cb + 16 jm .. +16.
-        if (pv_active) {
-#pragma unroll
-            for (int ks = 0; ks < TR / 32; ++ks) {
-                f16x8 wa[2];
-#pragma unroll
-                for (int ht = 0; ht < 2; ++ht)
-                    wa[ht] = *reinterpret_cast<const f16x8*>(
-                        &s_w[(16 * ht + n) * WSS + 32 * ks + 8 * g]);
-#pragma unroll
-                for (int jm = 0; jm < 4; ++jm) {
-                    const v2i xb = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-                        (MLA8_LDS v2i*)(MLA8_LDS uint8_t*)(xst + trb + 32 * ks * XS + 16 * jm));
-                    const f16x8 bx = cvt8((uint32_t)xb[0], (uint32_t)xb[1]);
-                    O[0][jm] = mfma16(wa[0], bx, O[0][jm]);
-                    O[1][jm] = mfma16(wa[1], bx, O[1][jm]);
-                }
-            }
-        }
-    };
-
-    for (int it = 0, st = 0; it < ntiles; ++it, st = (st == NST - 1) ? 0 : st + 1)
-        tile(it, st);
+        if (g == 0)
+            s_mx[(buf * HG + 16 * hh + n) * 4 + rq] = chk;
+    }
 
     // ---- epilogue: z over lane groups and row quarters; partial (m, z, cl)
     {
@@ -753,7 +929,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_split_partial(AttnArgs a)
     if (rq == 0 && g == 0) {
         const int h = 16 * hh + n, qh = qh0 + h;
         if (qh < a.n_qh) {
-            a.ws_m[pbase + qh] = hh ? mrun[1] : mrun[0];
+            a.ws_m[pbase + qh] = hh ? mrun1 : mrun0;
             a.ws_z[pbase + qh] = (s_z[h] + s_z[HG + h]) + (s_z[2 * HG + h] + s_z[3 * HG + h]);
         }
     }
@@ -761,11 +937,11 @@ __global__ __launch_bounds__(kThreads, 1) void k_split_partial(AttnArgs a)
 #pragma unroll
         for (int ht = 0; ht < 2; ++ht) {
             // cl = sum_t p_t scale_t x_t = 2^d * O
-            const float fown =
-                (mrun[ht] == -INFINITY || drun[ht] == -INFINITY) ? 0.0f : fast_exp2(drun[ht]);
+            const float mh = ht ? mrun1 : mrun0, dh = ht ? drun1 : drun0;
+            const float fo = (mh == -INFINITY || dh == -INFINITY) ? 0.0f : fast_exp2(dh);
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
-                const float f = __shfl(fown, 4 * g + v);
+                const float f = __shfl(fo, 4 * g + v);
                 const int qh = qh0 + 16 * ht + 4 * g + v;
                 if (qh < a.n_qh) {
                     float* dst = a.ws_cl + (pbase + qh) * a.lc;
