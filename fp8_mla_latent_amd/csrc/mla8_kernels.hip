@@ -75,7 +75,33 @@ __device__ __forceinline__ uint32_t enc_e4m3(float y)
     return sign | code;
 }
 
-// One wave per row, four rows per workgroup.
+// Maximum over the 16 lanes of each row (DPP: quad swaps, then half-row and
+// row mirrors), and over the whole wave (permlane swaps across rows).
+__device__ __forceinline__ float row16_max(float x)
+{
+    x = fmaxf(x, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xF, 0xF, false)));
+    x = fmaxf(x, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x4E, 0xF, 0xF, false)));
+    x = fmaxf(x, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x141, 0xF, 0xF, false)));
+    x = fmaxf(x, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x140, 0xF, 0xF, false)));
+    return x;
+}
+__device__ __forceinline__ float max_xor16(float x)
+{
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                    false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float max_xor32(float x)
+{
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                    false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+// One wave per row, four rows per workgroup; the row (d <= kMaxRowWidth
+// floats, at most three float4 per lane) stays in registers between the
+// amax pass and the encode pass.
+constexpr int kMaxRowWidth = 768;
 __global__ __launch_bounds__(256) void k_quantize_rows(const float* __restrict__ x,
                                                        int64_t n_rows, int32_t d,
                                                        uint8_t* __restrict__ codes,
@@ -87,18 +113,22 @@ __global__ __launch_bounds__(256) void k_quantize_rows(const float* __restrict__
         return;
     const float4* xr = reinterpret_cast<const float4*>(x + row * d);
     const int nv = d >> 2;
-    float amax = 0.0f;
-    for (int i = lane; i < nv; i += 64) {
-        const float4 v = xr[i];
-        const float e[4] = {fabsf(v.x), fabsf(v.y), fabsf(v.z), fabsf(v.w)};
+    float4 v[3];
 #pragma unroll
-        for (int k = 0; k < 4; ++k)
-            if (e[k] <= 3.402823466e38f)  // finite only: false for NaN and inf
-                amax = fmaxf(amax, e[k]);
+    for (int k = 0; k < 3; ++k) {
+        const int i = lane + 64 * k;
+        v[k] = (i < nv) ? xr[i] : make_float4(0.f, 0.f, 0.f, 0.f);
     }
+    float amax = 0.0f;
 #pragma unroll
-    for (int off = 32; off > 0; off >>= 1)
-        amax = fmaxf(amax, __shfl_xor(amax, off));
+    for (int k = 0; k < 3; ++k) {
+        const float e[4] = {fabsf(v[k].x), fabsf(v[k].y), fabsf(v[k].z), fabsf(v[k].w)};
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+            if (e[c] <= 3.402823466e38f)  // finite only: false for NaN and inf
+                amax = fmaxf(amax, e[c]);
+    }
+    amax = max_xor32(max_xor16(row16_max(amax)));
     // IEEE f32 quotients (the library is built with correctly rounded f32
     // division).  The guard: when 448/amax is not finite the row encodes as
     // signed zeros.
@@ -107,10 +137,12 @@ __global__ __launch_bounds__(256) void k_quantize_rows(const float* __restrict__
     if (!(inv <= 3.402823466e38f))
         inv = 0.0f;
     uint32_t* cr = reinterpret_cast<uint32_t*>(codes + row * d);
-    for (int i = lane; i < nv; i += 64) {
-        const float4 v = xr[i];
-        cr[i] = enc_e4m3(v.x * inv) | (enc_e4m3(v.y * inv) << 8) | (enc_e4m3(v.z * inv) << 16) |
-                (enc_e4m3(v.w * inv) << 24);
+#pragma unroll
+    for (int k = 0; k < 3; ++k) {
+        const int i = lane + 64 * k;
+        if (i < nv)
+            cr[i] = enc_e4m3(v[k].x * inv) | (enc_e4m3(v[k].y * inv) << 8) |
+                    (enc_e4m3(v[k].z * inv) << 16) | (enc_e4m3(v[k].w * inv) << 24);
     }
     if (lane == 0)
         scales[row] = scale;
@@ -189,16 +221,6 @@ struct QueryTerms {
     static constexpr int BYTES = 2 * NSLOT * 64 * 32;
 };
 
-// Maximum over the 16 lanes of each row (DPP: quad swaps, then half-row and
-// row mirrors).
-__device__ __forceinline__ float row16_max(float x)
-{
-    x = fmaxf(x, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xF, 0xF, false)));
-    x = fmaxf(x, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x4E, 0xF, 0xF, false)));
-    x = fmaxf(x, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x141, 0xF, 0xF, false)));
-    x = fmaxf(x, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x140, 0xF, 0xF, false)));
-    return x;
-}
 
 // Query loads of build_query_terms: thread t handles head h = t / 16 (16
 // threads per head, all in one wave) and the 4-element groups gi = t % 16 +
@@ -414,19 +436,6 @@ struct PartialLds {
     static_assert(TOTAL <= LIMIT, "LDS budget");
 };
 
-// max(x, x of lane ^ 16) and max(x, x of lane ^ 32) without LDS traffic.
-__device__ __forceinline__ float max_xor16(float x)
-{
-    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false,
-                                                    false);
-    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ __forceinline__ float max_xor32(float x)
-{
-    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
-                                                    false);
-    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
 // Value of quad lane V broadcast to the four lanes of every quad.
 template <int V>
 __device__ __forceinline__ float quad_bcast(float x)
@@ -532,7 +541,13 @@ __global__ __launch_bounds__(kThreads, 1) void k_split_partial(AttnArgs a)
         const int r = 16 * q4 + (ln & 15), c16 = 8 * j + 2 * (ln >> 4) + h;
         dpk[i] = (r << 16) | (r * a.d + (c16 < cpr ? 16 * c16 : 0));
     }
-    auto issue = [&](int t, int st) __attribute__((always_inline)) {
+    // Direct loads [I0, I1) of tile t into stage st (the last part also
+    // carries the scale load and, for a gather, the row indices).  A tile's
+    // loads are spread over its issuing phase so that the eight waves do not
+    // all queue on the load path at once.
+    auto issue = [&](int t, int st, auto I0_, auto I1_) __attribute__((always_inline)) {
+        constexpr int I0 = decltype(I0_)::value, I1 = decltype(I1_)::value;
+        constexpr bool LAST = I1 == KW;
         const uint32_t xst = lds_u32 + (uint32_t)(st * L::STAGE);
         const uint32_t sct = lds_u32 + (uint32_t)(L::SC + st * TR * 4);
         const int p0 = c0 + t * TR;
@@ -543,41 +558,55 @@ __global__ __launch_bounds__(kThreads, 1) void k_split_partial(AttnArgs a)
             const uint8_t* tb = a.codes + (size_t)p0 * a.d;
             if (nv >= TR) {
 #pragma unroll
-                for (int i = 0; i < KW; ++i) {
+                for (int i = I0; i < I1; ++i) {
                     const int k = (w + NW * i) % NINS;
                     dma_b128_s(tb, (uint32_t)(dpk[i] & 0xFFFF), xst + 1024 * k);
                 }
-                if (w == 0)
+                if (LAST && w == 0)
                     dma_b32_s(a.scales + p0, (uint32_t)(4 * lane), sct);
             } else {
 #pragma unroll
-                for (int i = 0; i < KW; ++i) {
+                for (int i = I0; i < I1; ++i) {
                     const int k = (w + NW * i) % NINS;
                     const int r = dpk[i] >> 16;
                     const uint32_t off =
                         (uint32_t)((dpk[i] & 0xFFFF) - (r < nv ? 0 : r * a.d));
                     dma_b128_s(tb, off, xst + 1024 * k);
                 }
-                if (w == 0)
+                if (LAST && w == 0)
                     dma_b32_s(a.scales + p0, (uint32_t)(4 * (lane < nv ? lane : 0)), sct);
             }
         } else {
             // Gather: absolute row indices; entries outside [0, t_rows) and
-            // positions past the list reload row 0.
+            // positions past the list reload row 0.  The indices are all
+            // loaded before the first direct load of the part is issued.
+            int32_t rows[(I1 > I0) ? I1 - I0 : 1];
 #pragma unroll
-            for (int i = 0; i < KW; ++i) {
+            for (int i = I0; i < I1; ++i)
+                rows[i - I0] = row_of(p0 + (dpk[i] >> 16));
+            int32_t srow = 0;
+            if (LAST && w == 0)
+                srow = row_of(p0 + lane);
+#pragma unroll
+            for (int i = I0; i < I1; ++i) {
                 const int k = (w + NW * i) % NINS;
                 const int r = dpk[i] >> 16;
                 const int cc = (dpk[i] & 0xFFFF) - r * a.d;
-                const int32_t row = row_of(p0 + r);
+                const int32_t row = rows[i - I0];
                 dma_b128(a.codes + (size_t)(row >= 0 ? row : 0) * a.d + cc, xst + 1024 * k);
             }
-            if (w == 0) {
-                const int32_t srow = row_of(p0 + lane);
+            if (LAST && w == 0) {
                 dma_b32(a.scales + (srow >= 0 ? srow : 0), sct);
                 s_row[st * TR + lane] = srow;
             }
         }
+    };
+    using IC0 = std::integral_constant<int, 0>;
+    using ICA = std::integral_constant<int, (KW + 2) / 3>;
+    using ICB = std::integral_constant<int, (2 * KW + 2) / 3>;
+    using ICK = std::integral_constant<int, KW>;
+    auto issue_all = [&](int t, int st) __attribute__((always_inline)) {
+        issue(t, st, IC0{}, ICK{});
     };
     // Tile t is complete once at most tile t+1's operations remain in flight
     // (two tiles ahead) or none (one tile ahead).
@@ -600,9 +629,9 @@ __global__ __launch_bounds__(kThreads, 1) void k_split_partial(AttnArgs a)
     float4 qin[2 * NB];
     load_query<NKB>(a, qh0, qin);
     if (ntiles > 0)
-        issue(0, 0);
+        issue_all(0, 0);
     if (DIST == 2 && ntiles > 1)
-        issue(1, 1);
+        issue_all(1, 1);
     build_query_terms<NKB>(a, qin, lds + L::QT, s_k);
     lds_barrier();
     v8i qv[Q::NSLOT];
@@ -858,19 +887,27 @@ __global__ __launch_bounds__(kThreads, 1) void k_split_partial(AttnArgs a)
         lds_barrier();  // (A) tile p visible; weights and sums of tile p-1
                         //     complete; stage (p + DIST) % NST (tile p + DIST
                         //     - NST) and buffers p & 1 free
-        if (p + DIST < ntiles)
-            issue(p + DIST, (st + DIST) % NST);
+        const bool more = p + DIST < ntiles;
+        const int sti = (st + DIST) % NST;
+        if (more)
+            issue(p + DIST, sti, IC0{}, ICA{});
         if (w < NW / 2) {
             if (p < ntiles)
                 scores(st);
+            if (more)
+                issue(p + DIST, sti, ICA{}, ICB{});
             if (p >= 1)
                 check_and_context(stp, bufp);
         } else {
             if (p >= 1)
                 check_and_context(stp, bufp);
+            if (more)
+                issue(p + DIST, sti, ICA{}, ICB{});
             if (p < ntiles)
                 scores(st);
         }
+        if (more)
+            issue(p + DIST, sti, ICB{}, ICK{});
         if (p == ntiles)
             break;
 
@@ -959,74 +996,78 @@ __global__ __launch_bounds__(kThreads, 1) void k_split_partial(AttnArgs a)
 
 // ---------------------------------------------------------------------------
 // Log-sum-exp merge of the n_chunks partials of every query-head.
-// Grid (n_qh, ceil(lc / 64)), 256 threads: lane = context column, the four
-// waves split the partials (p = wave, wave + 4, ...) with independent,
-// unrolled loads, then combine through LDS.
+// Grid (n_qh, ceil(lc / 64)), 256 threads: lane = context column; wave wv
+// folds partials p = wv, wv + 4, ... with an online maximum, kMergeBatch
+// partials per batch whose loads are all issued before any is used; the four
+// waves then combine through LDS:
 //   M = max_p m_p;  w_p = 2^(m_p - M);  out = sum_p w_p cl_p / sum_p w_p z_p;
 //   lse = (M + log2 sum_p w_p z_p) * ln 2.
+constexpr int kMergeBatch = 16;
 __global__ __launch_bounds__(256) void k_merge(const float* __restrict__ ws_m,
                                                const float* __restrict__ ws_z,
                                                const float* __restrict__ ws_cl, int32_t n_chunks,
                                                int32_t n_qh, int32_t lc, float* __restrict__ out,
                                                float* __restrict__ lse)
 {
-    __shared__ float s_part[4][64];
-    __shared__ float s_zp[4];
-    __shared__ float s_m[4];
+    __shared__ float s_a[4][64];
+    __shared__ float s_zw[4];
+    __shared__ float s_mw[4];
     const int qh = blockIdx.x;
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
     const int col = blockIdx.y * 64 + lane;
-    // M over all partials
-    float M = -INFINITY;
-    for (int p = threadIdx.x; p < n_chunks; p += 256)
-        M = fmaxf(M, ws_m[(size_t)p * n_qh + qh]);
+    const bool cv = col < lc;
+    float mw = -INFINITY, zw = 0.0f, aw = 0.0f;
+    for (int base = wv; base < n_chunks; base += 4 * kMergeBatch) {
+        float mp[kMergeBatch], zp[kMergeBatch], cp[kMergeBatch];
 #pragma unroll
-    for (int off = 32; off > 0; off >>= 1)
-        M = fmaxf(M, __shfl_xor(M, off));
-    if (lane == 0)
-        s_m[wv] = M;
-    __syncthreads();
-    M = fmaxf(fmaxf(s_m[0], s_m[1]), fmaxf(s_m[2], s_m[3]));
-    float Z = 0.0f, acc = 0.0f;
-    if (M != -INFINITY) {
-        const bool cv = col < lc;
-        int p = wv;
-        for (; p + 12 < n_chunks; p += 16) {
-            float mp[4], zp[4], cp[4];
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                const size_t i = (size_t)(p + 4 * k) * n_qh + qh;
-                mp[k] = ws_m[i];
-                zp[k] = ws_z[i];
-                cp[k] = cv ? ws_cl[i * lc + col] : 0.0f;
-            }
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                const float wgt = (mp[k] == -INFINITY) ? 0.0f : exp2f(mp[k] - M);
-                Z += wgt * zp[k];
-                acc += wgt * cp[k];
-            }
+        for (int k = 0; k < kMergeBatch; ++k) {
+            const int pp = base + 4 * k;
+            const bool ok = pp < n_chunks;
+            const size_t i = (size_t)(ok ? pp : 0) * n_qh + qh;
+            mp[k] = ok ? ws_m[i] : -INFINITY;
+            zp[k] = ok ? ws_z[i] : 0.0f;
+            cp[k] = (ok && cv) ? ws_cl[i * lc + col] : 0.0f;
         }
-        for (; p < n_chunks; p += 4) {
-            const size_t i = (size_t)p * n_qh + qh;
-            const float mp = ws_m[i];
-            const float wgt = (mp == -INFINITY) ? 0.0f : exp2f(mp - M);
-            Z += wgt * ws_z[i];
-            if (cv)
-                acc += wgt * ws_cl[i * lc + col];
+        float bm = -INFINITY;
+#pragma unroll
+        for (int k = 0; k < kMergeBatch; ++k)
+            bm = fmaxf(bm, mp[k]);
+        if (bm == -INFINITY)
+            continue;
+        if (bm > mw) {
+            const float f = (mw == -INFINITY) ? 0.0f : exp2f(mw - bm);
+            zw *= f;
+            aw *= f;
+            mw = bm;
+        }
+#pragma unroll
+        for (int k = 0; k < kMergeBatch; ++k) {
+            const float wgt = (mp[k] == -INFINITY) ? 0.0f : exp2f(mp[k] - mw);
+            zw += wgt * zp[k];
+            aw += wgt * cp[k];
         }
     }
-    s_part[wv][lane] = acc;
-    if (lane == 0)
-        s_zp[wv] = Z;
+    s_a[wv][lane] = aw;
+    if (lane == 0) {
+        s_zw[wv] = zw;
+        s_mw[wv] = mw;
+    }
     __syncthreads();
     if (wv == 0) {
-        const float A = (s_part[0][lane] + s_part[1][lane]) + (s_part[2][lane] + s_part[3][lane]);
-        const float ZZ = (s_zp[0] + s_zp[1]) + (s_zp[2] + s_zp[3]);
-        if (col < lc)
-            out[(size_t)qh * lc + col] = (M == -INFINITY) ? 0.0f : A / ZZ;
+        const float M = fmaxf(fmaxf(s_mw[0], s_mw[1]), fmaxf(s_mw[2], s_mw[3]));
+        float A = 0.0f, Z = 0.0f;
+        if (M != -INFINITY) {
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const float wk = (s_mw[k] == -INFINITY) ? 0.0f : exp2f(s_mw[k] - M);
+                A += wk * s_a[k][lane];
+                Z += wk * s_zw[k];
+            }
+        }
+        if (cv)
+            out[(size_t)qh * lc + col] = (M == -INFINITY) ? 0.0f : A / Z;
         if (lse != nullptr && blockIdx.y == 0 && lane == 0)
-            lse[qh] = (M == -INFINITY) ? -INFINITY : (M + log2f(ZZ)) * 0.69314718055994531f;
+            lse[qh] = (M == -INFINITY) ? -INFINITY : (M + log2f(Z)) * 0.69314718055994531f;
     }
 }
 
