@@ -790,8 +790,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_split_partial(AttnArgs a)
         }
     };
 
-    // Check of tile p-1 (weight buffer bufp) and its context (stage stp).
-    auto check_and_context = [&](int stp, int bufp) __attribute__((always_inline)) {
+    // Check of tile p-1 (weight buffer bufp).
+    auto check = [&](int bufp) __attribute__((always_inline)) {
         // Sums of p + w of tile p-1 per (head, row quarter); every wave reads
         // the same sums and holds the same state, so the vote is uniform
         // across the workgroup and the barriers below are reached by all
@@ -865,19 +865,12 @@ __global__ __launch_bounds__(kThreads, 1) void k_split_partial(AttnArgs a)
             weights_log(bufp);  // tile p-1 under the new state
             lds_barrier();      // (R2) rewritten weights visible; s_cr free
         }
-        if (pv_active) {
-            if (!ctx_half)
-                context(stp, bufp, std::false_type{});
-            else
-                context(stp, bufp, std::true_type{});
-        }
     };
 
     // Phase p: score tile p (ring stage p % NST, buffers p & 1), check the
-    // sums of tile p - 1 and accumulate its context.  The two waves sharing a
-    // SIMD (w and w + 4) take the score MFMAs and the check/context in
-    // opposite orders, so one issues MFMAs while the other runs VALU work.
-    // One extra phase finishes the last tile.
+    // sums of tile p - 1, then accumulate tile p-1's context while tile p's
+    // weights are computed (one block, so the weight arithmetic fills the gaps
+    // between the context MFMAs).  One extra phase finishes the last tile.
     for (int p = 0, st = 0, stp = NST - 1; p <= ntiles;
          ++p, stp = st, st = (st == NST - 1) ? 0 : st + 1) {
         // st = p % NST, stp = (p - 1) % NST
@@ -891,56 +884,64 @@ __global__ __launch_bounds__(kThreads, 1) void k_split_partial(AttnArgs a)
         const int sti = (st + DIST) % NST;
         if (more)
             issue(p + DIST, sti, IC0{}, ICA{});
-        if (w < NW / 2) {
-            if (p < ntiles)
-                scores(st);
-            if (more)
-                issue(p + DIST, sti, ICA{}, ICB{});
-            if (p >= 1)
-                check_and_context(stp, bufp);
+        const bool scored = p < ntiles;
+        if (scored)
+            scores(st);
+        if (p >= 1)
+            check(bufp);
+        if (more)
+            issue(p + DIST, sti, ICA{}, ICB{});
+
+        float chk = 0.0f;
+        if (scored) {
+            // ---- log2-domain scores u of tile p (rows 16rq + 4g + v, head
+            // 16hh + n); masking: rows past the list, invalid gathered rows,
+            // causal limit
+            const float* scs = s_sc + st * TR;
+            const int p0 = c0 + p * TR;
+            const float4 sc4 = *reinterpret_cast<const float4*>(scs + 16 * rq + 4 * g);
+            scv[0] = sc4.x;
+            scv[1] = sc4.y;
+            scv[2] = sc4.z;
+            scv[3] = sc4.w;
+            zsave = zacc;
+#pragma unroll
+            for (int v = 0; v < 4; ++v)
+                u[v] = (acc0[v] + acc1[v]) * scv[v];
+            const bool full = !GATHER && a.mode != kCausal && p0 + TR <= c1;
+            if (!full) {
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    const int r = 16 * rq + 4 * g + v;
+                    bool valid;
+                    if constexpr (GATHER) {
+                        valid = s_row[st * TR + r] >= 0;
+                    } else {
+                        valid = p0 + r < c1 && p0 + r < tlim;
+                    }
+                    u[v] = valid ? u[v] : -INFINITY;
+                }
+            }
+        }
+        const bool ctx = p >= 1 && pv_active;
+        if (ctx && scored && !ctx_half) {
+            context(stp, bufp, std::false_type{});
+            chk = weights_linear(buf);
         } else {
-            if (p >= 1)
-                check_and_context(stp, bufp);
-            if (more)
-                issue(p + DIST, sti, ICA{}, ICB{});
-            if (p < ntiles)
-                scores(st);
+            if (ctx) {
+                if (!ctx_half)
+                    context(stp, bufp, std::false_type{});
+                else
+                    context(stp, bufp, std::true_type{});
+            }
+            if (scored)
+                chk = weights_linear(buf);
         }
         if (more)
             issue(p + DIST, sti, ICB{}, ICK{});
         if (p == ntiles)
             break;
-
-        // ---- log2-domain scores u of tile p (rows 16rq + 4g + v, head
-        // 16hh + n) and this lane's weights
-        const float* scs = s_sc + st * TR;
-        const int p0 = c0 + p * TR;
-        const float4 sc4 = *reinterpret_cast<const float4*>(scs + 16 * rq + 4 * g);
-        scv[0] = sc4.x;
-        scv[1] = sc4.y;
-        scv[2] = sc4.z;
-        scv[3] = sc4.w;
-#pragma unroll
-        for (int v = 0; v < 4; ++v)
-            u[v] = (acc0[v] + acc1[v]) * scv[v];
-        // Masking: rows past the list, invalid gathered rows, causal limit.
-        const bool full = !GATHER && a.mode != kCausal && p0 + TR <= c1;
-        if (!full) {
-#pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                const int r = 16 * rq + 4 * g + v;
-                bool valid;
-                if constexpr (GATHER) {
-                    valid = s_row[st * TR + r] >= 0;
-                } else {
-                    valid = p0 + r < c1 && p0 + r < tlim;
-                }
-                u[v] = valid ? u[v] : -INFINITY;
-            }
-        }
-        zsave = zacc;
-        float chk = weights_linear(buf);
-        // sum over the wave's 16 rows (lane groups g)
+        // sum of p + w over the wave's 16 rows (lane groups g)
         {
             const auto r1 = __builtin_amdgcn_permlane16_swap(__float_as_uint(chk),
                                                              __float_as_uint(chk), false, false);
