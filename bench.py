@@ -49,8 +49,10 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=16,
                     help="heads of the CPU-oracle sample (full T, scaled to 64 heads)")
-    ap.add_argument("--traffic", type=str, default=None,
-                    help="JSON file with rocprofv3 FETCH/WRITE bytes per partial launch")
+    ap.add_argument("--traffic", type=str,
+                    default=os.path.join(ROOT, "profiles", "k_split_partial_long_t262144_traffic.txt"),
+                    help="calibrated rocprofv3 FETCH_SIZE + WRITE_SIZE bytes per partial launch "
+                         "(JSON); used only while the kernel source still matches its hash")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device copy (counter calibration) and exit")
     return ap.parse_args()
@@ -201,10 +203,17 @@ def main():
     achieved = alg_bytes / (part_us * 1e-6) / 1e9
     traffic = None
     if args.traffic and os.path.exists(args.traffic):
-        traffic = json.load(open(args.traffic)).get("bytes_per_launch")
+        import hashlib
+        rec = json.load(open(args.traffic))
+        src = os.path.join(ROOT, "fp8_mla_latent_amd", "csrc", "mla8_kernels.hip")
+        sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+        if rec.get("kernel_source_sha256") == sha:
+            traffic = rec.get("bytes_per_launch")
+        else:
+            log("traffic counters were taken on another kernel source: reporting null")
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                "kernel": "k_split_partial<9>", "kernel_us": round(part_us, 3),
+                "kernel": "k_split_partial<9,false>", "kernel_us": round(part_us, 3),
                 "kernel_us_p10_p90": [round(float(np.percentile(durs, 10)), 3),
                                       round(float(np.percentile(durs, 90)), 3)],
                 "algorithmic_bytes": alg_bytes}
