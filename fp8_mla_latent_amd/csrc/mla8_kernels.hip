@@ -523,6 +523,12 @@ __global__ __launch_bounds__(kThreads, 1) void k_split_partial(AttnArgs a)
     // Per row DMA i of this wave: r << 16 | (r * d + chunk offset), the same
     // for every tile, so it is packed once.
     int dpk[KW];
+    // LDS byte offset of this wave's row DMA i within a stage (wave-uniform,
+    // kept in scalar registers)
+    uint32_t kofs[KW];
+#pragma unroll
+    for (int i = 0; i < KW; ++i)
+        kofs[i] = __builtin_amdgcn_readfirstlane((uint32_t)(1024 * ((w + NW * i) % NINS)));
 #pragma unroll
     for (int i = 0; i < KW; ++i) {
         const int k = (w + NW * i) % NINS;
@@ -558,20 +564,17 @@ __global__ __launch_bounds__(kThreads, 1) void k_split_partial(AttnArgs a)
             const uint8_t* tb = a.codes + (size_t)p0 * a.d;
             if (nv >= TR) {
 #pragma unroll
-                for (int i = I0; i < I1; ++i) {
-                    const int k = (w + NW * i) % NINS;
-                    dma_b128_s(tb, (uint32_t)(dpk[i] & 0xFFFF), xst + 1024 * k);
-                }
+                for (int i = I0; i < I1; ++i)
+                    dma_b128_s(tb, (uint32_t)(dpk[i] & 0xFFFF), xst + kofs[i]);
                 if (LAST && w == 0)
                     dma_b32_s(a.scales + p0, (uint32_t)(4 * lane), sct);
             } else {
 #pragma unroll
                 for (int i = I0; i < I1; ++i) {
-                    const int k = (w + NW * i) % NINS;
                     const int r = dpk[i] >> 16;
                     const uint32_t off =
                         (uint32_t)((dpk[i] & 0xFFFF) - (r < nv ? 0 : r * a.d));
-                    dma_b128_s(tb, off, xst + 1024 * k);
+                    dma_b128_s(tb, off, xst + kofs[i]);
                 }
                 if (LAST && w == 0)
                     dma_b32_s(a.scales + p0, (uint32_t)(4 * (lane < nv ? lane : 0)), sct);
@@ -589,11 +592,10 @@ __global__ __launch_bounds__(kThreads, 1) void k_split_partial(AttnArgs a)
                 srow = row_of(p0 + lane);
 #pragma unroll
             for (int i = I0; i < I1; ++i) {
-                const int k = (w + NW * i) % NINS;
                 const int r = dpk[i] >> 16;
                 const int cc = (dpk[i] & 0xFFFF) - r * a.d;
                 const int32_t row = rows[i - I0];
-                dma_b128(a.codes + (size_t)(row >= 0 ? row : 0) * a.d + cc, xst + 1024 * k);
+                dma_b128(a.codes + (size_t)(row >= 0 ? row : 0) * a.d + cc, xst + kofs[i]);
             }
             if (LAST && w == 0) {
                 dma_b32(a.scales + (srow >= 0 ? srow : 0), sct);
@@ -805,6 +807,11 @@ __global__ __launch_bounds__(kThreads, 1) void k_split_partial(AttnArgs a)
             moved |= !(fmaxf(fmaxf(S4.x, S4.y), fmaxf(S4.z, S4.w)) <= kCheck);
         }
         if (uninit || __any(moved)) {
+            // Keep this path's arithmetic inside the branch: the empty asm
+            // makes u and the scales opaque here, so none of it is hoisted
+            // into the common path.
+            asm volatile("" : "+v"(u[0]), "+v"(u[1]), "+v"(u[2]), "+v"(u[3]), "+v"(scv[0]),
+                         "+v"(scv[1]), "+v"(scv[2]), "+v"(scv[3]));
             // exact maxima of tile p-1 per wave: Tw = max u, Cw = max (u - Tw)
             // + log2 scale, relative so that a large |u| never swallows log2
             // scale
@@ -892,13 +899,12 @@ __global__ __launch_bounds__(kThreads, 1) void k_split_partial(AttnArgs a)
         if (more)
             issue(p + DIST, sti, ICA{}, ICB{});
 
-        float chk = 0.0f;
-        if (scored) {
-            // ---- log2-domain scores u of tile p (rows 16rq + 4g + v, head
-            // 16hh + n); masking: rows past the list, invalid gathered rows,
-            // causal limit
-            const float* scs = s_sc + st * TR;
-            const int p0 = c0 + p * TR;
+        // ---- log2-domain scores u of tile p (rows 16rq + 4g + v, head
+        // 16hh + n) from the score accumulators; masking: rows past the list,
+        // invalid gathered rows, causal limit
+        const float* scs = s_sc + st * TR;
+        const int p0 = c0 + p * TR;
+        auto scores_to_u = [&](bool mask) __attribute__((always_inline)) {
             const float4 sc4 = *reinterpret_cast<const float4*>(scs + 16 * rq + 4 * g);
             scv[0] = sc4.x;
             scv[1] = sc4.y;
@@ -908,8 +914,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_split_partial(AttnArgs a)
 #pragma unroll
             for (int v = 0; v < 4; ++v)
                 u[v] = (acc0[v] + acc1[v]) * scv[v];
-            const bool full = !GATHER && a.mode != kCausal && p0 + TR <= c1;
-            if (!full) {
+            if (mask) {
 #pragma unroll
                 for (int v = 0; v < 4; ++v) {
                     const int r = 16 * rq + 4 * g + v;
@@ -922,10 +927,16 @@ __global__ __launch_bounds__(kThreads, 1) void k_split_partial(AttnArgs a)
                     u[v] = valid ? u[v] : -INFINITY;
                 }
             }
-        }
+        };
+        const bool full = !GATHER && a.mode != kCausal && p0 + TR <= c1;
         const bool ctx = p >= 1 && pv_active;
-        if (ctx && scored && !ctx_half) {
+        float chk = 0.0f;
+        if (ctx && scored && full && !ctx_half) {
+            // Common case, one block: the context MFMAs go into the pipe
+            // behind the score MFMAs, then the weight arithmetic (which waits
+            // on the scores) runs while they drain.
             context(stp, bufp, std::false_type{});
+            scores_to_u(false);
             chk = weights_linear(buf);
         } else {
             if (ctx) {
@@ -934,8 +945,10 @@ __global__ __launch_bounds__(kThreads, 1) void k_split_partial(AttnArgs a)
                 else
                     context(stp, bufp, std::true_type{});
             }
-            if (scored)
+            if (scored) {
+                scores_to_u(!full);
                 chk = weights_linear(buf);
+            }
         }
         if (more)
             issue(p + DIST, sti, ICB{}, ICK{});
