@@ -82,7 +82,8 @@ int run_attention(int32_t op, const uint8_t* codes, const float* scales, int64_t
                   int32_t lc, int32_t rc, const int32_t* sel, int64_t n_list, const float* q_lat,
                   const float* q_rope, int32_t n_qh, int32_t n_heads, int64_t pos0,
                   float sm_scale, float* out, float* lse, void* workspace, size_t ws_bytes,
-                  void* stream)
+                  void* stream, const float* x_new = nullptr, uint8_t* new_codes = nullptr,
+                  float* new_scales = nullptr, int64_t new0 = 0, int64_t n_new = 0)
 {
     const Plan p = make_plan(op, n_list, n_qh);
     const size_t need = ws_bytes_for(p, n_qh, lc);
@@ -118,6 +119,11 @@ int run_attention(int32_t op, const uint8_t* codes, const float* scales, int64_t
     a.ws_cl = reinterpret_cast<float*>(ws + 2 * r256(mz));
     a.out = out;
     a.lse = lse;
+    a.x_new = x_new;
+    a.new_codes = new_codes;
+    a.new_scales = new_scales;
+    a.new0 = (int32_t)new0;
+    a.n_new = (int32_t)n_new;
     return launch_attention(a, static_cast<hipStream_t>(stream), g_ev_before, g_ev_after) ==
                    hipSuccess
                ? MLA8_OK
@@ -203,6 +209,37 @@ int mla8_decode(const uint8_t* kv_codes, const float* kv_scales, int64_t t_rows,
     return run_attention(MLA8_OP_DECODE, kv_codes, kv_scales, t_rows, lc, rc, nullptr, t_rows,
                          q_lat, q_rope, n_heads, n_heads, 0, sm_scale, out, lse, workspace,
                          ws_bytes, stream);
+}
+
+int mla8_append_decode(uint8_t* kv_codes, float* kv_scales, int64_t cap_rows, int64_t* t_rows,
+                       const float* x_new, int64_t n_new, int32_t lc, int32_t rc,
+                       const float* q_lat, const float* q_rope, int32_t n_heads, float sm_scale,
+                       float* out, float* lse, void* workspace, size_t ws_bytes, void* stream)
+{
+    int st = check_shape(lc, rc);
+    if (st != MLA8_OK)
+        return st;
+    if (!kv_codes || !kv_scales || !t_rows || !x_new)
+        return MLA8_E_INVAL;
+    if (cap_rows <= 0 || cap_rows > kMaxRows || n_new <= 0 || *t_rows < 0 || *t_rows > cap_rows)
+        return MLA8_E_INVAL;
+    if (!aligned16(x_new))
+        return MLA8_E_INVAL;
+    if (n_new > kMaxFusedRows)
+        return MLA8_E_RANGE;
+    if (n_new > cap_rows - *t_rows)
+        return MLA8_E_CAPACITY;
+    const int64_t t_new = *t_rows + n_new;
+    st = check_decode_common(kv_codes, kv_scales, t_new, lc, rc, q_lat, q_rope, n_heads, sm_scale,
+                             out);
+    if (st != MLA8_OK)
+        return st;
+    st = run_attention(MLA8_OP_DECODE, kv_codes, kv_scales, t_new, lc, rc, nullptr, t_new, q_lat,
+                       q_rope, n_heads, n_heads, 0, sm_scale, out, lse, workspace, ws_bytes,
+                       stream, x_new, kv_codes, kv_scales, *t_rows, n_new);
+    if (st == MLA8_OK)
+        *t_rows = t_new;
+    return st;
 }
 
 int mla8_decode_sel(const uint8_t* kv_codes, const float* kv_scales, int64_t t_rows, int32_t lc,

@@ -41,7 +41,19 @@ struct AttnArgs {
     float* ws_cl;           // [n_chunks][n_qh][lc] unnormalised context
     float* out;             // [n_qh][lc]
     float* lse;             // [n_qh] or nullptr
+    // Fused append (kDense only): rows [new0, new0 + n_new) of the shadow are
+    // quantized from x_new[n_new][d] by the workgroups whose chunk holds them,
+    // before they stream it.  n_new = 0: nothing to append.
+    const float* x_new;
+    uint8_t* new_codes;     // the shadow codes, writable
+    float* new_scales;      // the shadow scales, writable
+    int32_t new0;
+    int32_t n_new;
 };
+
+// Largest n_new the fused append takes (rows quantized inside the attention
+// launch; larger appends use the quantize kernel).
+constexpr int kMaxFusedRows = 64;
 
 hipError_t launch_quantize(const float* x, int64_t n_rows, int32_t d, uint8_t* codes,
                            float* scales, hipStream_t stream);

@@ -98,20 +98,15 @@ __device__ __forceinline__ float max_xor32(float x)
     return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
-// One wave per row, four rows per workgroup; the row (d <= kMaxRowWidth
-// floats, at most three float4 per lane) stays in registers between the
-// amax pass and the encode pass.
+// One row by one wave: the row (d <= kMaxRowWidth floats, at most three
+// float4 per lane) stays in registers between the amax pass and the encode
+// pass.
 constexpr int kMaxRowWidth = 768;
-__global__ __launch_bounds__(256) void k_quantize_rows(const float* __restrict__ x,
-                                                       int64_t n_rows, int32_t d,
-                                                       uint8_t* __restrict__ codes,
-                                                       float* __restrict__ scales)
+__device__ __forceinline__ void quantize_row_wave(const float* __restrict__ x, int32_t d,
+                                                  uint8_t* __restrict__ codes_row,
+                                                  float* __restrict__ scale_out, int lane)
 {
-    const int lane = threadIdx.x & 63;
-    const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (row >= n_rows)
-        return;
-    const float4* xr = reinterpret_cast<const float4*>(x + row * d);
+    const float4* xr = reinterpret_cast<const float4*>(x);
     const int nv = d >> 2;
     float4 v[3];
 #pragma unroll
@@ -136,7 +131,7 @@ __global__ __launch_bounds__(256) void k_quantize_rows(const float* __restrict__
     float inv = 448.0f / amax;
     if (!(inv <= 3.402823466e38f))
         inv = 0.0f;
-    uint32_t* cr = reinterpret_cast<uint32_t*>(codes + row * d);
+    uint32_t* cr = reinterpret_cast<uint32_t*>(codes_row);
 #pragma unroll
     for (int k = 0; k < 3; ++k) {
         const int i = lane + 64 * k;
@@ -145,7 +140,20 @@ __global__ __launch_bounds__(256) void k_quantize_rows(const float* __restrict__
                     (enc_e4m3(v[k].z * inv) << 16) | (enc_e4m3(v[k].w * inv) << 24);
     }
     if (lane == 0)
-        scales[row] = scale;
+        *scale_out = scale;
+}
+
+// One wave per row, four rows per workgroup.
+__global__ __launch_bounds__(256) void k_quantize_rows(const float* __restrict__ x,
+                                                       int64_t n_rows, int32_t d,
+                                                       uint8_t* __restrict__ codes,
+                                                       float* __restrict__ scales)
+{
+    const int lane = threadIdx.x & 63;
+    const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (row >= n_rows)
+        return;
+    quantize_row_wave(x + row * d, d, codes + row * d, scales + row, lane);
 }
 
 __global__ __launch_bounds__(256) void k_test_encode(const float* __restrict__ x, int64_t n,
@@ -623,6 +631,33 @@ __global__ __launch_bounds__(kThreads, 1) void k_split_partial(AttnArgs a)
         }
     };
 
+    // ---- fused append: fresh rows [f0, f1) inside this chunk are quantized
+    // into the shadow by this workgroup (every head group of the chunk writes
+    // the same bytes) before any wave streams them.  Vector memory operations
+    // of a wave complete in issue order, so stores issued before the first
+    // tile's loads are complete once phase 1 has waited for its tile, and the
+    // phase barrier orders them before any wave's later loads: a chunk whose
+    // fresh rows start at tile DIST + 1 or later quantizes them after the
+    // prologue (the stall on the fresh row's load then overlaps the first
+    // tiles' loads).  Otherwise they are quantized and waited for before the
+    // first load is issued.
+    int f0 = 0, f1 = 0;
+    if (a.n_new > 0) {
+        f0 = max(c0, a.new0);
+        f1 = min(c1, a.new0 + a.n_new);
+    }
+    const bool fresh_late = f0 < f1 && (f0 - c0) / TR >= DIST + 1;
+    auto quantize_fresh = [&]() __attribute__((always_inline)) {
+        for (int r = f0 + w; r < f1; r += NW)
+            quantize_row_wave(a.x_new + (size_t)(r - a.new0) * a.d, a.d,
+                              a.new_codes + (size_t)r * a.d, a.new_scales + r, lane);
+    };
+    if (f0 < f1 && !fresh_late) {
+        quantize_fresh();
+        wait_vmcnt<0>();
+        __syncthreads();
+    }
+
     // ---- query terms for the group, staged in LDS (over the ring stages not
     // yet in flight when they fit there), then each wave keeps its head
     // half's in registers.  The query loads go out first, then the first
@@ -655,6 +690,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_split_partial(AttnArgs a)
                              ? a.pos0 + (qh_own < a.n_qh ? qh_own / a.n_heads : 0) + 1
                              : 0x7FFFFFFF;
     lds_barrier();  // staging area free for the ring
+    if (fresh_late)
+        quantize_fresh();
 
     // Softmax state, identical in every wave, for heads n and 16 + n of the
     // group: m = lazy max of u (z side), d = lazy max of (u - m) + log2 scale

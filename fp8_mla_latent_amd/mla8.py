@@ -25,7 +25,8 @@ MLA8_OP_DECODE = 0
 MLA8_OP_DECODE_SEL = 1
 MLA8_OP_BATCH = 2
 
-EXPORTED = ("mla8_quantize_rows", "mla8_append", "mla8_decode", "mla8_decode_sel", "mla8_batch",
+EXPORTED = ("mla8_quantize_rows", "mla8_append", "mla8_decode", "mla8_append_decode",
+            "mla8_decode_sel", "mla8_batch",
             "mla8_workspace_bytes", "mla8_force_splits", "mla8_plan_splits",
             "mla8_status_string", "mla8_version", "mla8_test_encode", "mla8_profile_events")
 
@@ -47,6 +48,8 @@ def _load() -> ctypes.CDLL:
         "mla8_quantize_rows": (ctypes.c_int, [P, i64, i32, i32, P, P, P]),
         "mla8_append": (ctypes.c_int, [P, P, i64, ctypes.POINTER(i64), P, i64, i32, i32, P]),
         "mla8_decode": (ctypes.c_int, [P, P, i64, i32, i32, P, P, i32, f32, P, P, P, sz, P]),
+        "mla8_append_decode": (ctypes.c_int, [P, P, i64, ctypes.POINTER(i64), P, i64, i32, i32,
+                                              P, P, i32, f32, P, P, P, sz, P]),
         "mla8_decode_sel": (ctypes.c_int,
                             [P, P, i64, i32, i32, P, i64, P, P, i32, f32, P, P, P, sz, P]),
         "mla8_batch": (ctypes.c_int,
@@ -151,6 +154,27 @@ def mla8_decode(kv_codes, kv_scales, t_rows: int, lc: int, rc: int, q_lat, q_rop
                            _ptr(q_rope), h, float(sm_scale), _ptr(out), _ptr(lse), _ptr(ws),
                            ws.numel(), _stream(q_lat)), "mla8_decode")
     return out, lse
+
+
+def mla8_append_decode(kv_codes, kv_scales, t_rows: int, x_new, lc: int, rc: int, q_lat, q_rope,
+                       sm_scale: float, out=None, lse=None, workspace=None,
+                       want_lse: bool = True):
+    """Append x_new [n, lc+rc] at rows [t_rows, t_rows + n) and decode over all
+    t_rows + n rows in one launch: returns (out, lse, new t_rows)."""
+    h = q_lat.shape[0]
+    dev = q_lat.device
+    n = x_new.shape[0]
+    if out is None:
+        out = torch.empty((h, lc), dtype=torch.float32, device=dev)
+    if lse is None and want_lse:
+        lse = torch.empty((h,), dtype=torch.float32, device=dev)
+    ws = _workspace(MLA8_OP_DECODE, t_rows + n, h, 1, lc, dev, workspace)
+    t = ctypes.c_int64(t_rows)
+    _check(lib.mla8_append_decode(_ptr(kv_codes), _ptr(kv_scales), kv_codes.shape[0],
+                                  ctypes.byref(t), _ptr(x_new), n, lc, rc, _ptr(q_lat),
+                                  _ptr(q_rope), h, float(sm_scale), _ptr(out), _ptr(lse),
+                                  _ptr(ws), ws.numel(), _stream(q_lat)), "mla8_append_decode")
+    return out, lse, int(t.value)
 
 
 def mla8_decode_sel(kv_codes, kv_scales, t_rows: int, lc: int, rc: int, sel, q_lat, q_rope,

@@ -114,6 +114,28 @@ MLA8_API int mla8_decode(const uint8_t* kv_codes, const float* kv_scales, int64_
                 void* stream);
 
 /*
+ * Append then decode in one launch: the same result as mla8_append(x_new,
+ * n_new rows) followed by mla8_decode over the new *t_rows rows, with the
+ * fresh rows quantized inside the attention launch by the workgroups whose
+ * row chunk holds them [KV8-base, attention_rows bullet: the producer
+ * quantizes the fresh row; KV8-long, kv_dev_sync8 and split-T bullets].
+ * kv_codes[cap_rows][lc + rc] and kv_scales[cap_rows] receive rows
+ * [*t_rows, *t_rows + n_new) exactly as mla8_append writes them; t_rows is a
+ * [host] pointer advanced by n_new on success.  1 <= n_new <= 64.
+ * Errors: E_INVAL (NULL, n_new <= 0, *t_rows outside [0, cap_rows], and the
+ * mla8_decode checks on the new row count), E_RANGE (n_new > 64),
+ * E_CAPACITY (*t_rows + n_new > cap_rows), E_UNSUPPORTED, E_WORKSPACE
+ * (workspace from mla8_workspace_bytes(MLA8_OP_DECODE, *t_rows + n_new,
+ * n_heads, 1, lc)), E_HIP.  On any error nothing is enqueued and *t_rows is
+ * unchanged.
+ */
+MLA8_API int mla8_append_decode(uint8_t* kv_codes, float* kv_scales, int64_t cap_rows,
+                       int64_t* t_rows, const float* x_new, int64_t n_new, int32_t lc,
+                       int32_t rc, const float* q_lat, const float* q_rope, int32_t n_heads,
+                       float sm_scale, float* out, float* lse, void* workspace,
+                       size_t ws_bytes, void* stream);
+
+/*
  * Selected-row (DSA gather) decode [KV8-long, DSA bullet]: as mla8_decode, but
  * each head attends only the rows listed in sel[0..ns), absolute indices into
  * the shadow read straight from it.  sel is a multiset (repeats count as often

@@ -26,8 +26,8 @@ def declared_symbols():
 
 def test_header_declares_the_product_calls():
     syms = declared_symbols()
-    for name in ("mla8_quantize_rows", "mla8_append", "mla8_decode", "mla8_decode_sel",
-                 "mla8_batch", "mla8_workspace_bytes", "mla8_status_string"):
+    for name in ("mla8_quantize_rows", "mla8_append", "mla8_decode", "mla8_append_decode",
+                 "mla8_decode_sel", "mla8_batch", "mla8_workspace_bytes", "mla8_status_string"):
         assert name in syms
 
 
@@ -145,3 +145,22 @@ def test_plans_and_workspace_sizes():
     finally:
         m.mla8_force_splits(prev)
     assert m.mla8_plan_splits(m.MLA8_OP_DECODE, 4096, 128) == 16
+
+
+def test_append_decode_refuses():
+    f = m.lib.mla8_append_decode
+    t = ctypes.c_int64(10)
+    base = [FAKE, FAKE, 100, ctypes.byref(t), FAKE, 1, 512, 64, FAKE, FAKE, 64, 0.1, FAKE, None,
+            FAKE, 1 << 30, None]
+    for idx, val, want in [(4, None, m.MLA8_E_INVAL),         # no fresh rows
+                           (5, 0, m.MLA8_E_INVAL),            # n_new = 0
+                           (5, 65, m.MLA8_E_RANGE),           # more than the fused maximum
+                           (2, 10, m.MLA8_E_CAPACITY),        # shadow full
+                           (4, FAKE_MISALIGNED, m.MLA8_E_INVAL),
+                           (6, 500, m.MLA8_E_UNSUPPORTED),
+                           (8, None, m.MLA8_E_INVAL),         # no q_lat
+                           (15, 10, m.MLA8_E_WORKSPACE)]:
+        args = list(base)
+        args[idx] = val
+        assert f(*args) == want, (idx, val)
+        assert t.value == 10  # never advanced on an error
