@@ -55,6 +55,7 @@ def lib() -> ctypes.CDLL:
         L.mla8o_decode_sel.argtypes = [P, P, i64, i32, i32, P, i64, P, P, i32, f32, P, P]
         L.mla8o_batch.argtypes = [P, P, i64, i32, i32, P, P, i32, i64, i32, f32, P, P]
         L.mla8o_decode_chunked.argtypes = [P, P, i64, i32, i32, P, P, i32, f32, i64, P, P]
+        L.mla8o_index_scores.argtypes = [P, P, i64, i32, P, P, i32, P]
         L.mla8o_threads.restype = ctypes.c_int
         _lib = L
     return _lib
@@ -156,6 +157,34 @@ def decode_chunked(codes, scales, t_rows, lc, rc, q_lat, q_rope, sm_scale, n_chu
     lib().mla8o_decode_chunked(_ptr(codes), _ptr(scales), t_rows, lc, rc, _ptr(ql), _ptr(qr),
                                h, float(np.float32(sm_scale)), n_chunks, _ptr(out), _ptr(lse))
     return out, lse
+
+
+def index_scores(k_codes, k_scales, q, w):
+    """Indexer scores I_t [T] f64 of one query token: q [n_ih, ihd] f32 (quantized
+    per head inside), w [n_ih] f32, keys e4m3 [T, ihd] with f32 scales [T]."""
+    kc = _c(k_codes, np.uint8)
+    ks = _c(k_scales, np.float32)
+    qq = _c(q, np.float32)
+    ww = _c(w, np.float32)
+    t, ihd = kc.shape
+    n_ih = qq.shape[0]
+    assert qq.shape == (n_ih, ihd) and ww.shape == (n_ih,) and ks.shape == (t,)
+    out = np.empty((t,), np.float64)
+    lib().mla8o_index_scores(_ptr(kc), _ptr(ks), t, ihd, _ptr(qq), _ptr(ww), n_ih, _ptr(out))
+    return out
+
+
+def index_topk(scores, top_k):
+    """[B2-indexer] top-k: the min(top_k, T) rows with the largest scores, ties
+    to the smaller row index, a NaN score below every other; returned as row
+    indices in ascending order (int32)."""
+    s = np.asarray(scores, np.float64)
+    t = np.arange(s.size)
+    nan = np.isnan(s)
+    neg = np.where(nan, 0.0, -s)
+    # sort keys, last is primary: NaN class, then score descending, then row
+    order = np.lexsort((t, neg, nan.astype(np.int8)))
+    return np.sort(order[:min(int(top_k), s.size)]).astype(np.int32)
 
 
 def threads() -> int:

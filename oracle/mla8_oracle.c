@@ -15,6 +15,11 @@
  *   [KV8-long]  same page, second commit message ("KV8 long-context CUDA"),
  *               the kv_dev_sync8 / split-T / DSA-gather bullets, and the PR
  *               description that restates them.
+ *   [B2-indexer] "B1 Mixed FP8/BF16 FMHA first pass" site, commit message of
+ *               the B2 fp8 indexer score + top-k kernel: the query (64 indexer
+ *               heads x 128) quantized to fp8, the keys read as e4m3, then
+ *               dequantization by q_scale * k_scale, ReLU, a weighted sum over
+ *               the heads and a top-k over the rows.
  *
  * Readings of points the pages leave open are listed in the design notes; the
  * ones this file depends on are repeated next to the code that takes them.
@@ -346,4 +351,41 @@ EXPORT int mla8o_threads(void)
     }
 #endif
     return n;
+}
+
+/* ------------------------------------------------------------------------- */
+/* Indexer scores.  [B2-indexer]: for one query token, indexer head j has a
+ * query vector q_j of ihd values, quantized to e4m3 with a scale q_scale_j;
+ * the keys are e4m3 rows with a scale k_scale_t; a head's score for row t is
+ * the dot product of the two byte vectors dequantized by q_scale_j * k_scale_t,
+ * passed through ReLU, and the row's index score is the sum over heads of
+ * w_j times that.  Readings: q_j is quantized with the per-row quantizer
+ * above (its scale is the head's amax/448); the keys are rows of the same
+ * shadow format with Lc = ihd and Rc = 0; w is f32 of either sign.
+ *     I_t = sum_j w_j * max(0, q_scale_j * k_scale_t * sum_d dec(q8_jd) dec(k8_td))
+ * The dot product of decoded bytes is exact in double (each product has at
+ * most 8 significant bits and their exponents span less than 53 bits for
+ * ihd <= 256), so I_t carries only the rounding of its last few operations. */
+EXPORT void mla8o_index_scores(const uint8_t* k_codes, const float* k_scales, int64_t t_rows,
+                               int32_t ihd, const float* q, const float* w, int32_t n_ih,
+                               double* scores)
+{
+    uint8_t* qc = (uint8_t*)malloc((size_t)n_ih * (size_t)ihd);
+    float* qs = (float*)malloc(sizeof(float) * (size_t)(n_ih > 0 ? n_ih : 1));
+    for (int32_t j = 0; j < n_ih; ++j)
+        mla8o_quantize_row(q + (int64_t)j * ihd, ihd, qc + (int64_t)j * ihd, qs + j);
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < t_rows; ++t) {
+        double acc = 0.0;
+        for (int32_t j = 0; j < n_ih; ++j) {
+            double dot = 0.0;
+            for (int32_t i = 0; i < ihd; ++i)
+                dot += mla8o_dec(qc[(int64_t)j * ihd + i]) * mla8o_dec(k_codes[t * ihd + i]);
+            double sj = (double)qs[j] * (double)k_scales[t] * dot;
+            acc += (double)w[j] * (sj > 0.0 ? sj : 0.0);
+        }
+        scores[t] = acc;
+    }
+    free(qc);
+    free(qs);
 }
