@@ -132,6 +132,14 @@ int run_attention(int32_t op, const uint8_t* codes, const float* scales, int64_t
 
 constexpr int64_t kMaxRows = 0x7FFFFFFF;
 
+// Indexer workspace: keys u32 [t], candidates u64 [t], the first-digit
+// histogram and two counters, each section 256-byte aligned.
+size_t r256(size_t b) { return (b + 255) & ~size_t(255); }
+size_t index_ws_bytes(int64_t t)
+{
+    return r256((size_t)t * 4) + r256((size_t)t * 8) + r256(kIndexHistBins * 4) + 256;
+}
+
 }  // namespace
 
 extern "C" {
@@ -278,11 +286,53 @@ int mla8_batch(const uint8_t* kv_codes, const float* kv_scales, int64_t t_rows, 
                          workspace, ws_bytes, stream);
 }
 
+int mla8_index_topk(const uint8_t* k_codes, const float* k_scales, int64_t t_rows, int32_t ihd,
+                    const float* q, const float* w, int32_t n_ih, int32_t top_k, int32_t* sel,
+                    float* scores, void* workspace, size_t ws_bytes, void* stream)
+{
+    if (!k_codes || !k_scales || !q || !w || !sel)
+        return MLA8_E_INVAL;
+    if (t_rows <= 0 || t_rows > kMaxRows || top_k <= 0 || n_ih <= 0 || ihd <= 0)
+        return MLA8_E_INVAL;
+    if (ihd != kIndexDim || (n_ih % 16) != 0 || n_ih > kIndexMaxHeads || top_k > kIndexMaxTopK)
+        return MLA8_E_UNSUPPORTED;
+    if (!aligned16(k_codes) || !aligned16(q) || (reinterpret_cast<uintptr_t>(k_scales) & 3u) ||
+        (reinterpret_cast<uintptr_t>(w) & 3u) || (reinterpret_cast<uintptr_t>(sel) & 3u) ||
+        (reinterpret_cast<uintptr_t>(scores) & 3u))
+        return MLA8_E_INVAL;
+    if (workspace == nullptr || ws_bytes < index_ws_bytes(t_rows))
+        return MLA8_E_WORKSPACE;
+    if (!aligned16(workspace))
+        return MLA8_E_INVAL;
+    char* ws = static_cast<char*>(workspace);
+    IndexArgs a;
+    a.k_codes = k_codes;
+    a.k_scales = k_scales;
+    a.t_rows = (int32_t)t_rows;
+    a.q = q;
+    a.w = w;
+    a.n_ih = n_ih;
+    a.top_k = top_k;
+    a.sel = sel;
+    a.scores = scores;
+    a.keys = reinterpret_cast<uint32_t*>(ws);
+    ws += r256((size_t)t_rows * 4);
+    a.cand = reinterpret_cast<uint64_t*>(ws);
+    ws += r256((size_t)t_rows * 8);
+    a.hist = reinterpret_cast<uint32_t*>(ws);
+    ws += r256(kIndexHistBins * 4);
+    a.counters = reinterpret_cast<uint32_t*>(ws);
+    return launch_index_topk(a, static_cast<hipStream_t>(stream)) == hipSuccess ? MLA8_OK
+                                                                                  : MLA8_E_HIP;
+}
+
 size_t mla8_workspace_bytes(int32_t op, int64_t rows, int32_t n_heads, int32_t n_q, int32_t lc)
 {
-    if (op < MLA8_OP_DECODE || op > MLA8_OP_BATCH || rows <= 0 || rows > kMaxRows ||
+    if (op < MLA8_OP_DECODE || op > MLA8_OP_INDEX || rows <= 0 || rows > kMaxRows ||
         n_heads <= 0 || lc <= 0)
         return 0;
+    if (op == MLA8_OP_INDEX)
+        return index_ws_bytes(rows);
     int64_t n_qh = n_heads;
     if (op == MLA8_OP_BATCH) {
         if (n_q <= 0)

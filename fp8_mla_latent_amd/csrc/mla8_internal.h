@@ -55,6 +55,29 @@ struct AttnArgs {
 // launch; larger appends use the quantize kernel).
 constexpr int kMaxFusedRows = 64;
 
+// One indexer score + top-k call (fp8 indexer keys of kIndexDim bytes per row).
+constexpr int kIndexDim = 128;       // indexer head dimension: one K=128 fp8 MFMA
+constexpr int kIndexMaxHeads = 64;   // indexer heads, a multiple of 16
+constexpr int kIndexMaxTopK = 4096;  // the selection is sorted in LDS
+constexpr int kIndexHistBins = 4096; // first radix digit: the key's top 12 bits
+struct IndexArgs {
+    const uint8_t* k_codes;  // [t_rows][kIndexDim] e4m3
+    const float* k_scales;   // [t_rows]
+    int32_t t_rows;
+    const float* q;          // [n_ih][kIndexDim] f32
+    const float* w;          // [n_ih] f32
+    int32_t n_ih;
+    int32_t top_k;           // < t_rows (t_rows <= top_k selects every row)
+    int32_t* sel;            // [min(top_k, t_rows)] ascending row indices
+    float* scores;           // [t_rows] or nullptr
+    uint32_t* keys;          // workspace [t_rows]: order keys of the scores
+    uint64_t* cand;          // workspace [t_rows]: (key, ~row) candidates
+    uint32_t* hist;          // workspace [kIndexHistBins]
+    uint32_t* counters;      // workspace [2]: candidates written, workgroups done
+};
+
+hipError_t launch_index_topk(const IndexArgs& a, hipStream_t stream);
+
 hipError_t launch_quantize(const float* x, int64_t n_rows, int32_t d, uint8_t* codes,
                            float* scales, hipStream_t stream);
 hipError_t launch_test_encode(const float* x, int64_t n, uint8_t* codes, hipStream_t stream);

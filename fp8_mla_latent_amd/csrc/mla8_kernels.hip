@@ -35,6 +35,7 @@
 //   * Online softmax with a lazy running max: the max is only moved when a
 //     tile beats it by more than 2^8, which keeps rescaling of the register
 //     accumulators off the common path.
+#include "mla8_device.h"
 #include "mla8_internal.h"
 
 #include <math.h>
@@ -42,106 +43,6 @@
 #include <type_traits>
 
 namespace mla8 {
-
-typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
-typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
-typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef int v8i __attribute__((ext_vector_type(8)));
-
-// ---------------------------------------------------------------------------
-// e4m3 encoder on the f32 bit pattern.  Round-to-nearest-even onto 3 mantissa
-// bits, saturation at 448, sign of zero kept, NaN -> 0x00.
-__device__ __forceinline__ uint32_t enc_e4m3(float y)
-{
-    const uint32_t b = __float_as_uint(y);
-    const uint32_t sign = (b >> 24) & 0x80u;
-    const uint32_t a = b & 0x7FFFFFFFu;
-    if (a > 0x7F800000u)
-        return 0u;                  // NaN of either sign: inert zero
-    if (a >= 0x43E00000u)
-        return sign | 0x7Eu;        // |y| >= 448, infinity included
-    uint32_t code;
-    if (a >= 0x3C800000u) {         // |y| >= 2^-6: e4m3 normal range
-        // Drop 20 mantissa bits with round-half-even; a carry out of the kept
-        // mantissa moves into the exponent field by itself.
-        const uint32_t r = a + 0x7FFFFu + ((a >> 20) & 1u);
-        code = (r >> 20) - (120u << 3);  // re-bias the exponent 127 -> 7
-    } else {
-        // e4m3 subnormals are the multiples of 2^-9 below 2^-6; the product is
-        // exact and v_rndne_f32 rounds half to even.  8 -> 0x08 = 2^-6.
-        code = (uint32_t)__builtin_rintf(__uint_as_float(a) * 512.0f);
-    }
-    return sign | code;
-}
-
-// Maximum over the 16 lanes of each row (DPP: quad swaps, then half-row and
-// row mirrors), and over the whole wave (permlane swaps across rows).
-__device__ __forceinline__ float row16_max(float x)
-{
-    x = fmaxf(x, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xF, 0xF, false)));
-    x = fmaxf(x, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x4E, 0xF, 0xF, false)));
-    x = fmaxf(x, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x141, 0xF, 0xF, false)));
-    x = fmaxf(x, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x140, 0xF, 0xF, false)));
-    return x;
-}
-__device__ __forceinline__ float max_xor16(float x)
-{
-    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false,
-                                                    false);
-    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ __forceinline__ float max_xor32(float x)
-{
-    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
-                                                    false);
-    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-
-// One row by one wave: the row (d <= kMaxRowWidth floats, at most three
-// float4 per lane) stays in registers between the amax pass and the encode
-// pass.
-constexpr int kMaxRowWidth = 768;
-__device__ __forceinline__ void quantize_row_wave(const float* __restrict__ x, int32_t d,
-                                                  uint8_t* __restrict__ codes_row,
-                                                  float* __restrict__ scale_out, int lane)
-{
-    const float4* xr = reinterpret_cast<const float4*>(x);
-    const int nv = d >> 2;
-    float4 v[3];
-#pragma unroll
-    for (int k = 0; k < 3; ++k) {
-        const int i = lane + 64 * k;
-        v[k] = (i < nv) ? xr[i] : make_float4(0.f, 0.f, 0.f, 0.f);
-    }
-    float amax = 0.0f;
-#pragma unroll
-    for (int k = 0; k < 3; ++k) {
-        const float e[4] = {fabsf(v[k].x), fabsf(v[k].y), fabsf(v[k].z), fabsf(v[k].w)};
-#pragma unroll
-        for (int c = 0; c < 4; ++c)
-            if (e[c] <= 3.402823466e38f)  // finite only: false for NaN and inf
-                amax = fmaxf(amax, e[c]);
-    }
-    amax = max_xor32(max_xor16(row16_max(amax)));
-    // IEEE f32 quotients (the library is built with correctly rounded f32
-    // division).  The guard: when 448/amax is not finite the row encodes as
-    // signed zeros.
-    const float scale = amax / 448.0f;
-    float inv = 448.0f / amax;
-    if (!(inv <= 3.402823466e38f))
-        inv = 0.0f;
-    uint32_t* cr = reinterpret_cast<uint32_t*>(codes_row);
-#pragma unroll
-    for (int k = 0; k < 3; ++k) {
-        const int i = lane + 64 * k;
-        if (i < nv)
-            cr[i] = enc_e4m3(v[k].x * inv) | (enc_e4m3(v[k].y * inv) << 8) |
-                    (enc_e4m3(v[k].z * inv) << 16) | (enc_e4m3(v[k].w * inv) << 24);
-    }
-    if (lane == 0)
-        *scale_out = scale;
-}
 
 // One wave per row, four rows per workgroup.
 __global__ __launch_bounds__(256) void k_quantize_rows(const float* __restrict__ x,

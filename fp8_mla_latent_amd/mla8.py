@@ -24,9 +24,10 @@ MLA8_E_HIP = -6
 MLA8_OP_DECODE = 0
 MLA8_OP_DECODE_SEL = 1
 MLA8_OP_BATCH = 2
+MLA8_OP_INDEX = 3
 
 EXPORTED = ("mla8_quantize_rows", "mla8_append", "mla8_decode", "mla8_append_decode",
-            "mla8_decode_sel", "mla8_batch",
+            "mla8_decode_sel", "mla8_batch", "mla8_index_topk",
             "mla8_workspace_bytes", "mla8_force_splits", "mla8_plan_splits",
             "mla8_status_string", "mla8_version", "mla8_test_encode", "mla8_profile_events")
 
@@ -54,6 +55,8 @@ def _load() -> ctypes.CDLL:
                             [P, P, i64, i32, i32, P, i64, P, P, i32, f32, P, P, P, sz, P]),
         "mla8_batch": (ctypes.c_int,
                        [P, P, i64, i32, i32, P, P, i32, i64, i32, f32, P, P, P, sz, P]),
+        "mla8_index_topk": (ctypes.c_int,
+                            [P, P, i64, i32, P, P, i32, i32, P, P, P, sz, P]),
         "mla8_workspace_bytes": (sz, [i32, i64, i32, i32, i32]),
         "mla8_force_splits": (i32, [i32]),
         "mla8_plan_splits": (i32, [i32, i64, i32, i32]),
@@ -209,6 +212,27 @@ def mla8_batch(kv_codes, kv_scales, t_rows: int, lc: int, rc: int, q_lat, q_rope
                           _ptr(q_rope), n_q, pos0, h, float(sm_scale), _ptr(out), _ptr(lse),
                           _ptr(ws), ws.numel(), _stream(q_lat)), "mla8_batch")
     return out, lse
+
+
+def mla8_index_topk(k_codes, k_scales, q, w, top_k: int, sel=None, scores=None,
+                    workspace=None, want_scores: bool = False):
+    """fp8 indexer score + top-k over key rows k_codes [T, 128] (e4m3) with
+    scales [T]; q [n_ih, 128] f32, w [n_ih] f32.  Returns (sel int32
+    [min(top_k, T)] ascending, scores f32 [T] or None)."""
+    t, ihd = k_codes.shape
+    n_ih = q.shape[0]
+    dev = q.device
+    if sel is None:
+        sel = torch.empty((min(top_k, t),), dtype=torch.int32, device=dev)
+    if scores is None and want_scores:
+        scores = torch.empty((t,), dtype=torch.float32, device=dev)
+    if workspace is None:
+        need = mla8_workspace_bytes(MLA8_OP_INDEX, t, n_ih, 1, ihd)
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    _check(lib.mla8_index_topk(_ptr(k_codes), _ptr(k_scales), t, ihd, _ptr(q), _ptr(w), n_ih,
+                               top_k, _ptr(sel), _ptr(scores), _ptr(workspace),
+                               workspace.numel(), _stream(q)), "mla8_index_topk")
+    return sel, scores
 
 
 def mla8_profile_events(before: "torch.cuda.Event | None", after: "torch.cuda.Event | None"):

@@ -49,7 +49,13 @@ DSA = Workload("dsa_t131072_ns2048", 64, 512, 64, 131072, seed=4,
 BATCH = Workload("batch_s64_t32768", 64, 512, 64, 32768, seed=5,
                  sm_scale=1.0 / math.sqrt(192.0), n_q=64, n_append=64)
 
-ALL = {w.name: w for w in (TINY, DSV3, LONG, DSA, BATCH)}
+# fp8 indexer over the DSA shadow's rows: 64 indexer heads of dimension 128
+# (n_heads = n_ih, lc = ihd), one 128-byte e4m3 key row per cached row,
+# top-k = the gather's 2048 rows.
+DSA_INDEX = Workload("dsa_index_t131072_k2048", 64, 128, 0, 131072, seed=6, sm_scale=1.0,
+                     n_sel=2048)
+
+ALL = {w.name: w for w in (TINY, DSV3, LONG, DSA, BATCH, DSA_INDEX)}
 
 
 def rng(seed: int) -> np.random.Generator:
@@ -82,3 +88,9 @@ def selection(w: Workload, t_rows: int | None = None, seed_offset: int = 0) -> n
     t = w.t_rows if t_rows is None else t_rows
     g = rng(w.seed * 1000 + 700 + seed_offset)
     return np.sort(g.choice(t, size=w.n_sel, replace=False)).astype(np.int32)
+
+
+def index_weights(w: Workload, seed_offset: int = 0) -> np.ndarray:
+    """Indexer head weights [n_ih] f32 ~ N(0, 1/n_ih) (either sign)."""
+    g = rng(w.seed * 1000 + 900 + seed_offset)
+    return (g.standard_normal(w.n_heads) / np.sqrt(w.n_heads)).astype(np.float32)

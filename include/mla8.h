@@ -63,7 +63,7 @@ enum {
 };
 
 /* Operation codes for mla8_workspace_bytes. */
-enum { MLA8_OP_DECODE = 0, MLA8_OP_DECODE_SEL = 1, MLA8_OP_BATCH = 2 };
+enum { MLA8_OP_DECODE = 0, MLA8_OP_DECODE_SEL = 1, MLA8_OP_BATCH = 2, MLA8_OP_INDEX = 3 };
 
 /*
  * Quantize n_rows f32 rows x[n_rows][lc + rc] into e4m3 codes[n_rows][lc + rc]
@@ -166,9 +166,40 @@ MLA8_API int mla8_batch(const uint8_t* kv_codes, const float* kv_scales, int64_t
                size_t ws_bytes, void* stream);
 
 /*
+ * fp8 indexer score + top-k: the selection that mla8_decode_sel attends.
+ * Source: "B1 Mixed FP8/BF16 FMHA first pass" site, commit message of the B2
+ * fp8 indexer score + top-k kernel: the indexer query is quantized to fp8, the
+ * keys are read as e4m3, each head's dot product is dequantized by
+ * q_scale * k_scale and passed through ReLU, the heads are summed with per-head
+ * weights and the top-k rows are kept.  For one query token:
+ *     I_t = sum_j w[j] * max(0, q_scale_j * k_scales[t] * sum_d q8[j][d] k_codes[t][d])
+ * where q8[j] / q_scale_j is row j of q quantized with the shadow's row
+ * quantizer (the same arithmetic as mla8_quantize_rows).
+ *   k_codes  [t_rows][ihd] e4m3 keys, k_scales [t_rows] f32: rows of the shadow
+ *            format with lc = ihd, rc = 0 (mla8_quantize_rows(x, n, ihd, 0, ...)).
+ *   q        [n_ih][ihd] f32 indexer query (16-byte aligned); w [n_ih] f32 weights.
+ *   sel      [min(top_k, t_rows)] int32 out: the rows with the top_k largest
+ *            I_t, a tie going to the smaller row, a NaN score below all others
+ *            and -0 equal to +0; written in ascending row order.  t_rows <= top_k
+ *            selects every row.
+ *   scores   [t_rows] f32 out (I_t in f32), or NULL.
+ * Supported: ihd = 128, n_ih in {16, 32, 48, 64}, 1 <= top_k <= 4096.
+ * workspace: mla8_workspace_bytes(MLA8_OP_INDEX, t_rows, n_ih, 1, ihd) bytes,
+ * 16-byte aligned; its contents on entry do not matter.
+ * Errors: E_INVAL (NULL pointer, t_rows or top_k < 1, misalignment),
+ * E_UNSUPPORTED (ihd, n_ih or top_k outside the supported set), E_WORKSPACE,
+ * E_HIP.  Calls that overlap on one workspace race.
+ */
+MLA8_API int mla8_index_topk(const uint8_t* k_codes, const float* k_scales, int64_t t_rows,
+                             int32_t ihd, const float* q, const float* w, int32_t n_ih,
+                             int32_t top_k, int32_t* sel, float* scores, void* workspace,
+                             size_t ws_bytes, void* stream);
+
+/*
  * Workspace bytes the given call needs on the current device.  `rows` is the
  * number of rows the call attends: t_rows for MLA8_OP_DECODE, ns for
- * MLA8_OP_DECODE_SEL, pos0 + n_q for MLA8_OP_BATCH.  n_q is ignored except for
+ * MLA8_OP_DECODE_SEL, pos0 + n_q for MLA8_OP_BATCH, t_rows for MLA8_OP_INDEX
+ * (whose n_heads is n_ih and lc is ihd).  n_q is ignored except for
  * MLA8_OP_BATCH.  Returns 0 for invalid arguments.
  */
 MLA8_API size_t mla8_workspace_bytes(int32_t op, int64_t rows, int32_t n_heads, int32_t n_q, int32_t lc);

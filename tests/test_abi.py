@@ -27,7 +27,8 @@ def declared_symbols():
 def test_header_declares_the_product_calls():
     syms = declared_symbols()
     for name in ("mla8_quantize_rows", "mla8_append", "mla8_decode", "mla8_append_decode",
-                 "mla8_decode_sel", "mla8_batch", "mla8_workspace_bytes", "mla8_status_string"):
+                 "mla8_decode_sel", "mla8_batch", "mla8_index_topk", "mla8_workspace_bytes",
+                 "mla8_status_string"):
         assert name in syms
 
 
@@ -164,3 +165,26 @@ def test_append_decode_refuses():
         args[idx] = val
         assert f(*args) == want, (idx, val)
         assert t.value == 10  # never advanced on an error
+
+
+def test_index_topk_refuses():
+    f = m.lib.mla8_index_topk
+    ws = m.lib.mla8_workspace_bytes(m.MLA8_OP_INDEX, 1000, 64, 1, 128)
+    assert ws >= 1000 * 12 + 4096 * 4
+    base = [FAKE, FAKE, 1000, 128, FAKE, FAKE, 64, 100, FAKE, None, FAKE, ws, None]
+    for idx, val, want in [(0, None, m.MLA8_E_INVAL),        # no keys
+                           (4, None, m.MLA8_E_INVAL),        # no query
+                           (5, None, m.MLA8_E_INVAL),        # no weights
+                           (8, None, m.MLA8_E_INVAL),        # no output
+                           (2, 0, m.MLA8_E_INVAL),           # no rows
+                           (7, 0, m.MLA8_E_INVAL),           # top_k = 0
+                           (3, 64, m.MLA8_E_UNSUPPORTED),    # ihd other than 128
+                           (6, 40, m.MLA8_E_UNSUPPORTED),    # n_ih not a multiple of 16
+                           (6, 80, m.MLA8_E_UNSUPPORTED),    # more than 64 heads
+                           (7, 4097, m.MLA8_E_UNSUPPORTED),  # top_k beyond the LDS sort
+                           (4, FAKE_MISALIGNED, m.MLA8_E_INVAL),
+                           (11, ws - 1, m.MLA8_E_WORKSPACE),
+                           (10, None, m.MLA8_E_WORKSPACE)]:
+        args = list(base)
+        args[idx] = val
+        assert f(*args) == want, (idx, val)

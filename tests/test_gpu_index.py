@@ -1,0 +1,173 @@
+"""GPU parity of the fp8 indexer score + top-k (mla8_index_topk) against the
+fp64 CPU oracle, through the C ABI.
+
+Keys are quantized on the GPU (bit-identical to the oracle's quantizer, checked
+here as well).  Scores are compared element by element within a bound derived
+from the f32 arithmetic (below).  The selection is checked two ways: exactly,
+as the top-k of the GPU's own f32 scores under the selection rule (ties to the
+smaller row, NaN lowest, -0 = +0, ascending output); and against the oracle's
+fp64 scores, where a chosen row may only be outranked by an unchosen one
+within the score bound (near-ties may legitimately resolve either way).
+
+Score bound: the MFMA sums 128 exact products in f32, then three f32 products
+and a sum over at most 64 heads follow, so |I_gpu - I_ref| <= c * 2^-24 * A_t
+with c ~ 127 + 64 + 4 and A_t = sum_j |w_j| q_scale_j k_scale_t sum_d
+|q8_jd k8_td|; the tests use 2e-5 * A_t.
+"""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from fp8_mla_latent_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+REL = 2e-5
+
+
+@pytest.fixture(scope="module")
+def m():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from fp8_mla_latent_amd import mla8
+    return mla8
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+
+
+def host(t):
+    torch.cuda.synchronize()
+    return t.cpu().numpy()
+
+
+def _bound(kc, ks, q, w):
+    qc, qs = oracle.quantize_rows(q)
+    aq = np.abs(oracle.dequant(qc, qs))          # [n_ih, 128]
+    ak = np.abs(oracle.dequant(kc, ks))          # [T, 128]
+    return REL * ((ak @ aq.T) @ np.abs(w.astype(np.float64))) + 1e-30
+
+
+def _check(sel, s_gpu, s_ref, bound, k, what):
+    t = s_ref.size
+    kk = min(k, t)
+    assert sel.shape == (kk,), what
+    assert (np.diff(sel) > 0).all() and sel.min() >= 0 and sel.max() < t, what
+    err = np.abs(s_gpu.astype(np.float64) - s_ref)
+    fin = np.isfinite(s_ref)
+    assert (err[fin] <= bound[fin]).all(), (what, float((err / bound)[fin].max()))
+    # exact: the top-k of the GPU's own scores
+    np.testing.assert_array_equal(sel, oracle.index_topk(s_gpu.astype(np.float64), k),
+                                  err_msg=what)
+    # against the oracle: no unchosen row beats a chosen one beyond the bound
+    if kk < t:
+        chosen = np.zeros(t, bool)
+        chosen[sel] = True
+        lo = (s_ref + bound)[chosen].min()
+        hi = (s_ref - bound)[~chosen].max()
+        assert lo >= hi, (what, lo, hi)
+    diff = np.setdiff1d(oracle.index_topk(s_ref, k), sel).size
+    say(f"  {what}: max err/bound {float((err / bound)[fin].max()):.3f}, "
+        f"rows differing from the fp64 selection: {diff}")
+
+
+def _run(m, keys, q, w, k):
+    kd = dev(keys)
+    kc, ks = m.mla8_quantize_rows(kd, keys.shape[1], 0)
+    qd, wd = dev(q), dev(w)
+    sel, sc = m.mla8_index_topk(kc, ks, qd, wd, k, want_scores=True)
+    return host(kc), host(ks), host(sel), host(sc)
+
+
+@pytest.mark.parametrize("t,n_ih,k", [(1, 16, 1), (15, 16, 4), (100, 32, 7), (513, 64, 64),
+                                      (5000, 48, 2048), (4096, 64, 4096), (20000, 64, 1)])
+def test_index_small(m, t, n_ih, k):
+    say(f"index t={t} n_ih={n_ih} k={k}")
+    g = np.random.Generator(np.random.PCG64(1000 + t + n_ih + k))
+    keys = g.standard_normal((t, 128)).astype(np.float32)
+    q = g.standard_normal((n_ih, 128)).astype(np.float32)
+    wt = (g.standard_normal(n_ih) / np.sqrt(n_ih)).astype(np.float32)
+    kc, ks, sel, sc = _run(m, keys, q, wt, k)
+    oc, os_ = oracle.quantize_rows(keys)
+    np.testing.assert_array_equal(kc, oc)
+    np.testing.assert_array_equal(ks.view(np.uint32), os_.view(np.uint32))
+    ref = oracle.index_scores(kc, ks, q, wt)
+    _check(sel, sc, ref, _bound(kc, ks, q, wt), k, f"t={t} n_ih={n_ih} k={k}")
+
+
+def test_index_workload(m):
+    w = W.DSA_INDEX
+    say(f"index workload {w.name}")
+    keys = W.rows(w, w.t_rows)
+    q = W.queries(w)[0]
+    wt = W.index_weights(w)
+    kc, ks, sel, sc = _run(m, keys, q, wt, w.n_sel)
+    ref = oracle.index_scores(kc, ks, q, wt)
+    _check(sel, sc, ref, _bound(kc, ks, q, wt), w.n_sel, w.name)
+
+
+def test_index_ties_zero_and_nan_weights(m):
+    say("index ties: zero and NaN weights")
+    g = np.random.Generator(np.random.PCG64(31))
+    keys = g.standard_normal((3000, 128)).astype(np.float32)
+    q = g.standard_normal((64, 128)).astype(np.float32)
+    for wt, what in [(np.zeros(64, np.float32), "zero"),
+                     (np.full(64, np.nan, np.float32), "nan"),
+                     (-np.abs(g.standard_normal(64)).astype(np.float32), "nonpositive")]:
+        kc, ks, sel, sc = _run(m, keys, q, wt, 500)
+        if what != "nonpositive":
+            # every score equal (0) or NaN: the first rows win
+            np.testing.assert_array_equal(sel, np.arange(500, dtype=np.int32), err_msg=what)
+        ref = oracle.index_scores(kc, ks, q, wt)
+        np.testing.assert_array_equal(sel, oracle.index_topk(sc.astype(np.float64), 500),
+                                      err_msg=what)
+        if what == "zero":
+            assert (sc == 0).all()
+
+
+def test_index_duplicate_rows_straddle_the_boundary(m):
+    # 40 copies of one key row: equal scores; k cuts through the copies, which
+    # must then go to the smallest row indices
+    say("index duplicates at the boundary")
+    g = np.random.Generator(np.random.PCG64(32))
+    keys = (g.standard_normal((2000, 128)) * 0.1).astype(np.float32)
+    q = g.standard_normal((16, 128)).astype(np.float32)
+    wt = np.abs(g.standard_normal(16)).astype(np.float32)
+    dup = np.sort(g.choice(2000, 40, replace=False))
+    keys[dup] = g.standard_normal(128).astype(np.float32) * 5.0  # far above the rest
+    kc, ks, sel, sc = _run(m, keys, q, wt, 25)
+    assert len(set(sc[dup].tolist())) == 1
+    np.testing.assert_array_equal(sel, dup[:25].astype(np.int32))
+
+
+def test_index_selection_feeds_the_gather_decode(m):
+    # the indexer's rows drive mla8_decode_sel over a latent shadow
+    say("index -> decode_sel")
+    wl, wi = W.DSA, W.DSA_INDEX
+    t = 8192
+    g = np.random.Generator(np.random.PCG64(33))
+    keys = g.standard_normal((t, 128)).astype(np.float32)
+    q = g.standard_normal((64, 128)).astype(np.float32)
+    wt = W.index_weights(wi)
+    kc, ks, sel, sc = _run(m, keys, q, wt, 512)
+    x = W.rows(wl, t)
+    codes, scales = m.mla8_quantize_rows(dev(x), wl.lc, wl.rc)
+    ql, qr = W.queries(wl)
+    out, lse = m.mla8_decode_sel(codes, scales, t, wl.lc, wl.rc, dev(sel), dev(ql), dev(qr),
+                                 wl.sm_scale)
+    oc, os_ = oracle.quantize_rows(x)
+    ro, rl = oracle.decode_sel(oc, os_, t, wl.lc, wl.rc, sel, ql, qr, wl.sm_scale)
+    from tests.tolerance import check_attention
+    check_attention(host(out), ro, host(lse), rl, "index -> decode_sel")
