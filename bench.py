@@ -47,7 +47,9 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--layers", type=int, default=8)
+    ap.add_argument("--layers", type=int, default=None,
+                    help="layers per step (default 8 for the decode, 16 for the indexer: "
+                         "more bytes than the 256 MB Infinity Cache holds)")
     ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of a graph")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=16,
@@ -56,6 +58,10 @@ def parse():
                     default=os.path.join(ROOT, "profiles", "k_split_partial_long_t262144_traffic.txt"),
                     help="calibrated rocprofv3 FETCH_SIZE + WRITE_SIZE bytes per partial launch "
                          "(JSON); used only while the kernel source still matches its hash")
+    ap.add_argument("--workload", default="long_t262144",
+                    choices=["long_t262144", "dsa_index_t131072_k2048"],
+                    help="long_t262144: the fused append + split-T decode step (default); "
+                         "dsa_index_t131072_k2048: the fp8 indexer score + top-k")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device copy (counter calibration) and exit")
     return ap.parse_args()
@@ -87,6 +93,168 @@ def cpu_baseline(w, heads):
                       f"T={w.t_rows} rows ({dt:.2f} s), scaled x{w.n_heads / heads:g} to all heads"}
 
 
+def settle(run, log_name):
+    """Untimed replays for SETTLE_S of wall time (GPU clock ramp after idle)."""
+    import torch
+    t_set = time.perf_counter()
+    n = 0
+    while time.perf_counter() - t_set < SETTLE_S:
+        for _ in range(10):
+            run()
+        torch.cuda.synchronize()
+        n += 10
+    log(f"clock settle: {n} untimed {log_name} in {time.perf_counter() - t_set:.3f} s")
+    return n
+
+
+def cpu_baseline_index(w, rows):
+    """The oracle's indexer score + top-k on the first `rows` rows of one
+    layer's keys, scaled to all T rows."""
+    import numpy as np
+
+    import oracle
+    from fp8_mla_latent_amd import workloads as W
+
+    keys = W.rows(w, rows)
+    kc, ks = oracle.quantize_rows(keys)
+    q = W.queries(w)[0]
+    wt = W.index_weights(w)
+    t0 = time.perf_counter()
+    sc = oracle.index_scores(kc, ks, q, wt)
+    oracle.index_topk(sc, w.n_sel)
+    dt = time.perf_counter() - t0
+    ms = dt * 1e3 * (w.t_rows / rows)
+    return {"value": round(ms, 3), "unit": "ms/layer-token", "cores": oracle.threads(),
+            "kind": "oracle",
+            "sample": f"fp64 indexer scores of {rows} of {w.t_rows} rows x {w.n_heads} heads "
+                      f"+ top-{w.n_sel} ({dt:.2f} s), scaled x{w.t_rows / rows:g}"}
+
+
+def bench_index(args):
+    """fp8 indexer score + top-k (k_index_score dominant): one token through
+    --layers layers, each with its own T=131072 x 128 e4m3 key cache."""
+    import numpy as np
+    import torch
+
+    from fp8_mla_latent_amd import mla8 as m
+    from fp8_mla_latent_amd import workloads as W
+
+    w = W.DSA_INDEX
+    L, K, WU = args.layers or 16, args.steps, args.warmup
+    T = w.t_rows
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    layers = []
+    for l in range(L):
+        x = torch.from_numpy(W.rows(w, T, seed_offset=l)).to(dev)
+        kc, ks = m.mla8_quantize_rows(x, w.lc, 0)
+        del x
+        layers.append(dict(kc=kc, ks=ks,
+                           q=torch.from_numpy(W.queries(w, seed_offset=l)[0]).to(dev),
+                           w=torch.from_numpy(W.index_weights(w, seed_offset=l)).to(dev),
+                           sel=torch.empty((w.n_sel,), dtype=torch.int32, device=dev)))
+    ws = torch.empty(m.mla8_workspace_bytes(m.MLA8_OP_INDEX, T, w.n_heads, 1, w.lc),
+                     dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+    log(f"{L} layers of {T} e4m3 key rows quantized")
+
+    def step():
+        for ly in layers:
+            m.mla8_index_topk(ly["kc"], ly["ks"], ly["q"], ly["w"], w.n_sel, sel=ly["sel"],
+                              workspace=ws)
+
+    for _ in range(max(WU, 1)):
+        step()
+    torch.cuda.synchronize()
+    graph = None
+    if not args.no_graph:
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step()
+        torch.cuda.synchronize()
+        run = graph.replay
+    else:
+        run = step
+    n_settle = settle(run, "steps")
+    for _ in range(WU):
+        run()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(K):
+        run()
+    e1.record()
+    torch.cuda.synchronize()
+    ms_step = e0.elapsed_time(e1) / K
+    ms_lt = ms_step / L
+    log(f"step {ms_step:.4f} ms ({L} layers), {ms_lt * 1e3:.2f} us/layer-token")
+
+    n_ev = K * L
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(n_ev)]
+    for a_, b_ in evs:
+        a_.record()
+        b_.record()
+    torch.cuda.synchronize()
+    for _ in range(30):
+        run()
+    i = 0
+    try:
+        for _ in range(K):
+            for ly in layers:
+                m.mla8_profile_events(*evs[i])
+                m.mla8_index_topk(ly["kc"], ly["ks"], ly["q"], ly["w"], w.n_sel, sel=ly["sel"],
+                                  workspace=ws)
+                i += 1
+    finally:
+        m.mla8_profile_events(None, None)
+    torch.cuda.synchronize()
+    durs = np.array([a.elapsed_time(b) for a, b in evs]) * 1e3
+    k_us = float(np.mean(durs))
+    key_bytes = T * (w.lc + 4)
+    alg_bytes = key_bytes + w.n_heads * w.lc * 4 + w.n_heads * 4  # keys + scales, q, w
+    achieved = alg_bytes / (k_us * 1e-6) / 1e9
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                "kernel": "k_index_score<4>", "kernel_us": round(k_us, 3),
+                "kernel_us_p10_p90": [round(float(np.percentile(durs, 10)), 3),
+                                      round(float(np.percentile(durs, 90)), 3)],
+                "algorithmic_bytes": alg_bytes}
+    log(f"score kernel {k_us:.2f} us mean -> {achieved:.0f} GB/s "
+        f"({100 * achieved / HBM_PEAK_GBS:.1f}% of {HBM_PEAK_GBS:.0f})")
+    for ly in layers:
+        s = ly["sel"]
+        assert bool(((s[1:] - s[:-1]) > 0).all()) and int(s.min()) >= 0 and int(s.max()) < T
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline_index(w, 16384)
+        log(f"cpu oracle: {cpu}")
+    rec = {
+        "metric": "ms/layer-token + achieved HBM GB/s (fp8 indexer keys), fp8 indexer score + "
+                  "top-k at T=131072",
+        "value": round(ms_lt, 6),
+        "unit": "ms/layer-token",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": WU,
+        "ms_per_step": round(ms_step, 6),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "e4m3 keys x e4m3 query (fp8 mfma), f32 scores; u32 radix top-k",
+        "data": "synthetic: seeded N(0,1) keys and queries, N(0,1/64) head weights",
+        "config": {"workload": w.name, "indexer_heads": w.n_heads, "index_dim": w.lc,
+                   "t_rows": T, "top_k": w.n_sel, "batch": 1, "layers_per_step": L,
+                   "launch": "hip graph" if graph is not None else "eager"},
+        "key_stream_gb_per_s": round(key_bytes / (ms_lt * 1e-3) / 1e9, 1),
+        "clock_settle": {"seconds": SETTLE_S, "untimed_steps": n_settle},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(rec), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -113,11 +281,15 @@ def main():
         print(json.dumps({"calibrate_copy_bytes": n, "launches": max(args.steps, 1)}))
         return
 
+    if args.workload == "dsa_index_t131072_k2048":
+        bench_index(args)
+        return
+
     from fp8_mla_latent_amd import mla8 as m
     from fp8_mla_latent_amd import workloads as W
 
     w = W.LONG
-    L, K, WU = args.layers, args.steps, args.warmup
+    L, K, WU = args.layers or 8, args.steps, args.warmup
     T, D = w.t_rows, w.d
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -165,14 +337,7 @@ def main():
     # milliseconds of load before its clocks reach their steady state (measured
     # here: the first 40 ms of replays run ~20% slower), so the step is
     # replayed for SETTLE_S of wall time before the W warm-up steps.
-    t_set = time.perf_counter()
-    n_settle = 0
-    while time.perf_counter() - t_set < SETTLE_S:
-        for _ in range(10):
-            run()
-        torch.cuda.synchronize()
-        n_settle += 10
-    log(f"clock settle: {n_settle} untimed steps in {time.perf_counter() - t_set:.3f} s")
+    n_settle = settle(run, "steps")
     for _ in range(WU):
         run()
     torch.cuda.synchronize()

@@ -133,11 +133,13 @@ int run_attention(int32_t op, const uint8_t* codes, const float* scales, int64_t
 constexpr int64_t kMaxRows = 0x7FFFFFFF;
 
 // Indexer workspace: keys u32 [t], candidates u64 [t], the first-digit
-// histogram and two counters, each section 256-byte aligned.
+// histogram copies and the per-slice candidate counts, each section 256-byte
+// aligned.
 size_t r256(size_t b) { return (b + 255) & ~size_t(255); }
 size_t index_ws_bytes(int64_t t)
 {
-    return r256((size_t)t * 4) + r256((size_t)t * 8) + r256(kIndexHistBins * 4) + 256;
+    return r256((size_t)t * 4) + r256((size_t)t * 8) + r256(kIndexHistCopies * kIndexHistBins * 4) +
+           r256((size_t)((t + 4095) / 4096) * 4);
 }
 
 }  // namespace
@@ -294,7 +296,8 @@ int mla8_index_topk(const uint8_t* k_codes, const float* k_scales, int64_t t_row
         return MLA8_E_INVAL;
     if (t_rows <= 0 || t_rows > kMaxRows || top_k <= 0 || n_ih <= 0 || ihd <= 0)
         return MLA8_E_INVAL;
-    if (ihd != kIndexDim || (n_ih % 16) != 0 || n_ih > kIndexMaxHeads || top_k > kIndexMaxTopK)
+    if (ihd != kIndexDim || (n_ih % 16) != 0 || n_ih > kIndexMaxHeads || top_k > kIndexMaxTopK ||
+        t_rows > kIndexMaxRows)
         return MLA8_E_UNSUPPORTED;
     if (!aligned16(k_codes) || !aligned16(q) || (reinterpret_cast<uintptr_t>(k_scales) & 3u) ||
         (reinterpret_cast<uintptr_t>(w) & 3u) || (reinterpret_cast<uintptr_t>(sel) & 3u) ||
@@ -320,10 +323,12 @@ int mla8_index_topk(const uint8_t* k_codes, const float* k_scales, int64_t t_row
     a.cand = reinterpret_cast<uint64_t*>(ws);
     ws += r256((size_t)t_rows * 8);
     a.hist = reinterpret_cast<uint32_t*>(ws);
-    ws += r256(kIndexHistBins * 4);
-    a.counters = reinterpret_cast<uint32_t*>(ws);
-    return launch_index_topk(a, static_cast<hipStream_t>(stream)) == hipSuccess ? MLA8_OK
-                                                                                  : MLA8_E_HIP;
+    ws += r256(kIndexHistCopies * kIndexHistBins * 4);
+    a.wg_cnt = reinterpret_cast<uint32_t*>(ws);
+    return launch_index_topk(a, static_cast<hipStream_t>(stream), g_ev_before, g_ev_after) ==
+                   hipSuccess
+               ? MLA8_OK
+               : MLA8_E_HIP;
 }
 
 size_t mla8_workspace_bytes(int32_t op, int64_t rows, int32_t n_heads, int32_t n_q, int32_t lc)

@@ -22,14 +22,19 @@
 //     in-lane plus two cross-lane adds.  Scores become order-preserving u32
 //     keys; a per-workgroup LDS histogram of the keys' top 12 bits is added
 //     to a global one.
-//   * k_index_select: the first radix digit b1 of the k-th largest key comes
-//     from the global histogram; every workgroup compacts the keys of its
-//     slice whose digit is >= b1 into a candidate list of 64-bit (key, ~row)
-//     values (unique, and larger for a larger score or, on a tie, a smaller
-//     row).  The last workgroup to finish (device-scope release/acquire on a
-//     counter) finds the k-th largest candidate exactly by a radix select over
-//     the 64 bits in LDS histograms, gathers the k rows at or above it and
-//     sorts them ascending in LDS (bitonic).
+//     The histogram has one copy per XCD (workgroups are dispatched
+//     round-robin over the 8 XCDs), so fewer workgroups add to each bin.
+//   * k_index_cand: the first radix digit b1 of the k-th largest key comes
+//     from the summed histogram; every workgroup compacts the keys of its
+//     4096-row slice whose digit is >= b1 into the slice's part of a
+//     candidate buffer, in row order, as (key << 32 | row).
+//   * k_index_final (one workgroup): the candidates, packed in row order into
+//     LDS, give the k-th largest key tau by a radix select in LDS histograms;
+//     the rows with a larger key and the first rows (in row order) with key
+//     tau make the selection, written in ascending order by one ordered
+//     compaction.  When the candidates do not fit in LDS (many equal scores)
+//     it selects over 64-bit (key, ~row) values in global memory and sorts the
+//     k rows in LDS instead.
 #include "mla8_device.h"
 #include "mla8_internal.h"
 
@@ -37,14 +42,15 @@ namespace mla8 {
 
 namespace {
 
-constexpr int kScoreThreads = 256;
-constexpr int kScoreRowsPerGroup = 512;   // 32 blocks of 16 rows, 8 per wave
-constexpr int kScoreBatch = 4;            // blocks whose loads are in flight together
+constexpr int kScoreThreads = 512;
+constexpr int kScoreRowsPerGroup = 512;  // 32 blocks of 16 rows
+constexpr int kScoreBlocksPerWave = kScoreRowsPerGroup / 16 / (kScoreThreads / 64);
 constexpr int kSelectThreads = 512;
-constexpr int kSelectKeysPerThread = 8;
+constexpr int kSelectKeysPerThread = 8;  // contiguous rows per thread
 constexpr int kSelectSlice = kSelectThreads * kSelectKeysPerThread;
 constexpr int kRadixBits = 11;
-constexpr int kRadixBins = 1 << kRadixBits;
+constexpr int kLdsCand = 12288;          // candidates resolved in LDS (96 KB)
+static_assert(kIndexMaxRows / kSelectSlice <= kIndexHistBins, "per-slice tables fit in LDS");
 
 __device__ __forceinline__ f32x4 mfma_fp8(v8i a, v8i b, f32x4 c)
 {
@@ -64,13 +70,12 @@ __device__ __forceinline__ uint32_t order_key(float s)
 
 }  // namespace
 
-__global__ __launch_bounds__(kThreads) void k_index_clear(uint32_t* __restrict__ hist,
-                                                          uint32_t* __restrict__ counters)
+// One workgroup per histogram copy.
+__global__ __launch_bounds__(kThreads) void k_index_clear(uint32_t* __restrict__ hist)
 {
+    uint32_t* h = hist + (size_t)blockIdx.x * kIndexHistBins;
     for (int i = threadIdx.x; i < kIndexHistBins; i += blockDim.x)
-        hist[i] = 0u;
-    if (threadIdx.x < 2)
-        counters[threadIdx.x] = 0u;
+        h[i] = 0u;
 }
 
 // ---------------------------------------------------------------------------
@@ -85,25 +90,50 @@ __global__ __launch_bounds__(kScoreThreads) void k_index_score(IndexArgs a)
 
     const int tid = threadIdx.x;
     const int w = tid >> 6, lane = tid & 63, n = lane & 15, g = lane >> 4;
+    constexpr int NW = kScoreThreads / 64;
+
+    // ---- query loads first, then the wave's key blocks w, w + 8, w + 16,
+    // w + 24, so the query quantization waits only for the query.  Lane group
+    // g of wave w quantizes heads 8w + 4i + g (i = 0, 1), lane n their values
+    // 8n .. 8n + 7; whether a head exists is uniform over the wave.
+    float4 v[2][2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        if (8 * w + 4 * i < 16 * NT) {
+            const float4* src = reinterpret_cast<const float4*>(
+                a.q + (size_t)(8 * w + 4 * i + g) * kIndexDim + 8 * n);
+            v[i][0] = src[0];
+            v[i][1] = src[1];
+        }
+    }
+    // Lane (n, g) loads row n of a key block, K bytes 16g .. 16g + 15 and
+    // 64 + 16g .. 64 + 16g + 15 (the MFMA operand split).
+    const int r0 = blockIdx.x * kScoreRowsPerGroup;
+    uint4 k0[kScoreBlocksPerWave], k1[kScoreBlocksPerWave];
+    float ks[kScoreBlocksPerWave];
+    int rows[kScoreBlocksPerWave];
+#pragma unroll
+    for (int j = 0; j < kScoreBlocksPerWave; ++j) {
+        rows[j] = r0 + 16 * (w + NW * j) + n;
+        const int rc = min(rows[j], a.t_rows - 1);  // rows past the end reload the last
+        const uint8_t* kp = a.k_codes + (size_t)rc * kIndexDim + 16 * g;
+        k0[j] = *reinterpret_cast<const uint4*>(kp);
+        k1[j] = *reinterpret_cast<const uint4*>(kp + 64);
+        ks[j] = a.k_scales[rc];
+    }
+
     for (int i = tid; i < kIndexHistBins; i += kScoreThreads)
         s_hist[i] = 0u;
     if (tid < 16 * NT)
         s_w[tid] = a.w[tid];
 
-    // ---- query quantization, the shadow's per-row arithmetic: lane group g
-    // of wave w takes heads 16w + 4i + g, lane n their values 8n .. 8n + 7
-    if (w < NT) {
-        float4 v[4][2];
+    // ---- query quantization with the shadow's per-row arithmetic
+    {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const float4* src = reinterpret_cast<const float4*>(
-                a.q + (size_t)(16 * w + 4 * i + g) * kIndexDim + 8 * n);
-            v[i][0] = src[0];
-            v[i][1] = src[1];
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int h = 16 * w + 4 * i + g;
+        for (int i = 0; i < 2; ++i) {
+            if (8 * w + 4 * i >= 16 * NT)
+                continue;
+            const int h = 8 * w + 4 * i + g;
             const float e[8] = {v[i][0].x, v[i][0].y, v[i][0].z, v[i][0].w,
                                 v[i][1].x, v[i][1].y, v[i][1].z, v[i][1].w};
             float amax = 0.0f;
@@ -127,8 +157,7 @@ __global__ __launch_bounds__(kScoreThreads) void k_index_score(IndexArgs a)
     }
     __syncthreads();
 
-    // A operand of head tile ht: head 16 ht + n, K bytes 16g .. 16g + 15 and
-    // 64 + 16g .. 64 + 16g + 15 (the same K split as the key operand).
+    // A operand of head tile ht: head 16 ht + n, the same K split as the keys.
     v8i qa[NT];
     float fq[NT][4], fw[NT][4];
 #pragma unroll
@@ -145,50 +174,37 @@ __global__ __launch_bounds__(kScoreThreads) void k_index_score(IndexArgs a)
         }
     }
 
-    // ---- key blocks: wave w takes blocks w, w + 4, ... of the group's rows
-    const int r0 = blockIdx.x * kScoreRowsPerGroup;
-    constexpr int kBlocksPerWave = kScoreRowsPerGroup / 16 / 4;
-    for (int b0 = 0; b0 < kBlocksPerWave; b0 += kScoreBatch) {
-        uint4 k0[kScoreBatch], k1[kScoreBatch];
-        float ks[kScoreBatch];
-        int rows[kScoreBatch];
+    // ---- scores: lane (n, g) gets heads 16 ht + 4g + v of key row n
 #pragma unroll
-        for (int j = 0; j < kScoreBatch; ++j) {
-            rows[j] = r0 + 16 * (w + 4 * (b0 + j)) + n;
-            const int rc = min(rows[j], a.t_rows - 1);  // rows past the end reload the last
-            const uint8_t* kp = a.k_codes + (size_t)rc * kIndexDim + 16 * g;
-            k0[j] = *reinterpret_cast<const uint4*>(kp);
-            k1[j] = *reinterpret_cast<const uint4*>(kp + 64);
-            ks[j] = a.k_scales[rc];
+    for (int j = 0; j < kScoreBlocksPerWave; ++j) {
+        const v8i kb = v8i{(int)k0[j].x, (int)k0[j].y, (int)k0[j].z, (int)k0[j].w,
+                           (int)k1[j].x, (int)k1[j].y, (int)k1[j].z, (int)k1[j].w};
+        float r = 0.0f;
+#pragma unroll
+        for (int ht = 0; ht < NT; ++ht) {
+            const f32x4 acc = mfma_fp8(qa[ht], kb, f32x4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+            for (int v = 0; v < 4; ++v)
+                r += fw[ht][v] * fmaxf((acc[v] * fq[ht][v]) * ks[j], 0.0f);
         }
-#pragma unroll
-        for (int j = 0; j < kScoreBatch; ++j) {
-            const v8i kb = v8i{(int)k0[j].x, (int)k0[j].y, (int)k0[j].z, (int)k0[j].w,
-                               (int)k1[j].x, (int)k1[j].y, (int)k1[j].z, (int)k1[j].w};
-            float r = 0.0f;
-#pragma unroll
-            for (int ht = 0; ht < NT; ++ht) {
-                const f32x4 acc = mfma_fp8(qa[ht], kb, f32x4{0.f, 0.f, 0.f, 0.f});
-#pragma unroll
-                for (int v = 0; v < 4; ++v)
-                    r += fw[ht][v] * fmaxf((acc[v] * fq[ht][v]) * ks[j], 0.0f);
-            }
-            r += __shfl_xor(r, 16);
-            r += __shfl_xor(r, 32);
-            if (g == 0 && rows[j] < a.t_rows) {
-                const uint32_t key = order_key(r);
-                a.keys[rows[j]] = key;
-                if (a.scores)
-                    a.scores[rows[j]] = r;
-                atomicAdd(&s_hist[key >> 20], 1u);
-            }
+        r += __shfl_xor(r, 16);
+        r += __shfl_xor(r, 32);
+        if (g == 0 && rows[j] < a.t_rows) {
+            const uint32_t key = order_key(r);
+            a.keys[rows[j]] = key;
+            if (a.scores)
+                a.scores[rows[j]] = r;
+            atomicAdd(&s_hist[key >> 20], 1u);
         }
     }
     __syncthreads();
+    // into the histogram copy of this workgroup's XCD (dispatch is
+    // round-robin over the 8 XCDs)
+    uint32_t* const hist = a.hist + (size_t)(blockIdx.x % kIndexHistCopies) * kIndexHistBins;
     for (int i = tid; i < kIndexHistBins; i += kScoreThreads) {
         const uint32_t c = s_hist[i];
         if (c)
-            atomicAdd(&a.hist[i], c);
+            atomicAdd(&hist[i], c);
     }
 }
 
@@ -261,105 +277,224 @@ __device__ __forceinline__ void find_bin_from_top(const uint32_t* h, int nb, uin
     __syncthreads();
 }
 
-}  // namespace
-
-__global__ __launch_bounds__(kSelectThreads) void k_index_select(IndexArgs a)
+// Radix select over n values of `bits` significant bits read by get(i):
+// the value of rank rem (1 = largest) and, in *rem_out, its rank among the
+// values equal to it.  s_h must hold 2^kRadixBits counters.
+template <typename Get>
+__device__ __forceinline__ uint64_t radix_select(Get get, uint32_t n, int bits, uint32_t rem,
+                                                 uint32_t* s_h, uint32_t* s_tmp, uint32_t* s_out,
+                                                 uint32_t* rem_out)
 {
-    __shared__ uint32_t s_h[kIndexHistBins];
-    __shared__ uint32_t s_tmp[kSelectThreads / 64];
-    __shared__ uint32_t s_out[2];
-    __shared__ uint32_t s_base;
-    __shared__ uint32_t s_last;
-    __shared__ uint32_t s_rows[kIndexMaxTopK];
-
     const int tid = threadIdx.x;
-    const uint32_t k = (uint32_t)a.top_k;
-
-    // ---- first digit of the k-th largest key, from the global histogram
-    for (int i = tid; i < kIndexHistBins; i += kSelectThreads)
-        s_h[i] = a.hist[i];
-    __syncthreads();
-    find_bin_from_top(s_h, kIndexHistBins, k, s_tmp, s_out);
-    const uint32_t b1 = s_out[0];
-
-    // ---- candidates of this slice: keys whose first digit is >= b1
-    const int t0 = blockIdx.x * kSelectSlice;
-    // (a candidate is never 0: its low word ~row is nonzero)
-    uint64_t c[kSelectKeysPerThread];
-    uint32_t cnt = 0;
-#pragma unroll
-    for (int j = 0; j < kSelectKeysPerThread; ++j) {
-        const int t = t0 + j * kSelectThreads + tid;
-        c[j] = 0;
-        if (t < a.t_rows) {
-            const uint32_t key = a.keys[t];
-            if ((key >> 20) >= b1) {
-                c[j] = ((uint64_t)key << 32) | (uint64_t)(~(uint32_t)t);
-                ++cnt;
-            }
-        }
-    }
-    uint32_t total;
-    const uint32_t off = block_excl_scan(cnt, s_tmp, &total);
-    if (tid == 0)
-        s_base = total ? atomicAdd(&a.counters[0], total) : 0u;
-    __syncthreads();
-    uint32_t pos = s_base + off;
-#pragma unroll
-    for (int j = 0; j < kSelectKeysPerThread; ++j)
-        if (c[j] != 0)
-            a.cand[pos++] = c[j];
-    // publish this workgroup's candidates; the last workgroup selects
-    __threadfence();
-    __syncthreads();
-    if (tid == 0) {
-        const uint32_t done = __hip_atomic_fetch_add(&a.counters[1], 1u, __ATOMIC_ACQ_REL,
-                                                     __HIP_MEMORY_SCOPE_AGENT);
-        s_last = (done == gridDim.x - 1) ? 1u : 0u;
-    }
-    __syncthreads();
-    if (!s_last)
-        return;
-    __threadfence();
-    const uint32_t n_cand = __hip_atomic_load(&a.counters[0], __ATOMIC_RELAXED,
-                                              __HIP_MEMORY_SCOPE_AGENT);
-
-    // ---- radix select of the k-th largest candidate, 11 bits at a time from
-    // the top (the last digit has 9)
     uint64_t prefix = 0;
-    int done_bits = 0;
-    uint32_t rem = k;
-    while (done_bits < 64) {
-        const int width = min(kRadixBits, 64 - done_bits);
-        const int shift = 64 - done_bits - width;
+    int done = 0;
+    while (done < bits) {
+        const int width = min(kRadixBits, bits - done);
+        const int shift = bits - done - width;
         const uint32_t nb = 1u << width;
         for (uint32_t i = tid; i < nb; i += kSelectThreads)
             s_h[i] = 0u;
         __syncthreads();
-        for (uint32_t i = tid; i < n_cand; i += kSelectThreads) {
-            const uint64_t v = a.cand[i];
-            if (done_bits == 0 || (v >> (64 - done_bits)) == prefix)
+        for (uint32_t i = tid; i < n; i += kSelectThreads) {
+            bool in;
+            const uint64_t v = get(i, in);
+            if (in && (done == 0 || (v >> (bits - done)) == prefix))
                 atomicAdd(&s_h[(uint32_t)(v >> shift) & (nb - 1)], 1u);
         }
         __syncthreads();
         find_bin_from_top(s_h, (int)nb, rem, s_tmp, s_out);
         prefix = (prefix << width) | s_out[0];
         rem = s_out[1];
-        done_bits += width;
+        done += width;
         __syncthreads();
     }
-    const uint64_t tau = prefix;  // the k-th largest candidate
+    *rem_out = rem;
+    return prefix;
+}
 
-    // ---- the k rows at or above tau, sorted ascending
-    if (tid == 0)
-        s_base = 0u;
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// Candidates.  Slice i (rows 4096 i ..) is workgroup i's: its keys whose first
+// digit is at least that of the k-th largest key go to cand[4096 i ..] in row
+// order as (key << 32 | row), their count to wg_cnt[i].
+__global__ __launch_bounds__(kSelectThreads) void k_index_cand(IndexArgs a)
+{
+    __shared__ uint32_t s_h[kIndexHistBins];
+    __shared__ uint32_t s_tmp[kSelectThreads / 64];
+    __shared__ uint32_t s_out[2];
+
+    const int tid = threadIdx.x;
+    // thread tid owns rows tb .. tb + 7; its keys load first
+    const int tb = blockIdx.x * kSelectSlice + kSelectKeysPerThread * tid;
+    uint32_t key[kSelectKeysPerThread];
+    if (tb + kSelectKeysPerThread <= a.t_rows) {
+        const uint4 x0 = *reinterpret_cast<const uint4*>(a.keys + tb);
+        const uint4 x1 = *reinterpret_cast<const uint4*>(a.keys + tb + 4);
+        key[0] = x0.x; key[1] = x0.y; key[2] = x0.z; key[3] = x0.w;
+        key[4] = x1.x; key[5] = x1.y; key[6] = x1.z; key[7] = x1.w;
+    } else {
+#pragma unroll
+        for (int j = 0; j < kSelectKeysPerThread; ++j)
+            key[j] = (tb + j < a.t_rows) ? a.keys[tb + j] : 0u;
+    }
+    // the histogram: the sum of the copies
+    for (int i = tid; i < kIndexHistBins; i += kSelectThreads) {
+        uint32_t c = 0;
+#pragma unroll
+        for (int r = 0; r < kIndexHistCopies; ++r)
+            c += a.hist[(size_t)r * kIndexHistBins + i];
+        s_h[i] = c;
+    }
     __syncthreads();
-    for (uint32_t i = tid; i < n_cand; i += kSelectThreads) {
-        const uint64_t v = a.cand[i];
-        if (v >= tau) {
-            const uint32_t p = atomicAdd(&s_base, 1u);
+    find_bin_from_top(s_h, kIndexHistBins, (uint32_t)a.top_k, s_tmp, s_out);
+    const uint32_t b1 = s_out[0];
+
+    uint32_t cnt = 0;
+#pragma unroll
+    for (int j = 0; j < kSelectKeysPerThread; ++j)
+        cnt += (tb + j < a.t_rows && (key[j] >> 20) >= b1) ? 1u : 0u;
+    uint32_t total;
+    uint32_t pos = block_excl_scan(cnt, s_tmp, &total);
+    uint64_t* const dst = a.cand + (size_t)blockIdx.x * kSelectSlice;
+#pragma unroll
+    for (int j = 0; j < kSelectKeysPerThread; ++j)
+        if (tb + j < a.t_rows && (key[j] >> 20) >= b1)
+            dst[pos++] = ((uint64_t)key[j] << 32) | (uint32_t)(tb + j);
+    if (tid == 0)
+        a.wg_cnt[blockIdx.x] = total;
+}
+
+// Final selection, one workgroup: the k-th largest candidate and the rows at
+// or above it, in ascending row order.  n_slices = ceil(t_rows / 4096).
+__global__ __launch_bounds__(kSelectThreads) void k_index_final(IndexArgs a, int32_t n_slices)
+{
+    __shared__ uint32_t s_h[kIndexHistBins];   // per-slice counts, then histograms
+    __shared__ uint32_t s_pre[kIndexHistBins]; // per-slice start in the packed order
+    __shared__ uint32_t s_tmp[kSelectThreads / 64];
+    __shared__ uint32_t s_out[2];
+    __shared__ uint64_t s_c[kLdsCand];
+
+    const int tid = threadIdx.x;
+    const uint32_t k = (uint32_t)a.top_k;
+    const uint32_t ns = (uint32_t)n_slices;
+
+    // ---- per-slice counts and their exclusive prefix
+    const uint32_t per = (ns + kSelectThreads - 1) / kSelectThreads;
+    uint32_t loc = 0;
+    for (uint32_t j = 0; j < per; ++j) {
+        const uint32_t i = tid * per + j;
+        const uint32_t c = (i < ns) ? a.wg_cnt[i] : 0u;
+        if (i < ns)
+            s_h[i] = c;
+        loc += c;
+    }
+    uint32_t n_cand;
+    uint32_t run = block_excl_scan(loc, s_tmp, &n_cand);
+    for (uint32_t j = 0; j < per; ++j) {
+        const uint32_t i = tid * per + j;
+        if (i < ns) {
+            s_pre[i] = run;
+            run += s_h[i];
+        }
+    }
+    __syncthreads();
+
+    if (n_cand <= (uint32_t)kLdsCand) {
+        // ---- candidates into LDS in row order: packed position p lies in
+        // the last slice whose start is <= p
+        for (uint32_t p0 = 0; p0 < n_cand; p0 += kSelectThreads * 8) {
+            uint64_t v[8];
+#pragma unroll
+            for (int b = 0; b < 8; ++b) {
+                const uint32_t p = p0 + b * kSelectThreads + tid;
+                v[b] = 0;
+                if (p < n_cand) {
+                    uint32_t lo = 0, hi = ns - 1;
+                    while (lo < hi) {
+                        const uint32_t mid = (lo + hi + 1) >> 1;
+                        if (s_pre[mid] <= p)
+                            lo = mid;
+                        else
+                            hi = mid - 1;
+                    }
+                    v[b] = a.cand[(size_t)lo * kSelectSlice + (p - s_pre[lo])];
+                }
+            }
+#pragma unroll
+            for (int b = 0; b < 8; ++b) {
+                const uint32_t p = p0 + b * kSelectThreads + tid;
+                if (p < n_cand)
+                    s_c[p] = v[b];
+            }
+        }
+        __syncthreads();
+
+        // ---- the k-th largest key tau; the rows taken are those with a
+        // larger key and the first `rem` (in row order) with key tau
+        uint32_t rem;
+        const uint32_t tau = (uint32_t)radix_select(
+            [&](uint32_t i, bool& in) -> uint64_t {
+                in = true;
+                return s_c[i] >> 32;
+            },
+            n_cand, 32, k, s_h, s_tmp, s_out, &rem);
+
+        // ---- ordered output: thread tid takes a contiguous run of the
+        // packed candidates; scans give tie ranks and output positions
+        const uint32_t ch = (n_cand + kSelectThreads - 1) / kSelectThreads;
+        const uint32_t c0 = min(n_cand, tid * ch), c1 = min(n_cand, c0 + ch);
+        uint32_t nt = 0;
+        for (uint32_t i = c0; i < c1; ++i)
+            nt += ((uint32_t)(s_c[i] >> 32) == tau) ? 1u : 0u;
+        uint32_t all;
+        const uint32_t tie0 = block_excl_scan(nt, s_tmp, &all);
+        uint32_t nsel = 0, tie = tie0;
+        for (uint32_t i = c0; i < c1; ++i) {
+            const uint32_t kk = (uint32_t)(s_c[i] >> 32);
+            nsel += (kk > tau || (kk == tau && tie++ < rem)) ? 1u : 0u;
+        }
+        uint32_t out = block_excl_scan(nsel, s_tmp, &all);
+        tie = tie0;
+        for (uint32_t i = c0; i < c1; ++i) {
+            const uint32_t kk = (uint32_t)(s_c[i] >> 32);
+            if (kk > tau || (kk == tau && tie++ < rem)) {
+                if (out < k)
+                    a.sel[out] = (int32_t)(uint32_t)s_c[i];
+                ++out;
+            }
+        }
+        return;
+    }
+
+    // ---- many candidates (many equal scores): select in global memory over
+    // 64-bit (key, ~row) values, unique and ordered by score then row, then
+    // sort the k rows.  Slot j of the candidate buffer is valid when its
+    // offset in slice j / 4096 is below that slice's count.
+    uint32_t rem;
+    const uint32_t nslot = ns * kSelectSlice;
+    const uint64_t tau = radix_select(
+        [&](uint32_t j, bool& in) -> uint64_t {
+            in = (j & (kSelectSlice - 1)) < s_h[j / kSelectSlice];
+            if (!in)
+                return 0;
+            const uint64_t v = a.cand[j];
+            return (v & 0xFFFFFFFF00000000ull) | (uint64_t)(~(uint32_t)v);
+        },
+        nslot, 64, k, s_pre /* the counts stay in s_h */, s_tmp, s_out, &rem);
+    uint32_t* const s_rows = reinterpret_cast<uint32_t*>(s_c);
+    if (tid == 0)
+        s_out[0] = 0u;
+    __syncthreads();
+    for (uint32_t j = tid; j < nslot; j += kSelectThreads) {
+        if ((j & (kSelectSlice - 1)) >= s_h[j / kSelectSlice])
+            continue;
+        const uint64_t v = a.cand[j];
+        const uint64_t cv = (v & 0xFFFFFFFF00000000ull) | (uint64_t)(~(uint32_t)v);
+        if (cv >= tau) {
+            const uint32_t p = atomicAdd(&s_out[0], 1u);
             if (p < k)
-                s_rows[p] = ~(uint32_t)v;
+                s_rows[p] = (uint32_t)v;
         }
     }
     __syncthreads();
@@ -396,10 +531,16 @@ __global__ __launch_bounds__(256) void k_index_all(int32_t* __restrict__ sel, in
         sel[i] = i;
 }
 
-hipError_t launch_index_topk(const IndexArgs& a, hipStream_t stream)
+hipError_t launch_index_topk(const IndexArgs& a, hipStream_t stream, hipEvent_t ev_before,
+                             hipEvent_t ev_after)
 {
-    hipLaunchKernelGGL(k_index_clear, dim3(1), dim3(kThreads), 0, stream, a.hist, a.counters);
+    hipLaunchKernelGGL(k_index_clear, dim3(kIndexHistCopies), dim3(kThreads), 0, stream, a.hist);
     const unsigned gs = (unsigned)((a.t_rows + kScoreRowsPerGroup - 1) / kScoreRowsPerGroup);
+    if (ev_before != nullptr) {
+        const hipError_t e = hipEventRecord(ev_before, stream);
+        if (e != hipSuccess)
+            return e;
+    }
     switch (a.n_ih / 16) {
     case 1: hipLaunchKernelGGL(k_index_score<1>, dim3(gs), dim3(kScoreThreads), 0, stream, a); break;
     case 2: hipLaunchKernelGGL(k_index_score<2>, dim3(gs), dim3(kScoreThreads), 0, stream, a); break;
@@ -407,12 +548,19 @@ hipError_t launch_index_topk(const IndexArgs& a, hipStream_t stream)
     case 4: hipLaunchKernelGGL(k_index_score<4>, dim3(gs), dim3(kScoreThreads), 0, stream, a); break;
     default: return hipErrorInvalidValue;
     }
+    if (ev_after != nullptr) {
+        const hipError_t e = hipEventRecord(ev_after, stream);
+        if (e != hipSuccess)
+            return e;
+    }
     if (a.t_rows <= a.top_k) {
         hipLaunchKernelGGL(k_index_all, dim3((unsigned)((a.t_rows + 255) / 256)), dim3(256), 0,
                            stream, a.sel, a.t_rows);
     } else {
         const unsigned gsel = (unsigned)((a.t_rows + kSelectSlice - 1) / kSelectSlice);
-        hipLaunchKernelGGL(k_index_select, dim3(gsel), dim3(kSelectThreads), 0, stream, a);
+        hipLaunchKernelGGL(k_index_cand, dim3(gsel), dim3(kSelectThreads), 0, stream, a);
+        hipLaunchKernelGGL(k_index_final, dim3(1), dim3(kSelectThreads), 0, stream, a,
+                           (int32_t)gsel);
     }
     return hipGetLastError();
 }

@@ -60,6 +60,8 @@ constexpr int kIndexDim = 128;       // indexer head dimension: one K=128 fp8 MF
 constexpr int kIndexMaxHeads = 64;   // indexer heads, a multiple of 16
 constexpr int kIndexMaxTopK = 4096;  // the selection is sorted in LDS
 constexpr int kIndexHistBins = 4096; // first radix digit: the key's top 12 bits
+constexpr int kIndexHistCopies = 8;  // one histogram per XCD's workgroups (less contention)
+constexpr int64_t kIndexMaxRows = int64_t(4096) * 4096;  // selection slices fit LDS tables
 struct IndexArgs {
     const uint8_t* k_codes;  // [t_rows][kIndexDim] e4m3
     const float* k_scales;   // [t_rows]
@@ -72,11 +74,13 @@ struct IndexArgs {
     float* scores;           // [t_rows] or nullptr
     uint32_t* keys;          // workspace [t_rows]: order keys of the scores
     uint64_t* cand;          // workspace [t_rows]: (key, ~row) candidates
-    uint32_t* hist;          // workspace [kIndexHistBins]
-    uint32_t* counters;      // workspace [2]: candidates written, workgroups done
+    uint32_t* hist;          // workspace [kIndexHistCopies][kIndexHistBins]
+    uint32_t* wg_cnt;        // workspace [ceil(t_rows / 4096)]: candidates per slice
 };
 
-hipError_t launch_index_topk(const IndexArgs& a, hipStream_t stream);
+// ev_before / ev_after (may be null) are recorded around the score kernel.
+hipError_t launch_index_topk(const IndexArgs& a, hipStream_t stream, hipEvent_t ev_before,
+                             hipEvent_t ev_after);
 
 hipError_t launch_quantize(const float* x, int64_t n_rows, int32_t d, uint8_t* codes,
                            float* scales, hipStream_t stream);

@@ -183,7 +183,8 @@ MLA8_API int mla8_batch(const uint8_t* kv_codes, const float* kv_scales, int64_t
  *            and -0 equal to +0; written in ascending row order.  t_rows <= top_k
  *            selects every row.
  *   scores   [t_rows] f32 out (I_t in f32), or NULL.
- * Supported: ihd = 128, n_ih in {16, 32, 48, 64}, 1 <= top_k <= 4096.
+ * Supported: ihd = 128, n_ih in {16, 32, 48, 64}, 1 <= top_k <= 4096,
+ * t_rows <= 2^24.
  * workspace: mla8_workspace_bytes(MLA8_OP_INDEX, t_rows, n_ih, 1, ihd) bytes,
  * 16-byte aligned; its contents on entry do not matter.
  * Errors: E_INVAL (NULL pointer, t_rows or top_k < 1, misalignment),
@@ -217,10 +218,12 @@ MLA8_API int32_t mla8_plan_splits(int32_t op, int64_t rows, int32_t n_heads, int
 
 /*
  * Measurement hook: while set, every attention call (mla8_decode,
- * mla8_decode_sel, mla8_batch) records the hipEvent_t `before` on its stream
- * just before launching the split-T partial kernel and `after` just after it,
- * so hipEventElapsedTime(before, after) is that kernel's duration.  Pass NULL,
- * NULL to clear.  Events are caller-owned.  Not thread-safe.  Returns MLA8_OK.
+ * mla8_append_decode, mla8_decode_sel, mla8_batch) records the hipEvent_t
+ * `before` on its stream just before launching the split-T partial kernel and
+ * `after` just after it, and mla8_index_topk does the same around its score
+ * kernel, so hipEventElapsedTime(before, after) is that kernel's duration.
+ * Pass NULL, NULL to clear.  Events are caller-owned.  Not thread-safe.
+ * Returns MLA8_OK.
  */
 MLA8_API int mla8_profile_events(void* before, void* after);
 

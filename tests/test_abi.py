@@ -182,6 +182,7 @@ def test_index_topk_refuses():
                            (6, 40, m.MLA8_E_UNSUPPORTED),    # n_ih not a multiple of 16
                            (6, 80, m.MLA8_E_UNSUPPORTED),    # more than 64 heads
                            (7, 4097, m.MLA8_E_UNSUPPORTED),  # top_k beyond the LDS sort
+                           (2, (1 << 24) + 1, m.MLA8_E_UNSUPPORTED),  # more rows than 2^24
                            (4, FAKE_MISALIGNED, m.MLA8_E_INVAL),
                            (11, ws - 1, m.MLA8_E_WORKSPACE),
                            (10, None, m.MLA8_E_WORKSPACE)]:

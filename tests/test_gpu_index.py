@@ -137,6 +137,26 @@ def test_index_ties_zero_and_nan_weights(m):
             assert (sc == 0).all()
 
 
+def test_index_many_equal_scores_take_the_global_path(m):
+    # 20000 equal scores: more candidates than the LDS holds, so the last
+    # workgroup selects in global memory; the first rows win
+    say("index: 20000 tied candidates")
+    g = np.random.Generator(np.random.PCG64(34))
+    keys = g.standard_normal((20000, 128)).astype(np.float32)
+    q = g.standard_normal((32, 128)).astype(np.float32)
+    kc, ks, sel, sc = _run(m, keys, q, np.zeros(32, np.float32), 3000)
+    np.testing.assert_array_equal(sel, np.arange(3000, dtype=np.int32))
+    # half the rows tied at the top: the tie cut still goes by row index
+    wt = np.abs(g.standard_normal(32)).astype(np.float32)
+    keys2 = keys.copy()
+    top = np.sort(g.choice(20000, 15000, replace=False))
+    qs = q.astype(np.float64).sum(axis=0)
+    keys2[top] = (30.0 * qs / np.linalg.norm(qs)).astype(np.float32)  # far above random rows
+    kc, ks, sel, sc = _run(m, keys2, q, wt, 4000)
+    np.testing.assert_array_equal(sel, top[:4000].astype(np.int32))
+    np.testing.assert_array_equal(sel, oracle.index_topk(sc.astype(np.float64), 4000))
+
+
 def test_index_duplicate_rows_straddle_the_boundary(m):
     # 40 copies of one key row: equal scores; k cuts through the copies, which
     # must then go to the smallest row indices
