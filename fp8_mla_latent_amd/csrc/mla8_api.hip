@@ -371,13 +371,16 @@ const char* mla8_status_string(int status)
     switch (status) {
     case MLA8_OK: return "ok";
     case MLA8_E_INVAL: return "invalid argument (NULL pointer, bad size or misaligned buffer)";
-    case MLA8_E_RANGE: return "row range outside the shadow (pos0 + n_q > t_rows)";
+    case MLA8_E_RANGE:
+        return "row range outside the shadow (pos0 + n_q > t_rows, or an append that does not "
+               "start at the file's committed end)";
     case MLA8_E_CAPACITY: return "append would exceed cap_rows";
     case MLA8_E_WORKSPACE: return "workspace smaller than mla8_workspace_bytes()";
     case MLA8_E_UNSUPPORTED:
-        return "unsupported shape: need 16<=lc<=512, 0<=rc<=128, both multiples of 16, "
-               "lc+rc<=640";
-    case MLA8_E_HIP: return "HIP launch failed";
+        return "unsupported shape or mode: need 16<=lc<=512, 0<=rc<=128, both multiples of 16, "
+               "lc+rc<=640 (indexer: ihd 128, n_ih a multiple of 16 up to 64, top_k <= 4096)";
+    case MLA8_E_HIP: return "HIP launch or copy failed";
+    case MLA8_E_IO: return "file I/O failed, or no valid header in the file";
     default: return "unknown status";
     }
 }

@@ -21,13 +21,15 @@ MLA8_E_CAPACITY = -3
 MLA8_E_WORKSPACE = -4
 MLA8_E_UNSUPPORTED = -5
 MLA8_E_HIP = -6
+MLA8_E_IO = -7
 MLA8_OP_DECODE = 0
 MLA8_OP_DECODE_SEL = 1
 MLA8_OP_BATCH = 2
 MLA8_OP_INDEX = 3
 
 EXPORTED = ("mla8_quantize_rows", "mla8_append", "mla8_decode", "mla8_append_decode",
-            "mla8_decode_sel", "mla8_batch", "mla8_index_topk",
+            "mla8_decode_sel", "mla8_batch", "mla8_index_topk", "mla8_kvfile_create",
+            "mla8_kvfile_info", "mla8_kvfile_append", "mla8_kvfile_load",
             "mla8_workspace_bytes", "mla8_force_splits", "mla8_plan_splits",
             "mla8_status_string", "mla8_version", "mla8_test_encode", "mla8_profile_events")
 
@@ -57,6 +59,14 @@ def _load() -> ctypes.CDLL:
                        [P, P, i64, i32, i32, P, P, i32, i64, i32, f32, P, P, P, sz, P]),
         "mla8_index_topk": (ctypes.c_int,
                             [P, P, i64, i32, P, P, i32, i32, P, P, P, sz, P]),
+        "mla8_kvfile_create": (ctypes.c_int, [ctypes.c_char_p, i32, i32, i32]),
+        "mla8_kvfile_info": (ctypes.c_int, [ctypes.c_char_p, ctypes.POINTER(i32),
+                                            ctypes.POINTER(i32), ctypes.POINTER(i32),
+                                            ctypes.POINTER(i32), ctypes.POINTER(i64)]),
+        "mla8_kvfile_append": (ctypes.c_int, [ctypes.c_char_p, i32, P, P, i64, i64, i32, i32,
+                                              i32, P]),
+        "mla8_kvfile_load": (ctypes.c_int, [ctypes.c_char_p, i32, P, P, i64,
+                                            ctypes.POINTER(i64), i32, i32, i32, P, sz, P]),
         "mla8_workspace_bytes": (sz, [i32, i64, i32, i32, i32]),
         "mla8_force_splits": (i32, [i32]),
         "mla8_plan_splits": (i32, [i32, i64, i32, i32]),
@@ -233,6 +243,58 @@ def mla8_index_topk(k_codes, k_scales, q, w, top_k: int, sel=None, scores=None,
                                top_k, _ptr(sel), _ptr(scores), _ptr(workspace),
                                workspace.numel(), _stream(q)), "mla8_index_topk")
     return sel, scores
+
+
+def _mem_ptr(t) -> int:
+    """Address of a torch tensor (either device) or a numpy array."""
+    if isinstance(t, torch.Tensor):
+        return t.data_ptr()
+    return t.ctypes.data
+
+
+def _ptr_table(ts):
+    return (ctypes.c_void_p * len(ts))(*[_mem_ptr(t) for t in ts])
+
+
+def _on_device(t) -> bool:
+    return isinstance(t, torch.Tensor) and t.is_cuda
+
+
+def mla8_kvfile_create(path: str, n_layers: int, lc: int, rc: int) -> None:
+    _check(lib.mla8_kvfile_create(os.fsencode(path), n_layers, lc, rc), "mla8_kvfile_create")
+
+
+def mla8_kvfile_info(path: str) -> dict:
+    v, nl, lc, rc = (ctypes.c_int32() for _ in range(4))
+    nt = ctypes.c_int64()
+    _check(lib.mla8_kvfile_info(os.fsencode(path), ctypes.byref(v), ctypes.byref(nl),
+                                ctypes.byref(lc), ctypes.byref(rc), ctypes.byref(nt)),
+           "mla8_kvfile_info")
+    return {"version": v.value, "n_layers": nl.value, "lc": lc.value, "rc": rc.value,
+            "n_tokens": nt.value}
+
+
+def mla8_kvfile_append(path: str, codes, scales, t0: int, n_tok: int, lc: int, rc: int) -> None:
+    """Append rows [t0, t0 + n_tok) of every layer's shadow (lists of device
+    tensors, or of host arrays) to the file."""
+    dev = _on_device(codes[0])
+    _check(lib.mla8_kvfile_append(os.fsencode(path), len(codes), _ptr_table(codes),
+                                  _ptr_table(scales), t0, n_tok, lc, rc, int(dev),
+                                  _stream(codes[0]) if dev else None), "mla8_kvfile_append")
+
+
+def mla8_kvfile_load(path: str, codes, scales, lc: int, rc: int, workspace=None) -> int:
+    """Load the file's committed tokens into every layer's shadow; returns t_rows."""
+    dev = _on_device(codes[0])
+    t = ctypes.c_int64(0)
+    ws_ptr, ws_n = None, 0
+    if workspace is not None:
+        ws_ptr, ws_n = _mem_ptr(workspace), workspace.numel()
+    _check(lib.mla8_kvfile_load(os.fsencode(path), len(codes), _ptr_table(codes),
+                                _ptr_table(scales), codes[0].shape[0], ctypes.byref(t), lc, rc,
+                                int(dev), ws_ptr, ws_n, _stream(codes[0]) if dev else None),
+           "mla8_kvfile_load")
+    return int(t.value)
 
 
 def mla8_profile_events(before: "torch.cuda.Event | None", after: "torch.cuda.Event | None"):

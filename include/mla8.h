@@ -59,7 +59,8 @@ enum {
     MLA8_E_CAPACITY = -3,    /* append beyond cap_rows; *t_rows left unchanged */
     MLA8_E_WORKSPACE = -4,   /* workspace smaller than mla8_workspace_bytes() */
     MLA8_E_UNSUPPORTED = -5, /* shape outside the supported set (see above) */
-    MLA8_E_HIP = -6          /* a HIP launch or device query failed */
+    MLA8_E_HIP = -6,         /* a HIP launch, copy or device query failed */
+    MLA8_E_IO = -7           /* shadow file: I/O failed or no valid header */
 };
 
 /* Operation codes for mla8_workspace_bytes. */
@@ -226,6 +227,65 @@ MLA8_API int32_t mla8_plan_splits(int32_t op, int64_t rows, int32_t n_heads, int
  * Returns MLA8_OK.
  */
 MLA8_API int mla8_profile_events(void* before, void* after);
+
+/*
+ * Persistent shadow files  [KV8-base, the .coli_kv v2 bullet: a versioned file
+ * whose header names the row type, appended through a persistent handle and a
+ * staging buffer, holding fp8 rows plus scales; files of the previous version
+ * hold f32 rows, are quantized when a session resumes and stay untouched on
+ * disk until the first append rewrites them in the new version].
+ * These calls do host file I/O and SYNCHRONIZE `stream` (the one exception to
+ * the enqueue-only rule); they are not for the decode loop's critical path.
+ *
+ * Format (little-endian): two 64-byte header slots, then the body from byte
+ * 128, token-major.  Slot: "MLA8KV  ", u32 version (1 = f32 rows, 2 = e4m3
+ * rows + f32 scale), u32 n_layers, u32 lc, u32 rc, u64 n_tokens (committed),
+ * u64 seq, u32 FNV-1a of the 40 bytes before it, zero padding.  The valid
+ * slot with the larger seq is the committed state.  Version-2 token t, at
+ * 128 + t * n_layers * (D + 4): per layer, D = lc + rc code bytes then the
+ * scale.  Version-1 token: per layer, D f32 values.
+ * Crash safety: an append writes and flushes the new tokens past the committed
+ * end, then writes and flushes the other header slot; a crash leaves the
+ * previous commit readable.
+ *
+ * kv_codes / kv_scales are [host] arrays of n_layers pointers to each layer's
+ * shadow (codes[cap][lc + rc], scales[cap]); the shadows are device memory
+ * when on_device != 0, host memory otherwise.
+ */
+
+/* A new empty version-2 file (truncates an existing one).
+ * Errors: E_INVAL (NULL path, n_layers < 1), E_UNSUPPORTED (shape), E_IO. */
+MLA8_API int mla8_kvfile_create(const char* path, int32_t n_layers, int32_t lc, int32_t rc);
+
+/* [host] outputs: the committed header.  Errors: E_INVAL, E_IO. */
+MLA8_API int mla8_kvfile_info(const char* path, int32_t* version, int32_t* n_layers, int32_t* lc,
+                              int32_t* rc, int64_t* n_tokens);
+
+/* Append shadow rows [t0, t0 + n_tok) of every layer as tokens t0 .. of the
+ * file; t0 must equal the file's committed n_tokens.  A version-1 file is
+ * first rewritten as version 2 from shadow rows [0, t0 + n_tok) (the shadows
+ * hold its rows quantized by mla8_kvfile_load) into `path`.v2tmp, which then
+ * replaces `path`.  n_tok = 0 is a no-op.
+ * Errors: E_INVAL (NULL pointer, negative t0 / n_tok, a file of another
+ * n_layers / lc / rc), E_UNSUPPORTED (shape), E_RANGE (t0 != committed
+ * n_tokens), E_HIP (device copy), E_IO. */
+MLA8_API int mla8_kvfile_append(const char* path, int32_t n_layers, const uint8_t* const* kv_codes,
+                                const float* const* kv_scales, int64_t t0, int64_t n_tok,
+                                int32_t lc, int32_t rc, int32_t on_device, void* stream);
+
+/* Load the committed tokens into shadow rows [0, n_tokens) of every layer and
+ * set *t_rows [host] = n_tokens.  Version-2 rows are copied as they are.
+ * Version-1 (f32) rows are quantized on the device exactly as
+ * mla8_quantize_rows does, through `workspace` (device, 16-byte aligned, at
+ * least (lc + rc) * 4 bytes; more bytes convert more rows per round trip);
+ * the file itself is not changed.  Errors: E_INVAL (NULL pointer, cap_rows < 1,
+ * a file of another n_layers / lc / rc), E_UNSUPPORTED (shape; a version-1
+ * file into host shadows), E_CAPACITY (n_tokens > cap_rows, nothing loaded),
+ * E_WORKSPACE (version 1 without a large enough workspace), E_HIP, E_IO. */
+MLA8_API int mla8_kvfile_load(const char* path, int32_t n_layers, uint8_t* const* kv_codes,
+                              float* const* kv_scales, int64_t cap_rows, int64_t* t_rows,
+                              int32_t lc, int32_t rc, int32_t on_device, void* workspace,
+                              size_t ws_bytes, void* stream);
 
 /* Human-readable text for a status code (static storage). */
 MLA8_API const char* mla8_status_string(int status);
