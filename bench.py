@@ -59,9 +59,10 @@ def parse():
                     help="calibrated rocprofv3 FETCH_SIZE + WRITE_SIZE bytes per partial launch "
                          "(JSON); used only while the kernel source still matches its hash")
     ap.add_argument("--workload", default="long_t262144",
-                    choices=["long_t262144", "dsa_index_t131072_k2048"],
+                    choices=["long_t262144", "dsa_index_t131072_k2048", "kvfile_t262144"],
                     help="long_t262144: the fused append + split-T decode step (default); "
-                         "dsa_index_t131072_k2048: the fp8 indexer score + top-k")
+                         "dsa_index_t131072_k2048: the fp8 indexer score + top-k; "
+                         "kvfile_t262144: resume a persisted shadow file into device shadows")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device copy (counter calibration) and exit")
     return ap.parse_args()
@@ -255,6 +256,85 @@ def bench_index(args):
     print(json.dumps(rec), flush=True)
 
 
+def bench_kvfile(args):
+    """Persistent shadow file: append one token per layer (latency) and resume
+    a T=262144 file into device shadows (throughput).  Host file I/O through
+    the page cache plus pageable host-to-device copies; no GPU kernel."""
+    import tempfile
+
+    import numpy as np
+    import torch
+
+    from fp8_mla_latent_amd import mla8 as m
+    from fp8_mla_latent_amd import workloads as W
+
+    w = W.LONG
+    L, T, D = args.layers or 4, w.t_rows, w.d
+    dev = torch.device("cuda:0")
+    codes, scales = [], []
+    for l in range(L):
+        x = torch.from_numpy(W.rows(w, T, seed_offset=l)).to(dev)
+        c, sc = m.mla8_quantize_rows(x, w.lc, w.rc)
+        del x
+        codes.append(c)
+        scales.append(sc)
+    torch.cuda.synchronize()
+    tmpdir = tempfile.mkdtemp(prefix="mla8kv_", dir=os.environ.get("TMPDIR", "/tmp"))
+    path = os.path.join(tmpdir, "shadow.mla8kv")
+    try:
+        m.mla8_kvfile_create(path, L, w.lc, w.rc)
+        t0 = time.perf_counter()
+        m.mla8_kvfile_append(path, codes, scales, 0, T - 64, w.lc, w.rc)
+        t_bulk = time.perf_counter() - t0
+        lat = []
+        for t in range(T - 64, T):  # one token (all layers) per call, as a decode loop would
+            t1 = time.perf_counter()
+            m.mla8_kvfile_append(path, codes, scales, t, 1, w.lc, w.rc)
+            lat.append(time.perf_counter() - t1)
+        file_bytes = os.path.getsize(path)
+        c2 = [torch.empty_like(c) for c in codes]
+        s2 = [torch.empty_like(sc) for sc in scales]
+        loads = []
+        for _ in range(max(args.steps // 10, 3)):
+            t1 = time.perf_counter()
+            assert m.mla8_kvfile_load(path, c2, s2, w.lc, w.rc) == T
+            loads.append(time.perf_counter() - t1)
+        for l in range(L):
+            assert torch.equal(c2[l], codes[l]) and torch.equal(s2[l], scales[l])
+    finally:
+        for f in os.listdir(tmpdir):
+            os.unlink(os.path.join(tmpdir, f))
+        os.rmdir(tmpdir)
+    body = L * T * (D + 4)
+    load_s = float(np.median(loads))
+    rec = {
+        "metric": "GB/s shadow-file resume into device shadows (T=262144), us per appended token",
+        "value": round(body / load_s / 1e9, 3),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": len(loads),
+        "warmup": 0,
+        "ms_per_step": round(load_s * 1e3, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "e4m3 rows + f32 scales (bytes copied as stored)",
+        "data": "synthetic: seeded N(0,1) rows quantized on the GPU",
+        "config": {"workload": "kvfile_t262144", "layers": L, "t_rows": T, "row_bytes": D + 4,
+                   "file_bytes": file_bytes},
+        "append_us_per_token": {"median": round(float(np.median(lat)) * 1e6, 1),
+                                "p90": round(float(np.percentile(lat, 90)) * 1e6, 1)},
+        "bulk_append_gb_per_s": round(L * (T - 64) * (D + 4) / t_bulk / 1e9, 3),
+        "roofline": None,
+        "cpu_baseline": None,
+        "note": "host I/O path (page cache, fdatasync per commit, pageable copies); "
+                "no device kernel, so no roofline",
+    }
+    log(f"resume {load_s * 1e3:.1f} ms for {body / 1e6:.0f} MB; append median "
+        f"{rec['append_us_per_token']['median']} us/token")
+    print(json.dumps(rec), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -283,6 +363,9 @@ def main():
 
     if args.workload == "dsa_index_t131072_k2048":
         bench_index(args)
+        return
+    if args.workload == "kvfile_t262144":
+        bench_kvfile(args)
         return
 
     from fp8_mla_latent_amd import mla8 as m
