@@ -56,6 +56,13 @@ def lib() -> ctypes.CDLL:
         L.mla8o_batch.argtypes = [P, P, i64, i32, i32, P, P, i32, i64, i32, f32, P, P]
         L.mla8o_decode_chunked.argtypes = [P, P, i64, i32, i32, P, P, i32, f32, i64, P, P]
         L.mla8o_index_scores.argtypes = [P, P, i64, i32, P, P, i32, P]
+        L.mla8o_bf16.restype = ctypes.c_uint16
+        L.mla8o_bf16.argtypes = [f32]
+        L.mla8o_bf16_array.argtypes = [P, i64, P]
+        L.mla8o_bf16_value.restype = ctypes.c_double
+        L.mla8o_bf16_value.argtypes = [ctypes.c_uint16]
+        L.mla8o_quantize_rows_mx.argtypes = [P, i64, i32, i32, P, P]
+        L.mla8o_decode_mx.argtypes = [P, P, i64, i32, i32, P, P, i32, f32, P, P]
         L.mla8o_threads.restype = ctypes.c_int
         _lib = L
     return _lib
@@ -185,6 +192,46 @@ def index_topk(scores, top_k):
     # sort keys, last is primary: NaN class, then score descending, then row
     order = np.lexsort((t, neg, nan.astype(np.int8)))
     return np.sort(order[:min(int(top_k), s.size)]).astype(np.int32)
+
+
+def bf16(x) -> np.ndarray:
+    """float32 values -> bf16 bit patterns (uint16), round to nearest even."""
+    v = _c(np.asarray(x, np.float32).ravel(), np.float32)
+    out = np.empty(v.shape, np.uint16)
+    lib().mla8o_bf16_array(_ptr(v), v.size, _ptr(out))
+    return out.reshape(np.shape(x))
+
+
+def bf16_value(b) -> np.ndarray:
+    """bf16 bit patterns -> float64 values."""
+    v = np.asarray(b, np.uint16).ravel()
+    f = lib().mla8o_bf16_value
+    return np.array([f(int(t)) for t in v], np.float64).reshape(np.shape(b))
+
+
+def quantize_rows_mx(x, lc, rc) -> tuple[np.ndarray, np.ndarray]:
+    """Mixed rows: f32 [n, lc + rc] -> (rows uint8 [n, lc + 2 rc], scales f32 [n])."""
+    v = _c(x, np.float32)
+    n = v.shape[0]
+    assert v.shape[1] == lc + rc
+    rows = np.empty((n, lc + 2 * rc), np.uint8)
+    scales = np.empty((n,), np.float32)
+    lib().mla8o_quantize_rows_mx(_ptr(v), n, lc, rc, _ptr(rows), _ptr(scales))
+    return rows, scales
+
+
+def decode_mx(rows, scales, t_rows, lc, rc, q_lat, q_rope, sm_scale):
+    """Dense decode of H heads over mixed rows [0, t_rows)."""
+    r = _c(rows, np.uint8)
+    sc = _c(scales, np.float32)
+    ql = _c(q_lat, np.float32)
+    qr = _c(q_rope, np.float32)
+    h = ql.shape[0]
+    out = np.empty((h, lc), np.float64)
+    lse = np.empty((h,), np.float64)
+    lib().mla8o_decode_mx(_ptr(r), _ptr(sc), t_rows, lc, rc, _ptr(ql), _ptr(qr), h,
+                          float(np.float32(sm_scale)), _ptr(out), _ptr(lse))
+    return out, lse
 
 
 def threads() -> int:

@@ -15,6 +15,9 @@
  *   [KV8-long]  same page, second commit message ("KV8 long-context CUDA"),
  *               the kv_dev_sync8 / split-T / DSA-gather bullets, and the PR
  *               description that restates them.
+ *   [B1-FMHA]   "B1 Mixed FP8/BF16 FMHA first pass": the mixed cache format,
+ *               noPE part as e4m3 bytes with a per-row f32 scale and the RoPE
+ *               part kept in bf16 (the 512 / 448 / 64 shape).
  *   [B2-indexer] "B1 Mixed FP8/BF16 FMHA first pass" site, commit message of
  *               the B2 fp8 indexer score + top-k kernel: the query (64 indexer
  *               heads x 128) quantized to fp8, the keys read as e4m3, then
@@ -388,4 +391,128 @@ EXPORT void mla8o_index_scores(const uint8_t* k_codes, const float* k_scales, in
     }
     free(qc);
     free(qs);
+}
+
+/* ------------------------------------------------------------------------- */
+/* bf16.  [B1-FMHA]: the RoPE part of a mixed row stays in bf16.  Readings: one
+ * round-to-nearest-even rounding of the f32 value onto bfloat16 (8 significant
+ * bits, the f32 exponent range, subnormals included); a value that rounds to
+ * 2^128 or beyond becomes +/-inf; +/-inf stay; NaN becomes the quiet NaN 0x7FC0
+ * with its sign.  Written from the definition: scale |x| so that the kept bits
+ * are the integer part, round with rint, and take the bf16 bit pattern of the
+ * (exactly representable) result, which is the top half of its f32 pattern. */
+EXPORT uint16_t mla8o_bf16(float x)
+{
+    uint16_t sign = signbit(x) ? 0x8000 : 0x0000;
+    if (isnan(x))
+        return sign | 0x7FC0;
+    if (isinf(x))
+        return sign | 0x7F80;
+    double a = fabs((double)x);
+    if (a == 0.0)
+        return sign;
+    int ex;
+    (void)frexp(a, &ex);
+    int e = ex - 1;        /* a in [2^e, 2^(e+1)) */
+    if (e < -126)
+        e = -126;          /* subnormal range: quantum 2^-133 */
+    double v = ldexp(rint(ldexp(a, 7 - e)), e - 7);
+    if (v >= ldexp(1.0, 128))
+        return sign | 0x7F80;
+    float fv = (float)v;   /* exact */
+    uint32_t b;
+    memcpy(&b, &fv, 4);
+    return sign | (uint16_t)(b >> 16);
+}
+
+EXPORT void mla8o_bf16_array(const float* x, int64_t n, uint16_t* out)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < n; ++i)
+        out[i] = mla8o_bf16(x[i]);
+}
+
+/* Value of a bf16 bit pattern, from the format's definition: 1 sign bit, 8
+ * exponent bits with bias 127, 7 mantissa bits. */
+EXPORT double mla8o_bf16_value(uint16_t b)
+{
+    int s = b >> 15, e = (b >> 7) & 0xFF, m = b & 0x7F;
+    double v;
+    if (e == 0xFF)
+        v = m ? NAN : INFINITY;
+    else if (e == 0)
+        v = ldexp((double)m, -133);
+    else
+        v = ldexp(1.0 + m / 128.0, e - 127);
+    return s ? -v : v;
+}
+
+/* Mixed rows.  [B1-FMHA] storage format.  Readings: a row is lc noPE values
+ * then rc RoPE values (the page's 448 + 64); the noPE part goes through the
+ * per-row quantizer above (its scale is the noPE part's amax/448); the RoPE part
+ * is stored as bf16; a stored row is lc code bytes then rc little-endian bf16
+ * values, lc + 2 rc bytes. */
+EXPORT void mla8o_quantize_rows_mx(const float* x, int64_t n, int32_t lc, int32_t rc,
+                                   uint8_t* rows, float* scales)
+{
+    int64_t d = lc + rc, rb = lc + 2 * (int64_t)rc;
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < n; ++r) {
+        mla8o_quantize_row(x + r * d, lc, rows + r * rb, scales + r);
+        for (int32_t i = 0; i < rc; ++i) {
+            uint16_t b = mla8o_bf16(x[r * d + lc + i]);
+            rows[r * rb + lc + 2 * i] = (uint8_t)(b & 0xFF);
+            rows[r * rb + lc + 2 * i + 1] = (uint8_t)(b >> 8);
+        }
+    }
+}
+
+/* Dense decode over mixed rows.  Readings: the key of row t is the noPE part
+ * dequantized (dec(code) * scale_t) followed by the RoPE part's bf16 values,
+ * unscaled; the value is the dequantized noPE part (output width lc); the rest
+ * is the attention of attend_rows above. */
+EXPORT void mla8o_decode_mx(const uint8_t* rows, const float* scales, int64_t t_rows, int32_t lc,
+                            int32_t rc, const float* q_lat, const float* q_rope, int32_t n_heads,
+                            float sm_scale, double* out, double* lse)
+{
+    int64_t rb = lc + 2 * (int64_t)rc;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int32_t h = 0; h < n_heads; ++h) {
+        double q[4096];
+        make_query(q_lat + (int64_t)h * lc, q_rope + (int64_t)h * rc, lc, rc, q);
+        double* o = out + (int64_t)h * lc;
+        double* s = (double*)malloc(sizeof(double) * (t_rows > 0 ? t_rows : 1));
+        double smax = -INFINITY;
+        for (int64_t t = 0; t < t_rows; ++t) {
+            const uint8_t* row = rows + t * rb;
+            double acc = 0.0;
+            for (int32_t i = 0; i < lc; ++i)
+                acc += q[i] * (mla8o_dec(row[i]) * (double)scales[t]);
+            for (int32_t i = 0; i < rc; ++i) {
+                uint16_t b = (uint16_t)(row[lc + 2 * i] | (row[lc + 2 * i + 1] << 8));
+                acc += q[lc + i] * mla8o_bf16_value(b);
+            }
+            s[t] = (double)sm_scale * acc;
+            if (s[t] > smax)
+                smax = s[t];
+        }
+        for (int32_t i = 0; i < lc; ++i)
+            o[i] = 0.0;
+        if (smax == -INFINITY) {
+            lse[h] = -INFINITY;
+            free(s);
+            continue;
+        }
+        double z = 0.0;
+        for (int64_t t = 0; t < t_rows; ++t) {
+            double p = exp(s[t] - smax);
+            z += p;
+            for (int32_t i = 0; i < lc; ++i)
+                o[i] += p * (mla8o_dec(rows[t * rb + i]) * (double)scales[t]);
+        }
+        for (int32_t i = 0; i < lc; ++i)
+            o[i] /= z;
+        lse[h] = smax + log(z);
+        free(s);
+    }
 }
