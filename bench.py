@@ -59,10 +59,13 @@ def parse():
                     help="calibrated rocprofv3 FETCH_SIZE + WRITE_SIZE bytes per partial launch "
                          "(JSON); used only while the kernel source still matches its hash")
     ap.add_argument("--workload", default="long_t262144",
-                    choices=["long_t262144", "dsa_index_t131072_k2048", "kvfile_t262144"],
+                    choices=["long_t262144", "dsa_index_t131072_k2048", "kvfile_t262144",
+                             "mixed_t262144"],
                     help="long_t262144: the fused append + split-T decode step (default); "
                          "dsa_index_t131072_k2048: the fp8 indexer score + top-k; "
-                         "kvfile_t262144: resume a persisted shadow file into device shadows")
+                         "kvfile_t262144: resume a persisted shadow file into device shadows; "
+                         "mixed_t262144: the decode step over mixed rows (noPE e4m3 448 + RoPE "
+                         "bf16 64)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device copy (counter calibration) and exit")
     return ap.parse_args()
@@ -256,6 +259,162 @@ def bench_index(args):
     print(json.dumps(rec), flush=True)
 
 
+def cpu_baseline_mixed(w, lc, rc, heads):
+    """The oracle on mixed rows: quantize one fresh row, then fp64 attention of
+    `heads` heads over all T rows, scaled to every head."""
+    import numpy as np
+
+    import oracle
+    from fp8_mla_latent_amd import workloads as W
+
+    x = np.ascontiguousarray(W.rows(w, w.t_rows, seed_offset=0)[:, :lc + rc])
+    rows, scales = oracle.quantize_rows_mx(x, lc, rc)
+    ql, qr = W.queries(w, seed_offset=0)
+    ql = np.ascontiguousarray(ql[:heads, :lc])
+    t0 = time.perf_counter()
+    r1, s1 = oracle.quantize_rows_mx(x[-1:], lc, rc)
+    rows[-1], scales[-1] = r1[0], s1[0]
+    oracle.decode_mx(rows, scales, w.t_rows, lc, rc, ql, qr[:heads], w.sm_scale)
+    dt = time.perf_counter() - t0
+    ms = dt * 1e3 * (w.n_heads / heads)
+    return {"value": round(ms, 3), "unit": "ms/layer-token", "cores": oracle.threads(),
+            "kind": "oracle",
+            "sample": f"append 1 mixed row + fp64 attention of {heads} of {w.n_heads} heads over "
+                      f"T={w.t_rows} rows ({dt:.2f} s), scaled x{w.n_heads / heads:g} to all heads"}
+
+
+def bench_mixed(args):
+    """Decode step over mixed rows (448 noPE values e4m3 + 64 RoPE values bf16,
+    576 bytes + scale per row), H=64, T=262144: append one row, attend all."""
+    import numpy as np
+    import torch
+
+    from fp8_mla_latent_amd import mla8 as m
+    from fp8_mla_latent_amd import workloads as W
+
+    w = W.LONG
+    LC, RC = 448, 64
+    L, K, WU = args.layers or 8, args.steps, args.warmup
+    T = w.t_rows
+    RB = LC + 2 * RC
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    layers = []
+    for l in range(L):
+        x = torch.from_numpy(np.ascontiguousarray(W.rows(w, T, seed_offset=l)[:, :LC + RC])).to(dev)
+        rows = torch.empty((T, RB), dtype=torch.uint8, device=dev)
+        scales = torch.empty((T,), dtype=torch.float32, device=dev)
+        assert m.mla8_append_mx(rows, scales, 0, x[:T - 1], LC, RC) == T - 1
+        fresh = x[T - 1:].clone()
+        del x
+        ql, qr = W.queries(w, seed_offset=l)
+        layers.append(dict(rows=rows, scales=scales, fresh=fresh,
+                           ql=torch.from_numpy(np.ascontiguousarray(ql[:, :LC])).to(dev),
+                           qr=torch.from_numpy(qr).to(dev),
+                           out=torch.empty((w.n_heads, LC), dtype=torch.float32, device=dev),
+                           lse=torch.empty((w.n_heads,), dtype=torch.float32, device=dev)))
+    ws = torch.empty(m.mla8_workspace_bytes(m.MLA8_OP_DECODE, T, w.n_heads, 1, LC),
+                     dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+    log(f"{L} layers of {T - 1} mixed rows quantized")
+
+    def one(ly):
+        m.mla8_append_mx(ly["rows"], ly["scales"], T - 1, ly["fresh"], LC, RC)
+        m.mla8_decode_mx(ly["rows"], ly["scales"], T, LC, RC, ly["ql"], ly["qr"], w.sm_scale,
+                         out=ly["out"], lse=ly["lse"], workspace=ws)
+
+    def step():
+        for ly in layers:
+            one(ly)
+
+    for _ in range(max(WU, 1)):
+        step()
+    torch.cuda.synchronize()
+    graph = None
+    if not args.no_graph:
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step()
+        torch.cuda.synchronize()
+        run = graph.replay
+    else:
+        run = step
+    n_settle = settle(run, "steps")
+    for _ in range(WU):
+        run()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(K):
+        run()
+    e1.record()
+    torch.cuda.synchronize()
+    ms_step = e0.elapsed_time(e1) / K
+    ms_lt = ms_step / L
+    log(f"step {ms_step:.4f} ms ({L} layers), {ms_lt * 1e3:.2f} us/layer-token")
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(K * L)]
+    for a_, b_ in evs:
+        a_.record()
+        b_.record()
+    torch.cuda.synchronize()
+    for _ in range(30):
+        run()
+    i = 0
+    try:
+        for _ in range(K):
+            for ly in layers:
+                m.mla8_append_mx(ly["rows"], ly["scales"], T - 1, ly["fresh"], LC, RC)
+                m.mla8_profile_events(*evs[i])
+                m.mla8_decode_mx(ly["rows"], ly["scales"], T, LC, RC, ly["ql"], ly["qr"],
+                                 w.sm_scale, out=ly["out"], lse=ly["lse"], workspace=ws)
+                i += 1
+    finally:
+        m.mla8_profile_events(None, None)
+    torch.cuda.synchronize()
+    durs = np.array([a.elapsed_time(b) for a, b in evs]) * 1e3
+    part_us = float(np.mean(durs))
+    row_bytes = T * (RB + 4)
+    alg_bytes = row_bytes + w.n_heads * (LC + RC) * 4
+    achieved = alg_bytes / (part_us * 1e-6) / 1e9
+    for ly in layers:
+        assert torch.isfinite(ly["out"]).all() and torch.isfinite(ly["lse"]).all()
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline_mixed(w, LC, RC, args.cpu_heads)
+        log(f"cpu oracle: {cpu}")
+    rec = {
+        "metric": "ms/layer-token + achieved HBM GB/s (mixed fp8/bf16 rows), MLA decode at "
+                  "T=262144",
+        "value": round(ms_lt, 6),
+        "unit": "ms/layer-token",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": WU,
+        "ms_per_step": round(ms_step, 6),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "e4m3 noPE + bf16 RoPE rows; scores e4m3 x 4-term e4m3 q (fp8 mfma) + bf16 x "
+                 "2-term bf16 q (bf16 mfma), context f16 weights x e4m3->f16 (f16 mfma); "
+                 "f32 accumulate",
+        "data": "synthetic: seeded N(0,1) rows and queries",
+        "config": {"workload": "mixed_t262144", "heads": w.n_heads, "nope": LC, "rope": RC,
+                   "t_rows": T, "batch": 1, "layers_per_step": L,
+                   "launch": "hip graph" if graph is not None else "eager"},
+        "kv_stream_gb_per_s": round(row_bytes / (ms_lt * 1e-3) / 1e9, 1),
+        "clock_settle": {"seconds": SETTLE_S, "untimed_steps": n_settle},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "k_split_partial<9,false,true>", "kernel_us": round(part_us, 3),
+                     "algorithmic_bytes": alg_bytes},
+        "cpu_baseline": cpu,
+    }
+    log(f"partial kernel {part_us:.2f} us mean -> {achieved:.0f} GB/s")
+    print(json.dumps(rec), flush=True)
+
+
 def bench_kvfile(args):
     """Persistent shadow file: append one token per layer (latency) and resume
     a T=262144 file into device shadows (throughput).  Host file I/O through
@@ -366,6 +525,9 @@ def main():
         return
     if args.workload == "kvfile_t262144":
         bench_kvfile(args)
+        return
+    if args.workload == "mixed_t262144":
+        bench_mixed(args)
         return
 
     from fp8_mla_latent_amd import mla8 as m

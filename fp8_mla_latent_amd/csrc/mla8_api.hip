@@ -83,7 +83,8 @@ int run_attention(int32_t op, const uint8_t* codes, const float* scales, int64_t
                   const float* q_rope, int32_t n_qh, int32_t n_heads, int64_t pos0,
                   float sm_scale, float* out, float* lse, void* workspace, size_t ws_bytes,
                   void* stream, const float* x_new = nullptr, uint8_t* new_codes = nullptr,
-                  float* new_scales = nullptr, int64_t new0 = 0, int64_t n_new = 0)
+                  float* new_scales = nullptr, int64_t new0 = 0, int64_t n_new = 0,
+                  int32_t layout = kE4m3)
 {
     const Plan p = make_plan(op, n_list, n_qh);
     const size_t need = ws_bytes_for(p, n_qh, lc);
@@ -105,7 +106,8 @@ int run_attention(int32_t op, const uint8_t* codes, const float* scales, int64_t
     a.q_rope = q_rope;
     a.lc = lc;
     a.rc = rc;
-    a.d = lc + rc;
+    a.d = (layout == kMixed) ? lc + 2 * rc : lc + rc;
+    a.layout = layout;
     a.n_qh = n_qh;
     a.n_heads = n_heads;
     a.pos0 = (int32_t)pos0;
@@ -219,6 +221,73 @@ int mla8_decode(const uint8_t* kv_codes, const float* kv_scales, int64_t t_rows,
     return run_attention(MLA8_OP_DECODE, kv_codes, kv_scales, t_rows, lc, rc, nullptr, t_rows,
                          q_lat, q_rope, n_heads, n_heads, 0, sm_scale, out, lse, workspace,
                          ws_bytes, stream);
+}
+
+// Mixed rows: the 448 / 64 shape only.
+int check_shape_mx(int32_t lc, int32_t rc)
+{
+    return (lc == 448 && rc == 64) ? MLA8_OK : MLA8_E_UNSUPPORTED;
+}
+
+int mla8_quantize_rows_mx(const float* x, int64_t n_rows, int32_t lc, int32_t rc, uint8_t* rows,
+                          float* scales, void* stream)
+{
+    int st = check_shape_mx(lc, rc);
+    if (st != MLA8_OK)
+        return st;
+    if (n_rows < 0 || n_rows > kMaxRows)
+        return MLA8_E_INVAL;
+    if (n_rows == 0)
+        return MLA8_OK;
+    if (!x || !rows || !scales || !aligned16(x) || !aligned16(rows) ||
+        (reinterpret_cast<uintptr_t>(scales) & 3u))
+        return MLA8_E_INVAL;
+    return launch_quantize_mx(x, n_rows, lc, rc, rows, scales, static_cast<hipStream_t>(stream)) ==
+                   hipSuccess
+               ? MLA8_OK
+               : MLA8_E_HIP;
+}
+
+int mla8_append_mx(uint8_t* kv_rows, float* kv_scales, int64_t cap_rows, int64_t* t_rows,
+                   const float* x, int64_t n_rows, int32_t lc, int32_t rc, void* stream)
+{
+    int st = check_shape_mx(lc, rc);
+    if (st != MLA8_OK)
+        return st;
+    if (!kv_rows || !kv_scales || !t_rows || !x)
+        return MLA8_E_INVAL;
+    if (cap_rows <= 0 || cap_rows > kMaxRows || n_rows < 0 || *t_rows < 0 || *t_rows > cap_rows)
+        return MLA8_E_INVAL;
+    if (!aligned16(kv_rows) || !aligned16(x) || (reinterpret_cast<uintptr_t>(kv_scales) & 3u))
+        return MLA8_E_INVAL;
+    if (n_rows > cap_rows - *t_rows)
+        return MLA8_E_CAPACITY;
+    if (n_rows == 0)
+        return MLA8_OK;
+    const int64_t rb = lc + 2 * (int64_t)rc;
+    const hipError_t e = launch_quantize_mx(x, n_rows, lc, rc, kv_rows + *t_rows * rb,
+                                            kv_scales + *t_rows, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess)
+        return MLA8_E_HIP;
+    *t_rows += n_rows;
+    return MLA8_OK;
+}
+
+int mla8_decode_mx(const uint8_t* kv_rows, const float* kv_scales, int64_t t_rows, int32_t lc,
+                   int32_t rc, const float* q_lat, const float* q_rope, int32_t n_heads,
+                   float sm_scale, float* out, float* lse, void* workspace, size_t ws_bytes,
+                   void* stream)
+{
+    int st = check_shape_mx(lc, rc);
+    if (st != MLA8_OK)
+        return st;
+    st = check_decode_common(kv_rows, kv_scales, t_rows, lc, rc, q_lat, q_rope, n_heads, sm_scale,
+                             out);
+    if (st != MLA8_OK)
+        return st;
+    return run_attention(MLA8_OP_DECODE, kv_rows, kv_scales, t_rows, lc, rc, nullptr, t_rows,
+                         q_lat, q_rope, n_heads, n_heads, 0, sm_scale, out, lse, workspace,
+                         ws_bytes, stream, nullptr, nullptr, nullptr, 0, 0, kMixed);
 }
 
 int mla8_append_decode(uint8_t* kv_codes, float* kv_scales, int64_t cap_rows, int64_t* t_rows,

@@ -80,6 +80,17 @@ __device__ __forceinline__ float max_xor32(float x)
     return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
+// bf16 bits of an f32 value: round to nearest even (a finite value that rounds
+// past the largest bf16 becomes infinity, infinities stay), NaN -> the quiet
+// NaN 0x7FC0 with its sign.
+__device__ __forceinline__ uint32_t bf16_rne_bits(float x)
+{
+    const uint32_t b = __float_as_uint(x);
+    if ((b & 0x7FFFFFFFu) > 0x7F800000u)
+        return ((b >> 16) & 0x8000u) | 0x7FC0u;
+    return (b + 0x7FFFu + ((b >> 16) & 1u)) >> 16;
+}
+
 // One row by one wave: the row (d <= kMaxRowWidth floats, at most three
 // float4 per lane) stays in registers between the amax pass and the encode
 // pass.

@@ -17,6 +17,9 @@ constexpr int kThreads = 512;
 constexpr int kTargetGroups = 256;
 
 enum RowMode : int32_t { kDense = 0, kSelect = 1, kCausal = 2 };
+// Stored row layouts: all e4m3 (codes of Lc + Rc values), or mixed (Lc = 448
+// noPE values as e4m3, then Rc = 64 RoPE values as bf16).
+enum RowLayout : int32_t { kE4m3 = 0, kMixed = 1 };
 
 // One launch of the split-T attention (partial kernel + merge kernel).
 struct AttnArgs {
@@ -27,7 +30,8 @@ struct AttnArgs {
     int32_t n_list;         // length of the attended row list
     const float* q_lat;     // [n_qh][lc]
     const float* q_rope;    // [n_qh][rc]
-    int32_t lc, rc, d;
+    int32_t lc, rc, d;      // d: bytes of a stored row (lc + rc, or lc + 2 rc mixed)
+    int32_t layout;         // RowLayout
     int32_t n_qh;           // query-heads: n_heads, or n_q * n_heads for kCausal
     int32_t n_heads;        // heads per query position (kCausal)
     int32_t pos0;           // kCausal: position of query 0
@@ -84,6 +88,10 @@ hipError_t launch_index_topk(const IndexArgs& a, hipStream_t stream, hipEvent_t 
 
 hipError_t launch_quantize(const float* x, int64_t n_rows, int32_t d, uint8_t* codes,
                            float* scales, hipStream_t stream);
+// Mixed rows: lc noPE values -> e4m3 codes + scale, rc RoPE values -> bf16;
+// rows[n][lc + 2 rc] bytes.
+hipError_t launch_quantize_mx(const float* x, int64_t n_rows, int32_t lc, int32_t rc,
+                              uint8_t* rows, float* scales, hipStream_t stream);
 hipError_t launch_test_encode(const float* x, int64_t n, uint8_t* codes, hipStream_t stream);
 // ev_before / ev_after (may be null) are recorded around the partial kernel.
 hipError_t launch_attention(const AttnArgs& a, hipStream_t stream, hipEvent_t ev_before,

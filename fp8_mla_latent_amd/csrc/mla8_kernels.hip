@@ -57,6 +57,28 @@ __global__ __launch_bounds__(256) void k_quantize_rows(const float* __restrict__
     quantize_row_wave(x + row * d, d, codes + row * d, scales + row, lane);
 }
 
+// Mixed rows, one wave per row: the noPE part through the row quantizer (its
+// own amax and scale), the RoPE part to bf16.
+__global__ __launch_bounds__(256) void k_quantize_rows_mx(const float* __restrict__ x,
+                                                          int64_t n_rows, int32_t lc, int32_t rc,
+                                                          uint8_t* __restrict__ rows,
+                                                          float* __restrict__ scales)
+{
+    const int lane = threadIdx.x & 63;
+    const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (row >= n_rows)
+        return;
+    const float* xr = x + row * (lc + rc);
+    uint8_t* rr = rows + row * (lc + 2 * rc);
+    quantize_row_wave(xr, lc, rr, scales + row, lane);
+    if (lane < rc / 4) {
+        const float4 v = reinterpret_cast<const float4*>(xr + lc)[lane];
+        const uint32_t b0 = bf16_rne_bits(v.x), b1 = bf16_rne_bits(v.y);
+        const uint32_t b2 = bf16_rne_bits(v.z), b3 = bf16_rne_bits(v.w);
+        reinterpret_cast<uint2*>(rr + lc)[lane] = make_uint2(b0 | (b1 << 16), b2 | (b3 << 16));
+    }
+}
+
 __global__ __launch_bounds__(256) void k_test_encode(const float* __restrict__ x, int64_t n,
                                                      uint8_t* __restrict__ out)
 {
@@ -91,6 +113,12 @@ __device__ __forceinline__ f32x4 mfma16(f16x8 a, f16x8 b, f32x4 c)
 __device__ __forceinline__ f32x4 mfma_fp8_scaled(v8i a, v8i b, f32x4 c, int32_t sb)
 {
     return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 127, 0, sb);
+}
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+__device__ __forceinline__ f32x4 mfma_bf16(bf16x8 a, bf16x8 b, f32x4 c)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
@@ -224,6 +252,130 @@ __device__ __forceinline__ void build_query_terms(const AttnArgs& a,
     }
 }
 
+// ---------------------------------------------------------------------------
+// Mixed rows ("B1 Mixed FP8/BF16 FMHA first pass" storage format, the 448 / 64
+// shape): a stored row is the 448 noPE values as e4m3 bytes (scale: the
+// noPE part's amax/448) followed by the 64 RoPE values as bf16, 576 bytes.
+// The noPE part takes FOUR e4m3 query terms (t4 = e4m3(16 (... - t3)), about
+// 16 significant bits: with three, ties between outlier rows put some heads at
+// the tolerance), its last 64 elements forming the packed half block of K
+// block 3 (a full 128-byte LDS block whose second half holds RoPE bytes):
+// t1 | t2 and t3 | t4, as many MFMAs as the all-e4m3 row's three terms.  The RoPE part is scored on the bf16 MFMA:
+// e_rope = q_rope * sm * log2(e) splits into two bf16 terms hi + lo (about 16
+// significant bits), unscaled by the row scale, in two K steps of 32.
+// Staging after both head halves' e4m3 slots: qr[hh][slot 2m + term][lane][16
+// bytes], lane n + 16 g holding head 16 hh + n, RoPE elements 32 m + 8 g ..
+// 32 m + 8 g + 7 (the row operand reads the same elements: 16-byte chunk
+// 28 + 4 m + g of the row).
+struct QueryTermsMx {
+    static constexpr int LC = 448, RC = 64;
+    static constexpr int NFULL = 3;                 // full 128-element noPE blocks
+    static constexpr int NT = 4;                    // e4m3 terms
+    static constexpr int NSLOT = NT * NFULL + 2;    // e4m3 operand slots
+    static constexpr int NRS = 2 * (RC / 32);       // bf16 operand slots
+    static constexpr int RBASE = 2 * NSLOT * 64 * 32;
+    static constexpr int BYTES = RBASE + 2 * NRS * 64 * 16;
+    static constexpr int NG = LC / 4 / 16;          // noPE float4 groups per thread
+};
+
+// Query loads for mixed rows: thread t takes head t / 16; noPE groups
+// gi = t % 16 + 16 s (s < NG) and RoPE group t % 16.
+__device__ __forceinline__ void load_query_mx(const AttnArgs& a, int qh0,
+                                              float4 (&v)[QueryTermsMx::NG + 1])
+{
+    using Q = QueryTermsMx;
+    const int h = threadIdx.x >> 4, i = threadIdx.x & 15;
+    const int qh = qh0 + h;
+    const bool hv = qh < a.n_qh;
+#pragma unroll
+    for (int s = 0; s < Q::NG; ++s) {
+        const float4 x = *reinterpret_cast<const float4*>(
+            a.q_lat + (size_t)(hv ? qh : 0) * Q::LC + 4 * (i + 16 * s));
+        v[s] = hv ? x : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    const float4 x = *reinterpret_cast<const float4*>(a.q_rope + (size_t)(hv ? qh : 0) * Q::RC +
+                                                      4 * i);
+    v[Q::NG] = hv ? x : make_float4(0.f, 0.f, 0.f, 0.f);
+}
+
+__device__ __forceinline__ void build_query_terms_mx(const AttnArgs& a,
+                                                     const float4 (&v)[QueryTermsMx::NG + 1],
+                                                     uint8_t* qt, int* s_k)
+{
+    using Q = QueryTermsMx;
+    const int h = threadIdx.x >> 4, i = threadIdx.x & 15;
+    float amax = 0.0f;
+#pragma unroll
+    for (int s = 0; s < Q::NG; ++s)
+        amax = fmaxf(amax, fmaxf(fmaxf(fabsf(v[s].x), fabsf(v[s].y)),
+                                 fmaxf(fabsf(v[s].z), fabsf(v[s].w))));
+    amax = row16_max(amax);
+    const float es = a.sm_log2;
+    int ex = 0;
+    const float emax = amax * es;
+    if (emax > 0.0f)
+        (void)frexpf(emax, &ex);
+    // k <= 115 keeps the fourth term's scale 2^(-k - 12) an E8M0 value
+    const int k = (emax > 0.0f) ? min(8 - ex, 115) : 0;
+    if (i == 0)
+        s_k[h] = k;
+    const float mult = ldexpf(es, k);
+    const int hh = h >> 4, n = h & 15;
+    uint8_t* base = qt + (size_t)hh * Q::NSLOT * 64 * 32;
+    auto put = [&](int slot, int gl, int b, int val) __attribute__((always_inline)) {
+        *reinterpret_cast<int*>(base + ((slot * 64 + n + 16 * gl) * 32 + b)) = val;
+    };
+#pragma unroll
+    for (int s = 0; s < Q::NG; ++s) {
+        const int gi = i + 16 * s;  // noPE elements 4 gi .. 4 gi + 3
+        const int j = gi >> 5, g = (gi >> 3) & 3, b = 4 * (gi & 7);
+        float r[4] = {v[s].x * mult, v[s].y * mult, v[s].z * mult, v[s].w * mult};
+        int wd[Q::NT];
+#pragma unroll
+        for (int t = 0; t < Q::NT; ++t) {
+            wd[t] = __builtin_amdgcn_cvt_pk_fp8_f32(r[0], r[1], 0, false);
+            wd[t] = __builtin_amdgcn_cvt_pk_fp8_f32(r[2], r[3], wd[t], true);
+            if (t < Q::NT - 1) {
+                const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8(wd[t], false);
+                const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8(wd[t], true);
+                r[0] = (r[0] - lo[0]) * 16.0f;
+                r[1] = (r[1] - lo[1]) * 16.0f;
+                r[2] = (r[2] - hi[0]) * 16.0f;
+                r[3] = (r[3] - hi[1]) * 16.0f;
+            }
+        }
+        if (j < Q::NFULL) {
+#pragma unroll
+            for (int t = 0; t < Q::NT; ++t)
+                put(Q::NT * j + t, g, b, wd[t]);
+        } else {  // the packed half block: g < 2 here
+            put(Q::NT * Q::NFULL, g, b, wd[0]);
+            put(Q::NT * Q::NFULL, g + 2, b, wd[1]);
+            put(Q::NT * Q::NFULL + 1, g, b, wd[2]);
+            put(Q::NT * Q::NFULL + 1, g + 2, b, wd[3]);
+        }
+    }
+    // RoPE elements 4 i .. 4 i + 3: K step m = i / 8, lane group (i / 2) % 4,
+    // bf16 positions 4 (i % 2) .. + 3
+    const float4 e4 = v[Q::NG];
+    const float e[4] = {e4.x * es, e4.y * es, e4.z * es, e4.w * es};
+    uint32_t hi[4], lo[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+        hi[c] = bf16_rne_bits(e[c]);
+        lo[c] = bf16_rne_bits(e[c] - __uint_as_float(hi[c] << 16));
+    }
+    const int m = i >> 3, gl = (i >> 1) & 3, pos = 4 * (i & 1);
+    uint8_t* rb = qt + Q::RBASE;
+    auto put2 = [&](int slot, const uint32_t (&w)[4]) __attribute__((always_inline)) {
+        *reinterpret_cast<uint2*>(rb + (((hh * Q::NRS + slot) * 64 + n + 16 * gl) * 16 +
+                                        2 * pos)) =
+            make_uint2(w[0] | (w[1] << 16), w[2] | (w[3] << 16));
+    };
+    put2(2 * m, hi);
+    put2(2 * m + 1, lo);
+}
+
 constexpr float kTau = 8.0f;  // lazy-max slack, log2 units: weights stay <= 2^8
 
 // ---------------------------------------------------------------------------
@@ -310,7 +462,7 @@ __device__ __forceinline__ void dma_b32_s(const void* base, uint32_t voff, uint3
 // a transposed context read (8 rows x 16 bytes per 16 lanes) one linear
 // 128-byte read: no LDS bank conflicts.  The direct loads choose, lane by
 // lane, which 16 bytes of HBM land in each slot.
-template <int NKB>
+template <int NKB, bool MXL = false>
 struct PartialLds {
     static constexpr int TR = kTileRows;
     static constexpr int NW = kThreads / 64;
@@ -336,7 +488,8 @@ struct PartialLds {
     static constexpr int Z = CR + HG * 4 * 8;              // f32 [4][HG]
     static constexpr int HK = Z + 4 * HG * 4;              // i32 [HG] query exponent k
     static constexpr int END = HK + HG * 4;
-    static constexpr int QT_BYTES = QueryTerms<NKB>::BYTES;  // query terms, both head halves
+    // query terms, both head halves
+    static constexpr int QT_BYTES = MXL ? QueryTermsMx::BYTES : QueryTerms<NKB>::BYTES;
     // The staging area reuses the stages that are not filled before the
     // terms are built (tiles 0 .. DIST-1 are already in flight then).
     static constexpr int QT = (DIST * STAGE + QT_BYTES <= SC) ? DIST * STAGE : END;
@@ -368,11 +521,14 @@ typedef int v2i __attribute__((ext_vector_type(2)));
 // One barrier per tile: phase p scores tile p and writes its weights with the
 // softmax state as it stands, checks tile p-1's maxima against that state and
 // accumulates tile p-1's context.
-template <int NKB, bool GATHER>
+template <int NKB, bool GATHER, bool MXL = false>
 __global__ __launch_bounds__(kThreads, 1) void k_split_partial(AttnArgs a)
 {
-    using L = PartialLds<NKB>;
+    using L = PartialLds<NKB, MXL>;
     using Q = QueryTerms<NKB>;
+    using QM = QueryTermsMx;
+    static_assert(!MXL || (NKB == 9 && !GATHER), "mixed rows: the 448 / 64 dense decode");
+    constexpr int NSL = MXL ? QM::NSLOT : Q::NSLOT;  // e4m3 query operand slots
     constexpr int TR = L::TR, NW = L::NW, HG = L::HG, NB = L::NB, NFULL = L::NFULL;
     constexpr int RQB = L::RQB, WSS = L::WSS, NST = L::NST, DIST = L::DIST;
     constexpr int NINS = L::STAGE / 1024;     // 1-KB DMA instructions per tile
@@ -564,19 +720,37 @@ __global__ __launch_bounds__(kThreads, 1) void k_split_partial(AttnArgs a)
     // half's in registers.  The query loads go out first, then the first
     // tiles' direct loads, so that waiting for the query does not wait for
     // the tiles.
-    float4 qin[2 * NB];
-    load_query<NKB>(a, qh0, qin);
-    if (ntiles > 0)
-        issue_all(0, 0);
-    if (DIST == 2 && ntiles > 1)
-        issue_all(1, 1);
-    build_query_terms<NKB>(a, qin, lds + L::QT, s_k);
+    if constexpr (MXL) {
+        float4 qin[QM::NG + 1];
+        load_query_mx(a, qh0, qin);
+        if (ntiles > 0)
+            issue_all(0, 0);
+        if (DIST == 2 && ntiles > 1)
+            issue_all(1, 1);
+        build_query_terms_mx(a, qin, lds + L::QT, s_k);
+    } else {
+        float4 qin[2 * NB];
+        load_query<NKB>(a, qh0, qin);
+        if (ntiles > 0)
+            issue_all(0, 0);
+        if (DIST == 2 && ntiles > 1)
+            issue_all(1, 1);
+        build_query_terms<NKB>(a, qin, lds + L::QT, s_k);
+    }
     lds_barrier();
-    v8i qv[Q::NSLOT];
+    v8i qv[NSL];
 #pragma unroll
-    for (int sl = 0; sl < Q::NSLOT; ++sl)
+    for (int sl = 0; sl < NSL; ++sl)
         qv[sl] = *reinterpret_cast<const v8i*>(
-            lds + L::QT + ((hh * Q::NSLOT + sl) * 64 + lane) * 32);
+            lds + L::QT + ((hh * NSL + sl) * 64 + lane) * 32);
+    // mixed rows: the RoPE query terms (bf16), two per K step
+    bf16x8 qr[MXL ? QM::NRS : 1];
+    if constexpr (MXL) {
+#pragma unroll
+        for (int sl = 0; sl < QM::NRS; ++sl)
+            qr[sl] = *reinterpret_cast<const bf16x8*>(
+                lds + L::QT + QM::RBASE + ((hh * QM::NRS + sl) * 64 + lane) * 16);
+    }
     // E8M0 operand scales 2^(-k - 4t) of this lane's head.  The instruction
     // takes the scale of 32-element K block kb from lane group kb, and lane
     // group g's bytes 0-15 / 16-31 fall in blocks g / 2 and 2 + g / 2.  The
@@ -586,6 +760,9 @@ __global__ __launch_bounds__(kThreads, 1) void k_split_partial(AttnArgs a)
     const int kq = s_k[16 * hh + n];
     const int sbt0 = 127 - kq, sbt1 = sbt0 - kTermShift, sbt2 = sbt0 - 2 * kTermShift;
     const int sb_pack = (g & 1) ? sbt1 : sbt0;
+    // mixed rows: the fourth term's scale, and the packed t3 | t4 slot's
+    const int sbt3 = sbt0 - 3 * kTermShift;
+    const int sb_pack2 = (g & 1) ? sbt3 : sbt2;
     const int qh_own = qh0 + 16 * hh + n;
     const int32_t tlim = (a.mode == kCausal)
                              ? a.pos0 + (qh_own < a.n_qh ? qh_own / a.n_heads : 0) + 1
@@ -706,11 +883,45 @@ __global__ __launch_bounds__(kThreads, 1) void k_split_partial(AttnArgs a)
 
     // Scores of tile p (stage st): S^T[16 rows][16 heads] in log2 units of the
     // codes, two accumulators so consecutive MFMAs do not wait on each other.
-    f32x4 acc0, acc1;
+    f32x4 acc0, acc1, accr;
+    // Mixed rows: the noPE half block is the first half of LDS block 3 (a full
+    // 1-KB group pair); RoPE K step m reads 16-byte chunk 28 + 4m + g of row
+    // 16 rq + n, in LDS block 3 (m = 0, lane groups 2-3) or in the trailing
+    // half block 4 (m = 1, lane groups 0-1).
+    const int qa_mxh = rq * RQB + 3 * 2048 + 16 * (lane & 31);
+    const int ro0 = rq * RQB + 3 * 2048 + (g & 1) * 1024 + 16 * (n + 16 * (2 + (g >> 1)));
+    const int ro1 = rq * RQB + 4 * 2048 + (g & 1) * 512 + 16 * (n + 16 * (g >> 1));
     auto scores = [&](int st) __attribute__((always_inline)) {
         const uint8_t* xst = lds + st * L::STAGE;
         acc0 = f32x4{0.f, 0.f, 0.f, 0.f};
         acc1 = acc0;
+        if constexpr (MXL) {
+            accr = acc0;
+#pragma unroll
+            for (int j = 0; j <= QM::NFULL; ++j) {
+                const uint8_t* xp = (j < QM::NFULL) ? xst + qa + 2048 * j : xst + qa_mxh;
+                const uint4 x0 = *reinterpret_cast<const uint4*>(xp);
+                const uint4 x1 = *reinterpret_cast<const uint4*>(xp + 1024);
+                const v8i xv = v8i{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w,
+                                   (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
+                if (j < QM::NFULL) {
+                    acc0 = mfma_fp8_scaled(xv, qv[4 * j], acc0, sbt0);
+                    acc1 = mfma_fp8_scaled(xv, qv[4 * j + 1], acc1, sbt1);
+                    acc0 = mfma_fp8_scaled(xv, qv[4 * j + 2], acc0, sbt2);
+                    acc1 = mfma_fp8_scaled(xv, qv[4 * j + 3], acc1, sbt3);
+                } else {
+                    acc1 = mfma_fp8_scaled(xv, qv[4 * j], acc1, sb_pack);
+                    acc0 = mfma_fp8_scaled(xv, qv[4 * j + 1], acc0, sb_pack2);
+                }
+            }
+#pragma unroll
+            for (int m = 0; m < QM::NRS / 2; ++m) {
+                const bf16x8 xr = *reinterpret_cast<const bf16x8*>(xst + (m ? ro1 : ro0));
+                accr = mfma_bf16(xr, qr[2 * m], accr);
+                accr = mfma_bf16(xr, qr[2 * m + 1], accr);
+            }
+            return;
+        }
 #pragma unroll
         for (int j = 0; j < NB; ++j) {
             const uint8_t* xp = (j < NFULL) ? xst + qa + 2048 * j : xst + qa_half;
@@ -851,7 +1062,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_split_partial(AttnArgs a)
             zsave = zacc;
 #pragma unroll
             for (int v = 0; v < 4; ++v)
-                u[v] = (acc0[v] + acc1[v]) * scv[v];
+                u[v] = MXL ? (acc0[v] + acc1[v]) * scv[v] + accr[v] : (acc0[v] + acc1[v]) * scv[v];
             if (mask) {
 #pragma unroll
                 for (int v = 0; v < 4; ++v) {
@@ -1035,6 +1246,15 @@ hipError_t launch_quantize(const float* x, int64_t n_rows, int32_t d, uint8_t* c
     return hipGetLastError();
 }
 
+hipError_t launch_quantize_mx(const float* x, int64_t n_rows, int32_t lc, int32_t rc,
+                              uint8_t* rows, float* scales, hipStream_t stream)
+{
+    const int64_t blocks = (n_rows + 3) / 4;
+    hipLaunchKernelGGL(k_quantize_rows_mx, dim3((unsigned)blocks), dim3(256), 0, stream, x,
+                       n_rows, lc, rc, rows, scales);
+    return hipGetLastError();
+}
+
 hipError_t launch_test_encode(const float* x, int64_t n, uint8_t* codes, hipStream_t stream)
 {
     int64_t blocks = (n + 255) / 256;
@@ -1047,6 +1267,14 @@ hipError_t launch_test_encode(const float* x, int64_t n, uint8_t* codes, hipStre
 template <int NKB>
 static void launch_partial(const AttnArgs& a, hipStream_t stream)
 {
+    if constexpr (NKB == 9) {
+        if (a.layout == kMixed) {
+            hipLaunchKernelGGL((k_split_partial<9, false, true>),
+                               dim3((unsigned)(a.n_chunks * a.n_groups)), dim3(kThreads), 0,
+                               stream, a);
+            return;
+        }
+    }
     if (a.mode == kSelect)
         hipLaunchKernelGGL((k_split_partial<NKB, true>), dim3((unsigned)(a.n_chunks * a.n_groups)),
                            dim3(kThreads), 0, stream, a);

@@ -28,7 +28,8 @@ MLA8_OP_BATCH = 2
 MLA8_OP_INDEX = 3
 
 EXPORTED = ("mla8_quantize_rows", "mla8_append", "mla8_decode", "mla8_append_decode",
-            "mla8_decode_sel", "mla8_batch", "mla8_index_topk", "mla8_kvfile_create",
+            "mla8_decode_sel", "mla8_batch", "mla8_quantize_rows_mx", "mla8_append_mx",
+            "mla8_decode_mx", "mla8_index_topk", "mla8_kvfile_create",
             "mla8_kvfile_info", "mla8_kvfile_append", "mla8_kvfile_load",
             "mla8_workspace_bytes", "mla8_force_splits", "mla8_plan_splits",
             "mla8_status_string", "mla8_version", "mla8_test_encode", "mla8_profile_events")
@@ -57,6 +58,9 @@ def _load() -> ctypes.CDLL:
                             [P, P, i64, i32, i32, P, i64, P, P, i32, f32, P, P, P, sz, P]),
         "mla8_batch": (ctypes.c_int,
                        [P, P, i64, i32, i32, P, P, i32, i64, i32, f32, P, P, P, sz, P]),
+        "mla8_quantize_rows_mx": (ctypes.c_int, [P, i64, i32, i32, P, P, P]),
+        "mla8_append_mx": (ctypes.c_int, [P, P, i64, ctypes.POINTER(i64), P, i64, i32, i32, P]),
+        "mla8_decode_mx": (ctypes.c_int, [P, P, i64, i32, i32, P, P, i32, f32, P, P, P, sz, P]),
         "mla8_index_topk": (ctypes.c_int,
                             [P, P, i64, i32, P, P, i32, i32, P, P, P, sz, P]),
         "mla8_kvfile_create": (ctypes.c_int, [ctypes.c_char_p, i32, i32, i32]),
@@ -221,6 +225,41 @@ def mla8_batch(kv_codes, kv_scales, t_rows: int, lc: int, rc: int, q_lat, q_rope
     _check(lib.mla8_batch(_ptr(kv_codes), _ptr(kv_scales), t_rows, lc, rc, _ptr(q_lat),
                           _ptr(q_rope), n_q, pos0, h, float(sm_scale), _ptr(out), _ptr(lse),
                           _ptr(ws), ws.numel(), _stream(q_lat)), "mla8_batch")
+    return out, lse
+
+
+def mla8_quantize_rows_mx(x: torch.Tensor, lc: int, rc: int, rows=None, scales=None):
+    """Mixed rows: f32 [n, lc + rc] -> (uint8 rows [n, lc + 2 rc], f32 scales [n])."""
+    n = x.shape[0]
+    if rows is None:
+        rows = torch.empty((n, lc + 2 * rc), dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty((n,), dtype=torch.float32, device=x.device)
+    _check(lib.mla8_quantize_rows_mx(_ptr(x), n, lc, rc, _ptr(rows), _ptr(scales), _stream(x)),
+           "mla8_quantize_rows_mx")
+    return rows, scales
+
+
+def mla8_append_mx(kv_rows, kv_scales, t_rows: int, x, lc: int, rc: int) -> int:
+    t = ctypes.c_int64(t_rows)
+    _check(lib.mla8_append_mx(_ptr(kv_rows), _ptr(kv_scales), kv_rows.shape[0], ctypes.byref(t),
+                              _ptr(x), x.shape[0], lc, rc, _stream(x)), "mla8_append_mx")
+    return int(t.value)
+
+
+def mla8_decode_mx(kv_rows, kv_scales, t_rows: int, lc: int, rc: int, q_lat, q_rope,
+                   sm_scale: float, out=None, lse=None, workspace=None, want_lse: bool = True):
+    """Dense decode over mixed rows [0, t_rows): (out [H, lc], lse [H] or None)."""
+    h = q_lat.shape[0]
+    dev = q_lat.device
+    if out is None:
+        out = torch.empty((h, lc), dtype=torch.float32, device=dev)
+    if lse is None and want_lse:
+        lse = torch.empty((h,), dtype=torch.float32, device=dev)
+    ws = _workspace(MLA8_OP_DECODE, t_rows, h, 1, lc, dev, workspace)
+    _check(lib.mla8_decode_mx(_ptr(kv_rows), _ptr(kv_scales), t_rows, lc, rc, _ptr(q_lat),
+                              _ptr(q_rope), h, float(sm_scale), _ptr(out), _ptr(lse), _ptr(ws),
+                              ws.numel(), _stream(q_lat)), "mla8_decode_mx")
     return out, lse
 
 

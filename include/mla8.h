@@ -167,6 +167,30 @@ MLA8_API int mla8_batch(const uint8_t* kv_codes, const float* kv_scales, int64_t
                size_t ws_bytes, void* stream);
 
 /*
+ * Mixed row layout  [B1-FMHA, the storage-format list: noPE KV as e4m3 bytes
+ * with a per-row f32 scale, RoPE KV kept in bf16; the decode kernel is for the
+ * 512 / 448 / 64 shape].  A stored row holds the lc = 448 noPE values as e4m3
+ * codes (quantized exactly as mla8_quantize_rows does, over the noPE part
+ * alone: scale = its amax/448) followed by the rc = 64 RoPE values as
+ * little-endian bf16 (round to nearest even; a NaN becomes 0x7FC0 with its
+ * sign): rows[row][lc + 2 rc] bytes, scales[row] f32.  In attention the key is
+ * the dequantized noPE part followed by the bf16 RoPE values (the row scale
+ * does not apply to them) and the value is the dequantized noPE part, so out is
+ * [H][lc].  Only lc = 448, rc = 64 is supported (E_UNSUPPORTED otherwise).
+ */
+MLA8_API int mla8_quantize_rows_mx(const float* x, int64_t n_rows, int32_t lc, int32_t rc,
+                                   uint8_t* rows, float* scales, void* stream);
+/* As mla8_append, for mixed rows (kv_rows [cap_rows][lc + 2 rc]). */
+MLA8_API int mla8_append_mx(uint8_t* kv_rows, float* kv_scales, int64_t cap_rows, int64_t* t_rows,
+                            const float* x, int64_t n_rows, int32_t lc, int32_t rc, void* stream);
+/* As mla8_decode, over mixed rows; workspace from
+ * mla8_workspace_bytes(MLA8_OP_DECODE, t_rows, n_heads, 1, lc). */
+MLA8_API int mla8_decode_mx(const uint8_t* kv_rows, const float* kv_scales, int64_t t_rows,
+                            int32_t lc, int32_t rc, const float* q_lat, const float* q_rope,
+                            int32_t n_heads, float sm_scale, float* out, float* lse,
+                            void* workspace, size_t ws_bytes, void* stream);
+
+/*
  * fp8 indexer score + top-k: the selection that mla8_decode_sel attends.
  * Source: "B1 Mixed FP8/BF16 FMHA first pass" site, commit message of the B2
  * fp8 indexer score + top-k kernel: the indexer query is quantized to fp8, the

@@ -27,7 +27,8 @@ def declared_symbols():
 def test_header_declares_the_product_calls():
     syms = declared_symbols()
     for name in ("mla8_quantize_rows", "mla8_append", "mla8_decode", "mla8_append_decode",
-                 "mla8_decode_sel", "mla8_batch", "mla8_index_topk", "mla8_workspace_bytes",
+                 "mla8_decode_sel", "mla8_batch", "mla8_index_topk", "mla8_quantize_rows_mx",
+                 "mla8_append_mx", "mla8_decode_mx", "mla8_workspace_bytes",
                  "mla8_status_string"):
         assert name in syms
 
@@ -189,3 +190,26 @@ def test_index_topk_refuses():
         args = list(base)
         args[idx] = val
         assert f(*args) == want, (idx, val)
+
+
+def test_mixed_refuses():
+    q = m.lib.mla8_quantize_rows_mx
+    assert q(FAKE, 4, 512, 64, FAKE, FAKE, None) == m.MLA8_E_UNSUPPORTED
+    assert q(FAKE, 4, 448, 32, FAKE, FAKE, None) == m.MLA8_E_UNSUPPORTED
+    assert q(None, 4, 448, 64, FAKE, FAKE, None) == m.MLA8_E_INVAL
+    assert q(FAKE, -1, 448, 64, FAKE, FAKE, None) == m.MLA8_E_INVAL
+    assert q(FAKE_MISALIGNED, 4, 448, 64, FAKE, FAKE, None) == m.MLA8_E_INVAL
+    t = ctypes.c_int64(3)
+    a = m.lib.mla8_append_mx
+    assert a(FAKE, FAKE, 4, ctypes.byref(t), FAKE, 2, 448, 64, None) == m.MLA8_E_CAPACITY
+    assert a(FAKE, FAKE, 4, ctypes.byref(t), FAKE, 1, 448, 48, None) == m.MLA8_E_UNSUPPORTED
+    assert t.value == 3
+    d = m.lib.mla8_decode_mx
+    ws = m.lib.mla8_workspace_bytes(m.MLA8_OP_DECODE, 100, 64, 1, 448)
+    base = [FAKE, FAKE, 100, 448, 64, FAKE, FAKE, 64, 0.1, FAKE, None, FAKE, ws, None]
+    for idx, val, want in [(3, 512, m.MLA8_E_UNSUPPORTED), (0, None, m.MLA8_E_INVAL),
+                           (2, 0, m.MLA8_E_INVAL), (12, ws - 1, m.MLA8_E_WORKSPACE),
+                           (6, None, m.MLA8_E_INVAL)]:
+        args = list(base)
+        args[idx] = val
+        assert d(*args) == want, (idx, val)

@@ -1,0 +1,140 @@
+"""GPU parity of the mixed row layout (noPE e4m3 + per-row scale, RoPE bf16;
+the 512 / 448 / 64 shape of "B1 Mixed FP8/BF16 FMHA first pass") against the
+fp64 CPU oracle, through the C ABI: stored bytes bit-exact, attention within
+the per-vector tolerance of tests/tolerance.py.
+"""
+from __future__ import annotations
+
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from fp8_mla_latent_amd import workloads as W
+from tests.tolerance import check_attention
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+LC, RC = 448, 64
+SM = 1.0 / math.sqrt(192.0)
+
+
+@pytest.fixture(scope="module")
+def m():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from fp8_mla_latent_amd import mla8
+    return mla8
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+
+
+def host(t):
+    torch.cuda.synchronize()
+    return t.cpu().numpy()
+
+
+def mixed_rows(t, seed, outliers=0.0):
+    g = np.random.Generator(np.random.PCG64(seed))
+    x = g.standard_normal((t, LC + RC)).astype(np.float32)
+    if outliers:
+        idx = g.choice(t, max(1, int(outliers * t)), replace=False)
+        x[idx, :LC] *= np.float32(50.0)
+    return x
+
+
+def queries(h, seed):
+    g = np.random.Generator(np.random.PCG64(seed + 500))
+    return (g.standard_normal((h, LC)).astype(np.float32),
+            g.standard_normal((h, RC)).astype(np.float32))
+
+
+def test_quantize_mx_bit_exact(m):
+    say("mixed quantize")
+    x = mixed_rows(300, 1)
+    x[3, 5] = np.nan
+    x[4, LC + 2] = np.nan
+    x[5, LC + 7] = -np.inf
+    x[6, LC + 1] = np.float32(3.4e38)   # rounds past the largest bf16
+    x[7, :LC] *= np.float32(1e-38)      # the guard on the noPE part
+    x[8] = 0.0
+    rows, sc = m.mla8_quantize_rows_mx(dev(x), LC, RC)
+    orows, osc = oracle.quantize_rows_mx(x, LC, RC)
+    np.testing.assert_array_equal(host(rows), orows)
+    np.testing.assert_array_equal(host(sc).view(np.uint32), osc.view(np.uint32))
+
+
+@pytest.mark.parametrize("t,h,outl,splits", [(1, 16, 0.0, 0), (300, 16, 0.0, 0),
+                                             (4096, 128, 0.01, 0), (3000, 64, 0.0, 7),
+                                             (777, 33, 0.02, 0)])
+def test_decode_mx_parity(m, t, h, outl, splits):
+    say(f"mixed decode t={t} h={h} outliers={outl} splits={splits}")
+    x = mixed_rows(t, 10 + t, outl)
+    rows = torch.zeros((t + 5, LC + 2 * RC), dtype=torch.uint8, device=DEV)
+    scales = torch.zeros((t + 5,), dtype=torch.float32, device=DEV)
+    assert m.mla8_append_mx(rows, scales, 0, dev(x), LC, RC) == t
+    ql, qr = queries(h, t)
+    prev = m.mla8_force_splits(splits)
+    try:
+        out, lse = m.mla8_decode_mx(rows, scales, t, LC, RC, dev(ql), dev(qr), SM)
+        torch.cuda.synchronize()
+    finally:
+        m.mla8_force_splits(prev)
+    orows, osc = oracle.quantize_rows_mx(x, LC, RC)
+    np.testing.assert_array_equal(host(rows)[:t], orows)
+    ro, rl = oracle.decode_mx(orows, osc, t, LC, RC, ql, qr, SM)
+    check_attention(host(out), ro, host(lse), rl, f"mixed t={t} h={h}")
+
+
+def test_decode_mx_rope_carries_the_scores(m):
+    # noPE queries zero: only the bf16 RoPE part (unscaled by the row scale)
+    # decides the weights
+    say("mixed decode, RoPE-only scores")
+    t, h = 2000, 32
+    x = mixed_rows(t, 77)
+    x[::7, :LC] *= np.float32(1000.0)  # row scales that must not touch RoPE
+    rows, sc = m.mla8_quantize_rows_mx(dev(x), LC, RC)
+    ql = np.zeros((h, LC), np.float32)
+    qr = queries(h, 5)[1] * np.float32(3.0)
+    out, lse = m.mla8_decode_mx(rows, sc, t, LC, RC, dev(ql), dev(qr), SM)
+    orows, osc = oracle.quantize_rows_mx(x, LC, RC)
+    ro, rl = oracle.decode_mx(orows, osc, t, LC, RC, ql, qr, SM)
+    check_attention(host(out), ro, host(lse), rl, "mixed RoPE-only")
+
+
+def test_decode_mx_long_sampled(m):
+    # the bench shape: T = 262144, H = 64; two heads checked against fp64
+    say("mixed decode T=262144 sampled")
+    t, h = 262144, 64
+    w = W.LONG
+    x = W.rows(w, t)[:, :LC + RC]
+    rows, sc = m.mla8_quantize_rows_mx(dev(x), LC, RC)
+    ql, qr = queries(h, 99)
+    out, lse = m.mla8_decode_mx(rows, sc, t, LC, RC, dev(ql), dev(qr), SM)
+    hr, hs = host(rows), host(sc)
+    for hh in (0, 41):
+        ro, rl = oracle.decode_mx(hr, hs, t, LC, RC, ql[hh:hh + 1], qr[hh:hh + 1], SM)
+        check_attention(host(out)[hh:hh + 1], ro, host(lse)[hh:hh + 1], rl, f"long head {hh}")
+
+
+def test_mixed_refusals(m):
+    x = dev(mixed_rows(4, 3))
+    for lc, rc in [(512, 64), (448, 32), (448, 0)]:
+        with pytest.raises(m.Mla8Error) as e:
+            m.mla8_quantize_rows_mx(torch.zeros((4, lc + rc), device=DEV), lc, rc)
+        assert e.value.status == m.MLA8_E_UNSUPPORTED
+    rows = torch.zeros((3, LC + 2 * RC), dtype=torch.uint8, device=DEV)
+    scales = torch.zeros((3,), dtype=torch.float32, device=DEV)
+    with pytest.raises(m.Mla8Error) as e:
+        m.mla8_append_mx(rows, scales, 0, x, LC, RC)
+    assert e.value.status == m.MLA8_E_CAPACITY
