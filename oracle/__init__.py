@@ -63,6 +63,7 @@ def lib() -> ctypes.CDLL:
         L.mla8o_bf16_value.argtypes = [ctypes.c_uint16]
         L.mla8o_quantize_rows_mx.argtypes = [P, i64, i32, i32, P, P]
         L.mla8o_decode_mx.argtypes = [P, P, i64, i32, i32, P, P, i32, f32, P, P]
+        L.mla8o_decode_sel_mx.argtypes = [P, P, i64, i32, i32, P, i64, P, P, i32, f32, P, P]
         L.mla8o_threads.restype = ctypes.c_int
         _lib = L
     return _lib
@@ -231,6 +232,21 @@ def decode_mx(rows, scales, t_rows, lc, rc, q_lat, q_rope, sm_scale):
     lse = np.empty((h,), np.float64)
     lib().mla8o_decode_mx(_ptr(r), _ptr(sc), t_rows, lc, rc, _ptr(ql), _ptr(qr), h,
                           float(np.float32(sm_scale)), _ptr(out), _ptr(lse))
+    return out, lse
+
+
+def decode_sel_mx(rows, scales, t_rows, lc, rc, sel, q_lat, q_rope, sm_scale):
+    """Selected-row decode over mixed rows (a multiset; out-of-range skipped)."""
+    r = _c(rows, np.uint8)
+    sc = _c(scales, np.float32)
+    s = _c(sel, np.int32)
+    ql = _c(q_lat, np.float32)
+    qr = _c(q_rope, np.float32)
+    h = ql.shape[0]
+    out = np.empty((h, lc), np.float64)
+    lse = np.empty((h,), np.float64)
+    lib().mla8o_decode_sel_mx(_ptr(r), _ptr(sc), t_rows, lc, rc, _ptr(s), s.size, _ptr(ql),
+                              _ptr(qr), h, float(np.float32(sm_scale)), _ptr(out), _ptr(lse))
     return out, lse
 
 

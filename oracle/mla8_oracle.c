@@ -467,10 +467,81 @@ EXPORT void mla8o_quantize_rows_mx(const float* x, int64_t n, int32_t lc, int32_
     }
 }
 
-/* Dense decode over mixed rows.  Readings: the key of row t is the noPE part
- * dequantized (dec(code) * scale_t) followed by the RoPE part's bf16 values,
- * unscaled; the value is the dequantized noPE part (output width lc); the rest
- * is the attention of attend_rows above. */
+/* Attention over mixed rows, for one head, over a list of row indices (a
+ * multiset; entries outside [0, t_rows) are skipped, as for attend_rows).
+ * Readings: the key of row t is the noPE part dequantized (dec(code) *
+ * scale_t) followed by the RoPE part's bf16 values, unscaled; the value is the
+ * dequantized noPE part (output width lc); the rest is the attention of
+ * attend_rows above. */
+static void attend_rows_mx(const uint8_t* rows, const float* scales, int64_t t_rows, int32_t lc,
+                           int32_t rc, const int64_t* list, int64_t nlist, const double* q,
+                           double sm, double* o, double* lse)
+{
+    int64_t rb = lc + 2 * (int64_t)rc;
+    double* s = (double*)malloc(sizeof(double) * (nlist > 0 ? nlist : 1));
+    double smax = -INFINITY;
+    for (int64_t j = 0; j < nlist; ++j) {
+        int64_t t = list[j];
+        if (t < 0 || t >= t_rows) {
+            s[j] = -INFINITY;
+            continue;
+        }
+        const uint8_t* row = rows + t * rb;
+        double acc = 0.0;
+        for (int32_t i = 0; i < lc; ++i)
+            acc += q[i] * (mla8o_dec(row[i]) * (double)scales[t]);
+        for (int32_t i = 0; i < rc; ++i) {
+            uint16_t b = (uint16_t)(row[lc + 2 * i] | (row[lc + 2 * i + 1] << 8));
+            acc += q[lc + i] * mla8o_bf16_value(b);
+        }
+        s[j] = sm * acc;
+        if (s[j] > smax)
+            smax = s[j];
+    }
+    for (int32_t i = 0; i < lc; ++i)
+        o[i] = 0.0;
+    if (smax == -INFINITY) {
+        *lse = -INFINITY;
+        free(s);
+        return;
+    }
+    double z = 0.0;
+    for (int64_t j = 0; j < nlist; ++j) {
+        if (s[j] == -INFINITY)
+            continue;
+        int64_t t = list[j];
+        double p = exp(s[j] - smax);
+        z += p;
+        for (int32_t i = 0; i < lc; ++i)
+            o[i] += p * (mla8o_dec(rows[t * rb + i]) * (double)scales[t]);
+    }
+    for (int32_t i = 0; i < lc; ++i)
+        o[i] /= z;
+    *lse = smax + log(z);
+    free(s);
+}
+
+/* Selected-row decode over mixed rows ([KV8-long] DSA bullet with the mixed
+ * row of [B1-FMHA]). */
+EXPORT void mla8o_decode_sel_mx(const uint8_t* rows, const float* scales, int64_t t_rows,
+                                int32_t lc, int32_t rc, const int32_t* sel, int64_t ns,
+                                const float* q_lat, const float* q_rope, int32_t n_heads,
+                                float sm_scale, double* out, double* lse)
+{
+    int64_t* list = (int64_t*)malloc(sizeof(int64_t) * (ns > 0 ? ns : 1));
+    for (int64_t j = 0; j < ns; ++j)
+        list[j] = sel[j];
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int32_t h = 0; h < n_heads; ++h) {
+        double q[4096];
+        make_query(q_lat + (int64_t)h * lc, q_rope + (int64_t)h * rc, lc, rc, q);
+        attend_rows_mx(rows, scales, t_rows, lc, rc, list, ns, q, (double)sm_scale,
+                       out + (int64_t)h * lc, lse + h);
+    }
+    free(list);
+}
+
+/* Dense decode over mixed rows. */
 EXPORT void mla8o_decode_mx(const uint8_t* rows, const float* scales, int64_t t_rows, int32_t lc,
                             int32_t rc, const float* q_lat, const float* q_rope, int32_t n_heads,
                             float sm_scale, double* out, double* lse)

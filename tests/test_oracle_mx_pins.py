@@ -106,3 +106,35 @@ def test_decode_mx_closed_form_with_noPE_only_scales(lc, rc):
         o, l = _attention(k, k[:, :lc], q, sm)
         np.testing.assert_allclose(out[i], o, rtol=1e-12, atol=1e-12)
         np.testing.assert_allclose(lse[i], l, rtol=1e-12)
+
+
+def test_decode_sel_mx_identities():
+    # the selection of every row is the dense decode; a repeated row counts as
+    # often as it appears (closed form: weight 2 for a doubled row);
+    # out-of-range entries are skipped
+    g = np.random.Generator(np.random.PCG64(44))
+    lc, rc, t, h = 448, 64, 50, 4
+    x = g.standard_normal((t, lc + rc)).astype(np.float32)
+    rows, sc = oracle.quantize_rows_mx(x, lc, rc)
+    ql = g.standard_normal((h, lc)).astype(np.float32)
+    qr = g.standard_normal((h, rc)).astype(np.float32)
+    sm = 0.07
+    d_out, d_lse = oracle.decode_mx(rows, sc, t, lc, rc, ql, qr, sm)
+    s_out, s_lse = oracle.decode_sel_mx(rows, sc, t, lc, rc, np.arange(t)[::-1], ql, qr, sm)
+    np.testing.assert_allclose(s_out, d_out, rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(s_lse, d_lse, rtol=1e-12)
+    o1, l1 = oracle.decode_sel_mx(rows, sc, t, lc, rc, np.array([7, -1, 9, 7, t + 3]), ql, qr, sm)
+    o2, l2 = oracle.decode_sel_mx(rows, sc, t, lc, rc, np.array([9, 7]), ql, qr, sm)
+    # doubled row 7: lse grows by ln(1 + p7) where p7 is row 7's share
+    k = oracle.bf16_value(rows[:, lc:].copy().view(np.uint16))
+    kn = oracle.dec(rows[:, :lc]) * sc[:, None].astype(np.float64)
+    for i in range(h):
+        q = np.concatenate([ql[i], qr[i]]).astype(np.float64)
+        s7 = np.float32(sm) * (np.concatenate([kn[7], k[7]]) @ q)
+        s9 = np.float32(sm) * (np.concatenate([kn[9], k[9]]) @ q)
+        mmax = max(s7, s9)
+        w7, w9 = 2 * np.exp(s7 - mmax), np.exp(s9 - mmax)
+        np.testing.assert_allclose(o1[i], (w7 * kn[7] + w9 * kn[9]) / (w7 + w9), rtol=1e-10,
+                                   atol=1e-12)
+        np.testing.assert_allclose(l1[i], mmax + np.log(w7 + w9), rtol=1e-12)
+    assert not np.allclose(o1, o2)
