@@ -290,6 +290,25 @@ int mla8_decode_mx(const uint8_t* kv_rows, const float* kv_scales, int64_t t_row
                          ws_bytes, stream, nullptr, nullptr, nullptr, 0, 0, kMixed);
 }
 
+int mla8_decode_sel_mx(const uint8_t* kv_rows, const float* kv_scales, int64_t t_rows,
+                       int32_t lc, int32_t rc, const int32_t* sel, int64_t ns,
+                       const float* q_lat, const float* q_rope, int32_t n_heads, float sm_scale,
+                       float* out, float* lse, void* workspace, size_t ws_bytes, void* stream)
+{
+    int st = check_shape_mx(lc, rc);
+    if (st != MLA8_OK)
+        return st;
+    st = check_decode_common(kv_rows, kv_scales, t_rows, lc, rc, q_lat, q_rope, n_heads, sm_scale,
+                             out);
+    if (st != MLA8_OK)
+        return st;
+    if (!sel || ns <= 0 || ns > kMaxRows || (reinterpret_cast<uintptr_t>(sel) & 3u))
+        return MLA8_E_INVAL;
+    return run_attention(MLA8_OP_DECODE_SEL, kv_rows, kv_scales, t_rows, lc, rc, sel, ns, q_lat,
+                         q_rope, n_heads, n_heads, 0, sm_scale, out, lse, workspace, ws_bytes,
+                         stream, nullptr, nullptr, nullptr, 0, 0, kMixed);
+}
+
 int mla8_append_decode(uint8_t* kv_codes, float* kv_scales, int64_t cap_rows, int64_t* t_rows,
                        const float* x_new, int64_t n_new, int32_t lc, int32_t rc,
                        const float* q_lat, const float* q_rope, int32_t n_heads, float sm_scale,

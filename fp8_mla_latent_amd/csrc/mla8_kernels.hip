@@ -527,7 +527,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_split_partial(AttnArgs a)
     using L = PartialLds<NKB, MXL>;
     using Q = QueryTerms<NKB>;
     using QM = QueryTermsMx;
-    static_assert(!MXL || (NKB == 9 && !GATHER), "mixed rows: the 448 / 64 dense decode");
+    static_assert(!MXL || NKB == 9, "mixed rows: the 448 / 64 shape");
     constexpr int NSL = MXL ? QM::NSLOT : Q::NSLOT;  // e4m3 query operand slots
     constexpr int TR = L::TR, NW = L::NW, HG = L::HG, NB = L::NB, NFULL = L::NFULL;
     constexpr int RQB = L::RQB, WSS = L::WSS, NST = L::NST, DIST = L::DIST;
@@ -1269,9 +1269,14 @@ static void launch_partial(const AttnArgs& a, hipStream_t stream)
 {
     if constexpr (NKB == 9) {
         if (a.layout == kMixed) {
-            hipLaunchKernelGGL((k_split_partial<9, false, true>),
-                               dim3((unsigned)(a.n_chunks * a.n_groups)), dim3(kThreads), 0,
-                               stream, a);
+            if (a.mode == kSelect)
+                hipLaunchKernelGGL((k_split_partial<9, true, true>),
+                                   dim3((unsigned)(a.n_chunks * a.n_groups)), dim3(kThreads), 0,
+                                   stream, a);
+            else
+                hipLaunchKernelGGL((k_split_partial<9, false, true>),
+                                   dim3((unsigned)(a.n_chunks * a.n_groups)), dim3(kThreads), 0,
+                                   stream, a);
             return;
         }
     }

@@ -29,7 +29,7 @@ MLA8_OP_INDEX = 3
 
 EXPORTED = ("mla8_quantize_rows", "mla8_append", "mla8_decode", "mla8_append_decode",
             "mla8_decode_sel", "mla8_batch", "mla8_quantize_rows_mx", "mla8_append_mx",
-            "mla8_decode_mx", "mla8_index_topk", "mla8_kvfile_create",
+            "mla8_decode_mx", "mla8_decode_sel_mx", "mla8_index_topk", "mla8_kvfile_create",
             "mla8_kvfile_info", "mla8_kvfile_append", "mla8_kvfile_load",
             "mla8_workspace_bytes", "mla8_force_splits", "mla8_plan_splits",
             "mla8_status_string", "mla8_version", "mla8_test_encode", "mla8_profile_events")
@@ -61,6 +61,8 @@ def _load() -> ctypes.CDLL:
         "mla8_quantize_rows_mx": (ctypes.c_int, [P, i64, i32, i32, P, P, P]),
         "mla8_append_mx": (ctypes.c_int, [P, P, i64, ctypes.POINTER(i64), P, i64, i32, i32, P]),
         "mla8_decode_mx": (ctypes.c_int, [P, P, i64, i32, i32, P, P, i32, f32, P, P, P, sz, P]),
+        "mla8_decode_sel_mx": (ctypes.c_int,
+                               [P, P, i64, i32, i32, P, i64, P, P, i32, f32, P, P, P, sz, P]),
         "mla8_index_topk": (ctypes.c_int,
                             [P, P, i64, i32, P, P, i32, i32, P, P, P, sz, P]),
         "mla8_kvfile_create": (ctypes.c_int, [ctypes.c_char_p, i32, i32, i32]),
@@ -260,6 +262,25 @@ def mla8_decode_mx(kv_rows, kv_scales, t_rows: int, lc: int, rc: int, q_lat, q_r
     _check(lib.mla8_decode_mx(_ptr(kv_rows), _ptr(kv_scales), t_rows, lc, rc, _ptr(q_lat),
                               _ptr(q_rope), h, float(sm_scale), _ptr(out), _ptr(lse), _ptr(ws),
                               ws.numel(), _stream(q_lat)), "mla8_decode_mx")
+    return out, lse
+
+
+def mla8_decode_sel_mx(kv_rows, kv_scales, t_rows: int, lc: int, rc: int, sel, q_lat, q_rope,
+                       sm_scale: float, out=None, lse=None, workspace=None,
+                       want_lse: bool = True):
+    """Decode over the selected mixed rows sel (int32 device tensor)."""
+    h = q_lat.shape[0]
+    dev = q_lat.device
+    ns = sel.shape[0]
+    if out is None:
+        out = torch.empty((h, lc), dtype=torch.float32, device=dev)
+    if lse is None and want_lse:
+        lse = torch.empty((h,), dtype=torch.float32, device=dev)
+    ws = _workspace(MLA8_OP_DECODE_SEL, ns, h, 1, lc, dev, workspace)
+    _check(lib.mla8_decode_sel_mx(_ptr(kv_rows), _ptr(kv_scales), t_rows, lc, rc, _ptr(sel), ns,
+                                  _ptr(q_lat), _ptr(q_rope), h, float(sm_scale), _ptr(out),
+                                  _ptr(lse), _ptr(ws), ws.numel(), _stream(q_lat)),
+           "mla8_decode_sel_mx")
     return out, lse
 
 

@@ -189,6 +189,14 @@ MLA8_API int mla8_decode_mx(const uint8_t* kv_rows, const float* kv_scales, int6
                             int32_t lc, int32_t rc, const float* q_lat, const float* q_rope,
                             int32_t n_heads, float sm_scale, float* out, float* lse,
                             void* workspace, size_t ws_bytes, void* stream);
+/* As mla8_decode_sel (absolute row indices, a multiset, entries outside
+ * [0, t_rows) skipped), over mixed rows; workspace from
+ * mla8_workspace_bytes(MLA8_OP_DECODE_SEL, ns, n_heads, 1, lc). */
+MLA8_API int mla8_decode_sel_mx(const uint8_t* kv_rows, const float* kv_scales, int64_t t_rows,
+                                int32_t lc, int32_t rc, const int32_t* sel, int64_t ns,
+                                const float* q_lat, const float* q_rope, int32_t n_heads,
+                                float sm_scale, float* out, float* lse, void* workspace,
+                                size_t ws_bytes, void* stream);
 
 /*
  * fp8 indexer score + top-k: the selection that mla8_decode_sel attends.

@@ -28,7 +28,7 @@ def test_header_declares_the_product_calls():
     syms = declared_symbols()
     for name in ("mla8_quantize_rows", "mla8_append", "mla8_decode", "mla8_append_decode",
                  "mla8_decode_sel", "mla8_batch", "mla8_index_topk", "mla8_quantize_rows_mx",
-                 "mla8_append_mx", "mla8_decode_mx", "mla8_workspace_bytes",
+                 "mla8_append_mx", "mla8_decode_mx", "mla8_decode_sel_mx", "mla8_workspace_bytes",
                  "mla8_status_string"):
         assert name in syms
 

@@ -138,3 +138,29 @@ def test_mixed_refusals(m):
     with pytest.raises(m.Mla8Error) as e:
         m.mla8_append_mx(rows, scales, 0, x, LC, RC)
     assert e.value.status == m.MLA8_E_CAPACITY
+
+
+@pytest.mark.parametrize("case", ["sorted", "dups_and_out_of_range", "indexer"])
+def test_decode_sel_mx_parity(m, case):
+    say(f"mixed gather decode: {case}")
+    t, h = 20000, 64
+    x = mixed_rows(t, 123, 0.01)
+    rows, sc = m.mla8_quantize_rows_mx(dev(x), LC, RC)
+    g = np.random.Generator(np.random.PCG64(7))
+    if case == "sorted":
+        sel = np.sort(g.choice(t, 2048, replace=False)).astype(np.int32)
+    elif case == "dups_and_out_of_range":
+        sel = g.integers(-50, t + 50, 777).astype(np.int32)
+    else:
+        # the fp8 indexer picks the rows (DeepSeek-V4 style sparse attention
+        # over the mixed cache)
+        keys = g.standard_normal((t, 128)).astype(np.float32)
+        kc, ks = m.mla8_quantize_rows(dev(keys), 128, 0)
+        qi = dev(g.standard_normal((64, 128)).astype(np.float32))
+        wi = dev((g.standard_normal(64) / 8).astype(np.float32))
+        sel_d, _ = m.mla8_index_topk(kc, ks, qi, wi, 2048)
+        sel = host(sel_d)
+    ql, qr = queries(h, 31)
+    out, lse = m.mla8_decode_sel_mx(rows, sc, t, LC, RC, dev(sel), dev(ql), dev(qr), SM)
+    ro, rl = oracle.decode_sel_mx(host(rows), host(sc), t, LC, RC, sel, ql, qr, SM)
+    check_attention(host(out), ro, host(lse), rl, f"mixed gather {case}")
