@@ -121,3 +121,47 @@ def test_append_decode_full_64_rows_to_capacity(m):
     with pytest.raises(m.Mla8Error) as e:
         m.mla8_append_decode(cb, sb, 256, dev(x1), w.lc, w.rc, dev(ql), dev(qr), w.sm_scale)
     assert e.value.status == m.MLA8_E_CAPACITY
+
+
+def test_append_decode_graph_replays_match_eager(m):
+    # the bench replays a captured step; every replay must reproduce the eager
+    # result (the fused append rewrites the same fresh row each time)
+    w = W.DSV3
+    say("append_decode under graph replay")
+    t = 3000
+    x = W.rows(w, t, seed_offset=4)
+    ql, qr = W.queries(w, seed_offset=4)
+    codes = torch.zeros((t, w.d), dtype=torch.uint8, device=DEV)
+    scales = torch.zeros((t,), dtype=torch.float32, device=DEV)
+    assert m.mla8_append(codes, scales, 0, dev(x[:t - 1]), w.lc, w.rc) == t - 1
+    fresh, qld, qrd = dev(x[t - 1:]), dev(ql), dev(qr)
+    out = torch.empty((w.n_heads, w.lc), dtype=torch.float32, device=DEV)
+    lse = torch.empty((w.n_heads,), dtype=torch.float32, device=DEV)
+    ws = torch.empty(m.mla8_workspace_bytes(m.MLA8_OP_DECODE, t, w.n_heads, 1, w.lc),
+                     dtype=torch.uint8, device=DEV)
+
+    def step():
+        m.mla8_append_decode(codes, scales, t - 1, fresh, w.lc, w.rc, qld, qrd, w.sm_scale,
+                             out=out, lse=lse, workspace=ws)
+
+    step()
+    ref_out, ref_lse = host(out).copy(), host(lse).copy()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step()
+    torch.cuda.current_stream().wait_stream(s)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for r in range(4):
+        out.zero_()
+        lse.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(host(out), ref_out), r
+        assert np.array_equal(host(lse), ref_lse), r
+        _ = (torch.ones(1000, device=DEV) * 2).sum().item()  # eager work between replays
+    oc, os_ = oracle.quantize_rows(x)
+    ro, rl = oracle.decode(oc, os_, t, w.lc, w.rc, ql, qr, w.sm_scale)
+    check_attention(ref_out, ro, ref_lse, rl, "append_decode graph")
