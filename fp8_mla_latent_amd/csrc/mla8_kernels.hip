@@ -159,15 +159,16 @@ struct QueryTerms {
 };
 
 
-// Query loads of build_query_terms: thread t handles head h = t / 16 (16
-// threads per head, all in one wave) and the 4-element groups gi = t % 16 +
-// 16 s of that head.  Every load is issued before any is used.
+// Query loads of build_query_terms: work item t (0 .. 511) handles head
+// h = t / 16 (16 items per head, one 16-lane row of a wave) and the 4-element
+// groups gi = t % 16 + 16 s of that head.  Every load is issued before any is
+// used.
 template <int NKB>
-__device__ __forceinline__ void load_query(const AttnArgs& a, int qh0,
+__device__ __forceinline__ void load_query(const AttnArgs& a, int qh0, int t,
                                            float4 (&v)[2 * QueryTerms<NKB>::NB])
 {
     constexpr int PER = 2 * QueryTerms<NKB>::NB;  // NB blocks x 32 groups / 16 threads
-    const int h = threadIdx.x >> 4, i = threadIdx.x & 15;
+    const int h = t >> 4, i = t & 15;
     const int qh = qh0 + h;
     const bool hv = qh < a.n_qh;
 #pragma unroll
@@ -188,13 +189,13 @@ __device__ __forceinline__ void load_query(const AttnArgs& a, int qh0,
 }
 
 template <int NKB>
-__device__ __forceinline__ void build_query_terms(const AttnArgs& a,
+__device__ __forceinline__ void build_query_terms(const AttnArgs& a, int t,
                                                   const float4 (&v)[2 * QueryTerms<NKB>::NB],
                                                   uint8_t* qt, int* s_k)
 {
     using Q = QueryTerms<NKB>;
     constexpr int PER = 2 * Q::NB;
-    const int h = threadIdx.x >> 4, i = threadIdx.x & 15;
+    const int h = t >> 4, i = t & 15;
     float amax = 0.0f;
 #pragma unroll
     for (int s = 0; s < PER; ++s)
@@ -278,13 +279,13 @@ struct QueryTermsMx {
     static constexpr int NG = LC / 4 / 16;          // noPE float4 groups per thread
 };
 
-// Query loads for mixed rows: thread t takes head t / 16; noPE groups
+// Query loads for mixed rows: work item t takes head t / 16; noPE groups
 // gi = t % 16 + 16 s (s < NG) and RoPE group t % 16.
-__device__ __forceinline__ void load_query_mx(const AttnArgs& a, int qh0,
+__device__ __forceinline__ void load_query_mx(const AttnArgs& a, int qh0, int t,
                                               float4 (&v)[QueryTermsMx::NG + 1])
 {
     using Q = QueryTermsMx;
-    const int h = threadIdx.x >> 4, i = threadIdx.x & 15;
+    const int h = t >> 4, i = t & 15;
     const int qh = qh0 + h;
     const bool hv = qh < a.n_qh;
 #pragma unroll
@@ -298,12 +299,12 @@ __device__ __forceinline__ void load_query_mx(const AttnArgs& a, int qh0,
     v[Q::NG] = hv ? x : make_float4(0.f, 0.f, 0.f, 0.f);
 }
 
-__device__ __forceinline__ void build_query_terms_mx(const AttnArgs& a,
+__device__ __forceinline__ void build_query_terms_mx(const AttnArgs& a, int t,
                                                      const float4 (&v)[QueryTermsMx::NG + 1],
                                                      uint8_t* qt, int* s_k)
 {
     using Q = QueryTermsMx;
-    const int h = threadIdx.x >> 4, i = threadIdx.x & 15;
+    const int h = t >> 4, i = t & 15;
     float amax = 0.0f;
 #pragma unroll
     for (int s = 0; s < Q::NG; ++s)
@@ -510,17 +511,22 @@ typedef int v2i __attribute__((ext_vector_type(2)));
 
 // Split-T partial.  Grid: n_chunks * n_groups workgroups of 512 threads (8
 // waves, two per SIMD).  NKB = number of 64-byte blocks of the padded row.
-//   loads  : 64-row tiles stream HBM -> LDS through a ring of direct
-//            global_load_lds_dwordx4 (no register staging);
-//   scores : wave w takes rows 16*(w>>1) .. +16 of the tile and heads
+// The waves take two roles, one of each per SIMD, so that the MFMA-heavy score
+// work of one overlaps the conversion and softmax work of the other:
+//   score waves (0-3): rows 32*(w>>1) .. +32 of each tile against heads
 //            16*(w&1) .. +16 of the group: 3 e4m3 query terms in registers x
-//            the raw e4m3 row bytes on the scaled fp8 MFMA;
-//   context: wave w owns context columns 64*w .. +64 for all 32 heads; the
-//            row bytes are read transposed (ds_read_b64_tr_b8) so the row
-//            index lands on the MFMA K index, widened to fp16 exactly.
-// One barrier per tile: phase p scores tile p and writes its weights with the
-// softmax state as it stands, checks tile p-1's maxima against that state and
-// accumulates tile p-1's context.
+//            the raw e4m3 row bytes on the scaled fp8 MFMA; then the
+//            weights and the check sums;
+//   context waves (4-7): context columns 128*(w-4) .. +128 for all 32 heads;
+//            the row bytes are read transposed (ds_read_b64_tr_b8) so the row
+//            index lands on the MFMA K index, widened to fp16 exactly; they
+//            also issue every direct load of the row stream.
+//   loads  : 64-row tiles stream HBM -> LDS through a ring of direct
+//            global_load_lds_dwordx4 (no register staging).
+// One barrier per tile: in phase p the score waves score tile p and write its
+// weights with the softmax state as it stands, while the context waves
+// accumulate tile p-1; both first vote on tile p-1's maxima against that
+// state.
 template <int NKB, bool GATHER, bool MXL = false>
 __global__ __launch_bounds__(kThreads, 1) void k_split_partial(AttnArgs a)
 {
@@ -532,7 +538,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_split_partial(AttnArgs a)
     constexpr int TR = L::TR, NW = L::NW, HG = L::HG, NB = L::NB, NFULL = L::NFULL;
     constexpr int RQB = L::RQB, WSS = L::WSS, NST = L::NST, DIST = L::DIST;
     constexpr int NINS = L::STAGE / 1024;     // 1-KB DMA instructions per tile
-    constexpr int KW = (NINS + NW - 1) / NW;  // row DMA instructions per wave per tile
+    constexpr int NWI = NW / 2;               // waves that issue the direct loads
+    constexpr int KW = (NINS + NWI - 1) / NWI;  // row DMA instructions per issuing wave per tile
     static_assert(KW + 1 < 64, "vmcnt range");
 
     __shared__ __attribute__((aligned(1024))) uint8_t lds[L::TOTAL];
@@ -548,8 +555,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_split_partial(AttnArgs a)
 
     const int tid = threadIdx.x;
     const int w = tid >> 6, lane = tid & 63, n = lane & 15, g = lane >> 4;
-    const int hh = w & 1;   // head half of the group this wave scores
-    const int rq = w >> 1;  // row quarter of the tile this wave scores
+    const int hh = w & 1;  // head half of the group a score wave scores
 
     // Workgroup -> (chunk, head group).  Dispatch is round-robin over the 8
     // XCDs; keep the head groups of one chunk on one XCD, launched back to back.
@@ -570,15 +576,18 @@ __global__ __launch_bounds__(kThreads, 1) void k_split_partial(AttnArgs a)
     const int c1 = min(a.n_list, c0 + a.chunk_rows);
     const int ntiles = c1 > c0 ? (c1 - c0 + TR - 1) / TR : 0;
 
-    // ---- tile issue.  Every wave issues KW row DMAs per tile and wave 0 one
-    // more for the row scales, so a fixed per-wave vmcnt marks a tile
-    // complete.  Row DMA instruction k fills stage slots [64k, 64k + 64)
+    // ---- tile issue.  The context waves (w >= NWI) issue every direct load:
+    // KW row DMAs per tile each and the first of them one more for the row
+    // scales, so a fixed per-wave vmcnt marks a tile complete.  The score
+    // waves, which carry the longer dependency chain, issue none.  Row DMA instruction k fills stage slots [64k, 64k + 64)
     // (16 bytes each, layout above).  Slots past the row's data (zero-pad
     // columns) and rows outside the list load chunk 0 / the tile's first row
     // instead: finite bytes that are multiplied by a zero query element, masked
     // out of the softmax, or never read.  Spare instruction slots (k >= NINS)
     // repeat instruction k % NINS (the same bytes to the same place).
     const int cpr = a.d >> 4;  // 16-byte data chunks per row
+    const int wi = (w >= NWI) ? w - NWI : 0;  // issuer index
+    const bool dma_lead = w == NWI;           // issues the scale loads too
     auto row_of = [&](int pos) __attribute__((always_inline)) -> int32_t {
         if (pos >= c1)
             return -1;
@@ -593,10 +602,10 @@ __global__ __launch_bounds__(kThreads, 1) void k_split_partial(AttnArgs a)
     uint32_t kofs[KW];
 #pragma unroll
     for (int i = 0; i < KW; ++i)
-        kofs[i] = __builtin_amdgcn_readfirstlane((uint32_t)(1024 * ((w + NW * i) % NINS)));
+        kofs[i] = __builtin_amdgcn_readfirstlane((uint32_t)(1024 * ((wi + NWI * i) % NINS)));
 #pragma unroll
     for (int i = 0; i < KW; ++i) {
-        const int k = (w + NW * i) % NINS;
+        const int k = (wi + NWI * i) % NINS;
         const int sl = 64 * k + lane;
         const int q4 = sl / (64 * NKB), s1 = sl - q4 * (64 * NKB);
         int j, h, ln;
@@ -631,7 +640,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_split_partial(AttnArgs a)
 #pragma unroll
                 for (int i = I0; i < I1; ++i)
                     dma_b128_s(tb, (uint32_t)(dpk[i] & 0xFFFF), xst + kofs[i]);
-                if (LAST && w == 0)
+                if (LAST && dma_lead)
                     dma_b32_s(a.scales + p0, (uint32_t)(4 * lane), sct);
             } else {
 #pragma unroll
@@ -641,7 +650,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_split_partial(AttnArgs a)
                         (uint32_t)((dpk[i] & 0xFFFF) - (r < nv ? 0 : r * a.d));
                     dma_b128_s(tb, off, xst + kofs[i]);
                 }
-                if (LAST && w == 0)
+                if (LAST && dma_lead)
                     dma_b32_s(a.scales + p0, (uint32_t)(4 * (lane < nv ? lane : 0)), sct);
             }
         } else {
@@ -653,7 +662,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_split_partial(AttnArgs a)
             for (int i = I0; i < I1; ++i)
                 rows[i - I0] = row_of(p0 + (dpk[i] >> 16));
             int32_t srow = 0;
-            if (LAST && w == 0)
+            if (LAST && dma_lead)
                 srow = row_of(p0 + lane);
 #pragma unroll
             for (int i = I0; i < I1; ++i) {
@@ -662,7 +671,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_split_partial(AttnArgs a)
                 const int32_t row = rows[i - I0];
                 dma_b128(a.codes + (size_t)(row >= 0 ? row : 0) * a.d + cc, xst + kofs[i]);
             }
-            if (LAST && w == 0) {
+            if (LAST && dma_lead) {
                 dma_b32(a.scales + (srow >= 0 ? srow : 0), sct);
                 s_row[st * TR + lane] = srow;
             }
@@ -679,7 +688,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_split_partial(AttnArgs a)
     // (two tiles ahead) or none (one tile ahead).
     auto wait_tile = [&](bool next_in_flight) __attribute__((always_inline)) {
         if (DIST == 2 && next_in_flight) {
-            if (w == 0)
+            if (dma_lead)
                 wait_vmcnt<KW + 1>();
             else
                 wait_vmcnt<KW>();
@@ -694,465 +703,586 @@ __global__ __launch_bounds__(kThreads, 1) void k_split_partial(AttnArgs a)
     // of a wave complete in issue order, so stores issued before the first
     // tile's loads are complete once phase 1 has waited for its tile, and the
     // phase barrier orders them before any wave's later loads: a chunk whose
-    // fresh rows start at tile DIST + 1 or later quantizes them after the
-    // prologue (the stall on the fresh row's load then overlaps the first
-    // tiles' loads).  Otherwise they are quantized and waited for before the
-    // first load is issued.
+    // fresh rows start at tile DIST + 1 or later has them quantized after the
+    // prologue by the context waves, which wait for their loads every phase
+    // (the stall on the fresh row's load then overlaps the first tiles'
+    // loads).  Otherwise every wave quantizes, and waits, before the first
+    // load is issued.
     int f0 = 0, f1 = 0;
     if (a.n_new > 0) {
         f0 = max(c0, a.new0);
         f1 = min(c1, a.new0 + a.n_new);
     }
     const bool fresh_late = f0 < f1 && (f0 - c0) / TR >= DIST + 1;
-    auto quantize_fresh = [&]() __attribute__((always_inline)) {
-        for (int r = f0 + w; r < f1; r += NW)
+    auto quantize_fresh = [&](int first, int stride) __attribute__((always_inline)) {
+        for (int r = f0 + first; r < f1; r += stride)
             quantize_row_wave(a.x_new + (size_t)(r - a.new0) * a.d, a.d,
                               a.new_codes + (size_t)r * a.d, a.new_scales + r, lane);
     };
     if (f0 < f1 && !fresh_late) {
-        quantize_fresh();
+        quantize_fresh(w, NW);
         wait_vmcnt<0>();
         __syncthreads();
     }
 
-    // ---- query terms for the group, staged in LDS (over the ring stages not
-    // yet in flight when they fit there), then each wave keeps its head
-    // half's in registers.  The query loads go out first, then the first
-    // tiles' direct loads, so that waiting for the query does not wait for
-    // the tiles.
-    if constexpr (MXL) {
-        float4 qin[QM::NG + 1];
-        load_query_mx(a, qh0, qin);
+    // ---- the context waves issue the first tiles' direct loads at once; the
+    // score waves meanwhile build the query terms of the group (both head
+    // halves, in two passes of 256 work items) into an LDS staging area over
+    // the ring stages not yet in flight (when they fit there), and then keep
+    // their head half's in registers.
+    if (w >= NWI) {
         if (ntiles > 0)
             issue_all(0, 0);
         if (DIST == 2 && ntiles > 1)
             issue_all(1, 1);
-        build_query_terms_mx(a, qin, lds + L::QT, s_k);
+    } else if constexpr (MXL) {
+        float4 qin0[QM::NG + 1], qin1[QM::NG + 1];
+        load_query_mx(a, qh0, tid, qin0);
+        load_query_mx(a, qh0, tid + NWI * 64, qin1);
+        build_query_terms_mx(a, tid, qin0, lds + L::QT, s_k);
+        build_query_terms_mx(a, tid + NWI * 64, qin1, lds + L::QT, s_k);
     } else {
-        float4 qin[2 * NB];
-        load_query<NKB>(a, qh0, qin);
-        if (ntiles > 0)
-            issue_all(0, 0);
-        if (DIST == 2 && ntiles > 1)
-            issue_all(1, 1);
-        build_query_terms<NKB>(a, qin, lds + L::QT, s_k);
+        float4 qin0[2 * NB], qin1[2 * NB];
+        load_query<NKB>(a, qh0, tid, qin0);
+        load_query<NKB>(a, qh0, tid + NWI * 64, qin1);
+        build_query_terms<NKB>(a, tid, qin0, lds + L::QT, s_k);
+        build_query_terms<NKB>(a, tid + NWI * 64, qin1, lds + L::QT, s_k);
     }
     lds_barrier();
-    v8i qv[NSL];
-#pragma unroll
-    for (int sl = 0; sl < NSL; ++sl)
-        qv[sl] = *reinterpret_cast<const v8i*>(
-            lds + L::QT + ((hh * NSL + sl) * 64 + lane) * 32);
-    // mixed rows: the RoPE query terms (bf16), two per K step
-    bf16x8 qr[MXL ? QM::NRS : 1];
-    if constexpr (MXL) {
-#pragma unroll
-        for (int sl = 0; sl < QM::NRS; ++sl)
-            qr[sl] = *reinterpret_cast<const bf16x8*>(
-                lds + L::QT + QM::RBASE + ((hh * QM::NRS + sl) * 64 + lane) * 16);
-    }
-    // E8M0 operand scales 2^(-k - 4t) of this lane's head.  The instruction
-    // takes the scale of 32-element K block kb from lane group kb, and lane
-    // group g's bytes 0-15 / 16-31 fall in blocks g / 2 and 2 + g / 2.  The
-    // packed half block carries t1 in lane groups 0-1 (blocks 0 and 2) and t2
-    // in lane groups 2-3 (blocks 1 and 3): even lane groups give t1's scale,
-    // odd ones t2's.
-    const int kq = s_k[16 * hh + n];
-    const int sbt0 = 127 - kq, sbt1 = sbt0 - kTermShift, sbt2 = sbt0 - 2 * kTermShift;
-    const int sb_pack = (g & 1) ? sbt1 : sbt0;
-    // mixed rows: the fourth term's scale, and the packed t3 | t4 slot's
-    const int sbt3 = sbt0 - 3 * kTermShift;
-    const int sb_pack2 = (g & 1) ? sbt3 : sbt2;
-    const int qh_own = qh0 + 16 * hh + n;
-    const int32_t tlim = (a.mode == kCausal)
-                             ? a.pos0 + (qh_own < a.n_qh ? qh_own / a.n_heads : 0) + 1
-                             : 0x7FFFFFFF;
-    lds_barrier();  // staging area free for the ring
-    if (fresh_late)
-        quantize_fresh();
 
     // Softmax state, identical in every wave, for heads n and 16 + n of the
     // group: m = lazy max of u (z side), d = lazy max of (u - m) + log2 scale
     // (context side, relative to m).  The weights of tile p are computed with
     // the state as it stands, in the linear domain:
     //     p_t = 2^(u_t - m),  w_t = p_t * (scale_t * 2^-d),
-    // and the tile's sums of p + w per wave are checked one phase later.  Only
-    // when a sum leaves [0, 2^kTau] (a new maximum by more than kTau, the first
-    // tile, or an intermediate that left f32's range) is the state recomputed
-    // exactly in the log domain, the context rescaled and the tile's weights
-    // rewritten (as 2^((u - m) + log2 scale - d)).
+    // and the tile's sums of p + w per (head, row quarter) are checked one
+    // phase later.  Only when a sum leaves [0, 2^kTau] (a new maximum by more
+    // than kTau, the first tile, or an intermediate that left f32's range) is
+    // the state recomputed exactly in the log domain, the context rescaled and
+    // the tile's weights rewritten (as 2^((u - m) + log2 scale - d)).
     // (separate scalars, never an array: a lane-dependent pick from an array
     // would put it in scratch memory)
     float mrun0 = -INFINITY, mrun1 = -INFINITY, drun0 = -INFINITY, drun1 = -INFINITY;
-    float fown = 1.0f;   // 2^-d of this lane's own head (2^0 while d = -inf)
+    float fown = 1.0f;  // 2^-d of head 16 hh + n (2^0 while d = -inf); score waves
     // A head whose m is still -inf has not met a valid row, and the linear
     // weights of a first valid row may underflow to a zero sum: while any head
     // of the group is in that state every check takes the exact path
     // (uniform: every wave holds the same state).
     bool uninit = true;
-    float zacc = 0.0f;   // z partial over this lane's rows, head 16*hh + n
-    float zsave = 0.0f;  // zacc before the last scored tile
-    float u[4], scv[4];  // this lane's scores / row scales of the last scored tile
-    f32x4 O[2][4];
-#pragma unroll
-    for (int ht = 0; ht < 2; ++ht)
-#pragma unroll
-        for (int jm = 0; jm < 4; ++jm)
-            O[ht][jm] = f32x4{0.f, 0.f, 0.f, 0.f};
-    const int cb = 64 * w;  // this wave's context columns
-    const bool pv_active = cb < a.lc;
-    // Score operand: lane (n, g) of block j, half h reads slot n + 16 g of
-    // group (j, h) of its row quarter; in a trailing half block lanes g >= 2
-    // re-read the slots of g - 2, whose query elements carry the packed second
-    // term.
-    const int qa = rq * RQB + 16 * lane;
-    const int qa_half = rq * RQB + NFULL * 2048 + 16 * (lane & 31);
-    // Context operand: source lane 2k + h' of 16-lane group g' addresses row
-    // 8 g' + k (row quarter g' / 2, slot n = 8 (g' & 1) + k), bytes 8 h' .. of
-    // the column chunk; the transposed read hands lane (n, g') column n of
-    // rows 8 g' .. 8 g' + 7.  Wave w's columns 64 w .. are chunks 4 w .. 4 w
-    // + 3: block w / 2, lane groups 2 (w & 1) + jm / 2, halves jm & 1.
-    const int trl = (g >> 1) * RQB + 16 * (8 * (g & 1) + ((lane & 15) >> 1)) + 8 * (lane & 1);
-    const bool ctx_half = (w >> 1) >= NFULL;  // the wave's columns lie in a half block
-    const int trw = ctx_half ? NFULL * 2048 : (w >> 1) * 2048 + (w & 1) * 512;
-    _Float16* const s_w_own = s_w + (16 * hh + n) * WSS + 16 * rq + 4 * g;
     constexpr float kCheck = 256.0f;  // 2^kTau
     static_assert(kTau == 8.0f, "check threshold");
+    float2* const s_cr2 = reinterpret_cast<float2*>(s_cr);
 
-    // Weights of this lane's rows (linear form) into buffer buf; returns this
-    // lane's sum of p + w.
-    auto weights_linear = [&](int buf) __attribute__((always_inline)) -> float {
-        const float mu = hh ? mrun1 : mrun0;
-        const float mz = (mu == -INFINITY) ? 0.0f : mu;
-        float ps = 0.0f, chk = 0.0f;
-        f16x4 wv;
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-            const float pv = fast_exp2(u[v] - mz);
-            const float wt = pv * (scv[v] * fown);
-            ps += pv;
-            chk += pv + wt;
-            wv[v] = (_Float16)wt;
-        }
-        zacc = zsave + ps;
-        *reinterpret_cast<f16x4*>(s_w_own + buf * HG * WSS) = wv;
-        return chk;
-    };
-    // Same in the log domain (exact for any scale), used after a state move.
-    auto weights_log = [&](int buf) __attribute__((always_inline)) {
-        const float mu = hh ? mrun1 : mrun0;
-        const float dd = hh ? drun1 : drun0;
-        const float mz = (mu == -INFINITY) ? 0.0f : mu;
-        const float dn = (dd == -INFINITY) ? 0.0f : dd;
-        float ps = 0.0f;
-        f16x4 wv;
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-            const float av = u[v] - mz;
-            ps += fast_exp2(av);
-            wv[v] = (_Float16)fast_exp2((av + log2f(scv[v])) - dn);
-        }
-        zacc = zsave + ps;
-        *reinterpret_cast<f16x4*>(s_w_own + buf * HG * WSS) = wv;
-    };
-
-    // ---- context: O[32 heads][64 cols of this wave] += W . X of the tile in
-    // stage st with weight buffer buf.  MFMA (ht, jm) covers heads 16 ht ..
-    // +16 and columns cb + 16 jm .. +16.
-    auto context = [&](int st, int buf, auto HALF_) __attribute__((always_inline)) {
-        constexpr bool HALFC = decltype(HALF_)::value;
-        const uint8_t* xst = lds + st * L::STAGE + trw + trl;
-        const _Float16* sw = s_w + buf * HG * WSS;
-#pragma unroll
-        for (int ks = 0; ks < TR / 32; ++ks) {
-            f16x8 wa[2];
-#pragma unroll
-            for (int ht = 0; ht < 2; ++ht)
-                wa[ht] = *reinterpret_cast<const f16x8*>(&sw[(16 * ht + n) * WSS + 32 * ks + 8 * g]);
-#pragma unroll
-            for (int jm = 0; jm < 4; ++jm) {
-                const int off = 2 * ks * RQB + (jm & 1) * (HALFC ? 512 : 1024) + (jm >> 1) * 256;
-                const v2i xb = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-                    (MLA8_LDS v2i*)(MLA8_LDS uint8_t*)(xst + off));
-                const f16x8 bx = cvt8((uint32_t)xb[0], (uint32_t)xb[1]);
-                O[0][jm] = mfma16(wa[0], bx, O[0][jm]);
-                O[1][jm] = mfma16(wa[1], bx, O[1][jm]);
-            }
-        }
-    };
-
-    // Scores of tile p (stage st): S^T[16 rows][16 heads] in log2 units of the
-    // codes, two accumulators so consecutive MFMAs do not wait on each other.
-    f32x4 acc0, acc1, accr;
-    // Mixed rows: the noPE half block is the first half of LDS block 3 (a full
-    // 1-KB group pair); RoPE K step m reads 16-byte chunk 28 + 4m + g of row
-    // 16 rq + n, in LDS block 3 (m = 0, lane groups 2-3) or in the trailing
-    // half block 4 (m = 1, lane groups 0-1).
-    const int qa_mxh = rq * RQB + 3 * 2048 + 16 * (lane & 31);
-    const int ro0 = rq * RQB + 3 * 2048 + (g & 1) * 1024 + 16 * (n + 16 * (2 + (g >> 1)));
-    const int ro1 = rq * RQB + 4 * 2048 + (g & 1) * 512 + 16 * (n + 16 * (g >> 1));
-    auto scores = [&](int st) __attribute__((always_inline)) {
-        const uint8_t* xst = lds + st * L::STAGE;
-        acc0 = f32x4{0.f, 0.f, 0.f, 0.f};
-        acc1 = acc0;
-        if constexpr (MXL) {
-            accr = acc0;
-#pragma unroll
-            for (int j = 0; j <= QM::NFULL; ++j) {
-                const uint8_t* xp = (j < QM::NFULL) ? xst + qa + 2048 * j : xst + qa_mxh;
-                const uint4 x0 = *reinterpret_cast<const uint4*>(xp);
-                const uint4 x1 = *reinterpret_cast<const uint4*>(xp + 1024);
-                const v8i xv = v8i{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w,
-                                   (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
-                if (j < QM::NFULL) {
-                    acc0 = mfma_fp8_scaled(xv, qv[4 * j], acc0, sbt0);
-                    acc1 = mfma_fp8_scaled(xv, qv[4 * j + 1], acc1, sbt1);
-                    acc0 = mfma_fp8_scaled(xv, qv[4 * j + 2], acc0, sbt2);
-                    acc1 = mfma_fp8_scaled(xv, qv[4 * j + 3], acc1, sbt3);
-                } else {
-                    acc1 = mfma_fp8_scaled(xv, qv[4 * j], acc1, sb_pack);
-                    acc0 = mfma_fp8_scaled(xv, qv[4 * j + 1], acc0, sb_pack2);
-                }
-            }
-#pragma unroll
-            for (int m = 0; m < QM::NRS / 2; ++m) {
-                const bf16x8 xr = *reinterpret_cast<const bf16x8*>(xst + (m ? ro1 : ro0));
-                accr = mfma_bf16(xr, qr[2 * m], accr);
-                accr = mfma_bf16(xr, qr[2 * m + 1], accr);
-            }
-            return;
-        }
-#pragma unroll
-        for (int j = 0; j < NB; ++j) {
-            const uint8_t* xp = (j < NFULL) ? xst + qa + 2048 * j : xst + qa_half;
-            const int hoff = (j < NFULL) ? 1024 : 512;
-            const uint4 x0 = *reinterpret_cast<const uint4*>(xp);
-            const uint4 x1 = *reinterpret_cast<const uint4*>(xp + hoff);
-            const v8i xv = v8i{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w,
-                               (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
-            if (j < Q::NFULL) {
-                acc0 = mfma_fp8_scaled(xv, qv[3 * j], acc0, sbt0);
-                acc1 = mfma_fp8_scaled(xv, qv[3 * j + 1], acc1, sbt1);
-                acc0 = mfma_fp8_scaled(xv, qv[3 * j + 2], acc0, sbt2);
-            } else {
-                acc1 = mfma_fp8_scaled(xv, qv[3 * j], acc1, sb_pack);
-                acc0 = mfma_fp8_scaled(xv, qv[3 * j + 1], acc0, sbt2);
-            }
-        }
-    };
-
-    // Check of tile p-1 (weight buffer bufp).
-    auto check = [&](int bufp) __attribute__((always_inline)) {
-        // Sums of p + w of tile p-1 per (head, row quarter); every wave reads
-        // the same sums and holds the same state, so the vote is uniform
-        // across the workgroup and the barriers below are reached by all
-        // waves or none.
+    // Vote on tile p-1 (weight buffer bufp): every wave reads the same sums
+    // and holds the same state, so the result is uniform across the
+    // workgroup and the barriers of the exact path are reached by all waves
+    // or none.
+    auto vote_read = [&](int bufp, float4 (&S4)[2]) __attribute__((always_inline)) {
         const float* mxp = s_mx + bufp * HG * 4;
+#pragma unroll
+        for (int ht = 0; ht < 2; ++ht)
+            S4[ht] = *reinterpret_cast<const float4*>(mxp + (16 * ht + n) * 4);
+    };
+    auto vote = [&](const float4 (&S4)[2]) __attribute__((always_inline)) -> bool {
         bool moved = false;
 #pragma unroll
-        for (int ht = 0; ht < 2; ++ht) {
-            const float4 S4 = *reinterpret_cast<const float4*>(mxp + (16 * ht + n) * 4);
-            // false for NaN: a non-finite intermediate also recomputes
-            moved |= !(fmaxf(fmaxf(S4.x, S4.y), fmaxf(S4.z, S4.w)) <= kCheck);
-        }
-        if (uninit || __any(moved)) {
-            // Keep this path's arithmetic inside the branch: the empty asm
-            // makes u and the scales opaque here, so none of it is hoisted
-            // into the common path.
-            asm volatile("" : "+v"(u[0]), "+v"(u[1]), "+v"(u[2]), "+v"(u[3]), "+v"(scv[0]),
-                         "+v"(scv[1]), "+v"(scv[2]), "+v"(scv[3]));
-            // exact maxima of tile p-1 per wave: Tw = max u, Cw = max (u - Tw)
-            // + log2 scale, relative so that a large |u| never swallows log2
-            // scale
-            float tw = fmaxf(fmaxf(u[0], u[1]), fmaxf(u[2], u[3]));
-            tw = max_xor32(max_xor16(tw));
-            float cw = -INFINITY;
-            if (tw != -INFINITY) {
-#pragma unroll
-                for (int v = 0; v < 4; ++v)
-                    cw = fmaxf(cw, (u[v] - tw) + log2f(scv[v]));
-            }
-            cw = max_xor32(max_xor16(cw));
-            float2* const s_cr2 = reinterpret_cast<float2*>(s_cr);
-            if (g == 0)
-                s_cr2[(16 * hh + n) * 4 + rq] = make_float2(tw, cw);
-            lds_barrier();  // (R1)
-            float alz[2], alo[2];
-#pragma unroll
-            for (int ht = 0; ht < 2; ++ht) {
-                const int h = 16 * ht + n;
-                const float4 r01 = *reinterpret_cast<const float4*>(&s_cr2[h * 4]);
-                const float4 r23 = *reinterpret_cast<const float4*>(&s_cr2[h * 4 + 2]);
-                const float Tk[4] = {r01.x, r01.z, r23.x, r23.z};
-                const float Ck[4] = {r01.y, r01.w, r23.y, r23.w};
-                const float T = fmaxf(fmaxf(Tk[0], Tk[1]), fmaxf(Tk[2], Tk[3]));
-                float& mr = ht ? mrun1 : mrun0;
-                float& dr = ht ? drun1 : drun0;
-                const float mold = mr;
-                const float mnew = (T > mold + kTau) ? T : mold;
-                alz[ht] = (mnew == mold) ? 1.0f : fast_exp2(mold - mnew);
-                const float mu = (mnew == -INFINITY) ? 0.0f : mnew;
-                float tb = -INFINITY;
-#pragma unroll
-                for (int k = 0; k < 4; ++k)
-                    if (Tk[k] != -INFINITY)
-                        tb = fmaxf(tb, Ck[k] + (Tk[k] - mu));
-                const float dshift = (mnew == mold) ? dr : dr + (mold - mnew);
-                const float dnew = (tb > dshift + kTau) ? tb : dshift;
-                alo[ht] = (dnew == dshift) ? 1.0f : fast_exp2(dshift - dnew);
-                mr = mnew;
-                dr = dnew;
-            }
-            // O holds tiles < p-1 in units of the old state; its heads
-            // 16*ht + 4*g + v take their factors from lanes 4*g + v.
-#pragma unroll
-            for (int ht = 0; ht < 2; ++ht)
-#pragma unroll
-                for (int v = 0; v < 4; ++v) {
-                    const float f = __shfl(alo[ht], 4 * g + v);
-#pragma unroll
-                    for (int jm = 0; jm < 4; ++jm)
-                        O[ht][jm][v] *= f;
-                }
-            zsave *= hh ? alz[1] : alz[0];
-            const float dd = hh ? drun1 : drun0;
-            fown = (dd == -INFINITY) ? 1.0f : fast_exp2(-dd);
-            uninit = __any(mrun0 == -INFINITY || mrun1 == -INFINITY);
-            weights_log(bufp);  // tile p-1 under the new state
-            lds_barrier();      // (R2) rewritten weights visible; s_cr free
-        }
+        for (int ht = 0; ht < 2; ++ht)  // false for NaN: a non-finite intermediate also recomputes
+            moved |= !(fmaxf(fmaxf(S4[ht].x, S4[ht].y), fmaxf(S4[ht].z, S4[ht].w)) <= kCheck);
+        return uninit || __any(moved);
     };
-
-    // Phase p: score tile p (ring stage p % NST, buffers p & 1), check the
-    // sums of tile p - 1, then accumulate tile p-1's context while tile p's
-    // weights are computed (one block, so the weight arithmetic fills the gaps
-    // between the context MFMAs).  One extra phase finishes the last tile.
-    for (int p = 0, st = 0, stp = NST - 1; p <= ntiles;
-         ++p, stp = st, st = (st == NST - 1) ? 0 : st + 1) {
-        // st = p % NST, stp = (p - 1) % NST
-        const int buf = p & 1, bufp = buf ^ 1;
-        if (p < ntiles)
-            wait_tile(p + 1 < ntiles);
-        lds_barrier();  // (A) tile p visible; weights and sums of tile p-1
-                        //     complete; stage (p + DIST) % NST (tile p + DIST
-                        //     - NST) and buffers p & 1 free
-        const bool more = p + DIST < ntiles;
-        const int sti = (st + DIST) % NST;
-        if (more)
-            issue(p + DIST, sti, IC0{}, ICA{});
-        const bool scored = p < ntiles;
-        if (scored)
-            scores(st);
-        if (p >= 1)
-            check(bufp);
-        if (more)
-            issue(p + DIST, sti, ICA{}, ICB{});
-
-        // ---- log2-domain scores u of tile p (rows 16rq + 4g + v, head
-        // 16hh + n) from the score accumulators; masking: rows past the list,
-        // invalid gathered rows, causal limit
-        const float* scs = s_sc + st * TR;
-        const int p0 = c0 + p * TR;
-        auto scores_to_u = [&](bool mask) __attribute__((always_inline)) {
-            const float4 sc4 = *reinterpret_cast<const float4*>(scs + 16 * rq + 4 * g);
-            scv[0] = sc4.x;
-            scv[1] = sc4.y;
-            scv[2] = sc4.z;
-            scv[3] = sc4.w;
-            zsave = zacc;
+    // Exact state move from the tile maxima (T, C) per (head, row quarter) in
+    // s_cr; alz / alo receive the factors for z and for the context
+    // accumulators of heads n, 16 + n.
+    auto state_move = [&](float (&alz)[2], float (&alo)[2]) __attribute__((always_inline)) {
 #pragma unroll
-            for (int v = 0; v < 4; ++v)
-                u[v] = MXL ? (acc0[v] + acc1[v]) * scv[v] + accr[v] : (acc0[v] + acc1[v]) * scv[v];
-            if (mask) {
+        for (int ht = 0; ht < 2; ++ht) {
+            const int h = 16 * ht + n;
+            const float4 r01 = *reinterpret_cast<const float4*>(&s_cr2[h * 4]);
+            const float4 r23 = *reinterpret_cast<const float4*>(&s_cr2[h * 4 + 2]);
+            const float Tk[4] = {r01.x, r01.z, r23.x, r23.z};
+            const float Ck[4] = {r01.y, r01.w, r23.y, r23.w};
+            const float T = fmaxf(fmaxf(Tk[0], Tk[1]), fmaxf(Tk[2], Tk[3]));
+            float& mr = ht ? mrun1 : mrun0;
+            float& dr = ht ? drun1 : drun0;
+            const float mold = mr;
+            const float mnew = (T > mold + kTau) ? T : mold;
+            alz[ht] = (mnew == mold) ? 1.0f : fast_exp2(mold - mnew);
+            const float mu = (mnew == -INFINITY) ? 0.0f : mnew;
+            float tb = -INFINITY;
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+                if (Tk[k] != -INFINITY)
+                    tb = fmaxf(tb, Ck[k] + (Tk[k] - mu));
+            const float dshift = (mnew == mold) ? dr : dr + (mold - mnew);
+            const float dnew = (tb > dshift + kTau) ? tb : dshift;
+            alo[ht] = (dnew == dshift) ? 1.0f : fast_exp2(dshift - dnew);
+            mr = mnew;
+            dr = dnew;
+        }
+        const float dd = hh ? drun1 : drun0;
+        fown = (dd == -INFINITY) ? 1.0f : fast_exp2(-dd);
+        uninit = __any(mrun0 == -INFINITY || mrun1 == -INFINITY);
+    };
+    const size_t pbase = (size_t)chunk * a.n_qh;
+
+    // Phase p (one barrier): the score waves score tile p (ring stage p % NST)
+    // and write its weights into buffer p & 1; the context waves accumulate
+    // tile p-1 from the previous buffer.  Both vote on tile p-1 first.  One
+    // extra phase finishes the last tile.
+    if (w < NW / 2) {
+        // ======== score waves: rows 32 rh .. +32 (row quarters 2 rh, 2 rh + 1),
+        // heads 16 hh .. +16
+        const int rh = w >> 1;
+        v8i qv[NSL];
+#pragma unroll
+        for (int sl = 0; sl < NSL; ++sl)
+            qv[sl] = *reinterpret_cast<const v8i*>(
+                lds + L::QT + ((hh * NSL + sl) * 64 + lane) * 32);
+        // mixed rows: the RoPE query terms (bf16), two per K step
+        bf16x8 qr[MXL ? QM::NRS : 1];
+        if constexpr (MXL) {
+#pragma unroll
+            for (int sl = 0; sl < QM::NRS; ++sl)
+                qr[sl] = *reinterpret_cast<const bf16x8*>(
+                    lds + L::QT + QM::RBASE + ((hh * QM::NRS + sl) * 64 + lane) * 16);
+        }
+        // E8M0 operand scales 2^(-k - 4t) of this lane's head.  The
+        // instruction takes the scale of 32-element K block kb from lane group
+        // kb, and lane group g's bytes 0-15 / 16-31 fall in blocks g / 2 and 2
+        // + g / 2.  The packed half block carries t1 in lane groups 0-1
+        // (blocks 0 and 2) and t2 in lane groups 2-3 (blocks 1 and 3): even
+        // lane groups give t1's scale, odd ones t2's.
+        const int kq = s_k[16 * hh + n];
+        const int sbt0 = 127 - kq, sbt1 = sbt0 - kTermShift, sbt2 = sbt0 - 2 * kTermShift;
+        const int sb_pack = (g & 1) ? sbt1 : sbt0;
+        // mixed rows: the fourth term's scale, and the packed t3 | t4 slot's
+        const int sbt3 = sbt0 - 3 * kTermShift;
+        const int sb_pack2 = (g & 1) ? sbt3 : sbt2;
+        const int qh_own = qh0 + 16 * hh + n;
+        const int32_t tlim = (a.mode == kCausal)
+                                 ? a.pos0 + (qh_own < a.n_qh ? qh_own / a.n_heads : 0) + 1
+                                 : 0x7FFFFFFF;
+        lds_barrier();  // staging area free for the ring
+
+        float zacc = 0.0f;   // z partial over this lane's rows, head 16 hh + n
+        float zsave = 0.0f;  // zacc before the last scored tile
+        float u[8], scv[8];  // scores / row scales of the last scored tile, [quarter][v]
+        // weights of rows 32 rh + 16 r + 4 g + v, head 16 hh + n
+        _Float16* const s_w_own = s_w + (16 * hh + n) * WSS + 32 * rh + 4 * g;
+
+        // Weights of this lane's rows (linear form) into buffer buf; chk[r]
+        // receives this lane's sum of p + w in row quarter 2 rh + r.
+        auto weights_linear = [&](int buf, float (&chk)[2]) __attribute__((always_inline)) {
+            const float mu = hh ? mrun1 : mrun0;
+            const float mz = (mu == -INFINITY) ? 0.0f : mu;
+            float ps = 0.0f;
+#pragma unroll
+            for (int r = 0; r < 2; ++r) {
+                f16x4 wv;
+                chk[r] = 0.0f;
 #pragma unroll
                 for (int v = 0; v < 4; ++v) {
-                    const int r = 16 * rq + 4 * g + v;
-                    bool valid;
-                    if constexpr (GATHER) {
-                        valid = s_row[st * TR + r] >= 0;
-                    } else {
-                        valid = p0 + r < c1 && p0 + r < tlim;
+                    const float pv = fast_exp2(u[4 * r + v] - mz);
+                    const float wt = pv * (scv[4 * r + v] * fown);
+                    ps += pv;
+                    chk[r] += pv + wt;
+                    wv[v] = (_Float16)wt;
+                }
+                *reinterpret_cast<f16x4*>(s_w_own + buf * HG * WSS + 16 * r) = wv;
+            }
+            zacc = zsave + ps;
+        };
+        // Same in the log domain (exact for any scale), used after a state move.
+        auto weights_log = [&](int buf) __attribute__((always_inline)) {
+            const float mu = hh ? mrun1 : mrun0;
+            const float dd = hh ? drun1 : drun0;
+            const float mz = (mu == -INFINITY) ? 0.0f : mu;
+            const float dn = (dd == -INFINITY) ? 0.0f : dd;
+            float ps = 0.0f;
+#pragma unroll
+            for (int r = 0; r < 2; ++r) {
+                f16x4 wv;
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    const float av = u[4 * r + v] - mz;
+                    ps += fast_exp2(av);
+                    wv[v] = (_Float16)fast_exp2((av + log2f(scv[4 * r + v])) - dn);
+                }
+                *reinterpret_cast<f16x4*>(s_w_own + buf * HG * WSS + 16 * r) = wv;
+            }
+            zacc = zsave + ps;
+        };
+
+        // Scores of tile p (stage st): S^T[16 rows][16 heads] per row quarter
+        // in log2 units of the codes; two accumulators per quarter, and the
+        // two quarters' MFMAs alternate, so consecutive MFMAs never wait on
+        // each other.  Score operand: lane (n, g) of block j, half h reads
+        // slot n + 16 g of group (j, h) of its row quarter; in a trailing half
+        // block lanes g >= 2 re-read the slots of g - 2, whose query elements
+        // carry the packed second term.
+        const int qa = 2 * rh * RQB + 16 * lane;
+        const int qa_half = 2 * rh * RQB + NFULL * 2048 + 16 * (lane & 31);
+        // Mixed rows: the noPE half block is the first half of LDS block 3 (a
+        // full 1-KB group pair); RoPE K step m reads 16-byte chunk 28 + 4m + g
+        // of row 16 rq + n, in LDS block 3 (m = 0, lane groups 2-3) or in the
+        // trailing half block 4 (m = 1, lane groups 0-1).
+        const int qa_mxh = 2 * rh * RQB + 3 * 2048 + 16 * (lane & 31);
+        const int ro0 = 2 * rh * RQB + 3 * 2048 + (g & 1) * 1024 + 16 * (n + 16 * (2 + (g >> 1)));
+        const int ro1 = 2 * rh * RQB + 4 * 2048 + (g & 1) * 512 + 16 * (n + 16 * (g >> 1));
+        f32x4 acc0[2], acc1[2], accr[2];
+        auto scores = [&](int st) __attribute__((always_inline)) {
+            const uint8_t* xst = lds + st * L::STAGE;
+#pragma unroll
+            for (int r = 0; r < 2; ++r) {
+                acc0[r] = f32x4{0.f, 0.f, 0.f, 0.f};
+                acc1[r] = acc0[r];
+                accr[r] = acc0[r];
+            }
+            if constexpr (MXL) {
+#pragma unroll
+                for (int j = 0; j <= QM::NFULL; ++j) {
+                    v8i xv[2];
+#pragma unroll
+                    for (int r = 0; r < 2; ++r) {
+                        const uint8_t* xp =
+                            ((j < QM::NFULL) ? xst + qa + 2048 * j : xst + qa_mxh) + r * RQB;
+                        const uint4 x0 = *reinterpret_cast<const uint4*>(xp);
+                        const uint4 x1 = *reinterpret_cast<const uint4*>(xp + 1024);
+                        xv[r] = v8i{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w,
+                                    (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
                     }
-                    u[v] = valid ? u[v] : -INFINITY;
+                    if (j < QM::NFULL) {
+#pragma unroll
+                        for (int r = 0; r < 2; ++r)
+                            acc0[r] = mfma_fp8_scaled(xv[r], qv[4 * j], acc0[r], sbt0);
+#pragma unroll
+                        for (int r = 0; r < 2; ++r)
+                            acc1[r] = mfma_fp8_scaled(xv[r], qv[4 * j + 1], acc1[r], sbt1);
+#pragma unroll
+                        for (int r = 0; r < 2; ++r)
+                            acc0[r] = mfma_fp8_scaled(xv[r], qv[4 * j + 2], acc0[r], sbt2);
+#pragma unroll
+                        for (int r = 0; r < 2; ++r)
+                            acc1[r] = mfma_fp8_scaled(xv[r], qv[4 * j + 3], acc1[r], sbt3);
+                    } else {
+#pragma unroll
+                        for (int r = 0; r < 2; ++r)
+                            acc1[r] = mfma_fp8_scaled(xv[r], qv[4 * j], acc1[r], sb_pack);
+#pragma unroll
+                        for (int r = 0; r < 2; ++r)
+                            acc0[r] = mfma_fp8_scaled(xv[r], qv[4 * j + 1], acc0[r], sb_pack2);
+                    }
+                }
+#pragma unroll
+                for (int m = 0; m < QM::NRS / 2; ++m) {
+#pragma unroll
+                    for (int r = 0; r < 2; ++r) {
+                        const bf16x8 xr =
+                            *reinterpret_cast<const bf16x8*>(xst + (m ? ro1 : ro0) + r * RQB);
+                        accr[r] = mfma_bf16(xr, qr[2 * m], accr[r]);
+                        accr[r] = mfma_bf16(xr, qr[2 * m + 1], accr[r]);
+                    }
+                }
+                return;
+            }
+#pragma unroll
+            for (int j = 0; j < NB; ++j) {
+                const int hoff = (j < NFULL) ? 1024 : 512;
+                v8i xv[2];
+#pragma unroll
+                for (int r = 0; r < 2; ++r) {
+                    const uint8_t* xp = ((j < NFULL) ? xst + qa + 2048 * j : xst + qa_half) + r * RQB;
+                    const uint4 x0 = *reinterpret_cast<const uint4*>(xp);
+                    const uint4 x1 = *reinterpret_cast<const uint4*>(xp + hoff);
+                    xv[r] = v8i{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w,
+                                (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
+                }
+                if (j < Q::NFULL) {
+#pragma unroll
+                    for (int r = 0; r < 2; ++r)
+                        acc0[r] = mfma_fp8_scaled(xv[r], qv[3 * j], acc0[r], sbt0);
+#pragma unroll
+                    for (int r = 0; r < 2; ++r)
+                        acc1[r] = mfma_fp8_scaled(xv[r], qv[3 * j + 1], acc1[r], sbt1);
+#pragma unroll
+                    for (int r = 0; r < 2; ++r)
+                        acc0[r] = mfma_fp8_scaled(xv[r], qv[3 * j + 2], acc0[r], sbt2);
+                } else {
+#pragma unroll
+                    for (int r = 0; r < 2; ++r)
+                        acc1[r] = mfma_fp8_scaled(xv[r], qv[3 * j], acc1[r], sb_pack);
+#pragma unroll
+                    for (int r = 0; r < 2; ++r)
+                        acc0[r] = mfma_fp8_scaled(xv[r], qv[3 * j + 1], acc0[r], sbt2);
                 }
             }
         };
-        const bool full = !GATHER && a.mode != kCausal && p0 + TR <= c1;
-        const bool ctx = p >= 1 && pv_active;
-        float chk = 0.0f;
-        if (ctx && scored && full && !ctx_half) {
-            // Common case, one block: the context MFMAs go into the pipe
-            // behind the score MFMAs, then the weight arithmetic (which waits
-            // on the scores) runs while they drain.
-            context(stp, bufp, std::false_type{});
-            scores_to_u(false);
-            chk = weights_linear(buf);
-        } else {
-            if (ctx) {
-                if (!ctx_half)
-                    context(stp, bufp, std::false_type{});
-                else
-                    context(stp, bufp, std::true_type{});
+        // Log2-domain scores u of tile p (rows 32 rh + 16 r + 4 g + v, head
+        // 16 hh + n) from the accumulators; masking: rows past the list,
+        // invalid gathered rows, causal limit.
+        auto scores_to_u = [&](const float4 (&scl)[2], int st, int p0, bool mask)
+                               __attribute__((always_inline)) {
+            zsave = zacc;
+#pragma unroll
+            for (int r = 0; r < 2; ++r) {
+                const float4 sc4 = scl[r];
+                scv[4 * r + 0] = sc4.x;
+                scv[4 * r + 1] = sc4.y;
+                scv[4 * r + 2] = sc4.z;
+                scv[4 * r + 3] = sc4.w;
+#pragma unroll
+                for (int v = 0; v < 4; ++v)
+                    u[4 * r + v] = MXL ? (acc0[r][v] + acc1[r][v]) * scv[4 * r + v] + accr[r][v]
+                                       : (acc0[r][v] + acc1[r][v]) * scv[4 * r + v];
             }
-            if (scored) {
-                scores_to_u(!full);
-                chk = weights_linear(buf);
+            if (mask) {
+#pragma unroll
+                for (int r = 0; r < 2; ++r)
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) {
+                        const int row = 32 * rh + 16 * r + 4 * g + v;
+                        bool valid;
+                        if constexpr (GATHER) {
+                            valid = s_row[st * TR + row] >= 0;
+                        } else {
+                            valid = p0 + row < c1 && p0 + row < tlim;
+                        }
+                        u[4 * r + v] = valid ? u[4 * r + v] : -INFINITY;
+                    }
             }
-        }
-        if (more)
-            issue(p + DIST, sti, ICB{}, ICK{});
-        if (p == ntiles)
-            break;
-        // sum of p + w over the wave's 16 rows (lane groups g)
-        {
-            const auto r1 = __builtin_amdgcn_permlane16_swap(__float_as_uint(chk),
-                                                             __float_as_uint(chk), false, false);
-            chk = __uint_as_float(r1[0]) + __uint_as_float(r1[1]);
-            const auto r2 = __builtin_amdgcn_permlane32_swap(__float_as_uint(chk),
-                                                             __float_as_uint(chk), false, false);
-            chk = __uint_as_float(r2[0]) + __uint_as_float(r2[1]);
-        }
-        if (g == 0)
-            s_mx[(buf * HG + 16 * hh + n) * 4 + rq] = chk;
-    }
+        };
 
-    // ---- epilogue: z over lane groups and row quarters; partial (m, z, cl)
-    {
+        for (int p = 0, st = 0; p <= ntiles; ++p, st = (st == NST - 1) ? 0 : st + 1) {
+            const int buf = p & 1, bufp = buf ^ 1;
+            lds_barrier();  // (A) tile p visible; weights and sums of tile p-1
+                            //     complete; stage (p + DIST) % NST (tile p + DIST
+                            //     - NST) and buffer p & 1 free
+            // the sums of tile p-1 and the scales of tile p are read ahead of
+            // the score operands, so they do not queue behind them
+            float4 S4[2];
+            if (p >= 1)
+                vote_read(bufp, S4);
+            const bool scored = p < ntiles;
+            float4 scl[2];
+            if (scored) {
+#pragma unroll
+                for (int r = 0; r < 2; ++r)
+                    scl[r] = *reinterpret_cast<const float4*>(s_sc + st * TR + 32 * rh + 16 * r + 4 * g);
+                scores(st);
+            }
+            if (p >= 1 && vote(S4)) {
+                // Keep this path's arithmetic inside the branch: the empty asm
+                // makes u and the scales opaque here, so none of it is hoisted
+                // into the common path.
+                asm volatile("" : "+v"(u[0]), "+v"(u[1]), "+v"(u[2]), "+v"(u[3]), "+v"(u[4]),
+                             "+v"(u[5]), "+v"(u[6]), "+v"(u[7]), "+v"(scv[0]), "+v"(scv[1]),
+                             "+v"(scv[2]), "+v"(scv[3]), "+v"(scv[4]), "+v"(scv[5]),
+                             "+v"(scv[6]), "+v"(scv[7]));
+                // exact maxima of tile p-1 per row quarter: T = max u, C =
+                // max (u - T) + log2 scale, relative so that a large |u| never
+                // swallows log2 scale
+#pragma unroll
+                for (int r = 0; r < 2; ++r) {
+                    float tw = fmaxf(fmaxf(u[4 * r], u[4 * r + 1]), fmaxf(u[4 * r + 2], u[4 * r + 3]));
+                    tw = max_xor32(max_xor16(tw));
+                    float cw = -INFINITY;
+                    if (tw != -INFINITY) {
+#pragma unroll
+                        for (int v = 0; v < 4; ++v)
+                            cw = fmaxf(cw, (u[4 * r + v] - tw) + log2f(scv[4 * r + v]));
+                    }
+                    cw = max_xor32(max_xor16(cw));
+                    if (g == 0)
+                        s_cr2[(16 * hh + n) * 4 + 2 * rh + r] = make_float2(tw, cw);
+                }
+                lds_barrier();  // (R1)
+                float alz[2], alo[2];
+                state_move(alz, alo);
+                zsave *= hh ? alz[1] : alz[0];
+                weights_log(bufp);  // tile p-1 under the new state
+                lds_barrier();      // (R2) rewritten weights visible; s_cr free
+            }
+            float chk[2] = {0.0f, 0.0f};
+            if (scored) {
+                const int p0 = c0 + p * TR;
+                const bool full = !GATHER && a.mode != kCausal && p0 + TR <= c1;
+                scores_to_u(scl, st, p0, !full);
+                weights_linear(buf, chk);
+            }
+            if (p == ntiles)
+                break;
+            // sums of p + w over the 16 rows of each row quarter (lane groups g)
+#pragma unroll
+            for (int r = 0; r < 2; ++r) {
+                float cs = chk[r];
+                const auto r1 = __builtin_amdgcn_permlane16_swap(__float_as_uint(cs),
+                                                                 __float_as_uint(cs), false, false);
+                cs = __uint_as_float(r1[0]) + __uint_as_float(r1[1]);
+                const auto r2 = __builtin_amdgcn_permlane32_swap(__float_as_uint(cs),
+                                                                 __float_as_uint(cs), false, false);
+                cs = __uint_as_float(r2[0]) + __uint_as_float(r2[1]);
+                if (g == 0)
+                    s_mx[(buf * HG + 16 * hh + n) * 4 + 2 * rh + r] = cs;
+            }
+        }
+        // z over lane groups
         float zz = zacc;
         zz += __shfl_xor(zz, 16);
         zz += __shfl_xor(zz, 32);
         if (g == 0)
-            s_z[rq * HG + 16 * hh + n] = zz;
-    }
-    __syncthreads();
-    const size_t pbase = (size_t)chunk * a.n_qh;
-    if (rq == 0 && g == 0) {
-        const int h = 16 * hh + n, qh = qh0 + h;
-        if (qh < a.n_qh) {
-            a.ws_m[pbase + qh] = hh ? mrun1 : mrun0;
-            a.ws_z[pbase + qh] = (s_z[h] + s_z[HG + h]) + (s_z[2 * HG + h] + s_z[3 * HG + h]);
+            s_z[rh * HG + 16 * hh + n] = zz;
+    } else {
+        // ======== context waves: O[32 heads][128 columns 128 c ..] += W . X of
+        // tile p-1.  Column tile jm (16 columns) is chunk 8 c + jm: LDS block
+        // c, lane group jm / 2, half jm % 2.  MFMA (ht, jm) covers heads
+        // 16 ht .. +16.
+        const int c = w - NW / 2;
+        const int nct = min(8, max(0, (a.lc >> 4) - 8 * c));  // 16-column tiles of this wave
+        const bool ctx_half = c >= NFULL;  // the wave's block is a trailing half block
+        // Context operand: source lane 2k + h' of 16-lane group g' addresses
+        // row 8 g' + k (row quarter g' / 2, slot n = 8 (g' & 1) + k), bytes
+        // 8 h' .. of the column chunk; the transposed read hands lane (n, g')
+        // column n of rows 8 g' .. 8 g' + 7.
+        const int trl = (g >> 1) * RQB + 16 * (8 * (g & 1) + ((lane & 15) >> 1)) + 8 * (lane & 1);
+        const int trw = ctx_half ? NFULL * 2048 : c * 2048;
+        lds_barrier();  // staging area free for the ring
+        if (fresh_late)
+            quantize_fresh(wi, NWI);
+        f32x4 O[2][8];
+#pragma unroll
+        for (int ht = 0; ht < 2; ++ht)
+#pragma unroll
+            for (int jm = 0; jm < 8; ++jm)
+                O[ht][jm] = f32x4{0.f, 0.f, 0.f, 0.f};
+        // Operands of one tile: the weights (A, heads x rows) and the row
+        // bytes read transposed (B, rows x columns).  The reads of tile p-1
+        // go out together with the vote on it; only a state move (which
+        // rewrites the tile's weights) makes the weights be read again.
+        constexpr int KS = TR / 32;
+        f16x8 wa[KS][2];
+        v2i xb[KS][8];
+        auto read_weights = [&](int buf) __attribute__((always_inline)) {
+            const _Float16* sw = s_w + buf * HG * WSS;
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+                for (int ht = 0; ht < 2; ++ht)
+                    wa[ks][ht] =
+                        *reinterpret_cast<const f16x8*>(&sw[(16 * ht + n) * WSS + 32 * ks + 8 * g]);
+        };
+        auto read_rows = [&](int st, auto GUARD_, auto HALF_) __attribute__((always_inline)) {
+            constexpr bool GUARD = decltype(GUARD_)::value, HALFC = decltype(HALF_)::value;
+            const uint8_t* xst = lds + st * L::STAGE + trw + trl;
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+                for (int jm = 0; jm < 8; ++jm) {
+                    if (GUARD && jm >= nct)
+                        break;
+                    const int off = 2 * ks * RQB + (jm & 1) * (HALFC ? 512 : 1024) + (jm >> 1) * 256;
+                    xb[ks][jm] = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+                        (MLA8_LDS v2i*)(MLA8_LDS uint8_t*)(xst + off));
+                }
+        };
+        auto accumulate = [&](auto GUARD_) __attribute__((always_inline)) {
+            constexpr bool GUARD = decltype(GUARD_)::value;
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+                for (int jm = 0; jm < 8; ++jm) {
+                    if (GUARD && jm >= nct)
+                        break;
+                    const f16x8 bx = cvt8((uint32_t)xb[ks][jm][0], (uint32_t)xb[ks][jm][1]);
+                    O[0][jm] = mfma16(wa[ks][0], bx, O[0][jm]);
+                    O[1][jm] = mfma16(wa[ks][1], bx, O[1][jm]);
+                }
+        };
+
+        for (int p = 0, st = 0, stp = NST - 1; p <= ntiles;
+             ++p, stp = st, st = (st == NST - 1) ? 0 : st + 1) {
+            // st = p % NST, stp = (p - 1) % NST
+            const int bufp = (p & 1) ^ 1;
+            if (p < ntiles)
+                wait_tile(p + 1 < ntiles);
+            lds_barrier();  // (A)
+            const bool more = p + DIST < ntiles;
+            const int sti = (st + DIST) % NST;
+            const bool ctx = p >= 1 && nct > 0;
+            float4 S4[2];
+            if (p >= 1)
+                vote_read(bufp, S4);
+            if (ctx) {
+                read_weights(bufp);
+                if (ctx_half)
+                    read_rows(stp, std::true_type{}, std::true_type{});
+                else if (nct < 8)
+                    read_rows(stp, std::true_type{}, std::false_type{});
+                else
+                    read_rows(stp, std::false_type{}, std::false_type{});
+            }
+            if (more)
+                issue(p + DIST, sti, IC0{}, ICA{});
+            if (p >= 1 && vote(S4)) {
+                lds_barrier();  // (R1) the score waves' tile maxima are in s_cr
+                float alz[2], alo[2];
+                state_move(alz, alo);
+                // O holds tiles < p-1 in units of the old state; its heads
+                // 16*ht + 4*g + v take their factors from lanes 4*g + v.
+#pragma unroll
+                for (int ht = 0; ht < 2; ++ht)
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) {
+                        const float f = __shfl(alo[ht], 4 * g + v);
+#pragma unroll
+                        for (int jm = 0; jm < 8; ++jm)
+                            O[ht][jm][v] *= f;
+                    }
+                lds_barrier();  // (R2) the rewritten weights of tile p-1 are visible
+                if (ctx)
+                    read_weights(bufp);
+            }
+            if (more)
+                issue(p + DIST, sti, ICA{}, ICB{});
+            if (ctx) {
+                if (nct < 8)
+                    accumulate(std::true_type{});
+                else
+                    accumulate(std::false_type{});
+            }
+            if (more)
+                issue(p + DIST, sti, ICB{}, ICK{});
+            if (p == ntiles)
+                break;
         }
-    }
-    if (pv_active) {
+        // partial cl = sum_t p_t scale_t x_t = 2^d * O
+        if (nct > 0) {
 #pragma unroll
-        for (int ht = 0; ht < 2; ++ht) {
-            // cl = sum_t p_t scale_t x_t = 2^d * O
-            const float mh = ht ? mrun1 : mrun0, dh = ht ? drun1 : drun0;
-            const float fo = (mh == -INFINITY || dh == -INFINITY) ? 0.0f : fast_exp2(dh);
+            for (int ht = 0; ht < 2; ++ht) {
+                const float mh = ht ? mrun1 : mrun0, dh = ht ? drun1 : drun0;
+                const float fo = (mh == -INFINITY || dh == -INFINITY) ? 0.0f : fast_exp2(dh);
 #pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                const float f = __shfl(fo, 4 * g + v);
-                const int qh = qh0 + 16 * ht + 4 * g + v;
-                if (qh < a.n_qh) {
-                    float* dst = a.ws_cl + (pbase + qh) * a.lc;
+                for (int v = 0; v < 4; ++v) {
+                    const float f = __shfl(fo, 4 * g + v);
+                    const int qh = qh0 + 16 * ht + 4 * g + v;
+                    if (qh < a.n_qh) {
+                        float* dst = a.ws_cl + (pbase + qh) * a.lc + 128 * c + n;
 #pragma unroll
-                    for (int jm = 0; jm < 4; ++jm) {
-                        const int col = cb + 16 * jm + n;
-                        if (col < a.lc)
-                            dst[col] = O[ht][jm][v] * f;
+                        for (int jm = 0; jm < 8; ++jm)
+                            if (jm < nct)
+                                dst[16 * jm] = O[ht][jm][v] * f;
                     }
                 }
             }
+        }
+    }
+
+    // ---- partial m and z (z summed over the two row halves)
+    __syncthreads();
+    if (w < 2 && g == 0) {
+        const int h = 16 * hh + n, qh = qh0 + h;
+        if (qh < a.n_qh) {
+            a.ws_m[pbase + qh] = hh ? mrun1 : mrun0;
+            a.ws_z[pbase + qh] = s_z[h] + s_z[HG + h];
         }
     }
 }
