@@ -270,7 +270,7 @@ MLA8_API int mla8_profile_events(void* before, void* after);
  * the enqueue-only rule); they are not for the decode loop's critical path.
  *
  * Format (little-endian): two 64-byte header slots, then the body from byte
- * 128, token-major.  Slot: "MLA8KV  ", u32 version (1 = f32 rows, 2 = e4m3
+ * 128, token-major.  Slot: "MLA8KV\0\0", u32 version (1 = f32 rows, 2 = e4m3
  * rows + f32 scale), u32 n_layers, u32 lc, u32 rc, u64 n_tokens (committed),
  * u64 seq, u32 FNV-1a of the 40 bytes before it, zero padding.  The valid
  * slot with the larger seq is the committed state.  Version-2 token t, at
