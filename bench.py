@@ -38,6 +38,18 @@ HBM_PEAK_GBS = 8000.0
 SETTLE_S = 0.25  # untimed replays before the warm-up steps (GPU clock ramp)
 
 
+
+def kernel_code_sha256(path: str) -> str:
+    """SHA-256 of a kernel source's code: comments removed and whitespace runs
+    collapsed, so that an edit to comments alone does not count as a change of
+    the kernel the traffic counters were taken on."""
+    import hashlib
+    import re
+    s = open(path).read()
+    s = re.sub(r"/\*.*?\*/", "", s, flags=re.S)
+    s = re.sub(r"//[^\n]*", "", s)
+    return hashlib.sha256(" ".join(s.split()).encode()).hexdigest()
+
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
@@ -635,14 +647,12 @@ def main():
     achieved = alg_bytes / (part_us * 1e-6) / 1e9
     traffic = None
     if args.traffic and os.path.exists(args.traffic):
-        import hashlib
         rec = json.load(open(args.traffic))
         src = os.path.join(ROOT, "fp8_mla_latent_amd", "csrc", "mla8_kernels.hip")
-        sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
-        if rec.get("kernel_source_sha256") == sha:
+        if rec.get("kernel_code_sha256") == kernel_code_sha256(src):
             traffic = rec.get("bytes_per_launch")
         else:
-            log("traffic counters were taken on another kernel source: reporting null")
+            log("traffic counters were taken on other kernel code: reporting null")
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                 "kernel": "k_split_partial<9,false>", "kernel_us": round(part_us, 3),

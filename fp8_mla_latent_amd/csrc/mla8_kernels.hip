@@ -261,9 +261,10 @@ __device__ __forceinline__ void build_query_terms(const AttnArgs& a, int t,
 // 16 significant bits: with three, ties between outlier rows put some heads at
 // the tolerance), its last 64 elements forming the packed half block of K
 // block 3 (a full 128-byte LDS block whose second half holds RoPE bytes):
-// t1 | t2 and t3 | t4, as many MFMAs as the all-e4m3 row's three terms.  The RoPE part is scored on the bf16 MFMA:
-// e_rope = q_rope * sm * log2(e) splits into two bf16 terms hi + lo (about 16
-// significant bits), unscaled by the row scale, in two K steps of 32.
+// t1 | t2 and t3 | t4, as many MFMAs as the all-e4m3 row's three terms.  The
+// RoPE part is scored on the bf16 MFMA: e_rope = q_rope * sm * log2(e) splits
+// into two bf16 terms hi + lo (about 16 significant bits), unscaled by the row
+// scale, in two K steps of 32.
 // Staging after both head halves' e4m3 slots: qr[hh][slot 2m + term][lane][16
 // bytes], lane n + 16 g holding head 16 hh + n, RoPE elements 32 m + 8 g ..
 // 32 m + 8 g + 7 (the row operand reads the same elements: 16-byte chunk
@@ -579,12 +580,14 @@ __global__ __launch_bounds__(kThreads, 1) void k_split_partial(AttnArgs a)
     // ---- tile issue.  The context waves (w >= NWI) issue every direct load:
     // KW row DMAs per tile each and the first of them one more for the row
     // scales, so a fixed per-wave vmcnt marks a tile complete.  The score
-    // waves, which carry the longer dependency chain, issue none.  Row DMA instruction k fills stage slots [64k, 64k + 64)
-    // (16 bytes each, layout above).  Slots past the row's data (zero-pad
-    // columns) and rows outside the list load chunk 0 / the tile's first row
-    // instead: finite bytes that are multiplied by a zero query element, masked
-    // out of the softmax, or never read.  Spare instruction slots (k >= NINS)
-    // repeat instruction k % NINS (the same bytes to the same place).
+    // waves issue none (their phase is the longer one; sharing the loads
+    // between both roles measured slower).  Row DMA instruction k fills stage
+    // slots [64k, 64k + 64) (16 bytes each, layout above).  Slots past the
+    // row's data (zero-pad columns) and rows outside the list load chunk 0 /
+    // the tile's first row instead: finite bytes that are multiplied by a zero
+    // query element, masked out of the softmax, or never read.  Spare
+    // instruction slots (k >= NINS) repeat instruction k % NINS (the same
+    // bytes to the same place).
     const int cpr = a.d >> 4;  // 16-byte data chunks per row
     const int wi = (w >= NWI) ? w - NWI : 0;  // issuer index
     const bool dma_lead = w == NWI;           // issues the scale loads too
