@@ -141,7 +141,7 @@ size_t r256(size_t b) { return (b + 255) & ~size_t(255); }
 size_t index_ws_bytes(int64_t t)
 {
     return r256((size_t)t * 4) + r256((size_t)t * 8) + r256(kIndexHistCopies * kIndexHistBins * 4) +
-           r256((size_t)((t + 4095) / 4096) * 4);
+           r256((size_t)((t + 4095) / 4096) * 4) + r256(kIndexHistCopies * 64);
 }
 
 }  // namespace
@@ -413,6 +413,8 @@ int mla8_index_topk(const uint8_t* k_codes, const float* k_scales, int64_t t_row
     a.hist = reinterpret_cast<uint32_t*>(ws);
     ws += r256(kIndexHistCopies * kIndexHistBins * 4);
     a.wg_cnt = reinterpret_cast<uint32_t*>(ws);
+    ws += r256((size_t)((t_rows + 4095) / 4096) * 4);
+    a.top = reinterpret_cast<uint32_t*>(ws);
     return launch_index_topk(a, static_cast<hipStream_t>(stream), g_ev_before, g_ev_after) ==
                    hipSuccess
                ? MLA8_OK

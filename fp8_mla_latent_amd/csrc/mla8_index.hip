@@ -23,9 +23,11 @@
 //     keys; a per-workgroup LDS histogram of the keys' top 12 bits is added
 //     to a global one.
 //     The histogram has one copy per XCD (workgroups are dispatched
-//     round-robin over the 8 XCDs), so fewer workgroups add to each bin.
+//     round-robin over the 8 XCDs), so fewer workgroups add to each bin; the
+//     largest key goes by atomic max to one word per copy likewise.
 //   * k_index_cand: the first radix digit b1 of the k-th largest key comes
-//     from the summed histogram; every workgroup compacts the keys of its
+//     from the summed histogram, read in windows from the largest key's bin
+//     down until k keys are counted; every workgroup compacts the keys of its
 //     4096-row slice whose digit is >= b1 into the slice's part of a
 //     candidate buffer, in row order, as (key << 32 | row).
 //   * k_index_final (one workgroup): the candidates, packed in row order into
@@ -50,6 +52,7 @@ constexpr int kSelectKeysPerThread = 8;  // contiguous rows per thread
 constexpr int kSelectSlice = kSelectThreads * kSelectKeysPerThread;
 constexpr int kRadixBits = 11;
 constexpr int kLdsCand = 12288;          // candidates resolved in LDS (96 KB)
+static_assert(kLdsCand < (1 << 16), "packed 16-bit counts in the ordered output");
 static_assert(kIndexMaxRows / kSelectSlice <= kIndexHistBins, "per-slice tables fit in LDS");
 
 __device__ __forceinline__ f32x4 mfma_fp8(v8i a, v8i b, f32x4 c)
@@ -70,12 +73,15 @@ __device__ __forceinline__ uint32_t order_key(float s)
 
 }  // namespace
 
-// One workgroup per histogram copy.
-__global__ __launch_bounds__(kThreads) void k_index_clear(uint32_t* __restrict__ hist)
+// One workgroup per histogram copy and largest-key word.
+__global__ __launch_bounds__(kThreads) void k_index_clear(uint32_t* __restrict__ hist,
+                                                          uint32_t* __restrict__ top)
 {
     uint32_t* h = hist + (size_t)blockIdx.x * kIndexHistBins;
     for (int i = threadIdx.x; i < kIndexHistBins; i += blockDim.x)
         h[i] = 0u;
+    if (threadIdx.x == 0)
+        top[16 * blockIdx.x] = 0u;
 }
 
 // ---------------------------------------------------------------------------
@@ -87,6 +93,7 @@ __global__ __launch_bounds__(kScoreThreads) void k_index_score(IndexArgs a)
     __shared__ float s_qs[kIndexMaxHeads];
     __shared__ float s_w[kIndexMaxHeads];
     __shared__ uint32_t s_hist[kIndexHistBins];
+    __shared__ uint32_t s_top;
 
     const int tid = threadIdx.x;
     const int w = tid >> 6, lane = tid & 63, n = lane & 15, g = lane >> 4;
@@ -124,6 +131,8 @@ __global__ __launch_bounds__(kScoreThreads) void k_index_score(IndexArgs a)
 
     for (int i = tid; i < kIndexHistBins; i += kScoreThreads)
         s_hist[i] = 0u;
+    if (tid == 0)
+        s_top = 0u;
     if (tid < 16 * NT)
         s_w[tid] = a.w[tid];
 
@@ -175,6 +184,7 @@ __global__ __launch_bounds__(kScoreThreads) void k_index_score(IndexArgs a)
     }
 
     // ---- scores: lane (n, g) gets heads 16 ht + 4g + v of key row n
+    uint32_t kmax = 0u;  // largest key this lane wrote
 #pragma unroll
     for (int j = 0; j < kScoreBlocksPerWave; ++j) {
         const v8i kb = v8i{(int)k0[j].x, (int)k0[j].y, (int)k0[j].z, (int)k0[j].w,
@@ -195,9 +205,17 @@ __global__ __launch_bounds__(kScoreThreads) void k_index_score(IndexArgs a)
             if (a.scores)
                 a.scores[rows[j]] = r;
             atomicAdd(&s_hist[key >> 20], 1u);
+            kmax = max(kmax, key);
         }
     }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1)
+        kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, o));
+    if (lane == 0)
+        atomicMax(&s_top, kmax);
     __syncthreads();
+    if (tid == 0)
+        atomicMax(&a.top[16 * (blockIdx.x % kIndexHistCopies)], s_top);
     // into the histogram copy of this workgroup's XCD (dispatch is
     // round-robin over the 8 XCDs)
     uint32_t* const hist = a.hist + (size_t)(blockIdx.x % kIndexHistCopies) * kIndexHistBins;
@@ -320,7 +338,6 @@ __device__ __forceinline__ uint64_t radix_select(Get get, uint32_t n, int bits, 
 // order as (key << 32 | row), their count to wg_cnt[i].
 __global__ __launch_bounds__(kSelectThreads) void k_index_cand(IndexArgs a)
 {
-    __shared__ uint32_t s_h[kIndexHistBins];
     __shared__ uint32_t s_tmp[kSelectThreads / 64];
     __shared__ uint32_t s_out[2];
 
@@ -338,17 +355,40 @@ __global__ __launch_bounds__(kSelectThreads) void k_index_cand(IndexArgs a)
         for (int j = 0; j < kSelectKeysPerThread; ++j)
             key[j] = (tb + j < a.t_rows) ? a.keys[tb + j] : 0u;
     }
-    // the histogram: the sum of the copies
-    for (int i = tid; i < kIndexHistBins; i += kSelectThreads) {
-        uint32_t c = 0;
+    // the bin b1 of the k-th largest key: windows of kSelectThreads bins of
+    // the summed histogram copies, from the bin of the largest key down,
+    // until the keys counted reach k (every key is counted, and k < t_rows,
+    // so the search ends by bin 0)
+    const uint32_t k = (uint32_t)a.top_k;
+    uint32_t above = 0;  // keys in the bins above the window
+    uint32_t tmax = 0u;
 #pragma unroll
-        for (int r = 0; r < kIndexHistCopies; ++r)
-            c += a.hist[(size_t)r * kIndexHistBins + i];
-        s_h[i] = c;
+    for (int r = 0; r < kIndexHistCopies; ++r)
+        tmax = max(tmax, a.top[16 * r]);
+    for (int wtop = (int)(tmax >> 20);; wtop -= kSelectThreads) {
+        const int b = wtop - tid;
+        uint32_t c = 0;
+        if (b >= 0) {
+#pragma unroll
+            for (int r = 0; r < kIndexHistCopies; ++r)
+                c += a.hist[(size_t)r * kIndexHistBins + b];
+        }
+        uint32_t tot;
+        const uint32_t ex = block_excl_scan(c, s_tmp, &tot);  // keys in bins b+1 .. wtop
+        if (above + ex < k && k <= above + ex + c) {
+            s_out[0] = (uint32_t)b;
+            s_out[1] = above + ex;  // keys in the bins above b
+        }
+        if (above + tot >= k || wtop - kSelectThreads < 0)
+            break;
+        above += tot;
     }
     __syncthreads();
-    find_bin_from_top(s_h, kIndexHistBins, (uint32_t)a.top_k, s_tmp, s_out);
     const uint32_t b1 = s_out[0];
+    if (blockIdx.x == 0 && tid == 0) {  // for the final selection
+        a.top[1] = b1;
+        a.top[2] = s_out[1];
+    }
 
     uint32_t cnt = 0;
 #pragma unroll
@@ -431,31 +471,37 @@ __global__ __launch_bounds__(kSelectThreads) void k_index_final(IndexArgs a, int
         __syncthreads();
 
         // ---- the k-th largest key tau; the rows taken are those with a
-        // larger key and the first `rem` (in row order) with key tau
+        // larger key and the first `rem` (in row order) with key tau.  Its top
+        // 12 bits are the candidate pass's bin b1, with `above` keys in higher
+        // bins, so only the low 20 bits of the keys in bin b1 are selected on.
+        const uint32_t b1 = a.top[1], above = a.top[2];
         uint32_t rem;
-        const uint32_t tau = (uint32_t)radix_select(
+        const uint32_t tau = (b1 << 20) | (uint32_t)radix_select(
             [&](uint32_t i, bool& in) -> uint64_t {
-                in = true;
-                return s_c[i] >> 32;
+                const uint32_t kk = (uint32_t)(s_c[i] >> 32);
+                in = (kk >> 20) == b1;
+                return kk & 0xFFFFFu;
             },
-            n_cand, 32, k, s_h, s_tmp, s_out, &rem);
+            n_cand, 20, k - above, s_h, s_tmp, s_out, &rem);
 
         // ---- ordered output: thread tid takes a contiguous run of the
-        // packed candidates; scans give tie ranks and output positions
+        // packed candidates.  One scan of (keys above tau, keys equal to tau)
+        // per thread, packed 16 + 16 bits (counts below 2^14), gives both the
+        // tie rank of the thread's first tie and its first output position:
+        // the ties are taken in row order, so min(tie0, rem) of them precede.
         const uint32_t ch = (n_cand + kSelectThreads - 1) / kSelectThreads;
         const uint32_t c0 = min(n_cand, tid * ch), c1 = min(n_cand, c0 + ch);
-        uint32_t nt = 0;
-        for (uint32_t i = c0; i < c1; ++i)
-            nt += ((uint32_t)(s_c[i] >> 32) == tau) ? 1u : 0u;
-        uint32_t all;
-        const uint32_t tie0 = block_excl_scan(nt, s_tmp, &all);
-        uint32_t nsel = 0, tie = tie0;
+        uint32_t ngt = 0, nt = 0;
         for (uint32_t i = c0; i < c1; ++i) {
             const uint32_t kk = (uint32_t)(s_c[i] >> 32);
-            nsel += (kk > tau || (kk == tau && tie++ < rem)) ? 1u : 0u;
+            ngt += (kk > tau) ? 1u : 0u;
+            nt += (kk == tau) ? 1u : 0u;
         }
-        uint32_t out = block_excl_scan(nsel, s_tmp, &all);
-        tie = tie0;
+        uint32_t all;
+        const uint32_t ex = block_excl_scan((nt << 16) | ngt, s_tmp, &all);
+        const uint32_t tie0 = ex >> 16;
+        uint32_t out = (ex & 0xFFFFu) + min(tie0, rem);
+        uint32_t tie = tie0;
         for (uint32_t i = c0; i < c1; ++i) {
             const uint32_t kk = (uint32_t)(s_c[i] >> 32);
             if (kk > tau || (kk == tau && tie++ < rem)) {
@@ -534,7 +580,8 @@ __global__ __launch_bounds__(256) void k_index_all(int32_t* __restrict__ sel, in
 hipError_t launch_index_topk(const IndexArgs& a, hipStream_t stream, hipEvent_t ev_before,
                              hipEvent_t ev_after)
 {
-    hipLaunchKernelGGL(k_index_clear, dim3(kIndexHistCopies), dim3(kThreads), 0, stream, a.hist);
+    hipLaunchKernelGGL(k_index_clear, dim3(kIndexHistCopies), dim3(kThreads), 0, stream, a.hist,
+                       a.top);
     const unsigned gs = (unsigned)((a.t_rows + kScoreRowsPerGroup - 1) / kScoreRowsPerGroup);
     if (ev_before != nullptr) {
         const hipError_t e = hipEventRecord(ev_before, stream);

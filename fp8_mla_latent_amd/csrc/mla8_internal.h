@@ -80,6 +80,9 @@ struct IndexArgs {
     uint64_t* cand;          // workspace [t_rows]: (key, ~row) candidates
     uint32_t* hist;          // workspace [kIndexHistCopies][kIndexHistBins]
     uint32_t* wg_cnt;        // workspace [ceil(t_rows / 4096)]: candidates per slice
+    uint32_t* top;           // workspace [kIndexHistCopies][16]: the largest order key of the
+                             // scores, one word per copy (64 bytes apart); words 1 and 2: the
+                             // k-th key's first-digit bin and the keys in higher bins
 };
 
 // ev_before / ev_after (may be null) are recorded around the score kernel.
