@@ -191,3 +191,22 @@ def test_index_selection_feeds_the_gather_decode(m):
     ro, rl = oracle.decode_sel(oc, os_, t, wl.lc, wl.rc, sel, ql, qr, wl.sm_scale)
     from tests.tolerance import check_attention
     check_attention(host(out), ro, host(lse), rl, "index -> decode_sel")
+
+
+def test_index_threshold_many_bins_below_the_largest_key(m):
+    # ten rows scaled by 1e30 put the largest keys ~790 first-digit bins above
+    # the rest, so the candidate pass reads several 512-bin windows of the
+    # histogram before it reaches the k-th key
+    say("index: k-th key far below the largest")
+    g = np.random.Generator(np.random.PCG64(35))
+    keys = g.standard_normal((9000, 128)).astype(np.float32)
+    big = np.sort(g.choice(9000, 10, replace=False))
+    keys[big] *= np.float32(1e30)
+    q = g.standard_normal((32, 128)).astype(np.float32)
+    wt = np.abs(g.standard_normal(32)).astype(np.float32) / np.float32(8.0)
+    kc, ks, sel, sc = _run(m, keys, q, wt, 300)
+    ref = oracle.index_scores(kc, ks, q, wt)
+    assert np.isfinite(ref).all() and ref.max() > 1e25
+    _check(sel, sc, ref, _bound(kc, ks, q, wt), 300, "outlier rows")
+    # the outlier rows with a positive score are all chosen
+    assert set(big[sc[big] > 1e20].tolist()) <= set(sel.tolist())
