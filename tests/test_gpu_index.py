@@ -210,3 +210,45 @@ def test_index_threshold_many_bins_below_the_largest_key(m):
     _check(sel, sc, ref, _bound(kc, ks, q, wt), 300, "outlier rows")
     # the outlier rows with a positive score are all chosen
     assert set(big[sc[big] > 1e20].tolist()) <= set(sel.tolist())
+
+
+def test_index_graph_replays_match_eager(m):
+    # the bench replays captured indexer calls: every replay must reproduce the
+    # eager selection and scores (the call clears its histogram and
+    # largest-key words with a kernel of its own, so replays start clean)
+    say("index under graph replay")
+    g = np.random.Generator(np.random.PCG64(36))
+    keys = g.standard_normal((30000, 128)).astype(np.float32)
+    q = g.standard_normal((64, 128)).astype(np.float32)
+    wt = (g.standard_normal(64) / 8).astype(np.float32)
+    kc, ks = m.mla8_quantize_rows(dev(keys), 128, 0)
+    qd, wd = dev(q), dev(wt)
+    sel = torch.empty((2048,), dtype=torch.int32, device=DEV)
+    sc = torch.empty((30000,), dtype=torch.float32, device=DEV)
+    need = m.mla8_workspace_bytes(m.MLA8_OP_INDEX, 30000, 64, 1, 128)
+    ws = torch.empty((need,), dtype=torch.uint8, device=DEV)
+
+    def call():
+        m.mla8_index_topk(kc, ks, qd, wd, 2048, sel=sel, scores=sc, workspace=ws)
+
+    call()
+    ref_sel, ref_sc = host(sel).copy(), host(sc).copy()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        call()
+    torch.cuda.current_stream().wait_stream(s)
+    gr = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(gr):
+        call()
+    for r in range(4):
+        sel.fill_(-1)
+        sc.zero_()
+        ws.fill_(0xAB)  # stale workspace contents must not matter
+        gr.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(host(sel), ref_sel), r
+        assert np.array_equal(host(sc).view(np.uint32), ref_sc.view(np.uint32)), r
+        _ = (torch.ones(1000, device=DEV) * 2).sum().item()  # eager work between replays
+    ref = oracle.index_scores(host(kc), host(ks), q, wt)
+    _check(ref_sel, ref_sc, ref, _bound(host(kc), host(ks), q, wt), 2048, "graph replay")

@@ -164,3 +164,41 @@ def test_decode_sel_mx_parity(m, case):
     out, lse = m.mla8_decode_sel_mx(rows, sc, t, LC, RC, dev(sel), dev(ql), dev(qr), SM)
     ro, rl = oracle.decode_sel_mx(host(rows), host(sc), t, LC, RC, sel, ql, qr, SM)
     check_attention(host(out), ro, host(lse), rl, f"mixed gather {case}")
+
+
+def test_decode_mx_graph_replays_match_eager(m):
+    # the mixed-layout bench replays captured decode calls
+    say("mixed decode under graph replay")
+    t, h = 5000, 64
+    x = mixed_rows(t, 321, 0.01)
+    rows, sc = m.mla8_quantize_rows_mx(dev(x), LC, RC)
+    ql, qr = queries(h, 321)
+    qld, qrd = dev(ql), dev(qr)
+    out = torch.empty((h, LC), dtype=torch.float32, device=DEV)
+    lse = torch.empty((h,), dtype=torch.float32, device=DEV)
+    ws = torch.empty(m.mla8_workspace_bytes(m.MLA8_OP_DECODE, t, h, 1, LC), dtype=torch.uint8,
+                     device=DEV)
+
+    def call():
+        m.mla8_decode_mx(rows, sc, t, LC, RC, qld, qrd, SM, out=out, lse=lse, workspace=ws)
+
+    call()
+    ref_out, ref_lse = host(out).copy(), host(lse).copy()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        call()
+    torch.cuda.current_stream().wait_stream(s)
+    gr = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(gr):
+        call()
+    for r in range(4):
+        out.zero_()
+        lse.zero_()
+        gr.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(host(out), ref_out), r
+        assert np.array_equal(host(lse), ref_lse), r
+        _ = (torch.ones(1000, device=DEV) * 2).sum().item()  # eager work between replays
+    ro, rl = oracle.decode_mx(host(rows), host(sc), t, LC, RC, ql, qr, SM)
+    check_attention(ref_out, ro, ref_lse, rl, "mixed graph replay")
