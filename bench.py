@@ -408,7 +408,7 @@ def bench_mixed(args):
         "higher_is_better": False,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "e4m3 noPE + bf16 RoPE rows; scores e4m3 x 4-term e4m3 q (fp8 mfma) + bf16 x "
+        "dtype": "e4m3 noPE + bf16 RoPE rows; scores e4m3->f16 x f16 hi+lo q (f16 mfma) + bf16 x "
                  "2-term bf16 q (bf16 mfma), context f16 weights x e4m3->f16 (f16 mfma); "
                  "f32 accumulate",
         "data": "synthetic: seeded N(0,1) rows and queries",
@@ -682,7 +682,7 @@ def main():
         "higher_is_better": False,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "e4m3 kv; scores e4m3 x 3-term e4m3 q (fp8 mfma), context f16 weights x e4m3->f16 rows (f16 mfma); f32 accumulate",
+        "dtype": "e4m3 kv; scores e4m3->f16 rows x f16 hi+lo q (f16 mfma), context f16 weights x e4m3->f16 rows (f16 mfma); f32 accumulate",
         "data": "synthetic: seeded N(0,1) rows and queries",
         "config": {"workload": w.name, "heads": w.n_heads, "kv_lora": w.lc, "rope": w.rc,
                    "t_rows": T, "batch": 1, "layers_per_step": L,

@@ -135,8 +135,8 @@ int run_attention(int32_t op, const uint8_t* codes, const float* scales, int64_t
 constexpr int64_t kMaxRows = 0x7FFFFFFF;
 
 // Indexer workspace: keys u32 [t], candidates u64 [t], the first-digit
-// histogram copies and the per-slice candidate counts, each section 256-byte
-// aligned.
+// histogram copies, the per-slice candidate counts and the largest-key words,
+// each section 256-byte aligned.
 size_t r256(size_t b) { return (b + 255) & ~size_t(255); }
 size_t index_ws_bytes(int64_t t)
 {
@@ -309,15 +309,15 @@ int mla8_decode_sel_mx(const uint8_t* kv_rows, const float* kv_scales, int64_t t
                          stream, nullptr, nullptr, nullptr, 0, 0, kMixed);
 }
 
-int mla8_append_decode(uint8_t* kv_codes, float* kv_scales, int64_t cap_rows, int64_t* t_rows,
-                       const float* x_new, int64_t n_new, int32_t lc, int32_t rc,
-                       const float* q_lat, const float* q_rope, int32_t n_heads, float sm_scale,
-                       float* out, float* lse, void* workspace, size_t ws_bytes, void* stream)
+// The fused step and the causal batch over mixed rows: the e4m3 entry
+// points' checks with the mixed shape; the kernels are the mixed instances.
+static int append_decode_layout(uint8_t* kv, float* kv_scales, int64_t cap_rows, int64_t* t_rows,
+                                const float* x_new, int64_t n_new, int32_t lc, int32_t rc,
+                                const float* q_lat, const float* q_rope, int32_t n_heads,
+                                float sm_scale, float* out, float* lse, void* workspace,
+                                size_t ws_bytes, void* stream, int32_t layout)
 {
-    int st = check_shape(lc, rc);
-    if (st != MLA8_OK)
-        return st;
-    if (!kv_codes || !kv_scales || !t_rows || !x_new)
+    if (!kv || !kv_scales || !t_rows || !x_new)
         return MLA8_E_INVAL;
     if (cap_rows <= 0 || cap_rows > kMaxRows || n_new <= 0 || *t_rows < 0 || *t_rows > cap_rows)
         return MLA8_E_INVAL;
@@ -328,16 +328,75 @@ int mla8_append_decode(uint8_t* kv_codes, float* kv_scales, int64_t cap_rows, in
     if (n_new > cap_rows - *t_rows)
         return MLA8_E_CAPACITY;
     const int64_t t_new = *t_rows + n_new;
-    st = check_decode_common(kv_codes, kv_scales, t_new, lc, rc, q_lat, q_rope, n_heads, sm_scale,
-                             out);
+    int st = check_decode_common(kv, kv_scales, t_new, lc, rc, q_lat, q_rope, n_heads, sm_scale,
+                                 out);
     if (st != MLA8_OK)
         return st;
-    st = run_attention(MLA8_OP_DECODE, kv_codes, kv_scales, t_new, lc, rc, nullptr, t_new, q_lat,
+    st = run_attention(MLA8_OP_DECODE, kv, kv_scales, t_new, lc, rc, nullptr, t_new, q_lat,
                        q_rope, n_heads, n_heads, 0, sm_scale, out, lse, workspace, ws_bytes,
-                       stream, x_new, kv_codes, kv_scales, *t_rows, n_new);
+                       stream, x_new, kv, kv_scales, *t_rows, n_new, layout);
     if (st == MLA8_OK)
         *t_rows = t_new;
     return st;
+}
+
+static int batch_layout(const uint8_t* kv, const float* kv_scales, int64_t t_rows, int32_t lc,
+                        int32_t rc, const float* q_lat, const float* q_rope, int32_t n_q,
+                        int64_t pos0, int32_t n_heads, float sm_scale, float* out, float* lse,
+                        void* workspace, size_t ws_bytes, void* stream, int32_t layout)
+{
+    int st = check_decode_common(kv, kv_scales, t_rows, lc, rc, q_lat, q_rope, n_heads, sm_scale,
+                                 out);
+    if (st != MLA8_OK)
+        return st;
+    if (n_q <= 0 || pos0 < 0)
+        return MLA8_E_INVAL;
+    if ((int64_t)n_q * (int64_t)n_heads > kMaxRows / 1024)
+        return MLA8_E_UNSUPPORTED;
+    if (pos0 + n_q > t_rows)
+        return MLA8_E_RANGE;
+    return run_attention(MLA8_OP_BATCH, kv, kv_scales, t_rows, lc, rc, nullptr, pos0 + n_q, q_lat,
+                         q_rope, n_q * n_heads, n_heads, pos0, sm_scale, out, lse, workspace,
+                         ws_bytes, stream, nullptr, nullptr, nullptr, 0, 0, layout);
+}
+
+int mla8_append_decode_mx(uint8_t* kv_rows, float* kv_scales, int64_t cap_rows, int64_t* t_rows,
+                          const float* x_new, int64_t n_new, int32_t lc, int32_t rc,
+                          const float* q_lat, const float* q_rope, int32_t n_heads,
+                          float sm_scale, float* out, float* lse, void* workspace,
+                          size_t ws_bytes, void* stream)
+{
+    const int st = check_shape_mx(lc, rc);
+    if (st != MLA8_OK)
+        return st;
+    return append_decode_layout(kv_rows, kv_scales, cap_rows, t_rows, x_new, n_new, lc, rc,
+                                q_lat, q_rope, n_heads, sm_scale, out, lse, workspace, ws_bytes,
+                                stream, kMixed);
+}
+
+int mla8_batch_mx(const uint8_t* kv_rows, const float* kv_scales, int64_t t_rows, int32_t lc,
+                  int32_t rc, const float* q_lat, const float* q_rope, int32_t n_q, int64_t pos0,
+                  int32_t n_heads, float sm_scale, float* out, float* lse, void* workspace,
+                  size_t ws_bytes, void* stream)
+{
+    const int st = check_shape_mx(lc, rc);
+    if (st != MLA8_OK)
+        return st;
+    return batch_layout(kv_rows, kv_scales, t_rows, lc, rc, q_lat, q_rope, n_q, pos0, n_heads,
+                        sm_scale, out, lse, workspace, ws_bytes, stream, kMixed);
+}
+
+int mla8_append_decode(uint8_t* kv_codes, float* kv_scales, int64_t cap_rows, int64_t* t_rows,
+                       const float* x_new, int64_t n_new, int32_t lc, int32_t rc,
+                       const float* q_lat, const float* q_rope, int32_t n_heads, float sm_scale,
+                       float* out, float* lse, void* workspace, size_t ws_bytes, void* stream)
+{
+    const int st = check_shape(lc, rc);
+    if (st != MLA8_OK)
+        return st;
+    return append_decode_layout(kv_codes, kv_scales, cap_rows, t_rows, x_new, n_new, lc, rc,
+                                q_lat, q_rope, n_heads, sm_scale, out, lse, workspace, ws_bytes,
+                                stream, kE4m3);
 }
 
 int mla8_decode_sel(const uint8_t* kv_codes, const float* kv_scales, int64_t t_rows, int32_t lc,
@@ -361,19 +420,8 @@ int mla8_batch(const uint8_t* kv_codes, const float* kv_scales, int64_t t_rows, 
                int32_t n_heads, float sm_scale, float* out, float* lse, void* workspace,
                size_t ws_bytes, void* stream)
 {
-    int st = check_decode_common(kv_codes, kv_scales, t_rows, lc, rc, q_lat, q_rope, n_heads,
-                                 sm_scale, out);
-    if (st != MLA8_OK)
-        return st;
-    if (n_q <= 0 || pos0 < 0)
-        return MLA8_E_INVAL;
-    if ((int64_t)n_q * (int64_t)n_heads > kMaxRows / 1024)
-        return MLA8_E_UNSUPPORTED;
-    if (pos0 + n_q > t_rows)
-        return MLA8_E_RANGE;
-    return run_attention(MLA8_OP_BATCH, kv_codes, kv_scales, t_rows, lc, rc, nullptr, pos0 + n_q,
-                         q_lat, q_rope, n_q * n_heads, n_heads, pos0, sm_scale, out, lse,
-                         workspace, ws_bytes, stream);
+    return batch_layout(kv_codes, kv_scales, t_rows, lc, rc, q_lat, q_rope, n_q, pos0, n_heads,
+                        sm_scale, out, lse, workspace, ws_bytes, stream, kE4m3);
 }
 
 int mla8_index_topk(const uint8_t* k_codes, const float* k_scales, int64_t t_rows, int32_t ihd,

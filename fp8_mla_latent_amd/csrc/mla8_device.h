@@ -131,4 +131,21 @@ __device__ __forceinline__ void quantize_row_wave(const float* __restrict__ x, i
         *scale_out = scale;
 }
 
+// Mixed row (noPE e4m3 + per-row scale, RoPE bf16) by one wave: the lc noPE
+// values of x through the row quantizer above (their own amax and scale),
+// the rc RoPE values that follow them to bf16 by round-to-nearest-even; the
+// stored row is lc code bytes then rc bf16 values (lc + 2 rc bytes).
+__device__ __forceinline__ void quantize_row_mx_wave(const float* __restrict__ x, int32_t lc,
+                                                     int32_t rc, uint8_t* __restrict__ row,
+                                                     float* __restrict__ scale_out, int lane)
+{
+    quantize_row_wave(x, lc, row, scale_out, lane);
+    if (lane < rc / 4) {
+        const float4 v = reinterpret_cast<const float4*>(x + lc)[lane];
+        const uint32_t b0 = bf16_rne_bits(v.x), b1 = bf16_rne_bits(v.y);
+        const uint32_t b2 = bf16_rne_bits(v.z), b3 = bf16_rne_bits(v.w);
+        reinterpret_cast<uint2*>(row + lc)[lane] = make_uint2(b0 | (b1 << 16), b2 | (b3 << 16));
+    }
+}
+
 }  // namespace mla8

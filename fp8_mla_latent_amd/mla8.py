@@ -29,7 +29,8 @@ MLA8_OP_INDEX = 3
 
 EXPORTED = ("mla8_quantize_rows", "mla8_append", "mla8_decode", "mla8_append_decode",
             "mla8_decode_sel", "mla8_batch", "mla8_quantize_rows_mx", "mla8_append_mx",
-            "mla8_decode_mx", "mla8_decode_sel_mx", "mla8_index_topk", "mla8_kvfile_create",
+            "mla8_decode_mx", "mla8_decode_sel_mx", "mla8_append_decode_mx", "mla8_batch_mx",
+            "mla8_index_topk", "mla8_kvfile_create",
             "mla8_kvfile_info", "mla8_kvfile_append", "mla8_kvfile_load",
             "mla8_workspace_bytes", "mla8_force_splits", "mla8_plan_splits",
             "mla8_status_string", "mla8_version", "mla8_test_encode", "mla8_profile_events")
@@ -63,6 +64,10 @@ def _load() -> ctypes.CDLL:
         "mla8_decode_mx": (ctypes.c_int, [P, P, i64, i32, i32, P, P, i32, f32, P, P, P, sz, P]),
         "mla8_decode_sel_mx": (ctypes.c_int,
                                [P, P, i64, i32, i32, P, i64, P, P, i32, f32, P, P, P, sz, P]),
+        "mla8_append_decode_mx": (ctypes.c_int, [P, P, i64, ctypes.POINTER(i64), P, i64, i32,
+                                                 i32, P, P, i32, f32, P, P, P, sz, P]),
+        "mla8_batch_mx": (ctypes.c_int,
+                          [P, P, i64, i32, i32, P, P, i32, i64, i32, f32, P, P, P, sz, P]),
         "mla8_index_topk": (ctypes.c_int,
                             [P, P, i64, i32, P, P, i32, i32, P, P, P, sz, P]),
         "mla8_kvfile_create": (ctypes.c_int, [ctypes.c_char_p, i32, i32, i32]),
@@ -177,7 +182,7 @@ def mla8_decode(kv_codes, kv_scales, t_rows: int, lc: int, rc: int, q_lat, q_rop
 
 def mla8_append_decode(kv_codes, kv_scales, t_rows: int, x_new, lc: int, rc: int, q_lat, q_rope,
                        sm_scale: float, out=None, lse=None, workspace=None,
-                       want_lse: bool = True):
+                       want_lse: bool = True, _fn: str = "mla8_append_decode"):
     """Append x_new [n, lc+rc] at rows [t_rows, t_rows + n) and decode over all
     t_rows + n rows in one launch: returns (out, lse, new t_rows)."""
     h = q_lat.shape[0]
@@ -189,11 +194,19 @@ def mla8_append_decode(kv_codes, kv_scales, t_rows: int, x_new, lc: int, rc: int
         lse = torch.empty((h,), dtype=torch.float32, device=dev)
     ws = _workspace(MLA8_OP_DECODE, t_rows + n, h, 1, lc, dev, workspace)
     t = ctypes.c_int64(t_rows)
-    _check(lib.mla8_append_decode(_ptr(kv_codes), _ptr(kv_scales), kv_codes.shape[0],
-                                  ctypes.byref(t), _ptr(x_new), n, lc, rc, _ptr(q_lat),
-                                  _ptr(q_rope), h, float(sm_scale), _ptr(out), _ptr(lse),
-                                  _ptr(ws), ws.numel(), _stream(q_lat)), "mla8_append_decode")
+    _check(getattr(lib, _fn)(_ptr(kv_codes), _ptr(kv_scales), kv_codes.shape[0],
+                             ctypes.byref(t), _ptr(x_new), n, lc, rc, _ptr(q_lat),
+                             _ptr(q_rope), h, float(sm_scale), _ptr(out), _ptr(lse),
+                             _ptr(ws), ws.numel(), _stream(q_lat)), _fn)
     return out, lse, int(t.value)
+
+
+def mla8_append_decode_mx(kv_rows, kv_scales, t_rows: int, x_new, lc: int, rc: int, q_lat,
+                          q_rope, sm_scale: float, out=None, lse=None, workspace=None,
+                          want_lse: bool = True):
+    """As mla8_append_decode over mixed rows (kv_rows [cap, lc + 2 rc])."""
+    return mla8_append_decode(kv_rows, kv_scales, t_rows, x_new, lc, rc, q_lat, q_rope, sm_scale,
+                              out, lse, workspace, want_lse, _fn="mla8_append_decode_mx")
 
 
 def mla8_decode_sel(kv_codes, kv_scales, t_rows: int, lc: int, rc: int, sel, q_lat, q_rope,
@@ -215,7 +228,8 @@ def mla8_decode_sel(kv_codes, kv_scales, t_rows: int, lc: int, rc: int, sel, q_l
 
 
 def mla8_batch(kv_codes, kv_scales, t_rows: int, lc: int, rc: int, q_lat, q_rope, pos0: int,
-               sm_scale: float, out=None, lse=None, workspace=None, want_lse: bool = True):
+               sm_scale: float, out=None, lse=None, workspace=None, want_lse: bool = True,
+               _fn: str = "mla8_batch"):
     """Causal batch: q [S, H, *]; query s attends rows [0, pos0 + s]."""
     n_q, h = q_lat.shape[0], q_lat.shape[1]
     dev = q_lat.device
@@ -224,10 +238,17 @@ def mla8_batch(kv_codes, kv_scales, t_rows: int, lc: int, rc: int, q_lat, q_rope
     if lse is None and want_lse:
         lse = torch.empty((n_q, h), dtype=torch.float32, device=dev)
     ws = _workspace(MLA8_OP_BATCH, pos0 + n_q, h, n_q, lc, dev, workspace)
-    _check(lib.mla8_batch(_ptr(kv_codes), _ptr(kv_scales), t_rows, lc, rc, _ptr(q_lat),
-                          _ptr(q_rope), n_q, pos0, h, float(sm_scale), _ptr(out), _ptr(lse),
-                          _ptr(ws), ws.numel(), _stream(q_lat)), "mla8_batch")
+    _check(getattr(lib, _fn)(_ptr(kv_codes), _ptr(kv_scales), t_rows, lc, rc, _ptr(q_lat),
+                             _ptr(q_rope), n_q, pos0, h, float(sm_scale), _ptr(out), _ptr(lse),
+                             _ptr(ws), ws.numel(), _stream(q_lat)), _fn)
     return out, lse
+
+
+def mla8_batch_mx(kv_rows, kv_scales, t_rows: int, lc: int, rc: int, q_lat, q_rope, pos0: int,
+                  sm_scale: float, out=None, lse=None, workspace=None, want_lse: bool = True):
+    """As mla8_batch over mixed rows."""
+    return mla8_batch(kv_rows, kv_scales, t_rows, lc, rc, q_lat, q_rope, pos0, sm_scale, out, lse,
+                      workspace, want_lse, _fn="mla8_batch_mx")
 
 
 def mla8_quantize_rows_mx(x: torch.Tensor, lc: int, rc: int, rows=None, scales=None):

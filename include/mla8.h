@@ -197,6 +197,26 @@ MLA8_API int mla8_decode_sel_mx(const uint8_t* kv_rows, const float* kv_scales, 
                                 const float* q_lat, const float* q_rope, int32_t n_heads,
                                 float sm_scale, float* out, float* lse, void* workspace,
                                 size_t ws_bytes, void* stream);
+/* As mla8_append_decode over mixed rows: the n_new (1..64) fresh f32 rows x_new
+ * [n_new][lc + rc] (16-byte aligned) are stored at rows [*t_rows, *t_rows +
+ * n_new) in the mla8_quantize_rows_mx format by the same launch that attends
+ * the t_rows + n_new rows; *t_rows advances on success only.  Workspace from
+ * mla8_workspace_bytes(MLA8_OP_DECODE, *t_rows + n_new, n_heads, 1, lc).
+ * Errors as mla8_append_decode (E_RANGE for n_new > 64, E_CAPACITY beyond
+ * cap_rows), E_UNSUPPORTED for a shape other than 448 / 64. */
+MLA8_API int mla8_append_decode_mx(uint8_t* kv_rows, float* kv_scales, int64_t cap_rows,
+                                   int64_t* t_rows, const float* x_new, int64_t n_new, int32_t lc,
+                                   int32_t rc, const float* q_lat, const float* q_rope,
+                                   int32_t n_heads, float sm_scale, float* out, float* lse,
+                                   void* workspace, size_t ws_bytes, void* stream);
+/* As mla8_batch (query s at position pos0 + s attends rows 0 .. pos0 + s;
+ * q_lat [n_q][n_heads][lc], q_rope [n_q][n_heads][rc]; out [n_q][n_heads][lc],
+ * lse [n_q][n_heads]) over mixed rows; workspace from
+ * mla8_workspace_bytes(MLA8_OP_BATCH, pos0 + n_q, n_heads, n_q, lc). */
+MLA8_API int mla8_batch_mx(const uint8_t* kv_rows, const float* kv_scales, int64_t t_rows,
+                           int32_t lc, int32_t rc, const float* q_lat, const float* q_rope,
+                           int32_t n_q, int64_t pos0, int32_t n_heads, float sm_scale, float* out,
+                           float* lse, void* workspace, size_t ws_bytes, void* stream);
 
 /*
  * fp8 indexer score + top-k: the selection that mla8_decode_sel attends.
@@ -251,9 +271,9 @@ MLA8_API int32_t mla8_plan_splits(int32_t op, int64_t rows, int32_t n_heads, int
 
 /*
  * Measurement hook: while set, every attention call (mla8_decode,
- * mla8_append_decode, mla8_decode_sel, mla8_batch) records the hipEvent_t
- * `before` on its stream just before launching the split-T partial kernel and
- * `after` just after it, and mla8_index_topk does the same around its score
+ * mla8_append_decode, mla8_decode_sel, mla8_batch and their _mx forms) records
+ * the hipEvent_t `before` on its stream just before launching the split-T
+ * partial kernel and `after` just after it, and mla8_index_topk does the same around its score
  * kernel, so hipEventElapsedTime(before, after) is that kernel's duration.
  * Pass NULL, NULL to clear.  Events are caller-owned.  Not thread-safe.
  * Returns MLA8_OK.

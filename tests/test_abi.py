@@ -213,3 +213,30 @@ def test_mixed_refuses():
         args = list(base)
         args[idx] = val
         assert d(*args) == want, (idx, val)
+
+
+def test_mixed_step_and_batch_refuse():
+    f = m.lib.mla8_append_decode_mx
+    t = ctypes.c_int64(10)
+    base = [FAKE, FAKE, 100, ctypes.byref(t), FAKE, 1, 448, 64, FAKE, FAKE, 64, 0.1, FAKE, None,
+            FAKE, 1 << 30, None]
+    for idx, val, want in [(6, 512, m.MLA8_E_UNSUPPORTED),   # the e4m3 shape is not mixed
+                           (7, 32, m.MLA8_E_UNSUPPORTED),
+                           (4, None, m.MLA8_E_INVAL),         # no fresh rows
+                           (5, 65, m.MLA8_E_RANGE),           # more than the fused maximum
+                           (2, 10, m.MLA8_E_CAPACITY),        # shadow full
+                           (4, FAKE_MISALIGNED, m.MLA8_E_INVAL),
+                           (15, 10, m.MLA8_E_WORKSPACE)]:
+        args = list(base)
+        args[idx] = val
+        assert f(*args) == want, (idx, val)
+        assert t.value == 10
+    b = m.lib.mla8_batch_mx
+    ws = m.lib.mla8_workspace_bytes(m.MLA8_OP_BATCH, 100, 16, 4, 448)
+    base = [FAKE, FAKE, 100, 448, 64, FAKE, FAKE, 4, 96, 16, 0.1, FAKE, None, FAKE, ws, None]
+    for idx, val, want in [(3, 512, m.MLA8_E_UNSUPPORTED), (7, 0, m.MLA8_E_INVAL),
+                           (8, 97, m.MLA8_E_RANGE), (14, ws - 1, m.MLA8_E_WORKSPACE),
+                           (5, None, m.MLA8_E_INVAL)]:
+        args = list(base)
+        args[idx] = val
+        assert b(*args) == want, (idx, val)

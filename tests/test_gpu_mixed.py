@@ -202,3 +202,90 @@ def test_decode_mx_graph_replays_match_eager(m):
         _ = (torch.ones(1000, device=DEV) * 2).sum().item()  # eager work between replays
     ro, rl = oracle.decode_mx(host(rows), host(sc), t, LC, RC, ql, qr, SM)
     check_attention(ref_out, ro, ref_lse, rl, "mixed graph replay")
+
+
+@pytest.mark.parametrize("t0,n_new", [(40, 3), (5000, 1), (20000, 64)])
+def test_append_decode_mx_parity(m, t0, n_new):
+    # fresh rows in the first tile (quantized before any row is loaded) or in
+    # the last chunk (quantized after the prologue); the stored bytes are the
+    # oracle's, the attention covers old and fresh rows
+    say(f"mixed fused append + decode t0={t0} n_new={n_new}")
+    h = 64
+    x = mixed_rows(t0 + n_new, 900 + t0, 0.01)
+    rows = torch.zeros((t0 + n_new + 7, LC + 2 * RC), dtype=torch.uint8, device=DEV)
+    scales = torch.zeros((t0 + n_new + 7,), dtype=torch.float32, device=DEV)
+    assert m.mla8_append_mx(rows, scales, 0, dev(x[:t0]), LC, RC) == t0
+    ql, qr = queries(h, t0)
+    out, lse, t1 = m.mla8_append_decode_mx(rows, scales, t0, dev(x[t0:]), LC, RC, dev(ql),
+                                           dev(qr), SM)
+    assert t1 == t0 + n_new
+    orows, osc = oracle.quantize_rows_mx(x, LC, RC)
+    np.testing.assert_array_equal(host(rows)[:t1], orows)
+    np.testing.assert_array_equal(host(scales)[:t1].view(np.uint32), osc.view(np.uint32))
+    assert not host(rows)[t1:].any()
+    ro, rl = oracle.decode_mx(orows, osc, t1, LC, RC, ql, qr, SM)
+    check_attention(host(out), ro, host(lse), rl, f"mixed append_decode t0={t0}")
+
+
+def test_append_decode_mx_graph_replays_match_eager(m):
+    say("mixed fused append + decode under graph replay")
+    t, h = 6000, 64
+    x = mixed_rows(t, 77, 0.01)
+    rows = torch.zeros((t, LC + 2 * RC), dtype=torch.uint8, device=DEV)
+    scales = torch.zeros((t,), dtype=torch.float32, device=DEV)
+    assert m.mla8_append_mx(rows, scales, 0, dev(x[:t - 1]), LC, RC) == t - 1
+    fresh = dev(x[t - 1:])
+    ql, qr = queries(h, 77)
+    qld, qrd = dev(ql), dev(qr)
+    out = torch.empty((h, LC), dtype=torch.float32, device=DEV)
+    lse = torch.empty((h,), dtype=torch.float32, device=DEV)
+    ws = torch.empty(m.mla8_workspace_bytes(m.MLA8_OP_DECODE, t, h, 1, LC), dtype=torch.uint8,
+                     device=DEV)
+
+    def step():
+        m.mla8_append_decode_mx(rows, scales, t - 1, fresh, LC, RC, qld, qrd, SM, out=out,
+                                lse=lse, workspace=ws)
+
+    step()
+    ref_out, ref_lse = host(out).copy(), host(lse).copy()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step()
+    torch.cuda.current_stream().wait_stream(s)
+    gr = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(gr):
+        step()
+    for r in range(4):
+        out.zero_()
+        lse.zero_()
+        rows[t - 1].zero_()  # the replay rewrites the fresh row
+        gr.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(host(out), ref_out), r
+        assert np.array_equal(host(lse), ref_lse), r
+        _ = (torch.ones(1000, device=DEV) * 2).sum().item()
+    orows, osc = oracle.quantize_rows_mx(x, LC, RC)
+    np.testing.assert_array_equal(host(rows), orows)
+    ro, rl = oracle.decode_mx(orows, osc, t, LC, RC, ql, qr, SM)
+    check_attention(ref_out, ro, ref_lse, rl, "mixed append_decode graph")
+
+
+@pytest.mark.parametrize("t,n_q,h", [(3000, 16, 16), (700, 64, 8)])
+def test_batch_mx_parity(m, t, n_q, h):
+    # query s at position pos0 + s attends rows 0 .. pos0 + s: the selected-row
+    # oracle over exactly those rows
+    say(f"mixed causal batch t={t} n_q={n_q} h={h}")
+    x = mixed_rows(t, 1234 + t, 0.01)
+    rows, sc = m.mla8_quantize_rows_mx(dev(x), LC, RC)
+    g = np.random.Generator(np.random.PCG64(55 + t))
+    ql = g.standard_normal((n_q, h, LC)).astype(np.float32)
+    qr = g.standard_normal((n_q, h, RC)).astype(np.float32)
+    pos0 = t - n_q
+    out, lse = m.mla8_batch_mx(rows, sc, t, LC, RC, dev(ql), dev(qr), pos0, SM)
+    hr, hs = host(rows), host(sc)
+    go, gl = host(out), host(lse)
+    for sidx in range(n_q):
+        sel = np.arange(pos0 + sidx + 1, dtype=np.int32)
+        ro, rl = oracle.decode_sel_mx(hr, hs, t, LC, RC, sel, ql[sidx], qr[sidx], SM)
+        check_attention(go[sidx], ro, gl[sidx], rl, f"mixed batch query {sidx}")
