@@ -331,9 +331,9 @@ def bench_mixed(args):
     log(f"{L} layers of {T - 1} mixed rows quantized")
 
     def one(ly):
-        m.mla8_append_mx(ly["rows"], ly["scales"], T - 1, ly["fresh"], LC, RC)
-        m.mla8_decode_mx(ly["rows"], ly["scales"], T, LC, RC, ly["ql"], ly["qr"], w.sm_scale,
-                         out=ly["out"], lse=ly["lse"], workspace=ws)
+        m.mla8_append_decode_mx(ly["rows"], ly["scales"], T - 1, ly["fresh"], LC, RC, ly["ql"],
+                                ly["qr"], w.sm_scale, out=ly["out"], lse=ly["lse"],
+                                workspace=ws)
 
     def step():
         for ly in layers:
@@ -377,10 +377,10 @@ def bench_mixed(args):
     try:
         for _ in range(K):
             for ly in layers:
-                m.mla8_append_mx(ly["rows"], ly["scales"], T - 1, ly["fresh"], LC, RC)
                 m.mla8_profile_events(*evs[i])
-                m.mla8_decode_mx(ly["rows"], ly["scales"], T, LC, RC, ly["ql"], ly["qr"],
-                                 w.sm_scale, out=ly["out"], lse=ly["lse"], workspace=ws)
+                m.mla8_append_decode_mx(ly["rows"], ly["scales"], T - 1, ly["fresh"], LC, RC,
+                                        ly["ql"], ly["qr"], w.sm_scale, out=ly["out"],
+                                        lse=ly["lse"], workspace=ws)
                 i += 1
     finally:
         m.mla8_profile_events(None, None)
