@@ -96,6 +96,21 @@ def test_decode_mx_parity(m, t, h, outl, splits):
     check_attention(host(out), ro, host(lse), rl, f"mixed t={t} h={h}")
 
 
+@pytest.mark.parametrize("qscale", [0.0, 1e-30, 1e-4, 1e4, 1e15])
+def test_decode_mx_query_magnitudes(m, qscale):
+    t, h = 2000, 16
+    say(f"mixed decode query scale {qscale}")
+    x = mixed_rows(t, 91)
+    rows, scales = m.mla8_quantize_rows_mx(dev(x), LC, RC)
+    ql, qr = queries(h, 91)
+    ql, qr = (ql * qscale).astype(np.float32), (qr * qscale).astype(np.float32)
+    out, lse = m.mla8_decode_mx(rows, scales, t, LC, RC, dev(ql), dev(qr), SM)
+    orows, osc = oracle.quantize_rows_mx(x, LC, RC)
+    np.testing.assert_array_equal(host(rows), orows)
+    ro, rl = oracle.decode_mx(orows, osc, t, LC, RC, ql, qr, SM)
+    check_attention(host(out), ro, host(lse), rl, f"mixed query scale {qscale}")
+
+
 def test_decode_mx_rope_carries_the_scores(m):
     # noPE queries zero: only the bf16 RoPE part (unscaled by the row scale)
     # decides the weights

@@ -217,6 +217,23 @@ def test_decode_shapes(m, h, lc, rc, t):
     check_attention(host(out), ro, host(lse), rl, f"H={h} lc={lc} rc={rc} T={t}")
 
 
+# The score operands scale each head's query by a power of two (largest |e|
+# in [2^14, 2^15), the exponent clamped at 100): zero, tiny, ordinary, large
+# and huge queries (one-hot softmax) all keep the tolerance.
+@pytest.mark.parametrize("qscale", [0.0, 1e-30, 1e-4, 1.0, 1e4, 1e15])
+def test_decode_query_magnitudes(m, qscale):
+    h, lc, rc, t = 16, 512, 64, 3001
+    say(f"decode query scale {qscale}")
+    g = np.random.Generator(np.random.PCG64(77))
+    x = g.standard_normal((t, lc + rc)).astype(np.float32)
+    ql = (g.standard_normal((h, lc)) * qscale).astype(np.float32)
+    qr = (g.standard_normal((h, rc)) * qscale).astype(np.float32)
+    oc, os_ = oracle.quantize_rows(x)
+    out, lse = m.mla8_decode(dev(oc), dev(os_), t, lc, rc, dev(ql), dev(qr), 1.0 / math.sqrt(192.0))
+    ro, rl = oracle.decode(oc, os_, t, lc, rc, ql, qr, 1.0 / math.sqrt(192.0))
+    check_attention(host(out), ro, host(lse), rl, f"query scale {qscale}")
+
+
 @pytest.mark.parametrize("splits", [1, 3, 8, 16, 64])
 def test_decode_split_count_invariance(m, splits):
     w = W.DSV3
