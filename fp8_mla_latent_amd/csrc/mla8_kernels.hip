@@ -15,19 +15,21 @@
 //   * One workgroup owns a chunk of rows and 32 query-heads, so every row is
 //     read from HBM once for all its heads; workgroups sharing a chunk are
 //     placed on the same XCD so the second head group hits that XCD's L2.
-//   * Rows stream HBM -> LDS in 64-row tiles through a 3-stage ring of direct
-//     global_load_lds_dwordx4 loads (two tiles in flight, no register
-//     staging).
-//   * 8 waves per workgroup (two per SIMD).  Scores S^T[row][head] = X . Q^T:
-//     each wave takes 16 rows x 16 heads on the scaled fp8 MFMA, straight on
-//     the e4m3 row bytes; the query is split into three e4m3 terms (about 12
-//     significant bits) held in registers, each with a per-head E8M0 operand
-//     scale.
-//   * Context O[head][col] += W . X: each wave owns a 64-column slice for all
-//     32 heads; ds_read_b64_tr_b8 reads the row bytes transposed so the row
-//     (contraction) index becomes the MFMA K index, and v_cvt_scalef32_pk_f16_fp8
-//     widens them to fp16 exactly (every e4m3 value is an fp16 normal) for
-//     v_mfma_f32_16x16x32_f16 with fp16 weights.
+//   * Rows stream HBM -> LDS in 64-row tiles through a ring of direct
+//     global_load_lds_dwordx4 loads (4 stages with two tiles in flight, or 3
+//     with one when 4 do not fit), laid out for the readers; no register
+//     staging.
+//   * 8 waves per workgroup (two per SIMD) in two roles, one of each per
+//     SIMD.  Score waves: S^T[row][head] = X . Q^T for 32 rows x 16 heads on
+//     v_mfma_f32_16x16x32_f16, the row bytes widened to fp16 exactly and the
+//     query split into fp16 hi + lo held in registers (the fp8 MFMAs cut their
+//     products in groups of 8, too coarse for the scores; see the query
+//     operands below); then the softmax weights.  Context waves: O[head][col]
+//     += W . X for a 128-column slice and all 32 heads; ds_read_b64_tr_b8
+//     reads the row bytes transposed so the row (contraction) index becomes
+//     the MFMA K index, and v_cvt_scalef32_pk_f16_fp8 widens them to fp16
+//     exactly (every e4m3 value is an fp16 value) for v_mfma_f32_16x16x32_f16
+//     with fp16 weights.  The context waves also issue every row load.
 //   * The row scale is hoisted: scores are (q . code) * scale_t, and the PV
 //     weight of row t is exp2((u_t - m) + log2 scale_t - d) with d a running
 //     max kept relative to the score max m, so fp16 weights never overflow or
