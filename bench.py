@@ -35,6 +35,7 @@ if ROOT not in sys.path:
 
 METRIC = "ms/layer-token + achieved HBM GB/s (fp8 KV stream), MLA decode at T=262144"
 HBM_PEAK_GBS = 8000.0
+MFMA_F16_PEAK_TFLOPS = 2500.0  # dense fp16 / bf16 MFMA
 SETTLE_S = 0.25  # untimed replays before the warm-up steps (GPU clock ramp)
 
 
@@ -72,12 +73,13 @@ def parse():
                          "(JSON); used only while the kernel source still matches its hash")
     ap.add_argument("--workload", default="long_t262144",
                     choices=["long_t262144", "dsa_index_t131072_k2048", "kvfile_t262144",
-                             "mixed_t262144"],
+                             "mixed_t262144", "dsa_t131072_ns2048", "batch_s64_t32768"],
                     help="long_t262144: the fused append + split-T decode step (default); "
                          "dsa_index_t131072_k2048: the fp8 indexer score + top-k; "
                          "kvfile_t262144: resume a persisted shadow file into device shadows; "
                          "mixed_t262144: the decode step over mixed rows (noPE e4m3 448 + RoPE "
-                         "bf16 64)")
+                         "bf16 64); dsa_t131072_ns2048: the selected-row decode over 2048 "
+                         "rows; batch_s64_t32768: the causal batch of 64 queries")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device copy (counter calibration) and exit")
     return ap.parse_args()
@@ -266,6 +268,265 @@ def bench_index(args):
         "key_stream_gb_per_s": round(key_bytes / (ms_lt * 1e-3) / 1e9, 1),
         "clock_settle": {"seconds": SETTLE_S, "untimed_steps": n_settle},
         "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(rec), flush=True)
+
+
+def _event_pass(run, K, layers, call):
+    """Library-side HIP events around every partial-kernel launch of K eager
+    steps (30 graph steps queued ahead so launches never wait for the GPU);
+    returns the durations in us."""
+    import numpy as np
+    import torch
+
+    from fp8_mla_latent_amd import mla8 as m
+
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(K * len(layers))]
+    for a_, b_ in evs:
+        a_.record()
+        b_.record()
+    torch.cuda.synchronize()
+    for _ in range(30):
+        run()
+    i = 0
+    try:
+        for _ in range(K):
+            for ly in layers:
+                m.mla8_profile_events(*evs[i])
+                call(ly)
+                i += 1
+    finally:
+        m.mla8_profile_events(None, None)
+    torch.cuda.synchronize()
+    return np.array([a.elapsed_time(b) for a, b in evs]) * 1e3
+
+
+def _timed_steps(step, args):
+    """Capture step as a HIP graph (unless --no-graph), settle the clocks, run
+    the warm-up, then time K steps; returns (run, ms per step, settle count,
+    graph or None)."""
+    import torch
+
+    for _ in range(max(args.warmup, 1)):
+        step()
+    torch.cuda.synchronize()
+    graph = None
+    if not args.no_graph:
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step()
+        torch.cuda.synchronize()
+        run = graph.replay
+    else:
+        run = step
+    n_settle = settle(run, "steps")
+    for _ in range(args.warmup):
+        run()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        run()
+    e1.record()
+    torch.cuda.synchronize()
+    return run, e0.elapsed_time(e1) / args.steps, n_settle, graph
+
+
+def bench_dsa(args):
+    """Selected-row (DSA gather) decode: per layer, mla8_decode_sel over 2048
+    sorted unique rows of its own T=131072 shadow, H=64.  Latency-bound: the
+    gathered rows are 1.19 MB."""
+    import numpy as np
+    import torch
+
+    from fp8_mla_latent_amd import mla8 as m
+    from fp8_mla_latent_amd import workloads as W
+
+    w = W.DSA
+    L, K = args.layers or 8, args.steps
+    T, NS = w.t_rows, w.n_sel
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    layers = []
+    for l in range(L):
+        x = torch.from_numpy(W.rows(w, T, seed_offset=l)).to(dev)
+        codes, scales = m.mla8_quantize_rows(x, w.lc, w.rc)
+        del x
+        ql, qr = W.queries(w, seed_offset=l)
+        layers.append(dict(codes=codes, scales=scales,
+                           sel=torch.from_numpy(W.selection(w, seed_offset=l)).to(dev),
+                           ql=torch.from_numpy(ql).to(dev), qr=torch.from_numpy(qr).to(dev),
+                           out=torch.empty((w.n_heads, w.lc), dtype=torch.float32, device=dev),
+                           lse=torch.empty((w.n_heads,), dtype=torch.float32, device=dev)))
+    ws = torch.empty(m.mla8_workspace_bytes(m.MLA8_OP_DECODE_SEL, NS, w.n_heads, 1, w.lc),
+                     dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+    log(f"{L} layers of {T} rows quantized, {NS} selected per layer")
+
+    def call(ly):
+        m.mla8_decode_sel(ly["codes"], ly["scales"], T, w.lc, w.rc, ly["sel"], ly["ql"], ly["qr"],
+                          w.sm_scale, out=ly["out"], lse=ly["lse"], workspace=ws)
+
+    def step():
+        for ly in layers:
+            call(ly)
+
+    run, ms_step, n_settle, graph = _timed_steps(step, args)
+    ms_lt = ms_step / L
+    log(f"step {ms_step:.4f} ms ({L} layers), {ms_lt * 1e3:.2f} us/layer-token")
+    durs = _event_pass(run, K, layers, call)
+    part_us = float(np.mean(durs))
+    alg_bytes = NS * (w.d + 4) + NS * 4 + w.n_heads * w.d * 4  # gathered rows + scales, indices, q
+    achieved = alg_bytes / (part_us * 1e-6) / 1e9
+    log(f"partial kernel {part_us:.2f} us mean -> {achieved:.0f} GB/s")
+    for ly in layers:
+        assert torch.isfinite(ly["out"]).all() and torch.isfinite(ly["lse"]).all()
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        x = W.rows(w, T, seed_offset=0)
+        oc, os_ = oracle.quantize_rows(x)
+        ql, qr = W.queries(w, seed_offset=0)
+        sel = W.selection(w, seed_offset=0)
+        t0 = time.perf_counter()
+        oracle.decode_sel(oc, os_, T, w.lc, w.rc, sel, ql, qr, w.sm_scale)
+        dt = time.perf_counter() - t0
+        cpu = {"value": round(dt * 1e3, 3), "unit": "ms/layer-token", "cores": oracle.threads(),
+               "kind": "oracle",
+               "sample": f"fp64 attention of all {w.n_heads} heads over the {NS} selected rows "
+                         f"of one layer ({dt:.3f} s)"}
+        log(f"cpu oracle: {cpu}")
+    rec = {
+        "metric": "ms/layer-token, DSA selected-row decode (2048 of T=131072 rows)",
+        "value": round(ms_lt, 6),
+        "unit": "ms/layer-token",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 6),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "e4m3 kv; scores e4m3->f16 rows x f16 hi+lo q (f16 mfma), context f16 weights "
+                 "x e4m3->f16 rows (f16 mfma); f32 accumulate",
+        "data": "synthetic: seeded N(0,1) rows and queries, sorted unique uniform selections",
+        "config": {"workload": w.name, "heads": w.n_heads, "kv_lora": w.lc, "rope": w.rc,
+                   "t_rows": T, "selected": NS, "batch": 1, "layers_per_step": L,
+                   "launch": "hip graph" if graph is not None else "eager"},
+        "clock_settle": {"seconds": SETTLE_S, "untimed_steps": n_settle},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "k_split_partial<9,true>", "kernel_us": round(part_us, 3),
+                     "algorithmic_bytes": alg_bytes,
+                     "note": "latency-bound: 1.19 MB of gathered rows per launch"},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(rec), flush=True)
+
+
+def bench_batch(args):
+    """Causal batch (prefill / streaming): per layer, append 64 fresh rows at
+    pos0 = 32704 of its own shadow (T = 32768), then mla8_batch with S = 64
+    queries, query s attending rows [0, pos0 + s], H = 64.  MFMA-bound."""
+    import numpy as np
+    import torch
+
+    from fp8_mla_latent_amd import mla8 as m
+    from fp8_mla_latent_amd import workloads as W
+
+    w = W.BATCH
+    L, K = args.layers or 8, args.steps
+    T, S = w.t_rows, w.n_q
+    pos0 = T - w.n_append
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    layers = []
+    for l in range(L):
+        x = torch.from_numpy(W.rows(w, T, seed_offset=l)).to(dev)
+        codes = torch.empty((T, w.d), dtype=torch.uint8, device=dev)
+        scales = torch.empty((T,), dtype=torch.float32, device=dev)
+        assert m.mla8_append(codes, scales, 0, x[:pos0], w.lc, w.rc) == pos0
+        fresh = x[pos0:].clone()
+        del x
+        ql, qr = W.queries(w, seed_offset=l)
+        layers.append(dict(codes=codes, scales=scales, fresh=fresh,
+                           ql=torch.from_numpy(ql).to(dev), qr=torch.from_numpy(qr).to(dev),
+                           out=torch.empty((S, w.n_heads, w.lc), dtype=torch.float32, device=dev),
+                           lse=torch.empty((S, w.n_heads), dtype=torch.float32, device=dev)))
+    ws = torch.empty(m.mla8_workspace_bytes(m.MLA8_OP_BATCH, T, w.n_heads, S, w.lc),
+                     dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+    log(f"{L} layers of {pos0} rows quantized; {S} fresh rows appended per step")
+
+    def attend(ly):
+        m.mla8_batch(ly["codes"], ly["scales"], T, w.lc, w.rc, ly["ql"], ly["qr"], pos0,
+                     w.sm_scale, out=ly["out"], lse=ly["lse"], workspace=ws)
+
+    def step():
+        for ly in layers:
+            m.mla8_append(ly["codes"], ly["scales"], pos0, ly["fresh"], w.lc, w.rc)
+            attend(ly)
+
+    run, ms_step, n_settle, graph = _timed_steps(step, args)
+    ms_layer = ms_step / L
+    log(f"step {ms_step:.4f} ms ({L} layers), {ms_layer * 1e3:.1f} us/layer, "
+        f"{ms_layer * 1e3 / S:.2f} us/layer-token")
+    durs = _event_pass(run, K, layers, attend)
+    part_us = float(np.mean(durs))
+    # algorithmic flops of the method (one pass per product): every query-head
+    # scores its rows (2 D flops each) and accumulates them (2 Lc flops each)
+    rows_attended = sum(pos0 + s + 1 for s in range(S))
+    alg_flops = w.n_heads * rows_attended * (2 * w.d + 2 * w.lc)
+    achieved = alg_flops / (part_us * 1e-6) / 1e12
+    log(f"partial kernel {part_us:.1f} us mean -> {achieved:.0f} TFLOP/s "
+        f"({100 * achieved / MFMA_F16_PEAK_TFLOPS:.1f}% of {MFMA_F16_PEAK_TFLOPS:.0f})")
+    for ly in layers:
+        assert torch.isfinite(ly["out"]).all() and torch.isfinite(ly["lse"]).all()
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        nq = 4
+        x = W.rows(w, T, seed_offset=0)
+        oc, os_ = oracle.quantize_rows(x)
+        ql, qr = W.queries(w, seed_offset=0)
+        t0 = time.perf_counter()
+        oracle.batch(oc, os_, T, w.lc, w.rc, np.ascontiguousarray(ql[:nq]),
+                     np.ascontiguousarray(qr[:nq]), pos0, w.sm_scale)
+        dt = time.perf_counter() - t0
+        cpu = {"value": round(dt * 1e3 / nq, 3), "unit": "ms/layer-token",
+               "cores": oracle.threads(), "kind": "oracle",
+               "sample": f"fp64 causal attention of {nq} of the {S} queries (all {w.n_heads} "
+                         f"heads, about {pos0} rows each; {dt:.2f} s), per query-token"}
+        log(f"cpu oracle: {cpu}")
+    rec = {
+        "metric": "ms/layer-token, causal batch (S=64 queries at T=32768) incl. the 64-row append",
+        "value": round(ms_layer / S, 6),
+        "unit": "ms/layer-token",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 6),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "e4m3 kv; scores e4m3->f16 rows x f16 hi+lo q (f16 mfma), context f16 weights "
+                 "x e4m3->f16 rows (f16 mfma); f32 accumulate",
+        "data": "synthetic: seeded N(0,1) rows and queries",
+        "config": {"workload": w.name, "heads": w.n_heads, "kv_lora": w.lc, "rope": w.rc,
+                   "t_rows": T, "queries": S, "pos0": pos0, "layers_per_step": L,
+                   "launch": "hip graph" if graph is not None else "eager"},
+        "ms_per_layer_batch": round(ms_layer, 6),
+        "clock_settle": {"seconds": SETTLE_S, "untimed_steps": n_settle},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2),
+                     "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / MFMA_F16_PEAK_TFLOPS, 4), "traffic": None,
+                     "kernel": "k_split_partial<9,false>", "kernel_us": round(part_us, 3),
+                     "algorithmic_flops": alg_flops,
+                     "note": "flops of one pass per product; the hi + lo query doubles the "
+                             "score MFMAs"},
         "cpu_baseline": cpu,
     }
     print(json.dumps(rec), flush=True)
@@ -537,6 +798,12 @@ def main():
         return
     if args.workload == "kvfile_t262144":
         bench_kvfile(args)
+        return
+    if args.workload == "dsa_t131072_ns2048":
+        bench_dsa(args)
+        return
+    if args.workload == "batch_s64_t32768":
+        bench_batch(args)
         return
     if args.workload == "mixed_t262144":
         bench_mixed(args)
