@@ -176,59 +176,18 @@ def bench_index(args):
     torch.cuda.synchronize()
     log(f"{L} layers of {T} e4m3 key rows quantized")
 
+    def call(ly):
+        m.mla8_index_topk(ly["kc"], ly["ks"], ly["q"], ly["w"], w.n_sel, sel=ly["sel"],
+                          workspace=ws)
+
     def step():
         for ly in layers:
-            m.mla8_index_topk(ly["kc"], ly["ks"], ly["q"], ly["w"], w.n_sel, sel=ly["sel"],
-                              workspace=ws)
+            call(ly)
 
-    for _ in range(max(WU, 1)):
-        step()
-    torch.cuda.synchronize()
-    graph = None
-    if not args.no_graph:
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph):
-            step()
-        torch.cuda.synchronize()
-        run = graph.replay
-    else:
-        run = step
-    n_settle = settle(run, "steps")
-    for _ in range(WU):
-        run()
-    torch.cuda.synchronize()
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(K):
-        run()
-    e1.record()
-    torch.cuda.synchronize()
-    ms_step = e0.elapsed_time(e1) / K
+    run, ms_step, n_settle, graph = _timed_steps(step, args)
     ms_lt = ms_step / L
     log(f"step {ms_step:.4f} ms ({L} layers), {ms_lt * 1e3:.2f} us/layer-token")
-
-    n_ev = K * L
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(n_ev)]
-    for a_, b_ in evs:
-        a_.record()
-        b_.record()
-    torch.cuda.synchronize()
-    for _ in range(30):
-        run()
-    i = 0
-    try:
-        for _ in range(K):
-            for ly in layers:
-                m.mla8_profile_events(*evs[i])
-                m.mla8_index_topk(ly["kc"], ly["ks"], ly["q"], ly["w"], w.n_sel, sel=ly["sel"],
-                                  workspace=ws)
-                i += 1
-    finally:
-        m.mla8_profile_events(None, None)
-    torch.cuda.synchronize()
-    durs = np.array([a.elapsed_time(b) for a, b in evs]) * 1e3
+    durs = _event_pass(run, K, layers, call)
     k_us = float(np.mean(durs))
     key_bytes = T * (w.lc + 4)
     alg_bytes = key_bytes + w.n_heads * w.lc * 4 + w.n_heads * 4  # keys + scales, q, w
@@ -591,62 +550,19 @@ def bench_mixed(args):
     torch.cuda.synchronize()
     log(f"{L} layers of {T - 1} mixed rows quantized")
 
-    def one(ly):
+    def call(ly):
         m.mla8_append_decode_mx(ly["rows"], ly["scales"], T - 1, ly["fresh"], LC, RC, ly["ql"],
                                 ly["qr"], w.sm_scale, out=ly["out"], lse=ly["lse"],
                                 workspace=ws)
 
     def step():
         for ly in layers:
-            one(ly)
+            call(ly)
 
-    for _ in range(max(WU, 1)):
-        step()
-    torch.cuda.synchronize()
-    graph = None
-    if not args.no_graph:
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph):
-            step()
-        torch.cuda.synchronize()
-        run = graph.replay
-    else:
-        run = step
-    n_settle = settle(run, "steps")
-    for _ in range(WU):
-        run()
-    torch.cuda.synchronize()
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(K):
-        run()
-    e1.record()
-    torch.cuda.synchronize()
-    ms_step = e0.elapsed_time(e1) / K
+    run, ms_step, n_settle, graph = _timed_steps(step, args)
     ms_lt = ms_step / L
     log(f"step {ms_step:.4f} ms ({L} layers), {ms_lt * 1e3:.2f} us/layer-token")
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(K * L)]
-    for a_, b_ in evs:
-        a_.record()
-        b_.record()
-    torch.cuda.synchronize()
-    for _ in range(30):
-        run()
-    i = 0
-    try:
-        for _ in range(K):
-            for ly in layers:
-                m.mla8_profile_events(*evs[i])
-                m.mla8_append_decode_mx(ly["rows"], ly["scales"], T - 1, ly["fresh"], LC, RC,
-                                        ly["ql"], ly["qr"], w.sm_scale, out=ly["out"],
-                                        lse=ly["lse"], workspace=ws)
-                i += 1
-    finally:
-        m.mla8_profile_events(None, None)
-    torch.cuda.synchronize()
-    durs = np.array([a.elapsed_time(b) for a, b in evs]) * 1e3
+    durs = _event_pass(run, K, layers, call)
     part_us = float(np.mean(durs))
     row_bytes = T * (RB + 4)
     alg_bytes = row_bytes + w.n_heads * (LC + RC) * 4
