@@ -849,6 +849,10 @@ def main():
     for ly in layers:
         assert torch.isfinite(ly["out"]).all() and torch.isfinite(ly["lse"]).all()
 
+    ceiling = stream_ceiling([ly["codes"] for ly in layers])
+    log(f"stream-read ceiling {ceiling['gb_per_s']:.0f} GB/s; the partial kernel reaches "
+        f"{100 * achieved / ceiling['gb_per_s']:.1f}% of it")
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(w, args.cpu_heads)
@@ -874,9 +878,36 @@ def main():
         "kv_stream_gb_per_s": round(kv_bytes / (ms_lt * 1e-3) / 1e9, 1),
         "clock_settle": {"seconds": SETTLE_S, "untimed_steps": n_settle},
         "roofline": roofline,
+        "stream_ceiling": dict(ceiling, kernel_frac=round(achieved / ceiling["gb_per_s"], 4)),
         "cpu_baseline": cpu,
     }
     print(json.dumps(rec), flush=True)
+
+
+def stream_ceiling(bufs, passes=10):
+    """The achievable-HBM line: mla8_stream_read over the same layer shadows
+    (every 16-byte word loaded once per pass, coalesced), timed with events
+    over `passes` passes after one untimed pass."""
+    import torch
+
+    from fp8_mla_latent_amd import mla8 as m
+
+    out = torch.empty((m.MLA8_STREAM_WORDS,), dtype=torch.int32, device=bufs[0].device)
+    for b in bufs:
+        m.mla8_stream_read(b, out)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(passes):
+        for b in bufs:
+            m.mla8_stream_read(b, out)
+    e1.record()
+    torch.cuda.synchronize()
+    nbytes = sum(b.numel() * b.element_size() for b in bufs)
+    gbs = passes * nbytes / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    return {"gb_per_s": round(gbs, 1), "bytes_per_pass": nbytes, "passes": passes,
+            "kernel": "k_stream_read (mla8_stream_read): 16-byte coalesced loads, XOR-folded per wave"}
 
 
 if __name__ == "__main__":

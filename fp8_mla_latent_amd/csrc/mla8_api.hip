@@ -532,6 +532,18 @@ int mla8_profile_events(void* before, void* after)
 
 const char* mla8_version(void) { return "mla8 0.1.0 gfx950"; }
 
+static_assert(kStreamWords == MLA8_STREAM_WORDS, "stream-read output words");
+
+int mla8_stream_read(const void* p, int64_t bytes, uint32_t* out, void* stream)
+{
+    if (!p || !out || bytes < 0 || (bytes & 15) != 0 ||
+        (reinterpret_cast<uintptr_t>(p) & 15) != 0 || (reinterpret_cast<uintptr_t>(out) & 15) != 0)
+        return MLA8_E_INVAL;
+    return launch_stream_read(p, bytes, out, static_cast<hipStream_t>(stream)) == hipSuccess
+               ? MLA8_OK
+               : MLA8_E_HIP;
+}
+
 int mla8_test_encode(const float* x, int64_t n, uint8_t* codes, void* stream)
 {
     if (!x || !codes || n < 0)

@@ -1332,6 +1332,49 @@ hipError_t launch_quantize_mx(const float* x, int64_t n_rows, int32_t lc, int32_
     return hipGetLastError();
 }
 
+// Read-bandwidth reference, a measurement aid outside the attention path:
+// every 16-byte word of the buffer is loaded once (coalesced, grid-stride,
+// eight loads in flight per thread; of the shapes measured, 8 loads x 8192
+// workgroups read fastest) and XOR-folded.  Wave v of workgroup b stores its
+// fold to out[4 b + v] (plain stores, one word per wave, so no two waves meet
+// on an address) and every wave stores, so the XOR of all kStreamWords words
+// is the XOR of the buffer's 32-bit words (the grid is kStreamWords / 4
+// workgroups of 4 waves).
+constexpr int kStreamBlocks = kStreamWords / 4;
+
+__global__ __launch_bounds__(256) void k_stream_read(const uint4* __restrict__ p, int64_t n16,
+                                                     uint32_t* __restrict__ out)
+{
+    const int64_t stride = (int64_t)gridDim.x * 256;
+    int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    uint32_t x = 0;
+    for (; i + 7 * stride < n16; i += 8 * stride) {
+        uint4 v[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k)
+            v[k] = p[i + k * stride];
+#pragma unroll
+        for (int k = 0; k < 8; ++k)
+            x ^= v[k].x ^ v[k].y ^ v[k].z ^ v[k].w;
+    }
+    for (; i < n16; i += stride) {
+        const uint4 a = p[i];
+        x ^= a.x ^ a.y ^ a.z ^ a.w;
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1)
+        x ^= (uint32_t)__shfl_xor((int)x, o);
+    if ((threadIdx.x & 63) == 0)
+        out[4 * blockIdx.x + (threadIdx.x >> 6)] = x;
+}
+
+hipError_t launch_stream_read(const void* p, int64_t bytes, uint32_t* out, hipStream_t stream)
+{
+    hipLaunchKernelGGL(k_stream_read, dim3(kStreamBlocks), dim3(256), 0, stream,
+                       static_cast<const uint4*>(p), bytes / 16, out);
+    return hipGetLastError();
+}
+
 hipError_t launch_test_encode(const float* x, int64_t n, uint8_t* codes, hipStream_t stream)
 {
     int64_t blocks = (n + 255) / 256;

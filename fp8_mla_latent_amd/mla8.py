@@ -33,7 +33,8 @@ EXPORTED = ("mla8_quantize_rows", "mla8_append", "mla8_decode", "mla8_append_dec
             "mla8_index_topk", "mla8_kvfile_create",
             "mla8_kvfile_info", "mla8_kvfile_append", "mla8_kvfile_load",
             "mla8_workspace_bytes", "mla8_force_splits", "mla8_plan_splits",
-            "mla8_status_string", "mla8_version", "mla8_test_encode", "mla8_profile_events")
+            "mla8_status_string", "mla8_version", "mla8_test_encode", "mla8_profile_events",
+            "mla8_stream_read")
 
 
 class Mla8Error(RuntimeError):
@@ -84,6 +85,7 @@ def _load() -> ctypes.CDLL:
         "mla8_status_string": (ctypes.c_char_p, [ctypes.c_int]),
         "mla8_version": (ctypes.c_char_p, []),
         "mla8_test_encode": (ctypes.c_int, [P, i64, P, P]),
+        "mla8_stream_read": (ctypes.c_int, [P, i64, P, P]),
         "mla8_profile_events": (ctypes.c_int, [P, P]),
     }
     for name, (res, args) in sig.items():
@@ -389,6 +391,19 @@ def mla8_profile_events(before: "torch.cuda.Event | None", after: "torch.cuda.Ev
             raise ValueError("mla8_profile_events: record the event once first")
         return ev.cuda_event
     _check(lib.mla8_profile_events(raw(before), raw(after)), "mla8_profile_events")
+
+
+MLA8_STREAM_WORDS = 32768
+
+
+def mla8_stream_read(t: torch.Tensor, out: torch.Tensor) -> None:
+    """Load every byte of the device tensor t once, XOR-folding its 32-bit
+    words into out (int32 [MLA8_STREAM_WORDS] on the device, one fold per
+    wave; their XOR is the buffer's): the read-bandwidth reference."""
+    if out.numel() * out.element_size() < 4 * MLA8_STREAM_WORDS:
+        raise ValueError("mla8_stream_read: out needs MLA8_STREAM_WORDS 32-bit words")
+    _check(lib.mla8_stream_read(_ptr(t), t.numel() * t.element_size(), _ptr(out), _stream(t)),
+           "mla8_stream_read")
 
 
 def mla8_test_encode(x: torch.Tensor, codes: torch.Tensor | None = None) -> torch.Tensor:

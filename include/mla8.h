@@ -346,6 +346,21 @@ MLA8_API const char* mla8_status_string(int status);
 MLA8_API const char* mla8_version(void);
 
 /*
+ * Measurement aid, not part of the attention path: the read-bandwidth
+ * reference that the decode's HBM rate is compared with.  Loads every 16-byte
+ * word of [p, p + bytes) once (coalesced, grid-stride) and XOR-folds them:
+ * out (device memory, MLA8_STREAM_WORDS uint32, 16-byte aligned) receives one
+ * fold per wave, every word written, so that the XOR of all its words is the
+ * XOR of the buffer's 32-bit words and no load can be dropped.  p: device
+ * pointer, 16-byte aligned; bytes a multiple of 16.  Enqueues on `stream`
+ * and returns.
+ * Errors: E_INVAL (NULL pointer, misalignment, bytes < 0 or not a multiple of
+ * 16), E_HIP.
+ */
+#define MLA8_STREAM_WORDS 32768
+MLA8_API int mla8_stream_read(const void* p, int64_t bytes, uint32_t* out, void* stream);
+
+/*
  * Not part of the product API: apply the device e4m3 encoder elementwise,
  * codes[i] = enc(x[i]) for i < n, with no scaling.  Exported so that tests can
  * compare the device encoder with the reference on every f32 bit pattern,

@@ -240,3 +240,13 @@ def test_mixed_step_and_batch_refuse():
         args = list(base)
         args[idx] = val
         assert b(*args) == want, (idx, val)
+
+
+def test_stream_read_refuses():
+    f = m.lib.mla8_stream_read
+    assert f(None, 64, FAKE, None) == m.MLA8_E_INVAL
+    assert f(FAKE, 64, None, None) == m.MLA8_E_INVAL
+    assert f(FAKE_MISALIGNED, 64, FAKE, None) == m.MLA8_E_INVAL
+    assert f(FAKE, 40, FAKE, None) == m.MLA8_E_INVAL      # not a multiple of 16
+    assert f(FAKE, -16, FAKE, None) == m.MLA8_E_INVAL
+    assert f(FAKE, 64, FAKE_MISALIGNED, None) == m.MLA8_E_INVAL

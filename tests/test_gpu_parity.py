@@ -379,3 +379,16 @@ def test_long_context_sampled(m):
     heads = np.array([0, 21, 63])
     ro, rl = oracle.decode(oc, os_, t, w.lc, w.rc, ql[heads], qr[heads], w.sm_scale)
     check_attention(o[heads], ro, l[heads], rl, w.name)
+
+
+# The read-bandwidth reference: every 32-bit word of the buffer reaches the
+# XOR fold (so no load can be dropped), for sizes below, at and past one
+# 4-load round of the grid and with a tail.
+@pytest.mark.parametrize("nbytes", [16, 4096, 999_984, 33_554_432 + 48])
+def test_stream_read_folds_every_word(m, nbytes):
+    g = np.random.Generator(np.random.PCG64(nbytes))
+    h = g.integers(0, 2**32, nbytes // 4, dtype=np.uint64).astype(np.uint32)
+    out = torch.full((m.MLA8_STREAM_WORDS,), -1, dtype=torch.int32, device=DEV)
+    m.mla8_stream_read(dev(h.view(np.uint8)), out)
+    got = int(np.bitwise_xor.reduce(host(out).view(np.uint32)))
+    assert got == int(np.bitwise_xor.reduce(h))
