@@ -1236,17 +1236,29 @@ __global__ __launch_bounds__(kThreads, 1) void k_split_partial(AttnArgs a)
 
 // ---------------------------------------------------------------------------
 // Log-sum-exp merge of the n_chunks partials of every query-head.
-// Grid (n_qh, ceil(lc / 128)), 512 threads: lane = two adjacent context
-// columns (one 8-byte load per partial; lc is a multiple of 16); wave wv folds
-// partials p = wv, wv + 8, ... with an online maximum, kMergeBatch partials
-// per batch whose loads are all issued before any is used (one batch covers
-// 128 partials); the eight waves then combine through LDS:
+// 512 threads = 8 waves; lane = two adjacent context columns (one 8-byte load
+// per partial; lc is a multiple of 16).  The waves split into slabs of W =
+// min(8, n_chunks rounded up to a power of two) waves: a slab covers 128
+// columns and its waves fold partials p = c, c + W, ... (c = the wave's rank
+// in the slab) with an online maximum, kMergeBatch partials per batch whose
+// loads are all issued before any is used; each slab's waves then combine
+// through LDS.  Grid (n_qh, ceil(lc / (128 * 8 / W))).  A few partials (the
+// causal batch's 2 chunks) thus fill the waves with columns instead of
+// leaving them idle.
 //   M = max_p m_p;  w_p = 2^(m_p - M);  out = sum_p w_p cl_p / sum_p w_p z_p;
 //   lse = (M + log2 sum_p w_p z_p) * ln 2.
 // Measured against one column per lane and four waves (two batches of 16 per
 // wave): 1.3 us less per decode call at the long-context shape.
 constexpr int kMergeBatch = 16;
 constexpr int kMergeWaves = 8;
+
+__host__ __device__ __forceinline__ int merge_slab_waves(int n_chunks)
+{
+    int w = 1;
+    while (w < n_chunks && w < kMergeWaves)
+        w <<= 1;
+    return w;
+}
 
 __global__ __launch_bounds__(64 * kMergeWaves) void k_merge(const float* __restrict__ ws_m,
                                                             const float* __restrict__ ws_z,
@@ -1260,16 +1272,18 @@ __global__ __launch_bounds__(64 * kMergeWaves) void k_merge(const float* __restr
     __shared__ float s_mw[kMergeWaves];
     const int qh = blockIdx.x;
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-    const int col = blockIdx.y * 128 + 2 * lane;
+    const int W = merge_slab_waves(n_chunks);
+    const int slab = wv / W, wc = wv - slab * W;
+    const int col = (blockIdx.y * (kMergeWaves / W) + slab) * 128 + 2 * lane;
     const bool cv = col < lc;  // lc even: both columns or neither
     float mw = -INFINITY, zw = 0.0f;
     float2 aw = make_float2(0.0f, 0.0f);
-    for (int base = wv; base < n_chunks; base += kMergeWaves * kMergeBatch) {
+    for (int base = wc; base < n_chunks; base += W * kMergeBatch) {
         float mp[kMergeBatch], zp[kMergeBatch];
         float2 cp[kMergeBatch];
 #pragma unroll
         for (int k = 0; k < kMergeBatch; ++k) {
-            const int pp = base + kMergeWaves * k;
+            const int pp = base + W * k;
             const bool ok = pp < n_chunks;
             const size_t i = (size_t)(ok ? pp : 0) * n_qh + qh;
             mp[k] = ok ? ws_m[i] : -INFINITY;
@@ -1304,20 +1318,19 @@ __global__ __launch_bounds__(64 * kMergeWaves) void k_merge(const float* __restr
         s_mw[wv] = mw;
     }
     __syncthreads();
-    if (wv == 0) {
-        float M = s_mw[0];
-#pragma unroll
-        for (int k = 1; k < kMergeWaves; ++k)
-            M = fmaxf(M, s_mw[k]);
+    if (wc == 0) {
+        const int w0 = slab * W;
+        float M = s_mw[w0];
+        for (int k = 1; k < W; ++k)
+            M = fmaxf(M, s_mw[w0 + k]);
         float2 A = make_float2(0.0f, 0.0f);
         float Z = 0.0f;
         if (M != -INFINITY) {
-#pragma unroll
-            for (int k = 0; k < kMergeWaves; ++k) {
-                const float wk = (s_mw[k] == -INFINITY) ? 0.0f : exp2f(s_mw[k] - M);
-                A.x += wk * s_a[k][lane].x;
-                A.y += wk * s_a[k][lane].y;
-                Z += wk * s_zw[k];
+            for (int k = 0; k < W; ++k) {
+                const float wk = (s_mw[w0 + k] == -INFINITY) ? 0.0f : exp2f(s_mw[w0 + k] - M);
+                A.x += wk * s_a[w0 + k][lane].x;
+                A.y += wk * s_a[w0 + k][lane].y;
+                Z += wk * s_zw[w0 + k];
             }
         }
         if (cv) {
@@ -1325,7 +1338,7 @@ __global__ __launch_bounds__(64 * kMergeWaves) void k_merge(const float* __restr
                                               : make_float2(A.x / Z, A.y / Z);
             *reinterpret_cast<float2*>(out + (size_t)qh * lc + col) = o;
         }
-        if (lse != nullptr && blockIdx.y == 0 && lane == 0)
+        if (lse != nullptr && blockIdx.y == 0 && slab == 0 && lane == 0)
             lse[qh] = (M == -INFINITY) ? -INFINITY : (M + log2f(Z)) * 0.69314718055994531f;
     }
 }
@@ -1462,7 +1475,8 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t stream, hipEvent_t ev
         if (e != hipSuccess)
             return e;
     }
-    hipLaunchKernelGGL(k_merge, dim3((unsigned)a.n_qh, (unsigned)((a.lc + 127) / 128)),
+    const int cols = 128 * (kMergeWaves / merge_slab_waves(a.n_chunks));  // columns per workgroup
+    hipLaunchKernelGGL(k_merge, dim3((unsigned)a.n_qh, (unsigned)((a.lc + cols - 1) / cols)),
                        dim3(64 * kMergeWaves), 0,
                        stream, a.ws_m, a.ws_z, a.ws_cl, a.n_chunks, a.n_qh, a.lc, a.out, a.lse);
     return hipGetLastError();
