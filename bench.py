@@ -66,15 +66,20 @@ def parse():
     ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of a graph")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=16,
-                    help="heads of the CPU-oracle sample (full T, scaled to 64 heads)")
+                    help="heads of the CPU-oracle sample on all threads (full T, scaled to 64 "
+                         "heads; also the heads of layer 0 checked against the oracle)")
+    ap.add_argument("--cpu-heads-one-core", type=int, default=2,
+                    help="heads of the one-thread CPU-oracle sample (full T, scaled)")
     ap.add_argument("--traffic", type=str,
                     default=os.path.join(ROOT, "profiles", "k_split_partial_long_t262144_traffic.txt"),
                     help="calibrated rocprofv3 FETCH_SIZE + WRITE_SIZE bytes per partial launch "
                          "(JSON); used only while the kernel source still matches its hash")
     ap.add_argument("--workload", default="long_t262144",
-                    choices=["long_t262144", "dsa_index_t131072_k2048", "kvfile_t262144",
+                    choices=["long_t262144", "dsv3_t4096", "dsa_index_t131072_k2048",
+                             "kvfile_t262144",
                              "mixed_t262144", "dsa_t131072_ns2048", "batch_s64_t32768"],
                     help="long_t262144: the fused append + split-T decode step (default); "
+                         "dsv3_t4096: the same step at the DeepSeek-V3 shape (H=128, T=4096); "
                          "dsa_index_t131072_k2048: the fp8 indexer score + top-k; "
                          "kvfile_t262144: resume a persisted shadow file into device shadows; "
                          "mixed_t262144: the decode step over mixed rows (noPE e4m3 448 + RoPE "
@@ -85,10 +90,29 @@ def parse():
     return ap.parse_args()
 
 
-def cpu_baseline(w, heads):
-    """The oracle (as it stands) on a bounded sample of the same step: quantize
-    one fresh row, then dense fp64 attention of `heads` heads over all T rows.
-    Scaled to the full 64-head layer-token."""
+def host_info():
+    """What the CPU baseline ran on: logical CPUs, the ones this process may
+    use, and the CPU model."""
+    model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return {"nproc": os.cpu_count(), "affinity_cpus": len(os.sched_getaffinity(0)),
+            "cpu_model": model}
+
+
+def cpu_baseline(w, heads, heads_one_core, runs=3):
+    """The oracle (as it stands) on bounded samples of the same step: quantize
+    the fresh row into row T-1, then dense fp64 attention over all T rows for
+    `heads` heads with every OpenMP thread, and for `heads_one_core` heads on
+    one thread; `runs` runs of each, the median scaled to the full 64-head
+    layer-token.  The inputs are layer 0's (the same seeds as the GPU's layer
+    0), so the all-threads run's outputs also check the GPU's layer-0 result.
+    Returns (record, (out, lse) of heads 0 .. heads-1)."""
     import numpy as np
 
     import oracle
@@ -99,16 +123,40 @@ def cpu_baseline(w, heads):
     codes = np.concatenate([codes, np.zeros((1, w.d), np.uint8)])
     scales = np.concatenate([scales, np.zeros(1, np.float32)])
     ql, qr = W.queries(w, seed_offset=0)
-    t0 = time.perf_counter()
-    c1, s1 = oracle.quantize_rows(x[-1:])
-    codes[-1], scales[-1] = c1[0], s1[0]
-    oracle.decode(codes, scales, w.t_rows, w.lc, w.rc, ql[:heads], qr[:heads], w.sm_scale)
-    dt = time.perf_counter() - t0
-    ms = dt * 1e3 * (w.n_heads / heads)
-    return {"value": round(ms, 3), "unit": "ms/layer-token", "cores": oracle.threads(),
-            "kind": "oracle",
-            "sample": f"append 1 row + fp64 attention of {heads} of {w.n_heads} heads over "
-                      f"T={w.t_rows} rows ({dt:.2f} s), scaled x{w.n_heads / heads:g} to all heads"}
+
+    def one(nh):
+        t0 = time.perf_counter()
+        c1, s1 = oracle.quantize_rows(x[-1:])
+        codes[-1], scales[-1] = c1[0], s1[0]
+        res = oracle.decode(codes, scales, w.t_rows, w.lc, w.rc, ql[:nh], qr[:nh], w.sm_scale)
+        return time.perf_counter() - t0, res
+
+    oracle.set_threads(0)
+    threads = oracle.threads()
+    t_all, res = [], None
+    for _ in range(runs):
+        dt, res = one(heads)
+        t_all.append(dt)
+    oracle.set_threads(1)
+    try:
+        t_one = [one(heads_one_core)[0] for _ in range(runs)]
+    finally:
+        oracle.set_threads(0)
+    ms_all = float(np.median(t_all)) * 1e3 * (w.n_heads / heads)
+    ms_one = float(np.median(t_one)) * 1e3 * (w.n_heads / heads_one_core)
+    info = host_info()
+    rec = {"value": round(ms_all, 3), "unit": "ms/layer-token", "cores": threads,
+           "kind": "oracle",
+           "sample": f"append 1 row + fp64 attention of {heads} of {w.n_heads} heads over "
+                     f"T={w.t_rows} rows on {threads} OpenMP threads, median of {runs} runs "
+                     f"({', '.join(f'{t:.2f}' for t in t_all)} s), scaled "
+                     f"x{w.n_heads / heads:g} to all heads",
+           "one_core": {"value": round(ms_one, 3), "unit": "ms/layer-token", "cores": 1,
+                        "sample": f"{heads_one_core} of {w.n_heads} heads on 1 thread, median "
+                                  f"of {runs} runs ({', '.join(f'{t:.2f}' for t in t_one)} s), "
+                                  f"scaled x{w.n_heads / heads_one_core:g}"},
+           **info}
+    return rec, res
 
 
 def settle(run, log_name):
@@ -176,9 +224,9 @@ def bench_index(args):
     torch.cuda.synchronize()
     log(f"{L} layers of {T} e4m3 key rows quantized")
 
-    def call(ly):
+    def call(ly, events=None):
         m.mla8_index_topk(ly["kc"], ly["ks"], ly["q"], ly["w"], w.n_sel, sel=ly["sel"],
-                          workspace=ws)
+                          workspace=ws, events=events)
 
     def step():
         for ly in layers:
@@ -250,14 +298,10 @@ def _event_pass(run, K, layers, call):
     for _ in range(30):
         run()
     i = 0
-    try:
-        for _ in range(K):
-            for ly in layers:
-                m.mla8_profile_events(*evs[i])
-                call(ly)
-                i += 1
-    finally:
-        m.mla8_profile_events(None, None)
+    for _ in range(K):
+        for ly in layers:
+            call(ly, events=evs[i])
+            i += 1
     torch.cuda.synchronize()
     return np.array([a.elapsed_time(b) for a, b in evs]) * 1e3
 
@@ -325,9 +369,9 @@ def bench_dsa(args):
     torch.cuda.synchronize()
     log(f"{L} layers of {T} rows quantized, {NS} selected per layer")
 
-    def call(ly):
+    def call(ly, events=None):
         m.mla8_decode_sel(ly["codes"], ly["scales"], T, w.lc, w.rc, ly["sel"], ly["ql"], ly["qr"],
-                          w.sm_scale, out=ly["out"], lse=ly["lse"], workspace=ws)
+                          w.sm_scale, out=ly["out"], lse=ly["lse"], workspace=ws, events=events)
 
     def step():
         for ly in layers:
@@ -386,6 +430,117 @@ def bench_dsa(args):
     print(json.dumps(rec), flush=True)
 
 
+def bench_dsv3(args):
+    """DeepSeek-V3-shaped decode step: per layer, one mla8_append_decode call
+    that quantizes the fresh row into row T-1 of its own shadow (T = 4096, 1 %
+    of rows scaled x50) and attends all 4096 rows with H = 128 heads.  A 2.4 MB
+    shadow per layer: MFMA- and launch-bound, not HBM-bound."""
+    import numpy as np
+    import torch
+
+    from fp8_mla_latent_amd import mla8 as m
+    from fp8_mla_latent_amd import workloads as W
+
+    w = W.DSV3
+    L, K = args.layers or 8, args.steps
+    T = w.t_rows
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    layers = []
+    for l in range(L):
+        x = torch.from_numpy(W.rows(w, T, seed_offset=l)).to(dev)
+        codes = torch.empty((T, w.d), dtype=torch.uint8, device=dev)
+        scales = torch.empty((T,), dtype=torch.float32, device=dev)
+        assert m.mla8_append(codes, scales, 0, x[:T - 1], w.lc, w.rc) == T - 1
+        fresh = x[T - 1:].clone()
+        del x
+        ql, qr = W.queries(w, seed_offset=l)
+        layers.append(dict(codes=codes, scales=scales, fresh=fresh,
+                           ql=torch.from_numpy(ql).to(dev), qr=torch.from_numpy(qr).to(dev),
+                           out=torch.empty((w.n_heads, w.lc), dtype=torch.float32, device=dev),
+                           lse=torch.empty((w.n_heads,), dtype=torch.float32, device=dev)))
+    ws = torch.empty(m.mla8_workspace_bytes(m.MLA8_OP_DECODE, T, w.n_heads, 1, w.lc),
+                     dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+    log(f"{L} layers of {T - 1} rows quantized")
+
+    def call(ly, events=None):
+        m.mla8_append_decode(ly["codes"], ly["scales"], T - 1, ly["fresh"], w.lc, w.rc,
+                             ly["ql"], ly["qr"], w.sm_scale, out=ly["out"], lse=ly["lse"],
+                             workspace=ws, events=events)
+
+    def step():
+        for ly in layers:
+            call(ly)
+
+    run, ms_step, n_settle, graph = _timed_steps(step, args)
+    ms_lt = ms_step / L
+    log(f"step {ms_step:.4f} ms ({L} layers), {ms_lt * 1e3:.2f} us/layer-token")
+    durs = _event_pass(run, K, layers, call)
+    part_us = float(np.mean(durs))
+    # the method's flops, one pass per product: scores over D, context over Lc
+    flops = 2.0 * w.n_heads * T * (w.d + w.lc)
+    tflops = flops / (part_us * 1e-6) / 1e12
+    log(f"partial kernel {part_us:.2f} us mean -> {tflops:.0f} TFLOP/s")
+    for ly in layers:
+        assert torch.isfinite(ly["out"]).all() and torch.isfinite(ly["lse"]).all()
+    cpu, parity = None, None
+    if not args.no_cpu_baseline:
+        import oracle
+        x = W.rows(w, T, seed_offset=0)
+        oc, os_ = oracle.quantize_rows(x)
+        ql, qr = W.queries(w, seed_offset=0)
+        times = []
+        for _ in range(3):
+            t0 = time.perf_counter()
+            ro, rl = oracle.decode(oc, os_, T, w.lc, w.rc, ql, qr, w.sm_scale)
+            times.append(time.perf_counter() - t0)
+        dt = float(np.median(times))
+        cpu = {"value": round(dt * 1e3, 3), "unit": "ms/layer-token", "cores": oracle.threads(),
+               "kind": "oracle",
+               "sample": f"fp64 attention of all {w.n_heads} heads over the {T} rows of one "
+                         f"layer, median of 3 runs", **host_info()}
+        log(f"cpu oracle: {cpu}")
+        # layer 0 against the oracle (outlier rows: the per-vector reading)
+        g = layers[0]["out"].double().cpu().numpy()
+        err = np.abs(g - ro).max(1)
+        bar = 1e-4 + 2e-3 * np.abs(ro).max(1)
+        parity = {"layer": 0, "heads_checked": w.n_heads,
+                  "worst_err_over_bar": round(float((err / bar).max()), 4),
+                  "form": "per (head) output vector", "ok": bool(np.all(err <= bar))}
+        log(f"layer-0 parity vs oracle: {parity}")
+        if not parity["ok"]:
+            raise SystemExit(f"bench.py: layer-0 output differs from the oracle: {parity}")
+    rec = {
+        "metric": "ms/layer-token, DeepSeek-V3-shaped decode (H=128, T=4096)",
+        "value": round(ms_lt, 6),
+        "unit": "ms/layer-token",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 6),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "e4m3 kv; scores e4m3->f16 rows x f16 hi+lo q (f16 mfma), context f16 weights "
+                 "x e4m3->f16 rows (f16 mfma); f32 accumulate",
+        "data": "synthetic: seeded N(0,1) rows (1 % of rows x50) and queries",
+        "config": {"workload": w.name, "heads": w.n_heads, "kv_lora": w.lc, "rope": w.rc,
+                   "t_rows": T, "batch": 1, "layers_per_step": L,
+                   "launch": "hip graph" if graph is not None else "eager",
+                   "splits": m.mla8_plan_splits(m.MLA8_OP_DECODE, T, w.n_heads)},
+        "clock_settle": {"seconds": SETTLE_S, "untimed_steps": n_settle},
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 1),
+                     "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(tflops / MFMA_F16_PEAK_TFLOPS, 4), "traffic": None,
+                     "kernel": "k_split_partial<9,false>", "kernel_us": round(part_us, 3),
+                     "algorithmic_flops": flops},
+        "cpu_baseline": cpu,
+        "parity": parity,
+    }
+    print(json.dumps(rec), flush=True)
+
+
 def bench_batch(args):
     """Causal batch (prefill / streaming): per layer, append 64 fresh rows at
     pos0 = 32704 of its own shadow (T = 32768), then mla8_batch with S = 64
@@ -420,9 +575,9 @@ def bench_batch(args):
     torch.cuda.synchronize()
     log(f"{L} layers of {pos0} rows quantized; {S} fresh rows appended per step")
 
-    def attend(ly):
+    def attend(ly, events=None):
         m.mla8_batch(ly["codes"], ly["scales"], T, w.lc, w.rc, ly["ql"], ly["qr"], pos0,
-                     w.sm_scale, out=ly["out"], lse=ly["lse"], workspace=ws)
+                     w.sm_scale, out=ly["out"], lse=ly["lse"], workspace=ws, events=events)
 
     def step():
         for ly in layers:
@@ -550,10 +705,10 @@ def bench_mixed(args):
     torch.cuda.synchronize()
     log(f"{L} layers of {T - 1} mixed rows quantized")
 
-    def call(ly):
+    def call(ly, events=None):
         m.mla8_append_decode_mx(ly["rows"], ly["scales"], T - 1, ly["fresh"], LC, RC, ly["ql"],
                                 ly["qr"], w.sm_scale, out=ly["out"], lse=ly["lse"],
-                                workspace=ws)
+                                workspace=ws, events=events)
 
     def step():
         for ly in layers:
@@ -718,6 +873,9 @@ def main():
     if args.workload == "dsa_t131072_ns2048":
         bench_dsa(args)
         return
+    if args.workload == "dsv3_t4096":
+        bench_dsv3(args)
+        return
     if args.workload == "batch_s64_t32768":
         bench_batch(args)
         return
@@ -812,16 +970,12 @@ def main():
     for _ in range(30):
         run()
     i = 0
-    try:
-        for _ in range(K):
-            for ly in layers:
-                m.mla8_profile_events(*evs[i])
-                m.mla8_append_decode(ly["codes"], ly["scales"], T - 1, ly["fresh"], w.lc,
-                                     w.rc, ly["ql"], ly["qr"], w.sm_scale, out=ly["out"],
-                                     lse=ly["lse"], workspace=ws)
-                i += 1
-    finally:
-        m.mla8_profile_events(None, None)
+    for _ in range(K):
+        for ly in layers:
+            m.mla8_append_decode(ly["codes"], ly["scales"], T - 1, ly["fresh"], w.lc,
+                                 w.rc, ly["ql"], ly["qr"], w.sm_scale, out=ly["out"],
+                                 lse=ly["lse"], workspace=ws, events=evs[i])
+            i += 1
     torch.cuda.synchronize()
     durs = np.array([a.elapsed_time(b) for a, b in evs]) * 1e3  # us
     part_us = float(np.mean(durs))
@@ -845,7 +999,7 @@ def main():
     log(f"partial kernel {part_us:.2f} us mean -> {achieved:.0f} GB/s "
         f"({100 * achieved / HBM_PEAK_GBS:.1f}% of {HBM_PEAK_GBS:.0f})")
 
-    # sanity: outputs finite
+    # every layer's output finite; layer 0 against the oracle below
     for ly in layers:
         assert torch.isfinite(ly["out"]).all() and torch.isfinite(ly["lse"]).all()
 
@@ -853,10 +1007,22 @@ def main():
     log(f"stream-read ceiling {ceiling['gb_per_s']:.0f} GB/s; the partial kernel reaches "
         f"{100 * achieved / ceiling['gb_per_s']:.1f}% of it")
 
-    cpu = None
+    cpu, parity = None, None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(w, args.cpu_heads)
+        cpu, (ro, rl) = cpu_baseline(w, args.cpu_heads, args.cpu_heads_one_core)
         log(f"cpu oracle: {cpu}")
+        # layer 0's last step against the oracle on the same inputs, elementwise
+        # (|gpu - ref| <= 1e-4 + 2e-3 |ref|), for the heads the oracle ran
+        g = layers[0]["out"][:args.cpu_heads].double().cpu().numpy()
+        gl = layers[0]["lse"][:args.cpu_heads].double().cpu().numpy()
+        ratio = float((np.abs(g - ro) / (1e-4 + 2e-3 * np.abs(ro))).max())
+        lratio = float((np.abs(gl - rl) / (1e-4 + 2e-3 * np.abs(rl))).max())
+        parity = {"layer": 0, "heads_checked": args.cpu_heads,
+                  "worst_err_over_bar": round(ratio, 4), "lse_worst_err_over_bar":
+                  round(lratio, 4), "ok": ratio <= 1.0 and lratio <= 1.0}
+        log(f"layer-0 parity vs oracle: {parity}")
+        if not parity["ok"]:
+            raise SystemExit(f"bench.py: layer-0 output differs from the oracle: {parity}")
 
     rec = {
         "metric": METRIC,
@@ -880,6 +1046,7 @@ def main():
         "roofline": roofline,
         "stream_ceiling": dict(ceiling, kernel_frac=round(achieved / ceiling["gb_per_s"], 4)),
         "cpu_baseline": cpu,
+        "parity": parity,
     }
     print(json.dumps(rec), flush=True)
 

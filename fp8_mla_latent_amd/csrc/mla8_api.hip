@@ -2,6 +2,7 @@
 // split planning, workspace carving and kernel launches.  Every check runs on
 // the host before any HIP call, so the error paths work without a GPU.
 #include "mla8.h"
+#include "mla8_aux.h"
 #include "mla8_internal.h"
 
 #include <math.h>
@@ -10,10 +11,6 @@
 namespace {
 
 using namespace mla8;
-
-int32_t g_forced_splits = 0;
-hipEvent_t g_ev_before = nullptr;
-hipEvent_t g_ev_after = nullptr;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -36,17 +33,22 @@ struct Plan {
 
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+int32_t forced_splits(const mla8_opts* o) { return (o != nullptr && o->n_splits > 0) ? o->n_splits : 0; }
+hipEvent_t ev_before(const mla8_opts* o) { return o ? static_cast<hipEvent_t>(o->ev_before) : nullptr; }
+hipEvent_t ev_after(const mla8_opts* o) { return o ? static_cast<hipEvent_t>(o->ev_after) : nullptr; }
+
 // Row chunks for a call that attends `rows` rows with `n_qh` query-heads.
 // Aim for one workgroup per CU; prefer a multiple of 8 chunks (one per XCD
 // round); keep chunks at least 256 rows (64 for a gather), so that the partial
 // (m, z, cl) traffic stays small next to the rows it summarises.
-Plan make_plan(int32_t op, int64_t rows, int32_t n_qh)
+// forced > 0: that many chunks (clamped below), the caller's per-call option.
+Plan make_plan(int32_t op, int64_t rows, int32_t n_qh, int32_t forced)
 {
     Plan p;
     p.n_groups = (int32_t)cdiv(n_qh, kHeadsPerGroup);
     int64_t P;
-    if (g_forced_splits > 0) {
-        P = g_forced_splits;
+    if (forced > 0) {
+        P = forced;
     } else {
         P = kTargetGroups / p.n_groups;
         if (P < 1)
@@ -82,11 +84,11 @@ int run_attention(int32_t op, const uint8_t* codes, const float* scales, int64_t
                   int32_t lc, int32_t rc, const int32_t* sel, int64_t n_list, const float* q_lat,
                   const float* q_rope, int32_t n_qh, int32_t n_heads, int64_t pos0,
                   float sm_scale, float* out, float* lse, void* workspace, size_t ws_bytes,
-                  void* stream, const float* x_new = nullptr, uint8_t* new_codes = nullptr,
-                  float* new_scales = nullptr, int64_t new0 = 0, int64_t n_new = 0,
-                  int32_t layout = kE4m3)
+                  void* stream, const mla8_opts* opts, const float* x_new = nullptr,
+                  uint8_t* new_codes = nullptr, float* new_scales = nullptr, int64_t new0 = 0,
+                  int64_t n_new = 0, int32_t layout = kE4m3)
 {
-    const Plan p = make_plan(op, n_list, n_qh);
+    const Plan p = make_plan(op, n_list, n_qh, forced_splits(opts));
     const size_t need = ws_bytes_for(p, n_qh, lc);
     if (workspace == nullptr || ws_bytes < need)
         return MLA8_E_WORKSPACE;
@@ -126,7 +128,7 @@ int run_attention(int32_t op, const uint8_t* codes, const float* scales, int64_t
     a.new_scales = new_scales;
     a.new0 = (int32_t)new0;
     a.n_new = (int32_t)n_new;
-    return launch_attention(a, static_cast<hipStream_t>(stream), g_ev_before, g_ev_after) ==
+    return launch_attention(a, static_cast<hipStream_t>(stream), ev_before(opts), ev_after(opts)) ==
                    hipSuccess
                ? MLA8_OK
                : MLA8_E_HIP;
@@ -212,7 +214,7 @@ static int check_decode_common(const uint8_t* codes, const float* scales, int64_
 int mla8_decode(const uint8_t* kv_codes, const float* kv_scales, int64_t t_rows, int32_t lc,
                 int32_t rc, const float* q_lat, const float* q_rope, int32_t n_heads,
                 float sm_scale, float* out, float* lse, void* workspace, size_t ws_bytes,
-                void* stream)
+                void* stream, const mla8_opts* opts)
 {
     int st = check_decode_common(kv_codes, kv_scales, t_rows, lc, rc, q_lat, q_rope, n_heads,
                                  sm_scale, out);
@@ -220,7 +222,7 @@ int mla8_decode(const uint8_t* kv_codes, const float* kv_scales, int64_t t_rows,
         return st;
     return run_attention(MLA8_OP_DECODE, kv_codes, kv_scales, t_rows, lc, rc, nullptr, t_rows,
                          q_lat, q_rope, n_heads, n_heads, 0, sm_scale, out, lse, workspace,
-                         ws_bytes, stream);
+                         ws_bytes, stream, opts);
 }
 
 // Mixed rows: the 448 / 64 shape only.
@@ -276,7 +278,7 @@ int mla8_append_mx(uint8_t* kv_rows, float* kv_scales, int64_t cap_rows, int64_t
 int mla8_decode_mx(const uint8_t* kv_rows, const float* kv_scales, int64_t t_rows, int32_t lc,
                    int32_t rc, const float* q_lat, const float* q_rope, int32_t n_heads,
                    float sm_scale, float* out, float* lse, void* workspace, size_t ws_bytes,
-                   void* stream)
+                   void* stream, const mla8_opts* opts)
 {
     int st = check_shape_mx(lc, rc);
     if (st != MLA8_OK)
@@ -287,13 +289,14 @@ int mla8_decode_mx(const uint8_t* kv_rows, const float* kv_scales, int64_t t_row
         return st;
     return run_attention(MLA8_OP_DECODE, kv_rows, kv_scales, t_rows, lc, rc, nullptr, t_rows,
                          q_lat, q_rope, n_heads, n_heads, 0, sm_scale, out, lse, workspace,
-                         ws_bytes, stream, nullptr, nullptr, nullptr, 0, 0, kMixed);
+                         ws_bytes, stream, opts, nullptr, nullptr, nullptr, 0, 0, kMixed);
 }
 
 int mla8_decode_sel_mx(const uint8_t* kv_rows, const float* kv_scales, int64_t t_rows,
                        int32_t lc, int32_t rc, const int32_t* sel, int64_t ns,
                        const float* q_lat, const float* q_rope, int32_t n_heads, float sm_scale,
-                       float* out, float* lse, void* workspace, size_t ws_bytes, void* stream)
+                       float* out, float* lse, void* workspace, size_t ws_bytes, void* stream,
+                       const mla8_opts* opts)
 {
     int st = check_shape_mx(lc, rc);
     if (st != MLA8_OK)
@@ -306,7 +309,7 @@ int mla8_decode_sel_mx(const uint8_t* kv_rows, const float* kv_scales, int64_t t
         return MLA8_E_INVAL;
     return run_attention(MLA8_OP_DECODE_SEL, kv_rows, kv_scales, t_rows, lc, rc, sel, ns, q_lat,
                          q_rope, n_heads, n_heads, 0, sm_scale, out, lse, workspace, ws_bytes,
-                         stream, nullptr, nullptr, nullptr, 0, 0, kMixed);
+                         stream, opts, nullptr, nullptr, nullptr, 0, 0, kMixed);
 }
 
 // The fused step and the causal batch over mixed rows: the e4m3 entry
@@ -315,7 +318,8 @@ static int append_decode_layout(uint8_t* kv, float* kv_scales, int64_t cap_rows,
                                 const float* x_new, int64_t n_new, int32_t lc, int32_t rc,
                                 const float* q_lat, const float* q_rope, int32_t n_heads,
                                 float sm_scale, float* out, float* lse, void* workspace,
-                                size_t ws_bytes, void* stream, int32_t layout)
+                                size_t ws_bytes, void* stream, const mla8_opts* opts,
+                                int32_t layout)
 {
     if (!kv || !kv_scales || !t_rows || !x_new)
         return MLA8_E_INVAL;
@@ -334,7 +338,7 @@ static int append_decode_layout(uint8_t* kv, float* kv_scales, int64_t cap_rows,
         return st;
     st = run_attention(MLA8_OP_DECODE, kv, kv_scales, t_new, lc, rc, nullptr, t_new, q_lat,
                        q_rope, n_heads, n_heads, 0, sm_scale, out, lse, workspace, ws_bytes,
-                       stream, x_new, kv, kv_scales, *t_rows, n_new, layout);
+                       stream, opts, x_new, kv, kv_scales, *t_rows, n_new, layout);
     if (st == MLA8_OK)
         *t_rows = t_new;
     return st;
@@ -343,7 +347,8 @@ static int append_decode_layout(uint8_t* kv, float* kv_scales, int64_t cap_rows,
 static int batch_layout(const uint8_t* kv, const float* kv_scales, int64_t t_rows, int32_t lc,
                         int32_t rc, const float* q_lat, const float* q_rope, int32_t n_q,
                         int64_t pos0, int32_t n_heads, float sm_scale, float* out, float* lse,
-                        void* workspace, size_t ws_bytes, void* stream, int32_t layout)
+                        void* workspace, size_t ws_bytes, void* stream, const mla8_opts* opts,
+                        int32_t layout)
 {
     int st = check_decode_common(kv, kv_scales, t_rows, lc, rc, q_lat, q_rope, n_heads, sm_scale,
                                  out);
@@ -357,52 +362,53 @@ static int batch_layout(const uint8_t* kv, const float* kv_scales, int64_t t_row
         return MLA8_E_RANGE;
     return run_attention(MLA8_OP_BATCH, kv, kv_scales, t_rows, lc, rc, nullptr, pos0 + n_q, q_lat,
                          q_rope, n_q * n_heads, n_heads, pos0, sm_scale, out, lse, workspace,
-                         ws_bytes, stream, nullptr, nullptr, nullptr, 0, 0, layout);
+                         ws_bytes, stream, opts, nullptr, nullptr, nullptr, 0, 0, layout);
 }
 
 int mla8_append_decode_mx(uint8_t* kv_rows, float* kv_scales, int64_t cap_rows, int64_t* t_rows,
                           const float* x_new, int64_t n_new, int32_t lc, int32_t rc,
                           const float* q_lat, const float* q_rope, int32_t n_heads,
                           float sm_scale, float* out, float* lse, void* workspace,
-                          size_t ws_bytes, void* stream)
+                          size_t ws_bytes, void* stream, const mla8_opts* opts)
 {
     const int st = check_shape_mx(lc, rc);
     if (st != MLA8_OK)
         return st;
     return append_decode_layout(kv_rows, kv_scales, cap_rows, t_rows, x_new, n_new, lc, rc,
                                 q_lat, q_rope, n_heads, sm_scale, out, lse, workspace, ws_bytes,
-                                stream, kMixed);
+                                stream, opts, kMixed);
 }
 
 int mla8_batch_mx(const uint8_t* kv_rows, const float* kv_scales, int64_t t_rows, int32_t lc,
                   int32_t rc, const float* q_lat, const float* q_rope, int32_t n_q, int64_t pos0,
                   int32_t n_heads, float sm_scale, float* out, float* lse, void* workspace,
-                  size_t ws_bytes, void* stream)
+                  size_t ws_bytes, void* stream, const mla8_opts* opts)
 {
     const int st = check_shape_mx(lc, rc);
     if (st != MLA8_OK)
         return st;
     return batch_layout(kv_rows, kv_scales, t_rows, lc, rc, q_lat, q_rope, n_q, pos0, n_heads,
-                        sm_scale, out, lse, workspace, ws_bytes, stream, kMixed);
+                        sm_scale, out, lse, workspace, ws_bytes, stream, opts, kMixed);
 }
 
 int mla8_append_decode(uint8_t* kv_codes, float* kv_scales, int64_t cap_rows, int64_t* t_rows,
                        const float* x_new, int64_t n_new, int32_t lc, int32_t rc,
                        const float* q_lat, const float* q_rope, int32_t n_heads, float sm_scale,
-                       float* out, float* lse, void* workspace, size_t ws_bytes, void* stream)
+                       float* out, float* lse, void* workspace, size_t ws_bytes, void* stream,
+                       const mla8_opts* opts)
 {
     const int st = check_shape(lc, rc);
     if (st != MLA8_OK)
         return st;
     return append_decode_layout(kv_codes, kv_scales, cap_rows, t_rows, x_new, n_new, lc, rc,
                                 q_lat, q_rope, n_heads, sm_scale, out, lse, workspace, ws_bytes,
-                                stream, kE4m3);
+                                stream, opts, kE4m3);
 }
 
 int mla8_decode_sel(const uint8_t* kv_codes, const float* kv_scales, int64_t t_rows, int32_t lc,
                     int32_t rc, const int32_t* sel, int64_t ns, const float* q_lat,
                     const float* q_rope, int32_t n_heads, float sm_scale, float* out, float* lse,
-                    void* workspace, size_t ws_bytes, void* stream)
+                    void* workspace, size_t ws_bytes, void* stream, const mla8_opts* opts)
 {
     int st = check_decode_common(kv_codes, kv_scales, t_rows, lc, rc, q_lat, q_rope, n_heads,
                                  sm_scale, out);
@@ -412,21 +418,22 @@ int mla8_decode_sel(const uint8_t* kv_codes, const float* kv_scales, int64_t t_r
         return MLA8_E_INVAL;
     return run_attention(MLA8_OP_DECODE_SEL, kv_codes, kv_scales, t_rows, lc, rc, sel, ns, q_lat,
                          q_rope, n_heads, n_heads, 0, sm_scale, out, lse, workspace, ws_bytes,
-                         stream);
+                         stream, opts);
 }
 
 int mla8_batch(const uint8_t* kv_codes, const float* kv_scales, int64_t t_rows, int32_t lc,
                int32_t rc, const float* q_lat, const float* q_rope, int32_t n_q, int64_t pos0,
                int32_t n_heads, float sm_scale, float* out, float* lse, void* workspace,
-               size_t ws_bytes, void* stream)
+               size_t ws_bytes, void* stream, const mla8_opts* opts)
 {
     return batch_layout(kv_codes, kv_scales, t_rows, lc, rc, q_lat, q_rope, n_q, pos0, n_heads,
-                        sm_scale, out, lse, workspace, ws_bytes, stream, kE4m3);
+                        sm_scale, out, lse, workspace, ws_bytes, stream, opts, kE4m3);
 }
 
 int mla8_index_topk(const uint8_t* k_codes, const float* k_scales, int64_t t_rows, int32_t ihd,
                     const float* q, const float* w, int32_t n_ih, int32_t top_k, int32_t* sel,
-                    float* scores, void* workspace, size_t ws_bytes, void* stream)
+                    float* scores, void* workspace, size_t ws_bytes, void* stream,
+                    const mla8_opts* opts)
 {
     if (!k_codes || !k_scales || !q || !w || !sel)
         return MLA8_E_INVAL;
@@ -463,13 +470,14 @@ int mla8_index_topk(const uint8_t* k_codes, const float* k_scales, int64_t t_row
     a.wg_cnt = reinterpret_cast<uint32_t*>(ws);
     ws += r256((size_t)((t_rows + 4095) / 4096) * 4);
     a.top = reinterpret_cast<uint32_t*>(ws);
-    return launch_index_topk(a, static_cast<hipStream_t>(stream), g_ev_before, g_ev_after) ==
+    return launch_index_topk(a, static_cast<hipStream_t>(stream), ev_before(opts), ev_after(opts)) ==
                    hipSuccess
                ? MLA8_OK
                : MLA8_E_HIP;
 }
 
-size_t mla8_workspace_bytes(int32_t op, int64_t rows, int32_t n_heads, int32_t n_q, int32_t lc)
+size_t mla8_workspace_bytes(int32_t op, int64_t rows, int32_t n_heads, int32_t n_q, int32_t lc,
+                            const mla8_opts* opts)
 {
     if (op < MLA8_OP_DECODE || op > MLA8_OP_INDEX || rows <= 0 || rows > kMaxRows ||
         n_heads <= 0 || lc <= 0)
@@ -484,24 +492,18 @@ size_t mla8_workspace_bytes(int32_t op, int64_t rows, int32_t n_heads, int32_t n
         if (n_qh > kMaxRows / 1024)
             return 0;
     }
-    return ws_bytes_for(make_plan(op, rows, (int32_t)n_qh), (int32_t)n_qh, lc);
+    return ws_bytes_for(make_plan(op, rows, (int32_t)n_qh, forced_splits(opts)), (int32_t)n_qh, lc);
 }
 
-int32_t mla8_force_splits(int32_t n_splits)
-{
-    const int32_t prev = g_forced_splits;
-    g_forced_splits = n_splits > 0 ? n_splits : 0;
-    return prev;
-}
-
-int32_t mla8_plan_splits(int32_t op, int64_t rows, int32_t n_heads, int32_t n_q)
+int32_t mla8_plan_splits(int32_t op, int64_t rows, int32_t n_heads, int32_t n_q,
+                         const mla8_opts* opts)
 {
     if (rows <= 0 || n_heads <= 0)
         return 0;
     const int64_t n_qh = op == MLA8_OP_BATCH ? (int64_t)n_q * n_heads : n_heads;
     if (n_qh <= 0 || n_qh > kMaxRows / 1024)
         return 0;
-    return make_plan(op, rows, (int32_t)n_qh).n_chunks;
+    return make_plan(op, rows, (int32_t)n_qh, forced_splits(opts)).n_chunks;
 }
 
 const char* mla8_status_string(int status)
@@ -521,13 +523,6 @@ const char* mla8_status_string(int status)
     case MLA8_E_IO: return "file I/O failed, or no valid header in the file";
     default: return "unknown status";
     }
-}
-
-int mla8_profile_events(void* before, void* after)
-{
-    g_ev_before = static_cast<hipEvent_t>(before);
-    g_ev_after = static_cast<hipEvent_t>(after);
-    return MLA8_OK;
 }
 
 const char* mla8_version(void) { return "mla8 0.1.0 gfx950"; }

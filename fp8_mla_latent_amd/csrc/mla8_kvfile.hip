@@ -151,15 +151,31 @@ bool pread_all(int fd, void* buf, size_t n, int64_t off)
     return true;
 }
 
-// The committed header (the valid slot with the larger seq) and which slot it
-// is in.
+// A slot whose check matches can still describe a file that cannot be read:
+// a corrupted or foreign header, or a body cut short after its commit.  Such a
+// slot is not used: the layer count and row width must be ones this library
+// writes, the token count below 2^31 (row counts are int32 on the device), and
+// the body must hold every committed token.
+bool slot_usable(const Header& h, int64_t file_bytes)
+{
+    if (h.n_layers > 65536 || h.lc + (uint64_t)h.rc > 640 || h.n_tokens > 0x7FFFFFFFull)
+        return false;
+    const int64_t sb = stride(h);
+    return sb > 0 && (int64_t)h.n_tokens <= (file_bytes - (int64_t)kBody) / sb;
+}
+
+// The committed header (the usable slot with the larger seq) and which slot
+// it is in.
 int read_header(int fd, Header& h, int& slot)
 {
     uint8_t s[kBody];
-    if (!pread_all(fd, s, kBody, 0))
+    struct stat sbuf;
+    if (fstat(fd, &sbuf) != 0 || !pread_all(fd, s, kBody, 0))
         return MLA8_E_IO;
+    const int64_t file_bytes = (int64_t)sbuf.st_size;
     Header a, b;
-    const bool va = decode_slot(s, a), vb = decode_slot(s + kSlot, b);
+    const bool va = decode_slot(s, a) && slot_usable(a, file_bytes);
+    const bool vb = decode_slot(s + kSlot, b) && slot_usable(b, file_bytes);
     if (!va && !vb)
         return MLA8_E_IO;
     if (va && (!vb || a.seq >= b.seq)) {
@@ -432,6 +448,18 @@ int mla8_kvfile_load(const char* path, int32_t n_layers, uint8_t* const* kv_code
                 for (int64_t t = 0; t < n; ++t) {
                     memcpy(cd.data() + t * d, rows.data() + t * rb, (size_t)d);
                     memcpy(&sc[(size_t)t], rows.data() + t * rb + d, 4);
+                }
+                // The row quantizer never writes a NaN code (0x7F / 0xFF) nor
+                // a negative or non-finite scale: a body holding one is corrupt
+                // and is not loaded (this chunk is refused before its copy).
+                bool body_ok = true;
+                for (size_t i = 0; i < cd.size() && body_ok; ++i)
+                    body_ok = (cd[i] & 0x7F) != 0x7F;
+                for (int64_t t = 0; t < n && body_ok; ++t)
+                    body_ok = sc[(size_t)t] >= 0.0f && sc[(size_t)t] <= 3.402823466e38f;
+                if (!body_ok) {
+                    st = MLA8_E_IO;
+                    break;
                 }
                 if (!copy_in(kv_codes[l] + c0 * d, cd.data(), cd.size(), dev, hs) ||
                     !copy_in(kv_scales[l] + c0, sc.data(), (size_t)n * 4, dev, hs))

@@ -67,6 +67,27 @@ enum {
 enum { MLA8_OP_DECODE = 0, MLA8_OP_DECODE_SEL = 1, MLA8_OP_BATCH = 2, MLA8_OP_INDEX = 3 };
 
 /*
+ * Per-call options, the last argument of every attention call, of
+ * mla8_index_topk, mla8_workspace_bytes and mla8_plan_splits.  NULL means
+ * the defaults (the automatic split plan, no events).  The library keeps no
+ * state between calls, so calls on different streams (or threads) with
+ * different options never affect each other.
+ *   n_splits   0: automatic split plan; > 0: this many row chunks (split-T
+ *              partials), clamped to what the row count allows.  The
+ *              workspace must then be sized with the same options.
+ *   ev_before, ev_after: hipEvent_t (as void*) recorded on the call's stream
+ *              just before and just after the split-T partial kernel (the
+ *              indexer's score kernel for mla8_index_topk), so that
+ *              hipEventElapsedTime(ev_before, ev_after) is that kernel's
+ *              duration; NULL to skip.  Caller-owned.
+ */
+typedef struct mla8_opts {
+    int32_t n_splits;
+    void* ev_before;
+    void* ev_after;
+} mla8_opts;
+
+/*
  * Quantize n_rows f32 rows x[n_rows][lc + rc] into e4m3 codes[n_rows][lc + rc]
  * and f32 scales[n_rows]  [KV8-base, c/kv_fp8.h bullet]:
  *   amax  = max |x_i| over the row's finite entries (NaN and +/-inf excluded);
@@ -112,7 +133,7 @@ MLA8_API int mla8_append(uint8_t* kv_codes, float* kv_scales, int64_t cap_rows, 
 MLA8_API int mla8_decode(const uint8_t* kv_codes, const float* kv_scales, int64_t t_rows, int32_t lc,
                 int32_t rc, const float* q_lat, const float* q_rope, int32_t n_heads,
                 float sm_scale, float* out, float* lse, void* workspace, size_t ws_bytes,
-                void* stream);
+                void* stream, const mla8_opts* opts);
 
 /*
  * Append then decode in one launch: the same result as mla8_append(x_new,
@@ -134,7 +155,7 @@ MLA8_API int mla8_append_decode(uint8_t* kv_codes, float* kv_scales, int64_t cap
                        int64_t* t_rows, const float* x_new, int64_t n_new, int32_t lc,
                        int32_t rc, const float* q_lat, const float* q_rope, int32_t n_heads,
                        float sm_scale, float* out, float* lse, void* workspace,
-                       size_t ws_bytes, void* stream);
+                       size_t ws_bytes, void* stream, const mla8_opts* opts);
 
 /*
  * Selected-row (DSA gather) decode [KV8-long, DSA bullet]: as mla8_decode, but
@@ -148,7 +169,7 @@ MLA8_API int mla8_append_decode(uint8_t* kv_codes, float* kv_scales, int64_t cap
 MLA8_API int mla8_decode_sel(const uint8_t* kv_codes, const float* kv_scales, int64_t t_rows, int32_t lc,
                     int32_t rc, const int32_t* sel, int64_t ns, const float* q_lat,
                     const float* q_rope, int32_t n_heads, float sm_scale, float* out, float* lse,
-                    void* workspace, size_t ws_bytes, void* stream);
+                    void* workspace, size_t ws_bytes, void* stream, const mla8_opts* opts);
 
 /*
  * Batched causal attention [KV8-long: the batch/prefill path over the cached
@@ -164,7 +185,7 @@ MLA8_API int mla8_decode_sel(const uint8_t* kv_codes, const float* kv_scales, in
 MLA8_API int mla8_batch(const uint8_t* kv_codes, const float* kv_scales, int64_t t_rows, int32_t lc,
                int32_t rc, const float* q_lat, const float* q_rope, int32_t n_q, int64_t pos0,
                int32_t n_heads, float sm_scale, float* out, float* lse, void* workspace,
-               size_t ws_bytes, void* stream);
+               size_t ws_bytes, void* stream, const mla8_opts* opts);
 
 /*
  * Mixed row layout  [B1-FMHA, the storage-format list: noPE KV as e4m3 bytes
@@ -188,7 +209,7 @@ MLA8_API int mla8_append_mx(uint8_t* kv_rows, float* kv_scales, int64_t cap_rows
 MLA8_API int mla8_decode_mx(const uint8_t* kv_rows, const float* kv_scales, int64_t t_rows,
                             int32_t lc, int32_t rc, const float* q_lat, const float* q_rope,
                             int32_t n_heads, float sm_scale, float* out, float* lse,
-                            void* workspace, size_t ws_bytes, void* stream);
+                            void* workspace, size_t ws_bytes, void* stream, const mla8_opts* opts);
 /* As mla8_decode_sel (absolute row indices, a multiset, entries outside
  * [0, t_rows) skipped), over mixed rows; workspace from
  * mla8_workspace_bytes(MLA8_OP_DECODE_SEL, ns, n_heads, 1, lc). */
@@ -196,7 +217,7 @@ MLA8_API int mla8_decode_sel_mx(const uint8_t* kv_rows, const float* kv_scales, 
                                 int32_t lc, int32_t rc, const int32_t* sel, int64_t ns,
                                 const float* q_lat, const float* q_rope, int32_t n_heads,
                                 float sm_scale, float* out, float* lse, void* workspace,
-                                size_t ws_bytes, void* stream);
+                                size_t ws_bytes, void* stream, const mla8_opts* opts);
 /* As mla8_append_decode over mixed rows: the n_new (1..64) fresh f32 rows x_new
  * [n_new][lc + rc] (16-byte aligned) are stored at rows [*t_rows, *t_rows +
  * n_new) in the mla8_quantize_rows_mx format by the same launch that attends
@@ -208,7 +229,7 @@ MLA8_API int mla8_append_decode_mx(uint8_t* kv_rows, float* kv_scales, int64_t c
                                    int64_t* t_rows, const float* x_new, int64_t n_new, int32_t lc,
                                    int32_t rc, const float* q_lat, const float* q_rope,
                                    int32_t n_heads, float sm_scale, float* out, float* lse,
-                                   void* workspace, size_t ws_bytes, void* stream);
+                                   void* workspace, size_t ws_bytes, void* stream, const mla8_opts* opts);
 /* As mla8_batch (query s at position pos0 + s attends rows 0 .. pos0 + s;
  * q_lat [n_q][n_heads][lc], q_rope [n_q][n_heads][rc]; out [n_q][n_heads][lc],
  * lse [n_q][n_heads]) over mixed rows; workspace from
@@ -216,7 +237,7 @@ MLA8_API int mla8_append_decode_mx(uint8_t* kv_rows, float* kv_scales, int64_t c
 MLA8_API int mla8_batch_mx(const uint8_t* kv_rows, const float* kv_scales, int64_t t_rows,
                            int32_t lc, int32_t rc, const float* q_lat, const float* q_rope,
                            int32_t n_q, int64_t pos0, int32_t n_heads, float sm_scale, float* out,
-                           float* lse, void* workspace, size_t ws_bytes, void* stream);
+                           float* lse, void* workspace, size_t ws_bytes, void* stream, const mla8_opts* opts);
 
 /*
  * fp8 indexer score + top-k: the selection that mla8_decode_sel attends.
@@ -247,38 +268,23 @@ MLA8_API int mla8_batch_mx(const uint8_t* kv_rows, const float* kv_scales, int64
 MLA8_API int mla8_index_topk(const uint8_t* k_codes, const float* k_scales, int64_t t_rows,
                              int32_t ihd, const float* q, const float* w, int32_t n_ih,
                              int32_t top_k, int32_t* sel, float* scores, void* workspace,
-                             size_t ws_bytes, void* stream);
+                             size_t ws_bytes, void* stream, const mla8_opts* opts);
 
 /*
- * Workspace bytes the given call needs on the current device.  `rows` is the
- * number of rows the call attends: t_rows for MLA8_OP_DECODE, ns for
- * MLA8_OP_DECODE_SEL, pos0 + n_q for MLA8_OP_BATCH, t_rows for MLA8_OP_INDEX
- * (whose n_heads is n_ih and lc is ihd).  n_q is ignored except for
- * MLA8_OP_BATCH.  Returns 0 for invalid arguments.
+ * Workspace bytes the given call needs.  `rows` is the number of rows the
+ * call attends: t_rows for MLA8_OP_DECODE, ns for MLA8_OP_DECODE_SEL,
+ * pos0 + n_q for MLA8_OP_BATCH, t_rows for MLA8_OP_INDEX (whose n_heads is
+ * n_ih and lc is ihd).  n_q is ignored except for MLA8_OP_BATCH.  opts: the
+ * options the call will be made with (NULL = defaults); the split count
+ * changes the size.  Returns 0 for invalid arguments.
  */
-MLA8_API size_t mla8_workspace_bytes(int32_t op, int64_t rows, int32_t n_heads, int32_t n_q, int32_t lc);
+MLA8_API size_t mla8_workspace_bytes(int32_t op, int64_t rows, int32_t n_heads, int32_t n_q, int32_t lc, const mla8_opts* opts);
 
-/*
- * Tuning / testing control: force the number of row chunks (split-T
- * partials) that subsequent decode calls in this process use; 0 restores the
- * automatic choice.  The value is clamped to what the row count allows.  Not
- * thread-safe with concurrent decode calls.  Returns the previous value.
- */
-MLA8_API int32_t mla8_force_splits(int32_t n_splits);
-
-/* Number of row chunks the automatic (or forced) plan uses for a call. */
-MLA8_API int32_t mla8_plan_splits(int32_t op, int64_t rows, int32_t n_heads, int32_t n_q);
-
-/*
- * Measurement hook: while set, every attention call (mla8_decode,
- * mla8_append_decode, mla8_decode_sel, mla8_batch and their _mx forms) records
- * the hipEvent_t `before` on its stream just before launching the split-T
- * partial kernel and `after` just after it, and mla8_index_topk does the same around its score
- * kernel, so hipEventElapsedTime(before, after) is that kernel's duration.
- * Pass NULL, NULL to clear.  Events are caller-owned.  Not thread-safe.
- * Returns MLA8_OK.
- */
-MLA8_API int mla8_profile_events(void* before, void* after);
+/* Number of row chunks (split-T partials) the plan for a call uses: the
+ * automatic plan, or opts->n_splits clamped to what the row count allows.
+ * Arguments as mla8_workspace_bytes; returns 0 for invalid arguments. */
+MLA8_API int32_t mla8_plan_splits(int32_t op, int64_t rows, int32_t n_heads, int32_t n_q,
+                                  const mla8_opts* opts);
 
 /*
  * Persistent shadow files  [KV8-base, the .coli_kv v2 bullet: a versioned file
@@ -333,7 +339,13 @@ MLA8_API int mla8_kvfile_append(const char* path, int32_t n_layers, const uint8_
  * the file itself is not changed.  Errors: E_INVAL (NULL pointer, cap_rows < 1,
  * a file of another n_layers / lc / rc), E_UNSUPPORTED (shape; a version-1
  * file into host shadows), E_CAPACITY (n_tokens > cap_rows, nothing loaded),
- * E_WORKSPACE (version 1 without a large enough workspace), E_HIP, E_IO. */
+ * E_WORKSPACE (version 1 without a large enough workspace), E_HIP, E_IO (no
+ * usable header slot, or a version-2 row that the quantizer cannot have
+ * written: a NaN code 0x7F / 0xFF, or a negative or non-finite scale; the
+ * rows before it may then already be in the shadows, *t_rows is unchanged).
+ * A header slot is usable when its check matches, its token count is below
+ * 2^31 and the body holds all of its tokens; of two usable slots the larger
+ * seq wins. */
 MLA8_API int mla8_kvfile_load(const char* path, int32_t n_layers, uint8_t* const* kv_codes,
                               float* const* kv_scales, int64_t cap_rows, int64_t* t_rows,
                               int32_t lc, int32_t rc, int32_t on_device, void* workspace,
@@ -344,30 +356,6 @@ MLA8_API const char* mla8_status_string(int status);
 
 /* Library version string (static storage). */
 MLA8_API const char* mla8_version(void);
-
-/*
- * Measurement aid, not part of the attention path: the read-bandwidth
- * reference that the decode's HBM rate is compared with.  Loads every 16-byte
- * word of [p, p + bytes) once (coalesced, grid-stride) and XOR-folds them:
- * out (device memory, MLA8_STREAM_WORDS uint32, 16-byte aligned) receives one
- * fold per wave, every word written, so that the XOR of all its words is the
- * XOR of the buffer's 32-bit words and no load can be dropped.  p: device
- * pointer, 16-byte aligned; bytes a multiple of 16.  Enqueues on `stream`
- * and returns.
- * Errors: E_INVAL (NULL pointer, misalignment, bytes < 0 or not a multiple of
- * 16), E_HIP.
- */
-#define MLA8_STREAM_WORDS 32768
-MLA8_API int mla8_stream_read(const void* p, int64_t bytes, uint32_t* out, void* stream);
-
-/*
- * Not part of the product API: apply the device e4m3 encoder elementwise,
- * codes[i] = enc(x[i]) for i < n, with no scaling.  Exported so that tests can
- * compare the device encoder with the reference on every f32 bit pattern,
- * including finite |x| > 448 which the quantizer never produces.
- * Errors: E_INVAL, E_HIP.
- */
-MLA8_API int mla8_test_encode(const float* x, int64_t n, uint8_t* codes, void* stream);
 
 #ifdef __cplusplus
 }

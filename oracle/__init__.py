@@ -65,6 +65,7 @@ def lib() -> ctypes.CDLL:
         L.mla8o_decode_mx.argtypes = [P, P, i64, i32, i32, P, P, i32, f32, P, P]
         L.mla8o_decode_sel_mx.argtypes = [P, P, i64, i32, i32, P, i64, P, P, i32, f32, P, P]
         L.mla8o_threads.restype = ctypes.c_int
+        L.mla8o_set_threads.argtypes = [ctypes.c_int]
         _lib = L
     return _lib
 
@@ -252,3 +253,8 @@ def decode_sel_mx(rows, scales, t_rows, lc, rc, sel, q_lat, q_rope, sm_scale):
 
 def threads() -> int:
     return int(lib().mla8o_threads())
+
+
+def set_threads(n: int) -> None:
+    """OpenMP threads for the following calls; n < 1 restores the default."""
+    lib().mla8o_set_threads(int(n))

@@ -342,6 +342,20 @@ EXPORT void mla8o_decode_chunked(const uint8_t* codes, const float* scales, int6
     }
 }
 
+/* Threads for the following calls (timing the oracle on one core or all);
+ * n < 1 restores the runtime's default.  No effect without OpenMP. */
+EXPORT void mla8o_set_threads(int n)
+{
+#ifdef _OPENMP
+    static int dflt = 0;
+    if (dflt == 0)
+        dflt = omp_get_max_threads();
+    omp_set_num_threads(n >= 1 ? n : dflt);
+#else
+    (void)n;
+#endif
+}
+
 /* Number of threads the OpenMP runtime will use (for reporting). */
 EXPORT int mla8o_threads(void)
 {

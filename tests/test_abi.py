@@ -1,7 +1,9 @@
 """C-ABI checks that need no GPU: the library loads, exports every symbol that
-include/mla8.h declares, and refuses bad arguments on the host before any HIP
-call.  No call here passes validation, so no kernel is ever launched (the fake
-device pointers below are never dereferenced)."""
+include/mla8.h and include/mla8_aux.h declare, and refuses bad arguments on
+the host before any HIP call; the Python binding refuses host tensors, wrong
+dtypes and shapes before any address reaches the library.  No call here passes
+validation, so no kernel is ever launched (the fake device pointers below are
+never dereferenced)."""
 from __future__ import annotations
 
 import ctypes
@@ -13,14 +15,14 @@ import pytest
 from fp8_mla_latent_amd import mla8 as m
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "mla8.h")
+HEADERS = [os.path.join(ROOT, "include", h) for h in ("mla8.h", "mla8_aux.h")]
 
 FAKE = ctypes.c_void_p(0x10000)          # aligned, never dereferenced
 FAKE_MISALIGNED = ctypes.c_void_p(0x10004)
 
 
 def declared_symbols():
-    text = open(HEADER).read()
+    text = "".join(open(h).read() for h in HEADERS)
     return sorted(set(re.findall(r"MLA8_API\s+[\w\s\*]+?\b(mla8_\w+)\s*\(", text)))
 
 
@@ -52,7 +54,8 @@ def dec(**kw):
              out=FAKE, lse=None, ws=FAKE, wsb=1 << 30)
     a.update(kw)
     return m.lib.mla8_decode(a["codes"], a["scales"], a["t"], a["lc"], a["rc"], a["ql"], a["qr"],
-                             a["h"], a["sm"], a["out"], a["lse"], a["ws"], a["wsb"], None)
+                             a["h"], a["sm"], a["out"], a["lse"], a["ws"], a["wsb"], None,
+                             a.get("opts"))
 
 
 @pytest.mark.parametrize("kw,want", [
@@ -85,12 +88,18 @@ def test_decode_workspace_exact_boundary():
     need = m.mla8_workspace_bytes(m.MLA8_OP_DECODE, 100, 64, 1, 512)
     assert need > 0
     assert dec(wsb=need - 1) == m.MLA8_E_WORKSPACE
+    # a forced split count changes the plan and the size, for that call only
+    o = m.Mla8Opts(2, None, None)
+    need2 = m.lib.mla8_workspace_bytes(m.MLA8_OP_DECODE, 100, 64, 1, 512, ctypes.byref(o))
+    assert need2 > need
+    assert dec(wsb=need2 - 1, opts=ctypes.byref(o)) == m.MLA8_E_WORKSPACE
+    assert dec(wsb=need - 1) == m.MLA8_E_WORKSPACE
 
 
 def test_decode_sel_refuses():
     f = m.lib.mla8_decode_sel
     base = [FAKE, FAKE, 100, 512, 64, FAKE, 10, FAKE, FAKE, 64, 0.1, FAKE, None, FAKE, 1 << 30,
-            None]
+            None, None]
     for idx, val, want in [(5, None, m.MLA8_E_INVAL), (6, 0, m.MLA8_E_INVAL),
                            (6, -3, m.MLA8_E_INVAL), (5, ctypes.c_void_p(0x10002), m.MLA8_E_INVAL),
                            (14, 10, m.MLA8_E_WORKSPACE), (3, 100, m.MLA8_E_UNSUPPORTED)]:
@@ -101,7 +110,8 @@ def test_decode_sel_refuses():
 
 def test_batch_refuses():
     f = m.lib.mla8_batch
-    base = [FAKE, FAKE, 100, 512, 64, FAKE, FAKE, 4, 96, 64, 0.1, FAKE, None, FAKE, 1 << 30, None]
+    base = [FAKE, FAKE, 100, 512, 64, FAKE, FAKE, 4, 96, 64, 0.1, FAKE, None, FAKE, 1 << 30, None,
+            None]
     for idx, val, want in [(7, 0, m.MLA8_E_INVAL), (8, -1, m.MLA8_E_INVAL),
                            (8, 97, m.MLA8_E_RANGE), (2, 50, m.MLA8_E_RANGE),
                            (14, 64, m.MLA8_E_WORKSPACE), (0, None, m.MLA8_E_INVAL)]:
@@ -140,20 +150,39 @@ def test_plans_and_workspace_sizes():
     assert m.mla8_plan_splits(m.MLA8_OP_BATCH, 32768, 64, 64) == 2
     assert m.mla8_workspace_bytes(m.MLA8_OP_DECODE, 0, 64, 1, 512) == 0
     assert m.mla8_workspace_bytes(7, 10, 64, 1, 512) == 0
-    prev = m.mla8_force_splits(5)
-    try:
-        assert m.mla8_plan_splits(m.MLA8_OP_DECODE, 4096, 128) == 5
-        assert m.mla8_plan_splits(m.MLA8_OP_DECODE, 100, 4) == 2  # clamped to the 64-row tiles
-    finally:
-        m.mla8_force_splits(prev)
+    assert m.mla8_plan_splits(m.MLA8_OP_DECODE, 4096, 128, n_splits=5) == 5
+    assert m.mla8_plan_splits(m.MLA8_OP_DECODE, 100, 4, n_splits=5) == 2  # 64-row tiles
     assert m.mla8_plan_splits(m.MLA8_OP_DECODE, 4096, 128) == 16
+
+
+def test_options_are_per_call():
+    """The library keeps no state between calls: two interleaved callers with
+    different split options (as two streams would be) each get their own plan
+    and workspace size, and a caller with events armed changes nothing for a
+    caller without."""
+    o7 = m.Mla8Opts(7, None, None)
+    o3 = m.Mla8Opts(3, None, None)
+    armed = m.Mla8Opts(0, ctypes.c_void_p(0x1234), ctypes.c_void_p(0x5678))  # never recorded
+    auto = m.lib.mla8_plan_splits(m.MLA8_OP_DECODE, 262144, 64, 1, None)
+    ws_auto = m.lib.mla8_workspace_bytes(m.MLA8_OP_DECODE, 262144, 64, 1, 512, None)
+    for _ in range(3):
+        assert m.lib.mla8_plan_splits(m.MLA8_OP_DECODE, 262144, 64, 1, ctypes.byref(o7)) == 7
+        assert m.lib.mla8_plan_splits(m.MLA8_OP_DECODE, 262144, 64, 1, ctypes.byref(o3)) == 3
+        assert m.lib.mla8_plan_splits(m.MLA8_OP_DECODE, 262144, 64, 1, ctypes.byref(armed)) == auto
+        assert m.lib.mla8_plan_splits(m.MLA8_OP_DECODE, 262144, 64, 1, None) == auto
+        w7 = m.lib.mla8_workspace_bytes(m.MLA8_OP_DECODE, 262144, 64, 1, 512, ctypes.byref(o7))
+        assert w7 == 2 * 7 * 64 * 4 + 7 * 64 * 512 * 4 + 3 * 0  # sections 256-byte rounded
+        assert m.lib.mla8_workspace_bytes(m.MLA8_OP_DECODE, 262144, 64, 1, 512, None) == ws_auto
+    # a refused call with options armed leaves the next default call unchanged
+    assert dec(wsb=10, opts=ctypes.byref(armed)) == m.MLA8_E_WORKSPACE
+    assert m.lib.mla8_plan_splits(m.MLA8_OP_DECODE, 262144, 64, 1, None) == auto
 
 
 def test_append_decode_refuses():
     f = m.lib.mla8_append_decode
     t = ctypes.c_int64(10)
     base = [FAKE, FAKE, 100, ctypes.byref(t), FAKE, 1, 512, 64, FAKE, FAKE, 64, 0.1, FAKE, None,
-            FAKE, 1 << 30, None]
+            FAKE, 1 << 30, None, None]
     for idx, val, want in [(4, None, m.MLA8_E_INVAL),         # no fresh rows
                            (5, 0, m.MLA8_E_INVAL),            # n_new = 0
                            (5, 65, m.MLA8_E_RANGE),           # more than the fused maximum
@@ -170,9 +199,9 @@ def test_append_decode_refuses():
 
 def test_index_topk_refuses():
     f = m.lib.mla8_index_topk
-    ws = m.lib.mla8_workspace_bytes(m.MLA8_OP_INDEX, 1000, 64, 1, 128)
+    ws = m.lib.mla8_workspace_bytes(m.MLA8_OP_INDEX, 1000, 64, 1, 128, None)
     assert ws >= 1000 * 12 + 4096 * 4
-    base = [FAKE, FAKE, 1000, 128, FAKE, FAKE, 64, 100, FAKE, None, FAKE, ws, None]
+    base = [FAKE, FAKE, 1000, 128, FAKE, FAKE, 64, 100, FAKE, None, FAKE, ws, None, None]
     for idx, val, want in [(0, None, m.MLA8_E_INVAL),        # no keys
                            (4, None, m.MLA8_E_INVAL),        # no query
                            (5, None, m.MLA8_E_INVAL),        # no weights
@@ -205,8 +234,8 @@ def test_mixed_refuses():
     assert a(FAKE, FAKE, 4, ctypes.byref(t), FAKE, 1, 448, 48, None) == m.MLA8_E_UNSUPPORTED
     assert t.value == 3
     d = m.lib.mla8_decode_mx
-    ws = m.lib.mla8_workspace_bytes(m.MLA8_OP_DECODE, 100, 64, 1, 448)
-    base = [FAKE, FAKE, 100, 448, 64, FAKE, FAKE, 64, 0.1, FAKE, None, FAKE, ws, None]
+    ws = m.lib.mla8_workspace_bytes(m.MLA8_OP_DECODE, 100, 64, 1, 448, None)
+    base = [FAKE, FAKE, 100, 448, 64, FAKE, FAKE, 64, 0.1, FAKE, None, FAKE, ws, None, None]
     for idx, val, want in [(3, 512, m.MLA8_E_UNSUPPORTED), (0, None, m.MLA8_E_INVAL),
                            (2, 0, m.MLA8_E_INVAL), (12, ws - 1, m.MLA8_E_WORKSPACE),
                            (6, None, m.MLA8_E_INVAL)]:
@@ -219,7 +248,7 @@ def test_mixed_step_and_batch_refuse():
     f = m.lib.mla8_append_decode_mx
     t = ctypes.c_int64(10)
     base = [FAKE, FAKE, 100, ctypes.byref(t), FAKE, 1, 448, 64, FAKE, FAKE, 64, 0.1, FAKE, None,
-            FAKE, 1 << 30, None]
+            FAKE, 1 << 30, None, None]
     for idx, val, want in [(6, 512, m.MLA8_E_UNSUPPORTED),   # the e4m3 shape is not mixed
                            (7, 32, m.MLA8_E_UNSUPPORTED),
                            (4, None, m.MLA8_E_INVAL),         # no fresh rows
@@ -232,8 +261,8 @@ def test_mixed_step_and_batch_refuse():
         assert f(*args) == want, (idx, val)
         assert t.value == 10
     b = m.lib.mla8_batch_mx
-    ws = m.lib.mla8_workspace_bytes(m.MLA8_OP_BATCH, 100, 16, 4, 448)
-    base = [FAKE, FAKE, 100, 448, 64, FAKE, FAKE, 4, 96, 16, 0.1, FAKE, None, FAKE, ws, None]
+    ws = m.lib.mla8_workspace_bytes(m.MLA8_OP_BATCH, 100, 16, 4, 448, None)
+    base = [FAKE, FAKE, 100, 448, 64, FAKE, FAKE, 4, 96, 16, 0.1, FAKE, None, FAKE, ws, None, None]
     for idx, val, want in [(3, 512, m.MLA8_E_UNSUPPORTED), (7, 0, m.MLA8_E_INVAL),
                            (8, 97, m.MLA8_E_RANGE), (14, ws - 1, m.MLA8_E_WORKSPACE),
                            (5, None, m.MLA8_E_INVAL)]:
@@ -250,3 +279,77 @@ def test_stream_read_refuses():
     assert f(FAKE, 40, FAKE, None) == m.MLA8_E_INVAL      # not a multiple of 16
     assert f(FAKE, -16, FAKE, None) == m.MLA8_E_INVAL
     assert f(FAKE, 64, FAKE_MISALIGNED, None) == m.MLA8_E_INVAL
+
+
+# ---------------------------------------------------------------------------
+# The binding's own checks: a host tensor, a wrong dtype or shape, or a row
+# count beyond the buffer is refused in Python, before the C ABI sees an address.
+
+import torch  # noqa: E402
+
+
+def _cpu(shape, dtype):
+    return torch.zeros(shape, dtype=dtype)
+
+
+@pytest.mark.parametrize("call", [
+    lambda: m.mla8_quantize_rows(_cpu((4, 576), torch.float32), 512, 64),
+    lambda: m.mla8_append(_cpu((8, 576), torch.uint8), _cpu((8,), torch.float32), 0,
+                          _cpu((1, 576), torch.float32), 512, 64),
+    lambda: m.mla8_decode(_cpu((8, 576), torch.uint8), _cpu((8,), torch.float32), 8, 512, 64,
+                          _cpu((4, 512), torch.float32), _cpu((4, 64), torch.float32), 0.1),
+    lambda: m.mla8_append_decode(_cpu((8, 576), torch.uint8), _cpu((8,), torch.float32), 7,
+                                 _cpu((1, 576), torch.float32), 512, 64,
+                                 _cpu((4, 512), torch.float32), _cpu((4, 64), torch.float32), 0.1),
+    lambda: m.mla8_decode_sel(_cpu((8, 576), torch.uint8), _cpu((8,), torch.float32), 8, 512, 64,
+                              _cpu((3,), torch.int32), _cpu((4, 512), torch.float32),
+                              _cpu((4, 64), torch.float32), 0.1),
+    lambda: m.mla8_batch(_cpu((8, 576), torch.uint8), _cpu((8,), torch.float32), 8, 512, 64,
+                         _cpu((2, 4, 512), torch.float32), _cpu((2, 4, 64), torch.float32), 6,
+                         0.1),
+    lambda: m.mla8_index_topk(_cpu((8, 128), torch.uint8), _cpu((8,), torch.float32),
+                              _cpu((16, 128), torch.float32), _cpu((16,), torch.float32), 4),
+    lambda: m.mla8_test_encode(_cpu((8,), torch.float32)),
+    lambda: m.mla8_stream_read(_cpu((64,), torch.uint8), _cpu((32768,), torch.int32)),
+])
+def test_binding_refuses_host_tensors(call):
+    with pytest.raises(ValueError, match="device"):
+        call()
+
+
+class _FakeDev:
+    """Stands in for a device tensor in the checks that come after the device
+    test (dtype, shape, rows): only the attributes the checks read."""
+
+    def __init__(self, shape, dtype):
+        self.shape = torch.Size(shape)
+        self.dtype = dtype
+        self.is_cuda = True
+        self.device = torch.device("cuda", 0)
+
+    def dim(self):
+        return len(self.shape)
+
+    def is_contiguous(self):
+        return True
+
+
+def test_binding_checks_dtype_shape_and_rows(monkeypatch):
+    monkeypatch.setattr(m, "_TENSOR", _FakeDev)
+    codes, scales = _FakeDev((8, 576), torch.uint8), _FakeDev((8,), torch.float32)
+    ql, qr = _FakeDev((4, 512), torch.float32), _FakeDev((4, 64), torch.float32)
+    with pytest.raises(ValueError, match="torch.float32"):   # f64 query
+        m.mla8_decode(codes, scales, 8, 512, 64, _FakeDev((4, 512), torch.float64), qr, 0.1)
+    with pytest.raises(ValueError, match="shape"):           # row width of another shape
+        m.mla8_decode(_FakeDev((8, 512), torch.uint8), scales, 8, 512, 64, ql, qr, 0.1)
+    with pytest.raises(ValueError, match="shape"):           # q_rope of another width
+        m.mla8_decode(codes, scales, 8, 512, 64, ql, _FakeDev((4, 32), torch.float32), 0.1)
+    with pytest.raises(ValueError, match="t_rows"):          # more rows than the buffer
+        m.mla8_decode(codes, scales, 9, 512, 64, ql, qr, 0.1)
+    with pytest.raises(ValueError, match="shape"):           # scales of another length
+        m.mla8_decode(codes, _FakeDev((7,), torch.float32), 8, 512, 64, ql, qr, 0.1)
+    with pytest.raises(ValueError, match="torch.int32"):     # int64 selection
+        m.mla8_decode_sel(codes, scales, 8, 512, 64, _FakeDev((3,), torch.int64), ql, qr, 0.1)
+    with pytest.raises(ValueError, match="t_rows"):          # batch rows beyond the buffer
+        m.mla8_batch(codes, scales, 9, 512, 64, _FakeDev((2, 4, 512), torch.float32),
+                     _FakeDev((2, 4, 64), torch.float32), 7, 0.1)

@@ -56,16 +56,13 @@ def _run(m, w, t_total, n_new, cap=None, splits=0, seed=0):
         t = m.mla8_append(codes, scales, 0, dev(x[:t_old]), w.lc, w.rc)
         assert t == t_old
         shadows.append((codes, scales))
-    prev = m.mla8_force_splits(splits)
-    try:
-        (ca, sa), (cb, sb) = shadows
-        t = m.mla8_append(ca, sa, t_old, dev(x[t_old:]), w.lc, w.rc)
-        out_a, lse_a = m.mla8_decode(ca, sa, t, w.lc, w.rc, dev(ql), dev(qr), w.sm_scale)
-        out_b, lse_b, tb = m.mla8_append_decode(cb, sb, t_old, dev(x[t_old:]), w.lc, w.rc,
-                                                dev(ql), dev(qr), w.sm_scale)
-        torch.cuda.synchronize()
-    finally:
-        m.mla8_force_splits(prev)
+    (ca, sa), (cb, sb) = shadows
+    t = m.mla8_append(ca, sa, t_old, dev(x[t_old:]), w.lc, w.rc)
+    out_a, lse_a = m.mla8_decode(ca, sa, t, w.lc, w.rc, dev(ql), dev(qr), w.sm_scale,
+                                 n_splits=splits)
+    out_b, lse_b, tb = m.mla8_append_decode(cb, sb, t_old, dev(x[t_old:]), w.lc, w.rc,
+                                            dev(ql), dev(qr), w.sm_scale, n_splits=splits)
+    torch.cuda.synchronize()
     assert tb == t_total
     oc, os_ = oracle.quantize_rows(x)
     ro, rl = oracle.decode(oc, os_, t_total, w.lc, w.rc, ql, qr, w.sm_scale)
@@ -83,7 +80,8 @@ def test_append_decode_matches_append_then_decode(m, w, n_new):
     assert np.array_equal(host(ca), host(cb)) and np.array_equal(host(sa), host(sb))
     # same kernels over the same bytes: identical results
     assert np.array_equal(host(oa), host(ob)) and np.array_equal(host(la), host(lb))
-    check_attention(host(ob), ro, host(lb), rl, f"append_decode {w.name} n_new={n_new}")
+    check_attention(host(ob), ro, host(lb), rl, f"append_decode {w.name} n_new={n_new}",
+                    outliers=w.outlier_frac > 0)
 
 
 def test_append_decode_fresh_rows_in_an_early_tile(m):
@@ -106,7 +104,7 @@ def test_append_decode_rows_straddle_a_chunk_boundary(m):
     (ca, sa, oa, la), (cb, sb, ob, lb), (oc, os_, ro, rl) = _run(m, w, 3842, 4, splits=16)
     assert np.array_equal(host(cb), oc) and np.array_equal(host(sb), os_)
     assert np.array_equal(host(oa), host(ob)) and np.array_equal(host(la), host(lb))
-    check_attention(host(ob), ro, host(lb), rl, "append_decode straddle")
+    check_attention(host(ob), ro, host(lb), rl, "append_decode straddle", outliers=True)
 
 
 def test_append_decode_full_64_rows_to_capacity(m):
@@ -164,4 +162,4 @@ def test_append_decode_graph_replays_match_eager(m):
         _ = (torch.ones(1000, device=DEV) * 2).sum().item()  # eager work between replays
     oc, os_ = oracle.quantize_rows(x)
     ro, rl = oracle.decode(oc, os_, t, w.lc, w.rc, ql, qr, w.sm_scale)
-    check_attention(ref_out, ro, ref_lse, rl, "append_decode graph")
+    check_attention(ref_out, ro, ref_lse, rl, "append_decode graph", outliers=True)

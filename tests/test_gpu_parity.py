@@ -161,7 +161,8 @@ def test_decode_workloads(m, w, seed):
     ql, qr = W.queries(w, seed_offset=seed)
     out, lse = m.mla8_decode(codes, scales, w.t_rows, w.lc, w.rc, dev(ql), dev(qr), w.sm_scale)
     ro, rl = oracle.decode(oc, os_, w.t_rows, w.lc, w.rc, ql, qr, w.sm_scale)
-    check_attention(host(out), ro, host(lse), rl, f"{w.name} seed {seed}")
+    check_attention(host(out), ro, host(lse), rl, f"{w.name} seed {seed}",
+                    outliers=w.outlier_frac > 0)
 
 
 # Rows with a 50x scale whose score on some head is a near-tie reached through
@@ -190,7 +191,8 @@ def test_decode_outlier_cancellation(m, seed):
     assert np.array_equal(host(codes), oc) and np.array_equal(host(scales), os_)
     out, lse = m.mla8_decode(codes, scales, t, lc, rc, dev(ql), dev(qr), sm)
     ro, rl = oracle.decode(oc, os_, t, lc, rc, ql, qr, sm)
-    worst = check_attention(host(out), ro, host(lse), rl, f"x50 outliers seed {seed}")
+    worst = check_attention(host(out), ro, host(lse), rl, f"x50 outliers seed {seed}",
+                            outliers=True)
     say(f"  worst err/bar {worst:.4f}")
     assert worst <= 0.5, f"scores below f32 grade: worst err/bar {worst:.3f}"
 
@@ -214,7 +216,8 @@ def test_decode_shapes(m, h, lc, rc, t):
     oc, os_ = oracle.quantize_rows(x)
     out, lse = m.mla8_decode(dev(oc), dev(os_), t, lc, rc, dev(ql), dev(qr), sm)
     ro, rl = oracle.decode(oc, os_, t, lc, rc, ql, qr, sm)
-    check_attention(host(out), ro, host(lse), rl, f"H={h} lc={lc} rc={rc} T={t}")
+    # row scales spread 100x over at most 4500 rows: a few rows carry each head
+    check_attention(host(out), ro, host(lse), rl, f"H={h} lc={lc} rc={rc} T={t}", few_rows=True)
 
 
 # The score operands scale each head's query by a power of two (largest |e|
@@ -240,15 +243,11 @@ def test_decode_split_count_invariance(m, splits):
     say(f"decode split invariance P={splits}")
     codes, scales, oc, os_ = _make_shadow(m, w, w.t_rows)
     ql, qr = W.queries(w)
-    prev = m.mla8_force_splits(splits)
-    try:
-        out, lse = m.mla8_decode(codes, scales, w.t_rows, w.lc, w.rc, dev(ql), dev(qr),
-                                 w.sm_scale)
-        o = host(out)
-    finally:
-        m.mla8_force_splits(prev)
+    out, lse = m.mla8_decode(codes, scales, w.t_rows, w.lc, w.rc, dev(ql), dev(qr),
+                             w.sm_scale, n_splits=splits)
+    o = host(out)
     ro, rl = oracle.decode(oc, os_, w.t_rows, w.lc, w.rc, ql, qr, w.sm_scale)
-    check_attention(o, ro, host(lse), rl, f"P={splits}")
+    check_attention(o, ro, host(lse), rl, f"P={splits}", outliers=True)
 
 
 def test_decode_degenerate_rows(m):
@@ -266,7 +265,7 @@ def test_decode_degenerate_rows(m):
     oc, os_ = oracle.quantize_rows(x)
     out, lse = m.mla8_decode(dev(oc), dev(os_), t, lc, rc, dev(ql), dev(qr), 0.1)
     ro, rl = oracle.decode(oc, os_, t, lc, rc, ql, qr, 0.1)
-    check_attention(host(out), ro, host(lse), rl, "degenerate rows")
+    check_attention(host(out), ro, host(lse), rl, "degenerate rows", outliers=True)
     # all-zero cache: uniform softmax over zero rows
     z = np.zeros((70, lc + rc), np.float32)
     oc, os_ = oracle.quantize_rows(z)
@@ -310,7 +309,8 @@ def test_decode_sel_edges(m, case):
     if case == "none_valid":
         assert np.all(host(out) == 0) and np.all(np.isneginf(host(lse)))
     else:
-        check_attention(host(out), ro, host(lse), rl, case)
+        # 1 to 131 distinct rows attended (all_rows: 1500)
+        check_attention(host(out), ro, host(lse), rl, case, few_rows=case != "all_rows")
 
 
 @pytest.mark.parametrize("h,n_q,t,lc,rc", [(3, 7, 300, 64, 16), (64, 5, 200, 512, 64),
@@ -327,12 +327,14 @@ def test_batch_small(m, h, n_q, t, lc, rc):
     oc, os_ = oracle.quantize_rows(x)
     out, lse = m.mla8_batch(dev(oc), dev(os_), t, lc, rc, dev(ql), dev(qr), pos0, sm)
     ro, rl = oracle.batch(oc, os_, t, lc, rc, ql, qr, pos0, sm)
-    check_attention(host(out), ro, host(lse), rl, f"batch H={h} S={n_q}")
+    # causal prefixes of 28 to 1999 rows
+    check_attention(host(out), ro, host(lse), rl, f"batch H={h} S={n_q}", few_rows=True)
 
 
-def test_batch_workload_sampled(m):
+def test_batch_workload_whole_queries(m):
     """Full-size causal batch (S=64, H=64, T=32768, 64 fresh rows appended
-    through the quantizer first), checked on sampled (query, head) pairs."""
+    through the quantizer first), checked on four whole queries (all 64 heads
+    each: the first, two inner ones and the last, which attends every row)."""
     w = W.BATCH
     base = w.t_rows - w.n_append
     say(f"batch {w.name}: build shadow")
@@ -349,36 +351,52 @@ def test_batch_workload_sampled(m):
     out, lse = m.mla8_batch(codes, scales, t, w.lc, w.rc, dev(ql), dev(qr), base, w.sm_scale)
     o, l = host(out), host(lse)
     assert np.all(np.isfinite(o)) and np.all(np.isfinite(l))
-    for s in (0, 1, 31, 63):
-        heads = np.array([0, 17, 42, 63])
-        ro, rl = oracle.decode(oc, os_, base + s + 1, w.lc, w.rc, ql[s, heads], qr[s, heads],
-                               w.sm_scale)
-        check_attention(o[s, heads], ro, l[s, heads], rl, f"batch s={s}")
+    for s in (0, 21, 42, 63):
+        say(f"batch {w.name}: oracle for query {s}, all {w.n_heads} heads")
+        ro, rl = oracle.decode(oc, os_, base + s + 1, w.lc, w.rc, ql[s], qr[s], w.sm_scale)
+        worst = check_attention(o[s], ro, l[s], rl, f"batch s={s}")
+        say(f"  query {s}: worst elementwise err/bar {worst:.4f}")
 
 
-def test_long_context_sampled(m):
-    """The long-context decode step at full size: 262143 quantized rows, one
-    fresh row appended through the quantizer, then all 262144 rows attended by
-    64 heads; sampled heads against the oracle, every head for sanity."""
+def test_long_context_step_full(m):
+    """The timed long-context step at full size, in the launch configuration
+    the benchmark times: a shadow of 262143 quantized rows, then one
+    mla8_append_decode call that quantizes the fresh row into row 262143 inside
+    the partial launch (the last tile of the last chunk) and attends all
+    262144 rows with 64 heads under the automatic 128-chunk plan.  Every head
+    and its lse against the oracle, and bit for bit against mla8_append +
+    mla8_decode on a second shadow."""
     w = W.LONG
-    say(f"{w.name}: build shadow")
-    x = W.rows(w, w.t_rows)
-    codes = torch.zeros((w.t_rows, w.d), dtype=torch.uint8, device=DEV)
-    scales = torch.zeros((w.t_rows,), dtype=torch.float32, device=DEV)
-    t = m.mla8_append(codes, scales, 0, dev(x[:-1]), w.lc, w.rc)
-    t = m.mla8_append(codes, scales, t, dev(x[-1:]), w.lc, w.rc)
-    assert t == w.t_rows
-    oc, os_ = oracle.quantize_rows(x)
-    assert np.array_equal(host(codes), oc)
-    assert np.array_equal(host(scales).view(np.uint32), os_.view(np.uint32))
+    T = w.t_rows
+    assert m.mla8_plan_splits(m.MLA8_OP_DECODE, T, w.n_heads) == 128
+    say(f"{w.name}: build two shadows of {T - 1} rows")
+    x = W.rows(w, T)
+    shadows = []
+    for _ in range(2):
+        codes = torch.zeros((T, w.d), dtype=torch.uint8, device=DEV)
+        scales = torch.zeros((T,), dtype=torch.float32, device=DEV)
+        assert m.mla8_append(codes, scales, 0, dev(x[:-1]), w.lc, w.rc) == T - 1
+        shadows.append((codes, scales))
     ql, qr = W.queries(w)
-    say(f"{w.name}: decode")
-    out, lse = m.mla8_decode(codes, scales, t, w.lc, w.rc, dev(ql), dev(qr), w.sm_scale)
-    o, l = host(out), host(lse)
-    assert np.all(np.isfinite(o)) and np.all(np.isfinite(l))
-    heads = np.array([0, 21, 63])
-    ro, rl = oracle.decode(oc, os_, t, w.lc, w.rc, ql[heads], qr[heads], w.sm_scale)
-    check_attention(o[heads], ro, l[heads], rl, w.name)
+    (ca, sa), (cb, sb) = shadows
+    say(f"{w.name}: mla8_append_decode (fresh row {T - 1})")
+    out_b, lse_b, tb = m.mla8_append_decode(cb, sb, T - 1, dev(x[-1:]), w.lc, w.rc, dev(ql),
+                                            dev(qr), w.sm_scale)
+    assert tb == T
+    say(f"{w.name}: mla8_append + mla8_decode")
+    assert m.mla8_append(ca, sa, T - 1, dev(x[-1:]), w.lc, w.rc) == T
+    out_a, lse_a = m.mla8_decode(ca, sa, T, w.lc, w.rc, dev(ql), dev(qr), w.sm_scale)
+    o, l = host(out_b), host(lse_b)
+    oc, os_ = oracle.quantize_rows(x)
+    assert np.array_equal(host(cb), oc), "shadow codes differ from the oracle quantizer"
+    assert np.array_equal(host(sb).view(np.uint32), os_.view(np.uint32))
+    assert np.array_equal(host(ca), host(cb)) and np.array_equal(host(sa), host(sb))
+    assert np.array_equal(host(out_a), o) and np.array_equal(host(lse_a), l), \
+        "the fused step differs from append + decode"
+    say(f"{w.name}: oracle, all {w.n_heads} heads over {T} rows")
+    ro, rl = oracle.decode(oc, os_, T, w.lc, w.rc, ql, qr, w.sm_scale)
+    worst = check_attention(o, ro, l, rl, w.name)
+    say(f"  worst elementwise err/bar {worst:.4f}")
 
 
 # The read-bandwidth reference: every 32-bit word of the buffer reaches the

@@ -79,7 +79,12 @@ def shadows(n_layers, cap, d):
 
 
 def random_rows(g, n_layers, t, d):
-    return ([g.integers(0, 256, (t, d), dtype=np.uint8) for _ in range(n_layers)],
+    """Random shadow rows as the quantizer writes them: any e4m3 byte but the
+    two NaN codes 0x7F / 0xFF, and finite positive scales."""
+    def codes():
+        c = g.integers(0, 256, (t, d), dtype=np.uint8)
+        return np.where((c & 0x7F) == 0x7F, c ^ 1, c).astype(np.uint8)
+    return ([codes() for _ in range(n_layers)],
             [g.random(t, dtype=np.float32) + 0.01 for _ in range(n_layers)])
 
 
@@ -140,9 +145,12 @@ def test_refusals(tmp_path):
     cases = [
         (lambda: m.mla8_kvfile_append(p, codes, scales, 4, 1, LC, RC), m.MLA8_E_RANGE),
         (lambda: m.mla8_kvfile_append(p, codes, scales, 6, 1, LC, RC), m.MLA8_E_RANGE),
-        (lambda: m.mla8_kvfile_append(p, codes, scales, 5, 1, LC, 32), m.MLA8_E_INVAL),
+        # shadows as wide as the call's lc + rc, so that the library sees the call
+        (lambda: m.mla8_kvfile_append(p, *shadows(2, 10, LC + 32), 5, 1, LC, 32),
+         m.MLA8_E_INVAL),
         (lambda: m.mla8_kvfile_append(p, codes[:1], scales[:1], 5, 1, LC, RC), m.MLA8_E_INVAL),
-        (lambda: m.mla8_kvfile_append(p, codes, scales, 5, 1, 72, RC), m.MLA8_E_UNSUPPORTED),
+        (lambda: m.mla8_kvfile_append(p, *shadows(2, 10, 72 + RC), 5, 1, 72, RC),
+         m.MLA8_E_UNSUPPORTED),
         (lambda: m.mla8_kvfile_load(p, *shadows(2, 4, D), LC, RC), m.MLA8_E_CAPACITY),
         (lambda: m.mla8_kvfile_load(str(tmp_path / "missing"), *shadows(2, 9, D), LC, RC),
          m.MLA8_E_IO),
@@ -152,6 +160,11 @@ def test_refusals(tmp_path):
         with pytest.raises(m.Mla8Error) as e:
             call()
         assert e.value.status == want
+    # buffers narrower than the call's rows never reach the library
+    with pytest.raises(ValueError, match="shape"):
+        m.mla8_kvfile_append(p, codes, scales, 5, 1, LC, 32)
+    with pytest.raises(ValueError, match="outside"):
+        m.mla8_kvfile_append(p, codes, scales, 5, 6, LC, RC)
     assert m.mla8_kvfile_info(p)["n_tokens"] == 5
     # a capacity refusal leaves the shadows untouched
     c2, s2 = shadows(2, 4, D)
@@ -219,3 +232,58 @@ def test_symbols_exported():
                  "mla8_kvfile_load"):
         assert hasattr(m.lib, name)
     assert m.lib.mla8_status_string(m.MLA8_E_IO)
+
+
+def test_unusable_headers_are_refused(tmp_path):
+    """A slot whose check matches but whose token count is absurd (2^63, which
+    an int64 cast would make negative) or larger than the body holds is not
+    used; an older slot that the body does hold is used instead."""
+    g = np.random.Generator(np.random.PCG64(11))
+    codes, scales = random_rows(g, 1, 6, D)
+    p = str(tmp_path / "h.mla8kv")
+    write_file(p, 2, list(zip(codes, scales)), LC, RC)
+    raw = bytearray(open(p, "rb").read())
+    for bad_n in (1 << 63, (1 << 64) - 1, 1 << 31, 7):
+        raw[:64] = slot_bytes(2, 1, LC, RC, bad_n, 5)
+        raw[64:128] = b"\0" * 64
+        open(p, "wb").write(bytes(raw))
+        with pytest.raises(m.Mla8Error) as e:
+            m.mla8_kvfile_info(p)
+        assert e.value.status == m.MLA8_E_IO, bad_n
+        c2, s2 = shadows(1, 8, D)
+        t = None
+        with pytest.raises(m.Mla8Error) as e:
+            t = m.mla8_kvfile_load(p, c2, s2, LC, RC)
+        assert e.value.status == m.MLA8_E_IO and t is None
+    # newest slot claims more tokens than the body holds; the older one fits
+    raw[:64] = slot_bytes(2, 1, LC, RC, 9, 5)
+    raw[64:128] = slot_bytes(2, 1, LC, RC, 4, 4)
+    open(p, "wb").write(bytes(raw))
+    assert m.mla8_kvfile_info(p)["n_tokens"] == 4
+    c2, s2 = shadows(1, 8, D)
+    assert m.mla8_kvfile_load(p, c2, s2, LC, RC) == 4
+    np.testing.assert_array_equal(c2[0][:4], codes[0][:4])
+
+
+@pytest.mark.parametrize("what", ["nan_code_pos", "nan_code_neg", "nan_scale", "neg_scale",
+                                  "inf_scale"])
+def test_corrupt_body_is_not_loaded(tmp_path, what):
+    g = np.random.Generator(np.random.PCG64(12))
+    codes, scales = random_rows(g, 2, 6, D)
+    p = str(tmp_path / "i.mla8kv")
+    if what == "nan_code_pos":
+        codes[1][3, 17] = 0x7F
+    elif what == "nan_code_neg":
+        codes[0][5, 0] = 0xFF
+    elif what == "nan_scale":
+        scales[1][2] = np.float32("nan")
+    elif what == "neg_scale":
+        scales[0][1] = np.float32(-0.5)
+    else:
+        scales[1][4] = np.float32("inf")
+    write_file(p, 2, list(zip(codes, scales)), LC, RC)
+    c2, s2 = shadows(2, 8, D)
+    with pytest.raises(m.Mla8Error) as e:
+        m.mla8_kvfile_load(p, c2, s2, LC, RC)
+    assert e.value.status == m.MLA8_E_IO
+    assert m.mla8_kvfile_info(p)["n_tokens"] == 6  # the header itself is fine

@@ -1,11 +1,26 @@
 """Comparison helpers shared by the GPU parity tests.
 
-Attention tolerance (stated for the absorbed fp8 decode path): per (query, head)
-output vector, max_k |gpu - ref| <= 1e-4 + 2e-3 * max_k |ref|, where ref is the
-fp64 oracle run on the same e4m3 bytes and scales.  The per-vector (normwise)
-form is used because near-tied, near one-hot heads (rows with outlier amax)
-make single small elements ill-conditioned even for exact f32 arithmetic.
-lse is checked to |gpu - ref| <= 1e-4 + 2e-3 * |ref|.
+Attention tolerance (stated for the absorbed fp8 decode path): max relative
+error 2e-3 with absolute floor 1e-4 against the fp64 oracle run on the same
+e4m3 bytes and scales.
+
+* Elementwise, the default: |gpu - ref| <= 1e-4 + 2e-3 * |ref| for every
+  output element.
+* Per (query, head) output vector: max_k |gpu - ref| <= 1e-4 + 2e-3 *
+  max_k |ref|, for two kinds of case, each named where it is used:
+  - caches with outlier rows (a 50x or larger row scale): near-tied, near
+    one-hot heads between two such rows make single small elements
+    ill-conditioned even for exact f32 arithmetic;
+  - calls where a handful of rows carry the softmax (a few selected rows, a
+    short causal prefix, rows whose scales spread 100x): there the context
+    weights' fp16 rounding (2^-11 relative) moves a near-zero element by
+    about 2^-12 of the rows' magnitude, above the 1e-4 floor, while every
+    vector stays within its bar.  The workload configurations, whose softmax
+    spreads over many rows, meet the elementwise form.
+
+lse is checked to |gpu - ref| <= 1e-4 + 2e-3 * |ref| in both cases.  The
+worst err/bar of the form that applies is returned; the elementwise worst is
+also reported in failure messages.
 """
 from __future__ import annotations
 
@@ -15,16 +30,36 @@ ABS = 1e-4
 REL = 2e-3
 
 
-def check_attention(out_gpu, out_ref, lse_gpu=None, lse_ref=None, what=""):
+def elementwise_ratio(g, r):
+    """Worst elementwise err/bar."""
+    g = np.asarray(g, np.float64)
+    r = np.asarray(r, np.float64)
+    if g.size == 0:
+        return 0.0
+    return float((np.abs(g - r) / (ABS + REL * np.abs(r))).max())
+
+
+def check_attention(out_gpu, out_ref, lse_gpu=None, lse_ref=None, what="", outliers=False,
+                    few_rows=False):
+    """outliers / few_rows: the per-vector form applies (see above)."""
+    per_vector = outliers or few_rows
     g = np.asarray(out_gpu, np.float64).reshape(-1, out_ref.shape[-1])
     r = np.asarray(out_ref, np.float64).reshape(-1, out_ref.shape[-1])
     assert np.all(np.isfinite(g)), f"{what}: non-finite output"
     err = np.abs(g - r).max(1)
     bar = ABS + REL * np.abs(r).max(1)
-    worst = float((err / bar).max()) if err.size else 0.0
+    worst_vec = float((err / bar).max()) if err.size else 0.0
+    worst_el = elementwise_ratio(g, r)
     bad = np.flatnonzero(err > bar)
     assert bad.size == 0, (f"{what}: {bad.size} of {err.size} vectors out of tolerance; "
-                           f"worst err/bar {worst:.3f} at vector {int(np.argmax(err / bar))}")
+                           f"worst err/bar {worst_vec:.3f} at vector {int(np.argmax(err / bar))}"
+                           f" (elementwise worst {worst_el:.3f})")
+    if not per_vector:
+        el_bar = ABS + REL * np.abs(r)
+        n_bad = int(np.count_nonzero(np.abs(g - r) > el_bar))
+        assert n_bad == 0, (f"{what}: {n_bad} of {g.size} elements out of the elementwise "
+                            f"tolerance; worst err/bar {worst_el:.3f} (per-vector worst "
+                            f"{worst_vec:.3f})")
     if lse_ref is not None:
         lg = np.asarray(lse_gpu, np.float64).reshape(-1)
         lr = np.asarray(lse_ref, np.float64).reshape(-1)
@@ -32,4 +67,4 @@ def check_attention(out_gpu, out_ref, lse_gpu=None, lse_ref=None, what=""):
         assert np.array_equal(np.isneginf(lg), inf), f"{what}: lse -inf mismatch"
         d = np.abs(lg[~inf] - lr[~inf])
         assert np.all(d <= ABS + REL * np.abs(lr[~inf])), f"{what}: lse max err {d.max()}"
-    return worst
+    return worst_vec if per_vector else worst_el
