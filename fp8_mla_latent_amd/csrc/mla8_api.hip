@@ -8,6 +8,18 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <atomic>
+#include <mutex>
+
+// Scratch of mla8_append_decode_noalloc, for callers that cannot allocate: the
+// split-T partials go to this file-scope device array instead of a caller
+// workspace.  Each GPU the library runs on holds its own copy until the
+// process ends.  Host code never passes the array's name to a kernel (on the
+// host it is only a stand-in for the symbol): its device address comes from
+// hipGetSymbolAddress, once per device.
+static constexpr size_t kScratchBytes = size_t(20) << 20;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
 namespace {
 
 using namespace mla8;
@@ -314,12 +326,11 @@ int mla8_decode_sel_mx(const uint8_t* kv_rows, const float* kv_scales, int64_t t
 
 // The fused step and the causal batch over mixed rows: the e4m3 entry
 // points' checks with the mixed shape; the kernels are the mixed instances.
-static int append_decode_layout(uint8_t* kv, float* kv_scales, int64_t cap_rows, int64_t* t_rows,
-                                const float* x_new, int64_t n_new, int32_t lc, int32_t rc,
-                                const float* q_lat, const float* q_rope, int32_t n_heads,
-                                float sm_scale, float* out, float* lse, void* workspace,
-                                size_t ws_bytes, void* stream, const mla8_opts* opts,
-                                int32_t layout)
+// Host checks of the fused append + decode step (no HIP call).
+static int append_decode_check(const uint8_t* kv, const float* kv_scales, int64_t cap_rows,
+                               const int64_t* t_rows, const float* x_new, int64_t n_new,
+                               int32_t lc, int32_t rc, const float* q_lat, const float* q_rope,
+                               int32_t n_heads, float sm_scale, const float* out)
 {
     if (!kv || !kv_scales || !t_rows || !x_new)
         return MLA8_E_INVAL;
@@ -331,11 +342,22 @@ static int append_decode_layout(uint8_t* kv, float* kv_scales, int64_t cap_rows,
         return MLA8_E_RANGE;
     if (n_new > cap_rows - *t_rows)
         return MLA8_E_CAPACITY;
-    const int64_t t_new = *t_rows + n_new;
-    int st = check_decode_common(kv, kv_scales, t_new, lc, rc, q_lat, q_rope, n_heads, sm_scale,
-                                 out);
+    return check_decode_common(kv, kv_scales, *t_rows + n_new, lc, rc, q_lat, q_rope, n_heads,
+                               sm_scale, out);
+}
+
+static int append_decode_layout(uint8_t* kv, float* kv_scales, int64_t cap_rows, int64_t* t_rows,
+                                const float* x_new, int64_t n_new, int32_t lc, int32_t rc,
+                                const float* q_lat, const float* q_rope, int32_t n_heads,
+                                float sm_scale, float* out, float* lse, void* workspace,
+                                size_t ws_bytes, void* stream, const mla8_opts* opts,
+                                int32_t layout)
+{
+    int st = append_decode_check(kv, kv_scales, cap_rows, t_rows, x_new, n_new, lc, rc, q_lat,
+                                 q_rope, n_heads, sm_scale, out);
     if (st != MLA8_OK)
         return st;
+    const int64_t t_new = *t_rows + n_new;
     st = run_attention(MLA8_OP_DECODE, kv, kv_scales, t_new, lc, rc, nullptr, t_new, q_lat,
                        q_rope, n_heads, n_heads, 0, sm_scale, out, lse, workspace, ws_bytes,
                        stream, opts, x_new, kv, kv_scales, *t_rows, n_new, layout);
@@ -402,6 +424,56 @@ int mla8_append_decode(uint8_t* kv_codes, float* kv_scales, int64_t cap_rows, in
         return st;
     return append_decode_layout(kv_codes, kv_scales, cap_rows, t_rows, x_new, n_new, lc, rc,
                                 q_lat, q_rope, n_heads, sm_scale, out, lse, workspace, ws_bytes,
+                                stream, opts, kE4m3);
+}
+
+// Device address of this GPU's copy of `scratch`, looked up once per device
+// (with that device current) and kept.
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_addr[kMaxDevices];
+std::mutex g_scratch_mu;
+
+static int scratch_address(void** addr)
+{
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+        return MLA8_E_HIP;
+    void* p = g_scratch_addr[dev].load(std::memory_order_acquire);
+    if (p == nullptr) {
+        std::lock_guard<std::mutex> lock(g_scratch_mu);
+        p = g_scratch_addr[dev].load(std::memory_order_relaxed);
+        if (p == nullptr) {
+            if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr)
+                return MLA8_E_HIP;
+            g_scratch_addr[dev].store(p, std::memory_order_release);
+        }
+    }
+    *addr = p;
+    return MLA8_OK;
+}
+
+int mla8_append_decode_noalloc(uint8_t* kv_codes, float* kv_scales, int64_t cap_rows,
+                               int64_t* t_rows, const float* x_new, int64_t n_new, int32_t lc,
+                               int32_t rc, const float* q_lat, const float* q_rope,
+                               int32_t n_heads, float sm_scale, float* out, float* lse,
+                               void* stream, const mla8_opts* opts)
+{
+    int st = check_shape(lc, rc);
+    if (st != MLA8_OK)
+        return st;
+    st = append_decode_check(kv_codes, kv_scales, cap_rows, t_rows, x_new, n_new, lc, rc, q_lat,
+                             q_rope, n_heads, sm_scale, out);
+    if (st != MLA8_OK)
+        return st;
+    const Plan p = make_plan(MLA8_OP_DECODE, *t_rows + n_new, n_heads, forced_splits(opts));
+    if (ws_bytes_for(p, n_heads, lc) > kScratchBytes)
+        return MLA8_E_SCRATCH;
+    void* ws = nullptr;
+    st = scratch_address(&ws);
+    if (st != MLA8_OK)
+        return st;
+    return append_decode_layout(kv_codes, kv_scales, cap_rows, t_rows, x_new, n_new, lc, rc,
+                                q_lat, q_rope, n_heads, sm_scale, out, lse, ws, kScratchBytes,
                                 stream, opts, kE4m3);
 }
 
@@ -521,6 +593,10 @@ const char* mla8_status_string(int status)
                "lc+rc<=640 (indexer: ihd 128, n_ih a multiple of 16 up to 64, top_k <= 4096)";
     case MLA8_E_HIP: return "HIP launch or copy failed";
     case MLA8_E_IO: return "file I/O failed, or no valid header in the file";
+    case MLA8_E_SCRATCH:
+        return "the call needs more than the library's static scratch (MLA8_SCRATCH_BYTES) of "
+               "mla8_append_decode_noalloc: fewer heads, rows or forced splits, or "
+               "mla8_append_decode with a workspace";
     default: return "unknown status";
     }
 }
@@ -528,6 +604,7 @@ const char* mla8_status_string(int status)
 const char* mla8_version(void) { return "mla8 0.1.0 gfx950"; }
 
 static_assert(kStreamWords == MLA8_STREAM_WORDS, "stream-read output words");
+static_assert(kScratchBytes == MLA8_SCRATCH_BYTES, "scratch size in the header");
 
 int mla8_stream_read(const void* p, int64_t bytes, uint32_t* out, void* stream)
 {

@@ -35,6 +35,8 @@ MLA8_E_WORKSPACE = -4
 MLA8_E_UNSUPPORTED = -5
 MLA8_E_HIP = -6
 MLA8_E_IO = -7
+MLA8_E_SCRATCH = -8
+MLA8_SCRATCH_BYTES = 20 << 20
 MLA8_OP_DECODE = 0
 MLA8_OP_DECODE_SEL = 1
 MLA8_OP_BATCH = 2
@@ -45,7 +47,7 @@ MLA8_STREAM_WORDS = 32768
 EXPORTED = ("mla8_quantize_rows", "mla8_append", "mla8_decode", "mla8_append_decode",
             "mla8_decode_sel", "mla8_batch", "mla8_quantize_rows_mx", "mla8_append_mx",
             "mla8_decode_mx", "mla8_decode_sel_mx", "mla8_append_decode_mx", "mla8_batch_mx",
-            "mla8_index_topk", "mla8_kvfile_create",
+            "mla8_append_decode_noalloc", "mla8_index_topk", "mla8_kvfile_create",
             "mla8_kvfile_info", "mla8_kvfile_append", "mla8_kvfile_load",
             "mla8_workspace_bytes", "mla8_plan_splits",
             "mla8_status_string", "mla8_version", "mla8_test_encode", "mla8_stream_read")
@@ -77,6 +79,8 @@ def _load() -> ctypes.CDLL:
         "mla8_decode": (ctypes.c_int, [P, P, i64, i32, i32, P, P, i32, f32, P, P, P, sz, P, O]),
         "mla8_append_decode": (ctypes.c_int, [P, P, i64, ctypes.POINTER(i64), P, i64, i32, i32,
                                               P, P, i32, f32, P, P, P, sz, P, O]),
+        "mla8_append_decode_noalloc": (ctypes.c_int, [P, P, i64, ctypes.POINTER(i64), P, i64,
+                                                      i32, i32, P, P, i32, f32, P, P, P, O]),
         "mla8_decode_sel": (ctypes.c_int,
                             [P, P, i64, i32, i32, P, i64, P, P, i32, f32, P, P, P, sz, P, O]),
         "mla8_batch": (ctypes.c_int,
@@ -354,6 +358,31 @@ def mla8_append_decode(kv_codes, kv_scales, t_rows: int, x_new, lc: int, rc: int
                              _ptr(out), _ptr(lse), _ptr(ws), ws.numel(), _stream(q_lat), _o(o)),
            _fn)
     return out, lse, int(t.value)
+
+
+def mla8_append_decode_noalloc(kv_codes, kv_scales, t_rows: int, x_new, lc: int, rc: int,
+                               q_lat, q_rope, sm_scale: float, out, lse=None,
+                               n_splits: int = 0) -> int:
+    """As mla8_append_decode with the library's static scratch instead of a
+    workspace; allocates nothing, so `out` ([H, lc] f32) must be given (lse
+    [H] f32 optional).  Returns the new t_rows."""
+    cap = _shadow(kv_codes, kv_scales, lc + rc)
+    dev = kv_codes.device
+    _dev(x_new, "x_new", torch.float32, (None, lc + rc), dev)
+    _dev(q_lat, "q_lat", torch.float32, (None, lc), dev)
+    h = q_lat.shape[0]
+    _queries(q_lat, q_rope, (h,), lc, rc, dev)
+    _dev(out, "out", torch.float32, (h, lc), dev)
+    if lse is not None:
+        _dev(lse, "lse", torch.float32, (h,), dev)
+    o = _opts(n_splits)
+    t = ctypes.c_int64(t_rows)
+    _check(lib.mla8_append_decode_noalloc(_ptr(kv_codes), _ptr(kv_scales), cap, ctypes.byref(t),
+                                          _ptr(x_new), x_new.shape[0], lc, rc, _ptr(q_lat),
+                                          _ptr(q_rope), h, float(sm_scale), _ptr(out),
+                                          _ptr(lse), _stream(q_lat), _o(o)),
+           "mla8_append_decode_noalloc")
+    return int(t.value)
 
 
 def mla8_append_decode_mx(kv_rows, kv_scales, t_rows: int, x_new, lc: int, rc: int, q_lat,

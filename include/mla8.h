@@ -60,7 +60,8 @@ enum {
     MLA8_E_WORKSPACE = -4,   /* workspace smaller than mla8_workspace_bytes() */
     MLA8_E_UNSUPPORTED = -5, /* shape outside the supported set (see above) */
     MLA8_E_HIP = -6,         /* a HIP launch, copy or device query failed */
-    MLA8_E_IO = -7           /* shadow file: I/O failed or no valid header */
+    MLA8_E_IO = -7,          /* shadow file: I/O failed or no valid header */
+    MLA8_E_SCRATCH = -8      /* beyond the static scratch of mla8_append_decode_noalloc */
 };
 
 /* Operation codes for mla8_workspace_bytes. */
@@ -156,6 +157,31 @@ MLA8_API int mla8_append_decode(uint8_t* kv_codes, float* kv_scales, int64_t cap
                        int32_t rc, const float* q_lat, const float* q_rope, int32_t n_heads,
                        float sm_scale, float* out, float* lse, void* workspace,
                        size_t ws_bytes, void* stream, const mla8_opts* opts);
+
+/*
+ * mla8_append_decode for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  Same arguments, checks, result and *t_rows update as
+ * mla8_append_decode, without `workspace`: the split-T partials live in the
+ * library's own static device array of MLA8_SCRATCH_BYTES, one copy per GPU,
+ * held until the process ends.  The call allocates nothing (no hipMalloc, no
+ * allocating library routine); it uses the scratch of the current device, so
+ * `stream` must belong to that device.  The automatic plan fits for any
+ * head count up to 8192 with lc <= 512 (its partials take at most about
+ * 16.8 MB); a call needing more (mla8_workspace_bytes(MLA8_OP_DECODE, *t_rows + n_new,
+ * n_heads, 1, lc, opts) > MLA8_SCRATCH_BYTES, e.g. with many forced splits)
+ * returns MLA8_E_SCRATCH before any HIP call.  Calls on one GPU share its
+ * scratch: calls that overlap in time on one GPU (two streams, two threads)
+ * race; the scratch needs no clearing between calls.
+ * Errors: those of mla8_append_decode except E_WORKSPACE, plus E_SCRATCH.
+ */
+#define MLA8_SCRATCH_BYTES (20u << 20)
+MLA8_API int mla8_append_decode_noalloc(uint8_t* kv_codes, float* kv_scales, int64_t cap_rows,
+                                        int64_t* t_rows, const float* x_new, int64_t n_new,
+                                        int32_t lc, int32_t rc, const float* q_lat,
+                                        const float* q_rope, int32_t n_heads, float sm_scale,
+                                        float* out, float* lse, void* stream,
+                                        const mla8_opts* opts);
 
 /*
  * Selected-row (DSA gather) decode [KV8-long, DSA bullet]: as mla8_decode, but

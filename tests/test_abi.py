@@ -43,7 +43,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_status_strings():
-    for st in (0, -1, -2, -3, -4, -5, -6):
+    for st in (0, -1, -2, -3, -4, -5, -6, -7, -8):
         assert m.mla8_status_string(st) and m.mla8_status_string(st) != "unknown status"
     assert m.mla8_status_string(-99) == "unknown status"
     assert "gfx950" in m.mla8_version()
@@ -195,6 +195,38 @@ def test_append_decode_refuses():
         args[idx] = val
         assert f(*args) == want, (idx, val)
         assert t.value == 10  # never advanced on an error
+
+
+def test_append_decode_noalloc_refuses():
+    """Host checks only (no HIP call is reached): the usual refusals, and a
+    call whose partials would not fit the static scratch."""
+    f = m.lib.mla8_append_decode_noalloc
+    t0 = 262143
+    t = ctypes.c_int64(t0)
+    base = [FAKE, FAKE, 300000, ctypes.byref(t), FAKE, 1, 512, 64, FAKE, FAKE, 64, 0.1, FAKE,
+            None, None, None]
+    too_many = m.Mla8Opts(1000, None, None)   # 1000 chunks x 64 heads x 514 x 4 B > 20 MiB
+    ok_splits = m.Mla8Opts(128, None, None)
+    assert m.lib.mla8_workspace_bytes(m.MLA8_OP_DECODE, 262144, 64, 1, 512,
+                                      ctypes.byref(too_many)) > m.MLA8_SCRATCH_BYTES
+    assert m.lib.mla8_workspace_bytes(m.MLA8_OP_DECODE, 262144, 64, 1, 512,
+                                      ctypes.byref(ok_splits)) <= m.MLA8_SCRATCH_BYTES
+    # the automatic plan fits for any head count up to 8192 (lc 512)
+    for h in (1, 16, 64, 100, 128, 1000, 8192):
+        assert m.lib.mla8_workspace_bytes(m.MLA8_OP_DECODE, 1 << 20, h, 1, 512, None) <= \
+            m.MLA8_SCRATCH_BYTES, h
+    for idx, val, want in [(4, None, m.MLA8_E_INVAL),         # no fresh rows
+                           (5, 0, m.MLA8_E_INVAL),            # n_new = 0
+                           (5, 65, m.MLA8_E_RANGE),           # more than the fused maximum
+                           (2, t0, m.MLA8_E_CAPACITY),        # shadow full
+                           (6, 500, m.MLA8_E_UNSUPPORTED),
+                           (12, None, m.MLA8_E_INVAL),        # no out
+                           (15, ctypes.byref(too_many), m.MLA8_E_SCRATCH)]:
+        args = list(base)
+        args[idx] = val
+        assert f(*args) == want, (idx, val)
+        assert t.value == t0  # never advanced on an error
+    assert "scratch" in m.mla8_status_string(m.MLA8_E_SCRATCH)
 
 
 def test_index_topk_refuses():
