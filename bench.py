@@ -71,7 +71,7 @@ def parse():
     ap.add_argument("--cpu-heads-one-core", type=int, default=2,
                     help="heads of the one-thread CPU-oracle sample (full T, scaled)")
     ap.add_argument("--traffic", type=str,
-                    default=os.path.join(ROOT, "profiles", "k_split_partial_long_t262144_traffic.txt"),
+                    default=os.path.join(ROOT, "profiles", "k_partial32_long_t262144_traffic.txt"),
                     help="calibrated rocprofv3 FETCH_SIZE + WRITE_SIZE bytes per partial launch "
                          "(JSON); used only while the kernel source still matches its hash")
     ap.add_argument("--workload", default="long_t262144",
@@ -533,7 +533,7 @@ def bench_dsv3(args):
         "roofline": {"bound": "mfma", "achieved": round(tflops, 1),
                      "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(tflops / MFMA_F16_PEAK_TFLOPS, 4), "traffic": None,
-                     "kernel": "k_split_partial<9,false>", "kernel_us": round(part_us, 3),
+                     "kernel": "k_partial32", "kernel_us": round(part_us, 3),
                      "algorithmic_flops": flops},
         "cpu_baseline": cpu,
         "parity": parity,
@@ -985,14 +985,14 @@ def main():
     traffic = None
     if args.traffic and os.path.exists(args.traffic):
         rec = json.load(open(args.traffic))
-        src = os.path.join(ROOT, "fp8_mla_latent_amd", "csrc", "mla8_kernels.hip")
+        src = os.path.join(ROOT, "fp8_mla_latent_amd", "csrc", "mla8_partial32.hip")
         if rec.get("kernel_code_sha256") == kernel_code_sha256(src):
             traffic = rec.get("bytes_per_launch")
         else:
             log("traffic counters were taken on other kernel code: reporting null")
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                "kernel": "k_split_partial<9,false>", "kernel_us": round(part_us, 3),
+                "kernel": "k_partial32", "kernel_us": round(part_us, 3),
                 "kernel_us_p10_p90": [round(float(np.percentile(durs, 10)), 3),
                                       round(float(np.percentile(durs, 90)), 3)],
                 "algorithmic_bytes": alg_bytes}

@@ -20,7 +20,8 @@ import sys
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
-SRC = [os.path.join(PKG, "csrc", f) for f in ("mla8_kernels.hip", "mla8_index.hip", "mla8_kvfile.hip",
+SRC = [os.path.join(PKG, "csrc", f) for f in ("mla8_kernels.hip", "mla8_partial32.hip",
+                                                   "mla8_index.hip", "mla8_kvfile.hip",
                                                    "mla8_api.hip")]
 LIB = os.path.join(PKG, "libmla8.so")
 

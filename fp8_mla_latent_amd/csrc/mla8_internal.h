@@ -98,6 +98,11 @@ hipError_t launch_quantize_mx(const float* x, int64_t n_rows, int32_t lc, int32_
 hipError_t launch_test_encode(const float* x, int64_t n, uint8_t* codes, hipStream_t stream);
 constexpr int kStreamWords = 32768;  // output words of the stream-read reference
 hipError_t launch_stream_read(const void* p, int64_t bytes, uint32_t* out, hipStream_t stream);
+// The 32x32x16-MFMA partial kernel (mla8_partial32.hip): dense e4m3 rows of
+// the Lc = 512, Rc = 64 shape, with or without the fused append.
+bool partial32_applies(const AttnArgs& a);
+void launch_partial32(const AttnArgs& a, hipStream_t stream);
+
 // ev_before / ev_after (may be null) are recorded around the partial kernel.
 hipError_t launch_attention(const AttnArgs& a, hipStream_t stream, hipEvent_t ev_before,
                             hipEvent_t ev_after);

@@ -1,0 +1,717 @@
+// Split-T partial kernel on the 32x32x16 fp16 MFMA, for the DeepSeek-V3 row
+// shape (Lc = 512, Rc = 64: 576 e4m3 bytes per row), dense rows with the
+// optional fused append of fresh rows.  Same result contract as
+// k_split_partial: per (row chunk, query-head) the online-softmax partial
+// (m in log2 units, z, cl = sum_t p_t scale_t x_t), merged by k_merge.
+//
+// Method source: colibri PR #300 "KV8 long-context CUDA: fp8 device shadow,
+// split-T kernels, DSA-aware gather", second commit ("KV8 long-context
+// CUDA"): split-T blocks emitting online-softmax partials (cl[K], m, z) and a
+// log-sum-exp merge; first commit ("KV8 base"): the latent row is both key
+// and value, the row scale is hoisted out of the dot, the producer quantizes
+// the fresh row.
+//
+// gfx950 design.  One workgroup = one row chunk x 32 query-heads, 512 threads,
+// one workgroup per CU; waves 0-3 score, waves 4-7 accumulate the context, so
+// each SIMD runs one wave of each role.  Measured on MI355X: the kernel is
+// bound by each SIMD's VALU issue (an e4m3 -> fp16 widening instruction
+// holds it about 6.5 cycles, other VALU instructions 4, a 32x32x16 MFMA a
+// few), next to the matrix pipe (32 cycles per 32x32x16 MFMA); the memory
+// stream is not the limit (the same kernel with its row loads removed takes
+// the same cycles per tile).  Hence:
+//   * every row byte is widened once for the scores and once for the
+//     context.  A score wave takes 32 rows x half of K (18 K steps of 16)
+//     for all 32 heads: columns = heads of one 32x32x16 MFMA, and each
+//     widened A operand feeds two MFMAs, the fp16 hi and lo query terms,
+//     into one accumulator.  The two K halves of a row half are added
+//     through LDS one phase later, each wave taking half of the values;
+//   * the context O[32 heads][32 columns] += W . X runs on the same MFMA with
+//     the transposed row bytes (ds_read_b64_tr_b8) widened to fp16;
+//   * a 64-row tile is stored as 16-row x 64-byte blocks of 16-byte slots
+//     (slot r + 16 c of a block holds row r, bytes 16 c ..): one direct load
+//     (global_load_lds_dwordx4) fills a block, a score read is four linear
+//     256-byte runs and a transposed context read eight consecutive slots, so
+//     neither reader meets a bank conflict;
+//   * the scores' and the context's readers of a tile both read it in the
+//     phase it is scored (the context keeps the bytes in registers for two
+//     phases), so a three-stage ring keeps two tiles in flight;
+//   * the lazy-max check is a per-wave flag (any weight or probability above
+//     2^8, or not finite) instead of cross-lane check sums.
+#include "mla8_device.h"
+#include "mla8_internal.h"
+#include "mla8_pipe.h"
+
+namespace mla8 {
+
+namespace p32 {
+constexpr int TR = kTileRows;            // 64 rows per tile
+constexpr int HG = kHeadsPerGroup;       // 32 query-heads per workgroup
+constexpr int LC = 512, RC = 64, D = LC + RC;
+constexpr int NCB = D / 64;              // 9 column blocks of 64 bytes
+constexpr int STAGE = TR * D;            // 36,864 bytes per tile
+constexpr int NST = 3;                   // ring stages
+constexpr int DIST = 2;                  // tiles issued ahead
+constexpr int NKS = D / 16;              // 36 score K steps of 16
+constexpr int KH = NKS / 2;              // 18 K steps per score wave
+constexpr int WSTR = TR + 8;             // weight row stride (halves)
+constexpr int NINS = STAGE / 1024;       // 36 row DMA instructions per tile
+constexpr int KW = NINS / 4;             // 9 per context wave
+// LDS map (bytes)
+constexpr int NSC = 4;                   // row-scale slots: tile t in slot t % 4
+constexpr int SC = NST * STAGE;          // f32 [NSC][TR] row scales
+constexpr int W = SC + NSC * TR * 4;     // f16 [2][HG][WSTR] weights
+constexpr int XC = W + 2 * HG * WSTR * 2;  // f32x4 [2][2 rh][2 kh][2][64] partial scores
+constexpr int FL = XC + 2 * 2 * 2 * 2 * 64 * 16;  // u32 [2][4] overflow flags
+constexpr int CR = FL + 2 * 4 * 4;       // float2 [HG][4] exact tile maxima (head, row quarter)
+constexpr int Z = CR + HG * 4 * 8;       // f32 [4][HG] z per score wave
+constexpr int HK = Z + 4 * HG * 4;       // i32 [HG] query scaling exponent
+constexpr int UV = HK + HG * 4;          // f32x4 [4 waves][4][64]: u, scale of the weighed tile
+constexpr int AL = UV + 4 * 4 * 64 * 16; // f32 [4 context waves][HG] accumulator factors
+constexpr int END = AL + 4 * HG * 4;
+// query operand staging (one term at a time): stage 2, first filled in phase 0
+constexpr int QT = 2 * STAGE;
+static_assert(NKS * 64 * 16 <= STAGE, "one query term fits a stage");
+static_assert(END <= 160 * 1024, "LDS budget");
+static_assert(NINS % 4 == 0, "row DMAs split evenly over the context waves");
+}  // namespace p32
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef int v2i32 __attribute__((ext_vector_type(2)));
+
+// sched_barrier mask: VALU, SALU, transcendental, VMEM and LDS writes may be
+// scheduled across; LDS reads and MFMAs stay on their side
+constexpr int kNoDsReadCross = 0x2 | 0x4 | 0x10 | 0x20 | 0x40 | 0x200 | 0x400;
+
+__device__ __forceinline__ f32x16 mfma32(f16x8 a, f16x8 b, f32x16 c)
+{
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
+
+__global__ __launch_bounds__(kThreads, 1) void k_partial32(AttnArgs a)
+{
+    using namespace p32;
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[END];
+    float* const s_sc = reinterpret_cast<float*>(lds + SC);
+    _Float16* const s_w = reinterpret_cast<_Float16*>(lds + W);
+    uint32_t* const s_fl = reinterpret_cast<uint32_t*>(lds + FL);
+    float2* const s_cr2 = reinterpret_cast<float2*>(lds + CR);
+    float* const s_z = reinterpret_cast<float*>(lds + Z);
+    int* const s_k = reinterpret_cast<int*>(lds + HK);
+    const uint32_t lds_u32 = (uint32_t)(uintptr_t)(MLA8_LDS uint8_t*)lds;
+
+    const int tid = threadIdx.x;
+    // w through readfirstlane: the compiler then knows the role branches are
+    // uniform and keeps the two roles' register live ranges apart
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, n = lane & 15;
+
+    // Workgroup -> (chunk, head group), the two head groups of a chunk on one
+    // XCD back to back (dispatch is round-robin over the 8 XCDs).
+    int chunk, grp;
+    {
+        const int b = blockIdx.x;
+        if ((a.n_chunks & 7) == 0) {
+            const int x = b & 7, r = b >> 3;
+            chunk = (r / a.n_groups) * 8 + x;
+            grp = r % a.n_groups;
+        } else {
+            chunk = b / a.n_groups;
+            grp = b % a.n_groups;
+        }
+    }
+    const int qh0 = grp * HG;
+    const int c0 = chunk * a.chunk_rows;
+    const int c1 = min(a.n_list, c0 + a.chunk_rows);
+    const int ntiles = c1 > c0 ? (c1 - c0 + TR - 1) / TR : 0;
+
+    // ---- row stream: the context waves (4-7) issue every direct load, KW row
+    // DMAs per tile each (instruction k = wi + 4 i fills block k = 9 rb + cb:
+    // lane r + 16 c loads row 16 rb + r, bytes 64 cb + 16 c ..), and wave 4
+    // one more for the 64 row scales, so a fixed per-wave vmcnt marks a tile
+    // complete.  A ragged last tile (nv < 64 rows left) loads the list's last
+    // 64 rows instead (the list holds at least 64): its first 64 - nv rows,
+    // already attended as part of the previous tile or chunk, get no weight.
+    const bool ctx_wave = w >= 4;
+    const int wi = ctx_wave ? w - 4 : 0;
+    const bool dma_lead = w == 4;
+    // lane r + 16 c of instruction i: row r of the block, bytes 16 c ..; the
+    // block's own offset in the tile (wave-uniform) goes to the scalar base
+    const uint32_t lane_off = (uint32_t)((lane & 15) * D + 16 * (lane >> 4));
+    auto blk_k = [&](int i) __attribute__((always_inline)) { return wi + 4 * i; };
+    auto blk_ofs = [&](int k) __attribute__((always_inline)) {  // 16 rb rows + 64 cb bytes
+        return (uint32_t)(64 * (k + 135 * (k / NCB)));
+    };
+    auto issue = [&](int t, int st, auto I0_, auto I1_) __attribute__((always_inline)) {
+        constexpr int I0 = decltype(I0_)::value, I1 = decltype(I1_)::value;
+        const uint32_t xst = lds_u32 + (uint32_t)(st * STAGE);
+        // tile t's scales are read until phase t + 1 (its weights), past the
+        // loads of tile t + 3 into its ring stage: a ring of their own
+        const uint32_t sct = lds_u32 + (uint32_t)(SC + (t & (NSC - 1)) * TR * 4);
+        const int p0 = min(c0 + t * TR, c1 - TR);
+        const uint8_t* tb = a.codes + (size_t)p0 * D;
+#pragma unroll
+        for (int i = I0; i < I1; ++i) {
+            const int k = blk_k(i);
+            dma_b128_s(tb + blk_ofs(k), lane_off, xst + (uint32_t)(1024 * k));
+        }
+        if (I1 == KW && dma_lead)
+            dma_b32_s(a.scales + p0, (uint32_t)(4 * lane), sct);
+    };
+    using IC0 = std::integral_constant<int, 0>;
+    using ICA = std::integral_constant<int, 3>;
+    using ICB = std::integral_constant<int, 6>;
+    using ICK = std::integral_constant<int, KW>;
+    static_assert(KW == 9, "three issue points of three loads");
+    auto wait_tile = [&](bool next_in_flight) __attribute__((always_inline)) {
+        if (next_in_flight) {
+            if (dma_lead)
+                wait_vmcnt<KW + 1>();
+            else
+                wait_vmcnt<KW>();
+        } else {
+            wait_vmcnt<0>();
+        }
+    };
+
+    // ---- fused append: fresh rows [f0, f1) of this chunk are quantized into
+    // the shadow by this workgroup before any wave streams them.  A wave's
+    // vector memory operations complete in issue order: fresh rows that start
+    // at tile DIST + 1 or later are quantized by the context waves after the
+    // prologue (their per-tile waits then cover the stores before the phase
+    // barrier that precedes those tiles' loads); otherwise every wave
+    // quantizes, and waits, before the first load.
+    // A ragged last tile also loads rows before the chunk, which may be fresh
+    // rows of the previous chunk: those are quantized here too (the same
+    // bytes as the other workgroup writes), so that no loaded byte is stale.
+    int f0 = 0, f1 = 0;
+    if (a.n_new > 0 && ntiles > 0) {
+        f0 = max(min(c0, c1 - TR), a.new0);
+        f1 = min(c1, a.new0 + a.n_new);
+    }
+    const bool fresh_late = f0 < f1 && f0 - c0 >= (DIST + 1) * TR;
+    auto quantize_fresh = [&](int first, int stride) __attribute__((always_inline)) {
+        for (int r = f0 + first; r < f1; r += stride)
+            quantize_row_wave(a.x_new + (size_t)(r - a.new0) * D, D, a.new_codes + (size_t)r * D,
+                              a.new_scales + r, lane);
+    };
+    if (f0 < f1 && !fresh_late) {
+        quantize_fresh(w, 8);
+        wait_vmcnt<0>();
+        __syncthreads();
+    }
+
+    // ---- prologue: query operands.  Work item t (all 512 threads) loads the
+    // nine float4 of head t / 16 at elements 4 (t % 16 + 16 s), s < 9; the
+    // head's e = q * sm_scale * log2(e) is scaled by 2^k (largest |e| in
+    // [2^14, 2^15)) and split into fp16 hi + lo (the subtraction is exact in
+    // f32).  Each term in turn is staged in the score waves' B operand
+    // layout (K step ks = 4 cb + 2 s' + t' covers elements 64 cb + 32 s' +
+    // 16 h + 8 t' + (0..7) for lane half h; lane = head + 32 h), and score
+    // wave kh loads K steps 18 kh .. + 18.  The context waves issue their
+    // query loads, then the first DIST tiles' loads, then build.
+    const int kh = w & 1;
+    f16x8 qhi[KH], qlo[KH];
+    {
+        const int h = tid >> 4, i = tid & 15;
+        const int qh = qh0 + h;
+        const bool hv = qh < a.n_qh;
+        float4 v[9];
+#pragma unroll
+        for (int s = 0; s < 9; ++s) {
+            const int e = 4 * (i + 16 * s);
+            const float* p = (e < LC) ? a.q_lat + (size_t)(hv ? qh : 0) * LC + e
+                                      : a.q_rope + (size_t)(hv ? qh : 0) * RC + (e - LC);
+            const float4 x = *reinterpret_cast<const float4*>(p);
+            v[s] = hv ? x : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+        if (ctx_wave) {
+            if (ntiles > 0)
+                issue(0, 0, IC0{}, ICK{});
+            if (ntiles > 1)
+                issue(1, 1, IC0{}, ICK{});
+        }
+        float amax = 0.0f;
+#pragma unroll
+        for (int s = 0; s < 9; ++s)
+            amax = fmaxf(amax, fmaxf(fmaxf(fabsf(v[s].x), fabsf(v[s].y)),
+                                     fmaxf(fabsf(v[s].z), fabsf(v[s].w))));
+        amax = row16_max(amax);
+        const float es = a.sm_log2;
+        const int k = query_exp(amax * es);
+        if (i == 0)
+            s_k[h] = k;
+        const float mult = ldexpf(es, k);
+        f16x4 lo4[9];
+        auto stage_ptr = [&](int s) __attribute__((always_inline)) -> uint8_t* {
+            const int e = 4 * (i + 16 * s);
+            const int cb = e >> 6, s2 = (e >> 5) & 1, hf = (e >> 4) & 1, t2 = (e >> 3) & 1;
+            const int ks = 4 * cb + 2 * s2 + t2;
+            return lds + QT + ((size_t)ks * 64 + h + 32 * hf) * 16 + 2 * (e & 7);
+        };
+#pragma unroll
+        for (int s = 0; s < 9; ++s) {
+            const float r[4] = {v[s].x * mult, v[s].y * mult, v[s].z * mult, v[s].w * mult};
+            f16x4 hi;
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                hi[c] = (_Float16)r[c];
+                lo4[s][c] = (_Float16)(r[c] - (float)hi[c]);
+            }
+            *reinterpret_cast<f16x4*>(stage_ptr(s)) = hi;
+        }
+        lds_barrier();
+        if (!ctx_wave) {
+#pragma unroll
+            for (int m = 0; m < KH; ++m)
+                qhi[m] = *reinterpret_cast<const f16x8*>(lds + QT + ((KH * kh + m) * 64 + lane) * 16);
+        }
+        lds_barrier();
+#pragma unroll
+        for (int s = 0; s < 9; ++s)
+            *reinterpret_cast<f16x4*>(stage_ptr(s)) = lo4[s];
+        lds_barrier();
+        if (!ctx_wave) {
+#pragma unroll
+            for (int m = 0; m < KH; ++m)
+                qlo[m] = *reinterpret_cast<const f16x8*>(lds + QT + ((KH * kh + m) * 64 + lane) * 16);
+        }
+        lds_barrier();  // staging area free for the ring
+    }
+
+    // Softmax state, identical in every wave, for heads n and 16 + n of the
+    // group (lane n = lane % 16): m = lazy max of u (z side), d = lazy max of
+    // (u - m) + log2 scale (context side, relative to m).  Tile p's weights
+    // are written with the state as it stands, in the linear domain,
+    //     p_t = 2^(u_t - m),  w_t = p_t * (scale_t * 2^-d),
+    // and every score wave publishes a flag when any of its p or w leaves
+    // [0, 2^kTau] (a new maximum by more than kTau, or a value that left f32's
+    // range; NaN is caught through the sums).  One phase later every wave
+    // reads the four flags: when one is set, or a head of the group has not
+    // met a valid row yet, every wave takes the exact path together: the
+    // score waves publish exact maxima per (head, row quarter), the state
+    // moves by the lazy rule, the context waves rescale their accumulators and
+    // the score waves rewrite the tile's weights in the log domain.  Separate
+    // scalars, never an array (a lane-dependent pick would go to scratch).
+    float mrun0 = -INFINITY, mrun1 = -INFINITY, drun0 = -INFINITY, drun1 = -INFINITY;
+    float fown = 1.0f;
+    bool uninit = true;
+    constexpr float kCheck = 256.0f;
+    static_assert(kTau == 8.0f, "check threshold 2^kTau");
+
+    auto vote = [&](uint4 fl) __attribute__((always_inline)) -> bool {
+        return uninit || ((fl.x | fl.y | fl.z | fl.w) != 0u);
+    };
+    auto state_move = [&](float (&alz)[2], float (&alo)[2], int own_hh)
+                          __attribute__((always_inline)) {
+#pragma unroll
+        for (int ht = 0; ht < 2; ++ht) {
+            const int h = 16 * ht + n;
+            const float4 r01 = *reinterpret_cast<const float4*>(&s_cr2[h * 4]);
+            const float4 r23 = *reinterpret_cast<const float4*>(&s_cr2[h * 4 + 2]);
+            const float Tk[4] = {r01.x, r01.z, r23.x, r23.z};
+            const float Ck[4] = {r01.y, r01.w, r23.y, r23.w};
+            const float T = fmaxf(fmaxf(Tk[0], Tk[1]), fmaxf(Tk[2], Tk[3]));
+            float& mr = ht ? mrun1 : mrun0;
+            float& dr = ht ? drun1 : drun0;
+            const float mold = mr;
+            const float mnew = (T > mold + kTau) ? T : mold;
+            alz[ht] = (mnew == mold) ? 1.0f : fast_exp2(mold - mnew);
+            const float mu = (mnew == -INFINITY) ? 0.0f : mnew;
+            float tb = -INFINITY;
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+                if (Tk[k] != -INFINITY)
+                    tb = fmaxf(tb, Ck[k] + (Tk[k] - mu));
+            const float dshift = (mnew == mold) ? dr : dr + (mold - mnew);
+            const float dnew = (tb > dshift + kTau) ? tb : dshift;
+            alo[ht] = (dnew == dshift) ? 1.0f : fast_exp2(dshift - dnew);
+            mr = mnew;
+            dr = dnew;
+        }
+        const float dd = own_hh ? drun1 : drun0;
+        fown = (dd == -INFINITY) ? 1.0f : fast_exp2(-dd);
+        uninit = __any(mrun0 == -INFINITY || mrun1 == -INFINITY);
+    };
+    const size_t pbase = (size_t)chunk * a.n_qh;
+
+    if (!ctx_wave) {
+        // ======== score waves: rows 32 rh .. +32 of each tile, K steps 18 kh
+        // .. +18, all 32 heads as the MFMA's columns.
+        auto score_role = [&](auto KHc_) __attribute__((always_inline)) {
+            constexpr int KHC = decltype(KHc_)::value;  // = kh
+            const int rh = w >> 1;
+            const int hf = lane >> 5;              // lane half: K elements 8 hf ..
+            const int hd = lane & 31;              // the lane's head (score column)
+            const int hsel = hd >> 4;              // state of head n (0) or 16 + n (1)
+            const float pk = ldexpf(1.0f, -s_k[hd]);  // the accumulators hold 2^k scores
+            // After the exchange the lane holds head hd, rows rb0 + (0..3) and
+            // rb0 + 8 + (0..3) of the wave's 32 (values 8 kh .. +8 of the
+            // 32x32 result; row quarter 2 rh + kh).
+            const int rb0 = 16 * KHC + 4 * hf;
+            float zacc = 0.0f, zsave = 0.0f;
+            float accp[8];        // this wave's half of tile p-1's partial scores
+            // the lane's u (2^k-scaled score x row scale) and row scales of the
+            // last weighed tile, kept for the exact path
+            float4* const s_uv = reinterpret_cast<float4*>(lds + UV) + w * 4 * 64 + lane;
+            _Float16* const s_w_own = s_w + hd * WSTR + 32 * rh + rb0;
+            // A operand: row l % 32 of the half, 16 bytes of half column block
+            // hb (slot hf + 2 (hb & 1) of column block hb / 2) at + 512 hb.
+            const int rowq = 32 * rh + (lane & 31);
+            const int a_off = (rowq >> 4) * (NCB * 1024) + ((rowq & 15) + 16 * hf) * 16 +
+                              512 * (KH / 2) * KHC;
+            // exchange: value 8 kh' + 4 j + c of wave (rh, kh) goes to wave
+            // (rh, kh') as float4 j at [parity][rh][kh'][j][lane]
+            auto xc_ptr = [&](int par, int dst) __attribute__((always_inline)) -> float4* {
+                return reinterpret_cast<float4*>(lds + XC) + ((par * 2 + rh) * 2 + dst) * 2 * 64 + lane;
+            };
+            f32x16 acc;
+
+            // Weights of tile t (= p - 1: own half in accp, the partner's in
+            // the exchange buffer; row scales in slot t % NSC) for this lane's
+            // rows, linear form, into buffer buf; true when all of them and
+            // their p are in [0, 2^kTau].  Only the last tile can be ragged,
+            // and it is weighed after the last stream (RAGGED); inside a
+            // stream the weighing has no branch, so that the scheduler can
+            // spread it among the MFMAs.
+            auto weigh = [&](int t, int buf, auto RAGGED_) __attribute__((always_inline)) -> bool {
+                const float* scp = s_sc + (t & (NSC - 1)) * TR + 32 * rh + rb0;
+                const float4 s0 = *reinterpret_cast<const float4*>(scp);
+                const float4 s1 = *reinterpret_cast<const float4*>(scp + 8);
+                const float4* xq = xc_ptr(t & 1, KHC);
+                const float4 y0 = xq[0], y1 = xq[64];
+                zsave = zacc;
+                const float scv[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+                const float yv[8] = {y0.x, y0.y, y0.z, y0.w, y1.x, y1.y, y1.z, y1.w};
+                float u[8];
+#pragma unroll
+                for (int v = 0; v < 8; ++v)
+                    u[v] = (accp[v] + yv[v]) * scv[v];
+                if constexpr (decltype(RAGGED_)::value) {
+                    const int lead = c0 + (t + 1) * TR - c1;  // rows before the tile's own
+#pragma unroll
+                    for (int r = 0; r < 2; ++r)
+#pragma unroll
+                        for (int v = 0; v < 4; ++v)
+                            if (32 * rh + rb0 + 8 * r + v < lead)
+                                u[4 * r + v] = -INFINITY;
+                }
+                s_uv[0] = make_float4(u[0], u[1], u[2], u[3]);
+                s_uv[64] = make_float4(u[4], u[5], u[6], u[7]);
+                s_uv[128] = s0;
+                s_uv[192] = s1;
+                const float mu = hsel ? mrun1 : mrun0;
+                const float nmz = (mu == -INFINITY) ? 0.0f : -mu;
+                float ps = 0.0f, ws = 0.0f, mx = 0.0f;
+#pragma unroll
+                for (int r = 0; r < 2; ++r) {
+                    f16x4 wv;
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) {
+                        const float pv = fast_exp2(fmaf(u[4 * r + v], pk, nmz));
+                        const float wt = pv * (scv[4 * r + v] * fown);
+                        ps += pv;
+                        ws += wt;
+                        mx = fmaxf(mx, fmaxf(pv, wt));
+                        wv[v] = (_Float16)wt;
+                    }
+                    *reinterpret_cast<f16x4*>(s_w_own + buf * HG * WSTR + 8 * r) = wv;
+                }
+                zacc = zsave + ps;
+                // fmaxf drops NaN; the sums keep it (every term is >= 0)
+                return (mx <= kCheck) && (ps + ws <= 4096.0f);
+            };
+            // Same in the log domain (exact for any scale), after a state move,
+            // from the unscaled scores u.
+            auto weights_log = [&](int buf, const float (&u)[8], const float (&scv)[8])
+                                   __attribute__((always_inline)) {
+                const float mu = hsel ? mrun1 : mrun0;
+                const float dd = hsel ? drun1 : drun0;
+                const float mz = (mu == -INFINITY) ? 0.0f : mu;
+                const float dn = (dd == -INFINITY) ? 0.0f : dd;
+                float ps = 0.0f;
+#pragma unroll
+                for (int r = 0; r < 2; ++r) {
+                    f16x4 wv;
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) {
+                        const float av = u[4 * r + v] - mz;
+                        ps += fast_exp2(av);
+                        wv[v] = (_Float16)fast_exp2((av + log2f(scv[4 * r + v])) - dn);
+                    }
+                    *reinterpret_cast<f16x4*>(s_w_own + buf * HG * WSTR + 8 * r) = wv;
+                }
+                zacc = zsave + ps;
+            };
+            // The score MFMAs of tile p (ring stage st) into acc: each half
+            // column block widened once, then its two K steps times the hi and
+            // lo query terms; with WW, the weights of tile p-1 are computed
+            // among them (independent work that fills the MFMA shadow).
+            auto stream = [&](int st, auto WW_, int t, int buf)
+                              __attribute__((always_inline)) -> bool {
+                constexpr bool WW = decltype(WW_)::value;
+                bool ok = true;
+                const uint8_t* xs = lds + st * STAGE + a_off;
+#pragma unroll
+                for (int v = 0; v < 16; ++v)
+                    acc[v] = 0.0f;
+                constexpr int NH = KH / 2;  // 9 half column blocks
+                constexpr int PF = 2;
+                uint4 xr[PF + 1];
+#pragma unroll
+                for (int j = 0; j < PF; ++j)
+                    xr[j] = *reinterpret_cast<const uint4*>(xs + 512 * j);
+                // the row reads stay PF half blocks ahead: no LDS read may
+                // sink below these points (everything else may cross them)
+                __builtin_amdgcn_sched_barrier(kNoDsReadCross);
+#pragma unroll
+                for (int j = 0; j < NH; ++j) {
+                    if (j + PF < NH)
+                        xr[(j + PF) % (PF + 1)] =
+                            *reinterpret_cast<const uint4*>(xs + 512 * (j + PF));
+                    __builtin_amdgcn_sched_barrier(kNoDsReadCross);
+                    const uint4 x = xr[j % (PF + 1)];
+                    const f16x8 a0 = cvt8(x.x, x.y), a1 = cvt8(x.z, x.w);
+                    acc = mfma32(a0, qhi[2 * j], acc);
+                    acc = mfma32(a0, qlo[2 * j], acc);
+                    acc = mfma32(a1, qhi[2 * j + 1], acc);
+                    acc = mfma32(a1, qlo[2 * j + 1], acc);
+                    if constexpr (WW) {
+                        if (j == 1)
+                            ok = weigh(t, buf, std::false_type{});
+                    }
+                }
+                return ok;
+            };
+
+            // Phase p (one barrier): the score MFMAs of tile p, the weights of
+            // tile p-1 and their flag; first the vote on tile p-2 (the context
+            // waves accumulate tile p-2 in this phase).  Two extra phases
+            // finish the pipeline.
+            for (int p = 0, st = 0; p <= ntiles + 1; ++p, st = (st == NST - 1) ? 0 : st + 1) {
+                const int bw = (p + 1) & 1;   // weight / flag buffer of tile p-1
+                lds_barrier();  // (A) tile p visible; tile p-1's partner half, the
+                                //     weights and flags of tile p-2 complete;
+                                //     buffer (p-1) & 1 free
+                uint4 fl = make_uint4(0u, 0u, 0u, 0u);
+                if (p >= 2)
+                    fl = *reinterpret_cast<const uint4*>(s_fl + 4 * (p & 1));
+                if (p >= 2 && vote(fl)) {
+                    // u and row scales of tile p-2 (stored by its weigh);
+                    // unscaled scores: pk is a power of 2
+                    const float4 u0 = s_uv[0], u1 = s_uv[64], sc0 = s_uv[128], sc1 = s_uv[192];
+                    const float u[8] = {u0.x * pk, u0.y * pk, u0.z * pk, u0.w * pk,
+                                        u1.x * pk, u1.y * pk, u1.z * pk, u1.w * pk};
+                    const float scv[8] = {sc0.x, sc0.y, sc0.z, sc0.w, sc1.x, sc1.y, sc1.z, sc1.w};
+                    // exact maxima of tile p-2 (u, scv) for this lane's row
+                    // quarter: T = max u, C = max (u - T) + log2 scale
+                    // (relative, so that a large |u| never swallows log2
+                    // scale); lanes l and l ^ 32 hold the quarter's 16 rows
+                    float tw = -INFINITY;
+#pragma unroll
+                    for (int v = 0; v < 8; ++v)
+                        tw = fmaxf(tw, u[v]);
+                    tw = max_xor32(tw);
+                    float cw = -INFINITY;
+                    if (tw != -INFINITY) {
+#pragma unroll
+                        for (int v = 0; v < 8; ++v)
+                            cw = fmaxf(cw, (u[v] - tw) + log2f(scv[v]));
+                    }
+                    cw = max_xor32(cw);
+                    if (hf == 0)
+                        s_cr2[hd * 4 + 2 * rh + KHC] = make_float2(tw, cw);
+                    lds_barrier();  // (R1)
+                    float alz[2], alo[2];
+                    state_move(alz, alo, hsel);
+                    zsave *= hsel ? alz[1] : alz[0];
+                    weights_log(p & 1, u, scv);  // tile p-2 under the new state
+                    lds_barrier();       // (R2) rewritten weights visible; s_cr free
+                }
+                const bool scored = p < ntiles, weighed = p >= 1 && p <= ntiles;
+                bool ok = true;
+                if (scored && weighed)
+                    ok = stream(st, std::true_type{}, p - 1, bw);
+                else if (scored)
+                    stream(st, std::false_type{}, 0, 0);
+                else if (weighed)
+                    ok = weigh(p - 1, bw, std::true_type{});
+                if (weighed) {
+                    const bool flag = __any(!ok);
+                    if (lane == 0)
+                        s_fl[4 * bw + w] = flag ? 1u : 0u;
+                }
+                if (scored) {
+                    // the partner's half of tile p to LDS, this wave's half kept
+                    float4* xo = xc_ptr(p & 1, 1 - KHC);
+                    constexpr int PO = 8 * (1 - KHC), OW = 8 * KHC;
+                    xo[0] = make_float4(acc[PO + 0], acc[PO + 1], acc[PO + 2], acc[PO + 3]);
+                    xo[64] = make_float4(acc[PO + 4], acc[PO + 5], acc[PO + 6], acc[PO + 7]);
+#pragma unroll
+                    for (int v = 0; v < 8; ++v)
+                        accp[v] = acc[OW + v];
+                }
+            }
+            // z of head hd over the lane's rows, then lanes l and l ^ 32
+            float zz = zacc;
+            zz += __shfl_xor(zz, 32);
+            if (lane < 32)
+                s_z[w * HG + lane] = zz;
+        };
+        if (kh == 0)
+            score_role(std::integral_constant<int, 0>{});
+        else
+            score_role(std::integral_constant<int, 1>{});
+    } else {
+        // ======== context waves: O[32 heads][128 columns 128 c ..] += W . X
+        // of tile p-2; column block jb = 32 columns, K step ks = 16 rows.
+        const int c = wi;
+        const int g = lane >> 4;
+        if (fresh_late)
+            quantize_fresh(wi, 4);
+        f32x16 O[4];
+#pragma unroll
+        for (int jb = 0; jb < 4; ++jb)
+#pragma unroll
+            for (int v = 0; v < 16; ++v)
+                O[jb][v] = 0.0f;
+        // Transposed read: 16-lane group g covers columns 16 (g & 1) .. of
+        // the 32-column block and rows 8 (g >> 1) .. of the K step; lanes
+        // 2 k, 2 k + 1 address row 8 (g >> 1) + k, bytes 8 (lane & 1) of the
+        // 16-byte slot.
+        const int tr_row = 8 * (g >> 1) + ((lane & 15) >> 1);
+        const int tr_off = (tr_row + 16 * (g & 1)) * 16 + 8 * (lane & 1);
+        // weight operand: head lane % 32, rows 16 ks + 8 (lane / 32) ..
+        const int w_off = (lane & 31) * WSTR + 8 * (lane >> 5);
+        f16x8 wa[4];
+        auto read_weights = [&](int buf) __attribute__((always_inline)) {
+            const _Float16* sw = s_w + buf * HG * WSTR + w_off;
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks)
+                wa[ks] = *reinterpret_cast<const f16x8*>(sw + 16 * ks);
+        };
+        auto read_rows = [&](int st, v2i32 (&xb)[4][4]) __attribute__((always_inline)) {
+            const uint8_t* xst = lds + st * STAGE + tr_off;
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+                for (int jb = 0; jb < 4; ++jb) {
+                    const int cb = 2 * c + (jb >> 1);
+                    const int off = (ks * NCB + cb) * 1024 + 32 * (jb & 1) * 16;
+                    xb[ks][jb] = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+                        (MLA8_LDS v2i32*)(MLA8_LDS uint8_t*)(xst + off));
+                }
+        };
+        auto accumulate = [&](const v2i32 (&xb)[4][4]) __attribute__((always_inline)) {
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+                for (int jb = 0; jb < 4; ++jb)
+                    O[jb] = mfma32(wa[ks], cvt8((uint32_t)xb[ks][jb][0], (uint32_t)xb[ks][jb][1]),
+                                   O[jb]);
+        };
+
+        // Phase p: the context of tile p-2 (its weights from buffer p & 1,
+        // its rows read into registers xb in phase p-2), after the vote on
+        // it; then the rows of tile p into the same registers, for phase p+2.
+        // Tile p-1's ring stage is free once this phase's barrier has passed
+        // (both readers read it in phase p-1), so the loads of tile p + DIST
+        // go there.
+        auto phase = [&](int p, int st, v2i32 (&xb)[4][4]) __attribute__((always_inline)) {
+            const int bw = p & 1;  // weight / flag buffer of tile p-2
+            if (p < ntiles)
+                wait_tile(p + 1 < ntiles);
+            lds_barrier();  // (A)
+            const bool more = p + DIST < ntiles;
+            const int sti = (st + DIST) % NST;
+            const bool ctx = p >= 2;
+            uint4 fl = make_uint4(0u, 0u, 0u, 0u);
+            if (ctx) {
+                fl = *reinterpret_cast<const uint4*>(s_fl + 4 * bw);
+                read_weights(bw);
+            }
+            if (more)
+                issue(p + DIST, sti, IC0{}, ICA{});
+            if (ctx && vote(fl)) {
+                lds_barrier();  // (R1) the score waves' tile maxima are in s_cr
+                float alz[2], alo[2];
+                state_move(alz, alo, 0);
+                // O holds tiles < p-2 in units of the old state; its head
+                // 8 (v / 4) + 4 (lane / 32) + v % 4 takes that head's factor,
+                // through a per-wave table in LDS (a wave's LDS accesses
+                // complete in order)
+                float* const al = reinterpret_cast<float*>(lds + AL) + HG * wi;
+                if (lane < 16) {
+                    al[lane] = alo[0];
+                    al[16 + lane] = alo[1];
+                }
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const float4 f = reinterpret_cast<const float4*>(al)[2 * q + (lane >> 5)];
+                    const float fv[4] = {f.x, f.y, f.z, f.w};
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+#pragma unroll
+                        for (int jb = 0; jb < 4; ++jb)
+                            O[jb][4 * q + r] *= fv[r];
+                }
+                lds_barrier();  // (R2) the rewritten weights of tile p-2 are visible
+                read_weights(bw);
+            }
+            if (more)
+                issue(p + DIST, sti, ICA{}, ICB{});
+            if (ctx)
+                accumulate(xb);
+            if (more)
+                issue(p + DIST, sti, ICB{}, ICK{});
+            if (p < ntiles)
+                read_rows(st, xb);
+        };
+        v2i32 xb0[4][4], xb1[4][4];
+        for (int p = 0, st = 0; p <= ntiles + 1; p += 2) {
+            phase(p, st, xb0);
+            st = (st == NST - 1) ? 0 : st + 1;
+            if (p + 1 <= ntiles + 1)
+                phase(p + 1, st, xb1);
+            st = (st == NST - 1) ? 0 : st + 1;
+        }
+        // partial cl = sum_t p_t scale_t x_t = 2^d * O
+        const float fo0 = (mrun0 == -INFINITY || drun0 == -INFINITY) ? 0.0f : fast_exp2(drun0);
+        const float fo1 = (mrun1 == -INFINITY || drun1 == -INFINITY) ? 0.0f : fast_exp2(drun1);
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+            const int hd = 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+            const float fa = __shfl(fo0, hd & 15), fb = __shfl(fo1, hd & 15);
+            const float f = (hd >> 4) ? fb : fa;
+            const int qh = qh0 + hd;
+            if (qh < a.n_qh) {
+                float* dst = a.ws_cl + (pbase + qh) * LC + 128 * c + (lane & 31);
+#pragma unroll
+                for (int jb = 0; jb < 4; ++jb)
+                    dst[32 * jb] = O[jb][v] * f;
+            }
+        }
+    }
+
+    // ---- partial m and z (z summed over the four score waves' row quarters)
+    __syncthreads();
+    if (w < 2 && lane < 16) {
+        const int h = 16 * (w & 1) + n, qh = qh0 + h;
+        if (qh < a.n_qh) {
+            a.ws_m[pbase + qh] = (w & 1) ? mrun1 : mrun0;
+            a.ws_z[pbase + qh] = (s_z[h] + s_z[HG + h]) + (s_z[2 * HG + h] + s_z[3 * HG + h]);
+        }
+    }
+}
+
+bool partial32_applies(const AttnArgs& a)
+{
+    return a.layout == kE4m3 && a.mode == kDense && a.lc == p32::LC && a.rc == p32::RC &&
+           a.n_list >= p32::TR;
+}
+
+void launch_partial32(const AttnArgs& a, hipStream_t stream)
+{
+    hipLaunchKernelGGL(k_partial32, dim3((unsigned)(a.n_chunks * a.n_groups)), dim3(kThreads), 0,
+                       stream, a);
+}
+
+}  // namespace mla8
