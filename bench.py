@@ -58,7 +58,7 @@ def log(*a):
 def parse():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--layers", type=int, default=None,
                     help="layers per step (default 8 for the decode, 16 for the indexer: "
@@ -1003,6 +1003,9 @@ def main():
     for ly in layers:
         assert torch.isfinite(ly["out"]).all() and torch.isfinite(ly["lse"]).all()
 
+    lo8 = time_score_lo8(m, w, layers, ws, T, K, WU, args.no_graph)
+    log(f"score_lo8 path: {lo8}")
+
     ceiling = stream_ceiling([ly["codes"] for ly in layers])
     log(f"stream-read ceiling {ceiling['gb_per_s']:.0f} GB/s; the partial kernel reaches "
         f"{100 * achieved / ceiling['gb_per_s']:.1f}% of it")
@@ -1047,8 +1050,67 @@ def main():
         "stream_ceiling": dict(ceiling, kernel_frac=round(achieved / ceiling["gb_per_s"], 4)),
         "cpu_baseline": cpu,
         "parity": parity,
+        "score_lo8": lo8,
     }
     print(json.dumps(rec), flush=True)
+
+
+def time_score_lo8(m, w, layers, ws, T, K, WU, no_graph):
+    """The same step with mla8_opts.score_lo8 (the query's lo term on the e4m3
+    MFMA; attention with that quantized query): step time per layer-token
+    and the partial kernel's mean duration (library events, eager pass).
+    Reported beside the headline value, which uses the default path."""
+    import numpy as np
+    import torch
+
+    def step():
+        for ly in layers:
+            m.mla8_append_decode(ly["codes"], ly["scales"], T - 1, ly["fresh"], w.lc, w.rc,
+                                 ly["ql"], ly["qr"], w.sm_scale, out=ly["out"],
+                                 lse=ly["lse"], workspace=ws, score_lo8=True)
+
+    for _ in range(max(WU, 1)):
+        step()
+    torch.cuda.synchronize()
+    run = step
+    if not no_graph:
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step()
+        torch.cuda.synchronize()
+        run = graph.replay
+    settle(run, "score_lo8 steps")
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(K):
+        run()
+    e1.record()
+    torch.cuda.synchronize()
+    ms_lt = e0.elapsed_time(e1) / K / len(layers)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(K * len(layers))]
+    for a_, b_ in evs:
+        a_.record()
+        b_.record()
+    torch.cuda.synchronize()
+    for _ in range(30):
+        run()
+    i = 0
+    for _ in range(K):
+        for ly in layers:
+            m.mla8_append_decode(ly["codes"], ly["scales"], T - 1, ly["fresh"], w.lc, w.rc,
+                                 ly["ql"], ly["qr"], w.sm_scale, out=ly["out"],
+                                 lse=ly["lse"], workspace=ws, events=evs[i], score_lo8=True)
+            i += 1
+    torch.cuda.synchronize()
+    durs = np.array([a.elapsed_time(b) for a, b in evs]) * 1e3
+    for ly in layers:
+        assert torch.isfinite(ly["out"]).all() and torch.isfinite(ly["lse"]).all()
+    return {"ms_per_layer_token": round(ms_lt, 6), "kernel": "k_partial32<lo8>",
+            "kernel_us": round(float(np.mean(durs)), 3),
+            "note": "opt-in mla8_opts.score_lo8: attention with the query's lo term "
+                    "quantized to e4m3 (oracle reading: oracle.query_lo8); not the headline"}
 
 
 def stream_ceiling(bufs, passes=10):

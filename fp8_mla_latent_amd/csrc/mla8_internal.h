@@ -53,6 +53,9 @@ struct AttnArgs {
     float* new_scales;      // the shadow scales, writable
     int32_t new0;
     int32_t n_new;
+    // 1: the dense 512/64 partial kernel runs its lo query term on the e4m3
+    // MFMA (mla8_opts.score_lo8); ignored elsewhere
+    int32_t lo8;
 };
 
 // Largest n_new the fused append takes (rows quantized inside the attention

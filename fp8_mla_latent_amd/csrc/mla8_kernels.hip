@@ -214,7 +214,11 @@ __device__ __forceinline__ void build_query_terms(const AttnArgs& a, int t,
     const float mult = ldexpf(es, k);  // e 2^k = q * mult up to one rounding
 #pragma unroll
     for (int s = 0; s < PER; ++s) {
-        const float r[4] = {v[s].x * mult, v[s].y * mult, v[s].z * mult, v[s].w * mult};
+        // one rounded f32 value per entry, opaque to the compiler, so that hi
+        // and lo are split from the same r (hi is otherwise free to become the
+        // fp16 rounding of the exact product, off by an fp16 step at ties)
+        float r[4] = {v[s].x * mult, v[s].y * mult, v[s].z * mult, v[s].w * mult};
+        asm volatile("" : "+v"(r[0]), "+v"(r[1]), "+v"(r[2]), "+v"(r[3]));
         put_query_f16<Q>(qt, h >> 4, h & 15, i + 16 * s, r);
     }
 }
@@ -282,7 +286,8 @@ __device__ __forceinline__ void build_query_terms_mx(const AttnArgs& a, int t,
     const float mult = ldexpf(es, k);
 #pragma unroll
     for (int s = 0; s < Q::NG; ++s) {
-        const float r[4] = {v[s].x * mult, v[s].y * mult, v[s].z * mult, v[s].w * mult};
+        float r[4] = {v[s].x * mult, v[s].y * mult, v[s].z * mult, v[s].w * mult};
+        asm volatile("" : "+v"(r[0]), "+v"(r[1]), "+v"(r[2]), "+v"(r[3]));  // as above
         put_query_f16<Q::NP>(qt, hh, n, i + 16 * s, r);
     }
     // RoPE elements 4 i .. 4 i + 3: K step m = i / 8, lane group (i / 2) % 4,

@@ -64,8 +64,8 @@ constexpr int XC = W + 2 * HG * WSTR * 2;  // f32x4 [2][2 rh][2 kh][2][64] parti
 constexpr int FL = XC + 2 * 2 * 2 * 2 * 64 * 16;  // u32 [2][4] overflow flags
 constexpr int CR = FL + 2 * 4 * 4;       // float2 [HG][4] exact tile maxima (head, row quarter)
 constexpr int Z = CR + HG * 4 * 8;       // f32 [4][HG] z per score wave
-constexpr int HK = Z + 4 * HG * 4;       // i32 [HG] query scaling exponent
-constexpr int UV = HK + HG * 4;          // f32x4 [4 waves][4][64]: u, scale of the weighed tile
+constexpr int HK = Z + 4 * HG * 4;       // i32 [2][HG] query scaling exponents k (and j, LO8)
+constexpr int UV = HK + 2 * HG * 4;      // f32x4 [4 waves][4][64]: u, scale of the weighed tile
 constexpr int AL = UV + 4 * 4 * 64 * 16; // f32 [4 context waves][HG] accumulator factors
 constexpr int END = AL + 4 * HG * 4;
 // query operand staging (one term at a time): stage 2, first filled in phase 0
@@ -77,6 +77,7 @@ static_assert(NINS % 4 == 0, "row DMAs split evenly over the context waves");
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef int v2i32 __attribute__((ext_vector_type(2)));
+typedef int v8i32 __attribute__((ext_vector_type(8)));
 
 // sched_barrier mask: VALU, SALU, transcendental, VMEM and LDS writes may be
 // scheduled across; LDS reads and MFMAs stay on their side
@@ -86,7 +87,14 @@ __device__ __forceinline__ f32x16 mfma32(f16x8 a, f16x8 b, f32x16 c)
 {
     return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
 }
+// e4m3 x e4m3, K = 64, A unscaled, B (the query's lo term) scaled by the
+// E8M0 exponent sb (value 2^(sb - 127)) of each lane's column
+__device__ __forceinline__ f32x16 mfma32_f8(v8i32 a, v8i32 b, f32x16 c, int sb)
+{
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, sb);
+}
 
+template <bool LO8>
 __global__ __launch_bounds__(kThreads, 1) void k_partial32(AttnArgs a)
 {
     using namespace p32;
@@ -206,10 +214,19 @@ __global__ __launch_bounds__(kThreads, 1) void k_partial32(AttnArgs a)
     // f32).  Each term in turn is staged in the score waves' B operand
     // layout (K step ks = 4 cb + 2 s' + t' covers elements 64 cb + 32 s' +
     // 16 h + 8 t' + (0..7) for lane half h; lane = head + 32 h), and score
-    // wave kh loads K steps 18 kh .. + 18.  The context waves issue their
-    // query loads, then the first DIST tiles' loads, then build.
+    // wave kh loads K steps 18 kh .. + 18.  LO8: the lo term is quantized
+    // to e4m3 with a per-head power-of-2 scale 2^j (largest |lo| 2^j in
+    // [128, 256)) for the e4m3 MFMA, which takes the row bytes as they are;
+    // score wave kh then holds column blocks 5 kh .. (5 or 4 of them), the
+    // hi term's K steps 20 kh .. and the lo term staged as [cb][lane] 32
+    // bytes (byte b < 16: element 64 cb + 16 h + b, b >= 16: 64 cb + 32 +
+    // 16 h + b - 16, the row bytes' order in the A operand).  The context
+    // waves issue their query loads, then the first DIST tiles' loads, then
+    // build.
     const int kh = w & 1;
-    f16x8 qhi[KH], qlo[KH];
+    constexpr int NQH = LO8 ? 20 : KH;  // hi K steps held by a score wave (at most)
+    f16x8 qhi[NQH], qlo[LO8 ? 1 : KH];
+    v8i32 ql8[LO8 ? 5 : 1];
     {
         const int h = tid >> 4, i = tid & 15;
         const int qh = qh0 + h;
@@ -249,7 +266,12 @@ __global__ __launch_bounds__(kThreads, 1) void k_partial32(AttnArgs a)
         };
 #pragma unroll
         for (int s = 0; s < 9; ++s) {
-            const float r[4] = {v[s].x * mult, v[s].y * mult, v[s].z * mult, v[s].w * mult};
+            // r = f32(q 2^k es), rounded once and opaque to the compiler: both
+            // terms are split from this one f32 value (otherwise hi may be
+            // recomputed as the fp16 rounding of the exact product, which
+            // differs where r sits on an fp16 rounding tie)
+            float r[4] = {v[s].x * mult, v[s].y * mult, v[s].z * mult, v[s].w * mult};
+            asm volatile("" : "+v"(r[0]), "+v"(r[1]), "+v"(r[2]), "+v"(r[3]));
             f16x4 hi;
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
@@ -260,19 +282,57 @@ __global__ __launch_bounds__(kThreads, 1) void k_partial32(AttnArgs a)
         }
         lds_barrier();
         if (!ctx_wave) {
+            const int ks0 = LO8 ? 20 * kh : KH * kh;
+            const int nks = LO8 ? 20 - 4 * kh : KH;
 #pragma unroll
-            for (int m = 0; m < KH; ++m)
-                qhi[m] = *reinterpret_cast<const f16x8*>(lds + QT + ((KH * kh + m) * 64 + lane) * 16);
+            for (int m = 0; m < NQH; ++m)
+                if (m < nks)
+                    qhi[m] = *reinterpret_cast<const f16x8*>(lds + QT + ((ks0 + m) * 64 + lane) * 16);
         }
         lds_barrier();
+        if constexpr (LO8) {
+            float lmax = 0.0f;
 #pragma unroll
-        for (int s = 0; s < 9; ++s)
-            *reinterpret_cast<f16x4*>(stage_ptr(s)) = lo4[s];
+            for (int s = 0; s < 9; ++s)
+#pragma unroll
+                for (int c = 0; c < 4; ++c)
+                    lmax = fmaxf(lmax, fabsf((float)lo4[s][c]));
+            lmax = row16_max(lmax);
+            int ex = 0;
+            if (lmax > 0.0f)
+                (void)frexpf(lmax, &ex);
+            const int j = (lmax > 0.0f) ? max(-100, min(100, 8 - ex)) : 0;
+            if (i == 0)
+                s_k[HG + h] = j;
+#pragma unroll
+            for (int s = 0; s < 9; ++s) {
+                const int e = 4 * (i + 16 * s);
+                const int cb = e >> 6, off = e & 63, hf = (off >> 4) & 1;
+                const int b = 16 * (off >> 5) + (off & 15);
+                uint32_t word = 0;
+#pragma unroll
+                for (int c = 0; c < 4; ++c)
+                    word |= enc_e4m3(ldexpf((float)lo4[s][c], j)) << (8 * c);
+                *reinterpret_cast<uint32_t*>(lds + QT + ((size_t)(cb * 64 + h + 32 * hf)) * 32 + b) =
+                    word;
+            }
+        } else {
+#pragma unroll
+            for (int s = 0; s < 9; ++s)
+                *reinterpret_cast<f16x4*>(stage_ptr(s)) = lo4[s];
+        }
         lds_barrier();
         if (!ctx_wave) {
+            if constexpr (LO8) {
 #pragma unroll
-            for (int m = 0; m < KH; ++m)
-                qlo[m] = *reinterpret_cast<const f16x8*>(lds + QT + ((KH * kh + m) * 64 + lane) * 16);
+                for (int c = 0; c < 5; ++c)
+                    if (c < 5 - kh)
+                        ql8[c] = *reinterpret_cast<const v8i32*>(lds + QT + ((5 * kh + c) * 64 + lane) * 32);
+            } else {
+#pragma unroll
+                for (int m = 0; m < KH; ++m)
+                    qlo[m] = *reinterpret_cast<const f16x8*>(lds + QT + ((KH * kh + m) * 64 + lane) * 16);
+            }
         }
         lds_barrier();  // staging area free for the ring
     }
@@ -343,6 +403,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_partial32(AttnArgs a)
             const int hd = lane & 31;              // the lane's head (score column)
             const int hsel = hd >> 4;              // state of head n (0) or 16 + n (1)
             const float pk = ldexpf(1.0f, -s_k[hd]);  // the accumulators hold 2^k scores
+            const int sb_lo = 127 - s_k[HG + hd];         // LO8: E8M0 scale 2^-j of the lo term
             // After the exchange the lane holds head hd, rows rb0 + (0..3) and
             // rb0 + 8 + (0..3) of the wave's 32 (values 8 kh .. +8 of the
             // 32x32 result; row quarter 2 rh + kh).
@@ -357,7 +418,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_partial32(AttnArgs a)
             // hb (slot hf + 2 (hb & 1) of column block hb / 2) at + 512 hb.
             const int rowq = 32 * rh + (lane & 31);
             const int a_off = (rowq >> 4) * (NCB * 1024) + ((rowq & 15) + 16 * hf) * 16 +
-                              512 * (KH / 2) * KHC;
+                              (LO8 ? 1024 * 5 * KHC : 512 * (KH / 2) * KHC);
             // exchange: value 8 kh' + 4 j + c of wave (rh, kh) goes to wave
             // (rh, kh') as float4 j at [parity][rh][kh'][j][lane]
             auto xc_ptr = [&](int par, int dst) __attribute__((always_inline)) -> float4* {
@@ -453,30 +514,70 @@ __global__ __launch_bounds__(kThreads, 1) void k_partial32(AttnArgs a)
 #pragma unroll
                 for (int v = 0; v < 16; ++v)
                     acc[v] = 0.0f;
-                constexpr int NH = KH / 2;  // 9 half column blocks
-                constexpr int PF = 2;
-                uint4 xr[PF + 1];
+                if constexpr (LO8) {
+                    // column block c of the wave: both halves (32 row bytes
+                    // per lane) feed the e4m3 MFMA as they are and, widened,
+                    // the four hi K steps
+                    constexpr int NC = KHC ? 4 : 5;
+                    // the lo products in an accumulator of their own, added
+                    // to the hi sum once at the end
+                    f32x16 acc_lo;
 #pragma unroll
-                for (int j = 0; j < PF; ++j)
-                    xr[j] = *reinterpret_cast<const uint4*>(xs + 512 * j);
-                // the row reads stay PF half blocks ahead: no LDS read may
-                // sink below these points (everything else may cross them)
-                __builtin_amdgcn_sched_barrier(kNoDsReadCross);
-#pragma unroll
-                for (int j = 0; j < NH; ++j) {
-                    if (j + PF < NH)
-                        xr[(j + PF) % (PF + 1)] =
-                            *reinterpret_cast<const uint4*>(xs + 512 * (j + PF));
+                    for (int v = 0; v < 16; ++v)
+                        acc_lo[v] = 0.0f;
+                    uint4 xa[2], xb2[2];
+                    xa[0] = *reinterpret_cast<const uint4*>(xs);
+                    xb2[0] = *reinterpret_cast<const uint4*>(xs + 512);
                     __builtin_amdgcn_sched_barrier(kNoDsReadCross);
-                    const uint4 x = xr[j % (PF + 1)];
-                    const f16x8 a0 = cvt8(x.x, x.y), a1 = cvt8(x.z, x.w);
-                    acc = mfma32(a0, qhi[2 * j], acc);
-                    acc = mfma32(a0, qlo[2 * j], acc);
-                    acc = mfma32(a1, qhi[2 * j + 1], acc);
-                    acc = mfma32(a1, qlo[2 * j + 1], acc);
-                    if constexpr (WW) {
-                        if (j == 1)
-                            ok = weigh(t, buf, std::false_type{});
+#pragma unroll
+                    for (int c = 0; c < NC; ++c) {
+                        if (c + 1 < NC) {
+                            xa[(c + 1) & 1] = *reinterpret_cast<const uint4*>(xs + 1024 * (c + 1));
+                            xb2[(c + 1) & 1] = *reinterpret_cast<const uint4*>(xs + 1024 * (c + 1) + 512);
+                        }
+                        __builtin_amdgcn_sched_barrier(kNoDsReadCross);
+                        const uint4 x0 = xa[c & 1], x1 = xb2[c & 1];
+                        acc = mfma32(cvt8(x0.x, x0.y), qhi[4 * c + 0], acc);
+                        acc = mfma32(cvt8(x0.z, x0.w), qhi[4 * c + 1], acc);
+                        acc = mfma32(cvt8(x1.x, x1.y), qhi[4 * c + 2], acc);
+                        acc = mfma32(cvt8(x1.z, x1.w), qhi[4 * c + 3], acc);
+                        const v8i32 araw = {(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w,
+                                            (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
+                        acc_lo = mfma32_f8(araw, ql8[c], acc_lo, sb_lo);
+                        if constexpr (WW) {
+                            if (c == 1)
+                                ok = weigh(t, buf, std::false_type{});
+                        }
+                    }
+#pragma unroll
+                    for (int v = 0; v < 16; ++v)
+                        acc[v] += acc_lo[v];
+                } else {
+                    constexpr int NH = KH / 2;  // 9 half column blocks
+                    constexpr int PF = 2;
+                    uint4 xr[PF + 1];
+#pragma unroll
+                    for (int j = 0; j < PF; ++j)
+                        xr[j] = *reinterpret_cast<const uint4*>(xs + 512 * j);
+                    // the row reads stay PF half blocks ahead: no LDS read may
+                    // sink below these points (nor MFMAs rise above them)
+                    __builtin_amdgcn_sched_barrier(kNoDsReadCross);
+#pragma unroll
+                    for (int j = 0; j < NH; ++j) {
+                        if (j + PF < NH)
+                            xr[(j + PF) % (PF + 1)] =
+                                *reinterpret_cast<const uint4*>(xs + 512 * (j + PF));
+                        __builtin_amdgcn_sched_barrier(kNoDsReadCross);
+                        const uint4 x = xr[j % (PF + 1)];
+                        const f16x8 a0 = cvt8(x.x, x.y), a1 = cvt8(x.z, x.w);
+                        acc = mfma32(a0, qhi[2 * j], acc);
+                        acc = mfma32(a0, qlo[2 * j], acc);
+                        acc = mfma32(a1, qhi[2 * j + 1], acc);
+                        acc = mfma32(a1, qlo[2 * j + 1], acc);
+                        if constexpr (WW) {
+                            if (j == 1)
+                                ok = weigh(t, buf, std::false_type{});
+                        }
                     }
                 }
                 return ok;
@@ -710,8 +811,11 @@ bool partial32_applies(const AttnArgs& a)
 
 void launch_partial32(const AttnArgs& a, hipStream_t stream)
 {
-    hipLaunchKernelGGL(k_partial32, dim3((unsigned)(a.n_chunks * a.n_groups)), dim3(kThreads), 0,
-                       stream, a);
+    const dim3 grid((unsigned)(a.n_chunks * a.n_groups));
+    if (a.lo8)
+        hipLaunchKernelGGL(k_partial32<true>, grid, dim3(kThreads), 0, stream, a);
+    else
+        hipLaunchKernelGGL(k_partial32<false>, grid, dim3(kThreads), 0, stream, a);
 }
 
 }  // namespace mla8

@@ -81,11 +81,26 @@ enum { MLA8_OP_DECODE = 0, MLA8_OP_DECODE_SEL = 1, MLA8_OP_BATCH = 2, MLA8_OP_IN
  *              indexer's score kernel for mla8_index_topk), so that
  *              hipEventElapsedTime(ev_before, ev_after) is that kernel's
  *              duration; NULL to skip.  Caller-owned.
+ *   score_lo8  0 (default): scores of f32 grade, the query as given.  1: the
+ *              faster score path for e4m3 rows with lc = 512, rc = 64 (dense
+ *              mla8_decode, mla8_append_decode, mla8_append_decode_noalloc
+ *              over at least 64 rows) [B1-FMHA first pass, intentional
+ *              limits: the noPE QK product on the fp8 tensor cores]: per
+ *              head, e = q * sm_scale * log2(e) is scaled by 2^k (largest |e|
+ *              in [2^14, 2^15)), split into its fp16 rounding hi and the rest
+ *              lo (rounded to fp16), and lo is quantized to e4m3 with a
+ *              power-of-2 scale 2^j (largest |lo| 2^j in [128, 256)); the
+ *              result is attention with the query (hi + e4m3(lo 2^j) 2^-j)
+ *              2^-k / (sm_scale log2(e)) in place of q.  That query differs
+ *              from q by about 2^-16 of its largest entry per head, which on
+ *              caches with outlier rows can move outputs by more than the
+ *              f32-grade path's tolerance.  Other calls ignore the flag.
  */
 typedef struct mla8_opts {
     int32_t n_splits;
     void* ev_before;
     void* ev_after;
+    int32_t score_lo8;
 } mla8_opts;
 
 /*

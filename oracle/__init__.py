@@ -258,3 +258,43 @@ def threads() -> int:
 def set_threads(n: int) -> None:
     """OpenMP threads for the following calls; n < 1 restores the default."""
     lib().mla8o_set_threads(int(n))
+
+
+def query_lo8(q_lat, q_rope, sm_scale):
+    """The query that the score_lo8 path attends with (mla8_opts.score_lo8).
+
+    Reading of [B1-FMHA first pass, intentional first-pass limits: the noPE QK
+    product on the fp8 tensor cores] on this library's terms: the query stays
+    f32 at the boundary; per head, e = q * es with es = f32(sm_scale) *
+    f32(log2 e) (an f32 product) is scaled by 2^k, k = 15 - ex(f32(max|q| *
+    es)) capped at 100 (0 for a zero head; ex is frexp's exponent), into r =
+    f32(q * f32(es 2^k)); hi = fp16(r) (round to nearest even), lo = fp16(r -
+    hi) (the difference is exact in f32); lo is quantized to e4m3 with the
+    power-of-2 scale 2^j, j = 8 - ex(max|lo|) clamped to [-100, 100] (0 when
+    lo is all zero): lo8 = enc(f32(lo 2^j)).  The scores are then
+    sum_i x_i (hi_i + dec(lo8_i) 2^-j) 2^-k in log2 units, i.e. the dense
+    attention of the query q' = (hi + dec(lo8) 2^-j) 2^-k / es, returned
+    rounded to f32 (2^-24 relative, far below what the quantization moves).
+    Returns (q_lat' [H, lc], q_rope' [H, rc]) as float32 arrays.
+    """
+    ql = np.asarray(q_lat, np.float32)
+    qr = np.asarray(q_rope, np.float32)
+    lc = ql.shape[1]
+    q = np.concatenate([ql, qr], axis=1)
+    es = np.float32(np.float32(sm_scale) * np.float32(1.4426950408889634))
+    out = np.empty(q.shape, np.float64)
+    for h in range(q.shape[0]):
+        e = q[h]
+        emax = np.float32(np.max(np.abs(e)) * es)
+        k = min(15 - int(np.frexp(emax)[1]), 100) if emax > 0 else 0
+        mult = np.float32(np.ldexp(es, k))
+        r = (e * mult).astype(np.float32)
+        hi = r.astype(np.float16)
+        lo = (r - hi.astype(np.float32)).astype(np.float16)
+        lmax = float(np.max(np.abs(lo.astype(np.float32))))
+        j = max(-100, min(100, 8 - int(np.frexp(lmax)[1]))) if lmax > 0 else 0
+        lo8 = enc(np.ldexp(lo.astype(np.float32), j).astype(np.float32))
+        term = hi.astype(np.float64) + np.ldexp(dec(lo8), -j)
+        out[h] = np.ldexp(term, -k) / np.float64(es)
+    out32 = out.astype(np.float32)
+    return np.ascontiguousarray(out32[:, :lc]), np.ascontiguousarray(out32[:, lc:])
