@@ -522,8 +522,8 @@ def bench_dsv3(args):
         "higher_is_better": False,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "e4m3 kv; scores e4m3->f16 rows x f16 hi+lo q (f16 mfma), context f16 weights "
-                 "x e4m3->f16 rows (f16 mfma); f32 accumulate",
+        "dtype": "e4m3 kv; scores e4m3->f16 rows x f16 hi q (f16 mfma) + e4m3 rows x e4m3 lo q "
+                 "(scaled e4m3 mfma), context f16 weights x e4m3->f16 rows (f16 mfma); f32 accumulate",
         "data": "synthetic: seeded N(0,1) rows (1 % of rows x50) and queries",
         "config": {"workload": w.name, "heads": w.n_heads, "kv_lora": w.lc, "rope": w.rc,
                    "t_rows": T, "batch": 1, "layers_per_step": L,
@@ -1003,8 +1003,8 @@ def main():
     for ly in layers:
         assert torch.isfinite(ly["out"]).all() and torch.isfinite(ly["lse"]).all()
 
-    lo8 = time_score_lo8(m, w, layers, ws, T, K, WU, args.no_graph)
-    log(f"score_lo8 path: {lo8}")
+    f32s = time_f32_scores(m, w, layers, ws, T, K, WU, args.no_graph)
+    log(f"f32_scores path: {f32s}")
 
     ceiling = stream_ceiling([ly["codes"] for ly in layers])
     log(f"stream-read ceiling {ceiling['gb_per_s']:.0f} GB/s; the partial kernel reaches "
@@ -1038,7 +1038,7 @@ def main():
         "higher_is_better": False,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "e4m3 kv; scores e4m3->f16 rows x f16 hi+lo q (f16 mfma), context f16 weights x e4m3->f16 rows (f16 mfma); f32 accumulate",
+        "dtype": "e4m3 kv; scores e4m3->f16 rows x f16 hi q (f16 mfma) + e4m3 rows x e4m3 lo q (scaled e4m3 mfma), context f16 weights x e4m3->f16 rows (f16 mfma); f32 accumulate",
         "data": "synthetic: seeded N(0,1) rows and queries",
         "config": {"workload": w.name, "heads": w.n_heads, "kv_lora": w.lc, "rope": w.rc,
                    "t_rows": T, "batch": 1, "layers_per_step": L,
@@ -1050,16 +1050,16 @@ def main():
         "stream_ceiling": dict(ceiling, kernel_frac=round(achieved / ceiling["gb_per_s"], 4)),
         "cpu_baseline": cpu,
         "parity": parity,
-        "score_lo8": lo8,
+        "f32_scores": f32s,
     }
     print(json.dumps(rec), flush=True)
 
 
-def time_score_lo8(m, w, layers, ws, T, K, WU, no_graph):
-    """The same step with mla8_opts.score_lo8 (the query's lo term on the e4m3
-    MFMA; attention with that quantized query): step time per layer-token
-    and the partial kernel's mean duration (library events, eager pass).
-    Reported beside the headline value, which uses the default path."""
+def time_f32_scores(m, w, layers, ws, T, K, WU, no_graph):
+    """The same step with mla8_opts.f32_scores (the query's lo term as fp16 on
+    the fp16 MFMA instead of e4m3 on the e4m3 MFMA: scores of f32 grade):
+    step time per layer-token and the partial kernel's mean duration (library
+    events, eager pass).  Reported beside the headline value (the default)."""
     import numpy as np
     import torch
 
@@ -1067,7 +1067,7 @@ def time_score_lo8(m, w, layers, ws, T, K, WU, no_graph):
         for ly in layers:
             m.mla8_append_decode(ly["codes"], ly["scales"], T - 1, ly["fresh"], w.lc, w.rc,
                                  ly["ql"], ly["qr"], w.sm_scale, out=ly["out"],
-                                 lse=ly["lse"], workspace=ws, score_lo8=True)
+                                 lse=ly["lse"], workspace=ws, f32_scores=True)
 
     for _ in range(max(WU, 1)):
         step()
@@ -1079,7 +1079,7 @@ def time_score_lo8(m, w, layers, ws, T, K, WU, no_graph):
             step()
         torch.cuda.synchronize()
         run = graph.replay
-    settle(run, "score_lo8 steps")
+    settle(run, "f32_scores steps")
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     e0.record()
@@ -1101,16 +1101,16 @@ def time_score_lo8(m, w, layers, ws, T, K, WU, no_graph):
         for ly in layers:
             m.mla8_append_decode(ly["codes"], ly["scales"], T - 1, ly["fresh"], w.lc, w.rc,
                                  ly["ql"], ly["qr"], w.sm_scale, out=ly["out"],
-                                 lse=ly["lse"], workspace=ws, events=evs[i], score_lo8=True)
+                                 lse=ly["lse"], workspace=ws, events=evs[i], f32_scores=True)
             i += 1
     torch.cuda.synchronize()
     durs = np.array([a.elapsed_time(b) for a, b in evs]) * 1e3
     for ly in layers:
         assert torch.isfinite(ly["out"]).all() and torch.isfinite(ly["lse"]).all()
-    return {"ms_per_layer_token": round(ms_lt, 6), "kernel": "k_partial32<lo8>",
+    return {"ms_per_layer_token": round(ms_lt, 6), "kernel": "k_partial32<f16 lo>",
             "kernel_us": round(float(np.mean(durs)), 3),
-            "note": "opt-in mla8_opts.score_lo8: attention with the query's lo term "
-                    "quantized to e4m3 (oracle reading: oracle.query_lo8); not the headline"}
+            "note": "mla8_opts.f32_scores: the query's lo term as fp16 on the fp16 MFMA "
+                    "(scores of f32 grade); not the headline"}
 
 
 def stream_ceiling(bufs, passes=10):

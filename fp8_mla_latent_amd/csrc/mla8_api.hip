@@ -48,7 +48,7 @@ int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 int32_t forced_splits(const mla8_opts* o) { return (o != nullptr && o->n_splits > 0) ? o->n_splits : 0; }
 hipEvent_t ev_before(const mla8_opts* o) { return o ? static_cast<hipEvent_t>(o->ev_before) : nullptr; }
 hipEvent_t ev_after(const mla8_opts* o) { return o ? static_cast<hipEvent_t>(o->ev_after) : nullptr; }
-int32_t score_lo8(const mla8_opts* o) { return (o != nullptr && o->score_lo8 != 0) ? 1 : 0; }
+int32_t lo8_scores(const mla8_opts* o) { return (o != nullptr && o->f32_scores != 0) ? 0 : 1; }
 
 // Row chunks for a call that attends `rows` rows with `n_qh` query-heads.
 // Aim for one workgroup per CU; prefer a multiple of 8 chunks (one per XCD
@@ -141,7 +141,7 @@ int run_attention(int32_t op, const uint8_t* codes, const float* scales, int64_t
     a.new_scales = new_scales;
     a.new0 = (int32_t)new0;
     a.n_new = (int32_t)n_new;
-    a.lo8 = score_lo8(opts);
+    a.lo8 = lo8_scores(opts);
     return launch_attention(a, static_cast<hipStream_t>(stream), ev_before(opts), ev_after(opts)) ==
                    hipSuccess
                ? MLA8_OK

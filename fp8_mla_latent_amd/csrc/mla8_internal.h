@@ -54,7 +54,7 @@ struct AttnArgs {
     int32_t new0;
     int32_t n_new;
     // 1: the dense 512/64 partial kernel runs its lo query term on the e4m3
-    // MFMA (mla8_opts.score_lo8); ignored elsewhere
+    // MFMA (the default; 0 with mla8_opts.f32_scores); ignored elsewhere
     int32_t lo8;
 };
 

@@ -16,9 +16,10 @@ append beyond cap_rows, queries beyond t_rows) is left to its status codes.
 Per-call options (the C struct mla8_opts): ``n_splits`` forces the number of
 row chunks of the split-T plan (0 = automatic), ``events`` = (before, after)
 torch.cuda.Event pair recorded around the split-T partial kernel (the
-indexer's score kernel for mla8_index_topk), ``score_lo8`` the faster score
-path whose result is attention with an e4m3-quantized query lo term (see
-mla8_opts in include/mla8.h).  Nothing is kept between calls.
+indexer's score kernel for mla8_index_topk), ``f32_scores`` scores of f32
+grade also for the e4m3 512/64 decode, which by default attends with the
+query's lo term quantized to e4m3 (see mla8_opts in include/mla8.h).
+Nothing is kept between calls.
 """
 from __future__ import annotations
 
@@ -58,7 +59,7 @@ EXPORTED = ("mla8_quantize_rows", "mla8_append", "mla8_decode", "mla8_append_dec
 class Mla8Opts(ctypes.Structure):
     """struct mla8_opts (include/mla8.h)."""
     _fields_ = [("n_splits", ctypes.c_int32), ("ev_before", ctypes.c_void_p),
-                ("ev_after", ctypes.c_void_p), ("score_lo8", ctypes.c_int32)]
+                ("ev_after", ctypes.c_void_p), ("f32_scores", ctypes.c_int32)]
 
 
 class Mla8Error(RuntimeError):
@@ -185,13 +186,13 @@ def _check(status: int, call: str) -> None:
         raise Mla8Error(status, call)
 
 
-def _opts(n_splits: int = 0, events=None, score_lo8: bool = False):
+def _opts(n_splits: int = 0, events=None, f32_scores: bool = False):
     """A Mla8Opts for one call, or None for the defaults.  events: (before,
     after) torch.cuda.Event; torch creates an event's hipEvent on its first
     record(), so both must have been recorded once."""
-    if not n_splits and events is None and not score_lo8:
+    if not n_splits and events is None and not f32_scores:
         return None
-    o = Mla8Opts(int(n_splits), None, None, 1 if score_lo8 else 0)
+    o = Mla8Opts(int(n_splits), None, None, 1 if f32_scores else 0)
     if events is not None:
         raw = []
         for ev in events:
@@ -304,7 +305,7 @@ def mla8_append_mx(kv_rows, kv_scales, t_rows: int, x, lc: int, rc: int) -> int:
 # attention
 
 def _decode_call(fn: str, row_bytes: int, kv, kv_scales, t_rows, lc, rc, q_lat, q_rope,
-                 sm_scale, out, lse, workspace, want_lse, n_splits, events, score_lo8=False):
+                 sm_scale, out, lse, workspace, want_lse, n_splits, events, f32_scores=False):
     cap = _shadow(kv, kv_scales, row_bytes)
     dev = kv.device
     if not (1 <= int(t_rows) <= cap):
@@ -314,7 +315,7 @@ def _decode_call(fn: str, row_bytes: int, kv, kv_scales, t_rows, lc, rc, q_lat, 
     _queries(q_lat, q_rope, (h,), lc, rc, dev)
     out, lse = _out_lse(out, lse, (h,), lc, dev, want_lse)
     ws = _workspace(MLA8_OP_DECODE, t_rows, h, 1, lc, dev, workspace, n_splits)
-    o = _opts(n_splits, events, score_lo8)
+    o = _opts(n_splits, events, f32_scores)
     _check(getattr(lib, fn)(_ptr(kv), _ptr(kv_scales), t_rows, lc, rc, _ptr(q_lat), _ptr(q_rope),
                             h, float(sm_scale), _ptr(out), _ptr(lse), _ptr(ws), ws.numel(),
                             _stream(q_lat), _o(o)), fn)
@@ -323,11 +324,11 @@ def _decode_call(fn: str, row_bytes: int, kv, kv_scales, t_rows, lc, rc, q_lat, 
 
 def mla8_decode(kv_codes, kv_scales, t_rows: int, lc: int, rc: int, q_lat, q_rope,
                 sm_scale: float, out=None, lse=None, workspace=None, want_lse: bool = True,
-                n_splits: int = 0, events=None, score_lo8: bool = False):
+                n_splits: int = 0, events=None, f32_scores: bool = False):
     """Dense decode over shadow rows [0, t_rows): returns (out [H, lc], lse [H] or None)."""
     return _decode_call("mla8_decode", lc + rc, kv_codes, kv_scales, t_rows, lc, rc, q_lat,
                         q_rope, sm_scale, out, lse, workspace, want_lse, n_splits, events,
-                        score_lo8)
+                        f32_scores)
 
 
 def mla8_decode_mx(kv_rows, kv_scales, t_rows: int, lc: int, rc: int, q_lat, q_rope,
@@ -341,7 +342,7 @@ def mla8_decode_mx(kv_rows, kv_scales, t_rows: int, lc: int, rc: int, q_lat, q_r
 def mla8_append_decode(kv_codes, kv_scales, t_rows: int, x_new, lc: int, rc: int, q_lat, q_rope,
                        sm_scale: float, out=None, lse=None, workspace=None,
                        want_lse: bool = True, n_splits: int = 0, events=None,
-                       score_lo8: bool = False, _fn: str = "mla8_append_decode"):
+                       f32_scores: bool = False, _fn: str = "mla8_append_decode"):
     """Append x_new [n, lc+rc] at rows [t_rows, t_rows + n) and decode over all
     t_rows + n rows in one launch: returns (out, lse, new t_rows)."""
     mixed = _fn == "mla8_append_decode_mx"
@@ -354,7 +355,7 @@ def mla8_append_decode(kv_codes, kv_scales, t_rows: int, x_new, lc: int, rc: int
     _queries(q_lat, q_rope, (h,), lc, rc, dev)
     out, lse = _out_lse(out, lse, (h,), lc, dev, want_lse)
     ws = _workspace(MLA8_OP_DECODE, t_rows + n, h, 1, lc, dev, workspace, n_splits)
-    o = _opts(n_splits, events, score_lo8)
+    o = _opts(n_splits, events, f32_scores)
     t = ctypes.c_int64(t_rows)
     _check(getattr(lib, _fn)(_ptr(kv_codes), _ptr(kv_scales), cap, ctypes.byref(t), _ptr(x_new),
                              n, lc, rc, _ptr(q_lat), _ptr(q_rope), h, float(sm_scale),
@@ -365,7 +366,7 @@ def mla8_append_decode(kv_codes, kv_scales, t_rows: int, x_new, lc: int, rc: int
 
 def mla8_append_decode_noalloc(kv_codes, kv_scales, t_rows: int, x_new, lc: int, rc: int,
                                q_lat, q_rope, sm_scale: float, out, lse=None,
-                               n_splits: int = 0, score_lo8: bool = False) -> int:
+                               n_splits: int = 0, f32_scores: bool = False) -> int:
     """As mla8_append_decode with the library's static scratch instead of a
     workspace; allocates nothing, so `out` ([H, lc] f32) must be given (lse
     [H] f32 optional).  Returns the new t_rows."""
@@ -378,7 +379,7 @@ def mla8_append_decode_noalloc(kv_codes, kv_scales, t_rows: int, x_new, lc: int,
     _dev(out, "out", torch.float32, (h, lc), dev)
     if lse is not None:
         _dev(lse, "lse", torch.float32, (h,), dev)
-    o = _opts(n_splits, None, score_lo8)
+    o = _opts(n_splits, None, f32_scores)
     t = ctypes.c_int64(t_rows)
     _check(lib.mla8_append_decode_noalloc(_ptr(kv_codes), _ptr(kv_scales), cap, ctypes.byref(t),
                                           _ptr(x_new), x_new.shape[0], lc, rc, _ptr(q_lat),

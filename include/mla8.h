@@ -81,26 +81,27 @@ enum { MLA8_OP_DECODE = 0, MLA8_OP_DECODE_SEL = 1, MLA8_OP_BATCH = 2, MLA8_OP_IN
  *              indexer's score kernel for mla8_index_topk), so that
  *              hipEventElapsedTime(ev_before, ev_after) is that kernel's
  *              duration; NULL to skip.  Caller-owned.
- *   score_lo8  0 (default): scores of f32 grade, the query as given.  1: the
- *              faster score path for e4m3 rows with lc = 512, rc = 64 (dense
+ *   f32_scores 0 (default): for e4m3 rows with lc = 512, rc = 64 (dense
  *              mla8_decode, mla8_append_decode, mla8_append_decode_noalloc
- *              over at least 64 rows) [B1-FMHA first pass, intentional
- *              limits: the noPE QK product on the fp8 tensor cores]: per
- *              head, e = q * sm_scale * log2(e) is scaled by 2^k (largest |e|
- *              in [2^14, 2^15)), split into its fp16 rounding hi and the rest
- *              lo (rounded to fp16), and lo is quantized to e4m3 with a
+ *              over at least 64 rows) the scores use the e4m3 MFMA for the
+ *              query's lo term [B1-FMHA first pass, intentional limits: the
+ *              noPE QK product on the fp8 tensor cores]: per head, e = q *
+ *              sm_scale * log2(e) is scaled by 2^k (largest |e| in [2^14,
+ *              2^15)), split into its fp16 rounding hi and the rest lo
+ *              (rounded to fp16), and lo is quantized to e4m3 with a
  *              power-of-2 scale 2^j (largest |lo| 2^j in [128, 256)); the
  *              result is attention with the query (hi + e4m3(lo 2^j) 2^-j)
- *              2^-k / (sm_scale log2(e)) in place of q.  That query differs
- *              from q by about 2^-16 of its largest entry per head, which on
- *              caches with outlier rows can move outputs by more than the
- *              f32-grade path's tolerance.  Other calls ignore the flag.
+ *              2^-k / (sm_scale log2(e)) in place of q, which differs from q
+ *              by about 2^-16 of its largest entry per head.  Every other call
+ *              attends with q as given, scores of f32 grade.  1: scores of f32
+ *              grade for those calls too (fp16 hi + lo terms on the fp16 MFMA,
+ *              slower).
  */
 typedef struct mla8_opts {
     int32_t n_splits;
     void* ev_before;
     void* ev_after;
-    int32_t score_lo8;
+    int32_t f32_scores;
 } mla8_opts;
 
 /*
@@ -139,7 +140,9 @@ MLA8_API int mla8_append(uint8_t* kv_codes, float* kv_scales, int64_t cap_rows, 
  *   s_t = sm_scale * (q . k_t);  p = softmax_t(s)  (natural exponential);
  *   out[h][k] = sum_t p_t k_t[k]  for k < lc;  lse[h] = ln sum_t e^{s_t}.
  * Computed split-T: row chunks yield (m, z, cl[lc]) partials in `workspace`,
- * then a log-sum-exp merge writes out.
+ * then a log-sum-exp merge writes out.  With lc = 512, rc = 64 and t_rows >=
+ * 64, q is the e4m3-lo-term query that mla8_opts.f32_scores describes unless
+ * that option is set.
  *   q_lat[n_heads][lc], q_rope[n_heads][rc]: f32.  out[n_heads][lc]: f32.
  *   lse[n_heads]: f32, or NULL to skip.
  * Errors: E_INVAL (NULL, t_rows <= 0, n_heads <= 0, non-finite sm_scale),

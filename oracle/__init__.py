@@ -261,7 +261,8 @@ def set_threads(n: int) -> None:
 
 
 def query_lo8(q_lat, q_rope, sm_scale):
-    """The query that the score_lo8 path attends with (mla8_opts.score_lo8).
+    """The query that the e4m3 512/64 decode attends with by default (its
+    scores' lo term on the e4m3 MFMA; mla8_opts.f32_scores turns it off).
 
     Reading of [B1-FMHA first pass, intentional first-pass limits: the noPE QK
     product on the fp8 tensor cores] on this library's terms: the query stays

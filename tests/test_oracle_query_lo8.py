@@ -1,5 +1,6 @@
-"""Pins of oracle.query_lo8, the query that the score_lo8 path attends with
-(fp16 hi term plus an e4m3 lo term with a per-head power-of-2 scale).  No GPU.
+"""Pins of oracle.query_lo8, the query that the e4m3 512/64 decode attends with
+by default (fp16 hi term plus an e4m3 lo term with a per-head power-of-2
+scale; mla8_opts.f32_scores turns it off).  No GPU.
 
 * identity: a query that the fp16 hi term already holds exactly (integers
   times a power-of-2 query scale) has lo = 0, so the reconstructed query is
