@@ -31,7 +31,7 @@ def test_code_hash_ignores_comments_but_not_code(tmp_path):
 
 
 def test_recorded_traffic_is_consistent():
-    rec = json.load(open(os.path.join(ROOT, "profiles", "k_split_partial_long_t262144_traffic.txt")))
+    rec = json.load(open(os.path.join(ROOT, "profiles", "k_partial32_long_t262144_traffic.txt")))
     assert len(rec["kernel_code_sha256"]) == 64
     assert rec["bytes_per_launch"] == rec["fetch_bytes"] + rec["write_bytes"]
     # calibrated = raw KiB x 1024 x (copy bytes / copy counter)
