@@ -1,13 +1,16 @@
 // Split-T partial kernel on the 32x32x16 fp16 MFMA, for the DeepSeek-V3 row
-// shape (Lc = 512, Rc = 64: 576 e4m3 bytes per row), dense rows with the
-// optional fused append of fresh rows.  Same result contract as
+// shape (Lc = 512, Rc = 64: 576 e4m3 bytes per row): dense rows with the
+// optional fused append of fresh rows, and the causal batch when each group of
+// 32 query-heads belongs to one query position (its rows end at that
+// position, inclusive).  Same result contract as
 // k_split_partial: per (row chunk, query-head) the online-softmax partial
 // (m in log2 units, z, cl = sum_t p_t scale_t x_t), merged by k_merge.
 //
 // Method source: colibri PR #300 "KV8 long-context CUDA: fp8 device shadow,
 // split-T kernels, DSA-aware gather", second commit ("KV8 long-context
 // CUDA"): split-T blocks emitting online-softmax partials (cl[K], m, z) and a
-// log-sum-exp merge; first commit ("KV8 base"): the latent row is both key
+// log-sum-exp merge, and the batch/prefill kernel over (query, head) pairs
+// with a causal limit; first commit ("KV8 base"): the latent row is both key
 // and value, the row scale is hoisted out of the dot, the producer quantizes
 // the fresh row.
 //
@@ -128,7 +131,11 @@ __global__ __launch_bounds__(kThreads, 1) void k_partial32(AttnArgs a)
     }
     const int qh0 = grp * HG;
     const int c0 = chunk * a.chunk_rows;
-    const int c1 = min(a.n_list, c0 + a.chunk_rows);
+    // causal batch: the group's 32 query-heads belong to one query position
+    // (n_heads is a multiple of 32), whose rows end at pos0 + s + 1
+    int c1 = min(a.n_list, c0 + a.chunk_rows);
+    if (a.mode == kCausal)
+        c1 = min(c1, a.pos0 + qh0 / a.n_heads + 1);
     const int ntiles = c1 > c0 ? (c1 - c0 + TR - 1) / TR : 0;
 
     // ---- row stream: the context waves (4-7) issue every direct load, KW row
@@ -805,8 +812,13 @@ __global__ __launch_bounds__(kThreads, 1) void k_partial32(AttnArgs a)
 
 bool partial32_applies(const AttnArgs& a)
 {
-    return a.layout == kE4m3 && a.mode == kDense && a.lc == p32::LC && a.rc == p32::RC &&
-           a.n_list >= p32::TR;
+    if (a.layout != kE4m3 || a.lc != p32::LC || a.rc != p32::RC || a.n_list < p32::TR)
+        return false;
+    if (a.mode == kDense)
+        return true;
+    // causal batch: every group within one query position, and every query's
+    // rows (at least pos0 + 1) fill a tile, which the ragged last tile needs
+    return a.mode == kCausal && a.n_heads % kHeadsPerGroup == 0 && a.pos0 + 1 >= p32::TR;
 }
 
 void launch_partial32(const AttnArgs& a, hipStream_t stream)

@@ -17,8 +17,8 @@ Per-call options (the C struct mla8_opts): ``n_splits`` forces the number of
 row chunks of the split-T plan (0 = automatic), ``events`` = (before, after)
 torch.cuda.Event pair recorded around the split-T partial kernel (the
 indexer's score kernel for mla8_index_topk), ``f32_scores`` scores of f32
-grade also for the e4m3 512/64 decode, which by default attends with the
-query's lo term quantized to e4m3 (see mla8_opts in include/mla8.h).
+grade also for the e4m3 512/64 decode and causal batch, which by default attend
+with the query's lo term quantized to e4m3 (see mla8_opts in include/mla8.h).
 Nothing is kept between calls.
 """
 from __future__ import annotations
@@ -437,7 +437,8 @@ def mla8_decode_sel_mx(kv_rows, kv_scales, t_rows: int, lc: int, rc: int, sel, q
 
 def mla8_batch(kv_codes, kv_scales, t_rows: int, lc: int, rc: int, q_lat, q_rope, pos0: int,
                sm_scale: float, out=None, lse=None, workspace=None, want_lse: bool = True,
-               n_splits: int = 0, events=None, _fn: str = "mla8_batch"):
+               n_splits: int = 0, events=None, f32_scores: bool = False,
+               _fn: str = "mla8_batch"):
     """Causal batch: q [S, H, *]; query s attends rows [0, pos0 + s]."""
     mixed = _fn == "mla8_batch_mx"
     cap = _shadow(kv_codes, kv_scales, lc + (2 if mixed else 1) * rc)
@@ -449,7 +450,7 @@ def mla8_batch(kv_codes, kv_scales, t_rows: int, lc: int, rc: int, q_lat, q_rope
     _queries(q_lat, q_rope, (n_q, h), lc, rc, dev)
     out, lse = _out_lse(out, lse, (n_q, h), lc, dev, want_lse)
     ws = _workspace(MLA8_OP_BATCH, pos0 + n_q, h, n_q, lc, dev, workspace, n_splits)
-    o = _opts(n_splits, events)
+    o = _opts(n_splits, events, f32_scores)
     _check(getattr(lib, _fn)(_ptr(kv_codes), _ptr(kv_scales), t_rows, lc, rc, _ptr(q_lat),
                              _ptr(q_rope), n_q, pos0, h, float(sm_scale), _ptr(out), _ptr(lse),
                              _ptr(ws), ws.numel(), _stream(q_lat), _o(o)), _fn)

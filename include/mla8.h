@@ -83,7 +83,8 @@ enum { MLA8_OP_DECODE = 0, MLA8_OP_DECODE_SEL = 1, MLA8_OP_BATCH = 2, MLA8_OP_IN
  *              duration; NULL to skip.  Caller-owned.
  *   f32_scores 0 (default): for e4m3 rows with lc = 512, rc = 64 (dense
  *              mla8_decode, mla8_append_decode, mla8_append_decode_noalloc
- *              over at least 64 rows) the scores use the e4m3 MFMA for the
+ *              over at least 64 rows; mla8_batch with n_heads a multiple of
+ *              32 and pos0 >= 63) the scores use the e4m3 MFMA for the
  *              query's lo term [B1-FMHA first pass, intentional limits: the
  *              noPE QK product on the fp8 tensor cores]: per head, e = q *
  *              sm_scale * log2(e) is scaled by 2^k (largest |e| in [2^14,
@@ -219,7 +220,9 @@ MLA8_API int mla8_decode_sel(const uint8_t* kv_codes, const float* kv_scales, in
  * Batched causal attention [KV8-long: the batch/prefill path over the cached
  * rows, one (query, head) pair per work unit]: query s in [0, n_q) sits at
  * absolute position pos0 + s and attends rows [0, pos0 + s] (its own row
- * included), with the same per-head arithmetic as mla8_decode.
+ * included), with the same per-head arithmetic as mla8_decode (for lc = 512,
+ * rc = 64, n_heads a multiple of 32 and pos0 >= 63, q is the e4m3-lo-term
+ * query that mla8_opts.f32_scores describes unless that option is set).
  *   q_lat[n_q][n_heads][lc], q_rope[n_q][n_heads][rc]: f32.
  *   out[n_q][n_heads][lc]: f32.  lse[n_q][n_heads] or NULL.
  * Errors: E_INVAL (NULL, n_q <= 0, pos0 < 0, ...), E_RANGE (pos0 + n_q >

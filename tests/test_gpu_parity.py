@@ -329,6 +329,10 @@ def test_batch_small(m, h, n_q, t, lc, rc):
     pos0 = t - n_q
     oc, os_ = oracle.quantize_rows(x)
     out, lse = m.mla8_batch(dev(oc), dev(os_), t, lc, rc, dev(ql), dev(qr), pos0, sm)
+    if lc == 512 and rc == 64 and h % 32 == 0 and pos0 >= 63:
+        # the e4m3-lo score path's query (mla8_opts.f32_scores)
+        qa, qb = oracle.query_lo8(ql.reshape(-1, lc), qr.reshape(-1, rc), sm)
+        ql, qr = qa.reshape(ql.shape), qb.reshape(qr.shape)
     ro, rl = oracle.batch(oc, os_, t, lc, rc, ql, qr, pos0, sm)
     # causal prefixes of 28 to 1999 rows
     check_attention(host(out), ro, host(lse), rl, f"batch H={h} S={n_q}", few_rows=True)
@@ -337,7 +341,9 @@ def test_batch_small(m, h, n_q, t, lc, rc):
 def test_batch_workload_whole_queries(m):
     """Full-size causal batch (S=64, H=64, T=32768, 64 fresh rows appended
     through the quantizer first), checked on four whole queries (all 64 heads
-    each: the first, two inner ones and the last, which attends every row)."""
+    each: the first, two inner ones and the last, which attends every row),
+    against the oracle run with the default path's query (oracle.query_lo8)
+    and with the exact query."""
     w = W.BATCH
     base = w.t_rows - w.n_append
     say(f"batch {w.name}: build shadow")
@@ -356,9 +362,14 @@ def test_batch_workload_whole_queries(m):
     assert np.all(np.isfinite(o)) and np.all(np.isfinite(l))
     for s in (0, 21, 42, 63):
         say(f"batch {w.name}: oracle for query {s}, all {w.n_heads} heads")
+        # the default e4m3-lo score path attends with the query of oracle.query_lo8
+        qa, qb = oracle.query_lo8(ql[s], qr[s], w.sm_scale)
+        ro, rl = oracle.decode(oc, os_, base + s + 1, w.lc, w.rc, qa, qb, w.sm_scale)
+        worst = check_attention(o[s], ro, l[s], rl, f"batch s={s}, its reading")
         ro, rl = oracle.decode(oc, os_, base + s + 1, w.lc, w.rc, ql[s], qr[s], w.sm_scale)
-        worst = check_attention(o[s], ro, l[s], rl, f"batch s={s}")
-        say(f"  query {s}: worst elementwise err/bar {worst:.4f}")
+        worst_exact = check_attention(o[s], ro, l[s], rl, f"batch s={s}, exact query")
+        say(f"  query {s}: worst elementwise err/bar {worst:.4f} (reading), "
+            f"{worst_exact:.4f} (exact query)")
 
 
 def test_long_context_step_full(m):

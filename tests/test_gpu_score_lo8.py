@@ -149,3 +149,40 @@ def test_f32_scores_ignored_outside_the_e4m3_lo_shape(m):
     b = m.mla8_decode(codes, scales, w.t_rows, w.lc, w.rc, dev(ql), dev(qr), w.sm_scale,
                       f32_scores=True)
     assert np.array_equal(host(a[0]), host(b[0])) and np.array_equal(host(a[1]), host(b[1]))
+
+
+@pytest.mark.parametrize("h,n_q,pos0,splits", [(32, 80, 63, 3), (64, 6, 700, 5), (96, 2, 130, 0),
+                                               (64, 3, 4000, 0)], ids=lambda v: str(v))
+def test_lo8_causal_batch(m, h, n_q, pos0, splits):
+    """The causal batch on the e4m3-lo score path (e4m3 rows, 512/64, n_heads
+    a multiple of 32, pos0 >= 63): chunks that end before a query's position
+    (empty partials), ragged last tiles whose leading rows belong to the
+    previous tile, several head groups per query.  The default call against
+    the quantized-query oracle and against the exact query; f32_scores against
+    the exact query."""
+    lc, rc, sm = 512, 64, 1.0 / math.sqrt(192.0)
+    t = pos0 + n_q
+    say(f"e4m3-lo causal batch H={h} S={n_q} pos0={pos0} splits={splits}")
+    g = np.random.Generator(np.random.PCG64(h * 1000 + n_q))
+    x = g.standard_normal((t, lc + rc)).astype(np.float32)
+    ql = g.standard_normal((n_q, h, lc)).astype(np.float32)
+    qr = g.standard_normal((n_q, h, rc)).astype(np.float32)
+    codes, scales = m.mla8_quantize_rows(dev(x), lc, rc)
+    oc, os_ = host(codes), host(scales)
+    # prefixes of a few hundred rows: the per-vector form (short causal prefix)
+    few = pos0 < 2000
+    out8, lse8 = m.mla8_batch(codes, scales, t, lc, rc, dev(ql), dev(qr), pos0, sm,
+                              n_splits=splits)
+    qql, qqr = oracle.query_lo8(ql.reshape(-1, lc), qr.reshape(-1, rc), sm)
+    r8, l8 = oracle.batch(oc, os_, t, lc, rc, qql.reshape(n_q, h, lc), qqr.reshape(n_q, h, rc),
+                          pos0, sm)
+    w8 = check_attention(host(out8), r8, host(lse8), l8, "e4m3-lo batch, its reading",
+                         few_rows=few)
+    ro, rl = oracle.batch(oc, os_, t, lc, rc, ql, qr, pos0, sm)
+    we = check_attention(host(out8), ro, host(lse8), rl, "e4m3-lo batch, exact query",
+                         few_rows=few)
+    out, lse = m.mla8_batch(codes, scales, t, lc, rc, dev(ql), dev(qr), pos0, sm,
+                            n_splits=splits, f32_scores=True)
+    wf = check_attention(host(out), ro, host(lse), rl, "f32_scores batch, exact query",
+                         few_rows=few)
+    say(f"  worst err/bar: reading {w8:.4f}, exact {we:.4f}, f32_scores {wf:.4f}")
