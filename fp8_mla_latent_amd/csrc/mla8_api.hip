@@ -629,4 +629,16 @@ int mla8_test_encode(const float* x, int64_t n, uint8_t* codes, void* stream)
                : MLA8_E_HIP;
 }
 
+int mla8_test_encode_pk(const float* x, int64_t n, uint8_t* codes, void* stream)
+{
+    if (!x || !codes || n < 0 || (n & 3) != 0 || (reinterpret_cast<uintptr_t>(x) & 15) != 0 ||
+        (reinterpret_cast<uintptr_t>(codes) & 3) != 0)
+        return MLA8_E_INVAL;
+    if (n == 0)
+        return MLA8_OK;
+    return launch_test_encode_pk(x, n, codes, static_cast<hipStream_t>(stream)) == hipSuccess
+               ? MLA8_OK
+               : MLA8_E_HIP;
+}
+
 }  // extern "C"

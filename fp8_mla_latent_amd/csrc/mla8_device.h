@@ -45,6 +45,17 @@ __device__ __forceinline__ uint32_t enc_e4m3(float y)
     return sign | code;
 }
 
+// Four values to e4m3 by the hardware conversion (v_cvt_pk_fp8_f32, two per
+// instruction: round to nearest even onto OCP e4m3), bytes in argument order.
+// It equals enc_e4m3 for finite |y| < 448, the only inputs it is given here;
+// it does not saturate, so larger or non-finite inputs give other codes.
+__device__ __forceinline__ uint32_t enc_e4m3_pk4(float y0, float y1, float y2, float y3)
+{
+    int w = __builtin_amdgcn_cvt_pk_fp8_f32(y0, y1, 0, false);
+    w = __builtin_amdgcn_cvt_pk_fp8_f32(y2, y3, w, true);
+    return (uint32_t)w;
+}
+
 // Maximum over the 16 lanes of each row (DPP: quad swaps, then half-row and
 // row mirrors), and over the whole wave (permlane swaps across rows).
 __device__ __forceinline__ float row16_max(float x)

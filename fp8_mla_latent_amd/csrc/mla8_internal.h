@@ -99,6 +99,8 @@ hipError_t launch_quantize(const float* x, int64_t n_rows, int32_t d, uint8_t* c
 hipError_t launch_quantize_mx(const float* x, int64_t n_rows, int32_t lc, int32_t rc,
                               uint8_t* rows, float* scales, hipStream_t stream);
 hipError_t launch_test_encode(const float* x, int64_t n, uint8_t* codes, hipStream_t stream);
+// n a multiple of 4, x 16-byte and codes 4-byte aligned
+hipError_t launch_test_encode_pk(const float* x, int64_t n, uint8_t* codes, hipStream_t stream);
 constexpr int kStreamWords = 32768;  // output words of the stream-read reference
 hipError_t launch_stream_read(const void* p, int64_t bytes, uint32_t* out, hipStream_t stream);
 // The 32x32x16-MFMA partial kernel (mla8_partial32.hip): dense e4m3 rows of

@@ -83,6 +83,18 @@ __global__ __launch_bounds__(256) void k_test_encode(const float* __restrict__ x
         out[i] = (uint8_t)enc_e4m3(x[i]);
 }
 
+// The packed hardware encoder of the e4m3 lo query term, four values per
+// thread (n4 groups of four).
+__global__ __launch_bounds__(256) void k_test_encode_pk(const float4* __restrict__ x, int64_t n4,
+                                                        uint32_t* __restrict__ out)
+{
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += stride) {
+        const float4 v = x[i];
+        out[i] = enc_e4m3_pk4(v.x, v.y, v.z, v.w);
+    }
+}
+
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 __device__ __forceinline__ f32x4 mfma_bf16(bf16x8 a, bf16x8 b, f32x4 c)
 {
@@ -1306,6 +1318,17 @@ hipError_t launch_stream_read(const void* p, int64_t bytes, uint32_t* out, hipSt
 {
     hipLaunchKernelGGL(k_stream_read, dim3(kStreamBlocks), dim3(256), 0, stream,
                        static_cast<const uint4*>(p), bytes / 16, out);
+    return hipGetLastError();
+}
+
+hipError_t launch_test_encode_pk(const float* x, int64_t n, uint8_t* codes, hipStream_t stream)
+{
+    const int64_t n4 = n / 4;
+    int64_t blocks = (n4 + 255) / 256;
+    if (blocks > 65536)
+        blocks = 65536;
+    hipLaunchKernelGGL(k_test_encode_pk, dim3((unsigned)blocks), dim3(256), 0, stream,
+                       reinterpret_cast<const float4*>(x), n4, reinterpret_cast<uint32_t*>(codes));
     return hipGetLastError();
 }
 

@@ -214,132 +214,158 @@ __global__ __launch_bounds__(kThreads, 1) void k_partial32(AttnArgs a)
         __syncthreads();
     }
 
-    // ---- prologue: query operands.  Work item t (all 512 threads) loads the
-    // nine float4 of head t / 16 at elements 4 (t % 16 + 16 s), s < 9; the
-    // head's e = q * sm_scale * log2(e) is scaled by 2^k (largest |e| in
-    // [2^14, 2^15)) and split into fp16 hi + lo (the subtraction is exact in
-    // f32).  Each term in turn is staged in the score waves' B operand
-    // layout (K step ks = 4 cb + 2 s' + t' covers elements 64 cb + 32 s' +
-    // 16 h + 8 t' + (0..7) for lane half h; lane = head + 32 h), and score
-    // wave kh loads K steps 18 kh .. + 18.  LO8: the lo term is quantized
-    // to e4m3 with a per-head power-of-2 scale 2^j (largest |lo| 2^j in
-    // [128, 256)) for the e4m3 MFMA, which takes the row bytes as they are;
-    // score wave kh then holds column blocks 5 kh .. (5 or 4 of them), the
-    // hi term's K steps 20 kh .. and the lo term staged as [cb][lane] 32
-    // bytes (byte b < 16: element 64 cb + 16 h + b, b >= 16: 64 cb + 32 +
-    // 16 h + b - 16, the row bytes' order in the A operand).  The context
-    // waves issue their query loads, then the first DIST tiles' loads, then
-    // build.
+    // ---- prologue: query operands, built by the score waves while the
+    // context waves issue the first DIST tiles' loads (a wave with those in
+    // flight could not wait for query loads of its own without waiting for
+    // them too).  Work item t (two per score-wave thread: t = tid and tid +
+    // 256) loads the nine float4 of head t / 16 at elements 4 (t % 16 + 16
+    // s), s < 9; the head's e = q * sm_scale * log2(e) is scaled by 2^k
+    // (largest |e| in [2^14, 2^15)) and split into fp16 hi + lo (the
+    // subtraction is exact in f32).  hi is staged in the score waves' B
+    // operand layout (K step ks = 4 cb + 2 s' + t' covers elements 64 cb +
+    // 32 s' + 16 h + 8 t' + (0..7) for lane half h; lane = head + 32 h).
+    // LO8: the lo term is quantized to e4m3 with a per-head power-of-2 scale
+    // 2^j (largest |lo| 2^j in [128, 256)) for the e4m3 MFMA, which takes the
+    // row bytes as they are, and staged at the same time in the weight and
+    // exchange buffers (unused until phase 0) as [cb][lane] 32 bytes (byte b
+    // < 16: element 64 cb + 16 h + b, b >= 16: 64 cb + 32 + 16 h + b - 16,
+    // the row bytes' order in the A operand); score wave kh then holds
+    // column blocks 5 kh .. (5 or 4 of them) and the hi term's K steps 20 kh
+    // ...  Without LO8 the fp16 lo term is staged where hi was, once hi has
+    // been read, and score wave kh holds K steps 18 kh .. + 18 of both.
     const int kh = w & 1;
     constexpr int NQH = LO8 ? 20 : KH;  // hi K steps held by a score wave (at most)
     f16x8 qhi[NQH], qlo[LO8 ? 1 : KH];
     v8i32 ql8[LO8 ? 5 : 1];
-    {
-        const int h = tid >> 4, i = tid & 15;
-        const int qh = qh0 + h;
-        const bool hv = qh < a.n_qh;
-        float4 v[9];
+    constexpr int QL8 = W;  // LO8: staging of the e4m3 lo term
+    static_assert(QL8 + NCB * 64 * 32 <= FL, "the lo term fits the weight and exchange buffers");
+    if (ctx_wave) {
+        if (ntiles > 0)
+            issue(0, 0, IC0{}, ICK{});
+        if (ntiles > 1)
+            issue(1, 1, IC0{}, ICK{});
+    }
+    f16x4 lo4[LO8 ? 1 : 2][9];  // without LO8: the lo term until its staging round
+    if (!ctx_wave) {
+        float4 v[2][9];
 #pragma unroll
-        for (int s = 0; s < 9; ++s) {
-            const int e = 4 * (i + 16 * s);
-            const float* p = (e < LC) ? a.q_lat + (size_t)(hv ? qh : 0) * LC + e
-                                      : a.q_rope + (size_t)(hv ? qh : 0) * RC + (e - LC);
-            const float4 x = *reinterpret_cast<const float4*>(p);
-            v[s] = hv ? x : make_float4(0.f, 0.f, 0.f, 0.f);
-        }
-        if (ctx_wave) {
-            if (ntiles > 0)
-                issue(0, 0, IC0{}, ICK{});
-            if (ntiles > 1)
-                issue(1, 1, IC0{}, ICK{});
-        }
-        float amax = 0.0f;
-#pragma unroll
-        for (int s = 0; s < 9; ++s)
-            amax = fmaxf(amax, fmaxf(fmaxf(fabsf(v[s].x), fabsf(v[s].y)),
-                                     fmaxf(fabsf(v[s].z), fabsf(v[s].w))));
-        amax = row16_max(amax);
-        const float es = a.sm_log2;
-        const int k = query_exp(amax * es);
-        if (i == 0)
-            s_k[h] = k;
-        const float mult = ldexpf(es, k);
-        f16x4 lo4[9];
-        auto stage_ptr = [&](int s) __attribute__((always_inline)) -> uint8_t* {
-            const int e = 4 * (i + 16 * s);
-            const int cb = e >> 6, s2 = (e >> 5) & 1, hf = (e >> 4) & 1, t2 = (e >> 3) & 1;
-            const int ks = 4 * cb + 2 * s2 + t2;
-            return lds + QT + ((size_t)ks * 64 + h + 32 * hf) * 16 + 2 * (e & 7);
-        };
-#pragma unroll
-        for (int s = 0; s < 9; ++s) {
-            // r = f32(q 2^k es), rounded once and opaque to the compiler: both
-            // terms are split from this one f32 value (otherwise hi may be
-            // recomputed as the fp16 rounding of the exact product, which
-            // differs where r sits on an fp16 rounding tie)
-            float r[4] = {v[s].x * mult, v[s].y * mult, v[s].z * mult, v[s].w * mult};
-            asm volatile("" : "+v"(r[0]), "+v"(r[1]), "+v"(r[2]), "+v"(r[3]));
-            f16x4 hi;
-#pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                hi[c] = (_Float16)r[c];
-                lo4[s][c] = (_Float16)(r[c] - (float)hi[c]);
-            }
-            *reinterpret_cast<f16x4*>(stage_ptr(s)) = hi;
-        }
-        lds_barrier();
-        if (!ctx_wave) {
-            const int ks0 = LO8 ? 20 * kh : KH * kh;
-            const int nks = LO8 ? 20 - 4 * kh : KH;
-#pragma unroll
-            for (int m = 0; m < NQH; ++m)
-                if (m < nks)
-                    qhi[m] = *reinterpret_cast<const f16x8*>(lds + QT + ((ks0 + m) * 64 + lane) * 16);
-        }
-        lds_barrier();
-        if constexpr (LO8) {
-            float lmax = 0.0f;
-#pragma unroll
-            for (int s = 0; s < 9; ++s)
-#pragma unroll
-                for (int c = 0; c < 4; ++c)
-                    lmax = fmaxf(lmax, fabsf((float)lo4[s][c]));
-            lmax = row16_max(lmax);
-            int ex = 0;
-            if (lmax > 0.0f)
-                (void)frexpf(lmax, &ex);
-            const int j = (lmax > 0.0f) ? max(-100, min(100, 8 - ex)) : 0;
-            if (i == 0)
-                s_k[HG + h] = j;
+        for (int it = 0; it < 2; ++it) {
+            const int t = tid + 256 * it, h = t >> 4, i = t & 15;
+            const int qh = qh0 + h;
+            const bool hv = qh < a.n_qh;
 #pragma unroll
             for (int s = 0; s < 9; ++s) {
                 const int e = 4 * (i + 16 * s);
-                const int cb = e >> 6, off = e & 63, hf = (off >> 4) & 1;
-                const int b = 16 * (off >> 5) + (off & 15);
-                uint32_t word = 0;
-#pragma unroll
-                for (int c = 0; c < 4; ++c)
-                    word |= enc_e4m3(ldexpf((float)lo4[s][c], j)) << (8 * c);
-                *reinterpret_cast<uint32_t*>(lds + QT + ((size_t)(cb * 64 + h + 32 * hf)) * 32 + b) =
-                    word;
+                const float* p = (e < LC) ? a.q_lat + (size_t)(hv ? qh : 0) * LC + e
+                                          : a.q_rope + (size_t)(hv ? qh : 0) * RC + (e - LC);
+                const float4 x = *reinterpret_cast<const float4*>(p);
+                v[it][s] = hv ? x : make_float4(0.f, 0.f, 0.f, 0.f);
             }
-        } else {
+        }
+#pragma unroll
+        for (int it = 0; it < 2; ++it) {
+            const int t = tid + 256 * it, h = t >> 4, i = t & 15;
+            float amax = 0.0f;
 #pragma unroll
             for (int s = 0; s < 9; ++s)
-                *reinterpret_cast<f16x4*>(stage_ptr(s)) = lo4[s];
+                amax = fmaxf(amax, fmaxf(fmaxf(fabsf(v[it][s].x), fabsf(v[it][s].y)),
+                                         fmaxf(fabsf(v[it][s].z), fabsf(v[it][s].w))));
+            amax = row16_max(amax);
+            const float es = a.sm_log2;
+            const int k = query_exp(amax * es);
+            if (i == 0)
+                s_k[h] = k;
+            const float mult = ldexpf(es, k);
+            f16x4 lot[9];
+#pragma unroll
+            for (int s = 0; s < 9; ++s) {
+                // r = f32(q 2^k es), rounded once and opaque to the compiler:
+                // both terms are split from this one f32 value (otherwise hi
+                // may be recomputed as the fp16 rounding of the exact product,
+                // which differs where r sits on an fp16 rounding tie)
+                float r[4] = {v[it][s].x * mult, v[it][s].y * mult, v[it][s].z * mult,
+                              v[it][s].w * mult};
+                asm volatile("" : "+v"(r[0]), "+v"(r[1]), "+v"(r[2]), "+v"(r[3]));
+                f16x4 hi;
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    hi[c] = (_Float16)r[c];
+                    lot[s][c] = (_Float16)(r[c] - (float)hi[c]);
+                }
+                const int e = 4 * (i + 16 * s);
+                const int cb = e >> 6, s2 = (e >> 5) & 1, hf = (e >> 4) & 1, t2 = (e >> 3) & 1;
+                const int ks = 4 * cb + 2 * s2 + t2;
+                *reinterpret_cast<f16x4*>(lds + QT + ((size_t)ks * 64 + h + 32 * hf) * 16 +
+                                          2 * (e & 7)) = hi;
+            }
+            if constexpr (LO8) {
+                float lmax = 0.0f;
+#pragma unroll
+                for (int s = 0; s < 9; ++s)
+#pragma unroll
+                    for (int c = 0; c < 4; ++c)
+                        lmax = fmaxf(lmax, fabsf((float)lot[s][c]));
+                lmax = row16_max(lmax);
+                int ex = 0;
+                if (lmax > 0.0f)
+                    (void)frexpf(lmax, &ex);
+                const int j = (lmax > 0.0f) ? max(-100, min(100, 8 - ex)) : 0;
+                if (i == 0)
+                    s_k[HG + h] = j;
+#pragma unroll
+                for (int s = 0; s < 9; ++s) {
+                    const int e = 4 * (i + 16 * s);
+                    const int cb = e >> 6, off = e & 63, hf = (off >> 4) & 1;
+                    const int b = 16 * (off >> 5) + (off & 15);
+                    // |lo 2^j| < 256: the packed hardware encoder is exact here
+                    *reinterpret_cast<uint32_t*>(lds + QL8 + ((size_t)(cb * 64 + h + 32 * hf)) * 32 +
+                                                 b) =
+                        enc_e4m3_pk4(ldexpf((float)lot[s][0], j), ldexpf((float)lot[s][1], j),
+                                     ldexpf((float)lot[s][2], j), ldexpf((float)lot[s][3], j));
+                }
+            } else {
+#pragma unroll
+                for (int s = 0; s < 9; ++s)
+                    lo4[LO8 ? 0 : it][s] = lot[s];
+            }
+        }
+    }
+    lds_barrier();
+    if (!ctx_wave) {
+        const int ks0 = LO8 ? 20 * kh : KH * kh;
+        const int nks = LO8 ? 20 - 4 * kh : KH;
+#pragma unroll
+        for (int m = 0; m < NQH; ++m)
+            if (m < nks)
+                qhi[m] = *reinterpret_cast<const f16x8*>(lds + QT + ((ks0 + m) * 64 + lane) * 16);
+        if constexpr (LO8) {
+#pragma unroll
+            for (int c = 0; c < 5; ++c)
+                if (c < 5 - kh)
+                    ql8[c] = *reinterpret_cast<const v8i32*>(lds + QL8 + ((5 * kh + c) * 64 + lane) * 32);
+        }
+    }
+    lds_barrier();  // LO8: staging areas free for the ring and the weights
+    if constexpr (!LO8) {
+        if (!ctx_wave) {
+#pragma unroll
+            for (int it = 0; it < 2; ++it) {
+                const int t = tid + 256 * it, h = t >> 4, i = t & 15;
+#pragma unroll
+                for (int s = 0; s < 9; ++s) {
+                    const int e = 4 * (i + 16 * s);
+                    const int cb = e >> 6, s2 = (e >> 5) & 1, hf = (e >> 4) & 1, t2 = (e >> 3) & 1;
+                    const int ks = 4 * cb + 2 * s2 + t2;
+                    *reinterpret_cast<f16x4*>(lds + QT + ((size_t)ks * 64 + h + 32 * hf) * 16 +
+                                              2 * (e & 7)) = lo4[it][s];
+                }
+            }
         }
         lds_barrier();
         if (!ctx_wave) {
-            if constexpr (LO8) {
 #pragma unroll
-                for (int c = 0; c < 5; ++c)
-                    if (c < 5 - kh)
-                        ql8[c] = *reinterpret_cast<const v8i32*>(lds + QT + ((5 * kh + c) * 64 + lane) * 32);
-            } else {
-#pragma unroll
-                for (int m = 0; m < KH; ++m)
-                    qlo[m] = *reinterpret_cast<const f16x8*>(lds + QT + ((KH * kh + m) * 64 + lane) * 16);
-            }
+            for (int m = 0; m < KH; ++m)
+                qlo[m] = *reinterpret_cast<const f16x8*>(lds + QT + ((KH * kh + m) * 64 + lane) * 16);
         }
         lds_barrier();  // staging area free for the ring
     }

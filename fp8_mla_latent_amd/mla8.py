@@ -53,7 +53,8 @@ EXPORTED = ("mla8_quantize_rows", "mla8_append", "mla8_decode", "mla8_append_dec
             "mla8_append_decode_noalloc", "mla8_index_topk", "mla8_kvfile_create",
             "mla8_kvfile_info", "mla8_kvfile_append", "mla8_kvfile_load",
             "mla8_workspace_bytes", "mla8_plan_splits",
-            "mla8_status_string", "mla8_version", "mla8_test_encode", "mla8_stream_read")
+            "mla8_status_string", "mla8_version", "mla8_test_encode", "mla8_test_encode_pk",
+            "mla8_stream_read")
 
 
 class Mla8Opts(ctypes.Structure):
@@ -113,6 +114,7 @@ def _load() -> ctypes.CDLL:
         "mla8_status_string": (ctypes.c_char_p, [ctypes.c_int]),
         "mla8_version": (ctypes.c_char_p, []),
         "mla8_test_encode": (ctypes.c_int, [P, i64, P, P]),
+        "mla8_test_encode_pk": (ctypes.c_int, [P, i64, P, P]),
         "mla8_stream_read": (ctypes.c_int, [P, i64, P, P]),
     }
     for name, (res, args) in sig.items():
@@ -604,4 +606,19 @@ def mla8_test_encode(x: torch.Tensor, codes: torch.Tensor | None = None) -> torc
         codes = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
     _dev(codes, "codes", torch.uint8, tuple(x.shape), x.device)
     _check(lib.mla8_test_encode(_ptr(x), x.numel(), _ptr(codes), _stream(x)), "mla8_test_encode")
+    return codes
+
+
+def mla8_test_encode_pk(x: torch.Tensor, codes: torch.Tensor | None = None) -> torch.Tensor:
+    """The packed hardware e4m3 encoder of the query's lo term, elementwise
+    (test aid, not product API; exact for finite |x| < 448).  x.numel() a
+    multiple of 4."""
+    _dev(x, "x", torch.float32)
+    if x.numel() % 4 != 0:
+        raise ValueError("mla8_test_encode_pk: x.numel() must be a multiple of 4")
+    if codes is None:
+        codes = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
+    _dev(codes, "codes", torch.uint8, tuple(x.shape), x.device)
+    _check(lib.mla8_test_encode_pk(_ptr(x), x.numel(), _ptr(codes), _stream(x)),
+           "mla8_test_encode_pk")
     return codes

@@ -34,6 +34,16 @@ MLA8_API int mla8_stream_read(const void* p, int64_t bytes, uint32_t* out, void*
  */
 MLA8_API int mla8_test_encode(const float* x, int64_t n, uint8_t* codes, void* stream);
 
+/*
+ * Test aid: the packed hardware e4m3 encoder that the e4m3 lo query term of
+ * mla8_opts uses (v_cvt_pk_fp8_f32, round to nearest even onto OCP e4m3),
+ * codes[i] = e4m3(x[i]) for i < n.  Exact for finite |x[i]| < 448, the only
+ * inputs the decode gives it (|lo 2^j| < 256); it does not saturate, so other
+ * inputs give codes that differ from mla8_test_encode.  n a multiple of 4, x
+ * 16-byte aligned, codes 4-byte aligned.  Errors: E_INVAL, E_HIP.
+ */
+MLA8_API int mla8_test_encode_pk(const float* x, int64_t n, uint8_t* codes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

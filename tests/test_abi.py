@@ -313,6 +313,16 @@ def test_stream_read_refuses():
     assert f(FAKE, 64, FAKE_MISALIGNED, None) == m.MLA8_E_INVAL
 
 
+def test_test_encode_pk_refuses():
+    f = m.lib.mla8_test_encode_pk
+    assert f(None, 8, FAKE, None) == m.MLA8_E_INVAL
+    assert f(FAKE, 8, None, None) == m.MLA8_E_INVAL
+    assert f(FAKE, 6, FAKE, None) == m.MLA8_E_INVAL        # not a multiple of 4
+    assert f(FAKE, -4, FAKE, None) == m.MLA8_E_INVAL
+    assert f(FAKE_MISALIGNED, 8, FAKE, None) == m.MLA8_E_INVAL
+    assert f(FAKE, 0, FAKE, None) == m.MLA8_OK             # nothing to do, nothing launched
+
+
 # ---------------------------------------------------------------------------
 # The binding's own checks: a host tensor, a wrong dtype or shape, or a row
 # count beyond the buffer is refused in Python, before the C ABI sees an address.
@@ -342,6 +352,7 @@ def _cpu(shape, dtype):
     lambda: m.mla8_index_topk(_cpu((8, 128), torch.uint8), _cpu((8,), torch.float32),
                               _cpu((16, 128), torch.float32), _cpu((16,), torch.float32), 4),
     lambda: m.mla8_test_encode(_cpu((8,), torch.float32)),
+    lambda: m.mla8_test_encode_pk(_cpu((8,), torch.float32)),
     lambda: m.mla8_stream_read(_cpu((64,), torch.uint8), _cpu((32768,), torch.int32)),
 ])
 def test_binding_refuses_host_tensors(call):

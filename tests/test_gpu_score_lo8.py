@@ -8,7 +8,9 @@ e4m3 lo query terms, the lo term on the e4m3 MFMA) through the C ABI:
   adds up to about 0.35 of it on the x50 recipe (30 seeds measured), so the
   same <= 0.5 holds, seeds 1 and 5 (the outlier test's) and 23 included;
 * mla8_opts.f32_scores (fp16 hi + lo on the fp16 MFMA) changes the result
-  there and nowhere else.
+  there and nowhere else;
+* the packed hardware e4m3 encoder that builds the lo term equals the
+  oracle's encoder on that term's whole input domain.
 """
 from __future__ import annotations
 
@@ -186,3 +188,24 @@ def test_lo8_causal_batch(m, h, n_q, pos0, splits):
     wf = check_attention(host(out), ro, host(lse), rl, "f32_scores batch, exact query",
                          few_rows=few)
     say(f"  worst err/bar: reading {w8:.4f}, exact {we:.4f}, f32_scores {wf:.4f}")
+
+
+def test_lo_term_encoder_matches_the_oracle(m):
+    """The packed hardware e4m3 encoder of the lo term (mla8_test_encode_pk)
+    against oracle.enc on every input the decode can give it: the lo term is
+    an fp16 value scaled by 2^j to below 256, so every finite fp16 value times
+    2^j, j in [-40, 40], with |y| < 448 (5 M values, both signs, the e4m3
+    subnormal and underflow ranges and every rounding tie included)."""
+    say("packed e4m3 encoder of the lo term against the oracle")
+    h = np.arange(65536, dtype=np.uint32).astype(np.uint16).view(np.float16).astype(np.float32)
+    h = h[np.isfinite(h)]
+    parts = []
+    for j in range(-40, 41):
+        y = np.ldexp(h, j).astype(np.float32)
+        parts.append(y[np.isfinite(y) & (np.abs(y) < 448.0)])
+    x = np.concatenate(parts)
+    x = np.concatenate([x, np.zeros((-x.size) % 4, np.float32)])
+    got = host(m.mla8_test_encode_pk(dev(x)))
+    ref = oracle.enc(x)
+    bad = np.flatnonzero(got != ref)
+    assert bad.size == 0, (int(bad.size), float(x[bad[0]]), int(got[bad[0]]), int(ref[bad[0]]))
