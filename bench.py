@@ -413,8 +413,9 @@ def bench_dsa(args):
         "higher_is_better": False,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "e4m3 kv; scores e4m3->f16 rows x f16 hi+lo q (f16 mfma), context f16 weights "
-                 "x e4m3->f16 rows (f16 mfma); f32 accumulate",
+        "dtype": "e4m3 kv; scores e4m3->f16 rows x f16 hi q (f16 mfma) + e4m3 rows x e4m3 lo q "
+                 "(scaled e4m3 mfma), context f16 weights x e4m3->f16 rows (f16 mfma); "
+                 "f32 accumulate",
         "data": "synthetic: seeded N(0,1) rows and queries, sorted unique uniform selections",
         "config": {"workload": w.name, "heads": w.n_heads, "kv_lora": w.lc, "rope": w.rc,
                    "t_rows": T, "selected": NS, "batch": 1, "layers_per_step": L,
@@ -422,7 +423,7 @@ def bench_dsa(args):
         "clock_settle": {"seconds": SETTLE_S, "untimed_steps": n_settle},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                     "kernel": "k_split_partial<9,true>", "kernel_us": round(part_us, 3),
+                     "kernel": "k_partial32<true,true>", "kernel_us": round(part_us, 3),
                      "algorithmic_bytes": alg_bytes,
                      "note": "latency-bound: 1.19 MB of gathered rows per launch"},
         "cpu_baseline": cpu,

@@ -70,7 +70,8 @@ constexpr int Z = CR + HG * 4 * 8;       // f32 [4][HG] z per score wave
 constexpr int HK = Z + 4 * HG * 4;       // i32 [2][HG] query scaling exponents k (and j, LO8)
 constexpr int UV = HK + 2 * HG * 4;      // f32x4 [4 waves][4][64]: u, scale of the weighed tile
 constexpr int AL = UV + 4 * 4 * 64 * 16; // f32 [4 context waves][HG] accumulator factors
-constexpr int END = AL + 4 * HG * 4;
+constexpr int VM = AL + 4 * HG * 4;      // gather: u64 [NSC] row-validity masks (bit = tile row)
+constexpr int END = VM + NSC * 8;
 // query operand staging (one term at a time): stage 2, first filled in phase 0
 constexpr int QT = 2 * STAGE;
 static_assert(NKS * 64 * 16 <= STAGE, "one query term fits a stage");
@@ -97,7 +98,7 @@ __device__ __forceinline__ f32x16 mfma32_f8(v8i32 a, v8i32 b, f32x16 c, int sb)
     return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, sb);
 }
 
-template <bool LO8>
+template <bool LO8, bool GATHER>
 __global__ __launch_bounds__(kThreads, 1) void k_partial32(AttnArgs a)
 {
     using namespace p32;
@@ -155,6 +156,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_partial32(AttnArgs a)
     auto blk_ofs = [&](int k) __attribute__((always_inline)) {  // 16 rb rows + 64 cb bytes
         return (uint32_t)(64 * (k + 135 * (k / NCB)));
     };
+    int32_t g_row[GATHER ? 4 : 1];  // gather: rows of the tile being issued, per row block
     auto issue = [&](int t, int st, auto I0_, auto I1_) __attribute__((always_inline)) {
         constexpr int I0 = decltype(I0_)::value, I1 = decltype(I1_)::value;
         const uint32_t xst = lds_u32 + (uint32_t)(st * STAGE);
@@ -162,14 +164,42 @@ __global__ __launch_bounds__(kThreads, 1) void k_partial32(AttnArgs a)
         // loads of tile t + 3 into its ring stage: a ring of their own
         const uint32_t sct = lds_u32 + (uint32_t)(SC + (t & (NSC - 1)) * TR * 4);
         const int p0 = min(c0 + t * TR, c1 - TR);
-        const uint8_t* tb = a.codes + (size_t)p0 * D;
+        if constexpr (!GATHER) {
+            const uint8_t* tb = a.codes + (size_t)p0 * D;
 #pragma unroll
-        for (int i = I0; i < I1; ++i) {
-            const int k = blk_k(i);
-            dma_b128_s(tb + blk_ofs(k), lane_off, xst + (uint32_t)(1024 * k));
+            for (int i = I0; i < I1; ++i) {
+                const int k = blk_k(i);
+                dma_b128_s(tb + blk_ofs(k), lane_off, xst + (uint32_t)(1024 * k));
+            }
+            if (I1 == KW && dma_lead)
+                dma_b32_s(a.scales + p0, (uint32_t)(4 * lane), sct);
+        } else {
+            // list entries p0 .. p0 + 63 are absolute row indices; one outside
+            // [0, t_rows) loads row 0 and gets no weight.  The indices of the
+            // tile's four row blocks are loaded with the first part.
+            if constexpr (I0 == 0) {
+#pragma unroll
+                for (int rb = 0; rb < 4; ++rb) {
+                    const int32_t r = a.sel[p0 + 16 * rb + (lane & 15)];
+                    g_row[rb] = (r >= 0 && r < a.t_rows) ? r : 0;
+                }
+            }
+#pragma unroll
+            for (int i = I0; i < I1; ++i) {
+                const int k = blk_k(i);
+                const int rb = k / NCB, cb = k - NCB * rb;
+                dma_b128(a.codes + (size_t)g_row[rb] * D + 64 * cb + 16 * (lane >> 4),
+                         xst + (uint32_t)(1024 * k));
+            }
+            if (I1 == KW && dma_lead) {
+                const int32_t r = a.sel[p0 + lane];
+                const bool ok = r >= 0 && r < a.t_rows;
+                dma_b32(a.scales + (ok ? r : 0), sct);
+                const uint64_t valid = __ballot(ok);
+                if (lane == 0)
+                    reinterpret_cast<uint64_t*>(lds + VM)[t & (NSC - 1)] = valid;
+            }
         }
-        if (I1 == KW && dma_lead)
-            dma_b32_s(a.scales + p0, (uint32_t)(4 * lane), sct);
     };
     using IC0 = std::integral_constant<int, 0>;
     using ICA = std::integral_constant<int, 3>;
@@ -245,11 +275,19 @@ __global__ __launch_bounds__(kThreads, 1) void k_partial32(AttnArgs a)
         if (ntiles > 1)
             issue(1, 1, IC0{}, ICK{});
     }
+    // A chunk of a few tiles (gathers, short lists) meets only a light load
+    // burst: there the context waves wait for their loads and build too, one
+    // work item per thread (t = tid), which halves the build.  (Not without
+    // LO8: the fp16 lo term it keeps for its own staging round would not fit
+    // beside the context waves' registers.)
+    const bool all_build = LO8 && ntiles <= 4;
     f16x4 lo4[LO8 ? 1 : 2][9];  // without LO8: the lo term until its staging round
-    if (!ctx_wave) {
-        float4 v[2][9];
+    // NIT work items t = tid + 256 it: all loads first, then the builds
+    auto build = [&](auto NIT_) __attribute__((always_inline)) {
+        constexpr int NIT = decltype(NIT_)::value;
+        float4 v[NIT][9];
 #pragma unroll
-        for (int it = 0; it < 2; ++it) {
+        for (int it = 0; it < NIT; ++it) {
             const int t = tid + 256 * it, h = t >> 4, i = t & 15;
             const int qh = qh0 + h;
             const bool hv = qh < a.n_qh;
@@ -263,7 +301,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_partial32(AttnArgs a)
             }
         }
 #pragma unroll
-        for (int it = 0; it < 2; ++it) {
+        for (int it = 0; it < NIT; ++it) {
             const int t = tid + 256 * it, h = t >> 4, i = t & 15;
             float amax = 0.0f;
 #pragma unroll
@@ -329,6 +367,16 @@ __global__ __launch_bounds__(kThreads, 1) void k_partial32(AttnArgs a)
                     lo4[LO8 ? 0 : it][s] = lot[s];
             }
         }
+    };
+    using IT1 = std::integral_constant<int, 1>;
+    using IT2 = std::integral_constant<int, 2>;
+    if (!ctx_wave) {
+        if (all_build)
+            build(IT1{});
+        else
+            build(IT2{});
+    } else if (all_build) {
+        build(IT1{});
     }
     lds_barrier();
     if (!ctx_wave) {
@@ -347,9 +395,11 @@ __global__ __launch_bounds__(kThreads, 1) void k_partial32(AttnArgs a)
     }
     lds_barrier();  // LO8: staging areas free for the ring and the weights
     if constexpr (!LO8) {
-        if (!ctx_wave) {
+        if (all_build || !ctx_wave) {
 #pragma unroll
             for (int it = 0; it < 2; ++it) {
+                if (it == 1 && all_build)
+                    break;
                 const int t = tid + 256 * it, h = t >> 4, i = t & 15;
 #pragma unroll
                 for (int s = 0; s < 9; ++s) {
@@ -479,6 +529,18 @@ __global__ __launch_bounds__(kThreads, 1) void k_partial32(AttnArgs a)
 #pragma unroll
                 for (int v = 0; v < 8; ++v)
                     u[v] = (accp[v] + yv[v]) * scv[v];
+                if constexpr (GATHER) {
+                    // -inf for list entries outside [0, t_rows): bit row of
+                    // the tile's validity mask
+                    const uint64_t mk = reinterpret_cast<const uint64_t*>(lds + VM)[t & (NSC - 1)];
+                    const uint32_t bits = (uint32_t)(mk >> (32 * rh + rb0));
+#pragma unroll
+                    for (int r = 0; r < 2; ++r)
+#pragma unroll
+                        for (int v = 0; v < 4; ++v)
+                            if (((bits >> (8 * r + v)) & 1u) == 0u)
+                                u[4 * r + v] = -INFINITY;
+                }
                 if constexpr (decltype(RAGGED_)::value) {
                     const int lead = c0 + (t + 1) * TR - c1;  // rows before the tile's own
 #pragma unroll
@@ -840,7 +902,7 @@ bool partial32_applies(const AttnArgs& a)
 {
     if (a.layout != kE4m3 || a.lc != p32::LC || a.rc != p32::RC || a.n_list < p32::TR)
         return false;
-    if (a.mode == kDense)
+    if (a.mode == kDense || a.mode == kSelect)
         return true;
     // causal batch: every group within one query position, and every query's
     // rows (at least pos0 + 1) fill a tile, which the ragged last tile needs
@@ -850,10 +912,15 @@ bool partial32_applies(const AttnArgs& a)
 void launch_partial32(const AttnArgs& a, hipStream_t stream)
 {
     const dim3 grid((unsigned)(a.n_chunks * a.n_groups));
-    if (a.lo8)
-        hipLaunchKernelGGL(k_partial32<true>, grid, dim3(kThreads), 0, stream, a);
+    const bool g = a.mode == kSelect;
+    if (a.lo8 && g)
+        hipLaunchKernelGGL((k_partial32<true, true>), grid, dim3(kThreads), 0, stream, a);
+    else if (a.lo8)
+        hipLaunchKernelGGL((k_partial32<true, false>), grid, dim3(kThreads), 0, stream, a);
+    else if (g)
+        hipLaunchKernelGGL((k_partial32<false, true>), grid, dim3(kThreads), 0, stream, a);
     else
-        hipLaunchKernelGGL(k_partial32<false>, grid, dim3(kThreads), 0, stream, a);
+        hipLaunchKernelGGL((k_partial32<false, false>), grid, dim3(kThreads), 0, stream, a);
 }
 
 }  // namespace mla8

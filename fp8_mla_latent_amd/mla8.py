@@ -17,8 +17,9 @@ Per-call options (the C struct mla8_opts): ``n_splits`` forces the number of
 row chunks of the split-T plan (0 = automatic), ``events`` = (before, after)
 torch.cuda.Event pair recorded around the split-T partial kernel (the
 indexer's score kernel for mla8_index_topk), ``f32_scores`` scores of f32
-grade also for the e4m3 512/64 decode and causal batch, which by default attend
-with the query's lo term quantized to e4m3 (see mla8_opts in include/mla8.h).
+grade also for the e4m3 512/64 decode, selected-row decode and causal batch,
+which by default attend with the query's lo term quantized to e4m3 (see
+mla8_opts in include/mla8.h).
 Nothing is kept between calls.
 """
 from __future__ import annotations
@@ -401,7 +402,7 @@ def mla8_append_decode_mx(kv_rows, kv_scales, t_rows: int, x_new, lc: int, rc: i
 
 
 def _sel_call(fn: str, row_bytes: int, kv, kv_scales, t_rows, lc, rc, sel, q_lat, q_rope,
-              sm_scale, out, lse, workspace, want_lse, n_splits, events):
+              sm_scale, out, lse, workspace, want_lse, n_splits, events, f32_scores=False):
     cap = _shadow(kv, kv_scales, row_bytes)
     dev = kv.device
     if not (1 <= int(t_rows) <= cap):
@@ -413,7 +414,7 @@ def _sel_call(fn: str, row_bytes: int, kv, kv_scales, t_rows, lc, rc, sel, q_lat
     _queries(q_lat, q_rope, (h,), lc, rc, dev)
     out, lse = _out_lse(out, lse, (h,), lc, dev, want_lse)
     ws = _workspace(MLA8_OP_DECODE_SEL, ns, h, 1, lc, dev, workspace, n_splits)
-    o = _opts(n_splits, events)
+    o = _opts(n_splits, events, f32_scores)
     _check(getattr(lib, fn)(_ptr(kv), _ptr(kv_scales), t_rows, lc, rc, _ptr(sel), ns,
                             _ptr(q_lat), _ptr(q_rope), h, float(sm_scale), _ptr(out), _ptr(lse),
                             _ptr(ws), ws.numel(), _stream(q_lat), _o(o)), fn)
@@ -422,11 +423,12 @@ def _sel_call(fn: str, row_bytes: int, kv, kv_scales, t_rows, lc, rc, sel, q_lat
 
 def mla8_decode_sel(kv_codes, kv_scales, t_rows: int, lc: int, rc: int, sel, q_lat, q_rope,
                     sm_scale: float, out=None, lse=None, workspace=None, want_lse: bool = True,
-                    n_splits: int = 0, events=None):
+                    n_splits: int = 0, events=None, f32_scores: bool = False):
     """Decode over the selected absolute rows sel [ns] (int32; entries outside
     [0, t_rows) are skipped by the kernel)."""
     return _sel_call("mla8_decode_sel", lc + rc, kv_codes, kv_scales, t_rows, lc, rc, sel, q_lat,
-                     q_rope, sm_scale, out, lse, workspace, want_lse, n_splits, events)
+                     q_rope, sm_scale, out, lse, workspace, want_lse, n_splits, events,
+                     f32_scores)
 
 
 def mla8_decode_sel_mx(kv_rows, kv_scales, t_rows: int, lc: int, rc: int, sel, q_lat, q_rope,

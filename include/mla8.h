@@ -83,8 +83,9 @@ enum { MLA8_OP_DECODE = 0, MLA8_OP_DECODE_SEL = 1, MLA8_OP_BATCH = 2, MLA8_OP_IN
  *              duration; NULL to skip.  Caller-owned.
  *   f32_scores 0 (default): for e4m3 rows with lc = 512, rc = 64 (dense
  *              mla8_decode, mla8_append_decode, mla8_append_decode_noalloc
- *              over at least 64 rows; mla8_batch with n_heads a multiple of
- *              32 and pos0 >= 63) the scores use the e4m3 MFMA for the
+ *              over at least 64 rows; mla8_decode_sel over at least 64 list
+ *              entries; mla8_batch with n_heads a multiple of 32 and pos0 >=
+ *              63) the scores use the e4m3 MFMA for the
  *              query's lo term [B1-FMHA first pass, intentional limits: the
  *              noPE QK product on the fp8 tensor cores]: per head, e = q *
  *              sm_scale * log2(e) is scaled by 2^k (largest |e| in [2^14,
@@ -207,7 +208,9 @@ MLA8_API int mla8_append_decode_noalloc(uint8_t* kv_codes, float* kv_scales, int
  * each head attends only the rows listed in sel[0..ns), absolute indices into
  * the shadow read straight from it.  sel is a multiset (repeats count as often
  * as they appear); entries outside [0, t_rows) are skipped.  If no entry is in
- * range, out is all zeros and lse is -inf.  No cap on ns beyond 2^31.
+ * range, out is all zeros and lse is -inf.  No cap on ns beyond 2^31.  For
+ * lc = 512, rc = 64 and ns >= 64, q is the e4m3-lo-term query that
+ * mla8_opts.f32_scores describes unless that option is set.
  * Errors: as mla8_decode, plus E_INVAL for ns <= 0; workspace from
  * mla8_workspace_bytes(MLA8_OP_DECODE_SEL, ns, n_heads, 1, lc).
  */

@@ -195,7 +195,9 @@ def test_index_selection_feeds_the_gather_decode(m):
     out, lse = m.mla8_decode_sel(codes, scales, t, wl.lc, wl.rc, dev(sel), dev(ql), dev(qr),
                                  wl.sm_scale)
     oc, os_ = oracle.quantize_rows(x)
-    ro, rl = oracle.decode_sel(oc, os_, t, wl.lc, wl.rc, sel, ql, qr, wl.sm_scale)
+    # 512 selected rows: the e4m3-lo score path, checked against its query reading
+    qa, qb = oracle.query_lo8(ql, qr, wl.sm_scale)
+    ro, rl = oracle.decode_sel(oc, os_, t, wl.lc, wl.rc, sel, qa, qb, wl.sm_scale)
     from tests.tolerance import check_attention
     check_attention(host(out), ro, host(lse), rl, "index -> decode_sel")
 

@@ -284,18 +284,30 @@ def test_decode_sel_workload(m):
     ql, qr = W.queries(w)
     out, lse = m.mla8_decode_sel(codes, scales, w.t_rows, w.lc, w.rc, dev(sel), dev(ql),
                                  dev(qr), w.sm_scale)
+    # the default e4m3-lo score path attends with the query of oracle.query_lo8
+    qa, qb = oracle.query_lo8(ql, qr, w.sm_scale)
+    ro, rl = oracle.decode_sel(oc, os_, w.t_rows, w.lc, w.rc, sel, qa, qb, w.sm_scale)
+    check_attention(host(out), ro, host(lse), rl, f"{w.name}, its reading")
     ro, rl = oracle.decode_sel(oc, os_, w.t_rows, w.lc, w.rc, sel, ql, qr, w.sm_scale)
-    check_attention(host(out), ro, host(lse), rl, w.name)
+    check_attention(host(out), ro, host(lse), rl, f"{w.name}, exact query")
+    out, lse = m.mla8_decode_sel(codes, scales, w.t_rows, w.lc, w.rc, dev(sel), dev(ql),
+                                 dev(qr), w.sm_scale, f32_scores=True)
+    check_attention(host(out), ro, host(lse), rl, f"{w.name}, f32_scores")
 
 
 @pytest.mark.parametrize("case", ["dups", "out_of_range", "single", "all_rows", "none_valid",
-                                  "ragged"])
+                                  "ragged", "out_of_range_long", "none_valid_long",
+                                  "straddle"])
 def test_decode_sel_edges(m, case):
+    """Selection edge cases.  Lists of 64 entries or more take the e4m3-lo
+    score path (checked against its query reading, and with f32_scores
+    against the exact query); shorter lists the general kernel."""
     lc, rc, t, h = 512, 64, 1500, 20
     g = np.random.Generator(np.random.PCG64(5))
     x = g.standard_normal((t, lc + rc)).astype(np.float32)
     ql = g.standard_normal((h, lc)).astype(np.float32)
     qr = g.standard_normal((h, rc)).astype(np.float32)
+    junk = np.array([-1, 1500, 1 << 30, -5, 2 ** 31 - 1, -(2 ** 31)], np.int32)
     sel = {
         "dups": np.array([5, 5, 5, 900, 17, 900, 1499, 0] * 9, np.int32),
         "out_of_range": np.array([-1, 3, 1500, 77, 1 << 30, -5, 1200, 2 ** 31 - 1], np.int32),
@@ -303,17 +315,30 @@ def test_decode_sel_edges(m, case):
         "all_rows": np.arange(t, dtype=np.int32),
         "none_valid": np.array([-3, 1500, 99999], np.int32),
         "ragged": np.sort(g.choice(t, 131, replace=False)).astype(np.int32),
+        # 100 entries, every third out of range, across the ragged last tile
+        "out_of_range_long": np.where(np.arange(100) % 3 == 0, np.resize(junk, 100),
+                                      g.integers(0, t, 100)).astype(np.int32),
+        "none_valid_long": np.resize(junk, 100).astype(np.int32),
+        # 64 x 3 + 5 entries over several chunks, out-of-range ones straddling
+        # tile boundaries
+        "straddle": np.where((np.arange(197) % 64) >= 61, np.resize(junk, 197),
+                             g.integers(0, t, 197)).astype(np.int32),
     }[case]
     say(f"decode_sel edge {case} ns={sel.size}")
     oc, os_ = oracle.quantize_rows(x)
     sm = 1 / math.sqrt(192)
-    out, lse = m.mla8_decode_sel(dev(oc), dev(os_), t, lc, rc, dev(sel), dev(ql), dev(qr), sm)
-    ro, rl = oracle.decode_sel(oc, os_, t, lc, rc, sel, ql, qr, sm)
-    if case == "none_valid":
-        assert np.all(host(out) == 0) and np.all(np.isneginf(host(lse)))
-    else:
-        # 1 to 131 distinct rows attended (all_rows: 1500)
-        check_attention(host(out), ro, host(lse), rl, case, few_rows=case != "all_rows")
+    lo8 = sel.size >= 64
+    for f32 in ((False, True) if lo8 else (False,)):
+        out, lse = m.mla8_decode_sel(dev(oc), dev(os_), t, lc, rc, dev(sel), dev(ql), dev(qr), sm,
+                                     f32_scores=f32)
+        qa, qb = (oracle.query_lo8(ql, qr, sm) if lo8 and not f32 else (ql, qr))
+        ro, rl = oracle.decode_sel(oc, os_, t, lc, rc, sel, qa, qb, sm)
+        if not (ro != 0).any() and np.all(np.isneginf(rl)):
+            assert np.all(host(out) == 0) and np.all(np.isneginf(host(lse)))
+        else:
+            # 1 to 197 distinct rows attended (all_rows: 1500)
+            check_attention(host(out), ro, host(lse), rl, f"{case} f32_scores={f32}",
+                            few_rows=case != "all_rows")
 
 
 @pytest.mark.parametrize("h,n_q,t,lc,rc", [(3, 7, 300, 64, 16), (64, 5, 200, 512, 64),
