@@ -144,15 +144,15 @@ def test_plans_and_workspace_sizes():
     assert m.mla8_plan_splits(m.MLA8_OP_DECODE, 262144, 64) == 128
     assert m.mla8_workspace_bytes(m.MLA8_OP_DECODE, 262144, 64, 1, 512) == \
         2 * 128 * 64 * 4 + 128 * 64 * 512 * 4
-    assert m.mla8_plan_splits(m.MLA8_OP_DECODE, 256, 4) == 1
-    assert m.mla8_plan_splits(m.MLA8_OP_DECODE, 4096, 128) == 16
+    assert m.mla8_plan_splits(m.MLA8_OP_DECODE, 256, 4) == 2     # chunks of at least 128 rows
+    assert m.mla8_plan_splits(m.MLA8_OP_DECODE, 4096, 128) == 32
     assert m.mla8_plan_splits(m.MLA8_OP_DECODE_SEL, 2048, 64) == 32
     assert m.mla8_plan_splits(m.MLA8_OP_BATCH, 32768, 64, 64) == 2
     assert m.mla8_workspace_bytes(m.MLA8_OP_DECODE, 0, 64, 1, 512) == 0
     assert m.mla8_workspace_bytes(7, 10, 64, 1, 512) == 0
     assert m.mla8_plan_splits(m.MLA8_OP_DECODE, 4096, 128, n_splits=5) == 5
     assert m.mla8_plan_splits(m.MLA8_OP_DECODE, 100, 4, n_splits=5) == 2  # 64-row tiles
-    assert m.mla8_plan_splits(m.MLA8_OP_DECODE, 4096, 128) == 16
+    assert m.mla8_plan_splits(m.MLA8_OP_DECODE, 4096, 128) == 32
 
 
 def test_options_are_per_call():
