@@ -1126,11 +1126,12 @@ __global__ __launch_bounds__(kThreads, 1) void k_split_partial(AttnArgs a)
                     const float f = __shfl(fo, 4 * g + v);
                     const int qh = qh0 + 16 * ht + 4 * g + v;
                     if (qh < a.n_qh) {
+                        // streaming stores: the merge reads them once, from beyond L2
                         float* dst = a.ws_cl + (pbase + qh) * a.lc + 128 * c + n;
 #pragma unroll
                         for (int jm = 0; jm < 8; ++jm)
                             if (jm < nct)
-                                dst[16 * jm] = O[ht][jm][v] * f;
+                                __builtin_nontemporal_store(O[ht][jm][v] * f, dst + 16 * jm);
                     }
                 }
             }

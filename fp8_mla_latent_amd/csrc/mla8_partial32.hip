@@ -879,10 +879,12 @@ __global__ __launch_bounds__(kThreads, 1) void k_partial32(AttnArgs a)
             const float f = (hd >> 4) ? fb : fa;
             const int qh = qh0 + hd;
             if (qh < a.n_qh) {
+                // streaming stores: the merge reads the partials once, from
+                // beyond L2 (another XCD's workgroups wrote most of them)
                 float* dst = a.ws_cl + (pbase + qh) * LC + 128 * c + (lane & 31);
 #pragma unroll
                 for (int jb = 0; jb < 4; ++jb)
-                    dst[32 * jb] = O[jb][v] * f;
+                    __builtin_nontemporal_store(O[jb][v] * f, dst + 32 * jb);
             }
         }
     }
