@@ -211,6 +211,47 @@ def bf16_value(b) -> np.ndarray:
     return np.array([f(int(t)) for t in v], np.float64).reshape(np.shape(b))
 
 
+def query_lo8_mx(q_lat, q_rope, sm_scale):
+    """The query that the mixed-row decode (noPE e4m3 + RoPE bf16) attends
+    with by default (mla8_opts.f32_scores turns it off): the query_lo8
+    construction on the noPE part alone, and the RoPE part as two bf16 terms.
+
+    Reading of [B1-FMHA first pass, intentional first-pass limits: the noPE QK
+    product on the fp8 tensor cores; RoPE stays bf16] on this library's terms.
+    es = f32(sm_scale) * f32(log2 e) (an f32 product).  noPE, per head: k = 15
+    - ex(f32(max|q_lat| * es)) capped at 100 (0 for a zero head), r =
+    f32(q_lat * f32(es 2^k)), hi = fp16(r), lo = fp16(r - hi), j = 8 -
+    ex(max|lo|) clamped to [-100, 100] (0 when lo is all zero), lo8 =
+    enc(f32(lo 2^j)); q_lat' = (hi + dec(lo8) 2^-j) 2^-k / es.  The RoPE part
+    does not enter k.  RoPE, per element: e = f32(q_rope * es), hi = bf16(e),
+    lo = bf16(f32(e - hi)) (round to nearest even); q_rope' = (hi + lo) / es.
+    Returns (q_lat' [H, lc], q_rope' [H, rc]) as float32 arrays.
+    """
+    ql = np.asarray(q_lat, np.float32)
+    qr = np.asarray(q_rope, np.float32)
+    es = np.float32(np.float32(sm_scale) * np.float32(1.4426950408889634))
+    out_l = np.empty(ql.shape, np.float64)
+    for h in range(ql.shape[0]):
+        e = ql[h]
+        emax = np.float32(np.max(np.abs(e)) * es) if e.size else np.float32(0)
+        k = min(15 - int(np.frexp(emax)[1]), 100) if emax > 0 else 0
+        mult = np.float32(np.ldexp(es, k))
+        r = (e * mult).astype(np.float32)
+        hi = r.astype(np.float16)
+        lo = (r - hi.astype(np.float32)).astype(np.float16)
+        lmax = float(np.max(np.abs(lo.astype(np.float32)))) if lo.size else 0.0
+        j = max(-100, min(100, 8 - int(np.frexp(lmax)[1]))) if lmax > 0 else 0
+        lo8 = enc(np.ldexp(lo.astype(np.float32), j).astype(np.float32))
+        out_l[h] = np.ldexp(hi.astype(np.float64) + np.ldexp(dec(lo8), -j), -k) / np.float64(es)
+    e = (qr * es).astype(np.float32)
+    rhi = bf16(e)
+    rhi_v = bf16_value(rhi)
+    rlo = bf16((e.astype(np.float64) - rhi_v).astype(np.float32))
+    out_r = (rhi_v + bf16_value(rlo)) / np.float64(es)
+    return (np.ascontiguousarray(out_l.astype(np.float32)),
+            np.ascontiguousarray(out_r.astype(np.float32)))
+
+
 def quantize_rows_mx(x, lc, rc) -> tuple[np.ndarray, np.ndarray]:
     """Mixed rows: f32 [n, lc + rc] -> (rows uint8 [n, lc + 2 rc], scales f32 [n])."""
     v = _c(x, np.float32)

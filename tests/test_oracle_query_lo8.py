@@ -12,6 +12,11 @@ scale; mla8_opts.f32_scores turns it off).  No GPU.
 * the e4m3 step against torch's float8_e4m3fn cast on the same scaled values
   (round to nearest even; the values stay below 448, so the saturating and
   the non-saturating encoder agree).
+
+oracle.query_lo8_mx, the mixed-row variant: the same identity and bounds for
+the noPE part, whose scaling exponent must ignore the RoPE part (checked with
+RoPE values 1e6 times larger), and the RoPE part as two bf16 terms, checked
+against torch's bf16 rounding.
 """
 import numpy as np
 import pytest
@@ -74,3 +79,60 @@ def test_e4m3_step_matches_torch():
     ours = oracle.dec(oracle.enc(v))
     ref = torch.from_numpy(v).to(torch.float8_e4m3fn).to(torch.float64).numpy()
     assert np.array_equal(ours, ref)
+
+
+# ---- oracle.query_lo8_mx: the mixed-row variant (noPE lo term in e4m3, k over
+# the noPE part alone; RoPE as two bf16 terms)
+
+def test_mx_exact_query_reconstructs_exactly():
+    """Integer noPE queries with es = 1 are held by the fp16 hi term (lo = 0);
+    small-integer RoPE values are bf16 values (their lo term is 0)."""
+    sm = _es_one_scale()
+    g = np.random.default_rng(13)
+    ql = g.integers(-7, 8, size=(4, 448)).astype(np.float32)
+    qr = g.integers(-100, 101, size=(4, 64)).astype(np.float32)
+    ql[:, 0] = 7.0
+    a, b = oracle.query_lo8_mx(ql, qr, sm)
+    assert np.array_equal(a, ql) and np.array_equal(b, qr)
+
+
+@pytest.mark.parametrize("rope_scale", [1.0, 1e6, 1e-6])
+def test_mx_bounds_and_noPE_scaling_ignores_rope(rope_scale):
+    """noPE within 2^-15 of each head's largest |q_lat| whatever the RoPE
+    magnitudes (a k taken over the RoPE part too would leave the noPE part
+    with fewer bits when RoPE is 1e6 times larger); RoPE within 2^-16 of each
+    element (two bf16 terms hold about 16 bits); and the noPE lo term is there
+    (the fp16 hi term alone misses by about 2^-12)."""
+    sm = 1.0 / np.sqrt(192.0)
+    g = np.random.default_rng(17)
+    ql = g.standard_normal((8, 448)).astype(np.float32)
+    qr = (g.standard_normal((8, 64)) * rope_scale).astype(np.float32)
+    a, b = oracle.query_lo8_mx(ql, qr, sm)
+    dev = np.abs(a.astype(np.float64) - ql).max(1) / np.abs(ql).max(1)
+    assert np.all(dev <= 2.0 ** -15), dev.max()
+    assert np.all(np.abs(b.astype(np.float64) - qr) <= 2.0 ** -16 * np.abs(qr)), \
+        float((np.abs(b.astype(np.float64) - qr) / np.abs(qr)).max())
+    es = np.float32(np.float32(sm) * np.float32(1.4426950408889634))
+    for h in range(ql.shape[0]):
+        e = ql[h]
+        k = 15 - int(np.frexp(np.float32(np.abs(e).max() * es))[1])
+        r = (e * np.float32(np.ldexp(es, k))).astype(np.float32)
+        hi = r.astype(np.float16).astype(np.float64)
+        hi_dev = np.abs(np.ldexp(hi, -k) / np.float64(es) - ql[h]).max() / np.abs(ql[h]).max()
+        assert dev[h] < hi_dev / 8, (h, dev[h], hi_dev)
+
+
+def test_mx_rope_terms_are_bf16_values():
+    """The RoPE reconstruction is the sum of two bf16 values (times 1/es): with
+    es = 1 it is exactly bf16(e) + bf16(e - bf16(e)), checked against torch's
+    bf16 rounding."""
+    sm = _es_one_scale()
+    g = np.random.default_rng(19)
+    qr = g.standard_normal((3, 64)).astype(np.float32)
+    ql = np.ones((3, 448), np.float32)
+    _, b = oracle.query_lo8_mx(ql, qr, sm)
+    t = torch.from_numpy(qr)
+    hi = t.to(torch.bfloat16).to(torch.float32)
+    lo = (t - hi).to(torch.bfloat16).to(torch.float32)
+    ref = (hi.double() + lo.double()).float().numpy()
+    assert np.array_equal(b, ref)
