@@ -742,9 +742,9 @@ def bench_mixed(args):
         "higher_is_better": False,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "e4m3 noPE + bf16 RoPE rows; scores e4m3->f16 x f16 hi+lo q (f16 mfma) + bf16 x "
-                 "2-term bf16 q (bf16 mfma), context f16 weights x e4m3->f16 (f16 mfma); "
-                 "f32 accumulate",
+        "dtype": "e4m3 noPE + bf16 RoPE rows; scores e4m3->f16 x f16 hi q (f16 mfma) + e4m3 x "
+                 "e4m3 lo q (scaled e4m3 mfma) + bf16 x 2-term bf16 q (bf16 mfma), context f16 "
+                 "weights x e4m3->f16 (f16 mfma); f32 accumulate",
         "data": "synthetic: seeded N(0,1) rows and queries",
         "config": {"workload": "mixed_t262144", "heads": w.n_heads, "nope": LC, "rope": RC,
                    "t_rows": T, "batch": 1, "layers_per_step": L,
@@ -753,7 +753,7 @@ def bench_mixed(args):
         "clock_settle": {"seconds": SETTLE_S, "untimed_steps": n_settle},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                     "kernel": "k_split_partial<9,false,true>", "kernel_us": round(part_us, 3),
+                     "kernel": "k_partial32<true,false,true>", "kernel_us": round(part_us, 3),
                      "algorithmic_bytes": alg_bytes},
         "cpu_baseline": cpu,
     }

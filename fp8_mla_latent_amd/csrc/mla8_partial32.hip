@@ -80,6 +80,7 @@ static_assert(NINS % 4 == 0, "row DMAs split evenly over the context waves");
 }  // namespace p32
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef int v2i32 __attribute__((ext_vector_type(2)));
 typedef int v8i32 __attribute__((ext_vector_type(8)));
 
@@ -91,6 +92,11 @@ __device__ __forceinline__ f32x16 mfma32(f16x8 a, f16x8 b, f32x16 c)
 {
     return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
 }
+// bf16 x bf16 (the RoPE part of a mixed row against the RoPE query terms)
+__device__ __forceinline__ f32x16 mfma32_bf16(bf16x8 a, bf16x8 b, f32x16 c)
+{
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
 // e4m3 x e4m3, K = 64, A unscaled, B (the query's lo term) scaled by the
 // E8M0 exponent sb (value 2^(sb - 127)) of each lane's column
 __device__ __forceinline__ f32x16 mfma32_f8(v8i32 a, v8i32 b, f32x16 c, int sb)
@@ -98,10 +104,17 @@ __device__ __forceinline__ f32x16 mfma32_f8(v8i32 a, v8i32 b, f32x16 c, int sb)
     return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, sb);
 }
 
-template <bool LO8, bool GATHER>
+template <bool LO8, bool GATHER, bool MXL>
 __global__ __launch_bounds__(kThreads, 1) void k_partial32(AttnArgs a)
 {
     using namespace p32;
+    // Mixed rows (MXL): 448 noPE e4m3 bytes (column blocks 0-6) then 64 RoPE
+    // bf16 values (blocks 7-8), the same 576 bytes; the output and the
+    // context cover the 448 noPE columns.  Only with LO8.
+    static_assert(!MXL || LO8, "mixed rows take the e4m3 lo term");
+    constexpr int LCO = MXL ? 448 : LC;     // q_lat width, output width
+    constexpr int NCN = MXL ? 7 : NCB;      // e4m3 column blocks
+    constexpr int NQF = MXL ? 8 : 9;        // query float4 per work item
     __shared__ __attribute__((aligned(1024))) uint8_t lds[END];
     float* const s_sc = reinterpret_cast<float*>(lds + SC);
     _Float16* const s_w = reinterpret_cast<_Float16*>(lds + W);
@@ -235,8 +248,12 @@ __global__ __launch_bounds__(kThreads, 1) void k_partial32(AttnArgs a)
     const bool fresh_late = f0 < f1 && f0 - c0 >= (DIST + 1) * TR;
     auto quantize_fresh = [&](int first, int stride) __attribute__((always_inline)) {
         for (int r = f0 + first; r < f1; r += stride)
-            quantize_row_wave(a.x_new + (size_t)(r - a.new0) * D, D, a.new_codes + (size_t)r * D,
-                              a.new_scales + r, lane);
+            if constexpr (MXL)
+                quantize_row_mx_wave(a.x_new + (size_t)(r - a.new0) * (LCO + RC), LCO, RC,
+                                     a.new_codes + (size_t)r * D, a.new_scales + r, lane);
+            else
+                quantize_row_wave(a.x_new + (size_t)(r - a.new0) * D, D, a.new_codes + (size_t)r * D,
+                                  a.new_scales + r, lane);
     };
     if (f0 < f1 && !fresh_late) {
         quantize_fresh(w, 8);
@@ -267,6 +284,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_partial32(AttnArgs a)
     constexpr int NQH = LO8 ? 20 : KH;  // hi K steps held by a score wave (at most)
     f16x8 qhi[NQH], qlo[LO8 ? 1 : KH];
     v8i32 ql8[LO8 ? 5 : 1];
+    bf16x8 qr[MXL ? 8 : 1];  // mixed rows, kh = 1: RoPE terms [K step m][hi, lo]
     constexpr int QL8 = W;  // LO8: staging of the e4m3 lo term
     static_assert(QL8 + NCB * 64 * 32 <= FL, "the lo term fits the weight and exchange buffers");
     if (ctx_wave) {
@@ -285,17 +303,21 @@ __global__ __launch_bounds__(kThreads, 1) void k_partial32(AttnArgs a)
     // NIT work items t = tid + 256 it: all loads first, then the builds
     auto build = [&](auto NIT_) __attribute__((always_inline)) {
         constexpr int NIT = decltype(NIT_)::value;
-        float4 v[NIT][9];
+        float4 v[NIT][NQF];
 #pragma unroll
         for (int it = 0; it < NIT; ++it) {
             const int t = tid + 256 * it, h = t >> 4, i = t & 15;
             const int qh = qh0 + h;
             const bool hv = qh < a.n_qh;
 #pragma unroll
-            for (int s = 0; s < 9; ++s) {
+            for (int s = 0; s < NQF; ++s) {
+                // elements 4 (i + 16 s): q_lat, then q_rope (mixed rows: the
+                // last float4 is RoPE elements 4 i ..)
                 const int e = 4 * (i + 16 * s);
-                const float* p = (e < LC) ? a.q_lat + (size_t)(hv ? qh : 0) * LC + e
-                                          : a.q_rope + (size_t)(hv ? qh : 0) * RC + (e - LC);
+                const float* p = MXL ? (s < 7 ? a.q_lat + (size_t)(hv ? qh : 0) * LCO + e
+                                              : a.q_rope + (size_t)(hv ? qh : 0) * RC + 4 * i)
+                                     : ((e < LC) ? a.q_lat + (size_t)(hv ? qh : 0) * LC + e
+                                                 : a.q_rope + (size_t)(hv ? qh : 0) * RC + (e - LC));
                 const float4 x = *reinterpret_cast<const float4*>(p);
                 v[it][s] = hv ? x : make_float4(0.f, 0.f, 0.f, 0.f);
             }
@@ -305,7 +327,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_partial32(AttnArgs a)
             const int t = tid + 256 * it, h = t >> 4, i = t & 15;
             float amax = 0.0f;
 #pragma unroll
-            for (int s = 0; s < 9; ++s)
+            for (int s = 0; s < NQF - (MXL ? 1 : 0); ++s)
                 amax = fmaxf(amax, fmaxf(fmaxf(fabsf(v[it][s].x), fabsf(v[it][s].y)),
                                          fmaxf(fabsf(v[it][s].z), fabsf(v[it][s].w))));
             amax = row16_max(amax);
@@ -316,7 +338,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_partial32(AttnArgs a)
             const float mult = ldexpf(es, k);
             f16x4 lot[9];
 #pragma unroll
-            for (int s = 0; s < 9; ++s) {
+            for (int s = 0; s < NQF - (MXL ? 1 : 0); ++s) {
                 // r = f32(q 2^k es), rounded once and opaque to the compiler:
                 // both terms are split from this one f32 value (otherwise hi
                 // may be recomputed as the fp16 rounding of the exact product,
@@ -336,10 +358,29 @@ __global__ __launch_bounds__(kThreads, 1) void k_partial32(AttnArgs a)
                 *reinterpret_cast<f16x4*>(lds + QT + ((size_t)ks * 64 + h + 32 * hf) * 16 +
                                           2 * (e & 7)) = hi;
             }
+            if constexpr (MXL) {
+                // RoPE elements 4 i .. + 3: e = q_rope es split into bf16 hi
+                // + lo (no 2^k, no row scale), staged after the 28 noPE hi K
+                // steps as [K step m][term][lane] 16 bytes, m = i / 4, lane =
+                // head + 32 ((i / 2) % 2), bf16 positions 4 (i % 2) ..
+                const float4 q4 = v[it][NQF - 1];
+                const float e[4] = {q4.x * es, q4.y * es, q4.z * es, q4.w * es};
+                uint32_t hb[4], lb[4];
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    hb[c] = bf16_rne_bits(e[c]);
+                    lb[c] = bf16_rne_bits(e[c] - __uint_as_float(hb[c] << 16));
+                }
+                const int m = i >> 2, hr = (i >> 1) & 1;
+                uint8_t* rq = lds + QT + 28 * 1024 + ((2 * m) * 64 + h + 32 * hr) * 16 + 8 * (i & 1);
+                *reinterpret_cast<uint2*>(rq) = make_uint2(hb[0] | (hb[1] << 16), hb[2] | (hb[3] << 16));
+                *reinterpret_cast<uint2*>(rq + 64 * 16) =
+                    make_uint2(lb[0] | (lb[1] << 16), lb[2] | (lb[3] << 16));
+            }
             if constexpr (LO8) {
                 float lmax = 0.0f;
 #pragma unroll
-                for (int s = 0; s < 9; ++s)
+                for (int s = 0; s < NQF - (MXL ? 1 : 0); ++s)
 #pragma unroll
                     for (int c = 0; c < 4; ++c)
                         lmax = fmaxf(lmax, fabsf((float)lot[s][c]));
@@ -351,7 +392,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_partial32(AttnArgs a)
                 if (i == 0)
                     s_k[HG + h] = j;
 #pragma unroll
-                for (int s = 0; s < 9; ++s) {
+                for (int s = 0; s < NQF - (MXL ? 1 : 0); ++s) {
                     const int e = 4 * (i + 16 * s);
                     const int cb = e >> 6, off = e & 63, hf = (off >> 4) & 1;
                     const int b = 16 * (off >> 5) + (off & 15);
@@ -380,8 +421,11 @@ __global__ __launch_bounds__(kThreads, 1) void k_partial32(AttnArgs a)
     }
     lds_barrier();
     if (!ctx_wave) {
-        const int ks0 = LO8 ? 20 * kh : KH * kh;
-        const int nks = LO8 ? 20 - 4 * kh : KH;
+        // LO8: wave kh holds column blocks CB0 kh .. (dense rows 5 and 4,
+        // mixed rows 4 and 3 noPE blocks, then the RoPE part on kh = 1)
+        constexpr int CB0 = MXL ? 4 : 5;
+        const int ks0 = LO8 ? 4 * CB0 * kh : KH * kh;
+        const int nks = LO8 ? 4 * (CB0 - kh) : KH;
 #pragma unroll
         for (int m = 0; m < NQH; ++m)
             if (m < nks)
@@ -389,8 +433,15 @@ __global__ __launch_bounds__(kThreads, 1) void k_partial32(AttnArgs a)
         if constexpr (LO8) {
 #pragma unroll
             for (int c = 0; c < 5; ++c)
-                if (c < 5 - kh)
-                    ql8[c] = *reinterpret_cast<const v8i32*>(lds + QL8 + ((5 * kh + c) * 64 + lane) * 32);
+                if (c < CB0 - kh)
+                    ql8[c] = *reinterpret_cast<const v8i32*>(lds + QL8 + ((CB0 * kh + c) * 64 + lane) * 32);
+        }
+        if constexpr (MXL) {
+            if (kh == 1) {
+#pragma unroll
+                for (int m = 0; m < 8; ++m)
+                    qr[m] = *reinterpret_cast<const bf16x8*>(lds + QT + 28 * 1024 + (m * 64 + lane) * 16);
+            }
         }
     }
     lds_barrier();  // LO8: staging areas free for the ring and the weights
@@ -486,6 +537,10 @@ __global__ __launch_bounds__(kThreads, 1) void k_partial32(AttnArgs a)
             const int hd = lane & 31;              // the lane's head (score column)
             const int hsel = hd >> 4;              // state of head n (0) or 16 + n (1)
             const float pk = ldexpf(1.0f, -s_k[hd]);  // the accumulators hold 2^k scores
+            // u as weighed: 2^k times the score (dense rows), or the score
+            // itself (mixed rows: the RoPE part carries neither 2^k nor the
+            // row scale, so each wave's part is scaled before the exchange)
+            const float upk = MXL ? 1.0f : pk;
             const int sb_lo = 127 - s_k[HG + hd];         // LO8: E8M0 scale 2^-j of the lo term
             // After the exchange the lane holds head hd, rows rb0 + (0..3) and
             // rb0 + 8 + (0..3) of the wave's 32 (values 8 kh .. +8 of the
@@ -501,7 +556,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_partial32(AttnArgs a)
             // hb (slot hf + 2 (hb & 1) of column block hb / 2) at + 512 hb.
             const int rowq = 32 * rh + (lane & 31);
             const int a_off = (rowq >> 4) * (NCB * 1024) + ((rowq & 15) + 16 * hf) * 16 +
-                              (LO8 ? 1024 * 5 * KHC : 512 * (KH / 2) * KHC);
+                              (LO8 ? 1024 * (MXL ? 4 : 5) * KHC : 512 * (KH / 2) * KHC);
             // exchange: value 8 kh' + 4 j + c of wave (rh, kh) goes to wave
             // (rh, kh') as float4 j at [parity][rh][kh'][j][lane]
             auto xc_ptr = [&](int par, int dst) __attribute__((always_inline)) -> float4* {
@@ -528,7 +583,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_partial32(AttnArgs a)
                 float u[8];
 #pragma unroll
                 for (int v = 0; v < 8; ++v)
-                    u[v] = (accp[v] + yv[v]) * scv[v];
+                    u[v] = MXL ? accp[v] + yv[v] : (accp[v] + yv[v]) * scv[v];
                 if constexpr (GATHER) {
                     // -inf for list entries outside [0, t_rows): bit row of
                     // the tile's validity mask
@@ -562,7 +617,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_partial32(AttnArgs a)
                     f16x4 wv;
 #pragma unroll
                     for (int v = 0; v < 4; ++v) {
-                        const float pv = fast_exp2(fmaf(u[4 * r + v], pk, nmz));
+                        const float pv = fast_exp2(fmaf(u[4 * r + v], upk, nmz));
                         const float wt = pv * (scv[4 * r + v] * fown);
                         ps += pv;
                         ws += wt;
@@ -601,7 +656,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_partial32(AttnArgs a)
             // column block widened once, then its two K steps times the hi and
             // lo query terms; with WW, the weights of tile p-1 are computed
             // among them (independent work that fills the MFMA shadow).
-            auto stream = [&](int st, auto WW_, int t, int buf)
+            auto stream = [&](int st, int ts, auto WW_, int t, int buf)
                               __attribute__((always_inline)) -> bool {
                 constexpr bool WW = decltype(WW_)::value;
                 bool ok = true;
@@ -613,7 +668,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_partial32(AttnArgs a)
                     // column block c of the wave: both halves (32 row bytes
                     // per lane) feed the e4m3 MFMA as they are and, widened,
                     // the four hi K steps
-                    constexpr int NC = KHC ? 4 : 5;
+                    constexpr int NC = MXL ? (KHC ? 3 : 4) : (KHC ? 4 : 5);
                     // the lo products in an accumulator of their own, added
                     // to the hi sum once at the end
                     f32x16 acc_lo;
@@ -647,6 +702,34 @@ __global__ __launch_bounds__(kThreads, 1) void k_partial32(AttnArgs a)
 #pragma unroll
                     for (int v = 0; v < 16; ++v)
                         acc[v] += acc_lo[v];
+                    if constexpr (MXL) {
+                        // this wave's part of the score of value v (row 8 (v /
+                        // 4) + 4 hf + v % 4 of the wave's 32): 2^-k scale acc,
+                        // with tile ts's row scales
+                        const float* scp = s_sc + (ts & (NSC - 1)) * TR + 32 * rh + 4 * hf;
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) {
+                            const float4 sq = *reinterpret_cast<const float4*>(scp + 8 * q);
+                            const float sv[4] = {sq.x, sq.y, sq.z, sq.w};
+#pragma unroll
+                            for (int c = 0; c < 4; ++c)
+                                acc[4 * q + c] = (acc[4 * q + c] * pk) * sv[c];
+                        }
+                    }
+                    if constexpr (MXL && KHC == 1) {
+                        // + the RoPE part (in score units already): blocks 7
+                        // and 8 (the wave's blocks 3 and 4), two 16-element K
+                        // steps each, bf16 as stored, hi and lo terms
+#pragma unroll
+                        for (int bb = 0; bb < 2; ++bb) {
+                            const bf16x8 r0 = *reinterpret_cast<const bf16x8*>(xs + 1024 * (3 + bb));
+                            const bf16x8 r1 = *reinterpret_cast<const bf16x8*>(xs + 1024 * (3 + bb) + 512);
+                            acc = mfma32_bf16(r0, qr[4 * bb + 0], acc);
+                            acc = mfma32_bf16(r0, qr[4 * bb + 1], acc);
+                            acc = mfma32_bf16(r1, qr[4 * bb + 2], acc);
+                            acc = mfma32_bf16(r1, qr[4 * bb + 3], acc);
+                        }
+                    }
                 } else {
                     constexpr int NH = KH / 2;  // 9 half column blocks
                     constexpr int PF = 2;
@@ -694,8 +777,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_partial32(AttnArgs a)
                     // u and row scales of tile p-2 (stored by its weigh);
                     // unscaled scores: pk is a power of 2
                     const float4 u0 = s_uv[0], u1 = s_uv[64], sc0 = s_uv[128], sc1 = s_uv[192];
-                    const float u[8] = {u0.x * pk, u0.y * pk, u0.z * pk, u0.w * pk,
-                                        u1.x * pk, u1.y * pk, u1.z * pk, u1.w * pk};
+                    const float u[8] = {u0.x * upk, u0.y * upk, u0.z * upk, u0.w * upk,
+                                        u1.x * upk, u1.y * upk, u1.z * upk, u1.w * upk};
                     const float scv[8] = {sc0.x, sc0.y, sc0.z, sc0.w, sc1.x, sc1.y, sc1.z, sc1.w};
                     // exact maxima of tile p-2 (u, scv) for this lane's row
                     // quarter: T = max u, C = max (u - T) + log2 scale
@@ -725,9 +808,9 @@ __global__ __launch_bounds__(kThreads, 1) void k_partial32(AttnArgs a)
                 const bool scored = p < ntiles, weighed = p >= 1 && p <= ntiles;
                 bool ok = true;
                 if (scored && weighed)
-                    ok = stream(st, std::true_type{}, p - 1, bw);
+                    ok = stream(st, p, std::true_type{}, p - 1, bw);
                 else if (scored)
-                    stream(st, std::false_type{}, 0, 0);
+                    stream(st, p, std::false_type{}, 0, 0);
                 else if (weighed)
                     ok = weigh(p - 1, bw, std::true_type{});
                 if (weighed) {
@@ -761,6 +844,9 @@ __global__ __launch_bounds__(kThreads, 1) void k_partial32(AttnArgs a)
         // of tile p-2; column block jb = 32 columns, K step ks = 16 rows.
         const int c = wi;
         const int g = lane >> 4;
+        // 32-column blocks of this wave (mixed rows: 448 columns, so the last
+        // wave has 2)
+        const int njb = (MXL && c == 3) ? 2 : 4;
         if (fresh_late)
             quantize_fresh(wi, 4);
         f32x16 O[4];
@@ -790,6 +876,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_partial32(AttnArgs a)
             for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
                 for (int jb = 0; jb < 4; ++jb) {
+                    if (jb >= njb)
+                        continue;
                     const int cb = 2 * c + (jb >> 1);
                     const int off = (ks * NCB + cb) * 1024 + 32 * (jb & 1) * 16;
                     xb[ks][jb] = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
@@ -801,8 +889,9 @@ __global__ __launch_bounds__(kThreads, 1) void k_partial32(AttnArgs a)
             for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
                 for (int jb = 0; jb < 4; ++jb)
-                    O[jb] = mfma32(wa[ks], cvt8((uint32_t)xb[ks][jb][0], (uint32_t)xb[ks][jb][1]),
-                                   O[jb]);
+                    if (jb < njb)
+                        O[jb] = mfma32(wa[ks], cvt8((uint32_t)xb[ks][jb][0], (uint32_t)xb[ks][jb][1]),
+                                       O[jb]);
         };
 
         // Phase p: the context of tile p-2 (its weights from buffer p & 1,
@@ -881,10 +970,11 @@ __global__ __launch_bounds__(kThreads, 1) void k_partial32(AttnArgs a)
             if (qh < a.n_qh) {
                 // streaming stores: the merge reads the partials once, from
                 // beyond L2 (another XCD's workgroups wrote most of them)
-                float* dst = a.ws_cl + (pbase + qh) * LC + 128 * c + (lane & 31);
+                float* dst = a.ws_cl + (pbase + qh) * LCO + 128 * c + (lane & 31);
 #pragma unroll
                 for (int jb = 0; jb < 4; ++jb)
-                    __builtin_nontemporal_store(O[jb][v] * f, dst + 32 * jb);
+                    if (jb < njb)
+                        __builtin_nontemporal_store(O[jb][v] * f, dst + 32 * jb);
             }
         }
     }
@@ -902,7 +992,11 @@ __global__ __launch_bounds__(kThreads, 1) void k_partial32(AttnArgs a)
 
 bool partial32_applies(const AttnArgs& a)
 {
-    if (a.layout != kE4m3 || a.lc != p32::LC || a.rc != p32::RC || a.n_list < p32::TR)
+    const bool e4 = a.layout == kE4m3 && a.lc == p32::LC && a.rc == p32::RC;
+    // mixed rows (448 e4m3 + 64 bf16) only with the e4m3 lo term; their
+    // f32-grade path is the general kernel's
+    const bool mx = a.layout == kMixed && a.lc == 448 && a.rc == p32::RC && a.lo8;
+    if (!(e4 || mx) || a.n_list < p32::TR)
         return false;
     if (a.mode == kDense || a.mode == kSelect)
         return true;
@@ -911,18 +1005,32 @@ bool partial32_applies(const AttnArgs& a)
     return a.mode == kCausal && a.n_heads % kHeadsPerGroup == 0 && a.pos0 + 1 >= p32::TR;
 }
 
-void launch_partial32(const AttnArgs& a, hipStream_t stream)
+template <bool LO8, bool GATHER, bool MXL>
+static void launch32(const AttnArgs& a, hipStream_t stream)
 {
     const dim3 grid((unsigned)(a.n_chunks * a.n_groups));
+    hipLaunchKernelGGL((k_partial32<LO8, GATHER, MXL>), grid, dim3(kThreads), 0, stream, a);
+}
+
+void launch_partial32(const AttnArgs& a, hipStream_t stream)
+{
     const bool g = a.mode == kSelect;
-    if (a.lo8 && g)
-        hipLaunchKernelGGL((k_partial32<true, true>), grid, dim3(kThreads), 0, stream, a);
-    else if (a.lo8)
-        hipLaunchKernelGGL((k_partial32<true, false>), grid, dim3(kThreads), 0, stream, a);
-    else if (g)
-        hipLaunchKernelGGL((k_partial32<false, true>), grid, dim3(kThreads), 0, stream, a);
-    else
-        hipLaunchKernelGGL((k_partial32<false, false>), grid, dim3(kThreads), 0, stream, a);
+    if (a.layout == kMixed) {
+        if (g)
+            launch32<true, true, true>(a, stream);
+        else
+            launch32<true, false, true>(a, stream);
+    } else if (a.lo8) {
+        if (g)
+            launch32<true, true, false>(a, stream);
+        else
+            launch32<true, false, false>(a, stream);
+    } else {
+        if (g)
+            launch32<false, true, false>(a, stream);
+        else
+            launch32<false, false, false>(a, stream);
+    }
 }
 
 }  // namespace mla8

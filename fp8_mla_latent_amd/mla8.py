@@ -336,10 +336,11 @@ def mla8_decode(kv_codes, kv_scales, t_rows: int, lc: int, rc: int, q_lat, q_rop
 
 def mla8_decode_mx(kv_rows, kv_scales, t_rows: int, lc: int, rc: int, q_lat, q_rope,
                    sm_scale: float, out=None, lse=None, workspace=None, want_lse: bool = True,
-                   n_splits: int = 0, events=None):
+                   n_splits: int = 0, events=None, f32_scores: bool = False):
     """Dense decode over mixed rows [0, t_rows): (out [H, lc], lse [H] or None)."""
     return _decode_call("mla8_decode_mx", lc + 2 * rc, kv_rows, kv_scales, t_rows, lc, rc,
-                        q_lat, q_rope, sm_scale, out, lse, workspace, want_lse, n_splits, events)
+                        q_lat, q_rope, sm_scale, out, lse, workspace, want_lse, n_splits, events,
+                        f32_scores)
 
 
 def mla8_append_decode(kv_codes, kv_scales, t_rows: int, x_new, lc: int, rc: int, q_lat, q_rope,
@@ -394,10 +395,11 @@ def mla8_append_decode_noalloc(kv_codes, kv_scales, t_rows: int, x_new, lc: int,
 
 def mla8_append_decode_mx(kv_rows, kv_scales, t_rows: int, x_new, lc: int, rc: int, q_lat,
                           q_rope, sm_scale: float, out=None, lse=None, workspace=None,
-                          want_lse: bool = True, n_splits: int = 0, events=None):
+                          want_lse: bool = True, n_splits: int = 0, events=None,
+                          f32_scores: bool = False):
     """As mla8_append_decode over mixed rows (kv_rows [cap, lc + 2 rc])."""
     return mla8_append_decode(kv_rows, kv_scales, t_rows, x_new, lc, rc, q_lat, q_rope, sm_scale,
-                              out, lse, workspace, want_lse, n_splits, events,
+                              out, lse, workspace, want_lse, n_splits, events, f32_scores,
                               _fn="mla8_append_decode_mx")
 
 
@@ -433,10 +435,12 @@ def mla8_decode_sel(kv_codes, kv_scales, t_rows: int, lc: int, rc: int, sel, q_l
 
 def mla8_decode_sel_mx(kv_rows, kv_scales, t_rows: int, lc: int, rc: int, sel, q_lat, q_rope,
                        sm_scale: float, out=None, lse=None, workspace=None,
-                       want_lse: bool = True, n_splits: int = 0, events=None):
+                       want_lse: bool = True, n_splits: int = 0, events=None,
+                       f32_scores: bool = False):
     """Decode over the selected mixed rows sel (int32 device tensor)."""
     return _sel_call("mla8_decode_sel_mx", lc + 2 * rc, kv_rows, kv_scales, t_rows, lc, rc, sel,
-                     q_lat, q_rope, sm_scale, out, lse, workspace, want_lse, n_splits, events)
+                     q_lat, q_rope, sm_scale, out, lse, workspace, want_lse, n_splits, events,
+                     f32_scores)
 
 
 def mla8_batch(kv_codes, kv_scales, t_rows: int, lc: int, rc: int, q_lat, q_rope, pos0: int,
@@ -463,10 +467,10 @@ def mla8_batch(kv_codes, kv_scales, t_rows: int, lc: int, rc: int, q_lat, q_rope
 
 def mla8_batch_mx(kv_rows, kv_scales, t_rows: int, lc: int, rc: int, q_lat, q_rope, pos0: int,
                   sm_scale: float, out=None, lse=None, workspace=None, want_lse: bool = True,
-                  n_splits: int = 0, events=None):
+                  n_splits: int = 0, events=None, f32_scores: bool = False):
     """As mla8_batch over mixed rows."""
     return mla8_batch(kv_rows, kv_scales, t_rows, lc, rc, q_lat, q_rope, pos0, sm_scale, out, lse,
-                      workspace, want_lse, n_splits, events, _fn="mla8_batch_mx")
+                      workspace, want_lse, n_splits, events, f32_scores, _fn="mla8_batch_mx")
 
 
 # ---------------------------------------------------------------------------

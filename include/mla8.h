@@ -94,10 +94,15 @@ enum { MLA8_OP_DECODE = 0, MLA8_OP_DECODE_SEL = 1, MLA8_OP_BATCH = 2, MLA8_OP_IN
  *              power-of-2 scale 2^j (largest |lo| 2^j in [128, 256)); the
  *              result is attention with the query (hi + e4m3(lo 2^j) 2^-j)
  *              2^-k / (sm_scale log2(e)) in place of q, which differs from q
- *              by about 2^-16 of its largest entry per head.  Every other call
- *              attends with q as given, scores of f32 grade.  1: scores of f32
- *              grade for those calls too (fp16 hi + lo terms on the fp16 MFMA,
- *              slower).
+ *              by about 2^-16 of its largest entry per head.  Mixed rows
+ *              (lc = 448, rc = 64; the *_mx calls under the same conditions):
+ *              the same for the noPE part, its 2^k and 2^j taken over the noPE
+ *              part alone; the RoPE part as the two bf16 terms hi =
+ *              bf16(q_rope sm_scale log2(e)), lo = bf16(that - hi), i.e. the
+ *              query (hi + lo) / (sm_scale log2(e)) in place of q_rope.  Every
+ *              other call attends with q as given, scores of f32 grade.  1:
+ *              scores of f32 grade for those calls too (fp16 hi + lo terms on
+ *              the fp16 MFMA, slower).
  */
 typedef struct mla8_opts {
     int32_t n_splits;

@@ -1,7 +1,13 @@
 """GPU parity of the mixed row layout (noPE e4m3 + per-row scale, RoPE bf16;
 the 512 / 448 / 64 shape of "B1 Mixed FP8/BF16 FMHA first pass") against the
 fp64 CPU oracle, through the C ABI: stored bytes bit-exact, attention within
-the per-vector tolerance of tests/tolerance.py.
+the tolerance of tests/tolerance.py.
+
+By default a call over at least 64 rows (or list entries; the causal batch
+with n_heads a multiple of 32 and pos0 >= 63) attends with the e4m3-lo-term
+query of oracle.query_lo8_mx, and is checked against the oracle run with that
+query; mla8_opts.f32_scores (and every shorter call) attends with the query
+as given.
 """
 from __future__ import annotations
 
@@ -53,6 +59,15 @@ def mixed_rows(t, seed, outliers=0.0):
     return x
 
 
+def reading(ql, qr, lo8=True):
+    """The query a call attends with: oracle.query_lo8_mx's when it takes the
+    e4m3-lo score path (lo8), else the query as given."""
+    if not lo8:
+        return ql, qr
+    a, b = oracle.query_lo8_mx(np.reshape(ql, (-1, LC)), np.reshape(qr, (-1, RC)), SM)
+    return a.reshape(np.shape(ql)), b.reshape(np.shape(qr))
+
+
 def queries(h, seed):
     g = np.random.Generator(np.random.PCG64(seed + 500))
     return (g.standard_normal((h, LC)).astype(np.float32),
@@ -84,12 +99,15 @@ def test_decode_mx_parity(m, t, h, outl, splits):
     scales = torch.zeros((t + 5,), dtype=torch.float32, device=DEV)
     assert m.mla8_append_mx(rows, scales, 0, dev(x), LC, RC) == t
     ql, qr = queries(h, t)
-    out, lse = m.mla8_decode_mx(rows, scales, t, LC, RC, dev(ql), dev(qr), SM, n_splits=splits)
-    torch.cuda.synchronize()
     orows, osc = oracle.quantize_rows_mx(x, LC, RC)
     np.testing.assert_array_equal(host(rows)[:t], orows)
-    ro, rl = oracle.decode_mx(orows, osc, t, LC, RC, ql, qr, SM)
-    check_attention(host(out), ro, host(lse), rl, f"mixed t={t} h={h}", outliers=outl > 0)
+    for f32 in (False, True):
+        out, lse = m.mla8_decode_mx(rows, scales, t, LC, RC, dev(ql), dev(qr), SM,
+                                    n_splits=splits, f32_scores=f32)
+        qa, qb = reading(ql, qr, lo8=t >= 64 and not f32)
+        ro, rl = oracle.decode_mx(orows, osc, t, LC, RC, qa, qb, SM)
+        check_attention(host(out), ro, host(lse), rl, f"mixed t={t} h={h} f32_scores={f32}",
+                        outliers=outl > 0)
 
 
 @pytest.mark.parametrize("qscale", [0.0, 1e-30, 1e-4, 1e4, 1e15])
@@ -103,7 +121,8 @@ def test_decode_mx_query_magnitudes(m, qscale):
     out, lse = m.mla8_decode_mx(rows, scales, t, LC, RC, dev(ql), dev(qr), SM)
     orows, osc = oracle.quantize_rows_mx(x, LC, RC)
     np.testing.assert_array_equal(host(rows), orows)
-    ro, rl = oracle.decode_mx(orows, osc, t, LC, RC, ql, qr, SM)
+    qa, qb = reading(ql, qr)
+    ro, rl = oracle.decode_mx(orows, osc, t, LC, RC, qa, qb, SM)
     check_attention(host(out), ro, host(lse), rl, f"mixed query scale {qscale}")
 
 
@@ -119,7 +138,8 @@ def test_decode_mx_rope_carries_the_scores(m):
     qr = queries(h, 5)[1] * np.float32(3.0)
     out, lse = m.mla8_decode_mx(rows, sc, t, LC, RC, dev(ql), dev(qr), SM)
     orows, osc = oracle.quantize_rows_mx(x, LC, RC)
-    ro, rl = oracle.decode_mx(orows, osc, t, LC, RC, ql, qr, SM)
+    qa, qb = reading(ql, qr)
+    ro, rl = oracle.decode_mx(orows, osc, t, LC, RC, qa, qb, SM)
     check_attention(host(out), ro, host(lse), rl, "mixed RoPE-only", outliers=True)
 
 
@@ -133,8 +153,9 @@ def test_decode_mx_long_sampled(m):
     ql, qr = queries(h, 99)
     out, lse = m.mla8_decode_mx(rows, sc, t, LC, RC, dev(ql), dev(qr), SM)
     hr, hs = host(rows), host(sc)
+    qa, qb = reading(ql, qr)
     for hh in (0, 41):
-        ro, rl = oracle.decode_mx(hr, hs, t, LC, RC, ql[hh:hh + 1], qr[hh:hh + 1], SM)
+        ro, rl = oracle.decode_mx(hr, hs, t, LC, RC, qa[hh:hh + 1], qb[hh:hh + 1], SM)
         check_attention(host(out)[hh:hh + 1], ro, host(lse)[hh:hh + 1], rl, f"long head {hh}")
 
 
@@ -172,9 +193,13 @@ def test_decode_sel_mx_parity(m, case):
         sel_d, _ = m.mla8_index_topk(kc, ks, qi, wi, 2048)
         sel = host(sel_d)
     ql, qr = queries(h, 31)
-    out, lse = m.mla8_decode_sel_mx(rows, sc, t, LC, RC, dev(sel), dev(ql), dev(qr), SM)
-    ro, rl = oracle.decode_sel_mx(host(rows), host(sc), t, LC, RC, sel, ql, qr, SM)
-    check_attention(host(out), ro, host(lse), rl, f"mixed gather {case}", outliers=True)
+    for f32 in (False, True):
+        out, lse = m.mla8_decode_sel_mx(rows, sc, t, LC, RC, dev(sel), dev(ql), dev(qr), SM,
+                                        f32_scores=f32)
+        qa, qb = reading(ql, qr, lo8=not f32)
+        ro, rl = oracle.decode_sel_mx(host(rows), host(sc), t, LC, RC, sel, qa, qb, SM)
+        check_attention(host(out), ro, host(lse), rl, f"mixed gather {case} f32_scores={f32}",
+                        outliers=True)
 
 
 def test_decode_mx_graph_replays_match_eager(m):
@@ -211,7 +236,8 @@ def test_decode_mx_graph_replays_match_eager(m):
         assert np.array_equal(host(out), ref_out), r
         assert np.array_equal(host(lse), ref_lse), r
         _ = (torch.ones(1000, device=DEV) * 2).sum().item()  # eager work between replays
-    ro, rl = oracle.decode_mx(host(rows), host(sc), t, LC, RC, ql, qr, SM)
+    qa, qb = reading(ql, qr)
+    ro, rl = oracle.decode_mx(host(rows), host(sc), t, LC, RC, qa, qb, SM)
     check_attention(ref_out, ro, ref_lse, rl, "mixed graph replay", outliers=True)
 
 
@@ -234,7 +260,8 @@ def test_append_decode_mx_parity(m, t0, n_new):
     np.testing.assert_array_equal(host(rows)[:t1], orows)
     np.testing.assert_array_equal(host(scales)[:t1].view(np.uint32), osc.view(np.uint32))
     assert not host(rows)[t1:].any()
-    ro, rl = oracle.decode_mx(orows, osc, t1, LC, RC, ql, qr, SM)
+    qa, qb = reading(ql, qr)
+    ro, rl = oracle.decode_mx(orows, osc, t1, LC, RC, qa, qb, SM)
     check_attention(host(out), ro, host(lse), rl, f"mixed append_decode t0={t0}", outliers=True)
 
 
@@ -278,11 +305,13 @@ def test_append_decode_mx_graph_replays_match_eager(m):
         _ = (torch.ones(1000, device=DEV) * 2).sum().item()
     orows, osc = oracle.quantize_rows_mx(x, LC, RC)
     np.testing.assert_array_equal(host(rows), orows)
-    ro, rl = oracle.decode_mx(orows, osc, t, LC, RC, ql, qr, SM)
+    qa, qb = reading(ql, qr)
+    ro, rl = oracle.decode_mx(orows, osc, t, LC, RC, qa, qb, SM)
     check_attention(ref_out, ro, ref_lse, rl, "mixed append_decode graph", outliers=True)
 
 
-@pytest.mark.parametrize("t,n_q,h", [(3000, 16, 16), (700, 64, 8)])
+@pytest.mark.parametrize("t,n_q,h", [(3000, 16, 16), (700, 64, 8), (2000, 12, 64),
+                                     (140, 80, 32)])
 def test_batch_mx_parity(m, t, n_q, h):
     # query s at position pos0 + s attends rows 0 .. pos0 + s: the selected-row
     # oracle over exactly those rows
@@ -296,7 +325,9 @@ def test_batch_mx_parity(m, t, n_q, h):
     out, lse = m.mla8_batch_mx(rows, sc, t, LC, RC, dev(ql), dev(qr), pos0, SM)
     hr, hs = host(rows), host(sc)
     go, gl = host(out), host(lse)
+    # heads a multiple of 32 and pos0 >= 63: the e4m3-lo score path
+    qa, qb = reading(ql, qr, lo8=h % 32 == 0 and pos0 >= 63)
     for sidx in range(n_q):
         sel = np.arange(pos0 + sidx + 1, dtype=np.int32)
-        ro, rl = oracle.decode_sel_mx(hr, hs, t, LC, RC, sel, ql[sidx], qr[sidx], SM)
+        ro, rl = oracle.decode_sel_mx(hr, hs, t, LC, RC, sel, qa[sidx], qb[sidx], SM)
         check_attention(go[sidx], ro, gl[sidx], rl, f"mixed batch query {sidx}", outliers=True)
