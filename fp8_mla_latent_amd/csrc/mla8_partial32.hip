@@ -293,12 +293,15 @@ __global__ __launch_bounds__(kThreads, 1) void k_partial32(AttnArgs a)
         if (ntiles > 1)
             issue(1, 1, IC0{}, ICK{});
     }
-    // A chunk of a few tiles (gathers, short lists) meets only a light load
-    // burst: there the context waves wait for their loads and build too, one
-    // work item per thread (t = tid), which halves the build.  (Not without
-    // LO8: the fp16 lo term it keeps for its own staging round would not fit
-    // beside the context waves' registers.)
-    const bool all_build = LO8 && ntiles <= 4;
+    // With LO8 the context waves build too, one work item per thread (t =
+    // tid), which halves the build: their query loads are waited for
+    // together with their first tiles' loads (the compiler's waits do not
+    // see the direct loads), which still ends before the score waves would
+    // have built two items each (measured at T = 262144: 64.1 against 64.5
+    // us per layer-token; and on short chunks, whose load burst is light).
+    // Not without LO8: the fp16 lo term kept for its own staging round would
+    // not fit beside the context waves' registers.
+    constexpr bool all_build = LO8;
     f16x4 lo4[LO8 ? 1 : 2][9];  // without LO8: the lo term until its staging round
     // NIT work items t = tid + 256 it: all loads first, then the builds
     auto build = [&](auto NIT_) __attribute__((always_inline)) {
