@@ -209,3 +209,82 @@ def test_lo_term_encoder_matches_the_oracle(m):
     ref = oracle.enc(x)
     bad = np.flatnonzero(got != ref)
     assert bad.size == 0, (int(bad.size), float(x[bad[0]]), int(got[bad[0]]), int(ref[bad[0]]))
+
+
+def test_f32_scores_switches_the_mixed_path(m):
+    """On mixed rows (448/64) the option selects the other kernel: the default
+    attends with query_lo8_mx's query, f32_scores with the query as given, so
+    the two results differ (and each matches its own reference elsewhere)."""
+    lc, rc, sm = 448, 64, 1.0 / math.sqrt(192.0)
+    t, h = 3000, 64
+    say("f32_scores on mixed rows")
+    g = np.random.Generator(np.random.PCG64(71))
+    x = g.standard_normal((t, lc + rc)).astype(np.float32)
+    ql = g.standard_normal((h, lc)).astype(np.float32)
+    qr = g.standard_normal((h, rc)).astype(np.float32)
+    rows, sc = m.mla8_quantize_rows_mx(dev(x), lc, rc)
+    a, _ = m.mla8_decode_mx(rows, sc, t, lc, rc, dev(ql), dev(qr), sm)
+    b, _ = m.mla8_decode_mx(rows, sc, t, lc, rc, dev(ql), dev(qr), sm, f32_scores=True)
+    assert not np.array_equal(host(a), host(b))
+
+
+@pytest.mark.parametrize("mode", ["sel", "batch", "sel_mx"])
+def test_graph_replays_of_the_gather_and_batch_paths(m, mode):
+    """The gathered, causal and mixed gathered calls on the 32x32 kernel
+    captured once and replayed, with eager work between replays: every replay
+    equals the eager result bit for bit."""
+    say(f"graph replay: {mode}")
+    g = np.random.Generator(np.random.PCG64(81))
+    sm = 1.0 / math.sqrt(192.0)
+    if mode == "sel_mx":
+        lc, rc, t, h = 448, 64, 6000, 64
+        x = g.standard_normal((t, lc + rc)).astype(np.float32)
+        codes, sc = m.mla8_quantize_rows_mx(dev(x), lc, rc)
+    else:
+        lc, rc, t, h = 512, 64, 6000, 64
+        x = g.standard_normal((t, lc + rc)).astype(np.float32)
+        codes, sc = m.mla8_quantize_rows(dev(x), lc, rc)
+    sel = dev(np.sort(g.choice(t, 700, replace=False)).astype(np.int32))
+    n_q = 4
+    if mode == "batch":
+        ql = dev(g.standard_normal((n_q, h, lc)).astype(np.float32))
+        qr = dev(g.standard_normal((n_q, h, rc)).astype(np.float32))
+        out = torch.empty((n_q, h, lc), dtype=torch.float32, device=DEV)
+        lse = torch.empty((n_q, h), dtype=torch.float32, device=DEV)
+        ws = torch.empty(m.mla8_workspace_bytes(m.MLA8_OP_BATCH, t, h, n_q, lc), dtype=torch.uint8,
+                         device=DEV)
+    else:
+        ql = dev(g.standard_normal((h, lc)).astype(np.float32))
+        qr = dev(g.standard_normal((h, rc)).astype(np.float32))
+        out = torch.empty((h, lc), dtype=torch.float32, device=DEV)
+        lse = torch.empty((h,), dtype=torch.float32, device=DEV)
+        ws = torch.empty(m.mla8_workspace_bytes(m.MLA8_OP_DECODE_SEL, 700, h, 1, lc),
+                         dtype=torch.uint8, device=DEV)
+
+    def call():
+        if mode == "sel":
+            m.mla8_decode_sel(codes, sc, t, lc, rc, sel, ql, qr, sm, out=out, lse=lse, workspace=ws)
+        elif mode == "sel_mx":
+            m.mla8_decode_sel_mx(codes, sc, t, lc, rc, sel, ql, qr, sm, out=out, lse=lse,
+                                 workspace=ws)
+        else:
+            m.mla8_batch(codes, sc, t, lc, rc, ql, qr, t - n_q, sm, out=out, lse=lse, workspace=ws)
+
+    call()
+    ref_out, ref_lse = host(out).copy(), host(lse).copy()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        call()
+    torch.cuda.current_stream().wait_stream(s)
+    gr = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(gr):
+        call()
+    for r in range(4):
+        out.zero_()
+        lse.zero_()
+        gr.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(host(out), ref_out), r
+        assert np.array_equal(host(lse), ref_lse), r
+        _ = (torch.ones(1000, device=DEV) * 2).sum().item()  # eager work between replays
