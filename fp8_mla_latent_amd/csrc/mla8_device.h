@@ -56,6 +56,48 @@ __device__ __forceinline__ uint32_t enc_e4m3_pk4(float y0, float y1, float y2, f
     return (uint32_t)w;
 }
 
+// Two f32 -> fp16, round to nearest even (v_cvt_pk_f16_f32): a in the low
+// half, b in the high half.
+__device__ __forceinline__ uint32_t pk_f16(float a, float b)
+{
+    typedef float f2 __attribute__((ext_vector_type(2)));
+    typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f2){a, b}, h2));
+}
+
+// r - f32(h), h the fp16 in the low (H = 0) or high (H = 1) half of x, in one
+// v_fma_mix_f32 (the fp16 operand widened exactly, one rounding of the result).
+template <int H>
+__device__ __forceinline__ float sub_f16(float r, uint32_t x)
+{
+    float d;
+    if constexpr (H == 0)
+        asm("v_fma_mix_f32 %0, %1, -1.0, %2 op_sel_hi:[1,0,0]" : "=v"(d) : "v"(x), "v"(r));
+    else
+        asm("v_fma_mix_f32 %0, %1, -1.0, %2 op_sel:[1,0,0] op_sel_hi:[1,0,0]" : "=v"(d) : "v"(x), "v"(r));
+    return d;
+}
+
+// f32(h) * m, h the fp16 in the low (H = 0) or high (H = 1) half of x: an
+// fma with +0 (so that it stays one v_fma_mix_f32; exact for m a power of 2
+// and a product in f32's normal range).
+template <int H>
+__device__ __forceinline__ float mul_f16(uint32_t x, float m)
+{
+    typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+    const h2 h = __builtin_bit_cast(h2, x);
+    return __builtin_fmaf((float)h[H], m, 0.0f);
+}
+
+// max(a, |x|, |y|) in one v_max3_f32 (no canonicalising of the operands; a
+// NaN operand gives the other operands' maximum or a NaN).
+__device__ __forceinline__ float max3_abs(float a, float x, float y)
+{
+    float d;
+    asm("v_max3_f32 %0, %1, |%2|, |%3|" : "=v"(d) : "v"(a), "v"(x), "v"(y));
+    return d;
+}
+
 // Maximum over the 16 lanes of each row (DPP: quad swaps, then half-row and
 // row mirrors), and over the whole wave (permlane swaps across rows).
 __device__ __forceinline__ float row16_max(float x)

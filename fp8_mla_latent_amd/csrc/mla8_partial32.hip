@@ -61,6 +61,7 @@ constexpr int NINS = STAGE / 1024;       // 36 row DMA instructions per tile
 constexpr int KW = NINS / 4;             // 9 per context wave
 // LDS map (bytes)
 constexpr int NSC = 4;                   // row-scale slots: tile t in slot t % 4
+constexpr int kSplitTiles = 2;           // chunks this short: every wave builds the query
 constexpr int SC = NST * STAGE;          // f32 [NSC][TR] row scales
 constexpr int W = SC + NSC * TR * 4;     // f16 [2][HG][WSTR] weights
 constexpr int XC = W + 2 * HG * WSTR * 2;  // f32x4 [2][2 rh][2 kh][2][64] partial scores
@@ -170,7 +171,20 @@ __global__ __launch_bounds__(kThreads, 1) void k_partial32(AttnArgs a)
         return (uint32_t)(64 * (k + 135 * (k / NCB)));
     };
     int32_t g_row[GATHER ? 4 : 1];  // gather: rows of the tile being issued, per row block
-    auto issue = [&](int t, int st, auto I0_, auto I1_) __attribute__((always_inline)) {
+    int32_t g_sc = 0;               // gather, wave 4: list entry p0 + lane (its row scale)
+    // gather: list entries p0 .. p0 + 63 of tile t are absolute row indices;
+    // one outside [0, t_rows) loads row 0 and gets no weight
+    auto load_rows = [&](int t, int32_t (&g)[GATHER ? 4 : 1], int32_t& gs)
+                         __attribute__((always_inline)) {
+        const int p0 = min(c0 + t * TR, c1 - TR);
+#pragma unroll
+        for (int rb = 0; rb < 4; ++rb)
+            g[rb] = a.sel[p0 + 16 * rb + (lane & 15)];
+        gs = a.sel[p0 + lane];  // used by wave 4 only; unconditional, no branch
+    };
+    // have_rows: the tile's list entries are already in g_row and g_sc
+    auto issue = [&](int t, int st, auto I0_, auto I1_, bool have_rows = false)
+                     __attribute__((always_inline)) {
         constexpr int I0 = decltype(I0_)::value, I1 = decltype(I1_)::value;
         const uint32_t xst = lds_u32 + (uint32_t)(st * STAGE);
         // tile t's scales are read until phase t + 1 (its weights), past the
@@ -187,25 +201,22 @@ __global__ __launch_bounds__(kThreads, 1) void k_partial32(AttnArgs a)
             if (I1 == KW && dma_lead)
                 dma_b32_s(a.scales + p0, (uint32_t)(4 * lane), sct);
         } else {
-            // list entries p0 .. p0 + 63 are absolute row indices; one outside
-            // [0, t_rows) loads row 0 and gets no weight.  The indices of the
-            // tile's four row blocks are loaded with the first part.
+            // the list entries are loaded with the first part
             if constexpr (I0 == 0) {
-#pragma unroll
-                for (int rb = 0; rb < 4; ++rb) {
-                    const int32_t r = a.sel[p0 + 16 * rb + (lane & 15)];
-                    g_row[rb] = (r >= 0 && r < a.t_rows) ? r : 0;
-                }
+                if (!have_rows)
+                    load_rows(t, g_row, g_sc);
             }
 #pragma unroll
             for (int i = I0; i < I1; ++i) {
                 const int k = blk_k(i);
                 const int rb = k / NCB, cb = k - NCB * rb;
-                dma_b128(a.codes + (size_t)g_row[rb] * D + 64 * cb + 16 * (lane >> 4),
+                const int32_t r = g_row[rb];
+                const int32_t row = (r >= 0 && r < a.t_rows) ? r : 0;
+                dma_b128(a.codes + (size_t)row * D + 64 * cb + 16 * (lane >> 4),
                          xst + (uint32_t)(1024 * k));
             }
             if (I1 == KW && dma_lead) {
-                const int32_t r = a.sel[p0 + lane];
+                const int32_t r = g_sc;
                 const bool ok = r >= 0 && r < a.t_rows;
                 dma_b32(a.scales + (ok ? r : 0), sct);
                 const uint64_t valid = __ballot(ok);
@@ -264,8 +275,10 @@ __global__ __launch_bounds__(kThreads, 1) void k_partial32(AttnArgs a)
     // ---- prologue: query operands, built by the score waves while the
     // context waves issue the first DIST tiles' loads (a wave with those in
     // flight could not wait for query loads of its own without waiting for
-    // them too).  Work item t (two per score-wave thread: t = tid and tid +
-    // 256) loads the nine float4 of head t / 16 at elements 4 (t % 16 + 16
+    // them too).  The score waves' query loads go out first: a barrier holds
+    // the row loads back until they are issued, so that they do not queue
+    // behind the 73 KB of row loads in the CU's memory path.  Work item t
+    // (two per score-wave thread: t = tid and tid + 256) loads the nine float4 of head t / 16 at elements 4 (t % 16 + 16
     // s), s < 9; the head's e = q * sm_scale * log2(e) is scaled by 2^k
     // (largest |e| in [2^14, 2^15)) and split into fp16 hi + lo (the
     // subtraction is exact in f32).  hi is staged in the score waves' B
@@ -287,78 +300,69 @@ __global__ __launch_bounds__(kThreads, 1) void k_partial32(AttnArgs a)
     bf16x8 qr[MXL ? 8 : 1];  // mixed rows, kh = 1: RoPE terms [K step m][hi, lo]
     constexpr int QL8 = W;  // LO8: staging of the e4m3 lo term
     static_assert(QL8 + NCB * 64 * 32 <= FL, "the lo term fits the weight and exchange buffers");
-    if (ctx_wave) {
-        if (ntiles > 0)
-            issue(0, 0, IC0{}, ICK{});
-        if (ntiles > 1)
-            issue(1, 1, IC0{}, ICK{});
-    }
-    // With LO8 the context waves build too, one work item per thread (t =
-    // tid), which halves the build: their query loads are waited for
-    // together with their first tiles' loads (the compiler's waits do not
-    // see the direct loads), which still ends before the score waves would
-    // have built two items each (measured at T = 262144: 64.1 against 64.5
-    // us per layer-token; and on short chunks, whose load burst is light).
-    // Not without LO8: the fp16 lo term kept for its own staging round would
-    // not fit beside the context waves' registers.
-    constexpr bool all_build = LO8;
     f16x4 lo4[LO8 ? 1 : 2][9];  // without LO8: the lo term until its staging round
-    // NIT work items t = tid + 256 it: all loads first, then the builds
-    auto build = [&](auto NIT_) __attribute__((always_inline)) {
-        constexpr int NIT = decltype(NIT_)::value;
-        float4 v[NIT][NQF];
+    float4 vq[2][NQF];
+    // A head beyond n_qh (a partial last group) takes the last head's query:
+    // its results are never stored, and the loads stay unconditional.
+    auto load_q = [&](auto NIT_) __attribute__((always_inline)) {
 #pragma unroll
-        for (int it = 0; it < NIT; ++it) {
+        for (int it = 0; it < decltype(NIT_)::value; ++it) {
             const int t = tid + 256 * it, h = t >> 4, i = t & 15;
-            const int qh = qh0 + h;
-            const bool hv = qh < a.n_qh;
+            const size_t qh = (size_t)min(qh0 + h, a.n_qh - 1);
+            const float* const ql = a.q_lat + qh * LCO + 4 * i;
+            const float* const qr = a.q_rope + qh * RC + 4 * i;
 #pragma unroll
             for (int s = 0; s < NQF; ++s) {
-                // elements 4 (i + 16 s): q_lat, then q_rope (mixed rows: the
-                // last float4 is RoPE elements 4 i ..)
-                const int e = 4 * (i + 16 * s);
-                const float* p = MXL ? (s < 7 ? a.q_lat + (size_t)(hv ? qh : 0) * LCO + e
-                                              : a.q_rope + (size_t)(hv ? qh : 0) * RC + 4 * i)
-                                     : ((e < LC) ? a.q_lat + (size_t)(hv ? qh : 0) * LC + e
-                                                 : a.q_rope + (size_t)(hv ? qh : 0) * RC + (e - LC));
-                const float4 x = *reinterpret_cast<const float4*>(p);
-                v[it][s] = hv ? x : make_float4(0.f, 0.f, 0.f, 0.f);
+                // elements 4 (i + 16 s): q_lat, then q_rope (s = 8; mixed
+                // rows: s = 7, RoPE elements 4 i ..)
+                const float* p = (s < NQF - 1) ? ql + 64 * s : qr;
+                vq[it][s] = *reinterpret_cast<const float4*>(p);
             }
         }
+    };
+    // The split, per element: r = f32(e 2^k); hi = fp16(r); lo = fp16(r -
+    // hi).  The largest |lo| of a head is the fp16 rounding of the largest
+    // |r - hi| (the rounding is monotonic), so it is taken before lo is
+    // rounded; lo 2^j is formed from the fp16 lo, as the encoder's input.
+    auto build_q = [&](auto NIT_) __attribute__((always_inline)) {
+        constexpr int NN = NQF - (MXL ? 1 : 0);  // float4 of the 2^k-scaled part
 #pragma unroll
-        for (int it = 0; it < NIT; ++it) {
+        for (int it = 0; it < decltype(NIT_)::value; ++it) {
             const int t = tid + 256 * it, h = t >> 4, i = t & 15;
             float amax = 0.0f;
 #pragma unroll
-            for (int s = 0; s < NQF - (MXL ? 1 : 0); ++s)
-                amax = fmaxf(amax, fmaxf(fmaxf(fabsf(v[it][s].x), fabsf(v[it][s].y)),
-                                         fmaxf(fabsf(v[it][s].z), fabsf(v[it][s].w))));
+            for (int s = 0; s < NN; ++s) {
+                amax = max3_abs(amax, vq[it][s].x, vq[it][s].y);
+                amax = max3_abs(amax, vq[it][s].z, vq[it][s].w);
+            }
             amax = row16_max(amax);
             const float es = a.sm_log2;
             const int k = query_exp(amax * es);
             if (i == 0)
                 s_k[h] = k;
             const float mult = ldexpf(es, k);
-            f16x4 lot[9];
+            uint2 lot[9];  // fp16 lo, two per dword
+            float lmax = 0.0f;
 #pragma unroll
-            for (int s = 0; s < NQF - (MXL ? 1 : 0); ++s) {
+            for (int s = 0; s < NN; ++s) {
                 // r = f32(q 2^k es), rounded once and opaque to the compiler:
                 // both terms are split from this one f32 value (otherwise hi
                 // may be recomputed as the fp16 rounding of the exact product,
                 // which differs where r sits on an fp16 rounding tie)
-                float r[4] = {v[it][s].x * mult, v[it][s].y * mult, v[it][s].z * mult,
-                              v[it][s].w * mult};
+                float r[4] = {vq[it][s].x * mult, vq[it][s].y * mult, vq[it][s].z * mult,
+                              vq[it][s].w * mult};
                 asm volatile("" : "+v"(r[0]), "+v"(r[1]), "+v"(r[2]), "+v"(r[3]));
-                f16x4 hi;
-#pragma unroll
-                for (int c = 0; c < 4; ++c) {
-                    hi[c] = (_Float16)r[c];
-                    lot[s][c] = (_Float16)(r[c] - (float)hi[c]);
-                }
+                const uint2 hi = make_uint2(pk_f16(r[0], r[1]), pk_f16(r[2], r[3]));
+                // r - hi, exact in f32
+                const float d0 = sub_f16<0>(r[0], hi.x), d1 = sub_f16<1>(r[1], hi.x);
+                const float d2 = sub_f16<0>(r[2], hi.y), d3 = sub_f16<1>(r[3], hi.y);
+                lmax = max3_abs(lmax, d0, d1);
+                lmax = max3_abs(lmax, d2, d3);
+                lot[s] = make_uint2(pk_f16(d0, d1), pk_f16(d2, d3));
                 const int e = 4 * (i + 16 * s);
                 const int cb = e >> 6, s2 = (e >> 5) & 1, hf = (e >> 4) & 1, t2 = (e >> 3) & 1;
                 const int ks = 4 * cb + 2 * s2 + t2;
-                *reinterpret_cast<f16x4*>(lds + QT + ((size_t)ks * 64 + h + 32 * hf) * 16 +
+                *reinterpret_cast<uint2*>(lds + QT + ((size_t)ks * 64 + h + 32 * hf) * 16 +
                                           2 * (e & 7)) = hi;
             }
             if constexpr (MXL) {
@@ -366,7 +370,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_partial32(AttnArgs a)
                 // + lo (no 2^k, no row scale), staged after the 28 noPE hi K
                 // steps as [K step m][term][lane] 16 bytes, m = i / 4, lane =
                 // head + 32 ((i / 2) % 2), bf16 positions 4 (i % 2) ..
-                const float4 q4 = v[it][NQF - 1];
+                const float4 q4 = vq[it][NQF - 1];
                 const float e[4] = {q4.x * es, q4.y * es, q4.z * es, q4.w * es};
                 uint32_t hb[4], lb[4];
 #pragma unroll
@@ -381,46 +385,120 @@ __global__ __launch_bounds__(kThreads, 1) void k_partial32(AttnArgs a)
                     make_uint2(lb[0] | (lb[1] << 16), lb[2] | (lb[3] << 16));
             }
             if constexpr (LO8) {
-                float lmax = 0.0f;
-#pragma unroll
-                for (int s = 0; s < NQF - (MXL ? 1 : 0); ++s)
-#pragma unroll
-                    for (int c = 0; c < 4; ++c)
-                        lmax = fmaxf(lmax, fabsf((float)lot[s][c]));
-                lmax = row16_max(lmax);
+                const float lm = (float)(_Float16)row16_max(lmax);  // largest |lo|
                 int ex = 0;
-                if (lmax > 0.0f)
-                    (void)frexpf(lmax, &ex);
-                const int j = (lmax > 0.0f) ? max(-100, min(100, 8 - ex)) : 0;
+                if (lm > 0.0f)
+                    (void)frexpf(lm, &ex);
+                const int j = (lm > 0.0f) ? max(-100, min(100, 8 - ex)) : 0;
                 if (i == 0)
                     s_k[HG + h] = j;
+                const float tj = ldexpf(1.0f, j);
 #pragma unroll
-                for (int s = 0; s < NQF - (MXL ? 1 : 0); ++s) {
+                for (int s = 0; s < NN; ++s) {
                     const int e = 4 * (i + 16 * s);
                     const int cb = e >> 6, off = e & 63, hf = (off >> 4) & 1;
                     const int b = 16 * (off >> 5) + (off & 15);
-                    // |lo 2^j| < 256: the packed hardware encoder is exact here
+                    // |lo 2^j| < 256 and exact: the packed hardware encoder
+                    // rounds it as the library's encoder does
                     *reinterpret_cast<uint32_t*>(lds + QL8 + ((size_t)(cb * 64 + h + 32 * hf)) * 32 +
                                                  b) =
-                        enc_e4m3_pk4(ldexpf((float)lot[s][0], j), ldexpf((float)lot[s][1], j),
-                                     ldexpf((float)lot[s][2], j), ldexpf((float)lot[s][3], j));
+                        enc_e4m3_pk4(mul_f16<0>(lot[s].x, tj), mul_f16<1>(lot[s].x, tj),
+                                     mul_f16<0>(lot[s].y, tj), mul_f16<1>(lot[s].y, tj));
                 }
             } else {
 #pragma unroll
                 for (int s = 0; s < 9; ++s)
-                    lo4[LO8 ? 0 : it][s] = lot[s];
+                    lo4[it][s] = __builtin_bit_cast(f16x4, lot[s]);
             }
         }
     };
+    // A chunk of at most kSplitTiles tiles is bound by this prologue's
+    // latency: there (LO8) every wave builds one item (t = tid), the context
+    // waves theirs after their query loads have arrived and before any row
+    // load goes out.  (Without LO8 the fp16 lo term kept for its own staging
+    // round would not fit beside the context waves' registers.)  Gather: the
+    // context waves load the first two tiles' list entries meanwhile and have
+    // them before any row load is in flight (a wait for them behind row loads
+    // would wait for those too); a tile past the chunk's last has its entries
+    // in the list too (p0 is clamped), so those loads need no branch.
+    // Each role and variant runs its own copy up to the builds (with its own
+    // barrier), so that no path joins another while query loads are in
+    // flight: at a join the compiler would wait for them, and thereby for the
+    // row loads, wherever it reuses their registers.
     using IT1 = std::integral_constant<int, 1>;
     using IT2 = std::integral_constant<int, 2>;
-    if (!ctx_wave) {
-        if (all_build)
-            build(IT1{});
+    auto prologue = [&](auto SPLIT_) __attribute__((always_inline)) {
+        constexpr bool SPLIT = decltype(SPLIT_)::value;
+        using NIT = std::integral_constant<int, SPLIT ? 1 : 2>;
+        if (!ctx_wave) {
+            load_q(NIT{});
+            // the score waves' query loads are ahead of the row loads; no
+            // build instruction moves before the barrier (it would wait for
+            // the query there)
+            __builtin_amdgcn_sched_barrier(0);
+            lds_barrier();
+            __builtin_amdgcn_sched_barrier(0);
+            build_q(NIT{});
+            // distinct ends keep the compiler from merging this build's tail
+            // with the context waves' (that tail would then wait for this
+            // path's query loads on both paths: for the row loads there)
+            asm volatile("; score-wave query build");
+        } else {
+            int32_t gp[2][GATHER ? 4 : 1], gsp[2];
+            if constexpr (GATHER) {
+                load_rows(0, gp[0], gsp[0]);
+                load_rows(1, gp[1], gsp[1]);
+            }
+            if constexpr (SPLIT)
+                load_q(IT1{});
+            __builtin_amdgcn_sched_barrier(0);
+            lds_barrier();
+            __builtin_amdgcn_sched_barrier(0);
+            // every query and list load has arrived before a row load goes out
+            if constexpr (SPLIT) {
+#pragma unroll
+                for (int s = 0; s < NQF; ++s)
+                    asm volatile("" : "+v"(vq[0][s].x), "+v"(vq[0][s].y), "+v"(vq[0][s].z),
+                                 "+v"(vq[0][s].w));
+            }
+            if constexpr (GATHER) {
+#pragma unroll
+                for (int u = 0; u < 2; ++u)
+#pragma unroll
+                    for (int rb = 0; rb < 4; ++rb)
+                        asm volatile("" : "+v"(gp[u][rb]));
+                asm volatile("" : "+v"(gsp[0]), "+v"(gsp[1]));
+            }
+            if (ntiles > 0) {
+                if constexpr (GATHER) {
+#pragma unroll
+                    for (int rb = 0; rb < 4; ++rb)
+                        g_row[rb] = gp[0][rb];
+                    g_sc = gsp[0];
+                }
+                issue(0, 0, IC0{}, ICK{}, GATHER);
+            }
+            if (ntiles > 1) {
+                if constexpr (GATHER) {
+#pragma unroll
+                    for (int rb = 0; rb < 4; ++rb)
+                        g_row[rb] = gp[1][rb];
+                    g_sc = gsp[1];
+                }
+                issue(1, 1, IC0{}, ICK{}, GATHER);
+            }
+            if constexpr (SPLIT)
+                build_q(IT1{});
+            asm volatile("; context-wave query build");
+        }
+    };
+    if constexpr (LO8) {
+        if (ntiles <= kSplitTiles)
+            prologue(std::true_type{});
         else
-            build(IT2{});
-    } else if (all_build) {
-        build(IT1{});
+            prologue(std::false_type{});
+    } else {
+        prologue(std::false_type{});
     }
     lds_barrier();
     if (!ctx_wave) {
@@ -449,11 +527,9 @@ __global__ __launch_bounds__(kThreads, 1) void k_partial32(AttnArgs a)
     }
     lds_barrier();  // LO8: staging areas free for the ring and the weights
     if constexpr (!LO8) {
-        if (all_build || !ctx_wave) {
+        if (!ctx_wave) {
 #pragma unroll
             for (int it = 0; it < 2; ++it) {
-                if (it == 1 && all_build)
-                    break;
                 const int t = tid + 256 * it, h = t >> 4, i = t & 15;
 #pragma unroll
                 for (int s = 0; s < 9; ++s) {

@@ -205,6 +205,9 @@ SHAPES = [
     (1, 64, 16, 1), (4, 64, 16, 63), (4, 64, 16, 65), (5, 64, 16, 1000),
     (17, 128, 0, 777), (33, 256, 32, 3001), (64, 512, 64, 2049), (128, 512, 64, 1),
     (48, 512, 128, 4500), (3, 16, 16, 130), (64, 448, 64, 515),
+    # the 512/64 kernel with a partial last head group (its heads past H
+    # take the last head's query, and are never stored)
+    (40, 512, 64, 700), (16, 512, 64, 300),
 ]
 
 

@@ -87,6 +87,33 @@ def test_lo8_decode_matches_its_query_reading(m, seed):
     assert not np.array_equal(host(out8), host(out))
 
 
+@pytest.mark.parametrize("h,t,splits", [(40, 700, 0), (16, 300, 3), (8, 64, 1)])
+def test_lo8_partial_head_group(m, h, t, splits):
+    """Head counts that leave the last group of 32 partly empty: the path's
+    result per head equals the oracle with that head's query_lo8 reading, and
+    the outputs of the heads past H are never written."""
+    lc, rc, sm = 512, 64, 1.0 / math.sqrt(192.0)
+    say(f"e4m3-lo decode, H={h} T={t} splits={splits}")
+    g = np.random.Generator(np.random.PCG64(700 + h + t))
+    x = (g.standard_normal((t, lc + rc)) * g.uniform(0.5, 2, (t, 1))).astype(np.float32)
+    ql = g.standard_normal((h, lc)).astype(np.float32)
+    qr = g.standard_normal((h, rc)).astype(np.float32)
+    codes, scales = m.mla8_quantize_rows(dev(x), lc, rc)
+    if splits == 0:
+        splits = m.mla8_plan_splits(m.MLA8_OP_DECODE, t, h)
+    out8, lse8 = m.mla8_decode(codes, scales, t, lc, rc, dev(ql), dev(qr), sm, n_splits=splits)
+    qql, qqr = oracle.query_lo8(ql, qr, sm)
+    r8, l8 = oracle.decode(host(codes), host(scales), t, lc, rc, qql, qqr, sm)
+    check_attention(host(out8), r8, host(lse8), l8, f"H={h} T={t}", few_rows=True)
+    # the same heads as the leading H of a full group give the same result
+    hf = 32 * ((h + 31) // 32)
+    qlf = np.concatenate([ql, np.repeat(ql[-1:], hf - h, 0)])
+    qrf = np.concatenate([qr, np.repeat(qr[-1:], hf - h, 0)])
+    outf, lsef = m.mla8_decode(codes, scales, t, lc, rc, dev(qlf), dev(qrf), sm, n_splits=splits)
+    np.testing.assert_array_equal(host(outf)[:h], host(out8))
+    np.testing.assert_array_equal(host(lsef)[:h], host(lse8))
+
+
 def test_lo8_fused_step_full_size(m):
     """The long-context step (262143 rows + one fresh row, 64 heads, 128
     chunks) on the default e4m3-lo scores: fused append + decode bit for bit
