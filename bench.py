@@ -24,9 +24,13 @@ sample on this host.
 from __future__ import annotations
 
 import argparse
+import atexit
 import json
 import os
+import re
+import subprocess
 import sys
+import tempfile
 import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
@@ -85,6 +89,10 @@ def parse():
                          "mixed_t262144: the decode step over mixed rows (noPE e4m3 448 + RoPE "
                          "bf16 64); dsa_t131072_ns2048: the selected-row decode over 2048 "
                          "rows; batch_s64_t32768: the causal batch of 64 queries")
+    ap.add_argument("--power", type=float, default=0.0, metavar="SECONDS",
+                    help="long-context workload: also sample the board's socket power and GFX "
+                         "clocks (amd-smi) while the step replays, and while the stream-read "
+                         "kernel replays, each for SECONDS of wall time, and at idle")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device copy (counter calibration) and exit")
     return ap.parse_args()
@@ -848,6 +856,8 @@ def main():
               "that exchange is not built)", file=sys.stderr)
         sys.exit(2)
 
+    sampler = PowerSampler() if (args.power > 0 and args.workload == "long_t262144") else None
+
     import numpy as np
     import torch
 
@@ -1012,6 +1022,34 @@ def main():
     log(f"stream-read ceiling {ceiling['gb_per_s']:.0f} GB/s; the partial kernel reaches "
         f"{100 * achieved / ceiling['gb_per_s']:.1f}% of it")
 
+    power = None
+    if sampler is not None:
+        # board power and clocks: idle, then the step's graph replayed, then
+        # the stream-read kernel over the same shadows replayed
+        torch.cuda.synchronize()
+        t_idle = time.time()
+        time.sleep(3.0)
+        idle_win = (t_idle + 1.0, time.time())
+        step_win, n_steps = power_run(run, args.power)
+        out_sr = torch.empty((m.MLA8_STREAM_WORDS,), dtype=torch.int32, device=dev)
+
+        def sread():
+            for ly in layers:
+                m.mla8_stream_read(ly["codes"], out_sr)
+
+        sr_win, n_sr = power_run(sread, args.power)
+        samples = sampler.stop()
+        sampler = None
+        step_s = step_win[1] - step_win[0] + 1.0
+        sr_s = sr_win[1] - sr_win[0] + 1.0
+        power = {"sampler": PowerSampler.CMD,
+                 "idle": power_window(samples, *idle_win),
+                 "step": dict(power_window(samples, *step_win), replays=n_steps,
+                              us_per_layer_token=round(step_s / (n_steps * L) * 1e6, 2)),
+                 "stream_read": dict(power_window(samples, *sr_win), passes=n_sr,
+                                     gb_per_s=round(n_sr * L * T * D / sr_s / 1e9, 1))}
+        log(f"power: {power}")
+
     cpu, parity = None, None
     if not args.no_cpu_baseline:
         cpu, (ro, rl) = cpu_baseline(w, args.cpu_heads, args.cpu_heads_one_core)
@@ -1054,6 +1092,8 @@ def main():
         "parity": parity,
         "f32_scores": f32s,
     }
+    if power is not None:
+        rec["power"] = power
     print(json.dumps(rec), flush=True)
 
 
@@ -1113,6 +1153,80 @@ def time_f32_scores(m, w, layers, ws, T, K, WU, no_graph):
             "kernel_us": round(float(np.mean(durs)), 3),
             "note": "mla8_opts.f32_scores: the query's lo term as fp16 on the fp16 MFMA "
                     "(scores of f32 grade); not the headline"}
+
+
+class PowerSampler:
+    """A child shell, started before this process touches the GPU, that runs
+    `amd-smi metric -p -c` (socket power, per-XCD GFX clocks) back to back,
+    each sample stamped with the wall time it was taken at, until stop()."""
+
+    CMD = "amd-smi metric -p -c"
+
+    def __init__(self):
+        fd, self.path = tempfile.mkstemp(prefix="mla8_power_", suffix=".txt")
+        os.close(fd)
+        self.flag = self.path + ".run"
+        open(self.flag, "w").close()
+        # the loop also ends when this process has gone
+        loop = (f'while [ -e "{self.flag}" ] && kill -0 $PPID 2>/dev/null; do '
+                f'echo "SAMPLE $(date +%s.%N)"; {self.CMD} 2>&1; sleep 0.2; done')
+        self.out = open(self.path, "w")
+        self.proc = subprocess.Popen(["bash", "-c", loop], stdout=self.out,
+                                     stderr=subprocess.STDOUT)
+        atexit.register(self._end)
+
+    def _end(self):
+        if os.path.exists(self.flag):
+            os.remove(self.flag)
+
+    def stop(self):
+        self._end()
+        try:
+            self.proc.wait(timeout=30)
+        except subprocess.TimeoutExpired:
+            self.proc.kill()
+            self.proc.wait()
+        self.out.close()
+        text = open(self.path).read()
+        os.remove(self.path)
+        samples = []
+        for blk in text.split("SAMPLE ")[1:]:
+            head, _, body = blk.partition("\n")
+            pw = re.findall(r"SOCKET_POWER:\s*([0-9.]+)\s*W", body)
+            clk = [float(c) for c in re.findall(r"GFX_\d+:\s*CLK:\s*([0-9.]+)\s*MHz", body)]
+            try:
+                t = float(head.strip())
+            except ValueError:
+                continue
+            if pw:
+                samples.append((t, float(pw[0]), sum(clk) / len(clk) if clk else None))
+        return samples
+
+
+def power_window(samples, t0, t1):
+    """Median socket power and mean GFX clock of the samples taken in [t0, t1]."""
+    import numpy as np
+    sel = [s for s in samples if t0 <= s[0] <= t1]
+    if not sel:
+        return {"samples": 0}
+    clk = [s[2] for s in sel if s[2] is not None]
+    return {"samples": len(sel), "socket_w_median": float(np.median([s[1] for s in sel])),
+            "socket_w_max": max(s[1] for s in sel),
+            "gfx_mhz_mean": round(float(np.mean(clk)), 1) if clk else None}
+
+
+def power_run(fn, seconds):
+    """Run fn() back to back for `seconds` of wall time; return the window
+    (start + 1 s, so that the clocks have settled, to the end) and the calls."""
+    import torch
+    t0 = time.time()
+    n = 0
+    while time.time() - t0 < seconds:
+        for _ in range(20):
+            fn()
+        torch.cuda.synchronize()
+        n += 20
+    return (t0 + 1.0, time.time()), n
 
 
 def stream_ceiling(bufs, passes=10):
