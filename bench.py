@@ -89,6 +89,9 @@ def parse():
                          "mixed_t262144: the decode step over mixed rows (noPE e4m3 448 + RoPE "
                          "bf16 64); dsa_t131072_ns2048: the selected-row decode over 2048 "
                          "rows; batch_s64_t32768: the causal batch of 64 queries")
+    ap.add_argument("--splits", type=int, default=0,
+                    help="dsa_t131072_ns2048 and dsv3_t4096: force this many row chunks "
+                         "(mla8_opts.n_splits) instead of the library's plan")
     ap.add_argument("--power", type=float, default=0.0, metavar="SECONDS",
                     help="long-context workload: also sample the board's socket power and GFX "
                          "clocks (amd-smi) while the step replays, and while the stream-read "
@@ -372,14 +375,16 @@ def bench_dsa(args):
                            ql=torch.from_numpy(ql).to(dev), qr=torch.from_numpy(qr).to(dev),
                            out=torch.empty((w.n_heads, w.lc), dtype=torch.float32, device=dev),
                            lse=torch.empty((w.n_heads,), dtype=torch.float32, device=dev)))
-    ws = torch.empty(m.mla8_workspace_bytes(m.MLA8_OP_DECODE_SEL, NS, w.n_heads, 1, w.lc),
+    ws = torch.empty(m.mla8_workspace_bytes(m.MLA8_OP_DECODE_SEL, NS, w.n_heads, 1, w.lc,
+                                            args.splits),
                      dtype=torch.uint8, device=dev)
     torch.cuda.synchronize()
     log(f"{L} layers of {T} rows quantized, {NS} selected per layer")
 
     def call(ly, events=None):
         m.mla8_decode_sel(ly["codes"], ly["scales"], T, w.lc, w.rc, ly["sel"], ly["ql"], ly["qr"],
-                          w.sm_scale, out=ly["out"], lse=ly["lse"], workspace=ws, events=events)
+                          w.sm_scale, out=ly["out"], lse=ly["lse"], workspace=ws, events=events,
+                          n_splits=args.splits)
 
     def step():
         for ly in layers:
@@ -427,11 +432,13 @@ def bench_dsa(args):
         "data": "synthetic: seeded N(0,1) rows and queries, sorted unique uniform selections",
         "config": {"workload": w.name, "heads": w.n_heads, "kv_lora": w.lc, "rope": w.rc,
                    "t_rows": T, "selected": NS, "batch": 1, "layers_per_step": L,
-                   "launch": "hip graph" if graph is not None else "eager"},
+                   "launch": "hip graph" if graph is not None else "eager",
+                   "splits": m.mla8_plan_splits(m.MLA8_OP_DECODE_SEL, NS, w.n_heads, 1,
+                                                args.splits)},
         "clock_settle": {"seconds": SETTLE_S, "untimed_steps": n_settle},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                     "kernel": "k_partial32<true,true>", "kernel_us": round(part_us, 3),
+                     "kernel": "k_partial32<true, true, false>", "kernel_us": round(part_us, 3),
                      "algorithmic_bytes": alg_bytes,
                      "note": "latency-bound: 1.19 MB of gathered rows per launch"},
         "cpu_baseline": cpu,
@@ -468,7 +475,7 @@ def bench_dsv3(args):
                            ql=torch.from_numpy(ql).to(dev), qr=torch.from_numpy(qr).to(dev),
                            out=torch.empty((w.n_heads, w.lc), dtype=torch.float32, device=dev),
                            lse=torch.empty((w.n_heads,), dtype=torch.float32, device=dev)))
-    ws = torch.empty(m.mla8_workspace_bytes(m.MLA8_OP_DECODE, T, w.n_heads, 1, w.lc),
+    ws = torch.empty(m.mla8_workspace_bytes(m.MLA8_OP_DECODE, T, w.n_heads, 1, w.lc, args.splits),
                      dtype=torch.uint8, device=dev)
     torch.cuda.synchronize()
     log(f"{L} layers of {T - 1} rows quantized")
@@ -476,7 +483,7 @@ def bench_dsv3(args):
     def call(ly, events=None):
         m.mla8_append_decode(ly["codes"], ly["scales"], T - 1, ly["fresh"], w.lc, w.rc,
                              ly["ql"], ly["qr"], w.sm_scale, out=ly["out"], lse=ly["lse"],
-                             workspace=ws, events=events)
+                             workspace=ws, events=events, n_splits=args.splits)
 
     def step():
         for ly in layers:
@@ -537,12 +544,12 @@ def bench_dsv3(args):
         "config": {"workload": w.name, "heads": w.n_heads, "kv_lora": w.lc, "rope": w.rc,
                    "t_rows": T, "batch": 1, "layers_per_step": L,
                    "launch": "hip graph" if graph is not None else "eager",
-                   "splits": m.mla8_plan_splits(m.MLA8_OP_DECODE, T, w.n_heads)},
+                   "splits": m.mla8_plan_splits(m.MLA8_OP_DECODE, T, w.n_heads, 1, args.splits)},
         "clock_settle": {"seconds": SETTLE_S, "untimed_steps": n_settle},
         "roofline": {"bound": "mfma", "achieved": round(tflops, 1),
                      "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(tflops / MFMA_F16_PEAK_TFLOPS, 4), "traffic": None,
-                     "kernel": "k_partial32", "kernel_us": round(part_us, 3),
+                     "kernel": "k_partial32<true, false, false>", "kernel_us": round(part_us, 3),
                      "algorithmic_flops": flops},
         "cpu_baseline": cpu,
         "parity": parity,
@@ -647,7 +654,7 @@ def bench_batch(args):
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2),
                      "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / MFMA_F16_PEAK_TFLOPS, 4), "traffic": None,
-                     "kernel": "k_partial32<true>", "kernel_us": round(part_us, 3),
+                     "kernel": "k_partial32<true, false, false>", "kernel_us": round(part_us, 3),
                      "algorithmic_flops": alg_flops,
                      "note": "flops of one pass per product; the hi and lo query terms take "
                              "1.5x the matrix-pipe time of one fp16 pass over the scores"},
@@ -761,7 +768,7 @@ def bench_mixed(args):
         "clock_settle": {"seconds": SETTLE_S, "untimed_steps": n_settle},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                     "kernel": "k_partial32<true,false,true>", "kernel_us": round(part_us, 3),
+                     "kernel": "k_partial32<true, false, true>", "kernel_us": round(part_us, 3),
                      "algorithmic_bytes": alg_bytes},
         "cpu_baseline": cpu,
     }
@@ -1004,7 +1011,7 @@ def main():
             log("traffic counters were taken on other kernel code: reporting null")
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                "kernel": "k_partial32", "kernel_us": round(part_us, 3),
+                "kernel": "k_partial32<true, false, false>", "kernel_us": round(part_us, 3),
                 "kernel_us_p10_p90": [round(float(np.percentile(durs, 10)), 3),
                                       round(float(np.percentile(durs, 90)), 3)],
                 "algorithmic_bytes": alg_bytes}
@@ -1149,7 +1156,7 @@ def time_f32_scores(m, w, layers, ws, T, K, WU, no_graph):
     durs = np.array([a.elapsed_time(b) for a, b in evs]) * 1e3
     for ly in layers:
         assert torch.isfinite(ly["out"]).all() and torch.isfinite(ly["lse"]).all()
-    return {"ms_per_layer_token": round(ms_lt, 6), "kernel": "k_partial32<f16 lo>",
+    return {"ms_per_layer_token": round(ms_lt, 6), "kernel": "k_partial32<false, false, false>",
             "kernel_us": round(float(np.mean(durs)), 3),
             "note": "mla8_opts.f32_scores: the query's lo term as fp16 on the fp16 MFMA "
                     "(scores of f32 grade); not the headline"}
