@@ -275,11 +275,12 @@ __global__ __launch_bounds__(kThreads, 1) void k_partial32(AttnArgs a)
     // ---- prologue: query operands, built by the score waves while the
     // context waves issue the first DIST tiles' loads (a wave with those in
     // flight could not wait for query loads of its own without waiting for
-    // them too).  The score waves' query loads go out first: a barrier holds
-    // the row loads back until they are issued, so that they do not queue
-    // behind the 73 KB of row loads in the CU's memory path.  Work item t
-    // (two per score-wave thread: t = tid and tid + 256) loads the nine float4 of head t / 16 at elements 4 (t % 16 + 16
-    // s), s < 9; the head's e = q * sm_scale * log2(e) is scaled by 2^k
+    // them too; short chunks differ, below).  The score waves' query loads
+    // go out first: a barrier holds the row loads back until they are
+    // issued, so that they do not queue behind the 73 KB of row loads in the
+    // CU's memory path.  Work item t (two per score-wave thread: t = tid and
+    // tid + 256) loads the nine float4 of head t / 16 at elements 4 (t % 16 +
+    // 16 s), s < 9; the head's e = q * sm_scale * log2(e) is scaled by 2^k
     // (largest |e| in [2^14, 2^15)) and split into fp16 hi + lo (the
     // subtraction is exact in f32).  hi is staged in the score waves' B
     // operand layout (K step ks = 4 cb + 2 s' + t' covers elements 64 cb +
