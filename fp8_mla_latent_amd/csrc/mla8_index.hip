@@ -418,6 +418,9 @@ __global__ __launch_bounds__(kSelectThreads) void k_index_final(IndexArgs a, int
     const int tid = threadIdx.x;
     const uint32_t k = (uint32_t)a.top_k;
     const uint32_t ns = (uint32_t)n_slices;
+    // the candidate pass's first-digit bin and the keys above it, loaded
+    // with the counts (not after a barrier, one memory round trip later)
+    const uint32_t b1 = a.top[1], above = a.top[2];
 
     // ---- per-slice counts and their exclusive prefix
     const uint32_t per = (ns + kSelectThreads - 1) / kSelectThreads;
@@ -474,7 +477,6 @@ __global__ __launch_bounds__(kSelectThreads) void k_index_final(IndexArgs a, int
         // larger key and the first `rem` (in row order) with key tau.  Its top
         // 12 bits are the candidate pass's bin b1, with `above` keys in higher
         // bins, so only the low 20 bits of the keys in bin b1 are selected on.
-        const uint32_t b1 = a.top[1], above = a.top[2];
         uint32_t rem;
         const uint32_t tau = (b1 << 20) | (uint32_t)radix_select(
             [&](uint32_t i, bool& in) -> uint64_t {
