@@ -1196,18 +1196,25 @@ class PowerSampler:
         self.out.close()
         text = open(self.path).read()
         os.remove(self.path)
-        samples = []
-        for blk in text.split("SAMPLE ")[1:]:
-            head, _, body = blk.partition("\n")
-            pw = re.findall(r"SOCKET_POWER:\s*([0-9.]+)\s*W", body)
-            clk = [float(c) for c in re.findall(r"GFX_\d+:\s*CLK:\s*([0-9.]+)\s*MHz", body)]
-            try:
-                t = float(head.strip())
-            except ValueError:
-                continue
-            if pw:
-                samples.append((t, float(pw[0]), sum(clk) / len(clk) if clk else None))
-        return samples
+        return parse_power_samples(text)
+
+
+def parse_power_samples(text):
+    """(wall time, socket W, mean GFX MHz or None) per sample of the
+    sampler's output: blocks that open with 'SAMPLE <unix time>'; a block
+    without a socket power reading is dropped."""
+    samples = []
+    for blk in text.split("SAMPLE ")[1:]:
+        head, _, body = blk.partition("\n")
+        pw = re.findall(r"SOCKET_POWER:\s*([0-9.]+)\s*W", body)
+        clk = [float(c) for c in re.findall(r"GFX_\d+:\s*CLK:\s*([0-9.]+)\s*MHz", body)]
+        try:
+            t = float(head.strip())
+        except ValueError:
+            continue
+        if pw:
+            samples.append((t, float(pw[0]), sum(clk) / len(clk) if clk else None))
+    return samples
 
 
 def power_window(samples, t0, t1):

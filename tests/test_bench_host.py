@@ -1,5 +1,6 @@
 """Host-side pieces of bench.py (no GPU): the code hash that ties the recorded
-HBM traffic counters to the kernel they were taken on."""
+HBM traffic counters to the kernel they were taken on, and the parsing of the
+power sampler's output and its windows."""
 from __future__ import annotations
 
 import importlib.util
@@ -38,3 +39,39 @@ def test_recorded_traffic_is_consistent():
     for raw, fac, cal in (("fetch_kib_raw", "fetch_factor", "fetch_bytes"),
                           ("write_kib_raw", "write_factor", "write_bytes")):
         assert abs(rec[raw] * 1024 * rec[fac] - rec[cal]) <= 1e-3 * rec[cal]
+
+
+SAMPLE_TEXT = """SAMPLE 100.25
+GPU: 0
+    POWER:
+        SOCKET_POWER: 1390 W
+    CLOCK:
+        GFX_0:
+            CLK: 1900 MHz
+            MIN_CLK: 500 MHz
+        GFX_1:
+            CLK: 2000 MHz
+        MEM_0:
+            CLK: 2000 MHz
+SAMPLE 101.50
+amd-smi: some error text
+SAMPLE 102.75
+GPU: 0
+    POWER:
+        SOCKET_POWER: 1100 W
+    CLOCK:
+        GFX_0:
+            CLK: 2400 MHz
+"""
+
+
+def test_power_samples_and_windows():
+    b = _bench()
+    s = b.parse_power_samples(SAMPLE_TEXT)
+    # the block without a power reading is dropped; MIN_CLK and MEM clocks are not GFX clocks
+    assert s == [(100.25, 1390.0, 1950.0), (102.75, 1100.0, 2400.0)]
+    w = b.power_window(s, 100.0, 101.0)
+    assert w["samples"] == 1 and w["socket_w_median"] == 1390.0 and w["gfx_mhz_mean"] == 1950.0
+    assert b.power_window(s, 0.0, 1.0) == {"samples": 0}
+    both = b.power_window(s, 100.0, 103.0)
+    assert both["samples"] == 2 and both["socket_w_max"] == 1390.0
