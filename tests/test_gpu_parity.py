@@ -441,6 +441,48 @@ def test_long_context_step_full(m):
     say(f"  worst elementwise err/bar {worst:.4f}")
 
 
+def test_shadow_past_2gib(m):
+    """A shadow of 2^22 rows: 2.42 GB of codes, so the rows past 3,728,270 lie
+    beyond byte 2^31 of the buffer.  Rows planted there (and one below) carry
+    head 0's largest scores, so a wrong address past 2^31 would move head 0's
+    output by about its magnitude.  Dense and selected-row decode (2048
+    sorted rows, the planted and the last ones among them), every head and
+    its lse against the oracle run with the path's query (query_lo8)."""
+    t, h, lc, rc = 1 << 22, 4, 512, 64
+    d = lc + rc
+    assert t * d > 2**31
+    g = np.random.Generator(np.random.PCG64(2022))
+    block = g.integers(0, 254, size=(1 << 16, d), dtype=np.uint8)
+    block[block >= 127] += 1  # no NaN codes (0x7F, 0xFF)
+    codes = np.tile(block, (t >> 16, 1))
+    scales = g.uniform(0.001, 0.004, t).astype(np.float32)
+    ql = g.standard_normal((h, lc)).astype(np.float32)
+    qr = g.standard_normal((h, rc)).astype(np.float32)
+    sm = 1.0 / math.sqrt(192.0)
+    # codes +-112, +-120, +-128 along head 0's query signs: the last two
+    # rows, past 2^31 bytes, carry head 0's largest scores
+    planted = np.array([3 << 20, t - 5000, t - 1], np.int64)
+    qsign = np.concatenate([np.sign(ql[0]), np.sign(qr[0])])
+    for k, r in enumerate(planted):
+        codes[r] = np.where(qsign >= 0, 0x6E + k, 0xEE + k).astype(np.uint8)
+        scales[r] = np.float32(0.01)
+    say(f"shadow of {t} rows ({codes.nbytes / 1e9:.2f} GB), {h} heads")
+    dc, ds = dev(codes), dev(scales)
+    qql, qqr = oracle.query_lo8(ql, qr, sm)
+    out, lse = m.mla8_decode(dc, ds, t, lc, rc, dev(ql), dev(qr), sm)
+    ro, rl = oracle.decode(codes, scales, t, lc, rc, qql, qqr, sm)
+    # head 0 attends the planted rows almost alone
+    assert np.abs(ro[0]).max() > 1.0
+    check_attention(host(out), ro, host(lse), rl, "dense, T = 2^22", few_rows=True)
+    rnd = g.choice(t - 5001, 2041, replace=False)  # below t - 5000, none equal to 3 << 20
+    rnd[rnd >= (3 << 20)] += 1
+    sel = np.sort(np.concatenate([rnd, planted, np.arange(t - 5, t - 1)])).astype(np.int32)
+    assert sel.size == 2048 and np.unique(sel).size == 2048 and sel[-1] == t - 1
+    out2, lse2 = m.mla8_decode_sel(dc, ds, t, lc, rc, dev(sel), dev(ql), dev(qr), sm)
+    ro2, rl2 = oracle.decode_sel(codes, scales, t, lc, rc, sel, qql, qqr, sm)
+    check_attention(host(out2), ro2, host(lse2), rl2, "selected, T = 2^22", few_rows=True)
+
+
 # The read-bandwidth reference: every 32-bit word of the buffer reaches the
 # XOR fold (so no load can be dropped), for sizes below, at and past one
 # 4-load round of the grid and with a tail.
