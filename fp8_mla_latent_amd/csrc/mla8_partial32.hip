@@ -1031,13 +1031,15 @@ __global__ __launch_bounds__(kThreads, 1) void k_partial32(AttnArgs a)
         }
     }
 
-    // ---- partial m and z (z summed over the four score waves' row quarters)
+    // ---- partial m and z (z summed over the four score waves' row quarters),
+    // streaming stores like cl's: no dirty L2 lines left for the kernel's end
     __syncthreads();
     if (w < 2 && lane < 16) {
         const int h = 16 * (w & 1) + n, qh = qh0 + h;
         if (qh < a.n_qh) {
-            a.ws_m[pbase + qh] = (w & 1) ? mrun1 : mrun0;
-            a.ws_z[pbase + qh] = (s_z[h] + s_z[HG + h]) + (s_z[2 * HG + h] + s_z[3 * HG + h]);
+            __builtin_nontemporal_store((w & 1) ? mrun1 : mrun0, a.ws_m + pbase + qh);
+            __builtin_nontemporal_store((s_z[h] + s_z[HG + h]) + (s_z[2 * HG + h] + s_z[3 * HG + h]),
+                                        a.ws_z + pbase + qh);
         }
     }
 }
