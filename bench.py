@@ -93,9 +93,10 @@ def parse():
                     help="dsa_t131072_ns2048 and dsv3_t4096: force this many row chunks "
                          "(mla8_opts.n_splits) instead of the library's plan")
     ap.add_argument("--power", type=float, default=0.0, metavar="SECONDS",
-                    help="long-context workload: also sample the board's socket power and GFX "
-                         "clocks (amd-smi) while the step replays, and while the stream-read "
-                         "kernel replays, each for SECONDS of wall time, and at idle")
+                    help="long-context and causal-batch workloads: also sample the board's socket "
+                         "power and GFX clocks (amd-smi) while the step replays (long context: and "
+                         "while the stream-read kernel replays), each for SECONDS of wall time, "
+                         "and at idle")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device copy (counter calibration) and exit")
     return ap.parse_args()
@@ -557,7 +558,7 @@ def bench_dsv3(args):
     print(json.dumps(rec), flush=True)
 
 
-def bench_batch(args):
+def bench_batch(args, sampler=None):
     """Causal batch (prefill / streaming): per layer, append 64 fresh rows at
     pos0 = 32704 of its own shadow (T = 32768), then mla8_batch with S = 64
     queries, query s attending rows [0, pos0 + s], H = 64.  MFMA-bound."""
@@ -615,6 +616,21 @@ def bench_batch(args):
         f"({100 * achieved / MFMA_F16_PEAK_TFLOPS:.1f}% of {MFMA_F16_PEAK_TFLOPS:.0f})")
     for ly in layers:
         assert torch.isfinite(ly["out"]).all() and torch.isfinite(ly["lse"]).all()
+    power = None
+    if sampler is not None:
+        # board power and clocks: idle, then the step's graph replayed
+        torch.cuda.synchronize()
+        t_idle = time.time()
+        time.sleep(3.0)
+        idle_win = (t_idle + 1.0, time.time())
+        step_win, n_steps = power_run(run, args.power)
+        samples = sampler.stop()
+        step_s = step_win[1] - step_win[0] + 1.0
+        power = {"sampler": PowerSampler.CMD,
+                 "idle": power_window(samples, *idle_win),
+                 "step": dict(power_window(samples, *step_win), replays=n_steps,
+                              us_per_layer_token=round(step_s / (n_steps * L * S) * 1e6, 3))}
+        log(f"power: {power}")
     cpu = None
     if not args.no_cpu_baseline:
         import oracle
@@ -660,6 +676,8 @@ def bench_batch(args):
                              "1.5x the matrix-pipe time of one fp16 pass over the scores"},
         "cpu_baseline": cpu,
     }
+    if power is not None:
+        rec["power"] = power
     print(json.dumps(rec), flush=True)
 
 
@@ -863,7 +881,8 @@ def main():
               "that exchange is not built)", file=sys.stderr)
         sys.exit(2)
 
-    sampler = PowerSampler() if (args.power > 0 and args.workload == "long_t262144") else None
+    sampler = (PowerSampler() if args.power > 0
+               and args.workload in ("long_t262144", "batch_s64_t32768") else None)
 
     import numpy as np
     import torch
@@ -896,7 +915,7 @@ def main():
         bench_dsv3(args)
         return
     if args.workload == "batch_s64_t32768":
-        bench_batch(args)
+        bench_batch(args, sampler)
         return
     if args.workload == "mixed_t262144":
         bench_mixed(args)
