@@ -1151,45 +1151,55 @@ __global__ __launch_bounds__(kThreads, 1) void k_split_partial(AttnArgs a)
 
 // ---------------------------------------------------------------------------
 // Log-sum-exp merge of the n_chunks partials of every query-head.
-// 512 threads = 8 waves; lane = two adjacent context columns (one 8-byte load
-// per partial; lc is a multiple of 16).  The waves split into slabs of W =
-// min(8, n_chunks rounded up to a power of two) waves: a slab covers 128
+// NW waves per workgroup; lane = two adjacent context columns (one 8-byte
+// load per partial; lc is a multiple of 16).  The waves split into slabs of
+// W = min(NW, n_chunks rounded up to a power of two) waves: a slab covers 128
 // columns and its waves fold partials p = c, c + W, ... (c = the wave's rank
 // in the slab) with an online maximum, kMergeBatch partials per batch whose
 // loads are all issued before any is used; each slab's waves then combine
-// through LDS.  Grid (n_qh, ceil(lc / (128 * 8 / W))).  A few partials (the
+// through LDS.  Grid (n_qh, ceil(lc / (128 * NW / W))).  A few partials (the
 // causal batch's 2 chunks) thus fill the waves with columns instead of
 // leaving them idle.
 //   M = max_p m_p;  w_p = 2^(m_p - M);  out = sum_p w_p cl_p / sum_p w_p z_p;
 //   lse = (M + log2 sum_p w_p z_p) * ln 2.
-// Measured against one column per lane and four waves (two batches of 16 per
-// wave): 1.3 us less per decode call at the long-context shape.
+// NW = 8 for more than 32 partials per query-head, else 4: measured against
+// 8 waves throughout, 0.25 us less per gathered decode call (32 partials) and
+// 0.7 us less at the DeepSeek-V3 shape (32), while the long-context shape
+// (128 partials) is 1.1 us slower with 4 and 0.8 us slower with 16.  Against
+// one column per lane and four waves (two batches of 16 per wave): 1.3 us
+// less per decode call at the long-context shape.
 constexpr int kMergeBatch = 16;
-constexpr int kMergeWaves = 8;
+constexpr int kMergeWavesMax = 8;
 
-__host__ __device__ __forceinline__ int merge_slab_waves(int n_chunks)
+__host__ __device__ __forceinline__ int merge_waves(int n_chunks)
+{
+    return n_chunks > 32 ? 8 : 4;
+}
+
+__host__ __device__ __forceinline__ int merge_slab_waves(int n_chunks, int nw)
 {
     int w = 1;
-    while (w < n_chunks && w < kMergeWaves)
+    while (w < n_chunks && w < nw)
         w <<= 1;
     return w;
 }
 
-__global__ __launch_bounds__(64 * kMergeWaves) void k_merge(const float* __restrict__ ws_m,
+template <int NW>
+__global__ __launch_bounds__(64 * NW) void k_merge(const float* __restrict__ ws_m,
                                                             const float* __restrict__ ws_z,
                                                             const float* __restrict__ ws_cl,
                                                             int32_t n_chunks, int32_t n_qh,
                                                             int32_t lc, float* __restrict__ out,
                                                             float* __restrict__ lse)
 {
-    __shared__ float2 s_a[kMergeWaves][64];
-    __shared__ float s_zw[kMergeWaves];
-    __shared__ float s_mw[kMergeWaves];
+    __shared__ float2 s_a[NW][64];
+    __shared__ float s_zw[NW];
+    __shared__ float s_mw[NW];
     const int qh = blockIdx.x;
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-    const int W = merge_slab_waves(n_chunks);
+    const int W = merge_slab_waves(n_chunks, NW);
     const int slab = wv / W, wc = wv - slab * W;
-    const int col = (blockIdx.y * (kMergeWaves / W) + slab) * 128 + 2 * lane;
+    const int col = (blockIdx.y * (NW / W) + slab) * 128 + 2 * lane;
     const bool cv = col < lc;  // lc even: both columns or neither
     float mw = -INFINITY, zw = 0.0f;
     float2 aw = make_float2(0.0f, 0.0f);
@@ -1407,10 +1417,15 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t stream, hipEvent_t ev
         if (e != hipSuccess)
             return e;
     }
-    const int cols = 128 * (kMergeWaves / merge_slab_waves(a.n_chunks));  // columns per workgroup
-    hipLaunchKernelGGL(k_merge, dim3((unsigned)a.n_qh, (unsigned)((a.lc + cols - 1) / cols)),
-                       dim3(64 * kMergeWaves), 0,
-                       stream, a.ws_m, a.ws_z, a.ws_cl, a.n_chunks, a.n_qh, a.lc, a.out, a.lse);
+    const int nw = merge_waves(a.n_chunks);
+    const int cols = 128 * (nw / merge_slab_waves(a.n_chunks, nw));  // columns per workgroup
+    const dim3 grid((unsigned)a.n_qh, (unsigned)((a.lc + cols - 1) / cols));
+    if (nw == kMergeWavesMax)
+        hipLaunchKernelGGL(k_merge<kMergeWavesMax>, grid, dim3(64 * kMergeWavesMax), 0, stream,
+                           a.ws_m, a.ws_z, a.ws_cl, a.n_chunks, a.n_qh, a.lc, a.out, a.lse);
+    else
+        hipLaunchKernelGGL(k_merge<4>, grid, dim3(64 * 4), 0, stream, a.ws_m, a.ws_z, a.ws_cl,
+                           a.n_chunks, a.n_qh, a.lc, a.out, a.lse);
     return hipGetLastError();
 }
 
