@@ -1155,22 +1155,23 @@ __global__ __launch_bounds__(kThreads, 1) void k_split_partial(AttnArgs a)
 // load per partial; lc is a multiple of 16).  The waves split into slabs of
 // W = min(NW, n_chunks rounded up to a power of two) waves: a slab covers 128
 // columns and its waves fold partials p = c, c + W, ... (c = the wave's rank
-// in the slab) with an online maximum, kMergeBatch partials per batch whose
-// loads are all issued before any is used; each slab's waves then combine
+// in the slab) with an online maximum, NB partials per batch whose loads are
+// all issued before any is used; each slab's waves then combine
 // through LDS.  Grid (n_qh, ceil(lc / (128 * NW / W))).  A few partials (the
 // causal batch's 2 chunks) thus fill the waves with columns instead of
 // leaving them idle.
 //   M = max_p m_p;  w_p = 2^(m_p - M);  out = sum_p w_p cl_p / sum_p w_p z_p;
 //   lse = (M + log2 sum_p w_p z_p) * ln 2.
-// NW = 8 for more than 32 partials per query-head, else 4: measured against
-// 8 waves throughout, 0.25 us less per gathered decode call (32 partials) and
-// 0.7 us less at the DeepSeek-V3 shape (32), while the long-context shape
-// (128 partials) is 1.1 us slower with 4 and 0.8 us slower with 16.  Against
-// one column per lane and four waves (two batches of 16 per wave): 1.3 us
-// less per decode call at the long-context shape.
-constexpr int kMergeBatch = 16;
-constexpr int kMergeWavesMax = 8;
-
+// (NW, NB) = (8, 16) for more than 32 partials per query-head, (4, 8) for 5
+// to 32, (4, 1) for at most 4, so that up to 128 partials each wave folds its
+// own in one batch.  Measured in pairs, alternating on one box: (4, 16)
+// against (8, 16): gathered decode (32 partials) -0.26 us per call,
+// DeepSeek-V3 shape (32) -0.69 us, causal batch (2) -1.0%, long context
+// (128) +1.1 us (and (16, 16) slower at every shape); (4, 8) against
+// (4, 16): -0.26 us, -0.32 us, -2.4%; (4, 4) against (4, 8): +0.56 us,
+// +0.5 us; (4, 1) against (4, 8) on the causal batch: -0.9%.  Against one
+// column per lane and four waves (two batches of 16 per wave): 1.3 us less
+// per decode call at the long-context shape.
 __host__ __device__ __forceinline__ int merge_waves(int n_chunks)
 {
     return n_chunks > 32 ? 8 : 4;
@@ -1184,13 +1185,13 @@ __host__ __device__ __forceinline__ int merge_slab_waves(int n_chunks, int nw)
     return w;
 }
 
-template <int NW>
+template <int NW, int NB>
 __global__ __launch_bounds__(64 * NW) void k_merge(const float* __restrict__ ws_m,
-                                                            const float* __restrict__ ws_z,
-                                                            const float* __restrict__ ws_cl,
-                                                            int32_t n_chunks, int32_t n_qh,
-                                                            int32_t lc, float* __restrict__ out,
-                                                            float* __restrict__ lse)
+                                                   const float* __restrict__ ws_z,
+                                                   const float* __restrict__ ws_cl,
+                                                   int32_t n_chunks, int32_t n_qh, int32_t lc,
+                                                   float* __restrict__ out,
+                                                   float* __restrict__ lse)
 {
     __shared__ float2 s_a[NW][64];
     __shared__ float s_zw[NW];
@@ -1203,11 +1204,11 @@ __global__ __launch_bounds__(64 * NW) void k_merge(const float* __restrict__ ws_
     const bool cv = col < lc;  // lc even: both columns or neither
     float mw = -INFINITY, zw = 0.0f;
     float2 aw = make_float2(0.0f, 0.0f);
-    for (int base = wc; base < n_chunks; base += W * kMergeBatch) {
-        float mp[kMergeBatch], zp[kMergeBatch];
-        float2 cp[kMergeBatch];
+    for (int base = wc; base < n_chunks; base += W * NB) {
+        float mp[NB], zp[NB];
+        float2 cp[NB];
 #pragma unroll
-        for (int k = 0; k < kMergeBatch; ++k) {
+        for (int k = 0; k < NB; ++k) {
             const int pp = base + W * k;
             const bool ok = pp < n_chunks;
             const size_t i = (size_t)(ok ? pp : 0) * n_qh + qh;
@@ -1218,7 +1219,7 @@ __global__ __launch_bounds__(64 * NW) void k_merge(const float* __restrict__ ws_
         }
         float bm = -INFINITY;
 #pragma unroll
-        for (int k = 0; k < kMergeBatch; ++k)
+        for (int k = 0; k < NB; ++k)
             bm = fmaxf(bm, mp[k]);
         if (bm == -INFINITY)
             continue;
@@ -1230,7 +1231,7 @@ __global__ __launch_bounds__(64 * NW) void k_merge(const float* __restrict__ ws_
             mw = bm;
         }
 #pragma unroll
-        for (int k = 0; k < kMergeBatch; ++k) {
+        for (int k = 0; k < NB; ++k) {
             const float wgt = (mp[k] == -INFINITY) ? 0.0f : exp2f(mp[k] - mw);
             zw += wgt * zp[k];
             aw.x += wgt * cp[k].x;
@@ -1420,12 +1421,15 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t stream, hipEvent_t ev
     const int nw = merge_waves(a.n_chunks);
     const int cols = 128 * (nw / merge_slab_waves(a.n_chunks, nw));  // columns per workgroup
     const dim3 grid((unsigned)a.n_qh, (unsigned)((a.lc + cols - 1) / cols));
-    if (nw == kMergeWavesMax)
-        hipLaunchKernelGGL(k_merge<kMergeWavesMax>, grid, dim3(64 * kMergeWavesMax), 0, stream,
-                           a.ws_m, a.ws_z, a.ws_cl, a.n_chunks, a.n_qh, a.lc, a.out, a.lse);
+    if (nw == 8)
+        hipLaunchKernelGGL((k_merge<8, 16>), grid, dim3(64 * 8), 0, stream, a.ws_m, a.ws_z,
+                           a.ws_cl, a.n_chunks, a.n_qh, a.lc, a.out, a.lse);
+    else if (a.n_chunks > 4)
+        hipLaunchKernelGGL((k_merge<4, 8>), grid, dim3(64 * 4), 0, stream, a.ws_m, a.ws_z,
+                           a.ws_cl, a.n_chunks, a.n_qh, a.lc, a.out, a.lse);
     else
-        hipLaunchKernelGGL(k_merge<4>, grid, dim3(64 * 4), 0, stream, a.ws_m, a.ws_z, a.ws_cl,
-                           a.n_chunks, a.n_qh, a.lc, a.out, a.lse);
+        hipLaunchKernelGGL((k_merge<4, 1>), grid, dim3(64 * 4), 0, stream, a.ws_m, a.ws_z,
+                           a.ws_cl, a.n_chunks, a.n_qh, a.lc, a.out, a.lse);
     return hipGetLastError();
 }
 
