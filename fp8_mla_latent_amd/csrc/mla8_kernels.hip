@@ -1151,15 +1151,20 @@ __global__ __launch_bounds__(kThreads, 1) void k_split_partial(AttnArgs a)
 
 // ---------------------------------------------------------------------------
 // Log-sum-exp merge of the n_chunks partials of every query-head.
-// NW waves per workgroup; lane = two adjacent context columns (one 8-byte
-// load per partial; lc is a multiple of 16).  The waves split into slabs of
-// W = min(NW, n_chunks rounded up to a power of two) waves: a slab covers 128
-// columns and its waves fold partials p = c, c + W, ... (c = the wave's rank
-// in the slab) with an online maximum, NB partials per batch whose loads are
-// all issued before any is used; each slab's waves then combine
-// through LDS.  Grid (n_qh, ceil(lc / (128 * NW / W))).  A few partials (the
-// causal batch's 2 chunks) thus fill the waves with columns instead of
-// leaving them idle.
+// NW waves per workgroup; lane = CPL adjacent context columns (one 8- or
+// 16-byte load per partial; lc is a multiple of 16).  The waves split into
+// slabs of W = min(NW, n_chunks rounded up to a power of two) waves: a slab
+// covers 64 CPL columns and its waves fold partials p = c, c + W, ... (c =
+// the wave's rank in the slab) with an online maximum, NB partials per batch
+// whose loads are all issued before any is used; each slab's waves then
+// combine through LDS.  Grid (n_qh, ceil(lc / (64 CPL NW / W))).  A few
+// partials (the causal batch's 2 chunks) thus fill the waves with columns
+// instead of leaving them idle.  CPL = 4 where that grid still has a
+// workgroup for each of the 256 CUs, else 2: against 2 throughout, the
+// DeepSeek-V3 shape (128 query-heads) 17.53 against 17.70 us per
+// layer-token and the causal batch 5.71 against 5.73, while the gathered
+// decode (64 query-heads, 128 workgroups with 4) and the long-context shape
+// were no faster with 4.
 //   M = max_p m_p;  w_p = 2^(m_p - M);  out = sum_p w_p cl_p / sum_p w_p z_p;
 //   lse = (M + log2 sum_p w_p z_p) * ln 2.
 // (NW, NB) = (8, 16) for more than 32 partials per query-head, (4, 8) for 5
@@ -1185,7 +1190,7 @@ __host__ __device__ __forceinline__ int merge_slab_waves(int n_chunks, int nw)
     return w;
 }
 
-template <int NW, int NB>
+template <int NW, int NB, int CPL>
 __global__ __launch_bounds__(64 * NW) void k_merge(const float* __restrict__ ws_m,
                                                    const float* __restrict__ ws_z,
                                                    const float* __restrict__ ws_cl,
@@ -1193,20 +1198,21 @@ __global__ __launch_bounds__(64 * NW) void k_merge(const float* __restrict__ ws_
                                                    float* __restrict__ out,
                                                    float* __restrict__ lse)
 {
-    __shared__ float2 s_a[NW][64];
+    typedef float fv __attribute__((ext_vector_type(CPL)));
+    __shared__ fv s_a[NW][64];
     __shared__ float s_zw[NW];
     __shared__ float s_mw[NW];
     const int qh = blockIdx.x;
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
     const int W = merge_slab_waves(n_chunks, NW);
     const int slab = wv / W, wc = wv - slab * W;
-    const int col = (blockIdx.y * (NW / W) + slab) * 128 + 2 * lane;
-    const bool cv = col < lc;  // lc even: both columns or neither
+    const int col = (blockIdx.y * (NW / W) + slab) * (64 * CPL) + CPL * lane;
+    const bool cv = col < lc;  // lc a multiple of 16: all CPL columns or none
     float mw = -INFINITY, zw = 0.0f;
-    float2 aw = make_float2(0.0f, 0.0f);
+    fv aw = fv(0.0f);
     for (int base = wc; base < n_chunks; base += W * NB) {
         float mp[NB], zp[NB];
-        float2 cp[NB];
+        fv cp[NB];
 #pragma unroll
         for (int k = 0; k < NB; ++k) {
             const int pp = base + W * k;
@@ -1214,8 +1220,7 @@ __global__ __launch_bounds__(64 * NW) void k_merge(const float* __restrict__ ws_
             const size_t i = (size_t)(ok ? pp : 0) * n_qh + qh;
             mp[k] = ok ? ws_m[i] : -INFINITY;
             zp[k] = ok ? ws_z[i] : 0.0f;
-            cp[k] = (ok && cv) ? *reinterpret_cast<const float2*>(ws_cl + i * lc + col)
-                               : make_float2(0.0f, 0.0f);
+            cp[k] = (ok && cv) ? *reinterpret_cast<const fv*>(ws_cl + i * lc + col) : fv(0.0f);
         }
         float bm = -INFINITY;
 #pragma unroll
@@ -1226,16 +1231,14 @@ __global__ __launch_bounds__(64 * NW) void k_merge(const float* __restrict__ ws_
         if (bm > mw) {
             const float f = (mw == -INFINITY) ? 0.0f : exp2f(mw - bm);
             zw *= f;
-            aw.x *= f;
-            aw.y *= f;
+            aw *= f;
             mw = bm;
         }
 #pragma unroll
         for (int k = 0; k < NB; ++k) {
             const float wgt = (mp[k] == -INFINITY) ? 0.0f : exp2f(mp[k] - mw);
             zw += wgt * zp[k];
-            aw.x += wgt * cp[k].x;
-            aw.y += wgt * cp[k].y;
+            aw += wgt * cp[k];
         }
     }
     s_a[wv][lane] = aw;
@@ -1249,22 +1252,20 @@ __global__ __launch_bounds__(64 * NW) void k_merge(const float* __restrict__ ws_
         float M = s_mw[w0];
         for (int k = 1; k < W; ++k)
             M = fmaxf(M, s_mw[w0 + k]);
-        float2 A = make_float2(0.0f, 0.0f);
+        fv A = fv(0.0f);
         float Z = 0.0f;
         if (M != -INFINITY) {
             for (int k = 0; k < W; ++k) {
                 const float wk = (s_mw[w0 + k] == -INFINITY) ? 0.0f : exp2f(s_mw[w0 + k] - M);
-                A.x += wk * s_a[w0 + k][lane].x;
-                A.y += wk * s_a[w0 + k][lane].y;
+                A += wk * s_a[w0 + k][lane];
                 Z += wk * s_zw[w0 + k];
             }
         }
         if (cv) {
             // a streaming store: the kernel's end then has no dirty L2 lines
             // to write back (0.1 us less per gathered decode call)
-            typedef float f2v __attribute__((ext_vector_type(2)));
-            const f2v o = (M == -INFINITY) ? f2v{0.0f, 0.0f} : f2v{A.x / Z, A.y / Z};
-            __builtin_nontemporal_store(o, reinterpret_cast<f2v*>(out + (size_t)qh * lc + col));
+            const fv o = (M == -INFINITY) ? fv(0.0f) : A / Z;
+            __builtin_nontemporal_store(o, reinterpret_cast<fv*>(out + (size_t)qh * lc + col));
         }
         if (lse != nullptr && blockIdx.y == 0 && slab == 0 && lane == 0)
             lse[qh] = (M == -INFINITY) ? -INFINITY : (M + log2f(Z)) * 0.69314718055994531f;
@@ -1379,6 +1380,20 @@ static void launch_partial(const AttnArgs& a, hipStream_t stream)
                            dim3((unsigned)(a.n_chunks * a.n_groups)), dim3(kThreads), 0, stream, a);
 }
 
+template <int CPL>
+static void launch_merge(const AttnArgs& a, int nw, dim3 grid, hipStream_t stream)
+{
+    if (nw == 8)
+        hipLaunchKernelGGL((k_merge<8, 16, CPL>), grid, dim3(64 * 8), 0, stream, a.ws_m, a.ws_z,
+                           a.ws_cl, a.n_chunks, a.n_qh, a.lc, a.out, a.lse);
+    else if (a.n_chunks > 4)
+        hipLaunchKernelGGL((k_merge<4, 8, CPL>), grid, dim3(64 * 4), 0, stream, a.ws_m, a.ws_z,
+                           a.ws_cl, a.n_chunks, a.n_qh, a.lc, a.out, a.lse);
+    else
+        hipLaunchKernelGGL((k_merge<4, 1, CPL>), grid, dim3(64 * 4), 0, stream, a.ws_m, a.ws_z,
+                           a.ws_cl, a.n_chunks, a.n_qh, a.lc, a.out, a.lse);
+}
+
 hipError_t launch_attention(const AttnArgs& a, hipStream_t stream, hipEvent_t ev_before,
                             hipEvent_t ev_after)
 {
@@ -1419,17 +1434,15 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t stream, hipEvent_t ev
             return e;
     }
     const int nw = merge_waves(a.n_chunks);
-    const int cols = 128 * (nw / merge_slab_waves(a.n_chunks, nw));  // columns per workgroup
+    // four columns per lane where the grid still gives every CU a workgroup
+    const int slabs = nw / merge_slab_waves(a.n_chunks, nw);
+    const int cpl = (long)a.n_qh * ((a.lc + 256 * slabs - 1) / (256 * slabs)) >= 256 ? 4 : 2;
+    const int cols = 64 * cpl * slabs;  // columns per workgroup
     const dim3 grid((unsigned)a.n_qh, (unsigned)((a.lc + cols - 1) / cols));
-    if (nw == 8)
-        hipLaunchKernelGGL((k_merge<8, 16>), grid, dim3(64 * 8), 0, stream, a.ws_m, a.ws_z,
-                           a.ws_cl, a.n_chunks, a.n_qh, a.lc, a.out, a.lse);
-    else if (a.n_chunks > 4)
-        hipLaunchKernelGGL((k_merge<4, 8>), grid, dim3(64 * 4), 0, stream, a.ws_m, a.ws_z,
-                           a.ws_cl, a.n_chunks, a.n_qh, a.lc, a.out, a.lse);
+    if (cpl == 4)
+        launch_merge<4>(a, nw, grid, stream);
     else
-        hipLaunchKernelGGL((k_merge<4, 1>), grid, dim3(64 * 4), 0, stream, a.ws_m, a.ws_z,
-                           a.ws_cl, a.n_chunks, a.n_qh, a.lc, a.out, a.lse);
+        launch_merge<2>(a, nw, grid, stream);
     return hipGetLastError();
 }
 
